@@ -1,0 +1,213 @@
+"""Python access to the CPU oracle (oracle.c) through ctypes.
+
+TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the bench's
+CPU-baseline leg import this package.  The product library and its Python
+binding never import it, and it imports nothing from them.
+
+All functions take and return numpy arrays on the host.  bfloat16 data is
+passed as its raw 16-bit patterns (uint16 arrays).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+# Flags that keep float arithmetic exactly IEEE binary32 with round-to-nearest:
+# no contraction into fused multiply-add, no reassociation, no excess precision.
+CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
+          "-fexcess-precision=standard", "-msse2", "-mfpmath=sse", "-Wall", "-Wextra"]
+
+F32, BF16 = 0, 1
+ERRORS = {0: "ok", 1: "bad argument", 4: "index out of range", 6: "out of memory"}
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so with gcc."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.run(["gcc", *CFLAGS, _SRC, "-o", tmp], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        i64, i32, vp, u64 = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_uint64
+        L.oracle_tree_sum_f32.argtypes = [vp, i64, vp]
+        L.oracle_tree_sum_bf16.argtypes = [vp, i64, vp]
+        L.oracle_sort_by_dest.argtypes = [vp, vp, i64, i32, vp, vp, vp]
+        L.oracle_scatter_reduce.argtypes = [vp, i32, i64, vp, ctypes.c_int, i64, vp, vp, vp, i64]
+        L.oracle_combine.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, i64, i32, vp, i64, vp]
+        L.oracle_splitk_reduce.argtypes = [vp, i32, i64, vp]
+        L.oracle_splitk_reference.argtypes = [vp, vp, i64, i64, i64, vp, vp]
+        L.oracle_splitk_partials.argtypes = [vp, vp, i64, i64, i64, i32, vp]
+        L.oracle_splitmix64_mix.argtypes = [u64]
+        L.oracle_splitmix64_mix.restype = u64
+        L.oracle_fingerprint.argtypes = [vp, i64]
+        L.oracle_fingerprint.restype = u64
+        for name in ("oracle_tree_sum_f32", "oracle_tree_sum_bf16", "oracle_sort_by_dest",
+                     "oracle_scatter_reduce", "oracle_combine", "oracle_splitk_reduce",
+                     "oracle_splitk_reference", "oracle_splitk_partials"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise OracleError(f"{what}: {ERRORS.get(rc, rc)}")
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def tree_sum_f32(v) -> np.float32:
+    v = _c(v, np.float32)
+    out = np.zeros(1, np.float32)
+    _check(lib().oracle_tree_sum_f32(_ptr(v), v.size, _ptr(out)), "tree_sum_f32")
+    return out[0]
+
+
+def tree_sum_bf16(bits) -> int:
+    v = _c(bits, np.uint16)
+    out = np.zeros(1, np.uint16)
+    _check(lib().oracle_tree_sum_bf16(_ptr(v), v.size, _ptr(out)), "tree_sum_bf16")
+    return int(out[0])
+
+
+def sort_by_dest(dest, num_dests: int, src_id=None):
+    """Returns (perm, seg_offsets, inv_perm) as int32 arrays."""
+    dest = _c(dest, np.int32)
+    n = dest.size
+    src = None if src_id is None else _c(src_id, np.int32)
+    perm = np.empty(n, np.int32)
+    seg = np.empty(num_dests + 1, np.int32)
+    inv = np.empty(n, np.int32)
+    _check(lib().oracle_sort_by_dest(_ptr(dest), _ptr(src), n, num_dests, _ptr(perm), _ptr(seg), _ptr(inv)),
+           "sort_by_dest")
+    return perm, seg, inv
+
+
+def _dtype_code(a) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError(f"unsupported source dtype {a.dtype}")
+
+
+def scatter_reduce(out0, src, index, src_id=None, dests=None):
+    """out[d] = out0[d] + T(contributions of d in (src_id, position) order).
+
+    out0: float32 [D, H].  src: float32 or uint16 (bf16 bits) [n, H].
+    dests: optional list of destination ids; then only those rows are returned
+    (shape [len(dests), H]) and out0 is only read at those rows.
+    """
+    out0 = np.asarray(out0, dtype=np.float32)
+    D, H = out0.shape
+    src = np.ascontiguousarray(src)
+    index = _c(index, np.int32)
+    n = index.size
+    assert src.shape == (n, H), (src.shape, n, H)
+    sid = None if src_id is None else _c(src_id, np.int32)
+    if dests is None:
+        out = np.array(out0, dtype=np.float32, copy=True, order="C")
+        dl, nd = None, 0
+    else:
+        dl = _c(dests, np.int32)
+        nd = dl.size
+        out = np.ascontiguousarray(out0[dl], dtype=np.float32)
+    _check(lib().oracle_scatter_reduce(_ptr(out), D, H, _ptr(src), _dtype_code(src), n, _ptr(index),
+                                       _ptr(sid), _ptr(dl), nd), "scatter_reduce")
+    return out
+
+
+def index_add(out0, src, index, dests=None):
+    """torch-style index_add_(0, index, src) in the defined order (source id = row i)."""
+    return scatter_reduce(out0, src, index, None, dests)
+
+
+def combine(rows, row_of, gates, tokens=None):
+    """out[t] = T(fl32(gate*row) over the token's slots, ordered by row index)."""
+    rows = np.ascontiguousarray(rows)
+    R, H = rows.shape
+    row_of = _c(row_of, np.int32)
+    gates = _c(gates, np.float32)
+    T, k = row_of.shape
+    if tokens is None:
+        tl, nt = None, T
+    else:
+        tl = _c(tokens, np.int64)
+        nt = tl.size
+    out = np.empty((nt, H), np.float32)
+    _check(lib().oracle_combine(_ptr(rows), _dtype_code(rows), R, H, _ptr(row_of), _ptr(gates), T, k,
+                                _ptr(tl), nt if tl is not None else 0, _ptr(out)), "combine")
+    return out
+
+
+def splitk_reduce(partials):
+    """partials: float32 [S, ...] -> float32 [...] reduced over the split axis by T."""
+    p = _c(partials, np.float32)
+    S = p.shape[0]
+    count = p.size // S
+    out = np.empty(p.shape[1:], np.float32)
+    _check(lib().oracle_splitk_reduce(_ptr(p), S, count, _ptr(out)), "splitk_reduce")
+    return out
+
+
+def splitk_reference(X, dY):
+    """fp64 (exact, absum) of X^T dY for bf16-bit inputs X [K, M], dY [K, N]."""
+    X = _c(X, np.uint16)
+    dY = _c(dY, np.uint16)
+    K, M = X.shape
+    N = dY.shape[1]
+    exact = np.empty((M, N), np.float64)
+    absum = np.empty((M, N), np.float64)
+    _check(lib().oracle_splitk_reference(_ptr(X), _ptr(dY), K, M, N, _ptr(exact), _ptr(absum)),
+           "splitk_reference")
+    return exact, absum
+
+
+def splitk_partials(X, dY, splits: int):
+    X = _c(X, np.uint16)
+    dY = _c(dY, np.uint16)
+    K, M = X.shape
+    N = dY.shape[1]
+    P = np.empty((splits, M, N), np.float64)
+    _check(lib().oracle_splitk_partials(_ptr(X), _ptr(dY), K, M, N, splits, _ptr(P)), "splitk_partials")
+    return P
+
+
+def splitmix64_mix(z: int) -> int:
+    return int(lib().oracle_splitmix64_mix(ctypes.c_uint64(z & ((1 << 64) - 1))))
+
+
+def fingerprint(data) -> int:
+    """Fingerprint of an array's bytes in logical (C-contiguous) order."""
+    b = np.ascontiguousarray(data)
+    raw = b.view(np.uint8).reshape(-1) if b.size else np.zeros(0, np.uint8)
+    buf = raw if raw.size else np.zeros(1, np.uint8)
+    return int(lib().oracle_fingerprint(_ptr(buf), raw.size))

@@ -1,0 +1,468 @@
+/*
+ * CPU oracle for the ordered fp32 scatter-reduce.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the bench's
+ * CPU-baseline leg load this file.  The product library never links or calls
+ * it, and the two share no code, headers, tables or constants.
+ *
+ * What it computes is the defined result of a deterministic, batch-invariant
+ * reduction of many contributions into shared destinations.  The sources are:
+ *   - a stable order of contributions per destination: sort by
+ *     (destination, source id), as in the MoE backward of the DeepSeek-V4 book
+ *     (ch. 9, section 3.2: sort tokens by (expert_id, original_token_id), then
+ *     merge in sorted order without atomicAdd);
+ *   - per-split private buffers reduced in split-id order (same chapter,
+ *     section 3.3, mHC backward);
+ *   - one fp32 reduction tree, whatever the partitioning (bitwise-determinism
+ *     interview note, "why pay the overhead": every EP size goes through the
+ *     same fp32 reduction tree);
+ *   - the fixed tree's shape: chunks of 8 contributions summed left to right,
+ *     chunk sums combined by a balanced pairwise tree, no fused multiply-add.
+ *
+ * Readings where the pages leave a step open:
+ *   - "balanced pairwise tree" over C chunk sums: split at the largest power
+ *     of two strictly below C, left part first.
+ *   - a left-to-right chunk sum starts from its first element (no +0.0 seed,
+ *     which would turn a lone -0.0 into +0.0).
+ *   - index_add: the destination's old value is added once, last, as the
+ *     left operand: out = old + T(contributions).  Rows with no contribution
+ *     are never written.
+ *   - combine: a token's contributions are ordered by the row index of the
+ *     expert output they come from (ties by slot); each contribution is
+ *     fl32(gate * row), rounded before it is added.
+ *   - split reduce: the same tree over the split ids 0..S-1.
+ *
+ * Arithmetic: IEEE-754 binary32, round to nearest even, no contraction
+ * (build with -ffp-contract=off), no excess precision (FLT_EVAL_METHOD 0,
+ * SSE), subnormals kept (no flush-to-zero).  The split-K reference is fp64.
+ *
+ * Everything here is plain loops; speed is not a goal.
+ */
+#include <float.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#if !defined(FLT_EVAL_METHOD) || FLT_EVAL_METHOD != 0
+#error "the oracle needs float arithmetic evaluated in float"
+#endif
+
+#define ORC_OK 0
+#define ORC_BAD_ARG 1
+#define ORC_INDEX_OUT_OF_RANGE 4
+#define ORC_NO_MEMORY 6
+
+enum { ORC_F32 = 0, ORC_BF16 = 1 };
+
+/* ------------------------------------------------------------------ */
+/* bfloat16 helpers                                                    */
+/* ------------------------------------------------------------------ */
+static float bf16_to_float(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* float -> bfloat16, round to nearest even; NaN stays NaN (quietened). */
+static uint16_t float_to_bf16(float f)
+{
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7F800000u) == 0x7F800000u && (u & 0x007FFFFFu) != 0)
+        return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t lsb = (u >> 16) & 1u;
+    u += 0x7FFFu + lsb;
+    return (uint16_t)(u >> 16);
+}
+
+static float load_elem(const void* base, int dtype, int64_t idx)
+{
+    if (dtype == ORC_BF16)
+        return bf16_to_float(((const uint16_t*)base)[idx]);
+    return ((const float*)base)[idx];
+}
+
+/* ------------------------------------------------------------------ */
+/* The fixed tree T(v_0 .. v_{L-1}), L >= 1                            */
+/* ------------------------------------------------------------------ */
+
+/* Sum of m >= 1 values, left to right, starting from the first. */
+static float chunk_sum(const float* v, int64_t m)
+{
+    float s = v[0];
+    for (int64_t i = 1; i < m; ++i)
+        s = s + v[i];
+    return s;
+}
+
+/* Balanced pairwise tree over c >= 1 chunk sums. */
+static float pair_tree(const float* s, int64_t c)
+{
+    if (c == 1)
+        return s[0];
+    int64_t p = 1;
+    while (p * 2 < c)
+        p *= 2; /* largest power of two strictly less than c */
+    float left = pair_tree(s, p);
+    float right = pair_tree(s + p, c - p);
+    return left + right;
+}
+
+/* T over L >= 1 values.  Returns 0 on success. */
+static int tree_sum(const float* v, int64_t L, float* result)
+{
+    int64_t c = (L + 7) / 8;
+    float* sums = (float*)malloc((size_t)c * sizeof(float));
+    if (!sums)
+        return ORC_NO_MEMORY;
+    for (int64_t j = 0; j < c; ++j) {
+        int64_t m = L - 8 * j < 8 ? L - 8 * j : 8;
+        sums[j] = chunk_sum(v + 8 * j, m);
+    }
+    *result = pair_tree(sums, c);
+    free(sums);
+    return ORC_OK;
+}
+
+int oracle_tree_sum_f32(const float* v, int64_t L, float* result)
+{
+    if (!v || !result || L < 1)
+        return ORC_BAD_ARG;
+    return tree_sum(v, L, result);
+}
+
+/* The same tree in a bfloat16 accumulator: every partial sum is rounded to
+ * bfloat16.  Test-only: it reproduces worked examples stated in bf16.  A bf16
+ * sum is formed as bf16(fl32(a + b)); for the sum of two bf16 values the double
+ * rounding is innocuous since 24 >= 2*8 + 2. */
+static uint16_t bf16_add(uint16_t a, uint16_t b)
+{
+    return float_to_bf16(bf16_to_float(a) + bf16_to_float(b));
+}
+
+static uint16_t pair_tree_bf16(const uint16_t* s, int64_t c)
+{
+    if (c == 1)
+        return s[0];
+    int64_t p = 1;
+    while (p * 2 < c)
+        p *= 2;
+    uint16_t left = pair_tree_bf16(s, p);
+    uint16_t right = pair_tree_bf16(s + p, c - p);
+    return bf16_add(left, right);
+}
+
+int oracle_tree_sum_bf16(const uint16_t* v, int64_t L, uint16_t* result)
+{
+    if (!v || !result || L < 1)
+        return ORC_BAD_ARG;
+    int64_t c = (L + 7) / 8;
+    uint16_t* sums = (uint16_t*)malloc((size_t)c * sizeof(uint16_t));
+    if (!sums)
+        return ORC_NO_MEMORY;
+    for (int64_t j = 0; j < c; ++j) {
+        int64_t m = L - 8 * j < 8 ? L - 8 * j : 8;
+        uint16_t s = v[8 * j];
+        for (int64_t i = 1; i < m; ++i)
+            s = bf16_add(s, v[8 * j + i]);
+        sums[j] = s;
+    }
+    *result = pair_tree_bf16(sums, c);
+    free(sums);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Stable order of contributions: sort by (dest, src_id, position)     */
+/* ------------------------------------------------------------------ */
+typedef struct {
+    int32_t dest;
+    int32_t src;
+    int64_t pos;
+} contrib_key;
+
+static int cmp_contrib(const void* a, const void* b)
+{
+    const contrib_key* x = (const contrib_key*)a;
+    const contrib_key* y = (const contrib_key*)b;
+    if (x->dest != y->dest)
+        return x->dest < y->dest ? -1 : 1;
+    if (x->src != y->src)
+        return x->src < y->src ? -1 : 1;
+    if (x->pos != y->pos)
+        return x->pos < y->pos ? -1 : 1;
+    return 0;
+}
+
+/* perm[r] = input position of the r-th contribution in (dest, src_id) order,
+ * ties by input position; seg_offsets[d] = first r with dest d (length D+1);
+ * inv_perm (optional) is the inverse: inv_perm[perm[r]] = r.
+ * src_id == NULL means src_id[i] = i. */
+int oracle_sort_by_dest(const int32_t* dest, const int32_t* src_id, int64_t n, int32_t num_dests,
+                        int32_t* perm, int32_t* seg_offsets, int32_t* inv_perm)
+{
+    if (n < 0 || num_dests < 1 || (n > 0 && (!dest || !perm)) || !seg_offsets)
+        return ORC_BAD_ARG;
+    for (int64_t i = 0; i < n; ++i)
+        if (dest[i] < 0 || dest[i] >= num_dests)
+            return ORC_INDEX_OUT_OF_RANGE;
+    contrib_key* keys = (contrib_key*)malloc((size_t)(n > 0 ? n : 1) * sizeof(contrib_key));
+    if (!keys)
+        return ORC_NO_MEMORY;
+    for (int64_t i = 0; i < n; ++i) {
+        keys[i].dest = dest[i];
+        keys[i].src = src_id ? src_id[i] : (int32_t)i;
+        keys[i].pos = i;
+    }
+    qsort(keys, (size_t)n, sizeof(contrib_key), cmp_contrib);
+    for (int64_t r = 0; r < n; ++r) {
+        perm[r] = (int32_t)keys[r].pos;
+        if (inv_perm)
+            inv_perm[keys[r].pos] = (int32_t)r;
+    }
+    /* seg_offsets: exclusive prefix sum of the per-destination counts */
+    for (int32_t d = 0; d <= num_dests; ++d)
+        seg_offsets[d] = 0;
+    for (int64_t i = 0; i < n; ++i)
+        seg_offsets[dest[i] + 1] += 1;
+    for (int32_t d = 0; d < num_dests; ++d)
+        seg_offsets[d + 1] += seg_offsets[d];
+    free(keys);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* Scatter-reduce / index_add                                          */
+/* ------------------------------------------------------------------ */
+
+/* For every destination d (or the listed ones), with its contributions taken in
+ * (src_id, position) order:  out[d][h] = out[d][h] + T(src[i_0][h], ...).
+ *
+ * dests == NULL: out is [num_dests][H], updated in place.
+ * dests != NULL: out is [ndest][H] and holds the listed destinations' rows
+ * (initial contents in, result out); other destinations are not computed. */
+int oracle_scatter_reduce(float* out, int32_t num_dests, int64_t H, const void* src, int src_dtype,
+                          int64_t n, const int32_t* index, const int32_t* src_id,
+                          const int32_t* dests, int64_t ndest)
+{
+    if (!out || H < 1 || num_dests < 1 || n < 0 || (n > 0 && (!src || !index)))
+        return ORC_BAD_ARG;
+    if (src_dtype != ORC_F32 && src_dtype != ORC_BF16)
+        return ORC_BAD_ARG;
+    int32_t* perm = (int32_t*)malloc((size_t)(n > 0 ? n : 1) * sizeof(int32_t));
+    int32_t* seg = (int32_t*)malloc((size_t)(num_dests + 1) * sizeof(int32_t));
+    float* vals = (float*)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+    if (!perm || !seg || !vals) {
+        free(perm); free(seg); free(vals);
+        return ORC_NO_MEMORY;
+    }
+    int rc = oracle_sort_by_dest(index, src_id, n, num_dests, perm, seg, NULL);
+    if (rc != ORC_OK) {
+        free(perm); free(seg); free(vals);
+        return rc;
+    }
+    int64_t rows = dests ? ndest : num_dests;
+    for (int64_t q = 0; q < rows; ++q) {
+        int32_t d = dests ? dests[q] : (int32_t)q;
+        if (d < 0 || d >= num_dests) {
+            rc = ORC_INDEX_OUT_OF_RANGE;
+            break;
+        }
+        int64_t lo = seg[d], L = seg[d + 1] - seg[d];
+        if (L == 0)
+            continue; /* untouched row */
+        float* row = out + q * H;
+        for (int64_t h = 0; h < H; ++h) {
+            for (int64_t j = 0; j < L; ++j)
+                vals[j] = load_elem(src, src_dtype, (int64_t)perm[lo + j] * H + h);
+            float t;
+            rc = tree_sum(vals, L, &t);
+            if (rc != ORC_OK)
+                break;
+            row[h] = row[h] + t;
+        }
+        if (rc != ORC_OK)
+            break;
+    }
+    free(perm); free(seg); free(vals);
+    return rc;
+}
+
+/* ------------------------------------------------------------------ */
+/* MoE combine                                                         */
+/* ------------------------------------------------------------------ */
+
+/* out[t][h] = T over the token's k contributions fl32(gate[t][j] * rows[row_of[t][j]][h]),
+ * ordered by row index (ties by slot j).  Written, not accumulated.
+ * tokens == NULL: all T tokens, out is [T][H]; else out is [ntok][H]. */
+int oracle_combine(const void* rows, int rows_dtype, int64_t num_rows, int64_t H,
+                   const int32_t* row_of, const float* gates, int64_t T, int32_t k,
+                   const int64_t* tokens, int64_t ntok, float* out)
+{
+    if (!rows || !row_of || !gates || !out || H < 1 || k < 1 || T < 0 || num_rows < 0)
+        return ORC_BAD_ARG;
+    if (rows_dtype != ORC_F32 && rows_dtype != ORC_BF16)
+        return ORC_BAD_ARG;
+    int32_t* order = (int32_t*)malloc((size_t)k * sizeof(int32_t));
+    float* vals = (float*)malloc((size_t)k * sizeof(float));
+    if (!order || !vals) {
+        free(order); free(vals);
+        return ORC_NO_MEMORY;
+    }
+    int rc = ORC_OK;
+    int64_t count = tokens ? ntok : T;
+    for (int64_t q = 0; q < count && rc == ORC_OK; ++q) {
+        int64_t t = tokens ? tokens[q] : q;
+        if (t < 0 || t >= T) {
+            rc = ORC_INDEX_OUT_OF_RANGE;
+            break;
+        }
+        const int32_t* r = row_of + t * k;
+        const float* g = gates + t * k;
+        for (int32_t j = 0; j < k; ++j) {
+            if (r[j] < 0 || r[j] >= num_rows)
+                rc = ORC_INDEX_OUT_OF_RANGE;
+        }
+        if (rc != ORC_OK)
+            break;
+        /* insertion sort of the slots by (row, slot): stable */
+        for (int32_t j = 0; j < k; ++j)
+            order[j] = j;
+        for (int32_t a = 1; a < k; ++a) {
+            int32_t cur = order[a];
+            int32_t b = a - 1;
+            while (b >= 0 && r[order[b]] > r[cur]) {
+                order[b + 1] = order[b];
+                --b;
+            }
+            order[b + 1] = cur;
+        }
+        for (int64_t h = 0; h < H; ++h) {
+            for (int32_t j = 0; j < k; ++j) {
+                int32_t slot = order[j];
+                float y = load_elem(rows, rows_dtype, (int64_t)r[slot] * H + h);
+                float p = g[slot] * y; /* rounded to float before any add */
+                vals[j] = p;
+            }
+            float s;
+            rc = tree_sum(vals, k, &s);
+            if (rc != ORC_OK)
+                break;
+            out[q * H + h] = s;
+        }
+    }
+    free(order); free(vals);
+    return rc;
+}
+
+/* ------------------------------------------------------------------ */
+/* Split-K                                                             */
+/* ------------------------------------------------------------------ */
+
+/* out[e] = T(partials[0][e], partials[1][e], ..., partials[S-1][e]) in split-id order. */
+int oracle_splitk_reduce(const float* partials, int32_t S, int64_t count, float* out)
+{
+    if (!partials || !out || S < 1 || count < 0)
+        return ORC_BAD_ARG;
+    float* vals = (float*)malloc((size_t)S * sizeof(float));
+    if (!vals)
+        return ORC_NO_MEMORY;
+    int rc = ORC_OK;
+    for (int64_t e = 0; e < count && rc == ORC_OK; ++e) {
+        for (int32_t s = 0; s < S; ++s)
+            vals[s] = partials[(int64_t)s * count + e];
+        rc = tree_sum(vals, S, &out[e]);
+    }
+    free(vals);
+    return rc;
+}
+
+/* Exact reference of dW = X^T dY for bf16 X [K][M], dY [K][N]:
+ * exact[m][n] = sum_t x[t][m]*dy[t][n] and absum[m][n] = sum_t |x[t][m]*dy[t][n]|,
+ * both in fp64 (each bf16 x bf16 product is exact in fp64). */
+int oracle_splitk_reference(const uint16_t* X, const uint16_t* dY, int64_t K, int64_t M, int64_t N,
+                            double* exact, double* absum)
+{
+    if (!X || !dY || !exact || !absum || K < 0 || M < 1 || N < 1)
+        return ORC_BAD_ARG;
+    double* dy = (double*)malloc((size_t)N * sizeof(double));
+    if (!dy)
+        return ORC_NO_MEMORY;
+    for (int64_t i = 0; i < M * N; ++i) {
+        exact[i] = 0.0;
+        absum[i] = 0.0;
+    }
+    for (int64_t t = 0; t < K; ++t) {
+        for (int64_t c = 0; c < N; ++c)
+            dy[c] = (double)bf16_to_float(dY[t * N + c]);
+        for (int64_t m = 0; m < M; ++m) {
+            double x = (double)bf16_to_float(X[t * M + m]);
+            double* e = exact + m * N;
+            double* a = absum + m * N;
+            for (int64_t c = 0; c < N; ++c) {
+                double p = x * dy[c];
+                e[c] += p;
+                a[c] += p < 0 ? -p : p;
+            }
+        }
+    }
+    free(dy);
+    return ORC_OK;
+}
+
+/* fp64 per-split sums: P[s][m][n] = sum over tokens t of split s of x[t][m]*dy[t][n].
+ * Split s covers tokens [s*c, min(K, (s+1)*c)) with c = ceil(K / S). */
+int oracle_splitk_partials(const uint16_t* X, const uint16_t* dY, int64_t K, int64_t M, int64_t N,
+                           int32_t S, double* P)
+{
+    if (!X || !dY || !P || K < 1 || M < 1 || N < 1 || S < 1)
+        return ORC_BAD_ARG;
+    double* scratch = (double*)malloc((size_t)(M * N) * sizeof(double));
+    if (!scratch)
+        return ORC_NO_MEMORY;
+    int64_t c = (K + S - 1) / S;
+    int rc = ORC_OK;
+    for (int32_t s = 0; s < S && rc == ORC_OK; ++s) {
+        int64_t lo = (int64_t)s * c < K ? (int64_t)s * c : K;
+        int64_t hi = lo + c < K ? lo + c : K;
+        rc = oracle_splitk_reference(X + lo * M, dY + lo * N, hi - lo, M, N, P + (int64_t)s * M * N, scratch);
+    }
+    free(scratch);
+    return rc;
+}
+
+/* ------------------------------------------------------------------ */
+/* Fingerprint                                                         */
+/* ------------------------------------------------------------------ */
+
+/* SplitMix64's output finaliser (Steele, Lea and Flood, "Fast splittable
+ * pseudorandom number generators", OOPSLA 2014). */
+uint64_t oracle_splitmix64_mix(uint64_t z)
+{
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ULL;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebULL;
+    return z ^ (z >> 31);
+}
+
+/* h = mix(nbytes) + sum_i mix(w_i XOR mix(i + 1))  (mod 2^64), where w_i is the
+ * i-th little-endian 64-bit word of the bytes in logical order, the last word
+ * zero-padded.  Wrapping addition makes the value independent of the order in
+ * which the terms are added. */
+uint64_t oracle_fingerprint(const void* data, int64_t nbytes)
+{
+    const unsigned char* p = (const unsigned char*)data;
+    uint64_t h = oracle_splitmix64_mix((uint64_t)nbytes);
+    int64_t words = (nbytes + 7) / 8;
+    for (int64_t i = 0; i < words; ++i) {
+        uint64_t w = 0;
+        for (int b = 0; b < 8; ++b) {
+            int64_t at = i * 8 + b;
+            if (at < nbytes)
+                w |= (uint64_t)p[at] << (8 * b);
+        }
+        h += oracle_splitmix64_mix(w ^ oracle_splitmix64_mix((uint64_t)(i + 1)));
+    }
+    return h;
+}
