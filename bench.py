@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Throughput of the ordered fp32 scatter-reduce on one MI355X.
+
+A step is one pass of the hot path over one batch of synthetic input.  For the
+default workload, MoE unpermute/combine (T=16384 tokens, 256 experts, top-8,
+hidden 7168, bf16 expert outputs), a step is:
+  1. dr_sort_by_dest on the routing keys (stable expert-major dispatch order,
+     whose inverse permutation is the row of every (token, slot));
+  2. dr_combine: gather the 8 rows of every token, fp32 products with the
+     gates, the fixed-order sum, one write of the [16384, 7168] fp32 output;
+  3. dr_fingerprint of the output (the byte-wise check of a step).
+Inputs are resident in HBM before timing starts.  The line printed reports
+whole-step throughput in GB/s of algorithmic bytes.  It also reports the
+combine kernel against the HBM roofline (timed live with HIP events on the
+stream it runs on), the overhead against the atomicAdd baseline, and the CPU
+oracle timed on a bounded sample of the same workload.
+
+Other workloads (--workload sparse_attn_dk | embedding_grad | splitk_mhc |
+tiny_moe_combine) print the same kind of line for their own step.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "ordered scatter-reduce HBM GB/s (% of peak); overhead vs atomicAdd path"
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="moe_combine",
+                    choices=["moe_combine", "tiny_moe_combine", "sparse_attn_dk", "embedding_grad", "splitk_mhc"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target duration of the CPU oracle sample")
+    ap.add_argument("--json-out", default=None, help="also append the JSON line to this file")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------------------
+class Timer:
+    """HIP events on the current stream around named phases of each step."""
+
+    def __init__(self, torch, phases):
+        self.torch = torch
+        self.phases = phases
+        self.events = []
+
+    def step(self):
+        evs = [self.torch.cuda.Event(enable_timing=True) for _ in range(len(self.phases) + 1)]
+        self.events.append(evs)
+        return evs
+
+    def mean_ms(self):
+        self.torch.cuda.synchronize()
+        out = {}
+        for i, name in enumerate(self.phases):
+            out[name] = float(np.mean([e[i].elapsed_time(e[i + 1]) for e in self.events]))
+        return out
+
+
+def source_digest(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "bitwise_deterministic_fp32_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str, digest: str):
+    """HBM bytes per launch from a committed rocprofv3 PMC summary, if it was taken
+    on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(f"{kernel}/{workload}")
+    if not rec or rec.get("source_digest") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+def bench_moe(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
+    import oracle
+    import workloads
+    log(f"{name}: generating inputs")
+    inp = workloads.make(name)
+    T, E, k, H = inp.T, inp.E, inp.k, inp.H
+    elem = 2 if inp.rows_dtype == "bf16" else 4
+    keys = torch.from_numpy(inp.expert_ids.reshape(-1).copy()).cuda()
+    if inp.rows_dtype == "bf16":
+        rows = torch.from_numpy(inp.rows.view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        rows = torch.from_numpy(inp.rows).cuda()
+    gates = torch.from_numpy(inp.gates).cuda()
+    n = T * k
+    perm = torch.empty(n, dtype=torch.int32, device="cuda")
+    seg = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    inv = torch.empty(n, dtype=torch.int32, device="cuda")
+    ws_sort = torch.empty(dr.dr_sort_workspace_size(n, E), dtype=torch.uint8, device="cuda")
+    out = torch.empty(T, H, dtype=torch.float32, device="cuda")
+    fp = torch.empty(1, dtype=torch.int64, device="cuda")
+    ws_fp = torch.empty(dr.dr_fingerprint_workspace_size(out.numel() * 4), dtype=torch.uint8, device="cuda")
+    row_of = inv.view(T, k)
+
+    combine_bytes = n * H * elem + n * 4 + n * 4 + T * H * 4
+    sort_bytes = n * 4 * 3 + (E + 1) * 4
+    fp_bytes = T * H * 4
+    step_bytes = combine_bytes + sort_bytes + fp_bytes
+
+    timer = Timer(torch, ["sort", "combine", "fingerprint"])
+
+    def step(evs=None):
+        if evs: evs[0].record()
+        dr.dr_sort_by_dest(keys, E, perm=perm, seg_offsets=seg, inv_perm=inv, ws=ws_sort)
+        if evs: evs[1].record()
+        dr.dr_combine(rows, row_of, gates, out=out)
+        if evs: evs[2].record()
+        dr.dr_fingerprint(out, out=fp, ws=ws_fp)
+        if evs: evs[3].record()
+
+    log(f"{name}: warmup {warmup}")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    fps = set()
+    log(f"{name}: timing {steps} steps")
+    t0 = time.perf_counter()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        step(timer.step())
+    stop.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+    ms_per_step = start.elapsed_time(stop) / steps
+    phases = timer.mean_ms()
+    fps.add(int(fp.item()))
+
+    # atomic baseline: zeroing (scatter_add_ needs a zeroed output) + atomic combine
+    atimer = Timer(torch, ["zero", "combine_atomic"])
+    out_a = torch.empty_like(out)
+
+    def atomic_step(evs=None):
+        if evs: evs[0].record()
+        out_a.zero_()
+        if evs: evs[1].record()
+        dr.dr_combine_atomic(rows, row_of, gates, out=out_a)
+        if evs: evs[2].record()
+
+    for _ in range(warmup):
+        atomic_step()
+    for _ in range(steps):
+        atomic_step(atimer.step())
+    aph = atimer.mean_ms()
+    torch.testing.assert_close(out_a, out, rtol=1e-5, atol=1e-5)
+
+    # the step's output is the same every replay
+    for _ in range(2):
+        step()
+        fps.add(int(fp.item()))
+    assert len(fps) == 1, "combine step output changed between replays"
+
+    comb_ms = phases["combine"]
+    achieved = combine_bytes / (comb_ms * 1e-3) / 1e9
+    digest = source_digest("combine.hip", "internal.h")
+    result = {
+        "ms_per_step": ms_per_step,
+        "value": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "config": {"workload": f"{name}: MoE unpermute/combine T={T} tokens, {E} experts, top-{k}, hidden {H}, "
+                               f"{inp.rows_dtype} expert outputs, fp32 out",
+                   "tokens": T, "experts": E, "top_k": k, "hidden": H,
+                   "step": "dispatch sort + ordered combine + output fingerprint",
+                   "step_algorithmic_bytes": step_bytes},
+        "roofline": {"bound": "hbm", "kernel": "combine_kernel", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("combine_kernel", name, digest),
+                     "algorithmic_bytes_per_launch": combine_bytes, "avg_launch_ms": round(comb_ms, 4)},
+        "phases_ms": {k2: round(v, 4) for k2, v in phases.items()},
+        "overhead_vs_atomic": {
+            "deterministic_combine_ms": round(comb_ms, 4),
+            "atomic_zero_plus_combine_ms": round(aph["zero"] + aph["combine_atomic"], 4),
+            "atomic_combine_only_ms": round(aph["combine_atomic"], 4),
+            "overhead": round(comb_ms / (aph["zero"] + aph["combine_atomic"]) - 1, 4),
+            "overhead_vs_atomic_kernel_only": round(comb_ms / aph["combine_atomic"] - 1, 4),
+        },
+        "wall_ms_per_step": round(wall_ms, 4),
+    }
+    if want_cpu:
+        result["cpu_baseline"] = cpu_baseline_moe(oracle, inp, cpu_seconds)
+    return result
+
+
+def cpu_baseline_moe(oracle, inp, seconds):
+    """The oracle (single-threaded C) timed on a bounded sample of tokens."""
+    _, _, inv = oracle.sort_by_dest(inp.expert_ids.reshape(-1), inp.E)
+    row_of = inv.reshape(inp.T, inp.k)
+    elem = 2 if inp.rows_dtype == "bf16" else 4
+    per_token = inp.k * inp.H * elem + inp.k * 8 + inp.H * 4
+    probe = np.arange(min(16, inp.T))
+    t0 = time.perf_counter()
+    oracle.combine(inp.rows, row_of, inp.gates, tokens=probe)
+    dt = max(time.perf_counter() - t0, 1e-6) / len(probe)
+    count = int(min(inp.T, max(len(probe), seconds / dt)))
+    tokens = np.arange(count)
+    log(f"cpu baseline: oracle combine on {count} tokens (~{count * dt:.1f} s)")
+    t0 = time.perf_counter()
+    oracle.combine(inp.rows, row_of, inp.gates, tokens=tokens)
+    el = time.perf_counter() - t0
+    return {"value": round(per_token * count / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {count} of {inp.T} tokens of the same workload (combine only), {el:.1f} s",
+            "seconds": round(el, 2)}
+
+
+# ---------------------------------------------------------------------------
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import bitwise_deterministic_fp32_amd as dr
+    torch.cuda.set_device(0)
+    dr.dr_set_launch_params(reset=True)
+    name = args.workload
+    if name in ("moe_combine", "tiny_moe_combine"):
+        res = bench_moe(torch, dr, name, args.steps, args.warmup, args.cpu_seconds, not args.no_cpu_baseline)
+    else:
+        import bench_workloads
+        res = bench_workloads.run(torch, dr, name, args.steps, args.warmup, args.cpu_seconds,
+                                  not args.no_cpu_baseline)
+    line = {"metric": METRIC, "value": round(res.pop("value"), 2), "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res.pop("ms_per_step"), 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic (seeded numpy PCG64 draws of the configuration's shapes and distributions)"}
+    line.update(res)
+    text = json.dumps(line)
+    print(text, flush=True)
+    if args.json_out:
+        with open(args.json_out, "a") as f:
+            f.write(text + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,288 @@
+"""Python binding of libdetreduce: argument marshalling only.
+
+Every function here has the name of the C entry point it calls
+(include/detreduce.h).  It checks tensor placement and dtypes, allocates the
+outputs and workspaces it is not given (torch is used for device memory and
+streams only), and passes raw pointers and the current HIP stream to the
+library.  All arithmetic happens in the HIP kernels of libdetreduce.so; there
+is no fallback.  Importing this package fails if the library is not built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+__all__ = [
+    "DetReduceError", "LIB_PATH", "lib", "declared_functions",
+    "dr_status_string", "dr_last_error", "dr_version", "dr_set_launch_params",
+    "dr_sort_workspace_size", "dr_sort_by_dest",
+    "dr_combine", "dr_combine_atomic",
+    "dr_index_add_workspace_size", "dr_index_add", "dr_index_add_atomic",
+    "dr_splitk_gemm_tn", "dr_splitk_gemm_tn_atomic", "dr_splitk_reduce",
+    "dr_fingerprint_workspace_size", "dr_fingerprint", "fingerprint_value",
+    "dr_workspace_status", "dr_read_status",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdetreduce.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "detreduce.h")
+
+DR_F32, DR_BF16 = 0, 1
+_DTYPES = {torch.float32: DR_F32, torch.bfloat16: DR_BF16}
+
+
+class DetReduceError(RuntimeError):
+    def __init__(self, status: int, what: str, detail: str):
+        self.status = status
+        super().__init__(f"{what}: {_status_name(status)}: {detail}")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m bitwise_deterministic_fp32_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "dr_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        "dr_last_error": ([], ctypes.c_char_p),
+        "dr_version": ([], i32),
+        "dr_set_launch_params": ([vp], ctypes.c_int),
+        "dr_sort_workspace_size": ([i64, i32, i32], sz),
+        "dr_sort_by_dest": ([vp, vp, i32, i64, i32, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+        "dr_combine": ([vp, ctypes.c_int, i64, i64, vp, vp, i64, i32, vp, vp, vp], ctypes.c_int),
+        "dr_combine_atomic": ([vp, ctypes.c_int, i64, i64, vp, vp, i64, i32, vp, vp, vp], ctypes.c_int),
+        "dr_index_add_workspace_size": ([i64, i32, i64], sz),
+        "dr_index_add": ([vp, i32, i64, vp, ctypes.c_int, i64, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+        "dr_index_add_atomic": ([vp, i32, i64, vp, ctypes.c_int, i64, vp, vp, vp], ctypes.c_int),
+        "dr_splitk_gemm_tn": ([vp, vp, i64, i64, i64, i32, vp, vp], ctypes.c_int),
+        "dr_splitk_gemm_tn_atomic": ([vp, vp, i64, i64, i64, i32, vp, vp], ctypes.c_int),
+        "dr_splitk_reduce": ([vp, i32, i64, vp, vp], ctypes.c_int),
+        "dr_fingerprint_workspace_size": ([i64], sz),
+        "dr_fingerprint": ([vp, i64, vp, vp, sz, vp], ctypes.c_int),
+        "dr_workspace_status": ([vp, vp], ctypes.c_int),
+        "dr_read_status": ([vp, vp], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    return L
+
+
+lib = _load()
+
+
+def declared_functions() -> list[str]:
+    """Names of the functions that include/detreduce.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dr_[a-z0-9_]+)\s*\(", text)))
+
+
+def _status_name(s: int) -> str:
+    return lib.dr_status_string(s).decode()
+
+
+def dr_status_string(s: int) -> str:
+    return _status_name(s)
+
+
+def dr_last_error() -> str:
+    return lib.dr_last_error().decode()
+
+
+def dr_version() -> int:
+    return int(lib.dr_version())
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise DetReduceError(status, what, dr_last_error())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t: torch.Tensor, name: str, dtypes=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a tensor on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return t
+
+
+class _LaunchParams(ctypes.Structure):
+    _fields_ = [("grid_blocks", ctypes.c_int32), ("tile_chunks_log2", ctypes.c_int32),
+                ("sort_tile_log2", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+def dr_set_launch_params(grid_blocks: int = 0, tile_chunks_log2: int = 0, sort_tile_log2: int = 0,
+                         reset: bool = False) -> None:
+    """Thread-local launch overrides (tests of launch invariance); reset=True restores defaults."""
+    if reset:
+        _check(lib.dr_set_launch_params(None), "dr_set_launch_params")
+        return
+    p = _LaunchParams(grid_blocks, tile_chunks_log2, sort_tile_log2, 0)
+    _check(lib.dr_set_launch_params(ctypes.byref(p)), "dr_set_launch_params")
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------------------
+def dr_sort_workspace_size(n: int, num_dests: int, src_id_bound: int = 0) -> int:
+    return int(lib.dr_sort_workspace_size(n, num_dests, src_id_bound))
+
+
+def dr_sort_by_dest(dest, num_dests: int, src_id=None, src_id_bound: int = 0, *, perm=None, seg_offsets=None,
+                    inv_perm=None, want_inv: bool = True, ws=None, stream=None):
+    """Stable sort by (dest, src_id).  Returns (perm, seg_offsets, inv_perm or None)."""
+    _dev(dest, "dest", (torch.int32,))
+    n = dest.numel()
+    dev = dest.device
+    if src_id is not None:
+        _dev(src_id, "src_id", (torch.int32,))
+    perm = perm if perm is not None else torch.empty(n, dtype=torch.int32, device=dev)
+    seg_offsets = seg_offsets if seg_offsets is not None else torch.empty(num_dests + 1, dtype=torch.int32, device=dev)
+    if inv_perm is None and want_inv:
+        inv_perm = torch.empty(n, dtype=torch.int32, device=dev)
+    need = dr_sort_workspace_size(n, num_dests, src_id_bound if src_id is not None else 0)
+    ws = ws if ws is not None else _workspace(need, dev)
+    _check(lib.dr_sort_by_dest(_p(dest), _p(src_id), src_id_bound, n, num_dests, _p(perm), _p(seg_offsets),
+                               _p(inv_perm), _p(ws), ws.numel(), _stream(stream)), "dr_sort_by_dest")
+    return perm, seg_offsets, inv_perm
+
+
+def _combine_args(rows, row_of, gates):
+    _dev(rows, "rows", tuple(_DTYPES))
+    _dev(row_of, "row_of", (torch.int32,))
+    _dev(gates, "gates", (torch.float32,))
+    if rows.dim() != 2 or row_of.dim() != 2 or gates.shape != row_of.shape:
+        raise ValueError("rows must be [R, H]; row_of and gates [T, k]")
+    return rows.shape[0], rows.shape[1], row_of.shape[0], row_of.shape[1]
+
+
+def dr_combine(rows, row_of, gates, *, out=None, dev_status=None, stream=None):
+    """out[t] = ordered tree over fl32(gate * row) of the token's k rows (written)."""
+    R, H, T, k = _combine_args(rows, row_of, gates)
+    out = out if out is not None else torch.empty(T, H, dtype=torch.float32, device=rows.device)
+    _dev(out, "out", (torch.float32,))
+    _check(lib.dr_combine(_p(rows), _DTYPES[rows.dtype], R, H, _p(row_of), _p(gates), T, k, _p(out),
+                          _p(dev_status), _stream(stream)), "dr_combine")
+    return out
+
+
+def dr_combine_atomic(rows, row_of, gates, *, out, dev_status=None, stream=None):
+    """Nondeterministic baseline: atomically adds each fl32(gate * row) into out (caller zeroes it)."""
+    R, H, T, k = _combine_args(rows, row_of, gates)
+    _dev(out, "out", (torch.float32,))
+    _check(lib.dr_combine_atomic(_p(rows), _DTYPES[rows.dtype], R, H, _p(row_of), _p(gates), T, k, _p(out),
+                                 _p(dev_status), _stream(stream)), "dr_combine_atomic")
+    return out
+
+
+# ---------------------------------------------------------------------------
+def dr_index_add_workspace_size(n: int, num_dests: int, hidden: int) -> int:
+    return int(lib.dr_index_add_workspace_size(n, num_dests, hidden))
+
+
+def dr_index_add(out, src, index, *, perm=None, seg_offsets=None, ws=None, stream=None):
+    """out[d] += ordered tree of src rows i with index[i] == d (in place).  Returns (out, ws)."""
+    _dev(out, "out", (torch.float32,))
+    _dev(src, "src", tuple(_DTYPES))
+    _dev(index, "index", (torch.int32,))
+    D, H = out.shape
+    n = index.numel()
+    if src.shape != (n, H):
+        raise ValueError(f"src must be [{n}, {H}], got {tuple(src.shape)}")
+    ws = ws if ws is not None else _workspace(dr_index_add_workspace_size(n, D, H), out.device)
+    _check(lib.dr_index_add(_p(out), D, H, _p(src), _DTYPES[src.dtype], n, _p(index), _p(perm), _p(seg_offsets),
+                            _p(ws), ws.numel(), _stream(stream)), "dr_index_add")
+    return out, ws
+
+
+def dr_index_add_atomic(out, src, index, *, dev_status=None, stream=None):
+    _dev(out, "out", (torch.float32,))
+    _dev(src, "src", tuple(_DTYPES))
+    _dev(index, "index", (torch.int32,))
+    D, H = out.shape
+    n = index.numel()
+    _check(lib.dr_index_add_atomic(_p(out), D, H, _p(src), _DTYPES[src.dtype], n, _p(index), _p(dev_status),
+                                   _stream(stream)), "dr_index_add_atomic")
+    return out
+
+
+# ---------------------------------------------------------------------------
+def dr_splitk_gemm_tn(X, dY, splits: int, *, partials=None, stream=None):
+    """partials[s] = X_s^T dY_s (bf16 MFMA into fp32), one private buffer per split."""
+    _dev(X, "X", (torch.bfloat16,))
+    _dev(dY, "dY", (torch.bfloat16,))
+    K, M = X.shape
+    N = dY.shape[1]
+    partials = partials if partials is not None else torch.empty(splits, M, N, dtype=torch.float32, device=X.device)
+    _dev(partials, "partials", (torch.float32,))
+    _check(lib.dr_splitk_gemm_tn(_p(X), _p(dY), K, M, N, splits, _p(partials), _stream(stream)), "dr_splitk_gemm_tn")
+    return partials
+
+
+def dr_splitk_gemm_tn_atomic(X, dY, splits: int, *, out, stream=None):
+    _dev(X, "X", (torch.bfloat16,))
+    _dev(dY, "dY", (torch.bfloat16,))
+    _dev(out, "out", (torch.float32,))
+    K, M = X.shape
+    N = dY.shape[1]
+    _check(lib.dr_splitk_gemm_tn_atomic(_p(X), _p(dY), K, M, N, splits, _p(out), _stream(stream)),
+           "dr_splitk_gemm_tn_atomic")
+    return out
+
+
+def dr_splitk_reduce(partials, *, out=None, stream=None):
+    """out = ordered tree over the split axis of partials [S, ...]."""
+    _dev(partials, "partials", (torch.float32,))
+    S = partials.shape[0]
+    count = partials.numel() // S
+    out = out if out is not None else torch.empty(partials.shape[1:], dtype=torch.float32, device=partials.device)
+    _dev(out, "out", (torch.float32,))
+    _check(lib.dr_splitk_reduce(_p(partials), S, count, _p(out), _stream(stream)), "dr_splitk_reduce")
+    return out
+
+
+# ---------------------------------------------------------------------------
+def dr_fingerprint_workspace_size(nbytes: int) -> int:
+    return int(lib.dr_fingerprint_workspace_size(nbytes))
+
+
+def dr_fingerprint(t, *, out=None, ws=None, stream=None):
+    """Device-side 64-bit fingerprint of t's bytes in logical order (an int64 tensor of one element)."""
+    _dev(t, "tensor")
+    nbytes = t.numel() * t.element_size()
+    out = out if out is not None else torch.empty(1, dtype=torch.int64, device=t.device)
+    ws = ws if ws is not None else _workspace(dr_fingerprint_workspace_size(nbytes), t.device)
+    _check(lib.dr_fingerprint(_p(t), nbytes, _p(out), _p(ws), ws.numel(), _stream(stream)), "dr_fingerprint")
+    return out
+
+
+def fingerprint_value(t, stream=None) -> int:
+    """The fingerprint as an unsigned Python int (synchronises)."""
+    return int(dr_fingerprint(t, stream=stream).item()) & ((1 << 64) - 1)
+
+
+def dr_workspace_status(ws, stream=None) -> None:
+    """Raises DetReduceError if the device status word of a sort/index_add workspace is set."""
+    _check(lib.dr_workspace_status(_p(ws), _stream(stream)), "device status")
+
+
+def dr_read_status(dev_status, stream=None) -> None:
+    _check(lib.dr_read_status(_p(dev_status), _stream(stream)), "device status")

@@ -1,0 +1,525 @@
+// C-ABI layer of libdetreduce: argument validation (fail closed, nothing is
+// launched on a bad argument), workspace layout, and the order of kernel
+// launches for each entry point.  See include/detreduce.h for the contract.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+thread_local dr_launch_params g_params = {0, 0, 0, 0};
+
+dr_status fail(dr_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+dr_status ok() {
+    g_err.clear();
+    return DR_OK;
+}
+
+dr_status hip_fail(hipError_t e, const char* what) {
+    return fail(DR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define DR_TRY_HIP(expr, what)                        \
+    do {                                              \
+        hipError_t e_ = (expr);                       \
+        if (e_ != hipSuccess) return hip_fail(e_, what); \
+    } while (0)
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+// Carves a workspace into aligned slices; with base == nullptr it only sizes.
+struct Carver {
+    char* base;
+    size_t off = 0;
+    explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+    template <typename T>
+    T* take(int64_t count) {
+        T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+        off += align_up((size_t)(count > 0 ? count : 0) * sizeof(T));
+        return p;
+    }
+};
+
+int bitwidth(uint32_t x) {
+    int b = 0;
+    while (x) {
+        ++b;
+        x >>= 1;
+    }
+    return b;
+}
+
+struct DigitPass {
+    bool from_src;
+    int shift;
+    int bits;
+};
+
+// LSD passes: source-id digits first (least significant), then destination digits.
+std::vector<DigitPass> sort_passes(int32_t num_dests, bool has_src, int32_t src_bound) {
+    std::vector<DigitPass> passes;
+    auto add = [&](bool from_src, int total_bits) {
+        if (total_bits <= 0) return;
+        const int np = (total_bits + 7) / 8;
+        const int width = (total_bits + np - 1) / np;
+        for (int shift = 0; shift < total_bits; shift += width)
+            passes.push_back({from_src, shift, std::min(width, total_bits - shift)});
+    };
+    if (has_src) add(true, bitwidth((uint32_t)(src_bound - 1)));
+    add(false, bitwidth((uint32_t)(num_dests - 1)));
+    if (passes.empty()) passes.push_back({false, 0, 1});  // one destination: a single stable pass
+    return passes;
+}
+
+struct SortBuffers {
+    int32_t* hist;
+    int32_t* totals;
+    int32_t *dest_a, *dest_b, *val_a, *val_b, *src_a, *src_b;
+    int64_t nblocks;
+};
+
+SortBuffers carve_sort(Carver& c, int64_t n, bool has_src, int tile_log2) {
+    SortBuffers b{};
+    b.nblocks = (n + ((int64_t)1 << tile_log2) - 1) >> tile_log2;
+    b.hist = c.take<int32_t>(256 * b.nblocks);
+    b.totals = c.take<int32_t>(256);
+    b.dest_a = c.take<int32_t>(n);
+    b.dest_b = c.take<int32_t>(n);
+    b.val_a = c.take<int32_t>(n);
+    b.val_b = c.take<int32_t>(n);
+    b.src_a = has_src ? c.take<int32_t>(n) : nullptr;
+    b.src_b = has_src ? c.take<int32_t>(n) : nullptr;
+    return b;
+}
+
+// Launches the stable sort; the status word must already be cleared.
+dr_status run_sort(const int32_t* dest, const int32_t* src_id, int32_t src_bound, int64_t n, int32_t num_dests,
+                   int32_t* perm, int32_t* seg_offsets, int32_t* inv_perm, int32_t* status, const SortBuffers& b,
+                   int tile_log2, hipStream_t s) {
+    const bool has_src = src_id != nullptr;
+    const std::vector<DigitPass> passes = sort_passes(num_dests, has_src, src_bound);
+    int src_passes = 0;
+    for (const DigitPass& p : passes) src_passes += p.from_src;
+    const int32_t* cur_dest = dest;
+    const int32_t* cur_src = src_id;
+    const int32_t* cur_val = nullptr;
+    for (size_t i = 0; i < passes.size(); ++i) {
+        const bool last = i + 1 == passes.size();
+        const bool odd = i & 1;
+        const bool carry_src = has_src && (int)i + 1 < src_passes;
+        dr::SortPass sp{};
+        sp.digit_src = passes[i].from_src ? cur_src : cur_dest;
+        sp.shift = passes[i].shift;
+        sp.bits = passes[i].bits;
+        sp.dest_in = cur_dest;
+        sp.dest_out = odd ? b.dest_b : b.dest_a;
+        sp.src_in = (carry_src || passes[i].from_src) ? cur_src : nullptr;
+        sp.src_out = carry_src ? (odd ? b.src_b : b.src_a) : nullptr;
+        sp.val_in = cur_val;
+        sp.val_out = last ? perm : (odd ? b.val_b : b.val_a);
+        sp.inv_out = last ? inv_perm : nullptr;
+        if (i == 0)
+            DR_TRY_HIP(dr::launch_radix_validate_hist(dest, num_dests, src_id, src_bound, sp, n, tile_log2, b.hist,
+                                                      status, s),
+                       "radix histogram launch");
+        else
+            DR_TRY_HIP(dr::launch_radix_hist(sp, n, tile_log2, b.hist, status, s), "radix histogram launch");
+        DR_TRY_HIP(dr::launch_radix_scan(b.hist, b.nblocks, 1 << sp.bits, b.totals, status, s), "radix scan launch");
+        DR_TRY_HIP(dr::launch_radix_scatter(sp, n, tile_log2, b.hist, b.totals, status, s), "radix scatter launch");
+        cur_dest = sp.dest_out;
+        cur_src = sp.src_out;
+        cur_val = sp.val_out;
+    }
+    DR_TRY_HIP(dr::launch_seg_offsets(cur_dest, n, num_dests, seg_offsets, status, s), "segment offsets launch");
+    return DR_OK;
+}
+
+// Upper bounds of the index_add plan for tiles of tc = 2^m chunks.
+struct PlanBounds {
+    int64_t tiles, multis, pslots;
+};
+PlanBounds plan_bounds(int64_t n, int32_t num_dests, int tc_log2) {
+    const int64_t tc = (int64_t)1 << tc_log2;
+    const int64_t touched = std::min<int64_t>(num_dests, n);
+    PlanBounds b;
+    // sum_d ceil(C_d / tc) <= sum_d (C_d / tc + 1), sum_d C_d <= n/8 + touched
+    b.tiles = touched + (n / 8 + touched + tc - 1) / tc + 1;
+    // a multi-tile segment has more than 8*tc rows
+    b.multis = n / (8 * tc) + 1;
+    // its tile count is below 2*C_d/tc <= L_d/(4 tc) + 2/tc; summed, <= n/(2 tc)
+    b.pslots = n / (2 * tc) + 2;
+    return b;
+}
+
+struct IndexAddBuffers {
+    int32_t* status;
+    int32_t* perm;
+    int32_t* seg;
+    SortBuffers sort;
+    int32_t* block_sums;
+    dr::TileRec* tiles;
+    dr::MultiRec* multis;
+    float* partials;
+};
+
+IndexAddBuffers carve_index_add(Carver& c, int64_t n, int32_t num_dests, int64_t hidden, bool sort_inside,
+                                int tc_log2, int sort_tile_log2) {
+    IndexAddBuffers b{};
+    b.status = c.take<int32_t>(dr::kStatusBytes / sizeof(int32_t));
+    if (sort_inside) {
+        b.perm = c.take<int32_t>(n);
+        b.seg = c.take<int32_t>((int64_t)num_dests + 1);
+        b.sort = carve_sort(c, n, false, sort_tile_log2);
+    }
+    const PlanBounds pb = plan_bounds(n, num_dests, tc_log2);
+    b.block_sums = c.take<int32_t>(3 * dr::plan_blocks(num_dests));
+    b.tiles = c.take<dr::TileRec>(pb.tiles);
+    b.multis = c.take<dr::MultiRec>(pb.multis);
+    b.partials = c.take<float>(pb.pslots * hidden);
+    return b;
+}
+
+int elems16(dr_dtype dt) { return dt == DR_BF16 ? 8 : 4; }
+
+dr_status check_dtype(dr_dtype dt, const char* what) {
+    if (dt != DR_F32 && dt != DR_BF16) return fail(DR_ERR_UNSUPPORTED, "%s: dtype %d is not fp32 or bf16", what, (int)dt);
+    return DR_OK;
+}
+
+dr_status check_rows(const void* p, dr_dtype dt, int64_t hidden, const char* what) {
+    if (hidden < 1) return fail(DR_ERR_INVALID_ARGUMENT, "%s: hidden must be >= 1 (got %lld)", what, (long long)hidden);
+    if (hidden % elems16(dt) != 0)
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: hidden (%lld) must be a multiple of %d for this dtype", what,
+                    (long long)hidden, elems16(dt));
+    if (p && !aligned(p, 16)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: row data must be 16-byte aligned", what);
+    return DR_OK;
+}
+
+constexpr int64_t kMaxN = (int64_t)1 << 31;
+
+}  // namespace
+
+namespace dr {
+
+Launch launch_config() {
+    Launch l;
+    l.grid_blocks = g_params.grid_blocks;
+    l.tile_chunks_log2 = g_params.tile_chunks_log2 ? g_params.tile_chunks_log2 : kDefaultTileChunksLog2;
+    l.sort_tile_log2 = g_params.sort_tile_log2 ? g_params.sort_tile_log2 : kDefaultSortTileLog2;
+    return l;
+}
+
+int device_cu_count() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    const int slot = dev < 64 ? dev : 63;
+    if (cache[slot] <= 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+            cus = 256;
+        cache[slot] = cus;
+    }
+    return cache[slot];
+}
+
+}  // namespace dr
+
+extern "C" {
+
+const char* dr_status_string(dr_status s) {
+    switch (s) {
+        case DR_OK: return "DR_OK";
+        case DR_ERR_INVALID_ARGUMENT: return "DR_ERR_INVALID_ARGUMENT";
+        case DR_ERR_UNSUPPORTED: return "DR_ERR_UNSUPPORTED";
+        case DR_ERR_WORKSPACE_TOO_SMALL: return "DR_ERR_WORKSPACE_TOO_SMALL";
+        case DR_ERR_INDEX_OUT_OF_RANGE: return "DR_ERR_INDEX_OUT_OF_RANGE";
+        case DR_ERR_HIP: return "DR_ERR_HIP";
+        case DR_ERR_BAD_PLAN: return "DR_ERR_BAD_PLAN";
+    }
+    return "DR_ERR_UNKNOWN";
+}
+
+const char* dr_last_error(void) { return g_err.c_str(); }
+
+int32_t dr_version(void) { return 100; }
+
+dr_status dr_set_launch_params(const dr_launch_params* p) {
+    if (!p) {
+        g_params = dr_launch_params{0, 0, 0, 0};
+        return ok();
+    }
+    if (p->grid_blocks < 0 || p->grid_blocks > 65536)
+        return fail(DR_ERR_INVALID_ARGUMENT, "grid_blocks must be 0 or 1..65536");
+    if (p->tile_chunks_log2 != 0 &&
+        (p->tile_chunks_log2 < dr::kMinTileChunksLog2 || p->tile_chunks_log2 > dr::kMaxTileChunksLog2))
+        return fail(DR_ERR_INVALID_ARGUMENT, "tile_chunks_log2 must be 0 or %d..%d", dr::kMinTileChunksLog2,
+                    dr::kMaxTileChunksLog2);
+    if (p->sort_tile_log2 != 0 &&
+        (p->sort_tile_log2 < dr::kMinSortTileLog2 || p->sort_tile_log2 > dr::kMaxSortTileLog2))
+        return fail(DR_ERR_INVALID_ARGUMENT, "sort_tile_log2 must be 0 or %d..%d", dr::kMinSortTileLog2,
+                    dr::kMaxSortTileLog2);
+    if (p->reserved != 0) return fail(DR_ERR_INVALID_ARGUMENT, "reserved must be 0");
+    g_params = *p;
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+size_t dr_sort_workspace_size(int64_t n, int32_t num_dests, int32_t src_id_bound) {
+    (void)num_dests;
+    Carver c(nullptr);
+    c.take<int32_t>(dr::kStatusBytes / sizeof(int32_t));
+    carve_sort(c, n < 0 ? 0 : n, src_id_bound > 0, dr::launch_config().sort_tile_log2);
+    return c.off;
+}
+
+dr_status dr_sort_by_dest(const int32_t* dest, const int32_t* src_id, int32_t src_id_bound, int64_t n,
+                          int32_t num_dests, int32_t* perm, int32_t* seg_offsets, int32_t* inv_perm, void* ws,
+                          size_t ws_bytes, hipStream_t stream) {
+    const char* what = "dr_sort_by_dest";
+    if (n < 0 || n >= kMaxN) return fail(DR_ERR_INVALID_ARGUMENT, "%s: n must be in [0, 2^31)", what);
+    if (num_dests < 1) return fail(DR_ERR_INVALID_ARGUMENT, "%s: num_dests must be >= 1", what);
+    if (src_id && src_id_bound < 1) return fail(DR_ERR_INVALID_ARGUMENT, "%s: src_id_bound must be >= 1", what);
+    if (n > 0 && (!dest || !perm)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: null dest or perm", what);
+    if (!seg_offsets || !ws) return fail(DR_ERR_INVALID_ARGUMENT, "%s: null seg_offsets or workspace", what);
+    if (!aligned(ws, 16)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: workspace must be 16-byte aligned", what);
+    const int tile_log2 = dr::launch_config().sort_tile_log2;
+    Carver c(ws);
+    int32_t* status = c.take<int32_t>(dr::kStatusBytes / sizeof(int32_t));
+    const SortBuffers b = carve_sort(c, n, src_id != nullptr, tile_log2);
+    if (c.off > ws_bytes)
+        return fail(DR_ERR_WORKSPACE_TOO_SMALL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes, c.off);
+    DR_TRY_HIP(dr::launch_fill_status(status, stream), "status reset launch");
+    const dr_status st = run_sort(dest, src_id, src_id_bound, n, num_dests, perm, seg_offsets, inv_perm, status, b,
+                                  tile_log2, stream);
+    return st == DR_OK ? ok() : st;
+}
+
+// ---------------------------------------------------------------------------
+dr_status dr_combine(const void* rows, dr_dtype rows_dtype, int64_t num_rows, int64_t hidden,
+                     const int32_t* row_of, const float* gates, int64_t T, int32_t k, float* out,
+                     int32_t* dev_status, hipStream_t stream) {
+    const char* what = "dr_combine";
+    dr_status st = check_dtype(rows_dtype, what);
+    if (st != DR_OK) return st;
+    if ((st = check_rows(rows, rows_dtype, hidden, what)) != DR_OK) return st;
+    if (!aligned(out, 16)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: out must be 16-byte aligned", what);
+    if (T < 0 || num_rows < 0 || num_rows >= kMaxN) return fail(DR_ERR_INVALID_ARGUMENT, "%s: bad T or num_rows", what);
+    if (k < 1) return fail(DR_ERR_INVALID_ARGUMENT, "%s: k must be >= 1", what);
+    if (k > 64) return fail(DR_ERR_UNSUPPORTED, "%s: k = %d > 64 is not supported", what, k);
+    if (T > 0 && (!rows || !row_of || !gates || !out)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: null pointer", what);
+    if (T > 0 && (!aligned(row_of, 4) || !aligned(gates, 4)))
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: row_of/gates must be 4-byte aligned", what);
+    if (dev_status && !aligned(dev_status, 4)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: misaligned dev_status", what);
+    if (T * ((hidden / elems16(rows_dtype) + 63) / 64) >= ((int64_t)1 << 32))
+        return fail(DR_ERR_UNSUPPORTED, "%s: T * column slices must be below 2^32", what);
+    DR_TRY_HIP(dr::launch_combine(rows, rows_dtype, num_rows, hidden, row_of, gates, T, k, out, dev_status, false,
+                                  stream),
+               "combine launch");
+    return ok();
+}
+
+dr_status dr_combine_atomic(const void* rows, dr_dtype rows_dtype, int64_t num_rows, int64_t hidden,
+                            const int32_t* row_of, const float* gates, int64_t T, int32_t k, float* out,
+                            int32_t* dev_status, hipStream_t stream) {
+    const char* what = "dr_combine_atomic";
+    dr_status st = check_dtype(rows_dtype, what);
+    if (st != DR_OK) return st;
+    if ((st = check_rows(rows, rows_dtype, hidden, what)) != DR_OK) return st;
+    if (!aligned(out, 16)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: out must be 16-byte aligned", what);
+    if (T < 0 || num_rows < 0 || num_rows >= kMaxN) return fail(DR_ERR_INVALID_ARGUMENT, "%s: bad T or num_rows", what);
+    if (k < 1 || k > 64) return fail(DR_ERR_UNSUPPORTED, "%s: k must be in [1, 64]", what);
+    if (T > 0 && (!rows || !row_of || !gates || !out)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: null pointer", what);
+    if (T * k * ((hidden / elems16(rows_dtype) + 63) / 64) >= ((int64_t)1 << 32))
+        return fail(DR_ERR_UNSUPPORTED, "%s: T * k * column slices must be below 2^32", what);
+    DR_TRY_HIP(dr::launch_combine(rows, rows_dtype, num_rows, hidden, row_of, gates, T, k, out, dev_status, true,
+                                  stream),
+               "combine_atomic launch");
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+size_t dr_index_add_workspace_size(int64_t n, int32_t num_dests, int64_t hidden) {
+    const dr::Launch lc = dr::launch_config();
+    Carver c(nullptr);
+    carve_index_add(c, n < 0 ? 0 : n, num_dests < 1 ? 1 : num_dests, hidden < 1 ? 1 : hidden, true,
+                    lc.tile_chunks_log2, lc.sort_tile_log2);
+    return c.off;
+}
+
+dr_status dr_index_add(float* out, int32_t num_dests, int64_t hidden, const void* src, dr_dtype src_dtype, int64_t n,
+                       const int32_t* index, const int32_t* perm, const int32_t* seg_offsets, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+    const char* what = "dr_index_add";
+    dr_status st = check_dtype(src_dtype, what);
+    if (st != DR_OK) return st;
+    if ((st = check_rows(src, src_dtype, hidden, what)) != DR_OK) return st;
+    if (!out || !aligned(out, 16)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: out must be non-null and 16-byte aligned", what);
+    if (num_dests < 1) return fail(DR_ERR_INVALID_ARGUMENT, "%s: num_dests must be >= 1", what);
+    if (n < 0 || n >= kMaxN) return fail(DR_ERR_INVALID_ARGUMENT, "%s: n must be in [0, 2^31)", what);
+    if (n > 0 && (!src || !index)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: null src or index", what);
+    if ((perm == nullptr) != (seg_offsets == nullptr))
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: perm and seg_offsets must both be given or both be NULL", what);
+    if (!ws || !aligned(ws, 16)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: workspace must be non-null, 16-byte aligned", what);
+    const dr::Launch lc = dr::launch_config();
+    const bool sort_inside = perm == nullptr;
+    {
+        // the reduce kernels index (tile, column slice) work items with 32 bits
+        const PlanBounds pb = plan_bounds(n, num_dests, lc.tile_chunks_log2);
+        const int64_t slices = (hidden / 4 + 15) / 16;  // upper bound over both dtypes and group sizes
+        if (pb.tiles * slices >= ((int64_t)1 << 32))
+            return fail(DR_ERR_UNSUPPORTED, "%s: n and hidden too large for one call", what);
+    }
+    Carver c(ws);
+    const IndexAddBuffers b = carve_index_add(c, n, num_dests, hidden, sort_inside, lc.tile_chunks_log2,
+                                              lc.sort_tile_log2);
+    if (c.off > ws_bytes)
+        return fail(DR_ERR_WORKSPACE_TOO_SMALL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes, c.off);
+    DR_TRY_HIP(dr::launch_fill_status(b.status, stream), "status reset launch");
+    const int32_t* p = perm;
+    const int32_t* seg = seg_offsets;
+    if (sort_inside) {
+        st = run_sort(index, nullptr, 0, n, num_dests, b.perm, b.seg, nullptr, b.status, b.sort, lc.sort_tile_log2,
+                      stream);
+        if (st != DR_OK) return st;
+        p = b.perm;
+        seg = b.seg;
+    } else {
+        DR_TRY_HIP(dr::launch_plan_validate(perm, seg_offsets, index, n, num_dests, b.status, stream),
+                   "plan validation launch");
+    }
+    DR_TRY_HIP(dr::launch_plan_count(seg, num_dests, n, lc.tile_chunks_log2, b.block_sums, b.status, stream),
+               "plan count launch");
+    DR_TRY_HIP(dr::launch_plan_write(seg, num_dests, lc.tile_chunks_log2, b.block_sums, b.tiles, b.multis, b.status,
+                                     stream),
+               "plan write launch");
+    DR_TRY_HIP(dr::launch_segreduce(out, hidden, src, src_dtype, n, p, seg, b.tiles, b.partials, lc.tile_chunks_log2,
+                                    b.status, stream),
+               "segmented reduce launch");
+    DR_TRY_HIP(dr::launch_tilecombine(out, hidden, b.partials, b.multis, b.status, stream), "tile combine launch");
+    return ok();
+}
+
+dr_status dr_index_add_atomic(float* out, int32_t num_dests, int64_t hidden, const void* src, dr_dtype src_dtype,
+                              int64_t n, const int32_t* index, int32_t* dev_status, hipStream_t stream) {
+    const char* what = "dr_index_add_atomic";
+    dr_status st = check_dtype(src_dtype, what);
+    if (st != DR_OK) return st;
+    if ((st = check_rows(src, src_dtype, hidden, what)) != DR_OK) return st;
+    if (!out || !aligned(out, 16)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: out must be non-null and 16-byte aligned", what);
+    if (num_dests < 1 || n < 0 || n >= kMaxN) return fail(DR_ERR_INVALID_ARGUMENT, "%s: bad num_dests or n", what);
+    if (n > 0 && (!src || !index)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: null src or index", what);
+    if (n * (hidden / elems16(src_dtype)) >= ((int64_t)1 << 32))
+        return fail(DR_ERR_UNSUPPORTED, "%s: n * hidden too large for one call", what);
+    DR_TRY_HIP(dr::launch_index_add_atomic(out, num_dests, hidden, src, src_dtype, n, index, dev_status, stream),
+               "index_add_atomic launch");
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+static dr_status check_splitk(const void* X, const void* dY, int64_t K, int64_t M, int64_t N, int32_t splits,
+                              const void* out, const char* what) {
+    if (!X || !dY || !out) return fail(DR_ERR_INVALID_ARGUMENT, "%s: null pointer", what);
+    if (K < 1 || M < 1 || N < 1) return fail(DR_ERR_INVALID_ARGUMENT, "%s: K, M, N must be >= 1", what);
+    if (splits < 1 || splits > 65535) return fail(DR_ERR_INVALID_ARGUMENT, "%s: splits must be in [1, 65535]", what);
+    const int64_t kc = (K + splits - 1) / splits;
+    if ((int64_t)(splits - 1) * kc >= K)
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: %d splits of %lld tokens leave an empty split (K = %lld)", what, splits,
+                    (long long)kc, (long long)K);
+    if (!aligned(X, 16) || !aligned(dY, 2) || !aligned(out, 4))
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: X must be 16-byte aligned", what);
+    if ((M + 63) / 64 > 0x7FFFFFFF || (N + 31) / 32 > 65535)
+        return fail(DR_ERR_UNSUPPORTED, "%s: M or N too large for one launch", what);
+    return DR_OK;
+}
+
+dr_status dr_splitk_gemm_tn(const void* X, const void* dY, int64_t K, int64_t M, int64_t N, int32_t splits,
+                            float* partials, hipStream_t stream) {
+    const dr_status st = check_splitk(X, dY, K, M, N, splits, partials, "dr_splitk_gemm_tn");
+    if (st != DR_OK) return st;
+    DR_TRY_HIP(dr::launch_splitk_gemm(static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(dY), K, M, N,
+                                      splits, partials, false, stream),
+               "split-K GEMM launch");
+    return ok();
+}
+
+dr_status dr_splitk_gemm_tn_atomic(const void* X, const void* dY, int64_t K, int64_t M, int64_t N, int32_t splits,
+                                   float* out, hipStream_t stream) {
+    const dr_status st = check_splitk(X, dY, K, M, N, splits, out, "dr_splitk_gemm_tn_atomic");
+    if (st != DR_OK) return st;
+    DR_TRY_HIP(dr::launch_splitk_gemm(static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(dY), K, M, N,
+                                      splits, out, true, stream),
+               "split-K atomic GEMM launch");
+    return ok();
+}
+
+dr_status dr_splitk_reduce(const float* partials, int32_t splits, int64_t count, float* out, hipStream_t stream) {
+    const char* what = "dr_splitk_reduce";
+    if (splits < 1) return fail(DR_ERR_INVALID_ARGUMENT, "%s: splits must be >= 1", what);
+    if (count < 0) return fail(DR_ERR_INVALID_ARGUMENT, "%s: count must be >= 0", what);
+    if (count > 0 && (!partials || !out)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: null pointer", what);
+    if (count > 0 && (!aligned(partials, 16) || !aligned(out, 16)))
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: partials and out must be 16-byte aligned", what);
+    if (splits >= (1 << 27)) return fail(DR_ERR_UNSUPPORTED, "%s: too many splits", what);
+    DR_TRY_HIP(dr::launch_splitk_reduce(partials, splits, count, out, stream), "split reduce launch");
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+size_t dr_fingerprint_workspace_size(int64_t nbytes) {
+    (void)nbytes;
+    return dr::kStatusBytes + 1024 * sizeof(uint64_t);
+}
+
+dr_status dr_fingerprint(const void* data, int64_t nbytes, uint64_t* out_hash, void* ws, size_t ws_bytes,
+                         hipStream_t stream) {
+    const char* what = "dr_fingerprint";
+    if (nbytes < 0) return fail(DR_ERR_INVALID_ARGUMENT, "%s: nbytes must be >= 0", what);
+    if (nbytes > 0 && (!data || !aligned(data, 8)))
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: data must be non-null and 8-byte aligned", what);
+    if (!out_hash || !aligned(out_hash, 8)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: bad out_hash", what);
+    if (!ws || !aligned(ws, 16)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: bad workspace", what);
+    if (ws_bytes < dr_fingerprint_workspace_size(nbytes))
+        return fail(DR_ERR_WORKSPACE_TOO_SMALL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes,
+                    dr_fingerprint_workspace_size(nbytes));
+    uint64_t* partials = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + dr::kStatusBytes);
+    DR_TRY_HIP(dr::launch_fingerprint(data, nbytes, out_hash, partials, stream), "fingerprint launch");
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+dr_status dr_read_status(const int32_t* dev_status, hipStream_t stream) {
+    if (!dev_status) return fail(DR_ERR_INVALID_ARGUMENT, "dr_read_status: null pointer");
+    int32_t v = 0;
+    DR_TRY_HIP(hipMemcpyAsync(&v, dev_status, sizeof v, hipMemcpyDeviceToHost, stream), "status copy");
+    DR_TRY_HIP(hipStreamSynchronize(stream), "stream synchronize");
+    if (v == 0) return ok();
+    if (v & dr::kStatusPlan) return fail(DR_ERR_BAD_PLAN, "device reported an inconsistent plan (status word %d)", v);
+    return fail(DR_ERR_INDEX_OUT_OF_RANGE, "device reported an index out of range (status word %d)", v);
+}
+
+dr_status dr_workspace_status(const void* ws, hipStream_t stream) {
+    if (!ws) return fail(DR_ERR_INVALID_ARGUMENT, "dr_workspace_status: null workspace");
+    return dr_read_status(static_cast<const int32_t*>(ws), stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,243 @@
+// MoE token combine (unpermute) in the defined order, and its atomicAdd
+// baseline.
+//
+// out[t] = T over the token's k contributions fl32(gate * row), taken in
+// ascending row order.  With the expert-major layout that the dispatch sort
+// produces, that is expert-id order.  It is the same for every expert-parallel
+// size, since the order key is the row (expert), not the rank that computed
+// it.  This is the sorted-order merge of the DeepSeek-V4 MoE backward (ch. 9,
+// section 3.2) and the unpermute row of the Megatron-LM op catalog
+// (determinism reference, section 3.1).
+//
+// One wavefront owns one token and a slice of 64 x 16 bytes of its columns.
+// The k slots are ranked by row id with wave-uniform data.  Then each lane
+// issues all k row loads of the first chunk (up to 8 x 16 B in flight) and
+// sums the products left to right.  The output is written exactly once; the
+// same data never passes through an atomic, and no memset is needed.
+#include "internal.h"
+
+namespace dr {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWavesPerBlock = kThreads / 64;
+
+__device__ __forceinline__ int32_t uniform_lane(int32_t v, int lane) {
+    return __builtin_amdgcn_readlane(v, lane);
+}
+
+template <dr_dtype DT, int KMAX>
+__global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restrict__ rows, int64_t num_rows, int64_t H,
+                                                           const int32_t* __restrict__ row_of,
+                                                           const float* __restrict__ gates, int64_t T, int k,
+                                                           float* __restrict__ out, int32_t* dev_status,
+                                                           int64_t slices) {
+    constexpr int E = Vec<DT>::kElems;
+    constexpr int kElemBytes = DT == DR_BF16 ? 2 : 4;
+    const int lane = threadIdx.x & 63;
+    // the host keeps T * slices below 2^32
+    const uint32_t wave = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    const uint32_t t32 = wave / (uint32_t)slices;
+    if (t32 >= T) return;  // whole wavefront
+    const int64_t t = t32;
+    const uint32_t slice = wave - t32 * (uint32_t)slices;
+    const int64_t pieces = H / E;
+    const int64_t piece = (int64_t)slice * 64 + lane;
+    const bool active = piece < pieces;
+    const int64_t lane_off = (active ? piece : 0) * 16;  // idle lanes read a valid piece
+    float* orow = out + t * H + piece * E;
+
+    int32_t rid = INT32_MAX;
+    float g = 0.f;
+    if (lane < k) {
+        rid = row_of[t * k + lane];
+        g = gates[t * k + lane];
+    }
+    const bool bad = lane < k && (rid < 0 || rid >= num_rows);
+    if (__ballot(bad) != 0) {
+        // fail closed: never read outside rows; the token's output is poisoned
+        if (active) {
+            float nan[E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) nan[e] = __uint_as_float(0x7FC00000u);
+#pragma unroll
+            for (int e = 0; e < E; e += 4)
+                store16(orow + e, u32x4{__float_as_uint(nan[e]), __float_as_uint(nan[e + 1]),
+                                        __float_as_uint(nan[e + 2]), __float_as_uint(nan[e + 3])});
+        }
+        if (dev_status && lane == 0 && slice == 0) atomicOr(dev_status, kStatusIndex);
+        return;
+    }
+    const char* rb = reinterpret_cast<const char*>(rows);
+    const int64_t row_bytes = H * kElemBytes;
+
+
+    // rank of each slot by (row, slot)
+    int rank = 0;
+    for (int i = 0; i < k; ++i) {
+        const int32_t ri = __shfl(rid, i, 64);
+        rank += (ri < rid) || (ri == rid && i < lane);
+    }
+    if (lane >= k) rank = 64 + lane;  // never selected
+
+    float res[E];
+    if (KMAX <= 8) {
+        // one chunk: left to right over the sorted slots
+        // slots past k reload the last slot's row (a cache hit) so that all
+        // loads issue together; they are not added
+        u32x4 raw[8];
+        float gq[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const uint64_t sel = __ballot(rank == min(q, k - 1));
+            const int src_lane = __builtin_ctzll(sel);
+            const int32_t r = uniform_lane(rid, src_lane);
+            gq[q] = __int_as_float(uniform_lane(__float_as_int(g), src_lane));
+            raw[q] = load16_stream(rb + (int64_t)r * row_bytes + lane_off);
+        }
+        float y[E];
+        Vec<DT>::widen(raw[0], y);
+#pragma unroll
+        for (int e = 0; e < E; ++e) res[e] = gq[0] * y[e];
+#pragma unroll
+        for (int q = 1; q < 8; ++q) {
+            Vec<DT>::widen(raw[q], y);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float p = gq[q] * y[e];  // rounded product, then the add
+                const float a = res[e] + p;
+                res[e] = q < k ? a : res[e];
+            }
+        }
+    } else {
+        // up to 8 chunks of 8; chunk sums padded with -0.0 and paired by
+        // stride doubling, which is the tree T for any chunk count <= 8
+        float cs[8][E];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) cs[c][e] = neg_zero();
+        }
+        const int nchunks = (k + 7) >> 3;
+        for (int c = 0; c < nchunks; ++c) {
+            const int m = min(8, k - 8 * c);
+            u32x4 raw[8];
+            float gq[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint64_t sel = __ballot(rank == 8 * c + min(j, m - 1));
+                const int src_lane = __builtin_ctzll(sel);
+                const int32_t r = uniform_lane(rid, src_lane);
+                gq[j] = __int_as_float(uniform_lane(__float_as_int(g), src_lane));
+                raw[j] = load16_stream(rb + (int64_t)r * row_bytes + lane_off);
+            }
+            float s[E], y[E];
+            Vec<DT>::widen(raw[0], y);
+#pragma unroll
+            for (int e = 0; e < E; ++e) s[e] = gq[0] * y[e];
+#pragma unroll
+            for (int j = 1; j < 8; ++j) {
+                Vec<DT>::widen(raw[j], y);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float p = gq[j] * y[e];
+                    const float a = s[e] + p;
+                    s[e] = j < m ? a : s[e];
+                }
+            }
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc) {
+                if (cc == c) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) cs[cc][e] = s[e];
+                }
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const float a = cs[0][e] + cs[1][e], b = cs[2][e] + cs[3][e];
+            const float c2 = cs[4][e] + cs[5][e], d = cs[6][e] + cs[7][e];
+            const float ab = a + b, cd = c2 + d;
+            res[e] = ab + cd;
+        }
+    }
+    if (active) {
+#pragma unroll
+        for (int e = 0; e < E; e += 4)
+            store16_stream(orow + e, u32x4{__float_as_uint(res[e]), __float_as_uint(res[e + 1]),
+                                           __float_as_uint(res[e + 2]), __float_as_uint(res[e + 3])});
+    }
+}
+
+// The baseline: one wavefront per (token, slot, column slice), so the k
+// contributions of an output element come from k different wavefronts and are
+// added by hardware fp32 atomics in whatever order they arrive (the
+// scatter_add_ pattern over permuted rows).
+template <dr_dtype DT>
+__global__ __launch_bounds__(kThreads) void combine_atomic_kernel(const void* __restrict__ rows, int64_t num_rows,
+                                                                  int64_t H, const int32_t* __restrict__ row_of,
+                                                                  const float* __restrict__ gates, int64_t T, int k,
+                                                                  float* __restrict__ out, int32_t* dev_status,
+                                                                  int64_t slices) {
+    constexpr int E = Vec<DT>::kElems;
+    constexpr int kElemBytes = DT == DR_BF16 ? 2 : 4;
+    const int lane = threadIdx.x & 63;
+    // the host keeps T * k * slices below 2^32
+    const uint32_t wave = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    const uint32_t a = wave / (uint32_t)slices;  // assignment index t*k + j
+    if (a >= (uint64_t)T * k) return;
+    const uint32_t slice = wave - a * (uint32_t)slices;
+    const int64_t t = a / (uint32_t)k;
+    const int64_t piece = (int64_t)slice * 64 + lane;
+    if (piece >= H / E) return;
+    const int32_t r = row_of[a];
+    if (r < 0 || r >= num_rows) {
+        if (dev_status && lane == 0 && slice == 0) atomicOr(dev_status, kStatusIndex);
+        return;
+    }
+    const float g = gates[a];
+    float y[E];
+    Vec<DT>::widen(load16(reinterpret_cast<const char*>(rows) + (int64_t)r * H * kElemBytes + piece * 16), y);
+    float* o = out + t * H + piece * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const float p = g * y[e];
+        unsafeAtomicAdd(o + e, p);
+    }
+}
+
+template <dr_dtype DT>
+hipError_t launch_dt(const void* rows, int64_t num_rows, int64_t H, const int32_t* row_of, const float* gates,
+                     int64_t T, int32_t k, float* out, int32_t* dev_status, bool atomic, hipStream_t s) {
+    constexpr int E = Vec<DT>::kElems;
+    const int64_t pieces = H / E;
+    const int64_t slices = (pieces + 63) / 64;
+    if (atomic) {
+        const int64_t waves = T * k * slices;
+        const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
+        hipLaunchKernelGGL(combine_atomic_kernel<DT>, grid, dim3(kThreads), 0, s, rows, num_rows, H, row_of, gates, T,
+                           k, out, dev_status, slices);
+        return hipGetLastError();
+    }
+    const int64_t waves = T * slices;
+    const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
+    if (k <= 8)
+        hipLaunchKernelGGL((combine_kernel<DT, 8>), grid, dim3(kThreads), 0, s, rows, num_rows, H, row_of,
+                           gates, T, k, out, dev_status, slices);
+    else
+        hipLaunchKernelGGL((combine_kernel<DT, 64>), grid, dim3(kThreads), 0, s, rows, num_rows, H, row_of,
+                           gates, T, k, out, dev_status, slices);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void* rows, dr_dtype dt, int64_t num_rows, int64_t hidden, const int32_t* row_of,
+                          const float* gates, int64_t T, int32_t k, float* out, int32_t* dev_status, bool atomic,
+                          hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    if (dt == DR_BF16) return launch_dt<DR_BF16>(rows, num_rows, hidden, row_of, gates, T, k, out, dev_status, atomic, s);
+    return launch_dt<DR_F32>(rows, num_rows, hidden, row_of, gates, T, k, out, dev_status, atomic, s);
+}
+
+}  // namespace dr

@@ -1,0 +1,104 @@
+// Byte fingerprint of a tensor: h = mix(nbytes) + sum_i mix(w_i ^ mix(i + 1))
+// mod 2^64, where w_i are the little-endian 64-bit words of the bytes (the last
+// one zero-padded) and mix is SplitMix64's finaliser (Steele, Lea and Flood,
+// OOPSLA 2014).  Runs are compared byte for byte through such fingerprints
+// rather than through printed values (bitwise-determinism interview note, "how
+// to verify").  Integer addition is associative, so the two-stage reduction
+// below gives the same value for any grid.
+#include "internal.h"
+
+namespace dr {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxBlocks = 1024;
+
+__device__ __forceinline__ uint64_t mix64(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    return z ^ (z >> 31);
+}
+
+__device__ __forceinline__ uint64_t term(uint64_t w, int64_t i) { return mix64(w ^ mix64((uint64_t)i + 1)); }
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int off) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ uint64_t block_sum_u64(uint64_t v, uint64_t* smem) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += shfl_xor_u64(v, off);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) smem[w] = v;
+    __syncthreads();
+    uint64_t s = 0;
+    if (threadIdx.x == 0)
+        for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += smem[i];
+    return s;
+}
+
+__global__ __launch_bounds__(kThreads) void fp_partial_kernel(const unsigned char* __restrict__ data, int64_t nbytes,
+                                                              uint64_t* __restrict__ partials) {
+    __shared__ uint64_t smem[kThreads / 64];
+    const int64_t full = nbytes >> 3;        // complete 8-byte words
+    const int64_t words = (nbytes + 7) >> 3;
+    const int64_t pairs = full >> 1;          // 16-byte loads
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    uint64_t acc = 0;
+    const u32x4* d16 = reinterpret_cast<const u32x4*>(data);
+    const bool aligned16 = (reinterpret_cast<uintptr_t>(data) & 15) == 0;
+    if (aligned16) {
+        for (int64_t p = (int64_t)blockIdx.x * kThreads + threadIdx.x; p < pairs; p += stride) {
+            const u32x4 v = __builtin_nontemporal_load(d16 + p);
+            acc += term(((uint64_t)v.y << 32) | v.x, 2 * p);
+            acc += term(((uint64_t)v.w << 32) | v.z, 2 * p + 1);
+        }
+    }
+    const int64_t first_single = aligned16 ? 2 * pairs : 0;
+    const uint64_t* d8 = reinterpret_cast<const uint64_t*>(data);
+    for (int64_t i = first_single + (int64_t)blockIdx.x * kThreads + threadIdx.x; i < words; i += stride) {
+        uint64_t w = 0;
+        if (i < full) {
+            w = d8[i];
+        } else {
+            for (int64_t b = 0; b < nbytes - 8 * i; ++b) w |= (uint64_t)data[8 * i + b] << (8 * b);
+        }
+        acc += term(w, i);
+    }
+    const uint64_t s = block_sum_u64(acc, smem);
+    if (threadIdx.x == 0) partials[blockIdx.x] = s;
+}
+
+__global__ __launch_bounds__(kThreads) void fp_final_kernel(const uint64_t* __restrict__ partials, int nblocks,
+                                                            int64_t nbytes, uint64_t* __restrict__ out) {
+    __shared__ uint64_t smem[kThreads / 64];
+    uint64_t acc = 0;
+    for (int i = threadIdx.x; i < nblocks; i += kThreads) acc += partials[i];
+    const uint64_t s = block_sum_u64(acc, smem);
+    if (threadIdx.x == 0) *out = s + mix64((uint64_t)nbytes);
+}
+
+}  // namespace
+
+int64_t fingerprint_blocks(int64_t nbytes) {
+    const Launch lc = launch_config();
+    int64_t b = lc.grid_blocks > 0 ? lc.grid_blocks : (nbytes / 16 + kThreads * 4 - 1) / (kThreads * 4);
+    if (b < 1) b = 1;
+    if (b > kMaxBlocks) b = kMaxBlocks;
+    return b;
+}
+
+hipError_t launch_fingerprint(const void* data, int64_t nbytes, uint64_t* out, uint64_t* block_partials,
+                              hipStream_t s) {
+    const int64_t nb = fingerprint_blocks(nbytes);
+    hipLaunchKernelGGL(fp_partial_kernel, dim3((unsigned)nb), dim3(kThreads), 0, s,
+                       reinterpret_cast<const unsigned char*>(data), nbytes, block_partials);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(fp_final_kernel, dim3(1), dim3(kThreads), 0, s, block_partials, (int)nb, nbytes, out);
+    return hipGetLastError();
+}
+
+}  // namespace dr

@@ -1,0 +1,469 @@
+// index_add in the defined order: for each destination d, the rows of its
+// contributions (in source order, from the sort) reduced by the fixed tree T,
+// then out[d] = out[d] + T.
+//
+// The pages accumulate the many writers of a key row without atomics: the
+// DeepSeek-V4 sparse-attention backward keeps per-SM partial key gradients and
+// adds them in SM-id order (ch. 9, section 3.1).  That order depends on the
+// number of SMs and needs a key-buffer slice per SM.  Here the partition is a
+// property of the data instead: each destination's ordered contributions are
+// cut into tiles of 2^m chunks of 8 rows, aligned at the segment start.  The
+// tree splits only at aligned powers of two, so a tile's subtree sum is a
+// node of the destination's tree whatever m is, and any grid, tile size or
+// schedule gives the same bits.
+//
+//   plan_count / plan_write: tiles per destination, prefix sums, tile records.
+//   segreduce:   one lane group per (tile, 16-byte column slice).  It streams
+//                the tile's chunks (8 row loads in flight per lane), sums each
+//                chunk left to right, and merges chunk sums on a binary counter.
+//                A destination with one tile is updated in place; the tiles of
+//                a longer one write private partial rows.
+//   tilecombine: merges a destination's partial rows by the same counter, in
+//                tile order, then updates the destination row.
+#include "internal.h"
+
+namespace dr {
+namespace {
+
+constexpr int kPlanThreads = 256;
+constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int kReduceThreads = 256;
+constexpr int kCombineDepth = 26;  // tiles per destination < 2^26 for n < 2^31 rows
+
+struct TileCount {
+    int32_t tiles;   // tiles of the segment
+    int32_t multi;   // 1 if the segment has more than one tile
+    int32_t pslots;  // partial slots the segment needs (its tile count when multi)
+};
+
+__device__ __forceinline__ TileCount tile_count(int32_t L, int tc_log2) {
+    TileCount c{0, 0, 0};
+    if (L > 0) {
+        const int32_t chunks = (L + 7) >> 3;
+        c.tiles = (chunks + (1 << tc_log2) - 1) >> tc_log2;
+        c.multi = c.tiles > 1;
+        c.pslots = c.multi ? c.tiles : 0;
+    }
+    return c;
+}
+
+__device__ __forceinline__ int32_t wave_sum(int32_t v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ int32_t wave_inclusive_scan(int32_t v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t t = __shfl_up(v, off, 64);
+        if (lane >= off) v += t;
+    }
+    return v;
+}
+
+// Per destination: check the offsets, count tiles; per workgroup: the sums.
+__global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(const int32_t* __restrict__ seg, int32_t num_dests,
+                                                                  int64_t n, int tc_log2, int32_t* block_sums,
+                                                                  int32_t* status) {
+    __shared__ int32_t part[3][kPlanWaves];
+    if (status[kWordStatus] != 0) return;
+    const int64_t d = (int64_t)blockIdx.x * kPlanThreads + threadIdx.x;
+    TileCount c{0, 0, 0};
+    bool bad = false;
+    if (d < num_dests) {
+        const int32_t a = seg[d], b = seg[d + 1];
+        if (a < 0 || b < a || b > n) bad = true;
+        else c = tile_count(b - a, tc_log2);
+        if (d == 0 && a != 0) bad = true;
+        if (d == num_dests - 1 && b != n) bad = true;
+    }
+    if (bad) atomicOr(&status[kWordStatus], kStatusPlan);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int32_t st = wave_sum(c.tiles), sm = wave_sum(c.multi), sp = wave_sum(c.pslots);
+    if (lane == 0) {
+        part[0][w] = st;
+        part[1][w] = sm;
+        part[2][w] = sp;
+    }
+    __syncthreads();
+    if (threadIdx.x < 3) {
+        int32_t s = 0;
+        for (int i = 0; i < kPlanWaves; ++i) s += part[threadIdx.x][i];
+        block_sums[3 * blockIdx.x + threadIdx.x] = s;
+    }
+}
+
+// Exclusive prefix of the three counts over all destinations; writes one
+// TileRec per tile and one MultiRec per destination with several tiles.
+__global__ __launch_bounds__(kPlanThreads) void plan_write_kernel(const int32_t* __restrict__ seg, int32_t num_dests,
+                                                                  int tc_log2, const int32_t* __restrict__ block_sums,
+                                                                  TileRec* __restrict__ tiles,
+                                                                  MultiRec* __restrict__ multis, int32_t* status) {
+    __shared__ int32_t part[3][kPlanWaves];
+    __shared__ int32_t base[3];
+    if (status[kWordStatus] != 0) return;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    // sums of the earlier workgroups
+    int32_t pt = 0, pm = 0, pp = 0;
+    for (int64_t b = threadIdx.x; b < blockIdx.x; b += kPlanThreads) {
+        pt += block_sums[3 * b];
+        pm += block_sums[3 * b + 1];
+        pp += block_sums[3 * b + 2];
+    }
+    pt = wave_sum(pt);
+    pm = wave_sum(pm);
+    pp = wave_sum(pp);
+    if (lane == 0) {
+        part[0][w] = pt;
+        part[1][w] = pm;
+        part[2][w] = pp;
+    }
+    __syncthreads();
+    if (threadIdx.x < 3) {
+        int32_t s = 0;
+        for (int i = 0; i < kPlanWaves; ++i) s += part[threadIdx.x][i];
+        base[threadIdx.x] = s;
+    }
+    __syncthreads();
+    // own destinations
+    const int64_t d = (int64_t)blockIdx.x * kPlanThreads + threadIdx.x;
+    TileCount c{0, 0, 0};
+    if (d < num_dests) c = tile_count(seg[d + 1] - seg[d], tc_log2);
+    const int32_t it = wave_inclusive_scan(c.tiles), im = wave_inclusive_scan(c.multi),
+                  ip = wave_inclusive_scan(c.pslots);
+    __syncthreads();
+    if (lane == 63) {
+        part[0][w] = it;
+        part[1][w] = im;
+        part[2][w] = ip;
+    }
+    __syncthreads();
+    int32_t wt = 0, wm = 0, wp = 0, tt = 0, tm = 0;
+    for (int i = 0; i < kPlanWaves; ++i) {
+        if (i < w) {
+            wt += part[0][i];
+            wm += part[1][i];
+            wp += part[2][i];
+        }
+        tt += part[0][i];
+        tm += part[1][i];
+    }
+    const int32_t tile0 = base[0] + wt + it - c.tiles;
+    const int32_t multi0 = base[1] + wm + im - c.multi;
+    const int32_t pslot0 = base[2] + wp + ip - c.pslots;
+    for (int32_t j = 0; j < c.tiles; ++j) {
+        TileRec r;
+        r.dest = (int32_t)d;
+        r.chunk0 = j << tc_log2;
+        r.pslot = c.multi ? pslot0 + j : -1;
+        r.pad = 0;
+        tiles[tile0 + j] = r;
+    }
+    if (c.multi) {
+        MultiRec m;
+        m.dest = (int32_t)d;
+        m.pslot0 = pslot0;
+        m.ntiles = c.tiles;
+        m.pad = 0;
+        multis[multi0] = m;
+    }
+    if (blockIdx.x == gridDim.x - 1 && threadIdx.x == 0) {
+        status[kWordTiles] = base[0] + tt;
+        status[kWordMultis] = base[1] + tm;
+    }
+}
+
+// Checks a caller-supplied plan: every sorted position r holds a source row
+// p = perm[r] in range whose index[p] = d satisfies seg[d] <= r < seg[d+1].
+__global__ void plan_validate_kernel(const int32_t* __restrict__ perm, const int32_t* __restrict__ seg,
+                                     const int32_t* __restrict__ index, int64_t n, int32_t num_dests,
+                                     int32_t* status) {
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= n) return;
+    const int32_t p = perm[r];
+    int32_t err = 0;
+    if (p < 0 || p >= n) {
+        err = kStatusPlan;
+    } else {
+        const int32_t d = index[p];
+        if (d < 0 || d >= num_dests) err = kStatusIndex;
+        else if (r < seg[d] || r >= seg[d + 1]) err = kStatusPlan;
+    }
+    if (err) atomicOr(&status[kWordStatus], err);
+}
+
+// Binary counter of subtree sums: level l holds a complete subtree of 2^l
+// leaves.  push() merges the new leaf with the filled levels below the first
+// empty one (left operand first) and stores it there; fold() combines the
+// remaining subtrees from the right.  This gives T for any leaf count.  The
+// code is branch-free with compile-time level indices, so the levels stay in
+// registers: the number of merges is the count of trailing ones of count.
+template <int DEPTH, int E>
+struct TreeCounter {
+    float level[DEPTH][E];
+    uint32_t count = 0;
+
+    __device__ __forceinline__ TreeCounter() {
+#pragma unroll
+        for (int l = 0; l < DEPTH; ++l) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) level[l][e] = neg_zero();
+        }
+    }
+
+    __device__ __forceinline__ void push(float (&s)[E]) {
+        const int merges = __builtin_ctz(~count);
+#pragma unroll
+        for (int l = 0; l < DEPTH; ++l) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float a = level[l][e] + s[e];
+                s[e] = l < merges ? a : s[e];
+            }
+        }
+#pragma unroll
+        for (int l = 0; l < DEPTH; ++l) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) level[l][e] = l == merges ? s[e] : level[l][e];
+        }
+        ++count;
+    }
+
+    __device__ __forceinline__ void fold(float (&acc)[E]) const {
+        bool have = false;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = neg_zero();
+#pragma unroll
+        for (int l = 0; l < DEPTH; ++l) {
+            const bool bit = (count >> l) & 1u;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float a = level[l][e] + acc[e];
+                acc[e] = bit ? (have ? a : level[l][e]) : acc[e];
+            }
+            have = have || bit;
+        }
+    }
+};
+
+template <int E>
+__device__ __forceinline__ void rmw_row(float* dst, const float (&t)[E]) {
+    // out = old + T: the old value is the left operand, added once, last.
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+        const u32x4 o = load16(dst + e);
+        u32x4 r;
+        r.x = __float_as_uint(__uint_as_float(o.x) + t[e + 0]);
+        r.y = __float_as_uint(__uint_as_float(o.y) + t[e + 1]);
+        r.z = __float_as_uint(__uint_as_float(o.z) + t[e + 2]);
+        r.w = __float_as_uint(__uint_as_float(o.w) + t[e + 3]);
+        store16(dst + e, r);
+    }
+}
+
+template <int E>
+__device__ __forceinline__ void store_row(float* dst, const float (&t)[E]) {
+#pragma unroll
+    for (int e = 0; e < E; e += 4) {
+        u32x4 r;
+        r.x = __float_as_uint(t[e + 0]);
+        r.y = __float_as_uint(t[e + 1]);
+        r.z = __float_as_uint(t[e + 2]);
+        r.w = __float_as_uint(t[e + 3]);
+        store16(dst + e, r);
+    }
+}
+
+// Lane groups of GROUP lanes; each lane owns one 16-byte piece of a row.
+template <dr_dtype DT, int GROUP, int TCLOG>
+__global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
+    float* __restrict__ out, int64_t H, const void* __restrict__ src, int64_t n, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ seg, const TileRec* __restrict__ tiles, float* __restrict__ partials,
+    int64_t slices, int64_t pieces_per_row, int32_t* status) {
+    constexpr int E = Vec<DT>::kElems;
+    constexpr int kElemBytes = DT == DR_BF16 ? 2 : 4;
+    if (status[kWordStatus] != 0) return;
+    // the host keeps (tile bound) * slices below 2^32, so 32-bit division suffices
+    const uint32_t items = (uint32_t)status[kWordTiles] * (uint32_t)slices;
+    const int lane_in_group = threadIdx.x % GROUP;
+    const uint32_t group = (blockIdx.x * kReduceThreads + threadIdx.x) / GROUP;
+    const uint32_t ngroups = (gridDim.x * kReduceThreads) / GROUP;
+    const char* src_bytes = reinterpret_cast<const char*>(src);
+    const int64_t row_bytes = H * kElemBytes;
+    for (uint32_t it = group; it < items; it += ngroups) {
+        const uint32_t tile = it / (uint32_t)slices;
+        const uint32_t slice = it - tile * (uint32_t)slices;
+        const TileRec tr = tiles[tile];
+        const int64_t piece = (int64_t)slice * GROUP + lane_in_group;
+        const bool active = piece < pieces_per_row;
+        const int64_t lane_off = (active ? piece : 0) * 16;  // idle lanes read a valid piece
+        const int64_t r_begin = (int64_t)seg[tr.dest] + ((int64_t)tr.chunk0 << 3);
+        const int64_t r_end = min((int64_t)seg[tr.dest + 1], r_begin + ((int64_t)8 << TCLOG));
+        TreeCounter<TCLOG + 1, E> tc;
+        for (int64_t r0 = r_begin; r0 < r_end; r0 += 8) {
+            const int m = (int)min((int64_t)8, r_end - r0);
+            // A short last chunk reloads its last row for the missing slots (a
+            // cache hit) so that all eight loads issue together; those slots
+            // are then not added.
+            int32_t idx[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) idx[j] = perm[r0 + min(j, m - 1)];
+            u32x4 raw[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) raw[j] = load16(src_bytes + (int64_t)idx[j] * row_bytes + lane_off);
+            float s[E];
+            Vec<DT>::widen(raw[0], s);
+#pragma unroll
+            for (int j = 1; j < 8; ++j) {
+                float v[E];
+                Vec<DT>::widen(raw[j], v);
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float a = s[e] + v[e];
+                    s[e] = j < m ? a : s[e];
+                }
+            }
+            tc.push(s);
+        }
+        float t[E];
+        tc.fold(t);
+        if (active) {
+            if (tr.pslot < 0) rmw_row<E>(out + (int64_t)tr.dest * H + piece * E, t);
+            else store_row<E>(partials + (int64_t)tr.pslot * H + piece * E, t);
+        }
+    }
+}
+
+// Merges the partial rows of each multi-tile destination in tile order.
+template <int GROUP>
+__global__ __launch_bounds__(kReduceThreads) void tilecombine_kernel(float* __restrict__ out, int64_t H,
+                                                                     const float* __restrict__ partials,
+                                                                     const MultiRec* __restrict__ multis,
+                                                                     int64_t slices, int64_t pieces_per_row,
+                                                                     int32_t* status) {
+    if (status[kWordStatus] != 0) return;
+    const uint32_t items = (uint32_t)status[kWordMultis] * (uint32_t)slices;
+    const int lane_in_group = threadIdx.x % GROUP;
+    const uint32_t group = (blockIdx.x * kReduceThreads + threadIdx.x) / GROUP;
+    const uint32_t ngroups = (gridDim.x * kReduceThreads) / GROUP;
+    for (uint32_t it = group; it < items; it += ngroups) {
+        const uint32_t mi = it / (uint32_t)slices;
+        const uint32_t slice = it - mi * (uint32_t)slices;
+        const MultiRec mr = multis[mi];
+        const int64_t piece = (int64_t)slice * GROUP + lane_in_group;
+        if (piece >= pieces_per_row) continue;
+        TreeCounter<kCombineDepth, 4> tc;
+        for (int32_t q = 0; q < mr.ntiles; ++q) {
+            const u32x4 raw = load16(partials + (int64_t)(mr.pslot0 + q) * H + piece * 4);
+            float s[4];
+            Vec<DR_F32>::widen(raw, s);
+            tc.push(s);
+        }
+        float t[4];
+        tc.fold(t);
+        rmw_row<4>(out + (int64_t)mr.dest * H + piece * 4, t);
+    }
+}
+
+int group_for(int64_t pieces) {
+    if (pieces <= 16) return 16;
+    if (pieces <= 32) return 32;
+    return 64;
+}
+
+template <dr_dtype DT, int GROUP>
+hipError_t launch_segreduce_g(dim3 grid, float* out, int64_t H, const void* src, int64_t n, const int32_t* perm,
+                              const int32_t* seg, const TileRec* tiles, float* partials, int tc_log2,
+                              int64_t slices, int64_t pieces, int32_t* status, hipStream_t s) {
+#define DR_SEGREDUCE_CASE(TC)                                                                                  \
+    case TC:                                                                                                   \
+        hipLaunchKernelGGL((segreduce_kernel<DT, GROUP, TC>), grid, dim3(kReduceThreads), 0, s, out, H, src, n, \
+                           perm, seg, tiles, partials, slices, pieces, status);                                \
+        break;
+    switch (tc_log2) {
+        DR_SEGREDUCE_CASE(3)
+        DR_SEGREDUCE_CASE(4)
+        DR_SEGREDUCE_CASE(5)
+        DR_SEGREDUCE_CASE(6)
+        DR_SEGREDUCE_CASE(7)
+        default:
+            return hipErrorInvalidValue;
+    }
+#undef DR_SEGREDUCE_CASE
+    return hipGetLastError();
+}
+
+unsigned persistent_grid() {
+    const Launch lc = launch_config();
+    if (lc.grid_blocks > 0) return (unsigned)lc.grid_blocks;
+    return (unsigned)(device_cu_count() * 8);
+}
+
+}  // namespace
+
+int64_t plan_blocks(int32_t num_dests) { return ((int64_t)num_dests + kPlanThreads - 1) / kPlanThreads; }
+
+hipError_t launch_plan_count(const int32_t* seg_offsets, int32_t num_dests, int64_t n, int tc_log2,
+                             int32_t* block_sums, int32_t* status, hipStream_t s) {
+    hipLaunchKernelGGL(plan_count_kernel, dim3((unsigned)plan_blocks(num_dests)), dim3(kPlanThreads), 0, s,
+                       seg_offsets, num_dests, n, tc_log2, block_sums, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_plan_write(const int32_t* seg_offsets, int32_t num_dests, int tc_log2, const int32_t* block_sums,
+                             TileRec* tiles, MultiRec* multis, int32_t* status, hipStream_t s) {
+    hipLaunchKernelGGL(plan_write_kernel, dim3((unsigned)plan_blocks(num_dests)), dim3(kPlanThreads), 0, s,
+                       seg_offsets, num_dests, tc_log2, block_sums, tiles, multis, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_plan_validate(const int32_t* perm, const int32_t* seg, const int32_t* index, int64_t n,
+                                int32_t num_dests, int32_t* status, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(plan_validate_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, perm, seg, index, n,
+                       num_dests, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_segreduce(float* out, int64_t hidden, const void* src, dr_dtype dt, int64_t n, const int32_t* perm,
+                            const int32_t* seg_offsets, const TileRec* tiles, float* partials, int tc_log2,
+                            int32_t* status, hipStream_t s) {
+    const int64_t pieces = dt == DR_BF16 ? hidden / 8 : hidden / 4;
+    const int g = group_for(pieces);
+    const int64_t slices = (pieces + g - 1) / g;
+    const dim3 grid(persistent_grid());
+#define DR_SR(DT, G) \
+    return launch_segreduce_g<DT, G>(grid, out, hidden, src, n, perm, seg_offsets, tiles, partials, tc_log2, slices, \
+                                     pieces, status, s)
+    if (dt == DR_BF16) {
+        if (g == 16) DR_SR(DR_BF16, 16);
+        if (g == 32) DR_SR(DR_BF16, 32);
+        DR_SR(DR_BF16, 64);
+    }
+    if (g == 16) DR_SR(DR_F32, 16);
+    if (g == 32) DR_SR(DR_F32, 32);
+    DR_SR(DR_F32, 64);
+#undef DR_SR
+}
+
+hipError_t launch_tilecombine(float* out, int64_t hidden, const float* partials, const MultiRec* multis,
+                              int32_t* status, hipStream_t s) {
+    const int64_t pieces = hidden / 4;
+    const int g = group_for(pieces);
+    const int64_t slices = (pieces + g - 1) / g;
+    const dim3 grid(persistent_grid());
+    if (g == 16)
+        hipLaunchKernelGGL(tilecombine_kernel<16>, grid, dim3(kReduceThreads), 0, s, out, hidden, partials, multis,
+                           slices, pieces, status);
+    else if (g == 32)
+        hipLaunchKernelGGL(tilecombine_kernel<32>, grid, dim3(kReduceThreads), 0, s, out, hidden, partials, multis,
+                           slices, pieces, status);
+    else
+        hipLaunchKernelGGL(tilecombine_kernel<64>, grid, dim3(kReduceThreads), 0, s, out, hidden, partials, multis,
+                           slices, pieces, status);
+    return hipGetLastError();
+}
+
+}  // namespace dr

@@ -1,0 +1,253 @@
+// Stable LSD radix sort of contributions by (destination, source id), and the
+// CSR segment offsets of the sorted order.
+//
+// The order it produces is the one the DeepSeek-V4 MoE backward uses (ch. 9,
+// section 3.2: sort the tokens that land on a rank by (expert_id,
+// original_token_id) and merge in that order).  Stability comes from ranking
+// keys inside a workgroup in index order.  Integer atomics only count
+// histogram entries, whose totals do not depend on the order of the
+// increments; no atomic ever claims an output slot.
+//
+// Pass structure (per 2^b-bin digit): histogram per tile of keys, one scan per
+// digit row over the tiles, then a scatter that recomputes each key's stable
+// rank within its tile.
+#include "internal.h"
+
+namespace dr {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxBins = 256;
+
+__device__ __forceinline__ int digit_of(int32_t key, int shift, int bits) {
+    return (int)(((uint32_t)key >> shift) & ((1u << bits) - 1u));
+}
+
+__device__ __forceinline__ int32_t wave_inclusive_scan(int32_t v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        int32_t t = __shfl_up(v, off, 64);
+        if (lane >= off) v += t;
+    }
+    return v;
+}
+
+// Exclusive scan over the workgroup (kThreads threads); total gets the sum.
+__device__ int32_t block_exclusive_scan(int32_t v, int32_t& total, int32_t* wave_tot) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int32_t incl = wave_inclusive_scan(v);
+    if (lane == 63) wave_tot[w] = incl;
+    __syncthreads();
+    int32_t before = 0, all = 0;
+#pragma unroll
+    for (int i = 0; i < kWaves; ++i) {
+        const int32_t s = wave_tot[i];
+        before += (i < w) ? s : 0;
+        all += s;
+    }
+    __syncthreads();
+    total = all;
+    return before + incl - v;
+}
+
+__global__ void fill_status_kernel(int32_t* status) {
+    if (threadIdx.x < kStatusBytes / sizeof(int32_t)) status[threadIdx.x] = 0;
+}
+
+// Digit histogram of one tile of keys per workgroup.  With kValidate, also
+// checks every dest (and src_id) against its range: the first pass of a sort.
+template <bool kValidate>
+__global__ __launch_bounds__(kThreads) void radix_hist_kernel(SortPass p, int64_t n, int tile_log2, int32_t* hist,
+                                                              int64_t nblocks, const int32_t* __restrict__ dest,
+                                                              int32_t num_dests, const int32_t* __restrict__ src_id,
+                                                              int32_t src_bound, int32_t* status) {
+    __shared__ int32_t cnt[kMaxBins];
+    __shared__ int32_t bad;
+    if (!kValidate && status[kWordStatus] != 0) return;  // same value for every thread
+    const int bins = 1 << p.bits;
+    for (int d = threadIdx.x; d < bins; d += kThreads) cnt[d] = 0;
+    if (threadIdx.x == 0) bad = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x << tile_log2;
+    const int64_t end = min(n, base + ((int64_t)1 << tile_log2));
+    int my_bad = 0;
+    for (int64_t i = base + threadIdx.x; i < end; i += kThreads) {
+        if (kValidate) {
+            const int32_t dd = dest[i];
+            my_bad |= (dd < 0 || dd >= num_dests);
+            if (src_id) {
+                const int32_t ss = src_id[i];
+                my_bad |= (ss < 0 || ss >= src_bound);
+            }
+        }
+        atomicAdd(&cnt[digit_of(p.digit_src[i], p.shift, p.bits)], 1);
+    }
+    if (my_bad) bad = 1;
+    __syncthreads();
+    for (int d = threadIdx.x; d < bins; d += kThreads) hist[(int64_t)d * nblocks + blockIdx.x] = cnt[d];
+    if (kValidate && threadIdx.x == 0 && bad) atomicOr(&status[kWordStatus], kStatusIndex);
+}
+
+// One workgroup per digit: exclusive scan of that digit's counts over the
+// tiles (in place), and the digit's total.
+__global__ __launch_bounds__(kThreads) void radix_scan_kernel(int32_t* hist, int64_t nblocks, int32_t* totals,
+                                                              const int32_t* status) {
+    __shared__ int32_t wave_tot[kWaves];
+    if (status[kWordStatus] != 0) return;
+    int32_t* h = hist + (int64_t)blockIdx.x * nblocks;
+    int32_t carry = 0;
+    for (int64_t b0 = 0; b0 < nblocks; b0 += kThreads) {
+        const int64_t b = b0 + threadIdx.x;
+        const int32_t v = b < nblocks ? h[b] : 0;
+        int32_t tot;
+        const int32_t ex = block_exclusive_scan(v, tot, wave_tot);
+        if (b < nblocks) h[b] = carry + ex;
+        carry += tot;
+    }
+    if (threadIdx.x == 0) totals[blockIdx.x] = carry;
+}
+
+// Stable scatter of one tile.  Keys are visited in rounds of kThreads
+// consecutive keys; within a round a key's rank among equal digits is the
+// count in earlier waves plus the count of lower lanes in its own wave (wave
+// ballots), and rounds are visited in order, so equal digits keep input order.
+__global__ __launch_bounds__(kThreads) void radix_scatter_kernel(SortPass p, int64_t n, int tile_log2,
+                                                                 const int32_t* __restrict__ hist, int64_t nblocks,
+                                                                 const int32_t* __restrict__ totals,
+                                                                 const int32_t* status) {
+    __shared__ int32_t base_s[kMaxBins];
+    __shared__ int32_t running[kMaxBins];
+    __shared__ int32_t wave_cnt[kWaves][kMaxBins];
+    __shared__ int32_t wave_off[kWaves][kMaxBins];
+    __shared__ int32_t wave_tot[kWaves];
+    if (status[kWordStatus] != 0) return;
+    const int tid = threadIdx.x, w = tid >> 6;
+    const int bins = 1 << p.bits;
+    int32_t all;
+    const int32_t digit_base = block_exclusive_scan(tid < bins ? totals[tid] : 0, all, wave_tot);
+    if (tid < bins) {
+        base_s[tid] = digit_base + hist[(int64_t)tid * nblocks + blockIdx.x];
+        running[tid] = 0;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) wave_cnt[ww][tid] = 0;
+    }
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x << tile_log2;
+    const int64_t end = min(n, base + ((int64_t)1 << tile_log2));
+    const bool key_is_dest = p.digit_src == p.dest_in;
+    for (int64_t r0 = base; r0 < end; r0 += kThreads) {
+        const int64_t i = r0 + tid;
+        const bool valid = i < end;
+        int32_t key = 0;
+        int dg = 0;
+        if (valid) {
+            key = p.digit_src[i];
+            dg = digit_of(key, p.shift, p.bits);
+        }
+        uint64_t peers = __ballot(valid);
+        for (int b = 0; b < p.bits; ++b) {
+            const bool bit = (dg >> b) & 1;
+            const uint64_t m = __ballot(bit);
+            peers &= bit ? m : ~m;
+        }
+        const int rank = __popcll(peers & lanemask_lt());
+        if (valid && rank == 0) wave_cnt[w][dg] = __popcll(peers);
+        __syncthreads();
+        if (tid < bins) {
+            int32_t pre = running[tid];
+#pragma unroll
+            for (int ww = 0; ww < kWaves; ++ww) {
+                const int32_t c = wave_cnt[ww][tid];
+                wave_off[ww][tid] = pre;
+                pre += c;
+                wave_cnt[ww][tid] = 0;
+            }
+            running[tid] = pre;
+        }
+        __syncthreads();
+        if (valid) {
+            const int32_t pos = base_s[dg] + wave_off[w][dg] + rank;
+            const int32_t val = p.val_in ? p.val_in[i] : (int32_t)i;
+            p.val_out[pos] = val;
+            if (p.dest_out) p.dest_out[pos] = key_is_dest ? key : p.dest_in[i];
+            if (p.src_out) p.src_out[pos] = key_is_dest ? p.src_in[i] : key;
+            if (p.inv_out) p.inv_out[val] = pos;
+        }
+        // The next round's counter writes happen before its first barrier, and
+        // wave_off is rewritten only after that barrier, when every thread has
+        // finished reading this round's offsets.
+    }
+}
+
+// seg_offsets[d] = first sorted position whose dest is >= d (lower bound),
+// for d = 0 .. num_dests; sorted_dest is non-decreasing.
+__global__ void seg_offsets_kernel(const int32_t* __restrict__ sorted_dest, int64_t n, int32_t num_dests,
+                                   int32_t* __restrict__ seg, const int32_t* status) {
+    if (status[kWordStatus] != 0) return;
+    const int64_t d = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (d > num_dests) return;
+    int64_t lo = 0, hi = n;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi) >> 1;
+        if (sorted_dest[mid] < d) lo = mid + 1;
+        else hi = mid;
+    }
+    seg[d] = (int32_t)lo;
+}
+
+}  // namespace
+
+hipError_t launch_fill_status(int32_t* status_block, hipStream_t s) {
+    hipLaunchKernelGGL(fill_status_kernel, dim3(1), dim3(64), 0, s, status_block);
+    return hipGetLastError();
+}
+
+static int64_t tiles_for(int64_t n, int tile_log2) { return (n + ((int64_t)1 << tile_log2) - 1) >> tile_log2; }
+
+hipError_t launch_radix_validate_hist(const int32_t* dest, int32_t num_dests, const int32_t* src_id,
+                                      int32_t src_bound, const SortPass& p, int64_t n, int tile_log2,
+                                      int32_t* hist, int32_t* status, hipStream_t s) {
+    const int64_t nb = tiles_for(n, tile_log2);
+    if (nb == 0) return hipSuccess;
+    hipLaunchKernelGGL(radix_hist_kernel<true>, dim3((unsigned)nb), dim3(kThreads), 0, s, p, n, tile_log2, hist,
+                       nb, dest, num_dests, src_id, src_bound, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_radix_hist(const SortPass& p, int64_t n, int tile_log2, int32_t* hist, const int32_t* status,
+                             hipStream_t s) {
+    const int64_t nb = tiles_for(n, tile_log2);
+    if (nb == 0) return hipSuccess;
+    hipLaunchKernelGGL(radix_hist_kernel<false>, dim3((unsigned)nb), dim3(kThreads), 0, s, p, n, tile_log2, hist,
+                       nb, nullptr, 0, nullptr, 0, const_cast<int32_t*>(status));
+    return hipGetLastError();
+}
+
+hipError_t launch_radix_scan(int32_t* hist, int64_t nblocks, int bins, int32_t* totals, const int32_t* status,
+                             hipStream_t s) {
+    if (nblocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(radix_scan_kernel, dim3(bins), dim3(kThreads), 0, s, hist, nblocks, totals, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_radix_scatter(const SortPass& p, int64_t n, int tile_log2, const int32_t* hist,
+                                const int32_t* totals, const int32_t* status, hipStream_t s) {
+    const int64_t nb = tiles_for(n, tile_log2);
+    if (nb == 0) return hipSuccess;
+    hipLaunchKernelGGL(radix_scatter_kernel, dim3((unsigned)nb), dim3(kThreads), 0, s, p, n, tile_log2, hist, nb,
+                       totals, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_seg_offsets(const int32_t* sorted_dest, int64_t n, int32_t num_dests, int32_t* seg_offsets,
+                              const int32_t* status, hipStream_t s) {
+    const int64_t count = (int64_t)num_dests + 1;
+    const unsigned blocks = (unsigned)((count + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL(seg_offsets_kernel, dim3(blocks), dim3(kThreads), 0, s, sorted_dest, n, num_dests,
+                       seg_offsets, status);
+    return hipGetLastError();
+}
+
+}  // namespace dr

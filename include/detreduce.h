@@ -1,0 +1,260 @@
+/*
+ * libdetreduce: deterministic, batch-invariant fp32 reduction of many
+ * contributions into shared destinations, for AMD Instinct MI355X (gfx950).
+ *
+ * It replaces many-writer atomicAdd accumulation.  The pages behind this
+ * library name that pattern as the nondeterminism to remove: several writers
+ * adding into one address, with the arrival order deciding the last bits
+ * (bitwise-determinism interview note, table "where nondeterminism comes
+ * from", multiple-writers row; DeepSeek-V4 book ch. 9, "atomicAdd" glossary
+ * entry).  Their fix is one private slot per writer, merged in a fixed order.
+ *
+ * THE DEFINED ORDER (every deterministic entry point follows it)
+ *   1. The contributions of one destination are ordered by source id (ties by
+ *      input position).  This is a stable sort by (destination, source id),
+ *      as in the DeepSeek-V4 MoE backward (ch. 9, section 3.2).
+ *   2. T(v_0..v_{L-1}): chunks of 8 consecutive contributions are summed left
+ *      to right, starting from the first element.  The chunk sums are combined
+ *      by a balanced pairwise tree that splits at the largest power of two
+ *      strictly below the chunk count, left part first.
+ *   3. Arithmetic is IEEE binary32 with round to nearest even.  There is no
+ *      fused multiply-add and no flush of subnormals.  A product (the combine
+ *      gate times a row) is rounded to fp32 before it is added.
+ *   Because the tree splits only at aligned powers of two, any division of a
+ *   destination's contributions into aligned 2^m-chunk tiles gives the same
+ *   bits.  So results depend neither on the grid, the workgroup size or the
+ *   tile size, nor on which other destinations or tokens are in the batch
+ *   (batch invariance: DeepSeek-V4 book ch. 9, glossary, "batch invariant" and
+ *   "deterministic").
+ *
+ * CONVENTIONS
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *     allocates no memory.  Scratch space comes from caller workspaces sized
+ *     by the *_workspace_size functions.
+ *   - Every call is asynchronous on the given HIP stream and does not
+ *     synchronise, apart from dr_workspace_status and dr_read_status.
+ *   - Argument errors are returned synchronously and nothing is launched.
+ *     Bad values inside device arrays (an index out of range) are detected by
+ *     the kernels.  They set a device status word, and the call then writes
+ *     none of its outputs that accumulate (fail closed: the call refuses to run
+ *     rather than silently giving a different result; Megatron-LM determinism
+ *     reference, section 1.2, "fail closed").  There is never a fallback to an
+ *     unordered or atomic path.
+ *   - Layouts are row-major and contiguous.  Row data must be 16-byte aligned,
+ *     and `hidden` must be a multiple of 8 for bf16 or 4 for fp32.
+ *   - bf16 data are raw bfloat16 values.  They are widened to fp32 exactly.
+ *   - The library reads no environment variables.  Launch shapes are fixed
+ *     functions of the arguments.  dr_set_launch_params (thread-local) lets
+ *     tests vary them, which by construction cannot change any output bit.
+ *   - The *_atomic entry points are deliberately NONDETERMINISTIC baselines
+ *     with the same shapes.  They use hardware fp32 atomic adds, the pattern
+ *     being replaced (Megatron-LM determinism reference, section 3.1 op
+ *     catalog: the default unpermute path is an atomic scatter_add_).
+ */
+#ifndef DETREDUCE_H
+#define DETREDUCE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dr_status {
+    DR_OK = 0,
+    DR_ERR_INVALID_ARGUMENT = 1,   /* null/misaligned pointer, bad size or shape */
+    DR_ERR_UNSUPPORTED = 2,        /* valid request this library does not implement */
+    DR_ERR_WORKSPACE_TOO_SMALL = 3,
+    DR_ERR_INDEX_OUT_OF_RANGE = 4, /* device-detected: an index outside its range */
+    DR_ERR_HIP = 5,                /* a HIP runtime call failed */
+    DR_ERR_BAD_PLAN = 6            /* device-detected: perm/seg_offsets are inconsistent */
+} dr_status;
+
+typedef enum dr_dtype { DR_F32 = 0, DR_BF16 = 1 } dr_dtype;
+
+/* Launch shape overrides, for tests of launch invariance.  A zero field keeps
+ * the library default.  The setting is thread-local. */
+typedef struct dr_launch_params {
+    int32_t grid_blocks;        /* workgroups of the persistent kernels (index_add reduce and tile
+                                   combine, fingerprint), 1 .. 65536 */
+    int32_t tile_chunks_log2;   /* index_add tile = 2^m chunks of 8 rows, m in [3, 7] (default 5) */
+    int32_t sort_tile_log2;     /* radix sort keys per workgroup = 2^m, m in [8, 14] (default 12) */
+    int32_t reserved;           /* must be 0 */
+} dr_launch_params;
+
+/* Human-readable name of a status code.  Never NULL. */
+const char* dr_status_string(dr_status s);
+
+/* Detail of the last error returned on this thread ("" if none).  Never NULL. */
+const char* dr_last_error(void);
+
+/* Library ABI version (major * 100 + minor). */
+int32_t dr_version(void);
+
+/* Sets (p != NULL) or resets (p == NULL) this thread's launch overrides.
+ * Returns DR_ERR_INVALID_ARGUMENT for out-of-range fields, leaving the
+ * previous setting in place. */
+dr_status dr_set_launch_params(const dr_launch_params* p);
+
+/* ------------------------------------------------------------------------
+ * Stable sort of contributions by destination.
+ *
+ * Defines the order of contributions: by (dest, src_id), ties by input
+ * position.  This is the DeepSeek-V4 MoE backward (ch. 9, section 3.2): tokens
+ * are sorted by (expert_id, original_token_id) and merged in sorted order.
+ * Stable sorts are naturally deterministic (Megatron-LM determinism
+ * reference, section 3, naturally deterministic operations).
+ *
+ *   dest[n]          destination of each contribution, 0 <= dest < num_dests.
+ *   src_id[n]        source id of each contribution, 0 <= src_id < src_id_bound;
+ *                    NULL means src_id[i] = i (then src_id_bound is ignored).
+ *   perm[n]          OUT: perm[r] = input position of the r-th contribution
+ *                    in sorted order.
+ *   seg_offsets[num_dests+1]  OUT: CSR offsets; the contributions of d are
+ *                    perm[seg_offsets[d] .. seg_offsets[d+1]).
+ *   inv_perm[n]      OUT, optional (NULL to skip): inv_perm[perm[r]] = r.  For
+ *                    MoE dispatch with dest = expert and i = t*k + j, this is
+ *                    the row of (t, j) in the expert-major layout.
+ *   ws, ws_bytes     workspace of at least dr_sort_workspace_size(n,
+ *                    num_dests, src_id ? src_id_bound : 0) bytes, 16-byte
+ *                    aligned.  The first 256 bytes hold the call's device
+ *                    status word (see dr_workspace_status).
+ * Integer result, exactly reproducible.  n may be 0.  n < 2^31.
+ * An out-of-range dest or src_id sets the status word to
+ * DR_ERR_INDEX_OUT_OF_RANGE; perm, seg_offsets and inv_perm are then undefined.
+ * ---------------------------------------------------------------------- */
+size_t dr_sort_workspace_size(int64_t n, int32_t num_dests, int32_t src_id_bound);
+dr_status dr_sort_by_dest(const int32_t* dest, const int32_t* src_id, int32_t src_id_bound, int64_t n,
+                          int32_t num_dests, int32_t* perm, int32_t* seg_offsets, int32_t* inv_perm,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * MoE token combine (unpermute): out[t] = T over the token's k contributions.
+ *
+ * Contribution (t, j) is fl32(gates[t*k+j] * rows[row_of[t*k+j]]), taken in
+ * ascending row order (ties by slot j).  With the expert-major layout of the
+ * dispatch sort, this is expert-id order, which is the same for every expert-
+ * parallel size (bitwise-determinism interview note: every EP size goes
+ * through one fp32 reduction tree).  The operation is the MoE token
+ * unpermute of the Megatron-LM op catalog (determinism reference, section
+ * 3.1) and the merge step of the DeepSeek-V4 MoE backward (ch. 9, section 3.2).
+ *
+ *   rows[num_rows, hidden]  expert outputs, fp32 or bf16.
+ *   row_of[T, k], gates[T, k]  int32 row ids and fp32 gates.  1 <= k <= 64.
+ *   out[T, hidden]          OUT, fp32, written (not accumulated).
+ *   dev_status              optional device int32 status word (see
+ *                           dr_read_status).  If a token references a row
+ *                           outside [0, num_rows), that token's output row is
+ *                           set to NaN, no row outside the buffer is read, and
+ *                           an index error bit is OR-ed into *dev_status.  The
+ *                           library never clears the word; the caller zeroes it.
+ * ---------------------------------------------------------------------- */
+dr_status dr_combine(const void* rows, dr_dtype rows_dtype, int64_t num_rows, int64_t hidden,
+                     const int32_t* row_of, const float* gates, int64_t T, int32_t k, float* out,
+                     int32_t* dev_status, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * index_add: out[d] = out[d] + T(src rows i with index[i] == d, in order of i).
+ *
+ * This is torch's index_add_(0, index, src), which the Megatron-LM op catalog
+ * (determinism reference, section 3.1) uses for the deterministic MoE
+ * unpermute and which also forms the vocab-parallel embedding backward.  The
+ * DeepSeek-V4 sparse-attention backward (ch. 9, section 3.1) accumulates key
+ * gradients of many queries into shared keys in the same way.  The old
+ * destination value is added once, last; rows with no contribution are not
+ * written (collision-free final write).
+ *
+ *   out[num_dests, hidden]  fp32, accumulated in place.
+ *   src[n, hidden]          fp32 or bf16 contributions.
+ *   index[n]                int32 destinations.
+ *   perm, seg_offsets       either both NULL (the call sorts internally), or
+ *                           both from dr_sort_by_dest(index, src_id = NULL) on
+ *                           the same index (a reused plan).
+ *   ws, ws_bytes            workspace >= dr_index_add_workspace_size(), 16-byte
+ *                           aligned; the first 256 bytes are the status word.
+ * Device-detected errors (index out of range, inconsistent plan) leave out
+ * untouched and are reported by dr_workspace_status.
+ * ---------------------------------------------------------------------- */
+size_t dr_index_add_workspace_size(int64_t n, int32_t num_dests, int64_t hidden);
+dr_status dr_index_add(float* out, int32_t num_dests, int64_t hidden, const void* src, dr_dtype src_dtype,
+                       int64_t n, const int32_t* index, const int32_t* perm, const int32_t* seg_offsets,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Split-K contraction into private per-split buffers.
+ *
+ * partials[s] = X_s^T * dY_s for split s = tokens [s*c, min(K, (s+1)*c)),
+ * c = ceil(K / splits).  Each split writes its own buffer and nothing is
+ * reduced here (DeepSeek-V4 book ch. 9, section 3.3, mHC backward: every
+ * K-split outputs to its own buffer).  Split boundaries are a function of
+ * (K, splits) only, never of occupancy (ch. 9, glossary "split-K": a split
+ * chosen per batch breaks batch invariance).  Products of bf16 values are
+ * summed by bf16 MFMA into fp32, in a fixed order within each split, so a
+ * partial is bitwise repeatable and independent of the M/N tiling.
+ *
+ *   X[K, M], dY[K, N]   bf16.  1 <= splits, and every split non-empty:
+ *                       (splits - 1) * c < K.
+ *   partials[splits, M, N]  OUT fp32, written.
+ * ---------------------------------------------------------------------- */
+dr_status dr_splitk_gemm_tn(const void* X, const void* dY, int64_t K, int64_t M, int64_t N, int32_t splits,
+                            float* partials, hipStream_t stream);
+
+/* out[e] = T(partials[0][e], ..., partials[splits-1][e]): the deterministic
+ * reduce over split ids (DeepSeek-V4 book ch. 9, section 3.3: a dedicated
+ * reduce kernel sums the per-split buffers in split-id order).
+ *   partials[splits, count] fp32;  out[count] fp32, written. */
+dr_status dr_splitk_reduce(const float* partials, int32_t splits, int64_t count, float* out,
+                           hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Byte fingerprint of a tensor, for comparing runs byte for byte rather than
+ * by printed values (bitwise-determinism interview note, "how to verify":
+ * per-step tensor fingerprints compared byte-wise).  The definition is this
+ * library's own:
+ *   h = mix(nbytes) + sum_i mix(w_i XOR mix(i + 1))   (mod 2^64)
+ * w_i is the i-th little-endian 64-bit word of the bytes in logical order,
+ * the last word zero-padded.  mix is SplitMix64's finaliser.  +0.0 and -0.0,
+ * and NaNs with different payloads, hash differently.
+ *   data       device pointer, 8-byte aligned (or nbytes == 0).
+ *   out_hash   OUT device uint64.
+ *   ws         >= dr_fingerprint_workspace_size(nbytes) bytes, 16-byte aligned.
+ * ---------------------------------------------------------------------- */
+size_t dr_fingerprint_workspace_size(int64_t nbytes);
+dr_status dr_fingerprint(const void* data, int64_t nbytes, uint64_t* out_hash, void* ws, size_t ws_bytes,
+                         hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Status words (these two calls synchronise the stream).
+ * A device status word is an int32 of error bits: 1 = an index out of range,
+ * 2 = an inconsistent caller-supplied plan.  These calls return DR_OK for 0,
+ * DR_ERR_BAD_PLAN if bit 2 is set, else DR_ERR_INDEX_OUT_OF_RANGE.
+ * dr_workspace_status reads the word at the head of a sort or index_add
+ * workspace, which every call on that workspace clears first.
+ * dr_read_status reads a caller-owned word such as dr_combine's.
+ * ---------------------------------------------------------------------- */
+dr_status dr_workspace_status(const void* ws, hipStream_t stream);
+dr_status dr_read_status(const int32_t* dev_status, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Deliberately nondeterministic atomicAdd baselines (same shapes).  The
+ * caller initialises out (zero for combine and split-K).  Out-of-range
+ * indices are skipped and OR an index error bit into *dev_status when it is
+ * not NULL.
+ * ---------------------------------------------------------------------- */
+dr_status dr_combine_atomic(const void* rows, dr_dtype rows_dtype, int64_t num_rows, int64_t hidden,
+                            const int32_t* row_of, const float* gates, int64_t T, int32_t k, float* out,
+                            int32_t* dev_status, hipStream_t stream);
+dr_status dr_index_add_atomic(float* out, int32_t num_dests, int64_t hidden, const void* src,
+                              dr_dtype src_dtype, int64_t n, const int32_t* index, int32_t* dev_status,
+                              hipStream_t stream);
+dr_status dr_splitk_gemm_tn_atomic(const void* X, const void* dY, int64_t K, int64_t M, int64_t N,
+                                   int32_t splits, float* out, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DETREDUCE_H */

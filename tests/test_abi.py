@@ -1,0 +1,176 @@
+"""CPU checks of the C-ABI library: it loads, exports every function the header
+declares, and refuses bad arguments synchronously, before any GPU work (fail
+closed).  No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "bitwise_deterministic_fp32_amd", "libdetreduce.so")
+HEADER = os.path.join(ROOT, "include", "detreduce.h")
+
+DR_OK, DR_ERR_INVALID_ARGUMENT, DR_ERR_UNSUPPORTED, DR_ERR_WORKSPACE_TOO_SMALL = 0, 1, 2, 3
+FAKE = 0x7F0000000000  # a 256-byte aligned address that is never dereferenced here
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from bitwise_deterministic_fp32_amd import build
+        build.build()
+    L = ctypes.CDLL(LIB)
+    L.dr_last_error.restype = ctypes.c_char_p
+    L.dr_status_string.restype = ctypes.c_char_p
+    return L
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dr_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared()
+    for required in ("dr_sort_by_dest", "dr_combine", "dr_index_add", "dr_splitk_reduce", "dr_fingerprint",
+                     "dr_combine_atomic", "dr_index_add_atomic", "dr_splitk_gemm_tn", "dr_splitk_gemm_tn_atomic"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\sT\s(dr_\w+)$", out, flags=re.M))
+    missing = [n for n in declared() if n not in exported]
+    assert not missing, missing
+    for n in declared():
+        assert getattr(lib, n) is not None
+
+
+def test_status_strings(lib):
+    for code in range(7):
+        assert lib.dr_status_string(code).decode().startswith("DR_")
+    assert lib.dr_version() >= 100
+
+
+def _err(lib):
+    return lib.dr_last_error().decode()
+
+
+def test_combine_rejects_bad_arguments(lib):
+    f = lib.dr_combine
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    # hidden not a multiple of 8 for bf16
+    assert f(FAKE, 1, 10, 100, FAKE, FAKE, 4, 2, FAKE, None, None) == DR_ERR_INVALID_ARGUMENT
+    assert "multiple of 8" in _err(lib)
+    # unknown dtype
+    assert f(FAKE, 7, 10, 128, FAKE, FAKE, 4, 2, FAKE, None, None) == DR_ERR_UNSUPPORTED
+    # k out of range
+    assert f(FAKE, 0, 10, 128, FAKE, FAKE, 4, 65, FAKE, None, None) == DR_ERR_UNSUPPORTED
+    assert f(FAKE, 0, 10, 128, FAKE, FAKE, 4, 0, FAKE, None, None) == DR_ERR_INVALID_ARGUMENT
+    # misaligned rows / out
+    assert f(FAKE + 4, 0, 10, 128, FAKE, FAKE, 4, 2, FAKE, None, None) == DR_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 0, 10, 128, FAKE, FAKE, 4, 2, FAKE + 8, None, None) == DR_ERR_INVALID_ARGUMENT
+    # null pointers with T > 0
+    assert f(FAKE, 0, 10, 128, None, FAKE, 4, 2, FAKE, None, None) == DR_ERR_INVALID_ARGUMENT
+
+
+def test_index_add_rejects_bad_arguments(lib):
+    f = lib.dr_index_add
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                  ctypes.c_void_p]
+    lib.dr_index_add_workspace_size.restype = ctypes.c_size_t
+    lib.dr_index_add_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int64]
+    need = lib.dr_index_add_workspace_size(1000, 64, 128)
+    assert need > 0
+    # workspace too small
+    assert f(FAKE, 64, 128, FAKE, 1, 1000, FAKE, None, None, FAKE, need - 1, None) == DR_ERR_WORKSPACE_TOO_SMALL
+    # only one of perm / seg_offsets
+    assert f(FAKE, 64, 128, FAKE, 1, 1000, FAKE, FAKE, None, FAKE, need, None) == DR_ERR_INVALID_ARGUMENT
+    # hidden not a multiple of 4 for fp32
+    assert f(FAKE, 64, 130, FAKE, 0, 1000, FAKE, None, None, FAKE, need, None) == DR_ERR_INVALID_ARGUMENT
+    # bad sizes
+    assert f(FAKE, 0, 128, FAKE, 1, 1000, FAKE, None, None, FAKE, need, None) == DR_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 64, 128, FAKE, 1, -1, FAKE, None, None, FAKE, need, None) == DR_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 64, 128, FAKE, 1, 1 << 31, FAKE, None, None, FAKE, need, None) == DR_ERR_INVALID_ARGUMENT
+    # misaligned workspace or out
+    assert f(FAKE, 64, 128, FAKE, 1, 1000, FAKE, None, None, FAKE + 4, need, None) == DR_ERR_INVALID_ARGUMENT
+    assert f(FAKE + 4, 64, 128, FAKE, 1, 1000, FAKE, None, None, FAKE, need, None) == DR_ERR_INVALID_ARGUMENT
+
+
+def test_sort_rejects_bad_arguments(lib):
+    f = lib.dr_sort_by_dest
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.dr_sort_workspace_size.restype = ctypes.c_size_t
+    lib.dr_sort_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
+    need = lib.dr_sort_workspace_size(5000, 300, 0)
+    assert f(FAKE, None, 0, 5000, 300, FAKE, FAKE, None, FAKE, need - 1, None) == DR_ERR_WORKSPACE_TOO_SMALL
+    assert f(FAKE, None, 0, 5000, 0, FAKE, FAKE, None, FAKE, need, None) == DR_ERR_INVALID_ARGUMENT
+    assert f(FAKE, FAKE, 0, 5000, 300, FAKE, FAKE, None, FAKE, need, None) == DR_ERR_INVALID_ARGUMENT  # src bound
+    assert f(None, None, 0, 5000, 300, FAKE, FAKE, None, FAKE, need, None) == DR_ERR_INVALID_ARGUMENT
+
+
+def test_splitk_rejects_bad_arguments(lib):
+    f = lib.dr_splitk_gemm_tn
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int32,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    # 10 tokens in 4 splits of 3 tokens: the last split is non-empty (9 < 10) -> accepted shape;
+    # 10 tokens in 6 splits of 2: split 5 starts at 10 -> empty -> rejected
+    assert f(FAKE, FAKE, 10, 64, 24, 6, FAKE, None) == DR_ERR_INVALID_ARGUMENT
+    assert "empty split" in _err(lib)
+    assert f(FAKE, FAKE, 10, 64, 24, 0, FAKE, None) == DR_ERR_INVALID_ARGUMENT
+    assert f(FAKE + 2, FAKE, 16384, 7168, 24, 64, FAKE, None) == DR_ERR_INVALID_ARGUMENT
+    g = lib.dr_splitk_reduce
+    g.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    assert g(FAKE, 0, 100, FAKE, None) == DR_ERR_INVALID_ARGUMENT
+    assert g(FAKE + 4, 64, 100, FAKE, None) == DR_ERR_INVALID_ARGUMENT
+
+
+def test_fingerprint_rejects_bad_arguments(lib):
+    f = lib.dr_fingerprint
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.dr_fingerprint_workspace_size.restype = ctypes.c_size_t
+    need = lib.dr_fingerprint_workspace_size(ctypes.c_int64(100))
+    assert f(FAKE + 4, 100, FAKE, FAKE, need, None) == DR_ERR_INVALID_ARGUMENT
+    assert f(FAKE, 100, FAKE, FAKE, need - 1, None) == DR_ERR_WORKSPACE_TOO_SMALL
+    assert f(FAKE, -1, FAKE, FAKE, need, None) == DR_ERR_INVALID_ARGUMENT
+
+
+def test_launch_params_validation(lib):
+    class P(ctypes.Structure):
+        _fields_ = [("grid_blocks", ctypes.c_int32), ("tile_chunks_log2", ctypes.c_int32),
+                    ("sort_tile_log2", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+    lib.dr_set_launch_params.argtypes = [ctypes.c_void_p]
+    assert lib.dr_set_launch_params(ctypes.byref(P(0, 2, 0, 0))) == DR_ERR_INVALID_ARGUMENT
+    assert lib.dr_set_launch_params(ctypes.byref(P(0, 0, 20, 0))) == DR_ERR_INVALID_ARGUMENT
+    assert lib.dr_set_launch_params(ctypes.byref(P(-1, 0, 0, 0))) == DR_ERR_INVALID_ARGUMENT
+    assert lib.dr_set_launch_params(ctypes.byref(P(0, 0, 0, 1))) == DR_ERR_INVALID_ARGUMENT
+    lib.dr_index_add_workspace_size.restype = ctypes.c_size_t
+    lib.dr_index_add_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int64]
+    default = lib.dr_index_add_workspace_size(100000, 1000, 128)
+    assert lib.dr_set_launch_params(ctypes.byref(P(64, 3, 10, 0))) == DR_OK
+    # smaller tiles need more partial-row space
+    assert lib.dr_index_add_workspace_size(100000, 1000, 128) > default
+    assert lib.dr_set_launch_params(None) == DR_OK
+    assert lib.dr_index_add_workspace_size(100000, 1000, 128) == default
+
+
+def test_kernels_have_no_fused_multiply_add():
+    """The defined order forbids contraction: the gfx950 assembly of every kernel
+    source holds no fused or packed fp32 multiply-add instruction."""
+    from bitwise_deterministic_fp32_amd import build
+    csrc = os.path.join(ROOT, "bitwise_deterministic_fp32_amd", "csrc")
+    bad = re.compile(r"\b(v_fma\w*|v_fmac\w*|v_fmamk\w*|v_fmaak\w*|v_pk_fma\w*|v_pk_add_f32|v_pk_mul_f32|v_mad_f32|v_mac_f32)\b")
+    for src in build.SOURCES:
+        if not src.endswith(".hip"):
+            continue
+        asm = subprocess.run([build.hipcc(), *build.FLAGS, "--cuda-device-only", "-S", os.path.join(csrc, src),
+                              "-o", "-"], capture_output=True, text=True, check=True).stdout
+        found = sorted(set(bad.findall(asm)))
+        assert not found, (src, found)
+        assert "scratch_store" not in asm or src == "splitk.hip", src

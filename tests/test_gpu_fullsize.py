@@ -1,0 +1,110 @@
+"""The five named configurations at full size, in the launch configuration the
+bench times.  Outputs the oracle can compute one by one are sampled (first,
+last, hottest, random and untouched rows).  The sort is compared whole, and
+properties that hold at any size (untouched rows unchanged, repeatability) are
+checked on every row."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_util import assert_bits_equal, dev, dev_bf16, host, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dr():
+    require_gpu()
+    import bitwise_deterministic_fp32_amd as m
+    m.dr_set_launch_params(reset=True)
+    return m
+
+
+def _sample(rng, total, extra=(), count=48):
+    s = set(int(x) for x in rng.choice(total, min(count, total), replace=False))
+    s.update(int(x) for x in extra if 0 <= x < total)
+    s.update([0, total - 1])
+    return np.array(sorted(s), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", ["tiny_moe_combine", "moe_combine"])
+def test_moe_combine_full(dr, name):
+    say(f"{name}: generating inputs")
+    inp = workloads.make(name)
+    T, E, k = inp.T, inp.E, inp.k
+    flat = inp.expert_ids.reshape(-1)
+    say(f"{name}: dispatch sort of {flat.size} keys")
+    perm, seg, inv = dr.dr_sort_by_dest(dev(flat), E)
+    want_perm, want_seg, want_inv = oracle.sort_by_dest(flat, E)
+    assert np.array_equal(host(perm), want_perm)
+    assert np.array_equal(host(seg), want_seg)
+    assert np.array_equal(host(inv), want_inv)
+    row_of = want_inv.reshape(T, k)
+    rows = dev(inp.rows) if inp.rows_dtype == "f32" else dev_bf16(inp.rows)
+    say(f"{name}: combine")
+    out = dr.dr_combine(rows, inv.view(T, k), dev(inp.gates))
+    if T <= 256:
+        tokens = np.arange(T)
+    else:
+        tokens = _sample(np.random.default_rng(2), T)
+    want = oracle.combine(inp.rows, row_of, inp.gates, tokens=tokens)
+    assert_bits_equal(host(out[dev(tokens)]), want, name)
+    fp = dr.fingerprint_value(out)
+    again = dr.dr_combine(rows, inv.view(T, k), dev(inp.gates))
+    assert dr.fingerprint_value(again) == fp
+    if name == "tiny_moe_combine":
+        # the bf16 order example that the tiny configuration carries
+        assert oracle.tree_sum_bf16(np.array([0x3F80, 0x3B40, 0x3B40], np.uint16)) == 0x3F80
+        assert oracle.tree_sum_bf16(np.array([0x3B40, 0x3B40, 0x3F80], np.uint16)) == 0x3F81
+
+
+@pytest.mark.parametrize("name", ["sparse_attn_dk", "embedding_grad"])
+def test_index_add_full(dr, name):
+    say(f"{name}: generating inputs")
+    inp = workloads.make(name)
+    D, H, n = inp.D, inp.H, inp.n
+    index = dev(inp.index)
+    say(f"{name}: sort of {n} keys")
+    perm, seg, _ = dr.dr_sort_by_dest(index, D, want_inv=False)
+    want_perm, want_seg, _ = oracle.sort_by_dest(inp.index, D)
+    assert np.array_equal(host(perm), want_perm)
+    assert np.array_equal(host(seg), want_seg)
+    counts = np.diff(want_seg)
+    say(f"{name}: index_add (max segment {counts.max()}, touched {int((counts > 0).sum())})")
+    out0 = dev(inp.out0)
+    out = out0.clone()
+    _, ws = dr.dr_index_add(out, dev_bf16(inp.src), index)
+    dr.dr_workspace_status(ws)
+    rng = np.random.default_rng(3)
+    hot = np.argsort(-counts, kind="stable")[:8]
+    untouched = np.nonzero(counts == 0)[0]
+    dests = _sample(rng, D, extra=list(hot) + list(untouched[:4]))
+    say(f"{name}: oracle on {dests.size} sampled rows")
+    want = oracle.index_add(inp.out0, inp.src, inp.index, dests=dests)
+    assert_bits_equal(host(out[dev(dests)]), want, name)
+    # every untouched row is bit-identical to its initial value
+    mask = dev(counts == 0)
+    assert torch.equal(out[mask].view(torch.int32), out0[mask].view(torch.int32))
+    # reused plan gives the same bytes
+    out2 = out0.clone()
+    dr.dr_index_add(out2, dev_bf16(inp.src), index, perm=perm, seg_offsets=seg)
+    assert dr.fingerprint_value(out2) == dr.fingerprint_value(out)
+
+
+def test_splitk_full(dr):
+    say("splitk_mhc: generating inputs")
+    inp = workloads.make("splitk_mhc")
+    X, dY = dev_bf16(inp.X), dev_bf16(inp.dY)
+    say("splitk_mhc: partials and reduce")
+    partials = dr.dr_splitk_gemm_tn(X, dY, inp.splits)
+    dW = dr.dr_splitk_reduce(partials)
+    P = host(partials)
+    assert_bits_equal(host(dW), oracle.splitk_reduce(P), "splitk reduce stage")
+    say("splitk_mhc: fp64 reference")
+    exact, A = oracle.splitk_reference(inp.X, inp.dY)
+    err = np.abs(host(dW).astype(np.float64) - exact)
+    assert np.all(err <= 1e-4 * A), float((err / A).max())
+    again = dr.dr_splitk_reduce(dr.dr_splitk_gemm_tn(X, dY, inp.splits))
+    assert dr.fingerprint_value(again) == dr.fingerprint_value(dW)

@@ -1,0 +1,216 @@
+"""Parity of every deterministic entry point with the CPU oracle, element by
+element, on seeded inputs at sizes the oracle finishes in seconds.  The sizes
+span several workgroup tiles and end in ragged tails.  All calls go through the
+C ABI (the ctypes binding)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.gpu_util import assert_bits_equal, dev, dev_bf16, host, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dr():
+    require_gpu()
+    import bitwise_deterministic_fp32_amd as m
+    m.dr_set_launch_params(reset=True)
+    return m
+
+
+# ---------------------------------------------------------------------------
+# sort
+# ---------------------------------------------------------------------------
+SORT_CASES = [
+    # (n, num_dests, with_src, src_bound, distribution)
+    (0, 5, False, 0, "uniform"),
+    (1, 1, False, 0, "uniform"),
+    (1000, 1, False, 0, "uniform"),
+    (4095, 7, False, 0, "uniform"),
+    (100003, 300, False, 0, "zipf"),
+    (100003, 65536, False, 0, "zipf"),
+    (70001, 131072, False, 0, "zipf"),
+    (50000, 256, True, 50000, "uniform"),
+    (30000, 1000, True, 7, "uniform"),  # many duplicate (dest, src) pairs: ties by position
+]
+
+
+@pytest.mark.parametrize("n,D,with_src,src_bound,dist", SORT_CASES)
+def test_sort_matches_oracle(dr, n, D, with_src, src_bound, dist):
+    say(f"sort n={n} D={D} src={with_src}")
+    rng = np.random.default_rng(n + D)
+    if dist == "zipf":
+        dest = np.minimum(rng.zipf(1.2, n) - 1, D - 1).astype(np.int32)
+    else:
+        dest = rng.integers(0, D, n).astype(np.int32)
+    src = rng.integers(0, src_bound, n).astype(np.int32) if with_src else None
+    perm, seg, inv = dr.dr_sort_by_dest(dev(dest), D, None if src is None else dev(src), src_bound)
+    want_perm, want_seg, want_inv = oracle.sort_by_dest(dest, D, src)
+    assert np.array_equal(host(perm), want_perm)
+    assert np.array_equal(host(seg), want_seg)
+    assert np.array_equal(host(inv), want_inv)
+
+
+# ---------------------------------------------------------------------------
+# combine
+# ---------------------------------------------------------------------------
+def _row_of(dr, expert_ids, E):
+    """Expert-major row of each (token, slot): the dispatch sort's inverse permutation."""
+    T, k = expert_ids.shape
+    _, _, inv = dr.dr_sort_by_dest(dev(expert_ids.reshape(-1)), E)
+    return inv.view(T, k)
+
+
+@pytest.mark.parametrize("T,E,k,H,rows_dtype", [
+    (256, 8, 2, 128, "f32"),     # the tiny configuration itself
+    (1000, 64, 8, 1000, "bf16"),  # 2 column slices, the second one ragged
+    (333, 64, 6, 7168, "bf16"),
+    (257, 16, 1, 64, "f32"),
+    (300, 128, 13, 136, "bf16"),  # k > 8: chunk tree
+    (100, 128, 64, 256, "f32"),
+])
+def test_combine_matches_oracle(dr, T, E, k, H, rows_dtype):
+    say(f"combine T={T} E={E} k={k} H={H} {rows_dtype}")
+    inp = workloads.moe_inputs(77 + k, T, E, k, H, rows_dtype, zipf_bias_s=1.2)
+    row_of_dev = _row_of(dr, inp.expert_ids, E)
+    _, _, inv = oracle.sort_by_dest(inp.expert_ids.reshape(-1), E)
+    row_of = inv.reshape(T, k)
+    assert np.array_equal(host(row_of_dev), row_of)
+    rows = dev(inp.rows) if rows_dtype == "f32" else dev_bf16(inp.rows)
+    out = dr.dr_combine(rows, row_of_dev, dev(inp.gates))
+    want = oracle.combine(inp.rows, row_of, inp.gates)
+    assert_bits_equal(host(out), want, "combine")
+
+
+def test_combine_order_example_fp32(dr):
+    """The fp32 analogue of the pages' order example through combine: gates 1, rows [1, x, x]
+    in row order give (1+x)+x; rows [x, x, 1] give (x+x)+1."""
+    x = np.float32(3 * 2.0 ** -26)
+    rows = np.array([[1.0] * 4, [x] * 4, [x] * 4, [x] * 4, [x] * 4, [1.0] * 4], np.float32)
+    row_of = np.array([[0, 1, 2], [3, 4, 5]], np.int32)
+    gates = np.ones((2, 3), np.float32)
+    out = host(dr.dr_combine(dev(rows), dev(row_of), dev(gates)))
+    assert out.view(np.uint32)[0, 0] == 0x3F800000
+    assert out.view(np.uint32)[1, 0] == 0x3F800001
+
+
+# ---------------------------------------------------------------------------
+# index_add
+# ---------------------------------------------------------------------------
+def _index_add_case(seed, n, D, H, src_dtype, dist):
+    rng = np.random.default_rng(seed)
+    if dist == "zipf":
+        index = np.minimum(rng.zipf(1.1, n) - 1, D - 1).astype(np.int32)
+    elif dist == "hot":
+        index = np.where(rng.random(n) < 0.5, 3, rng.integers(0, D, n)).astype(np.int32)
+    else:
+        index = rng.integers(0, D, n).astype(np.int32)
+    if src_dtype == "bf16":
+        src = workloads.normal_bf16(seed, 1, n * H).reshape(n, H)
+    else:
+        src = workloads.normal_f32(seed, 1, n * H).reshape(n, H)
+    out0 = workloads.normal_f32(seed, 2, D * H).reshape(D, H)
+    return index, src, out0
+
+
+@pytest.mark.parametrize("n,D,H,src_dtype,dist", [
+    (0, 10, 128, "bf16", "uniform"),
+    (1, 10, 128, "bf16", "uniform"),
+    (20000, 4096, 128, "bf16", "zipf"),     # long segments: many multi-tile rows
+    (20001, 50, 128, "f32", "hot"),         # one destination with ~10000 rows
+    (3000, 131072, 4096, "bf16", "zipf"),   # embedding-like: mostly singletons
+    (5000, 300, 136, "f32", "uniform"),     # ragged lane group (34 pieces)
+    (4000, 2000, 24, "bf16", "zipf"),       # a row narrower than one lane group
+])
+def test_index_add_matches_oracle(dr, n, D, H, src_dtype, dist):
+    say(f"index_add n={n} D={D} H={H} {src_dtype} {dist}")
+    index, src, out0 = _index_add_case(n + D + H, n, D, H, src_dtype, dist)
+    out = dev(out0.copy())
+    s = dev(src) if src_dtype == "f32" else dev_bf16(src)
+    _, ws = dr.dr_index_add(out, s, dev(index))
+    dr.dr_workspace_status(ws)
+    want = oracle.index_add(out0, src, index)
+    assert_bits_equal(host(out), want, "index_add")
+
+
+def test_index_add_reused_plan(dr):
+    say("index_add reused plan")
+    index, src, out0 = _index_add_case(5, 30000, 1000, 128, "bf16", "zipf")
+    perm, seg, _ = dr.dr_sort_by_dest(dev(index), 1000, want_inv=False)
+    out = dev(out0.copy())
+    _, ws = dr.dr_index_add(out, dev_bf16(src), dev(index), perm=perm, seg_offsets=seg)
+    dr.dr_workspace_status(ws)
+    assert_bits_equal(host(out), oracle.index_add(out0, src, index), "index_add with plan")
+
+
+def test_index_add_order_example_fp32(dr):
+    """old value added last: out0 = 1, contributions [x, x] -> 1 + 2^-23."""
+    x = np.float32(3 * 2.0 ** -26)
+    out = dev(np.ones((2, 4), np.float32))
+    dr.dr_index_add(out, dev(np.full((2, 4), x, np.float32)), dev(np.array([1, 1], np.int32)))
+    o = host(out).view(np.uint32)
+    assert (o[1] == 0x3F800001).all() and (o[0] == 0x3F800000).all()
+
+
+# ---------------------------------------------------------------------------
+# split-K
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("K,M,N,splits", [
+    (1024, 256, 24, 4),
+    (1000, 200, 24, 7),     # ragged splits and a ragged M tile
+    (777, 72, 40, 5),       # two N tiles, ragged
+    (256, 64, 1, 1),
+    (300, 1, 24, 3),
+])
+def test_splitk_matches_oracle(dr, K, M, N, splits):
+    say(f"splitk K={K} M={M} N={N} S={splits}")
+    inp = workloads.splitk_inputs(K + M + N, K, M, N, splits)
+    partials = dr.dr_splitk_gemm_tn(dev_bf16(inp.X), dev_bf16(inp.dY), splits)
+    dW = dr.dr_splitk_reduce(partials)
+    P = host(partials)
+    # reduce stage: bit-exact against the oracle's tree over the same partials
+    assert_bits_equal(host(dW), oracle.splitk_reduce(P), "splitk_reduce")
+    # partials and result within the tolerance of the exact fp64 sums
+    Pexact = oracle.splitk_partials(inp.X, inp.dY, splits)
+    c = -(-K // splits)
+    for s in range(splits):
+        _, A = oracle.splitk_reference(inp.X[s * c:(s + 1) * c], inp.dY[s * c:(s + 1) * c])
+        assert np.all(np.abs(P[s] - Pexact[s]) <= 1e-4 * A + 1e-30), s
+    exact, A = oracle.splitk_reference(inp.X, inp.dY)
+    assert np.all(np.abs(host(dW) - exact) <= 1e-4 * A + 1e-30)
+
+
+def test_splitk_reduce_ragged_counts(dr):
+    for S, count in [(1, 5), (3, 7), (64, 172032), (100, 1001), (9, 4)]:
+        say(f"splitk_reduce S={S} count={count}")
+        P = workloads.normal_f32(S + count, 0, S * count).reshape(S, count)
+        out = dr.dr_splitk_reduce(dev(P))
+        assert_bits_equal(host(out), oracle.splitk_reduce(P), f"splitk_reduce S={S}")
+
+
+# ---------------------------------------------------------------------------
+# fingerprint
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("nbytes", [0, 8, 16, 24, 40, 1000, 4096, 1 << 20, (1 << 22) + 24])
+def test_fingerprint_matches_oracle(dr, nbytes):
+    say(f"fingerprint nbytes={nbytes}")
+    rng = np.random.default_rng(nbytes)
+    data = rng.integers(0, 256, nbytes, dtype=np.uint8)
+    t = dev(data)
+    assert dr.fingerprint_value(t) == oracle.fingerprint(data)
+
+
+def test_fingerprint_odd_lengths_and_dtypes(dr):
+    rng = np.random.default_rng(1)
+    for n in [1, 3, 5, 7, 9, 1001]:  # int16 tensors: 2n bytes, tails of 2, 6, 10, 14, 18 bytes
+        a = rng.integers(-30000, 30000, n).astype(np.int16)
+        assert dr.fingerprint_value(dev(a)) == oracle.fingerprint(a)
+    f = workloads.normal_f32(3, 0, 12345)
+    assert dr.fingerprint_value(dev(f)) == oracle.fingerprint(f)
+    z = np.zeros(4, np.float32)
+    nz = z.copy()
+    nz[2] = -0.0
+    assert dr.fingerprint_value(dev(z)) != dr.fingerprint_value(dev(nz))
