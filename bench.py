@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target duration of the CPU oracle sample")
     ap.add_argument("--json-out", default=None, help="also append the JSON line to this file")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after timing, run a plain fp32 copy kernel of this many MiB (read + write), so that "
+                         "profiler byte counters can be scaled against a known transfer")
     return ap.parse_args()
 
 
@@ -249,6 +252,14 @@ def main():
         import bench_workloads
         res = bench_workloads.run(torch, dr, name, args.steps, args.warmup, args.cpu_seconds,
                                   not args.no_cpu_baseline)
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(2):
+            torch.mul(a, 1.0, out=b)  # elementwise copy: reads and writes n*4 bytes
+        torch.cuda.synchronize()
+        del a, b
     line = {"metric": METRIC, "value": round(res.pop("value"), 2), "unit": "GB/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(res.pop("ms_per_step"), 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",

@@ -1,0 +1,228 @@
+"""bench.py's steps for the index_add and split-K configurations.
+
+sparse_attn_dk / embedding_grad: a step is dr_index_add (stable sort of the
+  contributions by destination, tile plan, ordered segmented reduction,
+  destination update) followed by dr_fingerprint of the destination.  The
+  destination keeps accumulating from step to step; resetting it is not part of
+  the method.  The reused-plan time (sort done once, as when the indices are
+  known a step early) is reported beside it.
+splitk_mhc: a step is dr_splitk_gemm_tn (64 private fp32 partials by bf16
+  MFMA), dr_splitk_reduce in split-id order, and dr_fingerprint of dW.
+"""
+from __future__ import annotations
+
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def _log(msg):
+    import sys
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class _Timer:
+    def __init__(self, torch, phases):
+        self.torch, self.phases, self.events = torch, phases, []
+
+    def step(self):
+        evs = [self.torch.cuda.Event(enable_timing=True) for _ in range(len(self.phases) + 1)]
+        self.events.append(evs)
+        return evs
+
+    def mean_ms(self):
+        self.torch.cuda.synchronize()
+        return {n: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in self.events])) for i, n in enumerate(self.phases)}
+
+
+def _timed(torch, steps, fn):
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        fn()
+    stop.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / steps
+
+
+def run(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
+    if name in ("sparse_attn_dk", "embedding_grad"):
+        return _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu)
+    return _splitk(torch, dr, name, steps, warmup, cpu_seconds, want_cpu)
+
+
+def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
+    import oracle
+    import workloads
+    _log(f"{name}: generating inputs")
+    inp = workloads.make(name)
+    D, H, n = inp.D, inp.H, inp.n
+    index = torch.from_numpy(inp.index).cuda()
+    src = torch.from_numpy(inp.src.view(np.int16)).view(torch.bfloat16).cuda()
+    out = torch.from_numpy(inp.out0).cuda()
+    counts = np.bincount(inp.index, minlength=D)
+    touched = int((counts > 0).sum())
+    red_bytes = n * H * 2 + n * 4 + 2 * touched * H * 4     # contributions, index, RMW of touched rows
+    fp_bytes = D * H * 4
+    step_bytes = red_bytes + fp_bytes
+    ws = torch.empty(dr.dr_index_add_workspace_size(n, D, H), dtype=torch.uint8, device="cuda")
+    fp = torch.empty(1, dtype=torch.int64, device="cuda")
+    ws_fp = torch.empty(dr.dr_fingerprint_workspace_size(fp_bytes), dtype=torch.uint8, device="cuda")
+    timer = _Timer(torch, ["index_add", "fingerprint"])
+
+    def step(evs=None):
+        if evs: evs[0].record()
+        dr.dr_index_add(out, src, index, ws=ws)
+        if evs: evs[1].record()
+        dr.dr_fingerprint(out, out=fp, ws=ws_fp)
+        if evs: evs[2].record()
+
+    for _ in range(warmup):
+        step()
+    dr.dr_workspace_status(ws)
+    _log(f"{name}: timing {steps} steps")
+    ms_step = _timed(torch, steps, lambda: step(timer.step()))
+    ph = timer.mean_ms()
+
+    # reused plan: sort once, then only the plan + ordered reduction each step
+    perm, seg, _ = dr.dr_sort_by_dest(index, D, want_inv=False)
+    ws2 = torch.empty_like(ws)
+    for _ in range(warmup):
+        dr.dr_index_add(out, src, index, perm=perm, seg_offsets=seg, ws=ws2)
+    ms_plan = _timed(torch, steps, lambda: dr.dr_index_add(out, src, index, perm=perm, seg_offsets=seg, ws=ws2))
+    ws_sort = torch.empty(dr.dr_sort_workspace_size(n, D), dtype=torch.uint8, device="cuda")
+    ms_sort = _timed(torch, steps, lambda: dr.dr_sort_by_dest(index, D, perm=perm, seg_offsets=seg, want_inv=False,
+                                                               ws=ws_sort))
+    # atomic baseline on the same destination
+    for _ in range(warmup):
+        dr.dr_index_add_atomic(out, src, index)
+    ms_atomic = _timed(torch, steps, lambda: dr.dr_index_add_atomic(out, src, index))
+
+    det_ms = ph["index_add"]
+    achieved = red_bytes / (det_ms * 1e-3) / 1e9
+    res = {
+        "ms_per_step": ms_step,
+        "value": step_bytes / (ms_step * 1e-3) / 1e9,
+        "config": {"workload": f"{name}: index_add of {n} bf16 rows of width {H} into {D} fp32 rows "
+                               f"({touched} touched, longest segment {int(counts.max())})",
+                   "n": n, "num_dests": D, "hidden": H, "touched_rows": touched,
+                   "step": "dr_index_add (sort + plan + ordered reduce + update) + fingerprint",
+                   "step_algorithmic_bytes": step_bytes},
+        "roofline": {"bound": "hbm", "kernel": "dr_index_add call (sort, plan, segreduce, tilecombine)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": red_bytes, "avg_launch_ms": round(det_ms, 4)},
+        "phases_ms": {k: round(v, 4) for k, v in ph.items()},
+        "reused_plan_ms": round(ms_plan, 4), "sort_only_ms": round(ms_sort, 4),
+        "overhead_vs_atomic": {"deterministic_ms": round(det_ms, 4), "atomic_ms": round(ms_atomic, 4),
+                               "overhead": round(det_ms / ms_atomic - 1, 4),
+                               "overhead_reused_plan": round(ms_plan / ms_atomic - 1, 4)},
+    }
+    if want_cpu:
+        res["cpu_baseline"] = _cpu_index_add(oracle, inp, cpu_seconds)
+    return res
+
+
+def _cpu_index_add(oracle, inp, seconds):
+    """The oracle on the first contributions of the same workload (a prefix of the batch)."""
+    n, H = inp.n, inp.H
+    per_row = H * 2 + 4
+    m = min(n, 4096)
+    t0 = time.perf_counter()
+    oracle.index_add(inp.out0, inp.src[:m], inp.index[:m])
+    dt = max(time.perf_counter() - t0, 1e-6)
+    # the full-destination copy and sort dominate small prefixes; scale linearly as an estimate
+    m2 = int(min(n, m * max(1.0, seconds / dt)))
+    _log(f"cpu baseline: oracle index_add on the first {m2} of {n} contributions")
+    t0 = time.perf_counter()
+    oracle.index_add(inp.out0, inp.src[:m2], inp.index[:m2])
+    el = time.perf_counter() - t0
+    return {"value": round(per_row * m2 / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {m2} of {n} contributions of the same workload, {el:.1f} s", "seconds": round(el, 2)}
+
+
+def _splitk(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
+    import oracle
+    import workloads
+    _log(f"{name}: generating inputs")
+    inp = workloads.make(name)
+    K, M, N, S = inp.K, inp.M, inp.N, inp.splits
+    X = torch.from_numpy(inp.X.view(np.int16)).view(torch.bfloat16).cuda()
+    dY = torch.from_numpy(inp.dY.view(np.int16)).view(torch.bfloat16).cuda()
+    partials = torch.empty(S, M, N, dtype=torch.float32, device="cuda")
+    dW = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    fp = torch.empty(1, dtype=torch.int64, device="cuda")
+    ws_fp = torch.empty(dr.dr_fingerprint_workspace_size(M * N * 4), dtype=torch.uint8, device="cuda")
+    gemm_bytes = K * M * 2 + K * N * 2 + S * M * N * 4
+    red_bytes = S * M * N * 4 + M * N * 4
+    step_bytes = gemm_bytes + red_bytes + M * N * 4
+    flops = 2 * K * M * N
+    timer = _Timer(torch, ["splitk_gemm", "splitk_reduce", "fingerprint"])
+
+    def step(evs=None):
+        if evs: evs[0].record()
+        dr.dr_splitk_gemm_tn(X, dY, S, partials=partials)
+        if evs: evs[1].record()
+        dr.dr_splitk_reduce(partials, out=dW)
+        if evs: evs[2].record()
+        dr.dr_fingerprint(dW, out=fp, ws=ws_fp)
+        if evs: evs[3].record()
+
+    for _ in range(warmup):
+        step()
+    _log(f"{name}: timing {steps} steps")
+    ms_step = _timed(torch, steps, lambda: step(timer.step()))
+    ph = timer.mean_ms()
+    dW_a = torch.empty_like(dW)
+    atimer = _Timer(torch, ["zero", "splitk_gemm_atomic"])
+
+    def astep(evs=None):
+        if evs: evs[0].record()
+        dW_a.zero_()
+        if evs: evs[1].record()
+        dr.dr_splitk_gemm_tn_atomic(X, dY, S, out=dW_a)
+        if evs: evs[2].record()
+
+    for _ in range(warmup):
+        astep()
+    for _ in range(steps):
+        astep(atimer.step())
+    aph = atimer.mean_ms()
+    g_ms = ph["splitk_gemm"]
+    achieved = gemm_bytes / (g_ms * 1e-3) / 1e9
+    det_ms = ph["splitk_gemm"] + ph["splitk_reduce"]
+    at_ms = aph["zero"] + aph["splitk_gemm_atomic"]
+    res = {
+        "ms_per_step": ms_step,
+        "value": step_bytes / (ms_step * 1e-3) / 1e9,
+        "config": {"workload": f"{name}: dW = X^T dY, X bf16 [{K},{M}], dY bf16 [{K},{N}], {S} splits",
+                   "K": K, "M": M, "N": N, "splits": S,
+                   "step": "MFMA partials + ordered split reduce + fingerprint", "step_algorithmic_bytes": step_bytes},
+        "roofline": {"bound": "hbm", "kernel": "splitk_gemm_kernel", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes_per_launch": gemm_bytes, "avg_launch_ms": round(g_ms, 4),
+                     "mfma_tflops": round(flops / (g_ms * 1e-3) / 1e12, 2),
+                     "mfma_frac_of_bf16_peak": round(flops / (g_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 5)},
+        "phases_ms": {k: round(v, 4) for k, v in ph.items()},
+        "overhead_vs_atomic": {"deterministic_ms": round(det_ms, 4), "atomic_zero_plus_gemm_ms": round(at_ms, 4),
+                               "overhead": round(det_ms / at_ms - 1, 4)},
+    }
+    if want_cpu:
+        t0 = time.perf_counter()
+        cols = 64
+        oracle.splitk_reference(inp.X[:, :cols].copy(), inp.dY)
+        dt = time.perf_counter() - t0
+        cols = int(min(M, cols * max(1.0, cpu_seconds / max(dt, 1e-6))))
+        _log(f"cpu baseline: oracle split-K reference on {cols} of {M} columns")
+        Xs = np.ascontiguousarray(inp.X[:, :cols])
+        t0 = time.perf_counter()
+        oracle.splitk_reference(Xs, inp.dY)
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round((K * cols * 2 + K * N * 2) / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+                               "kind": "oracle", "sample": f"{cols} of {M} columns of X (fp64 reference), {el:.1f} s",
+                               "seconds": round(el, 2)}
+    return res

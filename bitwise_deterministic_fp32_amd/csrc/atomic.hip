@@ -11,28 +11,41 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// One wavefront per (contribution row, slice of 64*E columns); lane l owns
+// columns l + 64*e so every load and atomic instruction covers 64 consecutive
+// elements.
 template <dr_dtype DT>
 __global__ __launch_bounds__(kThreads) void index_add_atomic_kernel(float* __restrict__ out, int32_t num_dests,
                                                                     int64_t H, const void* __restrict__ src,
                                                                     int64_t n, const int32_t* __restrict__ index,
-                                                                    int32_t* dev_status, int64_t pieces) {
+                                                                    int32_t* dev_status, int64_t slices) {
     constexpr int E = Vec<DT>::kElems;
     constexpr int kElemBytes = DT == DR_BF16 ? 2 : 4;
-    // the host keeps n * pieces below 2^32
-    const uint32_t g = blockIdx.x * kThreads + threadIdx.x;
-    const uint32_t i = g / (uint32_t)pieces;
-    const int64_t piece = g - i * (uint32_t)pieces;
+    const int lane = threadIdx.x & 63;
+    // the host keeps n * slices below 2^32
+    const uint32_t wave = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    const uint32_t i = wave / (uint32_t)slices;
     if (i >= n) return;
+    const uint32_t slice = wave - i * (uint32_t)slices;
     const int32_t d = index[i];
     if (d < 0 || d >= num_dests) {
-        if (dev_status && piece == 0) atomicOr(dev_status, kStatusIndex);
+        if (dev_status && lane == 0 && slice == 0) atomicOr(dev_status, kStatusIndex);
         return;
     }
+    const char* row = reinterpret_cast<const char*>(src) + (int64_t)i * H * kElemBytes;
+    float* o = out + (int64_t)d * H;
+    const int64_t c0 = (int64_t)slice * 64 * E + lane;
     float v[E];
-    Vec<DT>::widen(load16(reinterpret_cast<const char*>(src) + ((int64_t)i * H + piece * E) * kElemBytes), v);
-    float* o = out + (int64_t)d * H + piece * E;
 #pragma unroll
-    for (int e = 0; e < E; ++e) unsafeAtomicAdd(o + e, v[e]);
+    for (int e = 0; e < E; ++e) {
+        const int64_t c = c0 + 64 * e;
+        v[e] = c < H ? load_elem<DT>(row, c) : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int64_t c = c0 + 64 * e;
+        if (c < H) unsafeAtomicAdd(o + c, v[e]);
+    }
 }
 
 }  // namespace
@@ -40,15 +53,16 @@ __global__ __launch_bounds__(kThreads) void index_add_atomic_kernel(float* __res
 hipError_t launch_index_add_atomic(float* out, int32_t num_dests, int64_t hidden, const void* src, dr_dtype dt,
                                    int64_t n, const int32_t* index, int32_t* dev_status, hipStream_t s) {
     if (n == 0) return hipSuccess;
-    const int64_t pieces = dt == DR_BF16 ? hidden / 8 : hidden / 4;
-    const int64_t threads = n * pieces;
-    const dim3 grid((unsigned)((threads + kThreads - 1) / kThreads));
+    const int64_t per_wave = 64 * (dt == DR_BF16 ? 8 : 4);
+    const int64_t slices = (hidden + per_wave - 1) / per_wave;
+    const int64_t waves = n * slices;
+    const dim3 grid((unsigned)((waves + kThreads / 64 - 1) / (kThreads / 64)));
     if (dt == DR_BF16)
         hipLaunchKernelGGL(index_add_atomic_kernel<DR_BF16>, grid, dim3(kThreads), 0, s, out, num_dests, hidden, src,
-                           n, index, dev_status, pieces);
+                           n, index, dev_status, slices);
     else
         hipLaunchKernelGGL(index_add_atomic_kernel<DR_F32>, grid, dim3(kThreads), 0, s, out, num_dests, hidden, src, n,
-                           index, dev_status, pieces);
+                           index, dev_status, slices);
     return hipGetLastError();
 }
 

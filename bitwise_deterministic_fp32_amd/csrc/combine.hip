@@ -169,10 +169,11 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
     }
 }
 
-// The baseline: one wavefront per (token, slot, column slice), so the k
-// contributions of an output element come from k different wavefronts and are
-// added by hardware fp32 atomics in whatever order they arrive (the
-// scatter_add_ pattern over permuted rows).
+// The baseline: one wavefront per (token, slot, slice of 64*E columns), so
+// the k contributions of an output element come from k different wavefronts
+// and are added by hardware fp32 atomics in whatever order they arrive (the
+// scatter_add_ pattern over permuted rows).  Lane l owns columns l + 64*e, so
+// every load and atomic instruction covers 64 consecutive elements.
 template <dr_dtype DT>
 __global__ __launch_bounds__(kThreads) void combine_atomic_kernel(const void* __restrict__ rows, int64_t num_rows,
                                                                   int64_t H, const int32_t* __restrict__ row_of,
@@ -188,21 +189,28 @@ __global__ __launch_bounds__(kThreads) void combine_atomic_kernel(const void* __
     if (a >= (uint64_t)T * k) return;
     const uint32_t slice = wave - a * (uint32_t)slices;
     const int64_t t = a / (uint32_t)k;
-    const int64_t piece = (int64_t)slice * 64 + lane;
-    if (piece >= H / E) return;
     const int32_t r = row_of[a];
     if (r < 0 || r >= num_rows) {
         if (dev_status && lane == 0 && slice == 0) atomicOr(dev_status, kStatusIndex);
         return;
     }
     const float g = gates[a];
+    const char* row = reinterpret_cast<const char*>(rows) + (int64_t)r * H * kElemBytes;
+    float* o = out + t * H;
+    const int64_t c0 = (int64_t)slice * 64 * E + lane;
     float y[E];
-    Vec<DT>::widen(load16(reinterpret_cast<const char*>(rows) + (int64_t)r * H * kElemBytes + piece * 16), y);
-    float* o = out + t * H + piece * E;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        const float p = g * y[e];
-        unsafeAtomicAdd(o + e, p);
+        const int64_t c = c0 + 64 * e;
+        y[e] = c < H ? load_elem<DT>(row, c) : 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int64_t c = c0 + 64 * e;
+        if (c < H) {
+            const float p = g * y[e];
+            unsafeAtomicAdd(o + c, p);
+        }
     }
 }
 

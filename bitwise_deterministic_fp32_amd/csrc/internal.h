@@ -167,6 +167,15 @@ __device__ __forceinline__ void store16_stream(void* p, u32x4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
+// Column-strided access for the atomic baselines: lane l of a wavefront owns
+// columns c0 + l + 64*e, so each memory or atomic instruction of the wavefront
+// covers 64 consecutive elements (coalesced).
+template <dr_dtype DT>
+__device__ __forceinline__ float load_elem(const void* row, int64_t col) {
+    if (DT == DR_BF16) return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[col] << 16);
+    return reinterpret_cast<const float*>(row)[col];
+}
+
 // -0.0 is an exact identity of IEEE addition (x + -0.0 == x for every x,
 // including +0.0 and -0.0), so padding a tree with it changes no bit.
 __device__ __forceinline__ float neg_zero() { return __uint_as_float(0x80000000u); }
