@@ -79,7 +79,7 @@ std::vector<DigitPass> sort_passes(int32_t num_dests, bool has_src, int32_t src_
     std::vector<DigitPass> passes;
     auto add = [&](bool from_src, int total_bits) {
         if (total_bits <= 0) return;
-        const int np = (total_bits + 7) / 8;
+        const int np = (total_bits + dr::kMaxDigitBits - 1) / dr::kMaxDigitBits;
         const int width = (total_bits + np - 1) / np;
         for (int shift = 0; shift < total_bits; shift += width)
             passes.push_back({from_src, shift, std::min(width, total_bits - shift)});
@@ -100,8 +100,8 @@ struct SortBuffers {
 SortBuffers carve_sort(Carver& c, int64_t n, bool has_src, int tile_log2) {
     SortBuffers b{};
     b.nblocks = (n + ((int64_t)1 << tile_log2) - 1) >> tile_log2;
-    b.hist = c.take<int32_t>(256 * b.nblocks);
-    b.totals = c.take<int32_t>(256);
+    b.hist = c.take<int32_t>((int64_t)(1 << dr::kMaxDigitBits) * b.nblocks);
+    b.totals = c.take<int32_t>(1 << dr::kMaxDigitBits);
     b.dest_a = c.take<int32_t>(n);
     b.dest_b = c.take<int32_t>(n);
     b.val_a = c.take<int32_t>(n);
@@ -224,7 +224,7 @@ Launch launch_config() {
     Launch l;
     l.grid_blocks = g_params.grid_blocks;
     l.tile_chunks_log2 = g_params.tile_chunks_log2 ? g_params.tile_chunks_log2 : kDefaultTileChunksLog2;
-    l.sort_tile_log2 = g_params.sort_tile_log2 ? g_params.sort_tile_log2 : kDefaultSortTileLog2;
+    l.sort_tile_log2 = g_params.sort_tile_log2;
     return l;
 }
 
@@ -288,7 +288,7 @@ size_t dr_sort_workspace_size(int64_t n, int32_t num_dests, int32_t src_id_bound
     (void)num_dests;
     Carver c(nullptr);
     c.take<int32_t>(dr::kStatusBytes / sizeof(int32_t));
-    carve_sort(c, n < 0 ? 0 : n, src_id_bound > 0, dr::launch_config().sort_tile_log2);
+    carve_sort(c, n < 0 ? 0 : n, src_id_bound > 0, dr::launch_config().sort_tile(n));
     return c.off;
 }
 
@@ -302,7 +302,7 @@ dr_status dr_sort_by_dest(const int32_t* dest, const int32_t* src_id, int32_t sr
     if (n > 0 && (!dest || !perm)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: null dest or perm", what);
     if (!seg_offsets || !ws) return fail(DR_ERR_INVALID_ARGUMENT, "%s: null seg_offsets or workspace", what);
     if (!aligned(ws, 16)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: workspace must be 16-byte aligned", what);
-    const int tile_log2 = dr::launch_config().sort_tile_log2;
+    const int tile_log2 = dr::launch_config().sort_tile(n);
     Carver c(ws);
     int32_t* status = c.take<int32_t>(dr::kStatusBytes / sizeof(int32_t));
     const SortBuffers b = carve_sort(c, n, src_id != nullptr, tile_log2);
@@ -362,7 +362,7 @@ size_t dr_index_add_workspace_size(int64_t n, int32_t num_dests, int64_t hidden)
     const dr::Launch lc = dr::launch_config();
     Carver c(nullptr);
     carve_index_add(c, n < 0 ? 0 : n, num_dests < 1 ? 1 : num_dests, hidden < 1 ? 1 : hidden, true,
-                    lc.tile_chunks_log2, lc.sort_tile_log2);
+                    lc.tile_chunks_log2, lc.sort_tile(n));
     return c.off;
 }
 
@@ -391,14 +391,14 @@ dr_status dr_index_add(float* out, int32_t num_dests, int64_t hidden, const void
     }
     Carver c(ws);
     const IndexAddBuffers b = carve_index_add(c, n, num_dests, hidden, sort_inside, lc.tile_chunks_log2,
-                                              lc.sort_tile_log2);
+                                              lc.sort_tile(n));
     if (c.off > ws_bytes)
         return fail(DR_ERR_WORKSPACE_TOO_SMALL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes, c.off);
     DR_TRY_HIP(dr::launch_fill_status(b.status, stream), "status reset launch");
     const int32_t* p = perm;
     const int32_t* seg = seg_offsets;
     if (sort_inside) {
-        st = run_sort(index, nullptr, 0, n, num_dests, b.perm, b.seg, nullptr, b.status, b.sort, lc.sort_tile_log2,
+        st = run_sort(index, nullptr, 0, n, num_dests, b.perm, b.seg, nullptr, b.status, b.sort, lc.sort_tile(n),
                       stream);
         if (st != DR_OK) return st;
         p = b.perm;
@@ -415,7 +415,8 @@ dr_status dr_index_add(float* out, int32_t num_dests, int64_t hidden, const void
     DR_TRY_HIP(dr::launch_segreduce(out, hidden, src, src_dtype, n, p, seg, b.tiles, b.partials, lc.tile_chunks_log2,
                                     b.status, stream),
                "segmented reduce launch");
-    DR_TRY_HIP(dr::launch_tilecombine(out, hidden, b.partials, b.multis, b.status, stream), "tile combine launch");
+    DR_TRY_HIP(dr::launch_tilecombine(out, hidden, b.partials, b.multis, n, lc.tile_chunks_log2, b.status, stream),
+               "tile combine launch");
     return ok();
 }
 
@@ -487,7 +488,7 @@ dr_status dr_splitk_reduce(const float* partials, int32_t splits, int64_t count,
 // ---------------------------------------------------------------------------
 size_t dr_fingerprint_workspace_size(int64_t nbytes) {
     (void)nbytes;
-    return dr::kStatusBytes + 1024 * sizeof(uint64_t);
+    return dr::kStatusBytes + 2048 * sizeof(uint64_t);
 }
 
 dr_status dr_fingerprint(const void* data, int64_t nbytes, uint64_t* out_hash, void* ws, size_t ws_bytes,

@@ -32,8 +32,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
                                                            const float* __restrict__ gates, int64_t T, int k,
                                                            float* __restrict__ out, int32_t* dev_status,
                                                            int64_t slices) {
-    constexpr int E = Vec<DT>::kElems;
+    using PC = Piece<DT>;
+    constexpr int P = PC::kPieces;
     constexpr int kElemBytes = DT == DR_BF16 ? 2 : 4;
+    constexpr int64_t W = 64 * 4 * P;  // columns of one wavefront slice
     const int lane = threadIdx.x & 63;
     // the host keeps T * slices below 2^32
     const uint32_t wave = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
@@ -41,11 +43,17 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
     if (t32 >= T) return;  // whole wavefront
     const int64_t t = t32;
     const uint32_t slice = wave - t32 * (uint32_t)slices;
-    const int64_t pieces = H / E;
-    const int64_t piece = (int64_t)slice * 64 + lane;
-    const bool active = piece < pieces;
-    const int64_t lane_off = (active ? piece : 0) * 16;  // idle lanes read a valid piece
-    float* orow = out + t * H + piece * E;
+    // piece p of this lane: columns col[p] .. col[p]+3; pieces of a wavefront
+    // are 256 columns apart so each load and store instruction is contiguous
+    int64_t col[P], lcol[P];
+    bool active[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        col[p] = (int64_t)slice * W + p * 256 + 4 * lane;
+        active[p] = col[p] < H;
+        lcol[p] = active[p] ? col[p] : 0;  // idle lanes read a valid piece
+    }
+    float* orow = out + t * H;
 
     int32_t rid = INT32_MAX;
     float g = 0.f;
@@ -56,21 +64,17 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
     const bool bad = lane < k && (rid < 0 || rid >= num_rows);
     if (__ballot(bad) != 0) {
         // fail closed: never read outside rows; the token's output is poisoned
-        if (active) {
-            float nan[E];
+        const float nan = __uint_as_float(0x7FC00000u);
 #pragma unroll
-            for (int e = 0; e < E; ++e) nan[e] = __uint_as_float(0x7FC00000u);
-#pragma unroll
-            for (int e = 0; e < E; e += 4)
-                store16(orow + e, u32x4{__float_as_uint(nan[e]), __float_as_uint(nan[e + 1]),
-                                        __float_as_uint(nan[e + 2]), __float_as_uint(nan[e + 3])});
-        }
+        for (int p = 0; p < P; ++p)
+            if (active[p])
+                store16(orow + col[p], u32x4{__float_as_uint(nan), __float_as_uint(nan), __float_as_uint(nan),
+                                             __float_as_uint(nan)});
         if (dev_status && lane == 0 && slice == 0) atomicOr(dev_status, kStatusIndex);
         return;
     }
     const char* rb = reinterpret_cast<const char*>(rows);
     const int64_t row_bytes = H * kElemBytes;
-
 
     // rank of each slot by (row, slot)
     int rank = 0;
@@ -80,12 +84,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
     }
     if (lane >= k) rank = 64 + lane;  // never selected
 
-    float res[E];
+    float res[P][4];
     if (KMAX <= 8) {
-        // one chunk: left to right over the sorted slots
-        // slots past k reload the last slot's row (a cache hit) so that all
-        // loads issue together; they are not added
-        u32x4 raw[8];
+        // one chunk: left to right over the sorted slots.  Slots past k reload
+        // the last slot's row (a cache hit) so that all loads issue together;
+        // they are not added.
+        typename PC::Raw raw[8][P];
         float gq[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
@@ -93,35 +97,40 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
             const int src_lane = __builtin_ctzll(sel);
             const int32_t r = uniform_lane(rid, src_lane);
             gq[q] = __int_as_float(uniform_lane(__float_as_int(g), src_lane));
-            raw[q] = load16_stream(rb + (int64_t)r * row_bytes + lane_off);
+#pragma unroll
+            for (int p = 0; p < P; ++p) raw[q][p] = PC::load_stream(rb + (int64_t)r * row_bytes, lcol[p]);
         }
-        float y[E];
-        Vec<DT>::widen(raw[0], y);
 #pragma unroll
-        for (int e = 0; e < E; ++e) res[e] = gq[0] * y[e];
+        for (int p = 0; p < P; ++p) {
+            float y[4];
+            PC::widen(raw[0][p], y);
 #pragma unroll
-        for (int q = 1; q < 8; ++q) {
-            Vec<DT>::widen(raw[q], y);
+            for (int e = 0; e < 4; ++e) res[p][e] = gq[0] * y[e];
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const float p = gq[q] * y[e];  // rounded product, then the add
-                const float a = res[e] + p;
-                res[e] = q < k ? a : res[e];
+            for (int q = 1; q < 8; ++q) {
+                PC::widen(raw[q][p], y);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float prod = gq[q] * y[e];  // rounded product, then the add
+                    const float a = res[p][e] + prod;
+                    res[p][e] = q < k ? a : res[p][e];
+                }
             }
         }
     } else {
         // up to 8 chunks of 8; chunk sums padded with -0.0 and paired by
         // stride doubling, which is the tree T for any chunk count <= 8
-        float cs[8][E];
+        float cs[8][P][4];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) {
+        for (int c = 0; c < 8; ++c)
 #pragma unroll
-            for (int e = 0; e < E; ++e) cs[c][e] = neg_zero();
-        }
+            for (int p = 0; p < P; ++p)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) cs[c][p][e] = neg_zero();
         const int nchunks = (k + 7) >> 3;
         for (int c = 0; c < nchunks; ++c) {
             const int m = min(8, k - 8 * c);
-            u32x4 raw[8];
+            typename PC::Raw raw[8][P];
             float gq[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
@@ -129,44 +138,53 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
                 const int src_lane = __builtin_ctzll(sel);
                 const int32_t r = uniform_lane(rid, src_lane);
                 gq[j] = __int_as_float(uniform_lane(__float_as_int(g), src_lane));
-                raw[j] = load16_stream(rb + (int64_t)r * row_bytes + lane_off);
+#pragma unroll
+                for (int p = 0; p < P; ++p) raw[j][p] = PC::load_stream(rb + (int64_t)r * row_bytes, lcol[p]);
             }
-            float s[E], y[E];
-            Vec<DT>::widen(raw[0], y);
+            float s[P][4];
 #pragma unroll
-            for (int e = 0; e < E; ++e) s[e] = gq[0] * y[e];
+            for (int p = 0; p < P; ++p) {
+                float y[4];
+                PC::widen(raw[0][p], y);
 #pragma unroll
-            for (int j = 1; j < 8; ++j) {
-                Vec<DT>::widen(raw[j], y);
+                for (int e = 0; e < 4; ++e) s[p][e] = gq[0] * y[e];
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float p = gq[j] * y[e];
-                    const float a = s[e] + p;
-                    s[e] = j < m ? a : s[e];
+                for (int j = 1; j < 8; ++j) {
+                    PC::widen(raw[j][p], y);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float prod = gq[j] * y[e];
+                        const float a = s[p][e] + prod;
+                        s[p][e] = j < m ? a : s[p][e];
+                    }
                 }
             }
 #pragma unroll
             for (int cc = 0; cc < 8; ++cc) {
                 if (cc == c) {
 #pragma unroll
-                    for (int e = 0; e < E; ++e) cs[cc][e] = s[e];
+                    for (int p = 0; p < P; ++p)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) cs[cc][p][e] = s[p][e];
                 }
             }
         }
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const float a = cs[0][e] + cs[1][e], b = cs[2][e] + cs[3][e];
-            const float c2 = cs[4][e] + cs[5][e], d = cs[6][e] + cs[7][e];
-            const float ab = a + b, cd = c2 + d;
-            res[e] = ab + cd;
+        for (int p = 0; p < P; ++p) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float a = cs[0][p][e] + cs[1][p][e], b = cs[2][p][e] + cs[3][p][e];
+                const float c2 = cs[4][p][e] + cs[5][p][e], d = cs[6][p][e] + cs[7][p][e];
+                const float ab = a + b, cd = c2 + d;
+                res[p][e] = ab + cd;
+            }
         }
     }
-    if (active) {
 #pragma unroll
-        for (int e = 0; e < E; e += 4)
-            store16_stream(orow + e, u32x4{__float_as_uint(res[e]), __float_as_uint(res[e + 1]),
-                                           __float_as_uint(res[e + 2]), __float_as_uint(res[e + 3])});
-    }
+    for (int p = 0; p < P; ++p)
+        if (active[p])
+            store16_stream(orow + col[p], u32x4{__float_as_uint(res[p][0]), __float_as_uint(res[p][1]),
+                                                __float_as_uint(res[p][2]), __float_as_uint(res[p][3])});
 }
 
 // The baseline: one wavefront per (token, slot, slice of 64*E columns), so

@@ -1,9 +1,10 @@
-// Byte fingerprint of a tensor: h = mix(nbytes) + sum_i mix(w_i ^ mix(i + 1))
-// mod 2^64, where w_i are the little-endian 64-bit words of the bytes (the last
-// one zero-padded) and mix is SplitMix64's finaliser (Steele, Lea and Flood,
-// OOPSLA 2014).  Runs are compared byte for byte through such fingerprints
-// rather than through printed values (bitwise-determinism interview note, "how
-// to verify").  Integer addition is associative, so the two-stage reduction
+// Byte fingerprint of a tensor: h = mix(nbytes) + sum_i mix(w_i ^ s_i) mod
+// 2^64, where w_i are the little-endian 64-bit words of the bytes (the last one
+// zero-padded), s_i = (i + 1) * 0x9e3779b97f4a7c15 is the (i+1)-th state of a
+// SplitMix64 generator started at 0, and mix is SplitMix64's finaliser
+// (Steele, Lea and Flood, OOPSLA 2014).  Runs are compared byte for byte
+// through such fingerprints rather than through printed values
+// (bitwise-determinism interview note, "how to verify").  Integer addition is associative, so the two-stage reduction
 // below gives the same value for any grid.
 #include "internal.h"
 
@@ -11,7 +12,7 @@ namespace dr {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxBlocks = 1024;
+constexpr int kMaxBlocks = 2048;
 
 __device__ __forceinline__ uint64_t mix64(uint64_t z) {
     z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
@@ -19,7 +20,9 @@ __device__ __forceinline__ uint64_t mix64(uint64_t z) {
     return z ^ (z >> 31);
 }
 
-__device__ __forceinline__ uint64_t term(uint64_t w, int64_t i) { return mix64(w ^ mix64((uint64_t)i + 1)); }
+__device__ __forceinline__ uint64_t term(uint64_t w, int64_t i) {
+    return mix64(w ^ ((uint64_t)(i + 1) * 0x9e3779b97f4a7c15ull));
+}
 
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int off) {
     const uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
@@ -50,7 +53,20 @@ __global__ __launch_bounds__(kThreads) void fp_partial_kernel(const unsigned cha
     const u32x4* d16 = reinterpret_cast<const u32x4*>(data);
     const bool aligned16 = (reinterpret_cast<uintptr_t>(data) & 15) == 0;
     if (aligned16) {
-        for (int64_t p = (int64_t)blockIdx.x * kThreads + threadIdx.x; p < pairs; p += stride) {
+        int64_t p = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+        // four independent 16-byte loads in flight per lane
+        for (; p + 3 * stride < pairs; p += 4 * stride) {
+            u32x4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(d16 + p + u * stride);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t q = p + u * stride;
+                acc += term(((uint64_t)v[u].y << 32) | v[u].x, 2 * q);
+                acc += term(((uint64_t)v[u].w << 32) | v[u].z, 2 * q + 1);
+            }
+        }
+        for (; p < pairs; p += stride) {
             const u32x4 v = __builtin_nontemporal_load(d16 + p);
             acc += term(((uint64_t)v.y << 32) | v.x, 2 * p);
             acc += term(((uint64_t)v.w << 32) | v.z, 2 * p + 1);

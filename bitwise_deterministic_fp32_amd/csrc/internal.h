@@ -23,23 +23,32 @@ constexpr int kWordStatus = 0;
 constexpr int kWordTiles = 1;
 constexpr int kWordMultis = 2;
 
+constexpr int kDefaultTileChunksLog2 = 5;
+constexpr int kMinTileChunksLog2 = 3;
+constexpr int kMaxTileChunksLog2 = 7;
+constexpr int kMinSortTileLog2 = 8;
+constexpr int kMaxSortTileLog2 = 12;
+constexpr int kMaxDigitBits = 9;  // radix digits of up to 9 bits (512 bins)
+// Default keys per sort workgroup: about n / 512, clamped to [2^8, 2^12], so
+// that small sorts still spread over the whole GPU.  A function of n only.
+inline int default_sort_tile_log2(int64_t n) {
+    int t = 0;
+    while (t < 62 && ((int64_t)1 << t) < n) ++t;
+    t -= 9;
+    return t < kMinSortTileLog2 ? kMinSortTileLog2 : (t > kMaxSortTileLog2 ? kMaxSortTileLog2 : t);
+}
+
 // ---------------------------------------------------------------------------
 // Launch configuration in force for the calling thread.
 // ---------------------------------------------------------------------------
 struct Launch {
     int grid_blocks;       // 0 = default
     int tile_chunks_log2;  // resolved value
-    int sort_tile_log2;    // resolved value
+    int sort_tile_log2;    // 0 = default_sort_tile_log2(n)
+    int sort_tile(int64_t n) const { return sort_tile_log2 ? sort_tile_log2 : default_sort_tile_log2(n); }
 };
 Launch launch_config();
 int device_cu_count();  // compute units of the current device (cached)
-
-constexpr int kDefaultTileChunksLog2 = 5;
-constexpr int kMinTileChunksLog2 = 3;
-constexpr int kMaxTileChunksLog2 = 7;
-constexpr int kDefaultSortTileLog2 = 12;
-constexpr int kMinSortTileLog2 = 8;
-constexpr int kMaxSortTileLog2 = 14;
 
 // ---------------------------------------------------------------------------
 // Plan records written by the index_add planner
@@ -100,8 +109,8 @@ hipError_t launch_plan_validate(const int32_t* perm, const int32_t* seg, const i
 hipError_t launch_segreduce(float* out, int64_t hidden, const void* src, dr_dtype src_dtype, int64_t n,
                             const int32_t* perm, const int32_t* seg_offsets, const TileRec* tiles,
                             float* partials, int tile_chunks_log2, int32_t* status, hipStream_t s);
-hipError_t launch_tilecombine(float* out, int64_t hidden, const float* partials, const MultiRec* multis,
-                              int32_t* status, hipStream_t s);
+hipError_t launch_tilecombine(float* out, int64_t hidden, const float* partials, const MultiRec* multis, int64_t n,
+                              int tile_chunks_log2, int32_t* status, hipStream_t s);
 
 // combine
 hipError_t launch_combine(const void* rows, dr_dtype dt, int64_t num_rows, int64_t hidden, const int32_t* row_of,
@@ -155,6 +164,51 @@ struct Vec<DR_F32> {
     __device__ __forceinline__ static void widen(const u32x4& raw, float (&v)[4]) {
         v[0] = __uint_as_float(raw.x); v[1] = __uint_as_float(raw.y);
         v[2] = __uint_as_float(raw.z); v[3] = __uint_as_float(raw.w);
+    }
+};
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// A lane's unit of row data: 4 consecutive columns, widened to fp32.  bf16
+// rows are read as 8-byte pieces and fp32 rows as 16-byte pieces.  A lane owns
+// kPieces pieces kSpan columns apart, so that both the loads and the 16-byte
+// fp32 stores of a lane group cover contiguous bytes.
+template <dr_dtype DT>
+struct Piece;
+
+template <>
+struct Piece<DR_BF16> {
+    static constexpr int kPieces = 2;
+    typedef u32x2 Raw;
+    __device__ __forceinline__ static Raw load(const void* row, int64_t col) {
+        return *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(row) + col);
+    }
+    __device__ __forceinline__ static Raw load_stream(const void* row, int64_t col) {
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(row) + col));
+    }
+    __device__ __forceinline__ static void widen(const Raw& r, float (&v)[4]) {
+        v[0] = __uint_as_float(r.x << 16);
+        v[1] = __uint_as_float(r.x & 0xFFFF0000u);
+        v[2] = __uint_as_float(r.y << 16);
+        v[3] = __uint_as_float(r.y & 0xFFFF0000u);
+    }
+};
+
+template <>
+struct Piece<DR_F32> {
+    static constexpr int kPieces = 1;
+    typedef u32x4 Raw;
+    __device__ __forceinline__ static Raw load(const void* row, int64_t col) {
+        return *reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(row) + col);
+    }
+    __device__ __forceinline__ static Raw load_stream(const void* row, int64_t col) {
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(reinterpret_cast<const float*>(row) + col));
+    }
+    __device__ __forceinline__ static void widen(const Raw& r, float (&v)[4]) {
+        v[0] = __uint_as_float(r.x);
+        v[1] = __uint_as_float(r.y);
+        v[2] = __uint_as_float(r.z);
+        v[3] = __uint_as_float(r.w);
     }
 };
 

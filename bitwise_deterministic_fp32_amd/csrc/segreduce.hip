@@ -28,7 +28,6 @@ namespace {
 constexpr int kPlanThreads = 256;
 constexpr int kPlanWaves = kPlanThreads / 64;
 constexpr int kReduceThreads = 256;
-constexpr int kCombineDepth = 26;  // tiles per destination < 2^26 for n < 2^31 rows
 
 struct TileCount {
     int32_t tiles;   // tiles of the segment
@@ -248,46 +247,37 @@ struct TreeCounter {
     }
 };
 
-template <int E>
-__device__ __forceinline__ void rmw_row(float* dst, const float (&t)[E]) {
-    // out = old + T: the old value is the left operand, added once, last.
-#pragma unroll
-    for (int e = 0; e < E; e += 4) {
-        const u32x4 o = load16(dst + e);
-        u32x4 r;
-        r.x = __float_as_uint(__uint_as_float(o.x) + t[e + 0]);
-        r.y = __float_as_uint(__uint_as_float(o.y) + t[e + 1]);
-        r.z = __float_as_uint(__uint_as_float(o.z) + t[e + 2]);
-        r.w = __float_as_uint(__uint_as_float(o.w) + t[e + 3]);
-        store16(dst + e, r);
-    }
+__device__ __forceinline__ u32x4 add4(const u32x4& old, const float* t) {
+    // out = old + T: the old value is the left operand, added once, last
+    u32x4 r;
+    r.x = __float_as_uint(__uint_as_float(old.x) + t[0]);
+    r.y = __float_as_uint(__uint_as_float(old.y) + t[1]);
+    r.z = __float_as_uint(__uint_as_float(old.z) + t[2]);
+    r.w = __float_as_uint(__uint_as_float(old.w) + t[3]);
+    return r;
 }
 
-template <int E>
-__device__ __forceinline__ void store_row(float* dst, const float (&t)[E]) {
-#pragma unroll
-    for (int e = 0; e < E; e += 4) {
-        u32x4 r;
-        r.x = __float_as_uint(t[e + 0]);
-        r.y = __float_as_uint(t[e + 1]);
-        r.z = __float_as_uint(t[e + 2]);
-        r.w = __float_as_uint(t[e + 3]);
-        store16(dst + e, r);
-    }
+__device__ __forceinline__ u32x4 pack4(const float* t) {
+    return u32x4{__float_as_uint(t[0]), __float_as_uint(t[1]), __float_as_uint(t[2]), __float_as_uint(t[3])};
 }
 
-// Lane groups of GROUP lanes; each lane owns one 16-byte piece of a row.
+// Lane groups of GROUP lanes; each lane owns P pieces of 4 columns, the pieces
+// of a group GROUP*4 columns apart, so that every load and 16-byte store of a
+// group covers contiguous bytes.  One group reduces one (tile, column slice).
 template <dr_dtype DT, int GROUP, int TCLOG>
 __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
-    float* __restrict__ out, int64_t H, const void* __restrict__ src, int64_t n, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ seg, const TileRec* __restrict__ tiles, float* __restrict__ partials,
-    int64_t slices, int64_t pieces_per_row, int32_t* status) {
-    constexpr int E = Vec<DT>::kElems;
+    float* __restrict__ out, int64_t H, const void* __restrict__ src, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ seg, const TileRec* __restrict__ tiles, float* __restrict__ partials, int64_t slices,
+    int32_t* status) {
+    using PC = Piece<DT>;
+    constexpr int P = PC::kPieces;
+    constexpr int E = 4 * P;
     constexpr int kElemBytes = DT == DR_BF16 ? 2 : 4;
+    constexpr int64_t W = (int64_t)GROUP * E;  // columns of one group slice
     if (status[kWordStatus] != 0) return;
     // the host keeps (tile bound) * slices below 2^32, so 32-bit division suffices
     const uint32_t items = (uint32_t)status[kWordTiles] * (uint32_t)slices;
-    const int lane_in_group = threadIdx.x % GROUP;
+    const int lig = threadIdx.x % GROUP;
     const uint32_t group = (blockIdx.x * kReduceThreads + threadIdx.x) / GROUP;
     const uint32_t ngroups = (gridDim.x * kReduceThreads) / GROUP;
     const char* src_bytes = reinterpret_cast<const char*>(src);
@@ -296,74 +286,125 @@ __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
         const uint32_t tile = it / (uint32_t)slices;
         const uint32_t slice = it - tile * (uint32_t)slices;
         const TileRec tr = tiles[tile];
-        const int64_t piece = (int64_t)slice * GROUP + lane_in_group;
-        const bool active = piece < pieces_per_row;
-        const int64_t lane_off = (active ? piece : 0) * 16;  // idle lanes read a valid piece
+        int64_t col[P], lcol[P];
+        bool active[P];
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+            col[p] = (int64_t)slice * W + p * (GROUP * 4) + 4 * lig;
+            active[p] = col[p] < H;
+            lcol[p] = active[p] ? col[p] : 0;  // idle lanes read a valid piece
+        }
         const int64_t r_begin = (int64_t)seg[tr.dest] + ((int64_t)tr.chunk0 << 3);
         const int64_t r_end = min((int64_t)seg[tr.dest + 1], r_begin + ((int64_t)8 << TCLOG));
+        float* orow = out + (int64_t)tr.dest * H;
+        // the destination row, fetched early when this tile updates it in place
+        u32x4 old[P];
+        if (tr.pslot < 0) {
+#pragma unroll
+            for (int p = 0; p < P; ++p) old[p] = load16(orow + lcol[p]);
+        }
         TreeCounter<TCLOG + 1, E> tc;
+        // A short last chunk reloads its last row for the missing slots (a
+        // cache hit) so that all eight loads issue together; those slots are
+        // then not added.
+        int32_t idx[8];
+        {
+            const int m0 = (int)min((int64_t)8, r_end - r_begin);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) idx[j] = perm[r_begin + min(j, m0 - 1)];
+        }
         for (int64_t r0 = r_begin; r0 < r_end; r0 += 8) {
             const int m = (int)min((int64_t)8, r_end - r0);
-            // A short last chunk reloads its last row for the missing slots (a
-            // cache hit) so that all eight loads issue together; those slots
-            // are then not added.
-            int32_t idx[8];
+            typename PC::Raw raw[8][P];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) idx[j] = perm[r0 + min(j, m - 1)];
-            u32x4 raw[8];
+            for (int j = 0; j < 8; ++j)
 #pragma unroll
-            for (int j = 0; j < 8; ++j) raw[j] = load16(src_bytes + (int64_t)idx[j] * row_bytes + lane_off);
+                for (int p = 0; p < P; ++p) raw[j][p] = PC::load(src_bytes + (int64_t)idx[j] * row_bytes, lcol[p]);
+            // the next chunk's source ids are fetched while these rows arrive
+            const int64_t r1 = r0 + 8;
+            if (r1 < r_end) {
+                const int m1 = (int)min((int64_t)8, r_end - r1);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) idx[j] = perm[r1 + min(j, m1 - 1)];
+            }
             float s[E];
-            Vec<DT>::widen(raw[0], s);
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                float v[4];
+                PC::widen(raw[0][p], v);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) s[4 * p + e] = v[e];
+            }
 #pragma unroll
             for (int j = 1; j < 8; ++j) {
-                float v[E];
-                Vec<DT>::widen(raw[j], v);
 #pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const float a = s[e] + v[e];
-                    s[e] = j < m ? a : s[e];
+                for (int p = 0; p < P; ++p) {
+                    float v[4];
+                    PC::widen(raw[j][p], v);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float a = s[4 * p + e] + v[e];
+                        s[4 * p + e] = j < m ? a : s[4 * p + e];
+                    }
                 }
             }
             tc.push(s);
         }
         float t[E];
         tc.fold(t);
-        if (active) {
-            if (tr.pslot < 0) rmw_row<E>(out + (int64_t)tr.dest * H + piece * E, t);
-            else store_row<E>(partials + (int64_t)tr.pslot * H + piece * E, t);
+        if (tr.pslot < 0) {
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+                if (active[p]) store16(orow + col[p], add4(old[p], t + 4 * p));
+        } else {
+            float* prow = partials + (int64_t)tr.pslot * H;
+#pragma unroll
+            for (int p = 0; p < P; ++p)
+                if (active[p]) store16(prow + col[p], pack4(t + 4 * p));
         }
     }
 }
 
-// Merges the partial rows of each multi-tile destination in tile order.
-template <int GROUP>
+// Merges the partial rows of each multi-tile destination in tile order (the
+// tiles are the leaves of the destination's tree at this level).  Eight
+// partial rows are in flight per lane.
+template <int GROUP, int DEPTH>
 __global__ __launch_bounds__(kReduceThreads) void tilecombine_kernel(float* __restrict__ out, int64_t H,
                                                                      const float* __restrict__ partials,
                                                                      const MultiRec* __restrict__ multis,
-                                                                     int64_t slices, int64_t pieces_per_row,
-                                                                     int32_t* status) {
+                                                                     int64_t slices, int32_t* status) {
     if (status[kWordStatus] != 0) return;
     const uint32_t items = (uint32_t)status[kWordMultis] * (uint32_t)slices;
-    const int lane_in_group = threadIdx.x % GROUP;
+    const int lig = threadIdx.x % GROUP;
     const uint32_t group = (blockIdx.x * kReduceThreads + threadIdx.x) / GROUP;
     const uint32_t ngroups = (gridDim.x * kReduceThreads) / GROUP;
     for (uint32_t it = group; it < items; it += ngroups) {
         const uint32_t mi = it / (uint32_t)slices;
         const uint32_t slice = it - mi * (uint32_t)slices;
         const MultiRec mr = multis[mi];
-        const int64_t piece = (int64_t)slice * GROUP + lane_in_group;
-        if (piece >= pieces_per_row) continue;
-        TreeCounter<kCombineDepth, 4> tc;
-        for (int32_t q = 0; q < mr.ntiles; ++q) {
-            const u32x4 raw = load16(partials + (int64_t)(mr.pslot0 + q) * H + piece * 4);
-            float s[4];
-            Vec<DR_F32>::widen(raw, s);
-            tc.push(s);
+        const int64_t col = (int64_t)slice * GROUP * 4 + 4 * lig;
+        if (col >= H) continue;
+        float* orow = out + (int64_t)mr.dest * H;
+        const u32x4 old = load16(orow + col);
+        TreeCounter<DEPTH, 4> tc;  // DEPTH levels hold any count below 2^DEPTH
+        for (int32_t q0 = 0; q0 < mr.ntiles; q0 += 8) {
+            const int m = min(8, mr.ntiles - q0);
+            u32x4 raw[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                raw[j] = load16(partials + (int64_t)(mr.pslot0 + q0 + min(j, m - 1)) * H + col);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (j < m) {
+                    float s[4];
+                    Vec<DR_F32>::widen(raw[j], s);
+                    tc.push(s);
+                }
+            }
         }
         float t[4];
         tc.fold(t);
-        rmw_row<4>(out + (int64_t)mr.dest * H + piece * 4, t);
+        store16(orow + col, add4(old, t));
     }
 }
 
@@ -374,13 +415,13 @@ int group_for(int64_t pieces) {
 }
 
 template <dr_dtype DT, int GROUP>
-hipError_t launch_segreduce_g(dim3 grid, float* out, int64_t H, const void* src, int64_t n, const int32_t* perm,
-                              const int32_t* seg, const TileRec* tiles, float* partials, int tc_log2,
-                              int64_t slices, int64_t pieces, int32_t* status, hipStream_t s) {
+hipError_t launch_segreduce_g(dim3 grid, float* out, int64_t H, const void* src, const int32_t* perm,
+                              const int32_t* seg, const TileRec* tiles, float* partials, int tc_log2, int64_t slices,
+                              int32_t* status, hipStream_t s) {
 #define DR_SEGREDUCE_CASE(TC)                                                                                  \
     case TC:                                                                                                   \
-        hipLaunchKernelGGL((segreduce_kernel<DT, GROUP, TC>), grid, dim3(kReduceThreads), 0, s, out, H, src, n, \
-                           perm, seg, tiles, partials, slices, pieces, status);                                \
+        hipLaunchKernelGGL((segreduce_kernel<DT, GROUP, TC>), grid, dim3(kReduceThreads), 0, s, out, H, src,    \
+                           perm, seg, tiles, partials, slices, status);                                        \
         break;
     switch (tc_log2) {
         DR_SEGREDUCE_CASE(3)
@@ -430,13 +471,14 @@ hipError_t launch_plan_validate(const int32_t* perm, const int32_t* seg, const i
 hipError_t launch_segreduce(float* out, int64_t hidden, const void* src, dr_dtype dt, int64_t n, const int32_t* perm,
                             const int32_t* seg_offsets, const TileRec* tiles, float* partials, int tc_log2,
                             int32_t* status, hipStream_t s) {
-    const int64_t pieces = dt == DR_BF16 ? hidden / 8 : hidden / 4;
-    const int g = group_for(pieces);
-    const int64_t slices = (pieces + g - 1) / g;
+    (void)n;
+    const int64_t lanes = dt == DR_BF16 ? hidden / 8 : hidden / 4;  // lanes needed per row
+    const int g = group_for(lanes);
+    const int64_t slices = (lanes + g - 1) / g;
     const dim3 grid(persistent_grid());
 #define DR_SR(DT, G) \
-    return launch_segreduce_g<DT, G>(grid, out, hidden, src, n, perm, seg_offsets, tiles, partials, tc_log2, slices, \
-                                     pieces, status, s)
+    return launch_segreduce_g<DT, G>(grid, out, hidden, src, perm, seg_offsets, tiles, partials, tc_log2, slices, \
+                                     status, s)
     if (dt == DR_BF16) {
         if (g == 16) DR_SR(DR_BF16, 16);
         if (g == 32) DR_SR(DR_BF16, 32);
@@ -448,21 +490,33 @@ hipError_t launch_segreduce(float* out, int64_t hidden, const void* src, dr_dtyp
 #undef DR_SR
 }
 
-hipError_t launch_tilecombine(float* out, int64_t hidden, const float* partials, const MultiRec* multis,
-                              int32_t* status, hipStream_t s) {
-    const int64_t pieces = hidden / 4;
-    const int g = group_for(pieces);
-    const int64_t slices = (pieces + g - 1) / g;
+hipError_t launch_tilecombine(float* out, int64_t hidden, const float* partials, const MultiRec* multis, int64_t n,
+                              int tc_log2, int32_t* status, hipStream_t s) {
+    const int64_t lanes = hidden / 4;
+    const int g = group_for(lanes);
+    const int64_t slices = (lanes + g - 1) / g;
     const dim3 grid(persistent_grid());
-    if (g == 16)
-        hipLaunchKernelGGL(tilecombine_kernel<16>, grid, dim3(kReduceThreads), 0, s, out, hidden, partials, multis,
-                           slices, pieces, status);
-    else if (g == 32)
-        hipLaunchKernelGGL(tilecombine_kernel<32>, grid, dim3(kReduceThreads), 0, s, out, hidden, partials, multis,
-                           slices, pieces, status);
-    else
-        hipLaunchKernelGGL(tilecombine_kernel<64>, grid, dim3(kReduceThreads), 0, s, out, hidden, partials, multis,
-                           slices, pieces, status);
+    // the most tiles one destination can have, and the counter depth it needs
+    const int64_t max_tiles = n / ((int64_t)8 << tc_log2) + 1;
+    int depth = 1;
+    while (depth < 62 && ((int64_t)1 << depth) <= max_tiles) ++depth;
+#define DR_TC(G, D)                                                                                             \
+    hipLaunchKernelGGL((tilecombine_kernel<G, D>), grid, dim3(kReduceThreads), 0, s, out, hidden, partials, multis, \
+                       slices, status)
+#define DR_TC_DEPTH(G)        \
+    if (depth <= 8) DR_TC(G, 8);  \
+    else if (depth <= 16) DR_TC(G, 16); \
+    else DR_TC(G, 26);
+    if (depth > 26) return hipErrorInvalidValue;
+    if (g == 16) {
+        DR_TC_DEPTH(16)
+    } else if (g == 32) {
+        DR_TC_DEPTH(32)
+    } else {
+        DR_TC_DEPTH(64)
+    }
+#undef DR_TC_DEPTH
+#undef DR_TC
     return hipGetLastError();
 }
 

@@ -8,9 +8,13 @@
 // histogram entries, whose totals do not depend on the order of the
 // increments; no atomic ever claims an output slot.
 //
-// Pass structure (per 2^b-bin digit): histogram per tile of keys, one scan per
-// digit row over the tiles, then a scatter that recomputes each key's stable
-// rank within its tile.
+// Pass structure (per digit of up to 9 bits):
+//   radix_hist:    digit counts of each tile of keys (LDS, wave-aggregated).
+//   radix_scan:    one workgroup per digit scans that digit's counts over the
+//                  tiles; totals per digit.
+//   radix_scatter: recomputes each key's stable rank inside its tile, stages
+//                  the tile in LDS in digit order, then writes each digit's run
+//                  to consecutive output positions (coalesced stores).
 #include "internal.h"
 
 namespace dr {
@@ -18,7 +22,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kMaxBins = 256;
+constexpr int kMaxBins = 1 << kMaxDigitBits;
 
 __device__ __forceinline__ int digit_of(int32_t key, int shift, int bits) {
     return (int)(((uint32_t)key >> shift) & ((1u << bits) - 1u));
@@ -52,6 +56,30 @@ __device__ int32_t block_exclusive_scan(int32_t v, int32_t& total, int32_t* wave
     return before + incl - v;
 }
 
+// Exclusive scan of bins (<= 2 * kThreads) values held in LDS, in place.
+__device__ void scan_bins_in_place(int32_t* a, int bins, int32_t* wave_tot) {
+    // thread t owns bins 2t and 2t+1
+    const int t = threadIdx.x;
+    const int32_t x0 = 2 * t < bins ? a[2 * t] : 0;
+    const int32_t x1 = 2 * t + 1 < bins ? a[2 * t + 1] : 0;
+    int32_t total;
+    const int32_t ex = block_exclusive_scan(x0 + x1, total, wave_tot);
+    if (2 * t < bins) a[2 * t] = ex;
+    if (2 * t + 1 < bins) a[2 * t + 1] = ex + x0;
+    __syncthreads();
+}
+
+// Lanes of the calling wavefront whose digit equals this lane's digit.
+__device__ __forceinline__ uint64_t peers_of(int dg, bool valid, int bits) {
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < bits; ++b) {
+        const bool bit = (dg >> b) & 1;
+        const uint64_t m = __ballot(bit);
+        peers &= bit ? m : ~m;
+    }
+    return peers;
+}
+
 __global__ void fill_status_kernel(int32_t* status) {
     if (threadIdx.x < kStatusBytes / sizeof(int32_t)) status[threadIdx.x] = 0;
 }
@@ -73,16 +101,24 @@ __global__ __launch_bounds__(kThreads) void radix_hist_kernel(SortPass p, int64_
     const int64_t base = (int64_t)blockIdx.x << tile_log2;
     const int64_t end = min(n, base + ((int64_t)1 << tile_log2));
     int my_bad = 0;
-    for (int64_t i = base + threadIdx.x; i < end; i += kThreads) {
-        if (kValidate) {
-            const int32_t dd = dest[i];
-            my_bad |= (dd < 0 || dd >= num_dests);
-            if (src_id) {
-                const int32_t ss = src_id[i];
-                my_bad |= (ss < 0 || ss >= src_bound);
+    for (int64_t r0 = base; r0 < end; r0 += kThreads) {
+        const int64_t i = r0 + threadIdx.x;
+        const bool valid = i < end;
+        int dg = 0;
+        if (valid) {
+            if (kValidate) {
+                const int32_t dd = dest[i];
+                my_bad |= (dd < 0 || dd >= num_dests);
+                if (src_id) {
+                    const int32_t ss = src_id[i];
+                    my_bad |= (ss < 0 || ss >= src_bound);
+                }
             }
+            dg = digit_of(p.digit_src[i], p.shift, p.bits);
         }
-        atomicAdd(&cnt[digit_of(p.digit_src[i], p.shift, p.bits)], 1);
+        // one LDS add per distinct digit of the wavefront
+        const uint64_t peers = peers_of(dg, valid, p.bits);
+        if (valid && __popcll(peers & lanemask_lt()) == 0) atomicAdd(&cnt[dg], (int32_t)__popcll(peers));
     }
     if (my_bad) bad = 1;
     __syncthreads();
@@ -110,74 +146,105 @@ __global__ __launch_bounds__(kThreads) void radix_scan_kernel(int32_t* hist, int
 }
 
 // Stable scatter of one tile.  Keys are visited in rounds of kThreads
-// consecutive keys; within a round a key's rank among equal digits is the
-// count in earlier waves plus the count of lower lanes in its own wave (wave
-// ballots), and rounds are visited in order, so equal digits keep input order.
+// consecutive keys; a key's rank among equal digits of the tile is the count
+// in earlier rounds, plus earlier waves of its round, plus lower lanes of its
+// wave (ballots).  The tile is staged in LDS in (digit, rank) order and each
+// digit's run is then written to consecutive global positions.
+template <int kTileMax>
 __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(SortPass p, int64_t n, int tile_log2,
                                                                  const int32_t* __restrict__ hist, int64_t nblocks,
                                                                  const int32_t* __restrict__ totals,
                                                                  const int32_t* status) {
-    __shared__ int32_t base_s[kMaxBins];
-    __shared__ int32_t running[kMaxBins];
+    __shared__ int32_t gbase[kMaxBins];    // global position of this tile's first key of digit d
+    __shared__ int32_t lbase[kMaxBins];    // position of digit d's run inside the staged tile
+    __shared__ int32_t running[kMaxBins];  // keys of digit d seen in earlier rounds
     __shared__ int32_t wave_cnt[kWaves][kMaxBins];
     __shared__ int32_t wave_off[kWaves][kMaxBins];
     __shared__ int32_t wave_tot[kWaves];
+    __shared__ int32_t st_dest[kTileMax];
+    __shared__ int32_t st_val[kTileMax];
+    __shared__ int32_t st_src[kTileMax];
     if (status[kWordStatus] != 0) return;
     const int tid = threadIdx.x, w = tid >> 6;
     const int bins = 1 << p.bits;
-    int32_t all;
-    const int32_t digit_base = block_exclusive_scan(tid < bins ? totals[tid] : 0, all, wave_tot);
-    if (tid < bins) {
-        base_s[tid] = digit_base + hist[(int64_t)tid * nblocks + blockIdx.x];
-        running[tid] = 0;
-#pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) wave_cnt[ww][tid] = 0;
-    }
-    __syncthreads();
+    const bool key_is_dest = p.digit_src == p.dest_in;
+    const bool carry_src = p.src_out != nullptr;
+    const bool stage_src = carry_src || !key_is_dest;  // source ids are needed in the write-out
     const int64_t base = (int64_t)blockIdx.x << tile_log2;
     const int64_t end = min(n, base + ((int64_t)1 << tile_log2));
-    const bool key_is_dest = p.digit_src == p.dest_in;
+    const int32_t count = (int32_t)(end - base);
+
+    // global bases: digit totals scanned over digits, plus this tile's offset;
+    // this tile's count of digit d is the next tile's offset minus its own
+    for (int d = tid; d < bins; d += kThreads) {
+        const int64_t at = (int64_t)d * nblocks + blockIdx.x;
+        const int32_t off = hist[at];
+        const int32_t next = blockIdx.x + 1 < nblocks ? hist[at + 1] : totals[d];
+        gbase[d] = totals[d];  // scanned below
+        lbase[d] = next - off;
+        running[d] = off;      // temporarily
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) wave_cnt[ww][d] = 0;
+    }
+    __syncthreads();
+    scan_bins_in_place(gbase, bins, wave_tot);
+    scan_bins_in_place(lbase, bins, wave_tot);
+    for (int d = tid; d < bins; d += kThreads) {
+        gbase[d] += running[d];
+        running[d] = 0;
+    }
+    __syncthreads();
+
     for (int64_t r0 = base; r0 < end; r0 += kThreads) {
         const int64_t i = r0 + tid;
         const bool valid = i < end;
-        int32_t key = 0;
+        int32_t key = 0, other = 0;
         int dg = 0;
         if (valid) {
             key = p.digit_src[i];
             dg = digit_of(key, p.shift, p.bits);
+            other = key_is_dest ? (stage_src ? p.src_in[i] : 0) : p.dest_in[i];
         }
-        uint64_t peers = __ballot(valid);
-        for (int b = 0; b < p.bits; ++b) {
-            const bool bit = (dg >> b) & 1;
-            const uint64_t m = __ballot(bit);
-            peers &= bit ? m : ~m;
-        }
+        const uint64_t peers = peers_of(dg, valid, p.bits);
         const int rank = __popcll(peers & lanemask_lt());
         if (valid && rank == 0) wave_cnt[w][dg] = __popcll(peers);
         __syncthreads();
-        if (tid < bins) {
-            int32_t pre = running[tid];
+        for (int d = tid; d < bins; d += kThreads) {
+            int32_t pre = running[d];
 #pragma unroll
             for (int ww = 0; ww < kWaves; ++ww) {
-                const int32_t c = wave_cnt[ww][tid];
-                wave_off[ww][tid] = pre;
+                const int32_t c = wave_cnt[ww][d];
+                wave_off[ww][d] = pre;
                 pre += c;
-                wave_cnt[ww][tid] = 0;
+                wave_cnt[ww][d] = 0;
             }
-            running[tid] = pre;
+            running[d] = pre;
         }
         __syncthreads();
         if (valid) {
-            const int32_t pos = base_s[dg] + wave_off[w][dg] + rank;
-            const int32_t val = p.val_in ? p.val_in[i] : (int32_t)i;
-            p.val_out[pos] = val;
-            if (p.dest_out) p.dest_out[pos] = key_is_dest ? key : p.dest_in[i];
-            if (p.src_out) p.src_out[pos] = key_is_dest ? p.src_in[i] : key;
-            if (p.inv_out) p.inv_out[val] = pos;
+            const int32_t lp = lbase[dg] + wave_off[w][dg] + rank;
+            st_val[lp] = p.val_in ? p.val_in[i] : (int32_t)i;
+            st_dest[lp] = key_is_dest ? key : other;
+            if (stage_src) st_src[lp] = key_is_dest ? other : key;
         }
-        // The next round's counter writes happen before its first barrier, and
-        // wave_off is rewritten only after that barrier, when every thread has
-        // finished reading this round's offsets.
+        // The next round writes wave_cnt before its first barrier and
+        // wave_off only after it, when every thread has finished this round.
+    }
+    __syncthreads();
+    // write-out in staged order: a digit's run goes to consecutive positions
+    for (int32_t j = tid; j < count; j += kThreads) {
+        const int32_t dk = st_dest[j];
+        const int32_t sk = stage_src ? st_src[j] : 0;
+        const int dg = digit_of(key_is_dest ? dk : sk, p.shift, p.bits);
+        const int32_t pos = gbase[dg] + (j - lbase[dg]);
+        const int32_t val = st_val[j];
+        // consistent histograms keep pos and val inside [0, n); the guard keeps
+        // a corrupted workspace from writing outside the outputs
+        if ((uint64_t)(uint32_t)pos >= (uint64_t)n || (uint64_t)(uint32_t)val >= (uint64_t)n) continue;
+        p.val_out[pos] = val;
+        if (p.dest_out) p.dest_out[pos] = dk;
+        if (carry_src) p.src_out[pos] = sk;
+        if (p.inv_out) p.inv_out[val] = pos;
     }
 }
 
@@ -236,8 +303,13 @@ hipError_t launch_radix_scatter(const SortPass& p, int64_t n, int tile_log2, con
                                 const int32_t* totals, const int32_t* status, hipStream_t s) {
     const int64_t nb = tiles_for(n, tile_log2);
     if (nb == 0) return hipSuccess;
-    hipLaunchKernelGGL(radix_scatter_kernel, dim3((unsigned)nb), dim3(kThreads), 0, s, p, n, tile_log2, hist, nb,
-                       totals, status);
+    if (tile_log2 <= 10)
+        hipLaunchKernelGGL(radix_scatter_kernel<1024>, dim3((unsigned)nb), dim3(kThreads), 0, s, p, n, tile_log2,
+                           hist, nb, totals, status);
+    else
+        hipLaunchKernelGGL(radix_scatter_kernel<(1 << kMaxSortTileLog2)>, dim3((unsigned)nb), dim3(kThreads), 0, s,
+                           p, n, tile_log2, hist, nb, totals, status);
+    static_assert(kMaxSortTileLog2 <= 12, "staged tile must fit in LDS");
     return hipGetLastError();
 }
 

@@ -5,9 +5,10 @@
 // only 24.  It must split the contraction, and it keeps one buffer per split,
 // reduced afterwards by a dedicated kernel in split-id order.  Here:
 //   splitk_gemm: one workgroup per (split, 64-row M tile, 32-column N tile).
-//     Tokens of the split are staged through LDS in rows of 64, and each of the
-//     two wavefronts accumulates a 32x32 tile with the bf16 MFMA
-//     v_mfma_f32_32x32x16_bf16, in token order, into fp32.  A partial depends
+//     The split's tokens (up to 256 per stage) are loaded in one phase (16
+//     independent 16-byte loads per thread) and staged in LDS: X row-major, dY
+//     transposed.  Each of the two wavefronts accumulates a 32x32 tile with the
+//     bf16 MFMA v_mfma_f32_32x32x16_bf16, in token order, into fp32.  A partial depends
 //     only on (split, m, n): not on the grid, the M/N tiling or other columns.
 //     The HBM stream is X (read once); the MFMA work is small beside it.
 //   splitk_reduce: out[e] = T(P_0[e], ..., P_{S-1}[e]); chunks of 8 splits left
@@ -22,14 +23,15 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 64;  // M rows per workgroup (two 32-row wavefront tiles)
-constexpr int BN = 32;  // N columns per workgroup
-constexpr int KT = 64;  // tokens per LDS stage
+constexpr int BM = 64;   // M rows per workgroup (two 32-row wavefront tiles)
+constexpr int BN = 32;   // N columns per workgroup
+constexpr int KT = 256;  // tokens per LDS stage (one whole split at the mHC shape)
 constexpr int kGemmThreads = 128;
-// Row strides (in bf16) padded so that the two half-wavefronts of a transposed
-// operand read (rows 8 apart) fall in different LDS banks.
-constexpr int XS = BM + 4;
-constexpr int YS = BN + 4;
+// LDS row strides in bf16, multiples of 8 (16-byte aligned rows).  X is kept
+// row-major [token][m]; dY is kept transposed [n][token] so that a lane's 8
+// consecutive tokens of one column are one 16-byte read.
+constexpr int XS = BM + 8;
+constexpr int YS = KT + 8;
 
 __device__ __forceinline__ __bf16 as_bf16(uint16_t b) { return __builtin_bit_cast(__bf16, b); }
 
@@ -38,54 +40,77 @@ __global__ __launch_bounds__(kGemmThreads) void splitk_gemm_kernel(const uint16_
                                                                    const uint16_t* __restrict__ dY, int64_t K,
                                                                    int64_t M, int64_t N, int64_t kc,
                                                                    float* __restrict__ out) {
-    __shared__ uint16_t xs[KT * XS];
-    __shared__ uint16_t ys[KT * YS];
+    __shared__ __attribute__((aligned(16))) uint16_t xs[KT * XS];
+    __shared__ __attribute__((aligned(16))) uint16_t ys[BN * YS];
     const int s = blockIdx.z;
     const int64_t m0 = (int64_t)blockIdx.x * BM;
     const int64_t n0 = (int64_t)blockIdx.y * BN;
     const int64_t t_begin = (int64_t)s * kc;
     const int64_t t_end = min(K, t_begin + kc);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const bool m_vec_ok = (M % 8) == 0;
+    const bool x_vec = (M % 8) == 0 && m0 + BM <= M;
+    const bool y_vec = (N % 8) == 0 && (reinterpret_cast<uintptr_t>(dY) & 15) == 0;
 
     f32x16 acc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = 0.f;
 
     for (int64_t t0 = t_begin; t0 < t_end; t0 += KT) {
-        // X[t0 .. t0+KT) x [m0 .. m0+BM) -> xs, zero outside the split / matrix
-        for (int p = tid; p < KT * (BM / 8); p += kGemmThreads) {
-            const int r = p / (BM / 8), c8 = (p % (BM / 8)) * 8;
-            const int64_t t = t0 + r, m = m0 + c8;
-            uint16_t v8[8];
-            if (t < t_end && m_vec_ok && m + 8 <= M) {
-                const u32x4 raw = load16(X + t * M + m);
-                v8[0] = raw.x & 0xFFFF; v8[1] = raw.x >> 16;
-                v8[2] = raw.y & 0xFFFF; v8[3] = raw.y >> 16;
-                v8[4] = raw.z & 0xFFFF; v8[5] = raw.z >> 16;
-                v8[6] = raw.w & 0xFFFF; v8[7] = raw.w >> 16;
-            } else {
+        const int rows = (int)min((int64_t)KT, t_end - t0);  // valid tokens in this stage
+        const int ksteps = (rows + 15) / 16;
+        const int rows16 = ksteps * 16;                        // rows the MFMAs read
+        // X[t0 .. t0+rows16) x [m0 .. m0+BM) -> xs; rows past the split are zero
+        if (x_vec) {
+            u32x4 v[KT * (BM / 8) / kGemmThreads];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v8[e] = (t < t_end && m + e < M) ? X[t * M + m + e] : (uint16_t)0;
+            for (int q = 0; q < KT * (BM / 8) / kGemmThreads; ++q) {
+                const int p = tid + q * kGemmThreads;
+                const int r = p / (BM / 8), c8 = (p % (BM / 8)) * 8;
+                v[q] = r < rows ? load16(X + (t0 + r) * M + m0 + c8) : u32x4{0u, 0u, 0u, 0u};
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) xs[r * XS + c8 + e] = v8[e];
+            for (int q = 0; q < KT * (BM / 8) / kGemmThreads; ++q) {
+                const int p = tid + q * kGemmThreads;
+                const int r = p / (BM / 8), c8 = (p % (BM / 8)) * 8;
+                if (r < rows16) *reinterpret_cast<u32x4*>(xs + r * XS + c8) = v[q];
+            }
+        } else {
+            for (int p = tid; p < rows16 * BM; p += kGemmThreads) {
+                const int r = p / BM, c = p % BM;
+                const int64_t m = m0 + c;
+                xs[r * XS + c] = (r < rows && m < M) ? X[(t0 + r) * M + m] : (uint16_t)0;
+            }
         }
-        for (int p = tid; p < KT * BN; p += kGemmThreads) {
-            const int r = p / BN, c = p % BN;
-            const int64_t t = t0 + r, n = n0 + c;
-            ys[r * YS + c] = (t < t_end && n < N) ? dY[t * N + n] : (uint16_t)0;
+        // dY[t0 .. t0+rows16) x [n0 .. n0+BN) -> ys transposed; columns past N are zero
+        if (y_vec) {
+            const int np = (int)((min(N - n0, (int64_t)BN) + 7) / 8);  // 8-column pieces in this N tile
+            for (int p = tid; p < rows16 * np; p += kGemmThreads) {
+                const int r = p / np, c8 = (p % np) * 8;
+                const u32x4 v = r < rows ? load16(dY + (t0 + r) * N + n0 + c8) : u32x4{0u, 0u, 0u, 0u};
+                ys[(c8 + 0) * YS + r] = v.x & 0xFFFF; ys[(c8 + 1) * YS + r] = v.x >> 16;
+                ys[(c8 + 2) * YS + r] = v.y & 0xFFFF; ys[(c8 + 3) * YS + r] = v.y >> 16;
+                ys[(c8 + 4) * YS + r] = v.z & 0xFFFF; ys[(c8 + 5) * YS + r] = v.z >> 16;
+                ys[(c8 + 6) * YS + r] = v.w & 0xFFFF; ys[(c8 + 7) * YS + r] = v.w >> 16;
+            }
+            for (int p = tid; p < (BN - np * 8) * (rows16 / 8); p += kGemmThreads) {
+                const int c = np * 8 + p / (rows16 / 8), r8 = (p % (rows16 / 8)) * 8;
+                *reinterpret_cast<u32x4*>(ys + c * YS + r8) = u32x4{0u, 0u, 0u, 0u};
+            }
+        } else {
+            for (int p = tid; p < rows16 * BN; p += kGemmThreads) {
+                const int r = p / BN, c = p % BN;
+                const int64_t n = n0 + c;
+                ys[c * YS + r] = (r < rows && n < N) ? dY[(t0 + r) * N + n] : (uint16_t)0;
+            }
         }
         __syncthreads();
         const int i = lane & 31, g = lane >> 5;
+        for (int ks = 0; ks < ksteps; ++ks) {
+            const int kk = ks * 16 + 8 * g;
+            bf16x8 a;
 #pragma unroll
-        for (int kk = 0; kk < KT; kk += 16) {
-            bf16x8 a, b;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                a[e] = as_bf16(xs[(kk + 8 * g + e) * XS + wv * 32 + i]);
-                b[e] = as_bf16(ys[(kk + 8 * g + e) * YS + i]);
-            }
+            for (int e = 0; e < 8; ++e) a[e] = as_bf16(xs[(kk + e) * XS + wv * 32 + i]);
+            const bf16x8 b = *reinterpret_cast<const bf16x8*>(ys + i * YS + kk);
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
         }
         __syncthreads();

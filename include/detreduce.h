@@ -81,7 +81,8 @@ typedef struct dr_launch_params {
     int32_t grid_blocks;        /* workgroups of the persistent kernels (index_add reduce and tile
                                    combine, fingerprint), 1 .. 65536 */
     int32_t tile_chunks_log2;   /* index_add tile = 2^m chunks of 8 rows, m in [3, 7] (default 5) */
-    int32_t sort_tile_log2;     /* radix sort keys per workgroup = 2^m, m in [8, 14] (default 12) */
+    int32_t sort_tile_log2;     /* radix sort keys per workgroup = 2^m, m in [8, 12] (default: about
+                                   n / 512, clamped to that range) */
     int32_t reserved;           /* must be 0 */
 } dr_launch_params;
 
@@ -214,10 +215,11 @@ dr_status dr_splitk_reduce(const float* partials, int32_t splits, int64_t count,
  * by printed values (bitwise-determinism interview note, "how to verify":
  * per-step tensor fingerprints compared byte-wise).  The definition is this
  * library's own:
- *   h = mix(nbytes) + sum_i mix(w_i XOR mix(i + 1))   (mod 2^64)
+ *   h = mix(nbytes) + sum_i mix(w_i XOR s_i)   (mod 2^64)
  * w_i is the i-th little-endian 64-bit word of the bytes in logical order,
- * the last word zero-padded.  mix is SplitMix64's finaliser.  +0.0 and -0.0,
- * and NaNs with different payloads, hash differently.
+ * the last word zero-padded; s_i = (i + 1) * 0x9e3779b97f4a7c15 (the states of
+ * a SplitMix64 generator started at 0); mix is SplitMix64's finaliser.  +0.0
+ * and -0.0, and NaNs with different payloads, hash differently.
  *   data       device pointer, 8-byte aligned (or nbytes == 0).
  *   out_hash   OUT device uint64.
  *   ws         >= dr_fingerprint_workspace_size(nbytes) bytes, 16-byte aligned.

@@ -446,13 +446,18 @@ uint64_t oracle_splitmix64_mix(uint64_t z)
     return z ^ (z >> 31);
 }
 
-/* h = mix(nbytes) + sum_i mix(w_i XOR mix(i + 1))  (mod 2^64), where w_i is the
- * i-th little-endian 64-bit word of the bytes in logical order, the last word
- * zero-padded.  Wrapping addition makes the value independent of the order in
- * which the terms are added. */
+/* h = mix(nbytes) + sum_i mix(w_i XOR s_i)  (mod 2^64), where w_i is the i-th
+ * little-endian 64-bit word of the bytes in logical order (the last word
+ * zero-padded) and s_i = (i + 1) * 0x9e3779b97f4a7c15 is the (i+1)-th state of
+ * a SplitMix64 generator started at 0.  For all-zero bytes each term is that
+ * generator's published output.  Wrapping addition makes the value
+ * independent of the order in which the terms are added.
+ * parity unpinned: the composition is this library's convention; its pieces
+ * are pinned by the published SplitMix64 outputs. */
 uint64_t oracle_fingerprint(const void* data, int64_t nbytes)
 {
     const unsigned char* p = (const unsigned char*)data;
+    const uint64_t gamma = 0x9e3779b97f4a7c15ULL;
     uint64_t h = oracle_splitmix64_mix((uint64_t)nbytes);
     int64_t words = (nbytes + 7) / 8;
     for (int64_t i = 0; i < words; ++i) {
@@ -462,7 +467,8 @@ uint64_t oracle_fingerprint(const void* data, int64_t nbytes)
             if (at < nbytes)
                 w |= (uint64_t)p[at] << (8 * b);
         }
-        h += oracle_splitmix64_mix(w ^ oracle_splitmix64_mix((uint64_t)(i + 1)));
+        uint64_t state = (uint64_t)(i + 1) * gamma;
+        h += oracle_splitmix64_mix(w ^ state);
     }
     return h;
 }

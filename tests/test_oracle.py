@@ -457,6 +457,16 @@ def test_splitmix64_published_outputs(golden_dir):
         assert oracle.splitmix64_mix((i * gamma) % 2 ** 64) == int(g[str(i)], 16)
 
 
+def test_fingerprint_of_zero_bytes_is_the_splitmix64_sequence(golden_dir):
+    """All-zero words turn every term into a published SplitMix64 output, so the
+    fingerprint of 8*w zero bytes is mix(8*w) plus the first w outputs."""
+    g = read_golden(os.path.join(golden_dir, "splitmix64_seed0.txt"))
+    outs = [int(g[str(i)], 16) for i in (1, 2, 3)]
+    for w in (1, 2, 3):
+        want = (oracle.splitmix64_mix(8 * w) + sum(outs[:w])) % 2 ** 64
+        assert oracle.fingerprint(np.zeros(8 * w, np.uint8)) == want
+
+
 def test_fingerprint_properties():
     rng = np.random.default_rng(60)
     data = rng.integers(0, 256, 1003, dtype=np.uint8)
