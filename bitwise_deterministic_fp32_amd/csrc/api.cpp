@@ -225,6 +225,7 @@ Launch launch_config() {
     l.grid_blocks = g_params.grid_blocks;
     l.tile_chunks_log2 = g_params.tile_chunks_log2 ? g_params.tile_chunks_log2 : kDefaultTileChunksLog2;
     l.sort_tile_log2 = g_params.sort_tile_log2;
+    l.chunks_in_flight = g_params.chunks_in_flight ? g_params.chunks_in_flight : 2;
     return l;
 }
 
@@ -278,7 +279,8 @@ dr_status dr_set_launch_params(const dr_launch_params* p) {
         (p->sort_tile_log2 < dr::kMinSortTileLog2 || p->sort_tile_log2 > dr::kMaxSortTileLog2))
         return fail(DR_ERR_INVALID_ARGUMENT, "sort_tile_log2 must be 0 or %d..%d", dr::kMinSortTileLog2,
                     dr::kMaxSortTileLog2);
-    if (p->reserved != 0) return fail(DR_ERR_INVALID_ARGUMENT, "reserved must be 0");
+    if (p->chunks_in_flight != 0 && p->chunks_in_flight != 1 && p->chunks_in_flight != 2)
+        return fail(DR_ERR_INVALID_ARGUMENT, "chunks_in_flight must be 0, 1 or 2");
     g_params = *p;
     return ok();
 }
@@ -413,7 +415,7 @@ dr_status dr_index_add(float* out, int32_t num_dests, int64_t hidden, const void
                                      stream),
                "plan write launch");
     DR_TRY_HIP(dr::launch_segreduce(out, hidden, src, src_dtype, n, p, seg, b.tiles, b.partials, lc.tile_chunks_log2,
-                                    b.status, stream),
+                                    lc.chunks_in_flight, b.status, stream),
                "segmented reduce launch");
     DR_TRY_HIP(dr::launch_tilecombine(out, hidden, b.partials, b.multis, n, lc.tile_chunks_log2, b.status, stream),
                "tile combine launch");

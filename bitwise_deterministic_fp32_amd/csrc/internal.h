@@ -45,6 +45,7 @@ struct Launch {
     int grid_blocks;       // 0 = default
     int tile_chunks_log2;  // resolved value
     int sort_tile_log2;    // 0 = default_sort_tile_log2(n)
+    int chunks_in_flight;  // resolved value (1 or 2)
     int sort_tile(int64_t n) const { return sort_tile_log2 ? sort_tile_log2 : default_sort_tile_log2(n); }
 };
 Launch launch_config();
@@ -108,7 +109,8 @@ hipError_t launch_plan_validate(const int32_t* perm, const int32_t* seg, const i
                                 int32_t num_dests, int32_t* status, hipStream_t s);
 hipError_t launch_segreduce(float* out, int64_t hidden, const void* src, dr_dtype src_dtype, int64_t n,
                             const int32_t* perm, const int32_t* seg_offsets, const TileRec* tiles,
-                            float* partials, int tile_chunks_log2, int32_t* status, hipStream_t s);
+                            float* partials, int tile_chunks_log2, int chunks_in_flight, int32_t* status,
+                            hipStream_t s);
 hipError_t launch_tilecombine(float* out, int64_t hidden, const float* partials, const MultiRec* multis, int64_t n,
                               int tile_chunks_log2, int32_t* status, hipStream_t s);
 

@@ -264,7 +264,7 @@ __device__ __forceinline__ u32x4 pack4(const float* t) {
 // Lane groups of GROUP lanes; each lane owns P pieces of 4 columns, the pieces
 // of a group GROUP*4 columns apart, so that every load and 16-byte store of a
 // group covers contiguous bytes.  One group reduces one (tile, column slice).
-template <dr_dtype DT, int GROUP, int TCLOG>
+template <dr_dtype DT, int GROUP, int TCLOG, int CIF>
 __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
     float* __restrict__ out, int64_t H, const void* __restrict__ src, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ seg, const TileRec* __restrict__ tiles, float* __restrict__ partials, int64_t slices,
@@ -304,51 +304,53 @@ __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
             for (int p = 0; p < P; ++p) old[p] = load16(orow + lcol[p]);
         }
         TreeCounter<TCLOG + 1, E> tc;
-        // A short last chunk reloads its last row for the missing slots (a
-        // cache hit) so that all eight loads issue together; those slots are
-        // then not added.
-        int32_t idx[8];
-        {
-            const int m0 = (int)min((int64_t)8, r_end - r_begin);
+        // CIF chunks (8*CIF rows) are loaded at once.  Slots past the tile's
+        // end reload its last row (a cache hit) so that all loads issue
+        // together; those slots are not added.
+        constexpr int R = 8 * CIF;
+        int32_t idx[R];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) idx[j] = perm[r_begin + min(j, m0 - 1)];
-        }
-        for (int64_t r0 = r_begin; r0 < r_end; r0 += 8) {
-            const int m = (int)min((int64_t)8, r_end - r0);
-            typename PC::Raw raw[8][P];
+        for (int j = 0; j < R; ++j) idx[j] = perm[min(r_begin + j, r_end - 1)];
+        for (int64_t r0 = r_begin; r0 < r_end; r0 += R) {
+            typename PC::Raw raw[R][P];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < R; ++j)
 #pragma unroll
                 for (int p = 0; p < P; ++p) raw[j][p] = PC::load(src_bytes + (int64_t)idx[j] * row_bytes, lcol[p]);
-            // the next chunk's source ids are fetched while these rows arrive
-            const int64_t r1 = r0 + 8;
+            // the next rows' source ids are fetched while these rows arrive
+            const int64_t r1 = r0 + R;
             if (r1 < r_end) {
-                const int m1 = (int)min((int64_t)8, r_end - r1);
 #pragma unroll
-                for (int j = 0; j < 8; ++j) idx[j] = perm[r1 + min(j, m1 - 1)];
-            }
-            float s[E];
-#pragma unroll
-            for (int p = 0; p < P; ++p) {
-                float v[4];
-                PC::widen(raw[0][p], v);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) s[4 * p + e] = v[e];
+                for (int j = 0; j < R; ++j) idx[j] = perm[min(r1 + j, r_end - 1)];
             }
 #pragma unroll
-            for (int j = 1; j < 8; ++j) {
+            for (int c = 0; c < CIF; ++c) {
+                const int m = (int)min((int64_t)8, r_end - (r0 + 8 * c));  // rows of chunk c (<= 0: none)
+                if (m > 0) {
+                    float s[E];
 #pragma unroll
-                for (int p = 0; p < P; ++p) {
-                    float v[4];
-                    PC::widen(raw[j][p], v);
+                    for (int p = 0; p < P; ++p) {
+                        float v[4];
+                        PC::widen(raw[8 * c][p], v);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float a = s[4 * p + e] + v[e];
-                        s[4 * p + e] = j < m ? a : s[4 * p + e];
+                        for (int e = 0; e < 4; ++e) s[4 * p + e] = v[e];
                     }
+#pragma unroll
+                    for (int j = 1; j < 8; ++j) {
+#pragma unroll
+                        for (int p = 0; p < P; ++p) {
+                            float v[4];
+                            PC::widen(raw[8 * c + j][p], v);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float a = s[4 * p + e] + v[e];
+                                s[4 * p + e] = j < m ? a : s[4 * p + e];
+                            }
+                        }
+                    }
+                    tc.push(s);
                 }
             }
-            tc.push(s);
         }
         float t[E];
         tc.fold(t);
@@ -414,14 +416,14 @@ int group_for(int64_t pieces) {
     return 64;
 }
 
-template <dr_dtype DT, int GROUP>
+template <dr_dtype DT, int GROUP, int CIF>
 hipError_t launch_segreduce_g(dim3 grid, float* out, int64_t H, const void* src, const int32_t* perm,
                               const int32_t* seg, const TileRec* tiles, float* partials, int tc_log2, int64_t slices,
                               int32_t* status, hipStream_t s) {
 #define DR_SEGREDUCE_CASE(TC)                                                                                  \
     case TC:                                                                                                   \
-        hipLaunchKernelGGL((segreduce_kernel<DT, GROUP, TC>), grid, dim3(kReduceThreads), 0, s, out, H, src,    \
-                           perm, seg, tiles, partials, slices, status);                                        \
+        hipLaunchKernelGGL((segreduce_kernel<DT, GROUP, TC, CIF>), grid, dim3(kReduceThreads), 0, s, out, H,    \
+                           src, perm, seg, tiles, partials, slices, status);                                   \
         break;
     switch (tc_log2) {
         DR_SEGREDUCE_CASE(3)
@@ -469,16 +471,18 @@ hipError_t launch_plan_validate(const int32_t* perm, const int32_t* seg, const i
 }
 
 hipError_t launch_segreduce(float* out, int64_t hidden, const void* src, dr_dtype dt, int64_t n, const int32_t* perm,
-                            const int32_t* seg_offsets, const TileRec* tiles, float* partials, int tc_log2,
+                            const int32_t* seg_offsets, const TileRec* tiles, float* partials, int tc_log2, int cif,
                             int32_t* status, hipStream_t s) {
     (void)n;
     const int64_t lanes = dt == DR_BF16 ? hidden / 8 : hidden / 4;  // lanes needed per row
     const int g = group_for(lanes);
     const int64_t slices = (lanes + g - 1) / g;
     const dim3 grid(persistent_grid());
-#define DR_SR(DT, G) \
-    return launch_segreduce_g<DT, G>(grid, out, hidden, src, perm, seg_offsets, tiles, partials, tc_log2, slices, \
-                                     status, s)
+#define DR_SR(DT, G)                                                                                              \
+    return cif == 1 ? launch_segreduce_g<DT, G, 1>(grid, out, hidden, src, perm, seg_offsets, tiles, partials,    \
+                                                   tc_log2, slices, status, s)                                    \
+                    : launch_segreduce_g<DT, G, 2>(grid, out, hidden, src, perm, seg_offsets, tiles, partials,    \
+                                                   tc_log2, slices, status, s)
     if (dt == DR_BF16) {
         if (g == 16) DR_SR(DR_BF16, 16);
         if (g == 32) DR_SR(DR_BF16, 32);

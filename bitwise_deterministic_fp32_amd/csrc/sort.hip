@@ -84,9 +84,11 @@ __global__ void fill_status_kernel(int32_t* status) {
     if (threadIdx.x < kStatusBytes / sizeof(int32_t)) status[threadIdx.x] = 0;
 }
 
-// Digit histogram of one tile of keys per workgroup.  With kValidate, also
-// checks every dest (and src_id) against its range: the first pass of a sort.
-template <bool kValidate>
+// Digit histogram of one tile of keys per workgroup.  Every thread first
+// loads its ITEMS keys (all loads in flight together), then counts them in
+// LDS; a wavefront whose keys all share one digit adds once.  With kValidate,
+// also checks every dest (and src_id) against its range: the first pass.
+template <bool kValidate, int ITEMS>
 __global__ __launch_bounds__(kThreads) void radix_hist_kernel(SortPass p, int64_t n, int tile_log2, int32_t* hist,
                                                               int64_t nblocks, const int32_t* __restrict__ dest,
                                                               int32_t num_dests, const int32_t* __restrict__ src_id,
@@ -97,28 +99,36 @@ __global__ __launch_bounds__(kThreads) void radix_hist_kernel(SortPass p, int64_
     const int bins = 1 << p.bits;
     for (int d = threadIdx.x; d < bins; d += kThreads) cnt[d] = 0;
     if (threadIdx.x == 0) bad = 0;
-    __syncthreads();
     const int64_t base = (int64_t)blockIdx.x << tile_log2;
     const int64_t end = min(n, base + ((int64_t)1 << tile_log2));
+    int32_t key[ITEMS];
     int my_bad = 0;
-    for (int64_t r0 = base; r0 < end; r0 += kThreads) {
-        const int64_t i = r0 + threadIdx.x;
-        const bool valid = i < end;
-        int dg = 0;
-        if (valid) {
-            if (kValidate) {
-                const int32_t dd = dest[i];
-                my_bad |= (dd < 0 || dd >= num_dests);
-                if (src_id) {
-                    const int32_t ss = src_id[i];
-                    my_bad |= (ss < 0 || ss >= src_bound);
-                }
+#pragma unroll
+    for (int r = 0; r < ITEMS; ++r) {
+        const int64_t i = base + r * kThreads + threadIdx.x;
+        key[r] = i < end ? p.digit_src[i] : 0;
+        if (kValidate && i < end) {
+            const int32_t dd = dest[i];
+            my_bad |= (dd < 0 || dd >= num_dests);
+            if (src_id) {
+                const int32_t ss = src_id[i];
+                my_bad |= (ss < 0 || ss >= src_bound);
             }
-            dg = digit_of(p.digit_src[i], p.shift, p.bits);
         }
-        // one LDS add per distinct digit of the wavefront
-        const uint64_t peers = peers_of(dg, valid, p.bits);
-        if (valid && __popcll(peers & lanemask_lt()) == 0) atomicAdd(&cnt[dg], (int32_t)__popcll(peers));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < ITEMS; ++r) {
+        const int64_t i = base + r * kThreads + threadIdx.x;
+        const bool valid = i < end;
+        const int dg = digit_of(key[r], p.shift, p.bits);
+        const uint64_t vmask = __ballot(valid);
+        const int first = __builtin_amdgcn_readfirstlane(dg);
+        if (vmask != 0 && __ballot(valid && dg == first) == vmask) {
+            if ((threadIdx.x & 63) == __builtin_ctzll(vmask)) atomicAdd(&cnt[first], (int32_t)__popcll(vmask));
+        } else if (valid) {
+            atomicAdd(&cnt[dg], 1);
+        }
     }
     if (my_bad) bad = 1;
     __syncthreads();
@@ -150,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void radix_scan_kernel(int32_t* hist, int
 // in earlier rounds, plus earlier waves of its round, plus lower lanes of its
 // wave (ballots).  The tile is staged in LDS in (digit, rank) order and each
 // digit's run is then written to consecutive global positions.
-template <int kTileMax>
+template <int ITEMS>
 __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(SortPass p, int64_t n, int tile_log2,
                                                                  const int32_t* __restrict__ hist, int64_t nblocks,
                                                                  const int32_t* __restrict__ totals,
@@ -161,9 +171,9 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(SortPass p, int
     __shared__ int32_t wave_cnt[kWaves][kMaxBins];
     __shared__ int32_t wave_off[kWaves][kMaxBins];
     __shared__ int32_t wave_tot[kWaves];
-    __shared__ int32_t st_dest[kTileMax];
-    __shared__ int32_t st_val[kTileMax];
-    __shared__ int32_t st_src[kTileMax];
+    __shared__ int32_t st_dest[ITEMS * kThreads];
+    __shared__ int32_t st_val[ITEMS * kThreads];
+    __shared__ int32_t st_src[ITEMS * kThreads];
     if (status[kWordStatus] != 0) return;
     const int tid = threadIdx.x, w = tid >> 6;
     const int bins = 1 << p.bits;
@@ -174,6 +184,19 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(SortPass p, int
     const int64_t end = min(n, base + ((int64_t)1 << tile_log2));
     const int32_t count = (int32_t)(end - base);
 
+    // this thread's keys, values and carried ids, all loads in flight together
+    int32_t key[ITEMS], other[ITEMS], val[ITEMS];
+#pragma unroll
+    for (int r = 0; r < ITEMS; ++r) {
+        const int64_t i = base + r * kThreads + tid;
+        key[r] = other[r] = 0;
+        val[r] = (int32_t)i;
+        if (i < end) {
+            key[r] = p.digit_src[i];
+            other[r] = key_is_dest ? (stage_src ? p.src_in[i] : 0) : p.dest_in[i];
+            if (p.val_in) val[r] = p.val_in[i];
+        }
+    }
     // global bases: digit totals scanned over digits, plus this tile's offset;
     // this tile's count of digit d is the next tile's offset minus its own
     for (int d = tid; d < bins; d += kThreads) {
@@ -195,16 +218,11 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(SortPass p, int
     }
     __syncthreads();
 
-    for (int64_t r0 = base; r0 < end; r0 += kThreads) {
-        const int64_t i = r0 + tid;
+#pragma unroll
+    for (int r = 0; r < ITEMS; ++r) {
+        const int64_t i = base + r * kThreads + tid;
         const bool valid = i < end;
-        int32_t key = 0, other = 0;
-        int dg = 0;
-        if (valid) {
-            key = p.digit_src[i];
-            dg = digit_of(key, p.shift, p.bits);
-            other = key_is_dest ? (stage_src ? p.src_in[i] : 0) : p.dest_in[i];
-        }
+        const int dg = digit_of(key[r], p.shift, p.bits);
         const uint64_t peers = peers_of(dg, valid, p.bits);
         const int rank = __popcll(peers & lanemask_lt());
         if (valid && rank == 0) wave_cnt[w][dg] = __popcll(peers);
@@ -223,9 +241,9 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(SortPass p, int
         __syncthreads();
         if (valid) {
             const int32_t lp = lbase[dg] + wave_off[w][dg] + rank;
-            st_val[lp] = p.val_in ? p.val_in[i] : (int32_t)i;
-            st_dest[lp] = key_is_dest ? key : other;
-            if (stage_src) st_src[lp] = key_is_dest ? other : key;
+            st_val[lp] = val[r];
+            st_dest[lp] = key_is_dest ? key[r] : other[r];
+            if (stage_src) st_src[lp] = key_is_dest ? other[r] : key[r];
         }
         // The next round writes wave_cnt before its first barrier and
         // wave_off only after it, when every thread has finished this round.
@@ -273,13 +291,25 @@ hipError_t launch_fill_status(int32_t* status_block, hipStream_t s) {
 
 static int64_t tiles_for(int64_t n, int tile_log2) { return (n + ((int64_t)1 << tile_log2) - 1) >> tile_log2; }
 
+#define DR_BY_ITEMS(tile_log2, MACRO) \
+    switch (tile_log2) {                 \
+        case 8: MACRO(1); break;         \
+        case 9: MACRO(2); break;         \
+        case 10: MACRO(4); break;        \
+        case 11: MACRO(8); break;        \
+        default: MACRO(16); break;       \
+    }
+
 hipError_t launch_radix_validate_hist(const int32_t* dest, int32_t num_dests, const int32_t* src_id,
                                       int32_t src_bound, const SortPass& p, int64_t n, int tile_log2,
                                       int32_t* hist, int32_t* status, hipStream_t s) {
     const int64_t nb = tiles_for(n, tile_log2);
     if (nb == 0) return hipSuccess;
-    hipLaunchKernelGGL(radix_hist_kernel<true>, dim3((unsigned)nb), dim3(kThreads), 0, s, p, n, tile_log2, hist,
-                       nb, dest, num_dests, src_id, src_bound, status);
+#define DR_H(IT)                                                                                              \
+    hipLaunchKernelGGL((radix_hist_kernel<true, IT>), dim3((unsigned)nb), dim3(kThreads), 0, s, p, n, tile_log2, \
+                       hist, nb, dest, num_dests, src_id, src_bound, status)
+    DR_BY_ITEMS(tile_log2, DR_H)
+#undef DR_H
     return hipGetLastError();
 }
 
@@ -287,8 +317,11 @@ hipError_t launch_radix_hist(const SortPass& p, int64_t n, int tile_log2, int32_
                              hipStream_t s) {
     const int64_t nb = tiles_for(n, tile_log2);
     if (nb == 0) return hipSuccess;
-    hipLaunchKernelGGL(radix_hist_kernel<false>, dim3((unsigned)nb), dim3(kThreads), 0, s, p, n, tile_log2, hist,
-                       nb, nullptr, 0, nullptr, 0, const_cast<int32_t*>(status));
+#define DR_H(IT)                                                                                               \
+    hipLaunchKernelGGL((radix_hist_kernel<false, IT>), dim3((unsigned)nb), dim3(kThreads), 0, s, p, n, tile_log2, \
+                       hist, nb, nullptr, 0, nullptr, 0, const_cast<int32_t*>(status))
+    DR_BY_ITEMS(tile_log2, DR_H)
+#undef DR_H
     return hipGetLastError();
 }
 
@@ -303,13 +336,12 @@ hipError_t launch_radix_scatter(const SortPass& p, int64_t n, int tile_log2, con
                                 const int32_t* totals, const int32_t* status, hipStream_t s) {
     const int64_t nb = tiles_for(n, tile_log2);
     if (nb == 0) return hipSuccess;
-    if (tile_log2 <= 10)
-        hipLaunchKernelGGL(radix_scatter_kernel<1024>, dim3((unsigned)nb), dim3(kThreads), 0, s, p, n, tile_log2,
-                           hist, nb, totals, status);
-    else
-        hipLaunchKernelGGL(radix_scatter_kernel<(1 << kMaxSortTileLog2)>, dim3((unsigned)nb), dim3(kThreads), 0, s,
-                           p, n, tile_log2, hist, nb, totals, status);
     static_assert(kMaxSortTileLog2 <= 12, "staged tile must fit in LDS");
+#define DR_S(IT)                                                                                           \
+    hipLaunchKernelGGL((radix_scatter_kernel<IT>), dim3((unsigned)nb), dim3(kThreads), 0, s, p, n, tile_log2, \
+                       hist, nb, totals, status)
+    DR_BY_ITEMS(tile_log2, DR_S)
+#undef DR_S
     return hipGetLastError();
 }
 

@@ -160,8 +160,10 @@ def test_index_add_launch_invariance(dr, dk):
             for st in (8, 10, 12):
                 if grid not in (0, 7) and (tc, st) != (5, 12):
                     continue
-                say(f"index_add launch grid={grid} tile=2^{tc} sort_tile=2^{st}")
-                dr.dr_set_launch_params(grid_blocks=grid, tile_chunks_log2=tc, sort_tile_log2=st)
+                cif = 1 + (tc + st + grid) % 2
+                say(f"index_add launch grid={grid} tile=2^{tc} sort_tile=2^{st} chunks_in_flight={cif}")
+                dr.dr_set_launch_params(grid_blocks=grid, tile_chunks_log2=tc, sort_tile_log2=st,
+                                        chunks_in_flight=cif)
                 try:
                     out = out0.clone()
                     dr.dr_index_add(out, src, index)
