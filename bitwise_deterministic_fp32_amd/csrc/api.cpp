@@ -225,7 +225,7 @@ Launch launch_config() {
     l.grid_blocks = g_params.grid_blocks;
     l.tile_chunks_log2 = g_params.tile_chunks_log2 ? g_params.tile_chunks_log2 : kDefaultTileChunksLog2;
     l.sort_tile_log2 = g_params.sort_tile_log2;
-    l.chunks_in_flight = g_params.chunks_in_flight ? g_params.chunks_in_flight : 2;
+    l.chunks_in_flight = g_params.chunks_in_flight ? g_params.chunks_in_flight : 1;
     return l;
 }
 

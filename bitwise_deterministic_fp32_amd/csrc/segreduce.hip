@@ -197,8 +197,8 @@ __global__ void plan_validate_kernel(const int32_t* __restrict__ perm, const int
 // leaves.  push() merges the new leaf with the filled levels below the first
 // empty one (left operand first) and stores it there; fold() combines the
 // remaining subtrees from the right.  This gives T for any leaf count.  The
-// code is branch-free with compile-time level indices, so the levels stay in
-// registers: the number of merges is the count of trailing ones of count.
+// code is branch-free with compile-time level indices (selects, no stores
+// under branches), which keeps the levels in registers.
 template <int DEPTH, int E>
 struct TreeCounter {
     float level[DEPTH][E];
@@ -213,7 +213,7 @@ struct TreeCounter {
     }
 
     __device__ __forceinline__ void push(float (&s)[E]) {
-        const int merges = __builtin_ctz(~count);
+        const int merges = __builtin_ctz(~count);  // carries of this increment
 #pragma unroll
         for (int l = 0; l < DEPTH; ++l) {
 #pragma unroll
@@ -304,19 +304,22 @@ __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
             for (int p = 0; p < P; ++p) old[p] = load16(orow + lcol[p]);
         }
         TreeCounter<TCLOG + 1, E> tc;
-        // CIF chunks (8*CIF rows) are loaded at once.  Slots past the tile's
-        // end reload its last row (a cache hit) so that all loads issue
-        // together; those slots are not added.
+        // CIF chunks (8*CIF rows) are loaded at once; slots past the tile's
+        // end are neither loaded nor added.
         constexpr int R = 8 * CIF;
         int32_t idx[R];
 #pragma unroll
         for (int j = 0; j < R; ++j) idx[j] = perm[min(r_begin + j, r_end - 1)];
         for (int64_t r0 = r_begin; r0 < r_end; r0 += R) {
             typename PC::Raw raw[R][P];
+            const int64_t live = r_end - r0;  // rows of this step that exist
 #pragma unroll
             for (int j = 0; j < R; ++j)
 #pragma unroll
-                for (int p = 0; p < P; ++p) raw[j][p] = PC::load(src_bytes + (int64_t)idx[j] * row_bytes, lcol[p]);
+                for (int p = 0; p < P; ++p) {
+                    raw[j][p] = typename PC::Raw{};
+                    if (j < live) raw[j][p] = PC::load(src_bytes + (int64_t)idx[j] * row_bytes, lcol[p]);
+                }
             // the next rows' source ids are fetched while these rows arrive
             const int64_t r1 = r0 + R;
             if (r1 < r_end) {
@@ -335,16 +338,29 @@ __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
 #pragma unroll
                         for (int e = 0; e < 4; ++e) s[4 * p + e] = v[e];
                     }
+                    if (m == 8) {
 #pragma unroll
-                    for (int j = 1; j < 8; ++j) {
+                        for (int j = 1; j < 8; ++j) {
 #pragma unroll
-                        for (int p = 0; p < P; ++p) {
-                            float v[4];
-                            PC::widen(raw[8 * c + j][p], v);
+                            for (int p = 0; p < P; ++p) {
+                                float v[4];
+                                PC::widen(raw[8 * c + j][p], v);
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const float a = s[4 * p + e] + v[e];
-                                s[4 * p + e] = j < m ? a : s[4 * p + e];
+                                for (int e = 0; e < 4; ++e) s[4 * p + e] = s[4 * p + e] + v[e];
+                            }
+                        }
+                    } else {
+#pragma unroll
+                        for (int j = 1; j < 8; ++j) {
+#pragma unroll
+                            for (int p = 0; p < P; ++p) {
+                                float v[4];
+                                PC::widen(raw[8 * c + j][p], v);
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    const float a = s[4 * p + e] + v[e];
+                                    s[4 * p + e] = j < m ? a : s[4 * p + e];
+                                }
                             }
                         }
                     }
@@ -441,7 +457,7 @@ hipError_t launch_segreduce_g(dim3 grid, float* out, int64_t H, const void* src,
 unsigned persistent_grid() {
     const Launch lc = launch_config();
     if (lc.grid_blocks > 0) return (unsigned)lc.grid_blocks;
-    return (unsigned)(device_cu_count() * 8);
+    return (unsigned)(device_cu_count() * 16);
 }
 
 }  // namespace

@@ -84,7 +84,7 @@ typedef struct dr_launch_params {
     int32_t sort_tile_log2;     /* radix sort keys per workgroup = 2^m, m in [8, 12] (default: about
                                    n / 512, clamped to that range) */
     int32_t chunks_in_flight;   /* index_add: chunks of 8 rows loaded at once per lane group, 1 or 2
-                                   (default 2) */
+                                   (default 1) */
 } dr_launch_params;
 
 /* Human-readable name of a status code.  Never NULL. */
