@@ -121,24 +121,22 @@ def bench_moe(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
     ws_sort = torch.empty(dr.dr_sort_workspace_size(n, E), dtype=torch.uint8, device="cuda")
     out = torch.empty(T, H, dtype=torch.float32, device="cuda")
     fp = torch.empty(1, dtype=torch.int64, device="cuda")
-    ws_fp = torch.empty(dr.dr_fingerprint_workspace_size(out.numel() * 4), dtype=torch.uint8, device="cuda")
+    ws_cfp = torch.empty(dr.dr_combine_fingerprinted_workspace_size(rows.dtype, H, T), dtype=torch.uint8,
+                         device="cuda")
     row_of = inv.view(T, k)
 
     combine_bytes = n * H * elem + n * 4 + n * 4 + T * H * 4
     sort_bytes = n * 4 * 3 + (E + 1) * 4
-    fp_bytes = T * H * 4
-    step_bytes = combine_bytes + sort_bytes + fp_bytes
+    step_bytes = combine_bytes + sort_bytes  # the fingerprint is taken as the output is stored
 
-    timer = Timer(torch, ["sort", "combine", "fingerprint"])
+    timer = Timer(torch, ["sort", "combine_fingerprinted"])
 
     def step(evs=None):
         if evs: evs[0].record()
         dr.dr_sort_by_dest(keys, E, perm=perm, seg_offsets=seg, inv_perm=inv, ws=ws_sort)
         if evs: evs[1].record()
-        dr.dr_combine(rows, row_of, gates, out=out)
+        dr.dr_combine_fingerprinted(rows, row_of, gates, out=out, out_hash=fp, ws=ws_cfp)
         if evs: evs[2].record()
-        dr.dr_fingerprint(out, out=fp, ws=ws_fp)
-        if evs: evs[3].record()
 
     log(f"{name}: warmup {warmup}")
     for _ in range(warmup):
@@ -157,6 +155,19 @@ def bench_moe(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
     wall_ms = (time.perf_counter() - t0) * 1e3 / steps
     ms_per_step = start.elapsed_time(stop) / steps
     phases = timer.mean_ms()
+    fps.add(int(fp.item()))
+
+    # the same combine without the fused fingerprint, and the separate fingerprint pass
+    ws_fp = torch.empty(dr.dr_fingerprint_workspace_size(out.numel() * 4), dtype=torch.uint8, device="cuda")
+    ptimer = Timer(torch, ["combine", "fingerprint"])
+    for i in range(warmup + steps):
+        evs = ptimer.step() if i >= warmup else None
+        if evs: evs[0].record()
+        dr.dr_combine(rows, row_of, gates, out=out)
+        if evs: evs[1].record()
+        dr.dr_fingerprint(out, out=fp, ws=ws_fp)
+        if evs: evs[2].record()
+    plain = ptimer.mean_ms()
     fps.add(int(fp.item()))
 
     # atomic baseline: zeroing (scatter_add_ needs a zeroed output) + atomic combine
@@ -183,7 +194,7 @@ def bench_moe(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
         fps.add(int(fp.item()))
     assert len(fps) == 1, "combine step output changed between replays"
 
-    comb_ms = phases["combine"]
+    comb_ms = phases["combine_fingerprinted"]
     achieved = combine_bytes / (comb_ms * 1e-3) / 1e9
     digest = source_digest("combine.hip", "internal.h")
     result = {
@@ -192,13 +203,15 @@ def bench_moe(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
         "config": {"workload": f"{name}: MoE unpermute/combine T={T} tokens, {E} experts, top-{k}, hidden {H}, "
                                f"{inp.rows_dtype} expert outputs, fp32 out",
                    "tokens": T, "experts": E, "top_k": k, "hidden": H,
-                   "step": "dispatch sort + ordered combine + output fingerprint",
+                   "step": "dispatch sort + ordered combine with the output fingerprint taken as it is stored",
                    "step_algorithmic_bytes": step_bytes},
-        "roofline": {"bound": "hbm", "kernel": "combine_kernel", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": "combine_kernel (fingerprinting) + its 1-workgroup final sum",
+                     "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("combine_kernel", name, digest),
+                     "traffic": measured_traffic("combine_kernel_fp", name, digest),
                      "algorithmic_bytes_per_launch": combine_bytes, "avg_launch_ms": round(comb_ms, 4)},
         "phases_ms": {k2: round(v, 4) for k2, v in phases.items()},
+        "unfused_ms": {k2: round(v, 4) for k2, v in plain.items()},
         "overhead_vs_atomic": {
             "deterministic_combine_ms": round(comb_ms, 4),
             "atomic_zero_plus_combine_ms": round(aph["zero"] + aph["combine_atomic"], 4),

@@ -19,7 +19,7 @@ __all__ = [
     "DetReduceError", "LIB_PATH", "lib", "declared_functions",
     "dr_status_string", "dr_last_error", "dr_version", "dr_set_launch_params",
     "dr_sort_workspace_size", "dr_sort_by_dest",
-    "dr_combine", "dr_combine_atomic",
+    "dr_combine", "dr_combine_atomic", "dr_combine_fingerprinted_workspace_size", "dr_combine_fingerprinted",
     "dr_index_add_workspace_size", "dr_index_add", "dr_index_add_atomic",
     "dr_splitk_gemm_tn", "dr_splitk_gemm_tn_atomic", "dr_splitk_reduce",
     "dr_fingerprint_workspace_size", "dr_fingerprint", "fingerprint_value",
@@ -42,7 +42,7 @@ class DetReduceError(RuntimeError):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run `python -m bitwise_deterministic_fp32_amd.build`")
+        raise ImportError(f"{LIB_PATH} is not built; run `python bitwise_deterministic_fp32_amd/build.py`")
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     sig = {
@@ -54,6 +54,9 @@ def _load() -> ctypes.CDLL:
         "dr_sort_by_dest": ([vp, vp, i32, i64, i32, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "dr_combine": ([vp, ctypes.c_int, i64, i64, vp, vp, i64, i32, vp, vp, vp], ctypes.c_int),
         "dr_combine_atomic": ([vp, ctypes.c_int, i64, i64, vp, vp, i64, i32, vp, vp, vp], ctypes.c_int),
+        "dr_combine_fingerprinted_workspace_size": ([ctypes.c_int, i64, i64], sz),
+        "dr_combine_fingerprinted": ([vp, ctypes.c_int, i64, i64, vp, vp, i64, i32, vp, vp, vp, sz, vp, vp],
+                                     ctypes.c_int),
         "dr_index_add_workspace_size": ([i64, i32, i64], sz),
         "dr_index_add": ([vp, i32, i64, vp, ctypes.c_int, i64, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "dr_index_add_atomic": ([vp, i32, i64, vp, ctypes.c_int, i64, vp, vp, vp], ctypes.c_int),
@@ -182,6 +185,23 @@ def dr_combine(rows, row_of, gates, *, out=None, dev_status=None, stream=None):
     _check(lib.dr_combine(_p(rows), _DTYPES[rows.dtype], R, H, _p(row_of), _p(gates), T, k, _p(out),
                           _p(dev_status), _stream(stream)), "dr_combine")
     return out
+
+
+def dr_combine_fingerprinted_workspace_size(rows_dtype, hidden: int, T: int) -> int:
+    return int(lib.dr_combine_fingerprinted_workspace_size(_DTYPES[rows_dtype], hidden, T))
+
+
+def dr_combine_fingerprinted(rows, row_of, gates, *, out=None, out_hash=None, ws=None, dev_status=None, stream=None):
+    """dr_combine plus the fingerprint of its output, hashed as it is stored.  Returns (out, out_hash)."""
+    R, H, T, k = _combine_args(rows, row_of, gates)
+    out = out if out is not None else torch.empty(T, H, dtype=torch.float32, device=rows.device)
+    _dev(out, "out", (torch.float32,))
+    out_hash = out_hash if out_hash is not None else torch.empty(1, dtype=torch.int64, device=rows.device)
+    ws = ws if ws is not None else _workspace(dr_combine_fingerprinted_workspace_size(rows.dtype, H, T), rows.device)
+    _check(lib.dr_combine_fingerprinted(_p(rows), _DTYPES[rows.dtype], R, H, _p(row_of), _p(gates), T, k, _p(out),
+                                        _p(out_hash), _p(ws), ws.numel(), _p(dev_status), _stream(stream)),
+           "dr_combine_fingerprinted")
+    return out, out_hash
 
 
 def dr_combine_atomic(rows, row_of, gates, *, out, dev_status=None, stream=None):

@@ -1,7 +1,8 @@
 """Builds libdetreduce.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
 
-Run as ``python -m bitwise_deterministic_fp32_amd.build``.  The library is
-written next to this file; object files go to ``_build/``.
+Run as ``python bitwise_deterministic_fp32_amd/build.py`` (as a script, so
+that the package and its library are not loaded).  The library is written next
+to this file; object files go to ``_build/``.
 """
 from __future__ import annotations
 

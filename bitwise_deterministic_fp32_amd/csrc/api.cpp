@@ -335,8 +335,46 @@ dr_status dr_combine(const void* rows, dr_dtype rows_dtype, int64_t num_rows, in
     if (T * ((hidden / elems16(rows_dtype) + 63) / 64) >= ((int64_t)1 << 32))
         return fail(DR_ERR_UNSUPPORTED, "%s: T * column slices must be below 2^32", what);
     DR_TRY_HIP(dr::launch_combine(rows, rows_dtype, num_rows, hidden, row_of, gates, T, k, out, dev_status, false,
-                                  stream),
+                                  nullptr, stream),
                "combine launch");
+    return ok();
+}
+
+size_t dr_combine_fingerprinted_workspace_size(dr_dtype rows_dtype, int64_t hidden, int64_t T) {
+    if (hidden < 1 || T < 0) return dr::kStatusBytes;
+    return dr::kStatusBytes + align_up((size_t)dr::combine_blocks(rows_dtype, hidden, T) * sizeof(uint64_t));
+}
+
+dr_status dr_combine_fingerprinted(const void* rows, dr_dtype rows_dtype, int64_t num_rows, int64_t hidden,
+                                   const int32_t* row_of, const float* gates, int64_t T, int32_t k, float* out,
+                                   uint64_t* out_hash, void* ws, size_t ws_bytes, int32_t* dev_status,
+                                   hipStream_t stream) {
+    const char* what = "dr_combine_fingerprinted";
+    dr_status st = check_dtype(rows_dtype, what);
+    if (st != DR_OK) return st;
+    if ((st = check_rows(rows, rows_dtype, hidden, what)) != DR_OK) return st;
+    if (!aligned(out, 16)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: out must be 16-byte aligned", what);
+    if (T < 0 || num_rows < 0 || num_rows >= kMaxN) return fail(DR_ERR_INVALID_ARGUMENT, "%s: bad T or num_rows", what);
+    if (k < 1) return fail(DR_ERR_INVALID_ARGUMENT, "%s: k must be >= 1", what);
+    if (k > 64) return fail(DR_ERR_UNSUPPORTED, "%s: k = %d > 64 is not supported", what, k);
+    if (T > 0 && (!rows || !row_of || !gates || !out)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: null pointer", what);
+    if (T > 0 && (!aligned(row_of, 4) || !aligned(gates, 4)))
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: row_of/gates must be 4-byte aligned", what);
+    if (!out_hash || !aligned(out_hash, 8)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: bad out_hash", what);
+    if (!ws || !aligned(ws, 16)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: bad workspace", what);
+    if (ws_bytes < dr_combine_fingerprinted_workspace_size(rows_dtype, hidden, T))
+        return fail(DR_ERR_WORKSPACE_TOO_SMALL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes,
+                    dr_combine_fingerprinted_workspace_size(rows_dtype, hidden, T));
+    if (dev_status && !aligned(dev_status, 4)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: misaligned dev_status", what);
+    if (T * ((hidden / elems16(rows_dtype) + 63) / 64) >= ((int64_t)1 << 32))
+        return fail(DR_ERR_UNSUPPORTED, "%s: T * column slices must be below 2^32", what);
+    uint64_t* partials = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + dr::kStatusBytes);
+    const int64_t nb = dr::combine_blocks(rows_dtype, hidden, T);
+    DR_TRY_HIP(dr::launch_combine(rows, rows_dtype, num_rows, hidden, row_of, gates, T, k, out, dev_status, false,
+                                  partials, stream),
+               "combine launch");
+    DR_TRY_HIP(dr::launch_fingerprint_final(partials, nb, T * hidden * (int64_t)sizeof(float), out_hash, stream),
+               "fingerprint launch");
     return ok();
 }
 
@@ -354,7 +392,7 @@ dr_status dr_combine_atomic(const void* rows, dr_dtype rows_dtype, int64_t num_r
     if (T * k * ((hidden / elems16(rows_dtype) + 63) / 64) >= ((int64_t)1 << 32))
         return fail(DR_ERR_UNSUPPORTED, "%s: T * k * column slices must be below 2^32", what);
     DR_TRY_HIP(dr::launch_combine(rows, rows_dtype, num_rows, hidden, row_of, gates, T, k, out, dev_status, true,
-                                  stream),
+                                  nullptr, stream),
                "combine_atomic launch");
     return ok();
 }

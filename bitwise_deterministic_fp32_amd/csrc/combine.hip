@@ -26,23 +26,19 @@ __device__ __forceinline__ int32_t uniform_lane(int32_t v, int lane) {
     return __builtin_amdgcn_readlane(v, lane);
 }
 
-template <dr_dtype DT, int KMAX>
-__global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restrict__ rows, int64_t num_rows, int64_t H,
-                                                           const int32_t* __restrict__ row_of,
-                                                           const float* __restrict__ gates, int64_t T, int k,
-                                                           float* __restrict__ out, int32_t* dev_status,
-                                                           int64_t slices) {
+// The work of one wavefront: token t, column slice `slice`.  Returns this
+// lane's sum of fingerprint terms of the bytes it stored (FP), else 0.
+template <dr_dtype DT, int KMAX, bool FP>
+__device__ __forceinline__ uint64_t combine_token(const void* __restrict__ rows, int64_t num_rows, int64_t H,
+                                                  const int32_t* __restrict__ row_of, const float* __restrict__ gates,
+                                                  int k, float* __restrict__ out, int32_t* dev_status, int64_t t,
+                                                  uint32_t slice) {
     using PC = Piece<DT>;
     constexpr int P = PC::kPieces;
     constexpr int kElemBytes = DT == DR_BF16 ? 2 : 4;
     constexpr int64_t W = 64 * 4 * P;  // columns of one wavefront slice
     const int lane = threadIdx.x & 63;
-    // the host keeps T * slices below 2^32
-    const uint32_t wave = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
-    const uint32_t t32 = wave / (uint32_t)slices;
-    if (t32 >= T) return;  // whole wavefront
-    const int64_t t = t32;
-    const uint32_t slice = wave - t32 * (uint32_t)slices;
+
     // piece p of this lane: columns col[p] .. col[p]+3; pieces of a wavefront
     // are 256 columns apart so each load and store instruction is contiguous
     int64_t col[P], lcol[P];
@@ -64,14 +60,20 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
     const bool bad = lane < k && (rid < 0 || rid >= num_rows);
     if (__ballot(bad) != 0) {
         // fail closed: never read outside rows; the token's output is poisoned
-        const float nan = __uint_as_float(0x7FC00000u);
+        const uint32_t nan = 0x7FC00000u;
+        uint64_t hash = 0;
 #pragma unroll
         for (int p = 0; p < P; ++p)
-            if (active[p])
-                store16(orow + col[p], u32x4{__float_as_uint(nan), __float_as_uint(nan), __float_as_uint(nan),
-                                             __float_as_uint(nan)});
+            if (active[p]) {
+                store16(orow + col[p], u32x4{nan, nan, nan, nan});
+                if (FP) {
+                    const int64_t i0 = (t * H + col[p]) >> 1;  // 8-byte word index
+                    const uint64_t w = ((uint64_t)nan << 32) | nan;
+                    hash += fp_term(w, i0) + fp_term(w, i0 + 1);
+                }
+            }
         if (dev_status && lane == 0 && slice == 0) atomicOr(dev_status, kStatusIndex);
-        return;
+        return hash;
     }
     const char* rb = reinterpret_cast<const char*>(rows);
     const int64_t row_bytes = H * kElemBytes;
@@ -180,11 +182,45 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
             }
         }
     }
+    uint64_t hash = 0;
 #pragma unroll
     for (int p = 0; p < P; ++p)
-        if (active[p])
-            store16_stream(orow + col[p], u32x4{__float_as_uint(res[p][0]), __float_as_uint(res[p][1]),
-                                                __float_as_uint(res[p][2]), __float_as_uint(res[p][3])});
+        if (active[p]) {
+            const u32x4 v{__float_as_uint(res[p][0]), __float_as_uint(res[p][1]), __float_as_uint(res[p][2]),
+                          __float_as_uint(res[p][3])};
+            store16_stream(orow + col[p], v);
+            if (FP) {
+                // the fingerprint's terms of the two 8-byte words just stored
+                const int64_t i0 = (t * H + col[p]) >> 1;
+                hash += fp_term(((uint64_t)v.y << 32) | v.x, i0) + fp_term(((uint64_t)v.w << 32) | v.z, i0 + 1);
+            }
+        }
+    return hash;
+}
+
+// One wavefront per (token, column slice).  With FP, the workgroup also sums
+// the fingerprint terms of what it stored into fp_partials[blockIdx.x]
+// (wrapping addition, so the total does not depend on the grid).
+template <dr_dtype DT, int KMAX, bool FP>
+__global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restrict__ rows, int64_t num_rows, int64_t H,
+                                                           const int32_t* __restrict__ row_of,
+                                                           const float* __restrict__ gates, int64_t T, int k,
+                                                           float* __restrict__ out, int32_t* dev_status,
+                                                           int64_t slices, uint64_t* __restrict__ fp_partials) {
+    // the host keeps T * slices below 2^32
+    const uint32_t wave = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    const uint32_t t32 = wave / (uint32_t)slices;
+    uint64_t hash = 0;
+    if (t32 < T) {  // whole wavefront
+        const int64_t t = t32;
+        hash = combine_token<DT, KMAX, FP>(rows, num_rows, H, row_of, gates, k, out, dev_status, t,
+                                           wave - t32 * (uint32_t)slices);
+    }
+    if (FP) {
+        __shared__ uint64_t smem[kWavesPerBlock];
+        const uint64_t s = block_sum_u64(hash, smem);
+        if (threadIdx.x == 0) fp_partials[blockIdx.x] = s;
+    }
 }
 
 // The baseline: one wavefront per (token, slot, slice of 64*E columns), so
@@ -234,7 +270,8 @@ __global__ __launch_bounds__(kThreads) void combine_atomic_kernel(const void* __
 
 template <dr_dtype DT>
 hipError_t launch_dt(const void* rows, int64_t num_rows, int64_t H, const int32_t* row_of, const float* gates,
-                     int64_t T, int32_t k, float* out, int32_t* dev_status, bool atomic, hipStream_t s) {
+                     int64_t T, int32_t k, float* out, int32_t* dev_status, bool atomic, uint64_t* fp_partials,
+                     hipStream_t s) {
     constexpr int E = Vec<DT>::kElems;
     const int64_t pieces = H / E;
     const int64_t slices = (pieces + 63) / 64;
@@ -247,23 +284,35 @@ hipError_t launch_dt(const void* rows, int64_t num_rows, int64_t H, const int32_
     }
     const int64_t waves = T * slices;
     const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
-    if (k <= 8)
-        hipLaunchKernelGGL((combine_kernel<DT, 8>), grid, dim3(kThreads), 0, s, rows, num_rows, H, row_of,
-                           gates, T, k, out, dev_status, slices);
-    else
-        hipLaunchKernelGGL((combine_kernel<DT, 64>), grid, dim3(kThreads), 0, s, rows, num_rows, H, row_of,
-                           gates, T, k, out, dev_status, slices);
+#define DR_COMBINE(KM, FPV)                                                                                      \
+    hipLaunchKernelGGL((combine_kernel<DT, KM, FPV>), grid, dim3(kThreads), 0, s, rows, num_rows, H, row_of, gates, \
+                       T, k, out, dev_status, slices, fp_partials)
+    if (fp_partials) {
+        if (k <= 8) DR_COMBINE(8, true);
+        else DR_COMBINE(64, true);
+    } else {
+        if (k <= 8) DR_COMBINE(8, false);
+        else DR_COMBINE(64, false);
+    }
+#undef DR_COMBINE
     return hipGetLastError();
 }
 
 }  // namespace
 
+int64_t combine_blocks(dr_dtype dt, int64_t hidden, int64_t T) {
+    const int64_t per_wave = 64 * (dt == DR_BF16 ? 8 : 4);
+    const int64_t slices = (hidden + per_wave - 1) / per_wave;
+    return (T * slices + kWavesPerBlock - 1) / kWavesPerBlock;
+}
+
 hipError_t launch_combine(const void* rows, dr_dtype dt, int64_t num_rows, int64_t hidden, const int32_t* row_of,
                           const float* gates, int64_t T, int32_t k, float* out, int32_t* dev_status, bool atomic,
-                          hipStream_t s) {
+                          uint64_t* fp_partials, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    if (dt == DR_BF16) return launch_dt<DR_BF16>(rows, num_rows, hidden, row_of, gates, T, k, out, dev_status, atomic, s);
-    return launch_dt<DR_F32>(rows, num_rows, hidden, row_of, gates, T, k, out, dev_status, atomic, s);
+    if (dt == DR_BF16)
+        return launch_dt<DR_BF16>(rows, num_rows, hidden, row_of, gates, T, k, out, dev_status, atomic, fp_partials, s);
+    return launch_dt<DR_F32>(rows, num_rows, hidden, row_of, gates, T, k, out, dev_status, atomic, fp_partials, s);
 }
 
 }  // namespace dr

@@ -14,33 +14,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxBlocks = 2048;
 
-__device__ __forceinline__ uint64_t mix64(uint64_t z) {
-    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
-    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
-    return z ^ (z >> 31);
-}
-
-__device__ __forceinline__ uint64_t term(uint64_t w, int64_t i) {
-    return mix64(w ^ ((uint64_t)(i + 1) * 0x9e3779b97f4a7c15ull));
-}
-
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int off) {
-    const uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
-    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
-    return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ uint64_t block_sum_u64(uint64_t v, uint64_t* smem) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) v += shfl_xor_u64(v, off);
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    if (lane == 0) smem[w] = v;
-    __syncthreads();
-    uint64_t s = 0;
-    if (threadIdx.x == 0)
-        for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += smem[i];
-    return s;
-}
+__device__ __forceinline__ uint64_t term(uint64_t w, int64_t i) { return fp_term(w, i); }
 
 __global__ __launch_bounds__(kThreads) void fp_partial_kernel(const unsigned char* __restrict__ data, int64_t nbytes,
                                                               uint64_t* __restrict__ partials) {
@@ -87,11 +61,11 @@ __global__ __launch_bounds__(kThreads) void fp_partial_kernel(const unsigned cha
     if (threadIdx.x == 0) partials[blockIdx.x] = s;
 }
 
-__global__ __launch_bounds__(kThreads) void fp_final_kernel(const uint64_t* __restrict__ partials, int nblocks,
+__global__ __launch_bounds__(kThreads) void fp_final_kernel(const uint64_t* __restrict__ partials, int64_t nblocks,
                                                             int64_t nbytes, uint64_t* __restrict__ out) {
     __shared__ uint64_t smem[kThreads / 64];
     uint64_t acc = 0;
-    for (int i = threadIdx.x; i < nblocks; i += kThreads) acc += partials[i];
+    for (int64_t i = threadIdx.x; i < nblocks; i += kThreads) acc += partials[i];
     const uint64_t s = block_sum_u64(acc, smem);
     if (threadIdx.x == 0) *out = s + mix64((uint64_t)nbytes);
 }
@@ -106,6 +80,12 @@ int64_t fingerprint_blocks(int64_t nbytes) {
     return b;
 }
 
+hipError_t launch_fingerprint_final(const uint64_t* block_partials, int64_t nblocks, int64_t nbytes, uint64_t* out,
+                                    hipStream_t s) {
+    hipLaunchKernelGGL(fp_final_kernel, dim3(1), dim3(kThreads), 0, s, block_partials, nblocks, nbytes, out);
+    return hipGetLastError();
+}
+
 hipError_t launch_fingerprint(const void* data, int64_t nbytes, uint64_t* out, uint64_t* block_partials,
                               hipStream_t s) {
     const int64_t nb = fingerprint_blocks(nbytes);
@@ -113,7 +93,7 @@ hipError_t launch_fingerprint(const void* data, int64_t nbytes, uint64_t* out, u
                        reinterpret_cast<const unsigned char*>(data), nbytes, block_partials);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fp_final_kernel, dim3(1), dim3(kThreads), 0, s, block_partials, (int)nb, nbytes, out);
+    hipLaunchKernelGGL(fp_final_kernel, dim3(1), dim3(kThreads), 0, s, block_partials, nb, nbytes, out);
     return hipGetLastError();
 }
 

@@ -115,9 +115,10 @@ hipError_t launch_tilecombine(float* out, int64_t hidden, const float* partials,
                               int tile_chunks_log2, int32_t* status, hipStream_t s);
 
 // combine
+// fp_partials != nullptr: also hash the written output (one partial per workgroup)
 hipError_t launch_combine(const void* rows, dr_dtype dt, int64_t num_rows, int64_t hidden, const int32_t* row_of,
                           const float* gates, int64_t T, int32_t k, float* out, int32_t* dev_status, bool atomic,
-                          hipStream_t s);
+                          uint64_t* fp_partials, hipStream_t s);
 // index_add atomic baseline
 hipError_t launch_index_add_atomic(float* out, int32_t num_dests, int64_t hidden, const void* src,
                                    dr_dtype dt, int64_t n, const int32_t* index, int32_t* dev_status,
@@ -131,6 +132,11 @@ hipError_t launch_splitk_reduce(const float* partials, int32_t splits, int64_t c
 int64_t fingerprint_blocks(int64_t nbytes);
 hipError_t launch_fingerprint(const void* data, int64_t nbytes, uint64_t* out, uint64_t* block_partials,
                               hipStream_t s);
+// out = mix(nbytes) + sum of nblocks per-workgroup partial sums
+hipError_t launch_fingerprint_final(const uint64_t* block_partials, int64_t nblocks, int64_t nbytes, uint64_t* out,
+                                    hipStream_t s);
+// number of workgroups (and fingerprint partials) of a combine launch
+int64_t combine_blocks(dr_dtype dt, int64_t hidden, int64_t T);
 
 }  // namespace dr
 
@@ -230,6 +236,36 @@ template <dr_dtype DT>
 __device__ __forceinline__ float load_elem(const void* row, int64_t col) {
     if (DT == DR_BF16) return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(row)[col] << 16);
     return reinterpret_cast<const float*>(row)[col];
+}
+
+// The fingerprint's terms (see dr_fingerprint in detreduce.h): SplitMix64's
+// finaliser (Steele, Lea and Flood, OOPSLA 2014) of a 64-bit word XOR the
+// generator state (i + 1) * gamma.
+__device__ __forceinline__ uint64_t mix64(uint64_t z) {
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    return z ^ (z >> 31);
+}
+__device__ __forceinline__ uint64_t fp_term(uint64_t w, int64_t i) {
+    return mix64(w ^ ((uint64_t)(i + 1) * 0x9e3779b97f4a7c15ull));
+}
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int off) {
+    const uint32_t lo = __shfl_xor((uint32_t)v, off, 64);
+    const uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, 64);
+    return ((uint64_t)hi << 32) | lo;
+}
+// Wrapping sum over the workgroup (blockDim.x a multiple of 64, <= 1024); the
+// result is valid in thread 0.  smem holds blockDim.x / 64 values.
+__device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, uint64_t* smem) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += shfl_xor_u64(v, off);
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) smem[w] = v;
+    __syncthreads();
+    uint64_t s = 0;
+    if (threadIdx.x == 0)
+        for (int i = 0; i < (int)(blockDim.x >> 6); ++i) s += smem[i];
+    return s;
 }
 
 // -0.0 is an exact identity of IEEE addition (x + -0.0 == x for every x,

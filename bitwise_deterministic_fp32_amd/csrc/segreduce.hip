@@ -313,13 +313,21 @@ __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
         for (int64_t r0 = r_begin; r0 < r_end; r0 += R) {
             typename PC::Raw raw[R][P];
             const int64_t live = r_end - r0;  // rows of this step that exist
+            if (live >= R) {
 #pragma unroll
-            for (int j = 0; j < R; ++j)
+                for (int j = 0; j < R; ++j)
 #pragma unroll
-                for (int p = 0; p < P; ++p) {
-                    raw[j][p] = typename PC::Raw{};
-                    if (j < live) raw[j][p] = PC::load(src_bytes + (int64_t)idx[j] * row_bytes, lcol[p]);
-                }
+                    for (int p = 0; p < P; ++p)
+                        raw[j][p] = PC::load_stream(src_bytes + (int64_t)idx[j] * row_bytes, lcol[p]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < R; ++j)
+#pragma unroll
+                    for (int p = 0; p < P; ++p) {
+                        raw[j][p] = typename PC::Raw{};
+                        if (j < live) raw[j][p] = PC::load_stream(src_bytes + (int64_t)idx[j] * row_bytes, lcol[p]);
+                    }
+            }
             // the next rows' source ids are fetched while these rows arrive
             const int64_t r1 = r0 + R;
             if (r1 < r_end) {

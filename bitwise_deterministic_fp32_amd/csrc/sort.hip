@@ -155,114 +155,115 @@ __global__ __launch_bounds__(kThreads) void radix_scan_kernel(int32_t* hist, int
     if (threadIdx.x == 0) totals[blockIdx.x] = carry;
 }
 
-// Stable scatter of one tile.  Keys are visited in rounds of kThreads
-// consecutive keys; a key's rank among equal digits of the tile is the count
-// in earlier rounds, plus earlier waves of its round, plus lower lanes of its
-// wave (ballots).  The tile is staged in LDS in (digit, rank) order and each
-// digit's run is then written to consecutive global positions.
-template <int ITEMS>
+// Stable scatter of one tile.  Wavefront w owns the contiguous slice
+// [64*ITEMS*w, 64*ITEMS*(w+1)) of the tile and visits it in ITEMS rounds of 64
+// consecutive keys.  A key's rank among equal digits of its wavefront is the
+// wavefront's count of that digit in earlier rounds (a per-wavefront LDS
+// counter, no barrier) plus the lower lanes of its round with the same digit
+// (ballots).  One barrier later, the tile rank adds the counts of earlier
+// wavefronts; equal digits therefore keep input order.  The tile is staged in
+// LDS in (digit, rank) order and each digit's run is written to consecutive
+// global positions.
+template <int ITEMS, int BINS, bool STAGE_SRC>
 __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(SortPass p, int64_t n, int tile_log2,
                                                                  const int32_t* __restrict__ hist, int64_t nblocks,
                                                                  const int32_t* __restrict__ totals,
                                                                  const int32_t* status) {
-    __shared__ int32_t gbase[kMaxBins];    // global position of this tile's first key of digit d
-    __shared__ int32_t lbase[kMaxBins];    // position of digit d's run inside the staged tile
-    __shared__ int32_t running[kMaxBins];  // keys of digit d seen in earlier rounds
-    __shared__ int32_t wave_cnt[kWaves][kMaxBins];
-    __shared__ int32_t wave_off[kWaves][kMaxBins];
+    __shared__ int32_t gbase[BINS];          // global position of this tile's first key of digit d
+    __shared__ int32_t lbase[BINS];          // position of digit d's run inside the staged tile
+    __shared__ int32_t wcount[kWaves][BINS];  // per-wavefront digit counts, then prefixes
     __shared__ int32_t wave_tot[kWaves];
     __shared__ int32_t st_dest[ITEMS * kThreads];
     __shared__ int32_t st_val[ITEMS * kThreads];
-    __shared__ int32_t st_src[ITEMS * kThreads];
+    __shared__ int32_t st_src[STAGE_SRC ? ITEMS * kThreads : 1];
     if (status[kWordStatus] != 0) return;
-    const int tid = threadIdx.x, w = tid >> 6;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int bins = 1 << p.bits;
     const bool key_is_dest = p.digit_src == p.dest_in;
-    const bool carry_src = p.src_out != nullptr;
-    const bool stage_src = carry_src || !key_is_dest;  // source ids are needed in the write-out
     const int64_t base = (int64_t)blockIdx.x << tile_log2;
     const int64_t end = min(n, base + ((int64_t)1 << tile_log2));
     const int32_t count = (int32_t)(end - base);
+    const int64_t wbase = base + (int64_t)w * 64 * ITEMS;  // this wavefront's slice
 
     // this thread's keys, values and carried ids, all loads in flight together
     int32_t key[ITEMS], other[ITEMS], val[ITEMS];
 #pragma unroll
     for (int r = 0; r < ITEMS; ++r) {
-        const int64_t i = base + r * kThreads + tid;
+        const int64_t i = wbase + r * 64 + lane;
         key[r] = other[r] = 0;
         val[r] = (int32_t)i;
         if (i < end) {
             key[r] = p.digit_src[i];
-            other[r] = key_is_dest ? (stage_src ? p.src_in[i] : 0) : p.dest_in[i];
+            other[r] = key_is_dest ? (STAGE_SRC ? p.src_in[i] : 0) : p.dest_in[i];
             if (p.val_in) val[r] = p.val_in[i];
         }
     }
-    // global bases: digit totals scanned over digits, plus this tile's offset;
-    // this tile's count of digit d is the next tile's offset minus its own
     for (int d = tid; d < bins; d += kThreads) {
-        const int64_t at = (int64_t)d * nblocks + blockIdx.x;
-        const int32_t off = hist[at];
-        const int32_t next = blockIdx.x + 1 < nblocks ? hist[at + 1] : totals[d];
-        gbase[d] = totals[d];  // scanned below
-        lbase[d] = next - off;
-        running[d] = off;      // temporarily
 #pragma unroll
-        for (int ww = 0; ww < kWaves; ++ww) wave_cnt[ww][d] = 0;
+        for (int ww = 0; ww < kWaves; ++ww) wcount[ww][d] = 0;
+        gbase[d] = totals[d];
+    }
+    __syncthreads();
+
+    // ranks inside the wavefront, in input order
+    int32_t rank[ITEMS];
+#pragma unroll
+    for (int r = 0; r < ITEMS; ++r) {
+        const bool valid = wbase + r * 64 + lane < end;
+        const int dg = digit_of(key[r], p.shift, p.bits);
+        const uint64_t peers = peers_of(dg, valid, p.bits);
+        const int below = __popcll(peers & lanemask_lt());
+        const int leader = peers ? __builtin_ctzll(peers) : lane;
+        int32_t prev = 0;
+        if (valid && below == 0) {
+            prev = wcount[w][dg];
+            wcount[w][dg] = prev + __popcll(peers);
+        }
+        prev = __shfl(prev, leader, 64);
+        rank[r] = prev + below;
+    }
+    __syncthreads();
+    // per digit: tile count, offsets of the wavefronts, and the global base
+    for (int d = tid; d < bins; d += kThreads) {
+        int32_t acc = 0;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) {
+            const int32_t c = wcount[ww][d];
+            wcount[ww][d] = acc;
+            acc += c;
+        }
+        lbase[d] = acc;  // the tile's count of digit d, scanned below
     }
     __syncthreads();
     scan_bins_in_place(gbase, bins, wave_tot);
     scan_bins_in_place(lbase, bins, wave_tot);
-    for (int d = tid; d < bins; d += kThreads) {
-        gbase[d] += running[d];
-        running[d] = 0;
-    }
+    for (int d = tid; d < bins; d += kThreads) gbase[d] += hist[(int64_t)d * nblocks + blockIdx.x];
     __syncthreads();
-
 #pragma unroll
     for (int r = 0; r < ITEMS; ++r) {
-        const int64_t i = base + r * kThreads + tid;
-        const bool valid = i < end;
-        const int dg = digit_of(key[r], p.shift, p.bits);
-        const uint64_t peers = peers_of(dg, valid, p.bits);
-        const int rank = __popcll(peers & lanemask_lt());
-        if (valid && rank == 0) wave_cnt[w][dg] = __popcll(peers);
-        __syncthreads();
-        for (int d = tid; d < bins; d += kThreads) {
-            int32_t pre = running[d];
-#pragma unroll
-            for (int ww = 0; ww < kWaves; ++ww) {
-                const int32_t c = wave_cnt[ww][d];
-                wave_off[ww][d] = pre;
-                pre += c;
-                wave_cnt[ww][d] = 0;
-            }
-            running[d] = pre;
-        }
-        __syncthreads();
-        if (valid) {
-            const int32_t lp = lbase[dg] + wave_off[w][dg] + rank;
+        if (wbase + r * 64 + lane < end) {
+            const int dg = digit_of(key[r], p.shift, p.bits);
+            const int32_t lp = lbase[dg] + wcount[w][dg] + rank[r];
             st_val[lp] = val[r];
             st_dest[lp] = key_is_dest ? key[r] : other[r];
-            if (stage_src) st_src[lp] = key_is_dest ? other[r] : key[r];
+            if (STAGE_SRC) st_src[lp] = key_is_dest ? other[r] : key[r];
         }
-        // The next round writes wave_cnt before its first barrier and
-        // wave_off only after it, when every thread has finished this round.
     }
     __syncthreads();
     // write-out in staged order: a digit's run goes to consecutive positions
     for (int32_t j = tid; j < count; j += kThreads) {
         const int32_t dk = st_dest[j];
-        const int32_t sk = stage_src ? st_src[j] : 0;
+        const int32_t sk = STAGE_SRC ? st_src[j] : 0;
         const int dg = digit_of(key_is_dest ? dk : sk, p.shift, p.bits);
         const int32_t pos = gbase[dg] + (j - lbase[dg]);
-        const int32_t val = st_val[j];
-        // consistent histograms keep pos and val inside [0, n); the guard keeps
+        const int32_t v = st_val[j];
+        // consistent histograms keep pos and v inside [0, n); the guard keeps
         // a corrupted workspace from writing outside the outputs
-        if ((uint64_t)(uint32_t)pos >= (uint64_t)n || (uint64_t)(uint32_t)val >= (uint64_t)n) continue;
-        p.val_out[pos] = val;
+        if ((uint64_t)(uint32_t)pos >= (uint64_t)n || (uint64_t)(uint32_t)v >= (uint64_t)n) continue;
+        p.val_out[pos] = v;
         if (p.dest_out) p.dest_out[pos] = dk;
-        if (carry_src) p.src_out[pos] = sk;
-        if (p.inv_out) p.inv_out[val] = pos;
+        if (STAGE_SRC && p.src_out) p.src_out[pos] = sk;
+        if (p.inv_out) p.inv_out[v] = pos;
     }
 }
 
@@ -332,14 +333,34 @@ hipError_t launch_radix_scan(int32_t* hist, int64_t nblocks, int bins, int32_t* 
     return hipGetLastError();
 }
 
+template <int ITEMS>
+static void launch_scatter_items(const SortPass& p, int64_t n, int tile_log2, const int32_t* hist,
+                                 const int32_t* totals, const int32_t* status, int64_t nb, hipStream_t s) {
+    const bool stage_src = p.src_out != nullptr || p.digit_src != p.dest_in;
+    const dim3 grid((unsigned)nb), block(kThreads);
+    if (p.bits <= 8) {
+        if (stage_src)
+            hipLaunchKernelGGL((radix_scatter_kernel<ITEMS, 256, true>), grid, block, 0, s, p, n, tile_log2, hist, nb,
+                               totals, status);
+        else
+            hipLaunchKernelGGL((radix_scatter_kernel<ITEMS, 256, false>), grid, block, 0, s, p, n, tile_log2, hist,
+                               nb, totals, status);
+    } else {
+        if (stage_src)
+            hipLaunchKernelGGL((radix_scatter_kernel<ITEMS, kMaxBins, true>), grid, block, 0, s, p, n, tile_log2, hist,
+                               nb, totals, status);
+        else
+            hipLaunchKernelGGL((radix_scatter_kernel<ITEMS, kMaxBins, false>), grid, block, 0, s, p, n, tile_log2,
+                               hist, nb, totals, status);
+    }
+}
+
 hipError_t launch_radix_scatter(const SortPass& p, int64_t n, int tile_log2, const int32_t* hist,
                                 const int32_t* totals, const int32_t* status, hipStream_t s) {
     const int64_t nb = tiles_for(n, tile_log2);
     if (nb == 0) return hipSuccess;
     static_assert(kMaxSortTileLog2 <= 12, "staged tile must fit in LDS");
-#define DR_S(IT)                                                                                           \
-    hipLaunchKernelGGL((radix_scatter_kernel<IT>), dim3((unsigned)nb), dim3(kThreads), 0, s, p, n, tile_log2, \
-                       hist, nb, totals, status)
+#define DR_S(IT) launch_scatter_items<IT>(p, n, tile_log2, hist, totals, status, nb, s)
     DR_BY_ITEMS(tile_log2, DR_S)
 #undef DR_S
     return hipGetLastError();

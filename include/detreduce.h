@@ -158,6 +158,17 @@ dr_status dr_combine(const void* rows, dr_dtype rows_dtype, int64_t num_rows, in
                      const int32_t* row_of, const float* gates, int64_t T, int32_t k, float* out,
                      int32_t* dev_status, hipStream_t stream);
 
+/* The same combine, also writing dr_fingerprint(out) to *out_hash: every
+ * workgroup hashes the bytes it stores, so the output is not read back.
+ * out_hash and the output bits equal those of dr_combine followed by
+ * dr_fingerprint.  ws: >= dr_combine_fingerprinted_workspace_size() bytes,
+ * 16-byte aligned. */
+size_t dr_combine_fingerprinted_workspace_size(dr_dtype rows_dtype, int64_t hidden, int64_t T);
+dr_status dr_combine_fingerprinted(const void* rows, dr_dtype rows_dtype, int64_t num_rows, int64_t hidden,
+                                   const int32_t* row_of, const float* gates, int64_t T, int32_t k, float* out,
+                                   uint64_t* out_hash, void* ws, size_t ws_bytes, int32_t* dev_status,
+                                   hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * index_add: out[d] = out[d] + T(src rows i with index[i] == d, in order of i).
  *

@@ -19,12 +19,20 @@ FAKE = 0x7F0000000000  # a 256-byte aligned address that is never dereferenced h
 @pytest.fixture(scope="module")
 def lib():
     if not os.path.exists(LIB):
-        from bitwise_deterministic_fp32_amd import build
-        build.build()
+        build_module().build()
     L = ctypes.CDLL(LIB)
     L.dr_last_error.restype = ctypes.c_char_p
     L.dr_status_string.restype = ctypes.c_char_p
     return L
+
+
+def build_module():
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("_detreduce_build",
+                                                  os.path.join(ROOT, "bitwise_deterministic_fp32_amd", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
 
 
 def declared():
@@ -163,7 +171,7 @@ def test_launch_params_validation(lib):
 def test_kernels_have_no_fused_multiply_add():
     """The defined order forbids contraction: the gfx950 assembly of every kernel
     source holds no fused or packed fp32 multiply-add instruction."""
-    from bitwise_deterministic_fp32_amd import build
+    build = build_module()
     csrc = os.path.join(ROOT, "bitwise_deterministic_fp32_amd", "csrc")
     bad = re.compile(r"\b(v_fma\w*|v_fmac\w*|v_fmamk\w*|v_fmaak\w*|v_pk_fma\w*|v_pk_add_f32|v_pk_mul_f32|v_mad_f32|v_mac_f32)\b")
     for src in build.SOURCES:

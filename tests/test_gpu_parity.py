@@ -214,3 +214,29 @@ def test_fingerprint_odd_lengths_and_dtypes(dr):
     nz = z.copy()
     nz[2] = -0.0
     assert dr.fingerprint_value(dev(z)) != dr.fingerprint_value(dev(nz))
+
+
+@pytest.mark.parametrize("T,E,k,H,rows_dtype", [
+    (1000, 64, 8, 1000, "bf16"),
+    (257, 16, 1, 64, "f32"),
+    (300, 128, 13, 136, "bf16"),
+])
+def test_combine_fingerprinted_matches_separate_calls(dr, T, E, k, H, rows_dtype):
+    say(f"combine_fingerprinted T={T} k={k} H={H} {rows_dtype}")
+    inp = workloads.moe_inputs(91 + k, T, E, k, H, rows_dtype, zipf_bias_s=1.2)
+    row_of = _row_of(dr, inp.expert_ids, E)
+    rows = dev(inp.rows) if rows_dtype == "f32" else dev_bf16(inp.rows)
+    gates = dev(inp.gates)
+    out, h = dr.dr_combine_fingerprinted(rows, row_of, gates)
+    ref = dr.dr_combine(rows, row_of, gates)
+    assert_bits_equal(host(out), host(ref), "fused combine output")
+    hv = int(h.item()) & ((1 << 64) - 1)
+    assert hv == dr.fingerprint_value(ref)
+    assert hv == oracle.fingerprint(host(ref))
+    # a poisoned token is hashed as written
+    bad = row_of.clone()
+    bad[T // 2, 0] = inp.T * inp.k + 5
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out2, h2 = dr.dr_combine_fingerprinted(rows, bad, gates, dev_status=status)
+    assert np.isnan(host(out2)[T // 2]).all()
+    assert int(h2.item()) & ((1 << 64) - 1) == oracle.fingerprint(host(out2))
