@@ -342,7 +342,9 @@ dr_status dr_combine(const void* rows, dr_dtype rows_dtype, int64_t num_rows, in
 
 size_t dr_combine_fingerprinted_workspace_size(dr_dtype rows_dtype, int64_t hidden, int64_t T) {
     if (hidden < 1 || T < 0) return dr::kStatusBytes;
-    return dr::kStatusBytes + align_up((size_t)dr::combine_blocks(rows_dtype, hidden, T) * sizeof(uint64_t));
+    const int64_t nb = dr::combine_blocks(rows_dtype, hidden, T);
+    return dr::kStatusBytes + align_up((size_t)nb * sizeof(uint64_t)) +
+           align_up((size_t)dr::fingerprint_group_count(nb) * sizeof(uint64_t));
 }
 
 dr_status dr_combine_fingerprinted(const void* rows, dr_dtype rows_dtype, int64_t num_rows, int64_t hidden,
@@ -368,12 +370,16 @@ dr_status dr_combine_fingerprinted(const void* rows, dr_dtype rows_dtype, int64_
     if (dev_status && !aligned(dev_status, 4)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: misaligned dev_status", what);
     if (T * ((hidden / elems16(rows_dtype) + 63) / 64) >= ((int64_t)1 << 32))
         return fail(DR_ERR_UNSUPPORTED, "%s: T * column slices must be below 2^32", what);
-    uint64_t* partials = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + dr::kStatusBytes);
     const int64_t nb = dr::combine_blocks(rows_dtype, hidden, T);
+    Carver c(ws);
+    c.take<uint8_t>(dr::kStatusBytes);
+    uint64_t* partials = c.take<uint64_t>(nb);
+    uint64_t* group_sums = c.take<uint64_t>(dr::fingerprint_group_count(nb));
     DR_TRY_HIP(dr::launch_combine(rows, rows_dtype, num_rows, hidden, row_of, gates, T, k, out, dev_status, false,
                                   partials, stream),
                "combine launch");
-    DR_TRY_HIP(dr::launch_fingerprint_final(partials, nb, T * hidden * (int64_t)sizeof(float), out_hash, stream),
+    DR_TRY_HIP(dr::launch_fingerprint_final(partials, nb, T * hidden * (int64_t)sizeof(float), out_hash, group_sums,
+                                            stream),
                "fingerprint launch");
     return ok();
 }

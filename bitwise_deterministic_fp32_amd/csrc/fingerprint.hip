@@ -80,8 +80,37 @@ int64_t fingerprint_blocks(int64_t nbytes) {
     return b;
 }
 
+// Sums groups of kGroup partials per workgroup (four loads in flight per
+// thread) into sums[blockIdx.x].
+constexpr int kGroup = 4 * kThreads;
+__global__ __launch_bounds__(kThreads) void fp_group_kernel(const uint64_t* __restrict__ partials, int64_t nblocks,
+                                                            uint64_t* __restrict__ sums) {
+    __shared__ uint64_t smem[kThreads / 64];
+    const int64_t base = (int64_t)blockIdx.x * kGroup + threadIdx.x;
+    uint64_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int64_t i = base + u * kThreads;
+        v[u] = i < nblocks ? partials[i] : 0;
+    }
+    const uint64_t s = block_sum_u64(v[0] + v[1] + v[2] + v[3], smem);
+    if (threadIdx.x == 0) sums[blockIdx.x] = s;
+}
+
+int64_t fingerprint_group_count(int64_t nblocks) { return (nblocks + kGroup - 1) / kGroup; }
+
 hipError_t launch_fingerprint_final(const uint64_t* block_partials, int64_t nblocks, int64_t nbytes, uint64_t* out,
-                                    hipStream_t s) {
+                                    uint64_t* group_sums, hipStream_t s) {
+    if (nblocks > kGroup && group_sums) {
+        // two levels: many workgroups fold the partials, one folds their sums
+        const int64_t groups = fingerprint_group_count(nblocks);
+        hipLaunchKernelGGL(fp_group_kernel, dim3((unsigned)groups), dim3(kThreads), 0, s, block_partials, nblocks,
+                           group_sums);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        block_partials = group_sums;
+        nblocks = groups;
+    }
     hipLaunchKernelGGL(fp_final_kernel, dim3(1), dim3(kThreads), 0, s, block_partials, nblocks, nbytes, out);
     return hipGetLastError();
 }
@@ -93,8 +122,7 @@ hipError_t launch_fingerprint(const void* data, int64_t nbytes, uint64_t* out, u
                        reinterpret_cast<const unsigned char*>(data), nbytes, block_partials);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(fp_final_kernel, dim3(1), dim3(kThreads), 0, s, block_partials, nb, nbytes, out);
-    return hipGetLastError();
+    return launch_fingerprint_final(block_partials, nb, nbytes, out, nullptr, s);
 }
 
 }  // namespace dr

@@ -132,9 +132,11 @@ hipError_t launch_splitk_reduce(const float* partials, int32_t splits, int64_t c
 int64_t fingerprint_blocks(int64_t nbytes);
 hipError_t launch_fingerprint(const void* data, int64_t nbytes, uint64_t* out, uint64_t* block_partials,
                               hipStream_t s);
-// out = mix(nbytes) + sum of nblocks per-workgroup partial sums
+// out = mix(nbytes) + sum of nblocks per-workgroup partial sums; group_sums
+// holds fingerprint_group_count(nblocks) values for a two-level sum
+int64_t fingerprint_group_count(int64_t nblocks);
 hipError_t launch_fingerprint_final(const uint64_t* block_partials, int64_t nblocks, int64_t nbytes, uint64_t* out,
-                                    hipStream_t s);
+                                    uint64_t* group_sums, hipStream_t s);
 // number of workgroups (and fingerprint partials) of a combine launch
 int64_t combine_blocks(dr_dtype dt, int64_t hidden, int64_t T);
 
