@@ -494,8 +494,10 @@ static dr_status check_splitk(const void* X, const void* dY, int64_t K, int64_t 
                     (long long)kc, (long long)K);
     if (!aligned(X, 16) || !aligned(dY, 2) || !aligned(out, 4))
         return fail(DR_ERR_INVALID_ARGUMENT, "%s: X must be 16-byte aligned", what);
-    if ((M + 63) / 64 > 0x7FFFFFFF || (N + 31) / 32 > 65535)
-        return fail(DR_ERR_UNSUPPORTED, "%s: M or N too large for one launch", what);
+    // (split, N tile, M tile) items are counted in 32 bits on the device
+    if ((M + 63) / 64 > 0x7FFFFFFF || (N + 31) / 32 > 0x7FFFFFFF ||
+        ((M + 63) / 64) * ((N + 31) / 32) > 0x7FFFFFFF / splits)
+        return fail(DR_ERR_UNSUPPORTED, "%s: M, N and splits give too many tiles for one launch", what);
     return DR_OK;
 }
 

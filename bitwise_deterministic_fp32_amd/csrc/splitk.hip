@@ -4,10 +4,10 @@
 // The DeepSeek-V4 mHC backward (ch. 9, section 3.3) has an output dimension of
 // only 24.  It must split the contraction, and it keeps one buffer per split,
 // reduced afterwards by a dedicated kernel in split-id order.  Here:
-//   splitk_gemm: one workgroup per (split, 64-row M tile, 32-column N tile).
-//     The split's tokens (up to 256 per stage) are loaded in one phase (16
-//     independent 16-byte loads per thread) and staged in LDS: X row-major, dY
-//     transposed.  Each of the two wavefronts accumulates a 32x32 tile with the
+//   splitk_gemm: persistent workgroups walk (split, 32-column N tile, 64-row M
+//     tile) items in stages of up to 256 tokens (16 independent 16-byte loads
+//     per thread), staged in LDS (X row-major, dY transposed); the next
+//     stage's loads are in flight while the current one is computed.  Each of the two wavefronts accumulates a 32x32 tile with the
 //     bf16 MFMA v_mfma_f32_32x32x16_bf16, in token order, into fp32.  A partial depends
 //     only on (split, m, n): not on the grid, the M/N tiling or other columns.
 //     The HBM stream is X (read once); the MFMA work is small beside it.
@@ -35,58 +35,105 @@ constexpr int YS = KT + 8;
 
 __device__ __forceinline__ __bf16 as_bf16(uint16_t b) { return __builtin_bit_cast(__bf16, b); }
 
+constexpr int kLoadsPerThread = KT * (BM / 8) / kGemmThreads;  // 16-byte X loads per thread per stage
+
+// Coordinates of one unit of work: a KT-token stage of one (split, N tile, M tile) item.
+struct Unit {
+    uint32_t item;  // (split, N tile, M tile), M tile fastest
+    int stage;      // KT-token stage within the split
+};
+
+struct UnitGeom {
+    int s;
+    int64_t m0, n0, t0;
+    int rows;        // valid tokens of the stage
+    bool last;       // last stage of its split
+    bool x_vec;      // full-width M tile with 16-byte rows
+};
+
+// 32-bit tile arithmetic: the host keeps the item count below 2^31.
+__device__ __forceinline__ UnitGeom geometry(const Unit& u, int64_t K, int64_t M, int64_t kc, uint32_t mtiles,
+                                             uint32_t ntiles) {
+    UnitGeom g;
+    const uint32_t mt = u.item % mtiles;
+    const uint32_t rest = u.item / mtiles;
+    const uint32_t nt = rest % ntiles;
+    g.s = (int)(rest / ntiles);
+    g.m0 = (int64_t)mt * BM;
+    g.n0 = (int64_t)nt * BN;
+    const int64_t t_begin = (int64_t)g.s * kc;
+    const int64_t t_end = min(K, t_begin + kc);
+    g.t0 = t_begin + (int64_t)u.stage * KT;
+    g.rows = (int)min((int64_t)KT, t_end - g.t0);
+    g.last = g.t0 + KT >= t_end;
+    g.x_vec = (M % 8) == 0 && g.m0 + BM <= M;
+    return g;
+}
+
+__device__ __forceinline__ Unit next_unit(const Unit& u, const UnitGeom& g) {
+    return g.last ? Unit{u.item + gridDim.x, 0} : Unit{u.item, u.stage + 1};
+}
+
+// Issues the 16-byte X loads of a full-width unit (rows past the split read as zero).
+__device__ __forceinline__ void load_x(const uint16_t* __restrict__ X, int64_t M, const UnitGeom& g,
+                                       u32x4 (&buf)[kLoadsPerThread]) {
+#pragma unroll
+    for (int q = 0; q < kLoadsPerThread; ++q) {
+        const int p = threadIdx.x + q * kGemmThreads;
+        const int r = p / (BM / 8), c8 = (p % (BM / 8)) * 8;
+        buf[q] = u32x4{0u, 0u, 0u, 0u};
+        if (r < g.rows) buf[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(X + (g.t0 + r) * M + g.m0 + c8));
+    }
+}
+
+// Persistent workgroups walk their units in order; the X loads of the next
+// unit are issued right after the current unit is staged in LDS, so they are
+// in flight during its MFMAs and epilogue.  A partial's accumulation order
+// (token order within its split) is the same for any grid.
 template <bool ATOMIC>
 __global__ __launch_bounds__(kGemmThreads) void splitk_gemm_kernel(const uint16_t* __restrict__ X,
                                                                    const uint16_t* __restrict__ dY, int64_t K,
-                                                                   int64_t M, int64_t N, int64_t kc,
+                                                                   int64_t M, int64_t N, int64_t kc, uint32_t items,
+                                                                   uint32_t mtiles, uint32_t ntiles,
                                                                    float* __restrict__ out) {
     __shared__ __attribute__((aligned(16))) uint16_t xs[KT * XS];
     __shared__ __attribute__((aligned(16))) uint16_t ys[BN * YS];
-    const int s = blockIdx.z;
-    const int64_t m0 = (int64_t)blockIdx.x * BM;
-    const int64_t n0 = (int64_t)blockIdx.y * BN;
-    const int64_t t_begin = (int64_t)s * kc;
-    const int64_t t_end = min(K, t_begin + kc);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const bool x_vec = (M % 8) == 0 && m0 + BM <= M;
     const bool y_vec = (N % 8) == 0 && (reinterpret_cast<uintptr_t>(dY) & 15) == 0;
+    Unit u{blockIdx.x, 0};
+    if (u.item >= items) return;
+    UnitGeom g = geometry(u, K, M, kc, mtiles, ntiles);
+    u32x4 buf[kLoadsPerThread];
+    if (g.x_vec) load_x(X, M, g, buf);
 
     f32x16 acc;
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[v] = 0.f;
 
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += KT) {
-        const int rows = (int)min((int64_t)KT, t_end - t0);  // valid tokens in this stage
-        const int ksteps = (rows + 15) / 16;
-        const int rows16 = ksteps * 16;                        // rows the MFMAs read
-        // X[t0 .. t0+rows16) x [m0 .. m0+BM) -> xs; rows past the split are zero
-        if (x_vec) {
-            u32x4 v[KT * (BM / 8) / kGemmThreads];
+    while (true) {
+        const int ksteps = (g.rows + 15) / 16;
+        const int rows16 = ksteps * 16;  // rows the MFMAs read
+        // X stage -> xs; rows past the split are zero
+        if (g.x_vec) {
 #pragma unroll
-            for (int q = 0; q < KT * (BM / 8) / kGemmThreads; ++q) {
+            for (int q = 0; q < kLoadsPerThread; ++q) {
                 const int p = tid + q * kGemmThreads;
                 const int r = p / (BM / 8), c8 = (p % (BM / 8)) * 8;
-                v[q] = r < rows ? load16(X + (t0 + r) * M + m0 + c8) : u32x4{0u, 0u, 0u, 0u};
-            }
-#pragma unroll
-            for (int q = 0; q < KT * (BM / 8) / kGemmThreads; ++q) {
-                const int p = tid + q * kGemmThreads;
-                const int r = p / (BM / 8), c8 = (p % (BM / 8)) * 8;
-                if (r < rows16) *reinterpret_cast<u32x4*>(xs + r * XS + c8) = v[q];
+                if (r < rows16) *reinterpret_cast<u32x4*>(xs + r * XS + c8) = buf[q];
             }
         } else {
             for (int p = tid; p < rows16 * BM; p += kGemmThreads) {
                 const int r = p / BM, c = p % BM;
-                const int64_t m = m0 + c;
-                xs[r * XS + c] = (r < rows && m < M) ? X[(t0 + r) * M + m] : (uint16_t)0;
+                const int64_t m = g.m0 + c;
+                xs[r * XS + c] = (r < g.rows && m < M) ? X[(g.t0 + r) * M + m] : (uint16_t)0;
             }
         }
-        // dY[t0 .. t0+rows16) x [n0 .. n0+BN) -> ys transposed; columns past N are zero
+        // dY stage -> ys transposed; columns past N are zero
         if (y_vec) {
-            const int np = (int)((min(N - n0, (int64_t)BN) + 7) / 8);  // 8-column pieces in this N tile
+            const int np = (int)((min(N - g.n0, (int64_t)BN) + 7) / 8);  // 8-column pieces in this N tile
             for (int p = tid; p < rows16 * np; p += kGemmThreads) {
                 const int r = p / np, c8 = (p % np) * 8;
-                const u32x4 v = r < rows ? load16(dY + (t0 + r) * N + n0 + c8) : u32x4{0u, 0u, 0u, 0u};
+                const u32x4 v = r < g.rows ? load16(dY + (g.t0 + r) * N + g.n0 + c8) : u32x4{0u, 0u, 0u, 0u};
                 ys[(c8 + 0) * YS + r] = v.x & 0xFFFF; ys[(c8 + 1) * YS + r] = v.x >> 16;
                 ys[(c8 + 2) * YS + r] = v.y & 0xFFFF; ys[(c8 + 3) * YS + r] = v.y >> 16;
                 ys[(c8 + 4) * YS + r] = v.z & 0xFFFF; ys[(c8 + 5) * YS + r] = v.z >> 16;
@@ -99,34 +146,46 @@ __global__ __launch_bounds__(kGemmThreads) void splitk_gemm_kernel(const uint16_
         } else {
             for (int p = tid; p < rows16 * BN; p += kGemmThreads) {
                 const int r = p / BN, c = p % BN;
-                const int64_t n = n0 + c;
-                ys[c * YS + r] = (r < rows && n < N) ? dY[(t0 + r) * N + n] : (uint16_t)0;
+                const int64_t n = g.n0 + c;
+                ys[c * YS + r] = (r < g.rows && n < N) ? dY[(g.t0 + r) * N + n] : (uint16_t)0;
             }
         }
         __syncthreads();
-        const int i = lane & 31, g = lane >> 5;
+        // the next unit's X is fetched while this one is computed
+        const Unit nu = next_unit(u, g);
+        const bool more = nu.item < items;
+        UnitGeom ng = g;
+        if (more) {
+            ng = geometry(nu, K, M, kc, mtiles, ntiles);
+            if (ng.x_vec) load_x(X, M, ng, buf);
+        }
+        const int i = lane & 31, h = lane >> 5;
         for (int ks = 0; ks < ksteps; ++ks) {
-            const int kk = ks * 16 + 8 * g;
+            const int kk = ks * 16 + 8 * h;
             bf16x8 a;
 #pragma unroll
             for (int e = 0; e < 8; ++e) a[e] = as_bf16(xs[(kk + e) * XS + wv * 32 + i]);
             const bf16x8 b = *reinterpret_cast<const bf16x8*>(ys + i * YS + kk);
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
         }
-        __syncthreads();
-    }
-
-    // accumulator layout of a 32x32 MFMA tile: lane holds column (lane % 32)
-    // and rows 8*(v/4) + 4*(lane/32) + (v%4) for v = 0..15
-    const int j = lane & 31, g = lane >> 5;
-    const int64_t n = n0 + j;
+        if (g.last) {
+            // accumulator layout of a 32x32 MFMA tile: lane holds column (lane % 32)
+            // and rows 8*(v/4) + 4*(lane/32) + (v%4) for v = 0..15
+            const int64_t n = g.n0 + (lane & 31);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int64_t m = m0 + wv * 32 + 8 * (v / 4) + 4 * g + (v % 4);
-        if (m < M && n < N) {
-            if (ATOMIC) unsafeAtomicAdd(out + m * N + n, acc[v]);
-            else out[(int64_t)s * M * N + m * N + n] = acc[v];
+            for (int v = 0; v < 16; ++v) {
+                const int64_t m = g.m0 + wv * 32 + 8 * (v / 4) + 4 * h + (v % 4);
+                if (m < M && n < N) {
+                    if (ATOMIC) unsafeAtomicAdd(out + m * N + n, acc[v]);
+                    else out[(int64_t)g.s * M * N + m * N + n] = acc[v];
+                }
+                acc[v] = 0.f;
+            }
         }
+        __syncthreads();
+        if (!more) break;
+        u = nu;
+        g = ng;
     }
 }
 
@@ -207,11 +266,18 @@ __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(const flo
 hipError_t launch_splitk_gemm(const uint16_t* X, const uint16_t* dY, int64_t K, int64_t M, int64_t N,
                               int32_t splits, float* out, bool atomic, hipStream_t s) {
     const int64_t kc = (K + splits - 1) / splits;
-    const dim3 grid((unsigned)((M + BM - 1) / BM), (unsigned)((N + BN - 1) / BN), (unsigned)splits);
+    const int64_t mtiles = (M + BM - 1) / BM, ntiles = (N + BN - 1) / BN;
+    const int64_t items = mtiles * ntiles * splits;
+    const Launch lc = launch_config();
+    // three workgroups fit in a CU's LDS
+    int64_t grid = lc.grid_blocks > 0 ? lc.grid_blocks : (int64_t)device_cu_count() * 3;
+    if (grid > items) grid = items;
     if (atomic)
-        hipLaunchKernelGGL(splitk_gemm_kernel<true>, grid, dim3(kGemmThreads), 0, s, X, dY, K, M, N, kc, out);
+        hipLaunchKernelGGL(splitk_gemm_kernel<true>, dim3((unsigned)grid), dim3(kGemmThreads), 0, s, X, dY, K, M, N, kc,
+                           (uint32_t)items, (uint32_t)mtiles, (uint32_t)ntiles, out);
     else
-        hipLaunchKernelGGL(splitk_gemm_kernel<false>, grid, dim3(kGemmThreads), 0, s, X, dY, K, M, N, kc, out);
+        hipLaunchKernelGGL(splitk_gemm_kernel<false>, dim3((unsigned)grid), dim3(kGemmThreads), 0, s, X, dY, K, M, N,
+                           kc, (uint32_t)items, (uint32_t)mtiles, (uint32_t)ntiles, out);
     return hipGetLastError();
 }
 

@@ -199,6 +199,22 @@ def test_fingerprint_grid_invariance(dr):
             dr.dr_set_launch_params(reset=True)
 
 
+def test_splitk_grid_invariance(dr):
+    """Persistent split-K workgroups may take any share of the (split, tile)
+    items: the partials, and so the reduced result, keep their bits."""
+    say("splitk grid invariance")
+    inp = workloads.splitk_inputs(23, 3000, 200, 24, 5)  # ragged M tile and a short last stage
+    X, dY = dev_bf16(inp.X), dev_bf16(inp.dY)
+    ref = host(dr.dr_splitk_gemm_tn(X, dY, 5))
+    for grid in (1, 3, 17, 1000):
+        dr.dr_set_launch_params(grid_blocks=grid)
+        try:
+            got = host(dr.dr_splitk_gemm_tn(X, dY, 5))
+        finally:
+            dr.dr_set_launch_params(reset=True)
+        assert_bits_equal(got, ref, f"grid {grid}")
+
+
 # ---------------------------------------------------------------------------
 # batch invariance
 # ---------------------------------------------------------------------------
