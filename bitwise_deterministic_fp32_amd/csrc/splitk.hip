@@ -4,13 +4,17 @@
 // The DeepSeek-V4 mHC backward (ch. 9, section 3.3) has an output dimension of
 // only 24.  It must split the contraction, and it keeps one buffer per split,
 // reduced afterwards by a dedicated kernel in split-id order.  Here:
-//   splitk_gemm: persistent workgroups walk (split, 32-column N tile, 64-row M
-//     tile) items in stages of up to 256 tokens (16 independent 16-byte loads
-//     per thread), staged in LDS (X row-major, dY transposed); the next
-//     stage's loads are in flight while the current one is computed.  Each of the two wavefronts accumulates a 32x32 tile with the
-//     bf16 MFMA v_mfma_f32_32x32x16_bf16, in token order, into fp32.  A partial depends
-//     only on (split, m, n): not on the grid, the M/N tiling or other columns.
-//     The HBM stream is X (read once); the MFMA work is small beside it.
+//   splitk_gemm: persistent workgroups walk contiguous ranges of (split,
+//     32-column N tile, 64-row M tile) items in stages of up to 256 tokens (16
+//     independent 16-byte loads per thread), staged in LDS (X row-major, dY
+//     transposed, dY kept while consecutive items share it); the next stage's
+//     loads are in flight while the current one is computed.  Each of the two
+//     wavefronts accumulates a 32x32 tile with the bf16 MFMA
+//     v_mfma_f32_32x32x16_bf16, in token order, into fp32, and the tile leaves
+//     through LDS as contiguous 16-byte stores.  A partial depends only on
+//     (split, m, n): not on the grid, the M/N tiling or other columns.  The HBM
+//     stream is X (read once) plus the partials (written once); the MFMA work
+//     is small beside it.
 //   splitk_reduce: out[e] = T(P_0[e], ..., P_{S-1}[e]); chunks of 8 splits left
 //     to right, then the pairwise tree, one thread per 4 consecutive elements.
 // The atomic baseline runs the same tile code and adds each split's tile into
@@ -71,10 +75,12 @@ __device__ __forceinline__ UnitGeom geometry(const Unit& u, int64_t K, int64_t M
 }
 
 __device__ __forceinline__ Unit next_unit(const Unit& u, const UnitGeom& g) {
-    return g.last ? Unit{u.item + gridDim.x, 0} : Unit{u.item, u.stage + 1};
+    return g.last ? Unit{u.item + 1, 0} : Unit{u.item, u.stage + 1};
 }
 
-// Issues the 16-byte X loads of a full-width unit (rows past the split read as zero).
+// Issues the 16-byte X loads of a full-width unit (rows past the split read as
+// zero).  Plain cached loads: for 128-byte row pieces strided by the row pitch
+// they sustain more bandwidth on gfx950 than loads with the streaming hint.
 __device__ __forceinline__ void load_x(const uint16_t* __restrict__ X, int64_t M, const UnitGeom& g,
                                        u32x4 (&buf)[kLoadsPerThread]) {
 #pragma unroll
@@ -82,14 +88,20 @@ __device__ __forceinline__ void load_x(const uint16_t* __restrict__ X, int64_t M
         const int p = threadIdx.x + q * kGemmThreads;
         const int r = p / (BM / 8), c8 = (p % (BM / 8)) * 8;
         buf[q] = u32x4{0u, 0u, 0u, 0u};
-        if (r < g.rows) buf[q] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(X + (g.t0 + r) * M + g.m0 + c8));
+        if (r < g.rows) buf[q] = *reinterpret_cast<const u32x4*>(X + (g.t0 + r) * M + g.m0 + c8);
     }
 }
 
-// Persistent workgroups walk their units in order; the X loads of the next
-// unit are issued right after the current unit is staged in LDS, so they are
-// in flight during its MFMAs and epilogue.  A partial's accumulation order
-// (token order within its split) is the same for any grid.
+// Output tile staging: fp32 [BM][OS] in the X stage's LDS, so that a split's
+// tile leaves as contiguous 16-byte stores.
+constexpr int OS = BN + 4;
+static_assert(BM * OS * 4 <= KT * XS * 2, "output tile must fit in the X stage");
+
+// Each persistent workgroup walks a contiguous range of items (consecutive M
+// tiles of one split share their dY stage, which is then staged once).  The X
+// loads of the next unit are issued right after the current unit is staged in
+// LDS, so they are in flight during its MFMAs and epilogue.  A partial's
+// accumulation order (token order within its split) is the same for any grid.
 template <bool ATOMIC>
 __global__ __launch_bounds__(kGemmThreads) void splitk_gemm_kernel(const uint16_t* __restrict__ X,
                                                                    const uint16_t* __restrict__ dY, int64_t K,
@@ -100,8 +112,13 @@ __global__ __launch_bounds__(kGemmThreads) void splitk_gemm_kernel(const uint16_
     __shared__ __attribute__((aligned(16))) uint16_t ys[BN * YS];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const bool y_vec = (N % 8) == 0 && (reinterpret_cast<uintptr_t>(dY) & 15) == 0;
-    Unit u{blockIdx.x, 0};
-    if (u.item >= items) return;
+    const bool out_vec = (N % 4) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+    // 32-bit range split: the host keeps items < 2^31 and the grid <= items
+    const uint32_t per = items / gridDim.x, extra = items % gridDim.x, wg = blockIdx.x;
+    const uint32_t begin = wg * per + min(wg, extra), end = begin + per + (wg < extra ? 1u : 0u);
+    if (begin >= end) return;
+    Unit u{begin, 0};
+    int64_t staged_t0 = -1, staged_n0 = -1;  // the dY stage held in ys
     UnitGeom g = geometry(u, K, M, kc, mtiles, ntiles);
     u32x4 buf[kLoadsPerThread];
     if (g.x_vec) load_x(X, M, g, buf);
@@ -129,7 +146,10 @@ __global__ __launch_bounds__(kGemmThreads) void splitk_gemm_kernel(const uint16_
             }
         }
         // dY stage -> ys transposed; columns past N are zero
-        if (y_vec) {
+        const bool stage_y = g.t0 != staged_t0 || g.n0 != staged_n0;
+        staged_t0 = g.t0;
+        staged_n0 = g.n0;
+        if (stage_y && y_vec) {
             const int np = (int)((min(N - g.n0, (int64_t)BN) + 7) / 8);  // 8-column pieces in this N tile
             for (int p = tid; p < rows16 * np; p += kGemmThreads) {
                 const int r = p / np, c8 = (p % np) * 8;
@@ -143,7 +163,7 @@ __global__ __launch_bounds__(kGemmThreads) void splitk_gemm_kernel(const uint16_
                 const int c = np * 8 + p / (rows16 / 8), r8 = (p % (rows16 / 8)) * 8;
                 *reinterpret_cast<u32x4*>(ys + c * YS + r8) = u32x4{0u, 0u, 0u, 0u};
             }
-        } else {
+        } else if (stage_y) {
             for (int p = tid; p < rows16 * BN; p += kGemmThreads) {
                 const int r = p / BN, c = p % BN;
                 const int64_t n = g.n0 + c;
@@ -153,7 +173,7 @@ __global__ __launch_bounds__(kGemmThreads) void splitk_gemm_kernel(const uint16_
         __syncthreads();
         // the next unit's X is fetched while this one is computed
         const Unit nu = next_unit(u, g);
-        const bool more = nu.item < items;
+        const bool more = nu.item < end;
         UnitGeom ng = g;
         if (more) {
             ng = geometry(nu, K, M, kc, mtiles, ntiles);
@@ -168,18 +188,38 @@ __global__ __launch_bounds__(kGemmThreads) void splitk_gemm_kernel(const uint16_
             const bf16x8 b = *reinterpret_cast<const bf16x8*>(ys + i * YS + kk);
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
         }
-        if (g.last) {
-            // accumulator layout of a 32x32 MFMA tile: lane holds column (lane % 32)
-            // and rows 8*(v/4) + 4*(lane/32) + (v%4) for v = 0..15
+        // accumulator layout of a 32x32 MFMA tile: lane holds column (lane % 32)
+        // and rows 8*(v/4) + 4*(lane/32) + (v%4) for v = 0..15
+        if (ATOMIC && g.last) {
             const int64_t n = g.n0 + (lane & 31);
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int64_t m = g.m0 + wv * 32 + 8 * (v / 4) + 4 * h + (v % 4);
-                if (m < M && n < N) {
-                    if (ATOMIC) unsafeAtomicAdd(out + m * N + n, acc[v]);
-                    else out[(int64_t)g.s * M * N + m * N + n] = acc[v];
-                }
+                if (m < M && n < N) unsafeAtomicAdd(out + m * N + n, acc[v]);
                 acc[v] = 0.f;
+            }
+        } else if (g.last) {
+            __syncthreads();  // xs is free: it now holds the output tile
+            float* ot = reinterpret_cast<float*>(xs);
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                ot[(wv * 32 + 8 * (v / 4) + 4 * h + (v % 4)) * OS + i] = acc[v];
+                acc[v] = 0.f;
+            }
+            __syncthreads();
+            const int rows_out = (int)min(M - g.m0, (int64_t)BM), cols = (int)min(N - g.n0, (int64_t)BN);
+            float* dst = out + (int64_t)g.s * M * N + g.m0 * N + g.n0;
+            if (out_vec) {
+                const int q4 = cols / 4;
+                for (int p = tid; p < rows_out * q4; p += kGemmThreads) {
+                    const int r = p / q4, c = (p % q4) * 4;
+                    store16_stream(dst + (int64_t)r * N + c, *reinterpret_cast<const u32x4*>(ot + r * OS + c));
+                }
+            } else {
+                for (int p = tid; p < rows_out * cols; p += kGemmThreads) {
+                    const int r = p / cols, c = p % cols;
+                    dst[(int64_t)r * N + c] = ot[r * OS + c];
+                }
             }
         }
         __syncthreads();
@@ -269,7 +309,7 @@ hipError_t launch_splitk_gemm(const uint16_t* X, const uint16_t* dY, int64_t K, 
     const int64_t mtiles = (M + BM - 1) / BM, ntiles = (N + BN - 1) / BN;
     const int64_t items = mtiles * ntiles * splits;
     const Launch lc = launch_config();
-    // three workgroups fit in a CU's LDS
+    // three workgroups fit in a CU's LDS; each takes a contiguous range of items
     int64_t grid = lc.grid_blocks > 0 ? lc.grid_blocks : (int64_t)device_cu_count() * 3;
     if (grid > items) grid = items;
     if (atomic)

@@ -79,7 +79,7 @@ typedef enum dr_dtype { DR_F32 = 0, DR_BF16 = 1 } dr_dtype;
  * the library default.  The setting is thread-local. */
 typedef struct dr_launch_params {
     int32_t grid_blocks;        /* workgroups of the persistent kernels (index_add reduce and tile
-                                   combine, fingerprint), 1 .. 65536 */
+                                   combine, split-K partials, fingerprint), 1 .. 65536 */
     int32_t tile_chunks_log2;   /* index_add tile = 2^m chunks of 8 rows, m in [3, 7] (default 5) */
     int32_t sort_tile_log2;     /* radix sort keys per workgroup = 2^m, m in [8, 12] (default: about
                                    n / 512, clamped to that range) */
