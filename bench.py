@@ -21,7 +21,6 @@ tiny_moe_combine) print the same kind of line for their own step.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -77,27 +76,6 @@ class Timer:
         for i, name in enumerate(self.phases):
             out[name] = float(np.mean([e[i].elapsed_time(e[i + 1]) for e in self.events]))
         return out
-
-
-def source_digest(*names) -> str:
-    h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "bitwise_deterministic_fp32_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
-def measured_traffic(kernel: str, workload: str, digest: str):
-    """HBM bytes per launch from a committed rocprofv3 PMC summary, if it was taken
-    on the current kernel source (else None)."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        rec = json.load(f).get(f"{kernel}/{workload}")
-    if not rec or rec.get("source_digest") != digest:
-        return None
-    return rec.get("hbm_bytes_per_launch")
 
 
 # ---------------------------------------------------------------------------
@@ -198,6 +176,7 @@ def bench_moe(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
 
     comb_ms = phases["combine_fingerprinted"]
     achieved = combine_bytes / (comb_ms * 1e-3) / 1e9
+    from bench_workloads import measured_traffic, source_digest
     digest = source_digest("combine.hip", "internal.h")
     result = {
         "ms_per_step": ms_per_step,

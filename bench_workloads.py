@@ -11,12 +11,38 @@ splitk_mhc: a step is dr_splitk_gemm_tn (64 private fp32 partials by bf16
 """
 from __future__ import annotations
 
+import hashlib
+import json
+import os
 import time
 
 import numpy as np
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def source_digest(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "bitwise_deterministic_fp32_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str, digest: str):
+    """HBM bytes per launch from a committed rocprofv3 PMC summary, if it was taken
+    on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(f"{kernel}/{workload}")
+    if not rec or rec.get("source_digest") != digest:
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def _log(msg):
@@ -114,7 +140,9 @@ def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
                    "step_algorithmic_bytes": step_bytes},
         "roofline": {"bound": "hbm", "kernel": "dr_index_add call (sort, plan, segreduce, tilecombine)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("dr_index_add", name,
+                                                 source_digest("sort.hip", "segreduce.hip", "internal.h")),
                      "algorithmic_bytes_per_launch": red_bytes, "avg_launch_ms": round(det_ms, 4)},
         "phases_ms": {k: round(v, 4) for k, v in ph.items()},
         "reused_plan_ms": round(ms_plan, 4), "sort_only_ms": round(ms_sort, 4),
@@ -204,7 +232,8 @@ def _splitk(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
                    "step": "MFMA partials + ordered split reduce + fingerprint", "step_algorithmic_bytes": step_bytes},
         "roofline": {"bound": "hbm", "kernel": "splitk_gemm_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "algorithmic_bytes_per_launch": gemm_bytes, "avg_launch_ms": round(g_ms, 4),
+                     "traffic": measured_traffic("splitk_gemm_kernel", name, source_digest("splitk.hip", "internal.h")),
+                     "algorithmic_bytes_per_launch": gemm_bytes, "avg_launch_ms": round(g_ms, 4),
                      "mfma_tflops": round(flops / (g_ms * 1e-3) / 1e12, 2),
                      "mfma_frac_of_bf16_peak": round(flops / (g_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 5)},
         "phases_ms": {k: round(v, 4) for k, v in ph.items()},
