@@ -452,8 +452,10 @@ uint64_t oracle_splitmix64_mix(uint64_t z)
  * a SplitMix64 generator started at 0.  For all-zero bytes each term is that
  * generator's published output.  Wrapping addition makes the value
  * independent of the order in which the terms are added.
- * parity unpinned: the composition is this library's convention; its pieces
- * are pinned by the published SplitMix64 outputs. */
+ * The composition is this library's convention (the pages name a tensor hash
+ * without defining one).  It is pinned by the published SplitMix64 outputs:
+ * words chosen as s_i XOR s_j turn term i into output j, which fixes the XOR,
+ * the word index, the byte order and the zero padding. */
 uint64_t oracle_fingerprint(const void* data, int64_t nbytes)
 {
     const unsigned char* p = (const unsigned char*)data;

@@ -467,6 +467,33 @@ def test_fingerprint_of_zero_bytes_is_the_splitmix64_sequence(golden_dir):
         assert oracle.fingerprint(np.zeros(8 * w, np.uint8)) == want
 
 
+def test_fingerprint_of_chosen_words_hits_published_outputs(golden_dir):
+    """A data word w_i = (i+1)*gamma XOR (j+1)*gamma turns term i into the
+    published output j+1.  Words are assembled little-endian and a short last
+    word is zero-padded, so the bytes below (and a 3-byte zero tail) fix the
+    XOR, the word index, the byte order and the padding against published
+    values."""
+    g = read_golden(os.path.join(golden_dir, "splitmix64_seed0.txt"))
+    gamma = int(g["gamma"], 16)
+    outs = {i: int(g[str(i)], 16) for i in (1, 2, 3)}
+    M = 2 ** 64
+
+    def words_to_bytes(ws):
+        return np.frombuffer(b"".join(int(w).to_bytes(8, "little") for w in ws), np.uint8).copy()
+
+    for targets in ([2], [3], [1, 3], [3, 1], [2, 2, 2], [3, 1, 2]):
+        ws = [((i + 1) * gamma % M) ^ (j * gamma % M) for i, j in enumerate(targets)]
+        data = words_to_bytes(ws)
+        want = (oracle.splitmix64_mix(len(data)) + sum(outs[j] for j in targets)) % M
+        assert oracle.fingerprint(data) == want, targets
+        # a zero tail shorter than a word is padded into one more zero word
+        i = len(targets)
+        tail = np.concatenate([data, np.zeros(3, np.uint8)])
+        want_tail = (oracle.splitmix64_mix(len(tail)) + sum(outs[j] for j in targets)
+                     + oracle.splitmix64_mix((i + 1) * gamma % M)) % M
+        assert oracle.fingerprint(tail) == want_tail, targets
+
+
 def test_fingerprint_properties():
     rng = np.random.default_rng(60)
     data = rng.integers(0, 256, 1003, dtype=np.uint8)
