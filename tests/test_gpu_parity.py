@@ -164,6 +164,9 @@ def test_index_add_order_example_fp32(dr):
     (777, 72, 40, 5),       # two N tiles, ragged
     (256, 64, 1, 1),
     (300, 1, 24, 3),
+    (2000, 136, 24, 3),     # three 256-token stages per split, the last one short
+    (1500, 128, 20, 1),     # six stages; N not a multiple of 8 (scalar dY staging)
+    (600, 64, 36, 2),       # second N tile of 4 columns
 ])
 def test_splitk_matches_oracle(dr, K, M, N, splits):
     say(f"splitk K={K} M={M} N={N} S={splits}")
