@@ -177,7 +177,7 @@ def bench_moe(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
     comb_ms = phases["combine_fingerprinted"]
     achieved = combine_bytes / (comb_ms * 1e-3) / 1e9
     from bench_workloads import measured_traffic, source_digest
-    digest = source_digest("combine.hip", "internal.h")
+    digest = source_digest("combine.hip", "device.h")
     result = {
         "ms_per_step": ms_per_step,
         "value": step_bytes / (ms_per_step * 1e-3) / 1e9,

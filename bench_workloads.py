@@ -142,7 +142,7 @@ def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("dr_index_add", name,
-                                                 source_digest("sort.hip", "segreduce.hip", "internal.h")),
+                                                 source_digest("sort.hip", "segreduce.hip", "internal.h", "device.h")),
                      "algorithmic_bytes_per_launch": red_bytes, "avg_launch_ms": round(det_ms, 4)},
         "phases_ms": {k: round(v, 4) for k, v in ph.items()},
         "reused_plan_ms": round(ms_plan, 4), "sort_only_ms": round(ms_sort, 4),
@@ -232,7 +232,7 @@ def _splitk(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
                    "step": "MFMA partials + ordered split reduce + fingerprint", "step_algorithmic_bytes": step_bytes},
         "roofline": {"bound": "hbm", "kernel": "splitk_gemm_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("splitk_gemm_kernel", name, source_digest("splitk.hip", "internal.h")),
+                     "traffic": measured_traffic("splitk_gemm_kernel", name, source_digest("splitk.hip", "device.h")),
                      "algorithmic_bytes_per_launch": gemm_bytes, "avg_launch_ms": round(g_ms, 4),
                      "mfma_tflops": round(flops / (g_ms * 1e-3) / 1e12, 2),
                      "mfma_frac_of_bf16_peak": round(flops / (g_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 5)},

@@ -92,6 +92,7 @@ std::vector<DigitPass> sort_passes(int32_t num_dests, bool has_src, int32_t src_
 
 struct SortBuffers {
     int32_t* hist;
+    int32_t* tile_flags;  // first pass: index-error flag per tile
     int32_t* totals;
     int32_t *dest_a, *dest_b, *val_a, *val_b, *src_a, *src_b;
     int64_t nblocks;
@@ -101,6 +102,7 @@ SortBuffers carve_sort(Carver& c, int64_t n, bool has_src, int tile_log2) {
     SortBuffers b{};
     b.nblocks = (n + ((int64_t)1 << tile_log2) - 1) >> tile_log2;
     b.hist = c.take<int32_t>((int64_t)(1 << dr::kMaxDigitBits) * b.nblocks);
+    b.tile_flags = c.take<int32_t>(b.nblocks);
     b.totals = c.take<int32_t>(1 << dr::kMaxDigitBits);
     b.dest_a = c.take<int32_t>(n);
     b.dest_b = c.take<int32_t>(n);
@@ -111,7 +113,9 @@ SortBuffers carve_sort(Carver& c, int64_t n, bool has_src, int tile_log2) {
     return b;
 }
 
-// Launches the stable sort; the status word must already be cleared.
+// Launches the stable sort.  It writes the status word itself (the first
+// pass's scan sets or clears the index-error bit), so no reset launch is
+// needed before it.
 dr_status run_sort(const int32_t* dest, const int32_t* src_id, int32_t src_bound, int64_t n, int32_t num_dests,
                    int32_t* perm, int32_t* seg_offsets, int32_t* inv_perm, int32_t* status, const SortBuffers& b,
                    int tile_log2, hipStream_t s) {
@@ -119,6 +123,10 @@ dr_status run_sort(const int32_t* dest, const int32_t* src_id, int32_t src_bound
     const std::vector<DigitPass> passes = sort_passes(num_dests, has_src, src_bound);
     int src_passes = 0;
     for (const DigitPass& p : passes) src_passes += p.from_src;
+    // with no keys no pass runs: the status is cleared here instead
+    if (n == 0) DR_TRY_HIP(dr::launch_fill_status(status, s), "status reset launch");
+    // a single destination pass sees whole destinations: its scatter writes seg_offsets
+    const bool seg_in_scatter = n > 0 && (int)passes.size() - src_passes == 1;
     const int32_t* cur_dest = dest;
     const int32_t* cur_src = src_id;
     const int32_t* cur_val = nullptr;
@@ -131,25 +139,31 @@ dr_status run_sort(const int32_t* dest, const int32_t* src_id, int32_t src_bound
         sp.shift = passes[i].shift;
         sp.bits = passes[i].bits;
         sp.dest_in = cur_dest;
-        sp.dest_out = odd ? b.dest_b : b.dest_a;
+        // the last pass's sorted keys are only needed by the segment-offset search
+        sp.dest_out = last && seg_in_scatter ? nullptr : (odd ? b.dest_b : b.dest_a);
         sp.src_in = (carry_src || passes[i].from_src) ? cur_src : nullptr;
         sp.src_out = carry_src ? (odd ? b.src_b : b.src_a) : nullptr;
         sp.val_in = cur_val;
         sp.val_out = last ? perm : (odd ? b.val_b : b.val_a);
         sp.inv_out = last ? inv_perm : nullptr;
+        sp.seg_out = last && seg_in_scatter ? seg_offsets : nullptr;
+        sp.num_dests = num_dests;
         if (i == 0)
             DR_TRY_HIP(dr::launch_radix_validate_hist(dest, num_dests, src_id, src_bound, sp, n, tile_log2, b.hist,
-                                                      status, s),
+                                                      b.tile_flags, s),
                        "radix histogram launch");
         else
             DR_TRY_HIP(dr::launch_radix_hist(sp, n, tile_log2, b.hist, status, s), "radix histogram launch");
-        DR_TRY_HIP(dr::launch_radix_scan(b.hist, b.nblocks, 1 << sp.bits, b.totals, status, s), "radix scan launch");
+        DR_TRY_HIP(dr::launch_radix_scan(b.hist, b.nblocks, 1 << sp.bits, b.totals, status,
+                                         i == 0 ? b.tile_flags : nullptr, s),
+                   "radix scan launch");
         DR_TRY_HIP(dr::launch_radix_scatter(sp, n, tile_log2, b.hist, b.totals, status, s), "radix scatter launch");
         cur_dest = sp.dest_out;
         cur_src = sp.src_out;
         cur_val = sp.val_out;
     }
-    DR_TRY_HIP(dr::launch_seg_offsets(cur_dest, n, num_dests, seg_offsets, status, s), "segment offsets launch");
+    if (!seg_in_scatter)
+        DR_TRY_HIP(dr::launch_seg_offsets(cur_dest, n, num_dests, seg_offsets, status, s), "segment offsets launch");
     return DR_OK;
 }
 
@@ -310,7 +324,6 @@ dr_status dr_sort_by_dest(const int32_t* dest, const int32_t* src_id, int32_t sr
     const SortBuffers b = carve_sort(c, n, src_id != nullptr, tile_log2);
     if (c.off > ws_bytes)
         return fail(DR_ERR_WORKSPACE_TOO_SMALL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes, c.off);
-    DR_TRY_HIP(dr::launch_fill_status(status, stream), "status reset launch");
     const dr_status st = run_sort(dest, src_id, src_id_bound, n, num_dests, perm, seg_offsets, inv_perm, status, b,
                                   tile_log2, stream);
     return st == DR_OK ? ok() : st;
@@ -440,16 +453,17 @@ dr_status dr_index_add(float* out, int32_t num_dests, int64_t hidden, const void
                                               lc.sort_tile(n));
     if (c.off > ws_bytes)
         return fail(DR_ERR_WORKSPACE_TOO_SMALL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes, c.off);
-    DR_TRY_HIP(dr::launch_fill_status(b.status, stream), "status reset launch");
     const int32_t* p = perm;
     const int32_t* seg = seg_offsets;
     if (sort_inside) {
+        // the sort writes the status word
         st = run_sort(index, nullptr, 0, n, num_dests, b.perm, b.seg, nullptr, b.status, b.sort, lc.sort_tile(n),
                       stream);
         if (st != DR_OK) return st;
         p = b.perm;
         seg = b.seg;
     } else {
+        DR_TRY_HIP(dr::launch_fill_status(b.status, stream), "status reset launch");
         DR_TRY_HIP(dr::launch_plan_validate(perm, seg_offsets, index, n, num_dests, b.status, stream),
                    "plan validation launch");
     }

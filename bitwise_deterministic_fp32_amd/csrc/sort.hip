@@ -10,11 +10,18 @@
 //
 // Pass structure (per digit of up to 9 bits):
 //   radix_hist:    digit counts of each tile of keys (LDS, wave-aggregated).
+//                  The first pass also checks every index and leaves one
+//                  error flag per tile.
 //   radix_scan:    one workgroup per digit scans that digit's counts over the
-//                  tiles; totals per digit.
+//                  tiles; totals per digit.  On the first pass one more
+//                  workgroup folds the tile flags into the call's status word
+//                  (set or cleared), so no separate reset launch is needed.
 //   radix_scatter: recomputes each key's stable rank inside its tile, stages
 //                  the tile in LDS in digit order, then writes each digit's run
-//                  to consecutive output positions (coalesced stores).
+//                  to consecutive output positions (coalesced stores).  When
+//                  the pass's digit is the whole destination (one dest pass),
+//                  workgroup 0 also writes the segment offsets, which are the
+//                  digit prefix sums it has already formed.
 #include "internal.h"
 
 namespace dr {
@@ -92,10 +99,11 @@ template <bool kValidate, int ITEMS>
 __global__ __launch_bounds__(kThreads) void radix_hist_kernel(SortPass p, int64_t n, int tile_log2, int32_t* hist,
                                                               int64_t nblocks, const int32_t* __restrict__ dest,
                                                               int32_t num_dests, const int32_t* __restrict__ src_id,
-                                                              int32_t src_bound, int32_t* status) {
+                                                              int32_t src_bound, int32_t* status_or_flags) {
     __shared__ int32_t cnt[kMaxBins];
     __shared__ int32_t bad;
-    if (!kValidate && status[kWordStatus] != 0) return;  // same value for every thread
+    // later passes: status word (same value for every thread); first pass: tile flags
+    if (!kValidate && status_or_flags[kWordStatus] != 0) return;
     const int bins = 1 << p.bits;
     for (int d = threadIdx.x; d < bins; d += kThreads) cnt[d] = 0;
     if (threadIdx.x == 0) bad = 0;
@@ -133,15 +141,27 @@ __global__ __launch_bounds__(kThreads) void radix_hist_kernel(SortPass p, int64_
     if (my_bad) bad = 1;
     __syncthreads();
     for (int d = threadIdx.x; d < bins; d += kThreads) hist[(int64_t)d * nblocks + blockIdx.x] = cnt[d];
-    if (kValidate && threadIdx.x == 0 && bad) atomicOr(&status[kWordStatus], kStatusIndex);
+    if (kValidate && threadIdx.x == 0) status_or_flags[blockIdx.x] = bad;
 }
 
 // One workgroup per digit: exclusive scan of that digit's counts over the
-// tiles (in place), and the digit's total.
+// tiles (in place), and the digit's total.  With tile_flags (first pass), the
+// last workgroup writes the status word from the flags instead; the digit
+// workgroups then scan regardless (the counts stay consistent for any key).
 __global__ __launch_bounds__(kThreads) void radix_scan_kernel(int32_t* hist, int64_t nblocks, int32_t* totals,
-                                                              const int32_t* status) {
+                                                              int32_t* status, const int32_t* tile_flags) {
     __shared__ int32_t wave_tot[kWaves];
-    if (status[kWordStatus] != 0) return;
+    if (tile_flags) {
+        if (blockIdx.x == gridDim.x - 1) {
+            int32_t any = 0;
+            for (int64_t b = threadIdx.x; b < nblocks; b += kThreads) any |= tile_flags[b];
+            any = __syncthreads_or(any);
+            if (threadIdx.x == 0) status[kWordStatus] = any ? kStatusIndex : 0;
+            return;
+        }
+    } else if (status[kWordStatus] != 0) {
+        return;
+    }
     int32_t* h = hist + (int64_t)blockIdx.x * nblocks;
     int32_t carry = 0;
     for (int64_t b0 = 0; b0 < nblocks; b0 += kThreads) {
@@ -237,7 +257,13 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(SortPass p, int
     __syncthreads();
     scan_bins_in_place(gbase, bins, wave_tot);
     scan_bins_in_place(lbase, bins, wave_tot);
-    for (int d = tid; d < bins; d += kThreads) gbase[d] += hist[(int64_t)d * nblocks + blockIdx.x];
+    // gbase[d] now counts all keys of digits below d
+    int32_t* seg = blockIdx.x == 0 ? p.seg_out : nullptr;
+    for (int d = tid; d < bins; d += kThreads) {
+        if (seg && d <= p.num_dests) seg[d] = gbase[d];
+        gbase[d] += hist[(int64_t)d * nblocks + blockIdx.x];
+    }
+    if (seg && tid == 0 && p.num_dests == bins) seg[bins] = (int32_t)n;
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < ITEMS; ++r) {
@@ -303,12 +329,12 @@ static int64_t tiles_for(int64_t n, int tile_log2) { return (n + ((int64_t)1 << 
 
 hipError_t launch_radix_validate_hist(const int32_t* dest, int32_t num_dests, const int32_t* src_id,
                                       int32_t src_bound, const SortPass& p, int64_t n, int tile_log2,
-                                      int32_t* hist, int32_t* status, hipStream_t s) {
+                                      int32_t* hist, int32_t* tile_flags, hipStream_t s) {
     const int64_t nb = tiles_for(n, tile_log2);
     if (nb == 0) return hipSuccess;
 #define DR_H(IT)                                                                                              \
     hipLaunchKernelGGL((radix_hist_kernel<true, IT>), dim3((unsigned)nb), dim3(kThreads), 0, s, p, n, tile_log2, \
-                       hist, nb, dest, num_dests, src_id, src_bound, status)
+                       hist, nb, dest, num_dests, src_id, src_bound, tile_flags)
     DR_BY_ITEMS(tile_log2, DR_H)
 #undef DR_H
     return hipGetLastError();
@@ -326,10 +352,11 @@ hipError_t launch_radix_hist(const SortPass& p, int64_t n, int tile_log2, int32_
     return hipGetLastError();
 }
 
-hipError_t launch_radix_scan(int32_t* hist, int64_t nblocks, int bins, int32_t* totals, const int32_t* status,
-                             hipStream_t s) {
+hipError_t launch_radix_scan(int32_t* hist, int64_t nblocks, int bins, int32_t* totals, int32_t* status,
+                             const int32_t* tile_flags, hipStream_t s) {
     if (nblocks == 0) return hipSuccess;
-    hipLaunchKernelGGL(radix_scan_kernel, dim3(bins), dim3(kThreads), 0, s, hist, nblocks, totals, status);
+    hipLaunchKernelGGL(radix_scan_kernel, dim3(bins + (tile_flags ? 1 : 0)), dim3(kThreads), 0, s, hist, nblocks,
+                       totals, status, tile_flags);
     return hipGetLastError();
 }
 
