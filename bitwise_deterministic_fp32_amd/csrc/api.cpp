@@ -355,7 +355,7 @@ dr_status dr_combine(const void* rows, dr_dtype rows_dtype, int64_t num_rows, in
 
 size_t dr_combine_fingerprinted_workspace_size(dr_dtype rows_dtype, int64_t hidden, int64_t T) {
     if (hidden < 1 || T < 0) return dr::kStatusBytes;
-    const int64_t nb = dr::combine_blocks(rows_dtype, hidden, T);
+    const int64_t nb = dr::combine_fp_blocks(rows_dtype, hidden, T, 64);  // the largest count over k
     return dr::kStatusBytes + align_up((size_t)nb * sizeof(uint64_t)) +
            align_up((size_t)dr::fingerprint_group_count(nb) * sizeof(uint64_t));
 }
@@ -383,11 +383,12 @@ dr_status dr_combine_fingerprinted(const void* rows, dr_dtype rows_dtype, int64_
     if (dev_status && !aligned(dev_status, 4)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: misaligned dev_status", what);
     if (T * ((hidden / elems16(rows_dtype) + 63) / 64) >= ((int64_t)1 << 32))
         return fail(DR_ERR_UNSUPPORTED, "%s: T * column slices must be below 2^32", what);
-    const int64_t nb = dr::combine_blocks(rows_dtype, hidden, T);
+    const int64_t nb_max = dr::combine_fp_blocks(rows_dtype, hidden, T, 64);
+    const int64_t nb = dr::combine_fp_blocks(rows_dtype, hidden, T, k);
     Carver c(ws);
     c.take<uint8_t>(dr::kStatusBytes);
-    uint64_t* partials = c.take<uint64_t>(nb);
-    uint64_t* group_sums = c.take<uint64_t>(dr::fingerprint_group_count(nb));
+    uint64_t* partials = c.take<uint64_t>(nb_max);
+    uint64_t* group_sums = c.take<uint64_t>(dr::fingerprint_group_count(nb_max));
     DR_TRY_HIP(dr::launch_combine(rows, rows_dtype, num_rows, hidden, row_of, gates, T, k, out, dev_status, false,
                                   partials, stream),
                "combine launch");

@@ -21,6 +21,10 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / 64;
+// The fingerprinting launch for k <= 8 uses 16-wavefront workgroups: a
+// quarter as many partial sums to fold afterwards.  (Larger k needs more
+// registers than a 1024-thread workgroup leaves a lane.)
+constexpr int kFpThreads = 1024;
 
 __device__ __forceinline__ int32_t uniform_lane(int32_t v, int lane) {
     return __builtin_amdgcn_readlane(v, lane);
@@ -201,14 +205,14 @@ __device__ __forceinline__ uint64_t combine_token(const void* __restrict__ rows,
 // One wavefront per (token, column slice).  With FP, the workgroup also sums
 // the fingerprint terms of what it stored into fp_partials[blockIdx.x]
 // (wrapping addition, so the total does not depend on the grid).
-template <dr_dtype DT, int KMAX, bool FP>
-__global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restrict__ rows, int64_t num_rows, int64_t H,
+template <dr_dtype DT, int KMAX, bool FP, int THREADS>
+__global__ __launch_bounds__(THREADS) void combine_kernel(const void* __restrict__ rows, int64_t num_rows, int64_t H,
                                                            const int32_t* __restrict__ row_of,
                                                            const float* __restrict__ gates, int64_t T, int k,
                                                            float* __restrict__ out, int32_t* dev_status,
                                                            int64_t slices, uint64_t* __restrict__ fp_partials) {
     // the host keeps T * slices below 2^32
-    const uint32_t wave = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    const uint32_t wave = blockIdx.x * (THREADS / 64) + (threadIdx.x >> 6);
     const uint32_t t32 = wave / (uint32_t)slices;
     uint64_t hash = 0;
     if (t32 < T) {  // whole wavefront
@@ -217,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const void* __restric
                                            wave - t32 * (uint32_t)slices);
     }
     if (FP) {
-        __shared__ uint64_t smem[kWavesPerBlock];
+        __shared__ uint64_t smem[THREADS / 64];
         const uint64_t s = block_sum_u64(hash, smem);
         if (threadIdx.x == 0) fp_partials[blockIdx.x] = s;
     }
@@ -283,16 +287,15 @@ hipError_t launch_dt(const void* rows, int64_t num_rows, int64_t H, const int32_
         return hipGetLastError();
     }
     const int64_t waves = T * slices;
-    const dim3 grid((unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock));
-#define DR_COMBINE(KM, FPV)                                                                                      \
-    hipLaunchKernelGGL((combine_kernel<DT, KM, FPV>), grid, dim3(kThreads), 0, s, rows, num_rows, H, row_of, gates, \
-                       T, k, out, dev_status, slices, fp_partials)
+#define DR_COMBINE(KM, FPV, TH)                                                                                 \
+    hipLaunchKernelGGL((combine_kernel<DT, KM, FPV, TH>), dim3((unsigned)((waves + TH / 64 - 1) / (TH / 64))), \
+                       dim3(TH), 0, s, rows, num_rows, H, row_of, gates, T, k, out, dev_status, slices, fp_partials)
     if (fp_partials) {
-        if (k <= 8) DR_COMBINE(8, true);
-        else DR_COMBINE(64, true);
+        if (k <= 8) DR_COMBINE(8, true, kFpThreads);
+        else DR_COMBINE(64, true, kThreads);
     } else {
-        if (k <= 8) DR_COMBINE(8, false);
-        else DR_COMBINE(64, false);
+        if (k <= 8) DR_COMBINE(8, false, kThreads);
+        else DR_COMBINE(64, false, kThreads);
     }
 #undef DR_COMBINE
     return hipGetLastError();
@@ -300,10 +303,11 @@ hipError_t launch_dt(const void* rows, int64_t num_rows, int64_t H, const int32_
 
 }  // namespace
 
-int64_t combine_blocks(dr_dtype dt, int64_t hidden, int64_t T) {
+int64_t combine_fp_blocks(dr_dtype dt, int64_t hidden, int64_t T, int32_t k) {
     const int64_t per_wave = 64 * (dt == DR_BF16 ? 8 : 4);
     const int64_t slices = (hidden + per_wave - 1) / per_wave;
-    return (T * slices + kWavesPerBlock - 1) / kWavesPerBlock;
+    const int64_t waves_per_block = (k <= 8 ? kFpThreads : kThreads) / 64;
+    return (T * slices + waves_per_block - 1) / waves_per_block;
 }
 
 hipError_t launch_combine(const void* rows, dr_dtype dt, int64_t num_rows, int64_t hidden, const int32_t* row_of,

@@ -70,6 +70,29 @@ __global__ __launch_bounds__(kThreads) void fp_final_kernel(const uint64_t* __re
     if (threadIdx.x == 0) *out = s + mix64((uint64_t)nbytes);
 }
 
+// One wide workgroup folds up to kWideMax partials (eight loads in flight per
+// thread) and adds the length term.
+constexpr int kWideThreads = 1024;
+constexpr int64_t kWideMax = 64 * kWideThreads;
+__global__ __launch_bounds__(kWideThreads) void fp_final_wide_kernel(const uint64_t* __restrict__ partials,
+                                                                     int64_t nblocks, int64_t nbytes,
+                                                                     uint64_t* __restrict__ out) {
+    __shared__ uint64_t smem[kWideThreads / 64];
+    uint64_t acc = 0;
+    for (int64_t b0 = 0; b0 < nblocks; b0 += 8 * kWideThreads) {
+        uint64_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t i = b0 + u * kWideThreads + threadIdx.x;
+            v[u] = i < nblocks ? partials[i] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += v[u];
+    }
+    const uint64_t s = block_sum_u64(acc, smem);
+    if (threadIdx.x == 0) *out = s + mix64((uint64_t)nbytes);
+}
+
 }  // namespace
 
 int64_t fingerprint_blocks(int64_t nbytes) {
@@ -101,6 +124,11 @@ int64_t fingerprint_group_count(int64_t nblocks) { return (nblocks + kGroup - 1)
 
 hipError_t launch_fingerprint_final(const uint64_t* block_partials, int64_t nblocks, int64_t nbytes, uint64_t* out,
                                     uint64_t* group_sums, hipStream_t s) {
+    if (nblocks > kGroup && nblocks <= kWideMax) {
+        hipLaunchKernelGGL(fp_final_wide_kernel, dim3(1), dim3(kWideThreads), 0, s, block_partials, nblocks, nbytes,
+                           out);
+        return hipGetLastError();
+    }
     if (nblocks > kGroup && group_sums) {
         // two levels: many workgroups fold the partials, one folds their sums
         const int64_t groups = fingerprint_group_count(nblocks);

@@ -142,8 +142,9 @@ hipError_t launch_fingerprint(const void* data, int64_t nbytes, uint64_t* out, u
 int64_t fingerprint_group_count(int64_t nblocks);
 hipError_t launch_fingerprint_final(const uint64_t* block_partials, int64_t nblocks, int64_t nbytes, uint64_t* out,
                                     uint64_t* group_sums, hipStream_t s);
-// number of workgroups (and fingerprint partials) of a combine launch
-int64_t combine_blocks(dr_dtype dt, int64_t hidden, int64_t T);
+// number of workgroups (and fingerprint partials) of a fingerprinting combine launch
+// (k = 64 gives the largest count, for any k)
+int64_t combine_fp_blocks(dr_dtype dt, int64_t hidden, int64_t T, int32_t k);
 
 }  // namespace dr
 
