@@ -27,9 +27,9 @@ constexpr int kDefaultTileChunksLog2 = 5;
 constexpr int kMinTileChunksLog2 = 3;
 constexpr int kMaxTileChunksLog2 = 7;
 constexpr int kMinSortTileLog2 = 8;
-constexpr int kMaxSortTileLog2 = 12;
+constexpr int kMaxSortTileLog2 = 13;
 constexpr int kMaxDigitBits = 9;  // radix digits of up to 9 bits (512 bins)
-// Default keys per sort workgroup: about n / 512, clamped to [2^8, 2^12], so
+// Default keys per sort workgroup: about n / 512, clamped to [2^8, 2^13], so
 // that small sorts still spread over the whole GPU.  A function of n only.
 inline int default_sort_tile_log2(int64_t n) {
     int t = 0;

@@ -13,9 +13,10 @@
 // schedule gives the same bits.
 //
 //   plan_count / plan_write: tiles per destination, prefix sums, tile records.
-//   segreduce:   one lane group per (tile, 16-byte column slice).  It streams
-//                the tile's chunks (8 row loads in flight per lane), sums each
-//                chunk left to right, and merges chunk sums on a binary counter.
+//   segreduce:   one lane group per (tile, column slice), 16 bytes of each row
+//                per lane.  It streams the tile's chunks (8 row loads in flight
+//                per lane), sums each chunk left to right, and merges chunk
+//                sums on a binary counter.
 //                A destination with one tile is updated in place; the tiles of
 //                a longer one write private partial rows.
 //   tilecombine: merges a destination's partial rows by the same counter, in
@@ -261,17 +262,18 @@ __device__ __forceinline__ u32x4 pack4(const float* t) {
     return u32x4{__float_as_uint(t[0]), __float_as_uint(t[1]), __float_as_uint(t[2]), __float_as_uint(t[3])};
 }
 
-// Lane groups of GROUP lanes; each lane owns P pieces of 4 columns, the pieces
-// of a group GROUP*4 columns apart, so that every load and 16-byte store of a
-// group covers contiguous bytes.  One group reduces one (tile, column slice).
+// Lane groups of GROUP lanes; each lane owns 16 consecutive bytes of a row (8
+// bf16 or 4 fp32 columns), so every row load is one 16-byte load per lane and
+// a group reads GROUP*16 contiguous bytes.  One group reduces one (tile,
+// column slice).
 template <dr_dtype DT, int GROUP, int TCLOG, int CIF>
 __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
     float* __restrict__ out, int64_t H, const void* __restrict__ src, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ seg, const TileRec* __restrict__ tiles, float* __restrict__ partials, int64_t slices,
     int32_t* status) {
-    using PC = Piece<DT>;
-    constexpr int P = PC::kPieces;
-    constexpr int E = 4 * P;
+    using V = Vec<DT>;
+    constexpr int E = V::kElems;  // columns of a lane
+    constexpr int Q = E / 4;      // 16-byte fp32 pieces of a lane's output
     constexpr int kElemBytes = DT == DR_BF16 ? 2 : 4;
     constexpr int64_t W = (int64_t)GROUP * E;  // columns of one group slice
     if (status[kWordStatus] != 0) return;
@@ -286,22 +288,17 @@ __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
         const uint32_t tile = it / (uint32_t)slices;
         const uint32_t slice = it - tile * (uint32_t)slices;
         const TileRec tr = tiles[tile];
-        int64_t col[P], lcol[P];
-        bool active[P];
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-            col[p] = (int64_t)slice * W + p * (GROUP * 4) + 4 * lig;
-            active[p] = col[p] < H;
-            lcol[p] = active[p] ? col[p] : 0;  // idle lanes read a valid piece
-        }
+        const int64_t col = (int64_t)slice * W + E * lig;
+        const bool active = col < H;
+        const int64_t lcol = active ? col : 0;  // idle lanes read a valid piece
         const int64_t r_begin = (int64_t)seg[tr.dest] + ((int64_t)tr.chunk0 << 3);
         const int64_t r_end = min((int64_t)seg[tr.dest + 1], r_begin + ((int64_t)8 << TCLOG));
         float* orow = out + (int64_t)tr.dest * H;
         // the destination row, fetched early when this tile updates it in place
-        u32x4 old[P];
+        u32x4 old[Q];
         if (tr.pslot < 0) {
 #pragma unroll
-            for (int p = 0; p < P; ++p) old[p] = load16(orow + lcol[p]);
+            for (int q = 0; q < Q; ++q) old[q] = load16(orow + lcol + 4 * q);
         }
         TreeCounter<TCLOG + 1, E> tc;
         // CIF chunks (8*CIF rows) are loaded at once; slots past the tile's
@@ -311,22 +308,18 @@ __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
 #pragma unroll
         for (int j = 0; j < R; ++j) idx[j] = perm[min(r_begin + j, r_end - 1)];
         for (int64_t r0 = r_begin; r0 < r_end; r0 += R) {
-            typename PC::Raw raw[R][P];
+            u32x4 raw[R];
             const int64_t live = r_end - r0;  // rows of this step that exist
             if (live >= R) {
 #pragma unroll
                 for (int j = 0; j < R; ++j)
-#pragma unroll
-                    for (int p = 0; p < P; ++p)
-                        raw[j][p] = PC::load_stream(src_bytes + (int64_t)idx[j] * row_bytes, lcol[p]);
+                    raw[j] = load16_stream(src_bytes + (int64_t)idx[j] * row_bytes + lcol * kElemBytes);
             } else {
 #pragma unroll
-                for (int j = 0; j < R; ++j)
-#pragma unroll
-                    for (int p = 0; p < P; ++p) {
-                        raw[j][p] = typename PC::Raw{};
-                        if (j < live) raw[j][p] = PC::load_stream(src_bytes + (int64_t)idx[j] * row_bytes, lcol[p]);
-                    }
+                for (int j = 0; j < R; ++j) {
+                    raw[j] = u32x4{0u, 0u, 0u, 0u};
+                    if (j < live) raw[j] = load16_stream(src_bytes + (int64_t)idx[j] * row_bytes + lcol * kElemBytes);
+                }
             }
             // the next rows' source ids are fetched while these rows arrive
             const int64_t r1 = r0 + R;
@@ -339,36 +332,24 @@ __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
                 const int m = (int)min((int64_t)8, r_end - (r0 + 8 * c));  // rows of chunk c (<= 0: none)
                 if (m > 0) {
                     float s[E];
-#pragma unroll
-                    for (int p = 0; p < P; ++p) {
-                        float v[4];
-                        PC::widen(raw[8 * c][p], v);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) s[4 * p + e] = v[e];
-                    }
+                    V::widen(raw[8 * c], s);
                     if (m == 8) {
 #pragma unroll
                         for (int j = 1; j < 8; ++j) {
+                            float v[E];
+                            V::widen(raw[8 * c + j], v);
 #pragma unroll
-                            for (int p = 0; p < P; ++p) {
-                                float v[4];
-                                PC::widen(raw[8 * c + j][p], v);
-#pragma unroll
-                                for (int e = 0; e < 4; ++e) s[4 * p + e] = s[4 * p + e] + v[e];
-                            }
+                            for (int e = 0; e < E; ++e) s[e] = s[e] + v[e];
                         }
                     } else {
 #pragma unroll
                         for (int j = 1; j < 8; ++j) {
+                            float v[E];
+                            V::widen(raw[8 * c + j], v);
 #pragma unroll
-                            for (int p = 0; p < P; ++p) {
-                                float v[4];
-                                PC::widen(raw[8 * c + j][p], v);
-#pragma unroll
-                                for (int e = 0; e < 4; ++e) {
-                                    const float a = s[4 * p + e] + v[e];
-                                    s[4 * p + e] = j < m ? a : s[4 * p + e];
-                                }
+                            for (int e = 0; e < E; ++e) {
+                                const float a = s[e] + v[e];
+                                s[e] = j < m ? a : s[e];
                             }
                         }
                     }
@@ -378,15 +359,15 @@ __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
         }
         float t[E];
         tc.fold(t);
-        if (tr.pslot < 0) {
+        if (active) {
+            if (tr.pslot < 0) {
 #pragma unroll
-            for (int p = 0; p < P; ++p)
-                if (active[p]) store16(orow + col[p], add4(old[p], t + 4 * p));
-        } else {
-            float* prow = partials + (int64_t)tr.pslot * H;
+                for (int q = 0; q < Q; ++q) store16(orow + col + 4 * q, add4(old[q], t + 4 * q));
+            } else {
+                float* prow = partials + (int64_t)tr.pslot * H;
 #pragma unroll
-            for (int p = 0; p < P; ++p)
-                if (active[p]) store16(prow + col[p], pack4(t + 4 * p));
+                for (int q = 0; q < Q; ++q) store16(prow + col + 4 * q, pack4(t + 4 * q));
+            }
         }
     }
 }

@@ -324,7 +324,8 @@ static int64_t tiles_for(int64_t n, int tile_log2) { return (n + ((int64_t)1 << 
         case 9: MACRO(2); break;         \
         case 10: MACRO(4); break;        \
         case 11: MACRO(8); break;        \
-        default: MACRO(16); break;       \
+        case 12: MACRO(16); break;       \
+        default: MACRO(32); break;       \
     }
 
 hipError_t launch_radix_validate_hist(const int32_t* dest, int32_t num_dests, const int32_t* src_id,
@@ -386,7 +387,9 @@ hipError_t launch_radix_scatter(const SortPass& p, int64_t n, int tile_log2, con
                                 const int32_t* totals, const int32_t* status, hipStream_t s) {
     const int64_t nb = tiles_for(n, tile_log2);
     if (nb == 0) return hipSuccess;
-    static_assert(kMaxSortTileLog2 <= 12, "staged tile must fit in LDS");
+    // the staged tile (dest, value and source id of 2^13 keys: 96 KB) plus
+    // counters stays within a gfx950 workgroup's 160 KB of LDS
+    static_assert(kMaxSortTileLog2 <= 13, "staged tile must fit in LDS");
 #define DR_S(IT) launch_scatter_items<IT>(p, n, tile_log2, hist, totals, status, nb, s)
     DR_BY_ITEMS(tile_log2, DR_S)
 #undef DR_S

@@ -81,7 +81,7 @@ typedef struct dr_launch_params {
     int32_t grid_blocks;        /* workgroups of the persistent kernels (index_add reduce and tile
                                    combine, split-K partials, fingerprint), 1 .. 65536 */
     int32_t tile_chunks_log2;   /* index_add tile = 2^m chunks of 8 rows, m in [3, 7] (default 5) */
-    int32_t sort_tile_log2;     /* radix sort keys per workgroup = 2^m, m in [8, 12] (default: about
+    int32_t sort_tile_log2;     /* radix sort keys per workgroup = 2^m, m in [8, 13] (default: about
                                    n / 512, clamped to that range) */
     int32_t chunks_in_flight;   /* index_add: chunks of 8 rows loaded at once per lane group, 1 or 2
                                    (default 1) */

@@ -157,7 +157,7 @@ def test_index_add_launch_invariance(dr, dk):
     ref = None
     for grid in (0, 1, 7, 64, 1000):
         for tc in (3, 4, 5, 6, 7):
-            for st in (8, 10, 12):
+            for st in (8, 10, 12, 13):
                 if grid not in (0, 7) and (tc, st) != (5, 12):
                     continue
                 cif = 1 + (tc + st + grid) % 2
@@ -177,7 +177,7 @@ def test_index_add_launch_invariance(dr, dk):
 def test_sort_launch_invariance(dr, dk):
     inp, src, index, out0 = dk
     ref = None
-    for st in (8, 9, 10, 11, 12):
+    for st in (8, 9, 10, 11, 12, 13):
         dr.dr_set_launch_params(sort_tile_log2=st)
         try:
             p, s, i = dr.dr_sort_by_dest(index, inp.D)

@@ -54,6 +54,33 @@ def test_sort_matches_oracle(dr, n, D, with_src, src_bound, dist):
     assert np.array_equal(host(inv), want_inv)
 
 
+@pytest.mark.parametrize("sort_tile_log2", [12, 13])
+@pytest.mark.parametrize("n,D,with_src,src_bound,dist", [
+    (100003, 65536, False, 0, "zipf"),
+    (20001, 512, False, 0, "uniform"),      # one 9-bit pass whose bins equal D
+    (50000, 256, True, 50000, "uniform"),   # source ids staged through LDS
+    (30000, 1000, True, 7, "uniform"),
+])
+def test_sort_large_tiles_match_oracle(dr, sort_tile_log2, n, D, with_src, src_bound, dist):
+    """The largest tiles (32 keys per thread) and a ragged last tile."""
+    say(f"sort n={n} D={D} src={with_src} tile=2^{sort_tile_log2}")
+    rng = np.random.default_rng(n + D + 1)
+    if dist == "zipf":
+        dest = np.minimum(rng.zipf(1.2, n) - 1, D - 1).astype(np.int32)
+    else:
+        dest = rng.integers(0, D, n).astype(np.int32)
+    src = rng.integers(0, src_bound, n).astype(np.int32) if with_src else None
+    dr.dr_set_launch_params(sort_tile_log2=sort_tile_log2)
+    try:
+        perm, seg, inv = dr.dr_sort_by_dest(dev(dest), D, None if src is None else dev(src), src_bound)
+    finally:
+        dr.dr_set_launch_params(reset=True)
+    want_perm, want_seg, want_inv = oracle.sort_by_dest(dest, D, src)
+    assert np.array_equal(host(perm), want_perm)
+    assert np.array_equal(host(seg), want_seg)
+    assert np.array_equal(host(inv), want_inv)
+
+
 # ---------------------------------------------------------------------------
 # combine
 # ---------------------------------------------------------------------------
