@@ -21,10 +21,10 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / 64;
-// The fingerprinting launch for k <= 8 uses 16-wavefront workgroups: a
-// quarter as many partial sums to fold afterwards.  (Larger k needs more
-// registers than a 1024-thread workgroup leaves a lane.)
-constexpr int kFpThreads = 1024;
+// k <= 8 uses 8-wavefront workgroups (measured a little faster than 4 or 16
+// at the MoE shape, and half as many fingerprint partials to fold as 4).
+// Larger k keeps 4: it needs more registers per lane.
+constexpr int kThreadsK8 = 512;
 
 __device__ __forceinline__ int32_t uniform_lane(int32_t v, int lane) {
     return __builtin_amdgcn_readlane(v, lane);
@@ -291,10 +291,10 @@ hipError_t launch_dt(const void* rows, int64_t num_rows, int64_t H, const int32_
     hipLaunchKernelGGL((combine_kernel<DT, KM, FPV, TH>), dim3((unsigned)((waves + TH / 64 - 1) / (TH / 64))), \
                        dim3(TH), 0, s, rows, num_rows, H, row_of, gates, T, k, out, dev_status, slices, fp_partials)
     if (fp_partials) {
-        if (k <= 8) DR_COMBINE(8, true, kFpThreads);
+        if (k <= 8) DR_COMBINE(8, true, kThreadsK8);
         else DR_COMBINE(64, true, kThreads);
     } else {
-        if (k <= 8) DR_COMBINE(8, false, kThreads);
+        if (k <= 8) DR_COMBINE(8, false, kThreadsK8);
         else DR_COMBINE(64, false, kThreads);
     }
 #undef DR_COMBINE
@@ -306,7 +306,7 @@ hipError_t launch_dt(const void* rows, int64_t num_rows, int64_t H, const int32_
 int64_t combine_fp_blocks(dr_dtype dt, int64_t hidden, int64_t T, int32_t k) {
     const int64_t per_wave = 64 * (dt == DR_BF16 ? 8 : 4);
     const int64_t slices = (hidden + per_wave - 1) / per_wave;
-    const int64_t waves_per_block = (k <= 8 ? kFpThreads : kThreads) / 64;
+    const int64_t waves_per_block = (k <= 8 ? kThreadsK8 : kThreads) / 64;
     return (T * slices + waves_per_block - 1) / waves_per_block;
 }
 

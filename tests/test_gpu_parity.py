@@ -250,8 +250,8 @@ def test_fingerprint_odd_lengths_and_dtypes(dr):
     (1000, 64, 8, 1000, "bf16"),
     (257, 16, 1, 64, "f32"),
     (300, 128, 13, 136, "bf16"),
-    (9000, 64, 8, 1024, "bf16"),   # 1125 partials: the one-workgroup wide final sum
-    (270000, 16, 9, 64, "f32"),    # 67500 partials: the two-level final sum
+    (9000, 64, 8, 1024, "bf16"),   # over 1024 partials: the one-workgroup wide final sum
+    (270000, 16, 9, 64, "f32"),    # over 65536 partials: the two-level final sum
 ])
 def test_combine_fingerprinted_matches_separate_calls(dr, T, E, k, H, rows_dtype):
     say(f"combine_fingerprinted T={T} k={k} H={H} {rows_dtype}")
