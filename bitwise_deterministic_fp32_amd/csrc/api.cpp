@@ -551,7 +551,7 @@ dr_status dr_splitk_reduce(const float* partials, int32_t splits, int64_t count,
 // ---------------------------------------------------------------------------
 size_t dr_fingerprint_workspace_size(int64_t nbytes) {
     (void)nbytes;
-    return dr::kStatusBytes + 2048 * sizeof(uint64_t);
+    return dr::kStatusBytes + dr::kMaxFingerprintBlocks * sizeof(uint64_t);
 }
 
 dr_status dr_fingerprint(const void* data, int64_t nbytes, uint64_t* out_hash, void* ws, size_t ws_bytes,

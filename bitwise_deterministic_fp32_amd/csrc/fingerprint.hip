@@ -12,9 +12,11 @@ namespace dr {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kMaxBlocks = 2048;
+constexpr int kMaxBlocks = kMaxFingerprintBlocks;
 
 __device__ __forceinline__ uint64_t term(uint64_t w, int64_t i) { return fp_term(w, i); }
+
+constexpr uint64_t kGamma = 0x9e3779b97f4a7c15ull;
 
 __global__ __launch_bounds__(kThreads) void fp_partial_kernel(const unsigned char* __restrict__ data, int64_t nbytes,
                                                               uint64_t* __restrict__ partials) {
@@ -28,6 +30,11 @@ __global__ __launch_bounds__(kThreads) void fp_partial_kernel(const unsigned cha
     const bool aligned16 = (reinterpret_cast<uintptr_t>(data) & 15) == 0;
     if (aligned16) {
         int64_t p = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+        // The generator states (i + 1) * gamma of the words are carried by
+        // wrapping additions (word i of pair p is 2p or 2p + 1), which leaves
+        // the two multiplications of the finaliser as the only ones per word.
+        const uint64_t step = (uint64_t)(2 * stride) * kGamma;  // state advance of one stride
+        uint64_t state = (uint64_t)(2 * p + 1) * kGamma;       // state of word 2p
         // four independent 16-byte loads in flight per lane
         for (; p + 3 * stride < pairs; p += 4 * stride) {
             u32x4 v[4];
@@ -35,15 +42,16 @@ __global__ __launch_bounds__(kThreads) void fp_partial_kernel(const unsigned cha
             for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(d16 + p + u * stride);
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int64_t q = p + u * stride;
-                acc += term(((uint64_t)v[u].y << 32) | v[u].x, 2 * q);
-                acc += term(((uint64_t)v[u].w << 32) | v[u].z, 2 * q + 1);
+                acc += mix64((((uint64_t)v[u].y << 32) | v[u].x) ^ state);
+                acc += mix64((((uint64_t)v[u].w << 32) | v[u].z) ^ (state + kGamma));
+                state += step;
             }
         }
         for (; p < pairs; p += stride) {
             const u32x4 v = __builtin_nontemporal_load(d16 + p);
-            acc += term(((uint64_t)v.y << 32) | v.x, 2 * p);
-            acc += term(((uint64_t)v.w << 32) | v.z, 2 * p + 1);
+            acc += mix64((((uint64_t)v.y << 32) | v.x) ^ state);
+            acc += mix64((((uint64_t)v.w << 32) | v.z) ^ (state + kGamma));
+            state += step;
         }
     }
     const int64_t first_single = aligned16 ? 2 * pairs : 0;

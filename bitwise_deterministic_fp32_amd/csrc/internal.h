@@ -134,6 +134,9 @@ hipError_t launch_splitk_gemm(const uint16_t* X, const uint16_t* dY, int64_t K, 
 hipError_t launch_splitk_reduce(const float* partials, int32_t splits, int64_t count, float* out,
                                 hipStream_t s);
 // fingerprint
+// most workgroups (and partials) of a fingerprint launch: 8 per SIMD of a
+// 256-CU device, enough wavefronts to hide the loads behind the hashing
+constexpr int kMaxFingerprintBlocks = 8192;
 int64_t fingerprint_blocks(int64_t nbytes);
 hipError_t launch_fingerprint(const void* data, int64_t nbytes, uint64_t* out, uint64_t* block_partials,
                               hipStream_t s);

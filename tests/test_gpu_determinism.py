@@ -191,7 +191,7 @@ def test_sort_launch_invariance(dr, dk):
 def test_fingerprint_grid_invariance(dr):
     t = dev(workloads.normal_f32(5, 0, (1 << 20) + 3))
     ref = dr.fingerprint_value(t)
-    for grid in (1, 3, 64, 1024):
+    for grid in (1, 3, 64, 1024, 8192):
         dr.dr_set_launch_params(grid_blocks=grid)
         try:
             assert dr.fingerprint_value(t) == ref, grid
