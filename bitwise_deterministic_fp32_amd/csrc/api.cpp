@@ -473,7 +473,7 @@ dr_status dr_index_add(float* out, int32_t num_dests, int64_t hidden, const void
     DR_TRY_HIP(dr::launch_plan_write(seg, num_dests, lc.tile_chunks_log2, b.block_sums, b.tiles, b.multis, b.status,
                                      stream),
                "plan write launch");
-    DR_TRY_HIP(dr::launch_segreduce(out, hidden, src, src_dtype, n, p, seg, b.tiles, b.partials, lc.tile_chunks_log2,
+    DR_TRY_HIP(dr::launch_segreduce(out, hidden, src, src_dtype, n, p, b.tiles, b.partials, lc.tile_chunks_log2,
                                     lc.chunks_in_flight, b.status, stream),
                "segmented reduce launch");
     DR_TRY_HIP(dr::launch_tilecombine(out, hidden, b.partials, b.multis, n, lc.tile_chunks_log2, b.status, stream),

@@ -55,10 +55,10 @@ int device_cu_count();  // compute units of the current device (cached)
 // Plan records written by the index_add planner
 // ---------------------------------------------------------------------------
 struct alignas(16) TileRec {
-    int32_t dest;    // destination row
-    int32_t chunk0;  // first chunk (of 8 rows) of the tile, relative to the segment start
-    int32_t pslot;   // partial slot, or -1 when the tile is the whole segment
-    int32_t pad;
+    int32_t dest;     // destination row
+    int32_t r_begin;  // sorted positions [r_begin, r_end) of the tile's rows
+    int32_t r_end;
+    int32_t pslot;    // partial slot, or -1 when the tile is the whole segment
 };
 struct alignas(16) MultiRec {
     int32_t dest;
@@ -113,9 +113,8 @@ hipError_t launch_plan_write(const int32_t* seg_offsets, int32_t num_dests, int 
 hipError_t launch_plan_validate(const int32_t* perm, const int32_t* seg, const int32_t* index, int64_t n,
                                 int32_t num_dests, int32_t* status, hipStream_t s);
 hipError_t launch_segreduce(float* out, int64_t hidden, const void* src, dr_dtype src_dtype, int64_t n,
-                            const int32_t* perm, const int32_t* seg_offsets, const TileRec* tiles,
-                            float* partials, int tile_chunks_log2, int chunks_in_flight, int32_t* status,
-                            hipStream_t s);
+                            const int32_t* perm, const TileRec* tiles, float* partials, int tile_chunks_log2,
+                            int chunks_in_flight, int32_t* status, hipStream_t s);
 hipError_t launch_tilecombine(float* out, int64_t hidden, const float* partials, const MultiRec* multis, int64_t n,
                               int tile_chunks_log2, int32_t* status, hipStream_t s);
 

@@ -156,9 +156,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_write_kernel(const int32_t*
     for (int32_t j = 0; j < c.tiles; ++j) {
         TileRec r;
         r.dest = (int32_t)d;
-        r.chunk0 = j << tc_log2;
+        r.r_begin = seg[d] + ((j << tc_log2) << 3);
+        r.r_end = (int32_t)min((int64_t)seg[d + 1], (int64_t)r.r_begin + (8 << tc_log2));  // no int32 overflow
         r.pslot = c.multi ? pslot0 + j : -1;
-        r.pad = 0;
         tiles[tile0 + j] = r;
     }
     if (c.multi) {
@@ -269,8 +269,7 @@ __device__ __forceinline__ u32x4 pack4(const float* t) {
 template <dr_dtype DT, int GROUP, int TCLOG, int CIF>
 __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
     float* __restrict__ out, int64_t H, const void* __restrict__ src, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ seg, const TileRec* __restrict__ tiles, float* __restrict__ partials, int64_t slices,
-    int32_t* status) {
+    const TileRec* __restrict__ tiles, float* __restrict__ partials, int64_t slices, int32_t* status) {
     using V = Vec<DT>;
     constexpr int E = V::kElems;  // columns of a lane
     constexpr int Q = E / 4;      // 16-byte fp32 pieces of a lane's output
@@ -284,15 +283,18 @@ __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
     const uint32_t ngroups = (gridDim.x * kReduceThreads) / GROUP;
     const char* src_bytes = reinterpret_cast<const char*>(src);
     const int64_t row_bytes = H * kElemBytes;
+    // the next item's tile record is fetched one item ahead
+    TileRec tr_next{};
+    if (group < items) tr_next = tiles[group / (uint32_t)slices];
     for (uint32_t it = group; it < items; it += ngroups) {
         const uint32_t tile = it / (uint32_t)slices;
         const uint32_t slice = it - tile * (uint32_t)slices;
-        const TileRec tr = tiles[tile];
+        const TileRec tr = tr_next;
+        if (it + ngroups < items) tr_next = tiles[(it + ngroups) / (uint32_t)slices];
         const int64_t col = (int64_t)slice * W + E * lig;
         const bool active = col < H;
         const int64_t lcol = active ? col : 0;  // idle lanes read a valid piece
-        const int64_t r_begin = (int64_t)seg[tr.dest] + ((int64_t)tr.chunk0 << 3);
-        const int64_t r_end = min((int64_t)seg[tr.dest + 1], r_begin + ((int64_t)8 << TCLOG));
+        const int64_t r_begin = tr.r_begin, r_end = tr.r_end;
         float* orow = out + (int64_t)tr.dest * H;
         // the destination row, fetched early when this tile updates it in place
         u32x4 old[Q];
@@ -423,12 +425,12 @@ int group_for(int64_t pieces) {
 
 template <dr_dtype DT, int GROUP, int CIF>
 hipError_t launch_segreduce_g(dim3 grid, float* out, int64_t H, const void* src, const int32_t* perm,
-                              const int32_t* seg, const TileRec* tiles, float* partials, int tc_log2, int64_t slices,
-                              int32_t* status, hipStream_t s) {
+                              const TileRec* tiles, float* partials, int tc_log2, int64_t slices, int32_t* status,
+                              hipStream_t s) {
 #define DR_SEGREDUCE_CASE(TC)                                                                                  \
     case TC:                                                                                                   \
         hipLaunchKernelGGL((segreduce_kernel<DT, GROUP, TC, CIF>), grid, dim3(kReduceThreads), 0, s, out, H,    \
-                           src, perm, seg, tiles, partials, slices, status);                                   \
+                           src, perm, tiles, partials, slices, status);                                        \
         break;
     switch (tc_log2) {
         DR_SEGREDUCE_CASE(3)
@@ -476,17 +478,17 @@ hipError_t launch_plan_validate(const int32_t* perm, const int32_t* seg, const i
 }
 
 hipError_t launch_segreduce(float* out, int64_t hidden, const void* src, dr_dtype dt, int64_t n, const int32_t* perm,
-                            const int32_t* seg_offsets, const TileRec* tiles, float* partials, int tc_log2, int cif,
-                            int32_t* status, hipStream_t s) {
+                            const TileRec* tiles, float* partials, int tc_log2, int cif, int32_t* status,
+                            hipStream_t s) {
     (void)n;
     const int64_t lanes = dt == DR_BF16 ? hidden / 8 : hidden / 4;  // lanes needed per row
     const int g = group_for(lanes);
     const int64_t slices = (lanes + g - 1) / g;
     const dim3 grid(persistent_grid());
 #define DR_SR(DT, G)                                                                                              \
-    return cif == 1 ? launch_segreduce_g<DT, G, 1>(grid, out, hidden, src, perm, seg_offsets, tiles, partials,    \
+    return cif == 1 ? launch_segreduce_g<DT, G, 1>(grid, out, hidden, src, perm, tiles, partials,    \
                                                    tc_log2, slices, status, s)                                    \
-                    : launch_segreduce_g<DT, G, 2>(grid, out, hidden, src, perm, seg_offsets, tiles, partials,    \
+                    : launch_segreduce_g<DT, G, 2>(grid, out, hidden, src, perm, tiles, partials,    \
                                                    tc_log2, slices, status, s)
     if (dt == DR_BF16) {
         if (g == 16) DR_SR(DR_BF16, 16);
