@@ -229,6 +229,43 @@ def cpu_baseline_moe(oracle, inp, seconds):
 
 
 # ---------------------------------------------------------------------------
+def copy_ceiling(torch, achieved_gbs: float, mib: int = 2048, reps: int = 5) -> dict:
+    """A device-to-device copy of 2 GiB (read + write), timed with events: the
+    practical HBM ceiling of a plain stream on this device, reported next to
+    the datasheet peak."""
+    n = mib * (1 << 20) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(reps):
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del a, b
+    ms = sorted(ts)[len(ts) // 2]
+    gbs = 2 * n * 4 / (ms * 1e-3) / 1e9
+    return {"copy_ceiling_gbs": round(gbs, 1), "frac_of_copy": round(achieved_gbs / gbs, 4)}
+
+
+def host_description() -> dict:
+    """The host the CPU baseline ran on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"host_cpu": model, "host_logical_cpus": os.cpu_count()}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -246,6 +283,9 @@ def main():
         import bench_workloads
         res = bench_workloads.run(torch, dr, name, args.steps, args.warmup, args.cpu_seconds,
                                   not args.no_cpu_baseline)
+    res["roofline"].update(copy_ceiling(torch, res["roofline"]["achieved"]))
+    if "cpu_baseline" in res:
+        res["cpu_baseline"].update(host_description())
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib * (1 << 20) // 4
         a = torch.ones(n, dtype=torch.float32, device="cuda")

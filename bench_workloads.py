@@ -220,6 +220,11 @@ def _splitk(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
     for _ in range(steps):
         astep(atimer.step())
     aph = atimer.mean_ms()
+    # the single-pass alternative: one split, so one workgroup per 64-column M tile walks all K tokens
+    p1 = torch.empty(1, M, N, dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        dr.dr_splitk_gemm_tn(X, dY, 1, partials=p1)
+    ms_nosplit = _timed(torch, steps, lambda: dr.dr_splitk_gemm_tn(X, dY, 1, partials=p1))
     g_ms = ph["splitk_gemm"]
     achieved = gemm_bytes / (g_ms * 1e-3) / 1e9
     det_ms = ph["splitk_gemm"] + ph["splitk_reduce"]
@@ -239,6 +244,7 @@ def _splitk(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
         "phases_ms": {k: round(v, 4) for k, v in ph.items()},
         "overhead_vs_atomic": {"deterministic_ms": round(det_ms, 4), "atomic_zero_plus_gemm_ms": round(at_ms, 4),
                                "overhead": round(det_ms / at_ms - 1, 4)},
+        "no_split_ms": round(ms_nosplit, 4),
     }
     if want_cpu:
         t0 = time.perf_counter()

@@ -56,6 +56,7 @@ def lib():
         L.oracle_sort_by_dest.argtypes = [vp, vp, i64, i32, vp, vp, vp]
         L.oracle_scatter_reduce.argtypes = [vp, i32, i64, vp, ctypes.c_int, i64, vp, vp, vp, i64]
         L.oracle_combine.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, i64, i32, vp, i64, vp]
+        L.oracle_sparse_attn_dk.argtypes = [vp, i32, i64, vp, ctypes.c_int, vp, vp, i64, i32, vp, i64]
         L.oracle_splitk_reduce.argtypes = [vp, i32, i64, vp]
         L.oracle_splitk_reference.argtypes = [vp, vp, i64, i64, i64, vp, vp]
         L.oracle_splitk_partials.argtypes = [vp, vp, i64, i64, i64, i32, vp]
@@ -64,7 +65,7 @@ def lib():
         L.oracle_fingerprint.argtypes = [vp, i64]
         L.oracle_fingerprint.restype = u64
         for name in ("oracle_tree_sum_f32", "oracle_tree_sum_bf16", "oracle_sort_by_dest",
-                     "oracle_scatter_reduce", "oracle_combine", "oracle_splitk_reduce",
+                     "oracle_scatter_reduce", "oracle_combine", "oracle_sparse_attn_dk", "oracle_splitk_reduce",
                      "oracle_splitk_reference", "oracle_splitk_partials"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -148,6 +149,29 @@ def scatter_reduce(out0, src, index, src_id=None, dests=None):
 def index_add(out0, src, index, dests=None):
     """torch-style index_add_(0, index, src) in the defined order (source id = row i)."""
     return scatter_reduce(out0, src, index, None, dests)
+
+
+def sparse_attn_dk(dK0, Q, dS, key_idx, keys=None):
+    """dK[key] = dK0[key] + T(fl32(dS[q, j] * Q[q]) over the (q, j) with key_idx[q, j] == key, in order of
+    q * topk + j).  Q: float32 or uint16 (bf16 bits) [nq, H]; dS: float32 [nq, topk]; key_idx: int32 [nq, topk].
+    keys: optional list of keys; then only those rows are returned."""
+    dK0 = np.asarray(dK0, dtype=np.float32)
+    num_keys, H = dK0.shape
+    Q = np.ascontiguousarray(Q)
+    dS = _c(dS, np.float32)
+    key_idx = _c(key_idx, np.int32)
+    nq, topk = key_idx.shape
+    assert Q.shape == (nq, H) and dS.shape == (nq, topk), (Q.shape, dS.shape, key_idx.shape)
+    if keys is None:
+        out = np.array(dK0, dtype=np.float32, copy=True, order="C")
+        kl, nk = None, 0
+    else:
+        kl = _c(keys, np.int32)
+        nk = kl.size
+        out = np.ascontiguousarray(dK0[kl], dtype=np.float32)
+    _check(lib().oracle_sparse_attn_dk(_ptr(out), num_keys, H, _ptr(Q), _dtype_code(Q), _ptr(dS), _ptr(key_idx),
+                                       nq, topk, _ptr(kl), nk), "sparse_attn_dk")
+    return out
 
 
 def combine(rows, row_of, gates, tokens=None):

@@ -31,6 +31,10 @@
  *     expert output they come from (ties by slot); each contribution is
  *     fl32(gate * row), rounded before it is added.
  *   - split reduce: the same tree over the split ids 0..S-1.
+ *   - sparse-attention key gradient: contribution q * topk + j is
+ *     fl32(dS[q][j] * Q[q]), rounded before it is added (like the gate
+ *     product), and the source id is q * topk + j; any softmax scale is
+ *     folded into dS by the caller.
  *
  * Arithmetic: IEEE-754 binary32, round to nearest even, no contraction
  * (build with -ffp-contract=off), no excess precision (FLT_EVAL_METHOD 0,
@@ -277,6 +281,73 @@ int oracle_scatter_reduce(float* out, int32_t num_dests, int64_t H, const void* 
         for (int64_t h = 0; h < H; ++h) {
             for (int64_t j = 0; j < L; ++j)
                 vals[j] = load_elem(src, src_dtype, (int64_t)perm[lo + j] * H + h);
+            float t;
+            rc = tree_sum(vals, L, &t);
+            if (rc != ORC_OK)
+                break;
+            row[h] = row[h] + t;
+        }
+        if (rc != ORC_OK)
+            break;
+    }
+    free(perm); free(seg); free(vals);
+    return rc;
+}
+
+/* ------------------------------------------------------------------ */
+/* Sparse-attention key gradient                                       */
+/* ------------------------------------------------------------------ */
+
+/* The backward of DeepSeek-V4's sparse attention (ch. 9, section 3.1): every
+ * query q selected topk keys, and the gradient of a selected key accumulates,
+ * over the queries that selected it, the query's row scaled by that query's
+ * score gradient.  Contribution i = q * topk + j is
+ *     c_i[h] = fl32(dS[i] * Q[q][h])      (one rounding, never fused)
+ * and dK[key][h] = dK[key][h] + T(c_i[h] over i with key_idx[i] == key, in
+ * order of i), the index_add order with the contribution formed on the fly.
+ * Q is [nq][H] fp32 or bf16, dS and key_idx are [nq][topk].
+ * keys == NULL: dK is [num_keys][H], updated in place.
+ * keys != NULL: dK is [nkeys][H] holding the listed keys' rows. */
+int oracle_sparse_attn_dk(float* dK, int32_t num_keys, int64_t H, const void* Q, int q_dtype, const float* dS,
+                          const int32_t* key_idx, int64_t nq, int32_t topk, const int32_t* keys, int64_t nkeys)
+{
+    if (!dK || H < 1 || num_keys < 1 || nq < 0 || topk < 1)
+        return ORC_BAD_ARG;
+    if (q_dtype != ORC_F32 && q_dtype != ORC_BF16)
+        return ORC_BAD_ARG;
+    const int64_t n = nq * (int64_t)topk;
+    if (n > 0 && (!Q || !dS || !key_idx))
+        return ORC_BAD_ARG;
+    int32_t* perm = (int32_t*)malloc((size_t)(n > 0 ? n : 1) * sizeof(int32_t));
+    int32_t* seg = (int32_t*)malloc((size_t)(num_keys + 1) * sizeof(int32_t));
+    float* vals = (float*)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+    if (!perm || !seg || !vals) {
+        free(perm); free(seg); free(vals);
+        return ORC_NO_MEMORY;
+    }
+    int rc = oracle_sort_by_dest(key_idx, NULL, n, num_keys, perm, seg, NULL);
+    if (rc != ORC_OK) {
+        free(perm); free(seg); free(vals);
+        return rc;
+    }
+    int64_t rows = keys ? nkeys : num_keys;
+    for (int64_t r = 0; r < rows; ++r) {
+        int32_t key = keys ? keys[r] : (int32_t)r;
+        if (key < 0 || key >= num_keys) {
+            rc = ORC_INDEX_OUT_OF_RANGE;
+            break;
+        }
+        int64_t lo = seg[key], L = seg[key + 1] - seg[key];
+        if (L == 0)
+            continue; /* a key no query selected */
+        float* row = dK + r * H;
+        for (int64_t h = 0; h < H; ++h) {
+            for (int64_t j = 0; j < L; ++j) {
+                int64_t i = perm[lo + j];
+                int64_t q = i / topk;
+                float product = dS[i] * load_elem(Q, q_dtype, q * H + h);
+                vals[j] = product;
+            }
             float t;
             rc = tree_sum(vals, L, &t);
             if (rc != ORC_OK)

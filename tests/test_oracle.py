@@ -366,6 +366,63 @@ def _expert_major_rows(expert_ids):
     return row_of.reshape(T, k)
 
 
+# ---------------------------------------------------------------------------
+# Sparse-attention key gradient (contributions formed on the fly)
+# ---------------------------------------------------------------------------
+def _sparse_case(seed, nq, topk, H, num_keys, bf16):
+    rng = np.random.default_rng(seed)
+    Qf = rng.standard_normal((nq, H)).astype(F32)
+    Q = workloads.bf16_bits(Qf) if bf16 else Qf
+    dS = (0.1 * rng.standard_normal((nq, topk))).astype(F32)
+    key_idx = np.stack([rng.choice(num_keys, topk, replace=False) for _ in range(nq)]).astype(np.int32)
+    dK0 = rng.standard_normal((num_keys, H)).astype(F32)
+    return Q, dS, key_idx, dK0
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_sparse_attn_dk_is_index_add_of_rounded_products(bf16):
+    """The fused form equals index_add over contributions that numpy forms as
+    float32 products (each element one IEEE rounding), source id q*topk + j."""
+    Q, dS, key_idx, dK0 = _sparse_case(70 + bf16, 300, 16, 24, 64, bf16)
+    nq, topk = key_idx.shape
+    Qf = (Q.astype(np.uint32) << 16).view(F32) if bf16 else Q
+    q_of = np.arange(nq * topk) // topk
+    contrib = dS.reshape(-1, 1) * Qf[q_of]
+    assert contrib.dtype == F32
+    want = oracle.index_add(dK0, contrib, key_idx.reshape(-1))
+    got = oracle.sparse_attn_dk(dK0, Q, dS, key_idx)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    keys = np.array([0, 5, 63, 17], np.int32)
+    assert np.array_equal(oracle.sparse_attn_dk(dK0, Q, dS, key_idx, keys=keys).view(np.uint32),
+                          want[keys].view(np.uint32))
+
+
+def test_sparse_attn_dk_closed_forms():
+    # one query per key: dK = dK0 + fl32(dS * Q), element by element
+    rng = np.random.default_rng(72)
+    nq, H = 20, 8
+    Q = rng.standard_normal((nq, H)).astype(F32)
+    dS = rng.standard_normal((nq, 1)).astype(F32)
+    key_idx = np.arange(nq, dtype=np.int32).reshape(nq, 1)[::-1].copy()
+    dK0 = rng.standard_normal((nq, H)).astype(F32)
+    want = dK0.copy()
+    for q in range(nq):
+        want[key_idx[q, 0]] = dK0[key_idx[q, 0]] + dS[q, 0] * Q[q]
+    got = oracle.sparse_attn_dk(dK0, Q, dS, key_idx)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    # the order is by query: three queries select key 0 with rows 1, x, x (x = 3 * 2^-26)
+    # and unit score gradients; T(1, x, x) = 1 but T(x, x, 1) = 1 + 2^-23
+    x = F32(3 * 2.0 ** -26)
+    dS1 = np.ones((3, 1), F32)
+    idx = np.zeros((3, 1), np.int32)
+    zero = np.zeros((1, 1), F32)
+    assert bits32(oracle.sparse_attn_dk(zero, np.array([[1.0], [x], [x]], F32), dS1, idx)[0, 0]) == 0x3F800000
+    assert bits32(oracle.sparse_attn_dk(zero, np.array([[x], [x], [1.0]], F32), dS1, idx)[0, 0]) == 0x3F800001
+    # keys no query selected are untouched, and an out-of-range key is refused
+    with pytest.raises(Exception):
+        oracle.sparse_attn_dk(zero, np.ones((1, 1), F32), dS1[:1], np.array([[1]], np.int32))
+
+
 def test_combine_k2_closed_form():
     inp = workloads.make("tiny_moe_combine")
     row_of = _expert_major_rows(inp.expert_ids)
