@@ -21,6 +21,7 @@ __all__ = [
     "dr_sort_workspace_size", "dr_sort_by_dest",
     "dr_combine", "dr_combine_atomic", "dr_combine_fingerprinted_workspace_size", "dr_combine_fingerprinted",
     "dr_index_add_workspace_size", "dr_index_add", "dr_index_add_atomic",
+    "dr_sparse_attn_dk_workspace_size", "dr_sparse_attn_dk",
     "dr_splitk_gemm_tn", "dr_splitk_gemm_tn_atomic", "dr_splitk_reduce",
     "dr_fingerprint_workspace_size", "dr_fingerprint", "fingerprint_value",
     "dr_workspace_status", "dr_read_status",
@@ -60,6 +61,8 @@ def _load() -> ctypes.CDLL:
         "dr_index_add_workspace_size": ([i64, i32, i64], sz),
         "dr_index_add": ([vp, i32, i64, vp, ctypes.c_int, i64, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "dr_index_add_atomic": ([vp, i32, i64, vp, ctypes.c_int, i64, vp, vp, vp], ctypes.c_int),
+        "dr_sparse_attn_dk_workspace_size": ([i64, i32, i32, i64], sz),
+        "dr_sparse_attn_dk": ([vp, i32, i64, vp, ctypes.c_int, vp, vp, i64, i32, vp, vp, vp, sz, vp], ctypes.c_int),
         "dr_splitk_gemm_tn": ([vp, vp, i64, i64, i64, i32, vp, vp], ctypes.c_int),
         "dr_splitk_gemm_tn_atomic": ([vp, vp, i64, i64, i64, i32, vp, vp], ctypes.c_int),
         "dr_splitk_reduce": ([vp, i32, i64, vp, vp], ctypes.c_int),
@@ -231,6 +234,27 @@ def dr_index_add(out, src, index, *, perm=None, seg_offsets=None, ws=None, strea
     _check(lib.dr_index_add(_p(out), D, H, _p(src), _DTYPES[src.dtype], n, _p(index), _p(perm), _p(seg_offsets),
                             _p(ws), ws.numel(), _stream(stream)), "dr_index_add")
     return out, ws
+
+
+def dr_sparse_attn_dk_workspace_size(num_queries: int, topk: int, num_keys: int, head_dim: int) -> int:
+    return int(lib.dr_sparse_attn_dk_workspace_size(num_queries, topk, num_keys, head_dim))
+
+
+def dr_sparse_attn_dk(dK, Q, dS, key_idx, *, perm=None, seg_offsets=None, ws=None, stream=None):
+    """dK[key] += ordered tree of fl32(dS[q, j] * Q[q]) over the (q, j) that selected key (in place).
+    Returns (dK, ws)."""
+    _dev(dK, "dK", (torch.float32,))
+    _dev(Q, "Q", tuple(_DTYPES))
+    _dev(dS, "dS", (torch.float32,))
+    _dev(key_idx, "key_idx", (torch.int32,))
+    K, H = dK.shape
+    nq, topk = key_idx.shape
+    if Q.shape != (nq, H) or dS.shape != (nq, topk):
+        raise ValueError(f"Q must be [{nq}, {H}] and dS [{nq}, {topk}], got {tuple(Q.shape)} and {tuple(dS.shape)}")
+    ws = ws if ws is not None else _workspace(dr_sparse_attn_dk_workspace_size(nq, topk, K, H), dK.device)
+    _check(lib.dr_sparse_attn_dk(_p(dK), K, H, _p(Q), _DTYPES[Q.dtype], _p(dS), _p(key_idx), nq, topk, _p(perm),
+                                 _p(seg_offsets), _p(ws), ws.numel(), _stream(stream)), "dr_sparse_attn_dk")
+    return dK, ws
 
 
 def dr_index_add_atomic(out, src, index, *, dev_status=None, stream=None):

@@ -426,17 +426,24 @@ size_t dr_index_add_workspace_size(int64_t n, int32_t num_dests, int64_t hidden)
     return c.off;
 }
 
-dr_status dr_index_add(float* out, int32_t num_dests, int64_t hidden, const void* src, dr_dtype src_dtype, int64_t n,
-                       const int32_t* index, const int32_t* perm, const int32_t* seg_offsets, void* ws,
-                       size_t ws_bytes, hipStream_t stream) {
-    const char* what = "dr_index_add";
-    dr_status st = check_dtype(src_dtype, what);
-    if (st != DR_OK) return st;
-    if ((st = check_rows(src, src_dtype, hidden, what)) != DR_OK) return st;
+namespace {
+
+// The contributions of an index_add: rows of src, or (scale != null) the
+// rows fl32(scale[p] * src[p / rows_per_src]) formed in the reduce kernel.
+struct Contributions {
+    const void* src;
+    dr_dtype dtype;
+    const float* scale;
+    int32_t rows_per_src;
+};
+
+dr_status run_index_add(const char* what, float* out, int32_t num_dests, int64_t hidden, const Contributions& c,
+                        int64_t n, const int32_t* index, const int32_t* perm, const int32_t* seg_offsets, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
     if (!out || !aligned(out, 16)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: out must be non-null and 16-byte aligned", what);
     if (num_dests < 1) return fail(DR_ERR_INVALID_ARGUMENT, "%s: num_dests must be >= 1", what);
     if (n < 0 || n >= kMaxN) return fail(DR_ERR_INVALID_ARGUMENT, "%s: n must be in [0, 2^31)", what);
-    if (n > 0 && (!src || !index)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: null src or index", what);
+    if (n > 0 && (!c.src || !index)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: null source rows or index", what);
     if ((perm == nullptr) != (seg_offsets == nullptr))
         return fail(DR_ERR_INVALID_ARGUMENT, "%s: perm and seg_offsets must both be given or both be NULL", what);
     if (!ws || !aligned(ws, 16)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: workspace must be non-null, 16-byte aligned", what);
@@ -449,17 +456,17 @@ dr_status dr_index_add(float* out, int32_t num_dests, int64_t hidden, const void
         if (pb.tiles * slices >= ((int64_t)1 << 32))
             return fail(DR_ERR_UNSUPPORTED, "%s: n and hidden too large for one call", what);
     }
-    Carver c(ws);
-    const IndexAddBuffers b = carve_index_add(c, n, num_dests, hidden, sort_inside, lc.tile_chunks_log2,
+    Carver cv(ws);
+    const IndexAddBuffers b = carve_index_add(cv, n, num_dests, hidden, sort_inside, lc.tile_chunks_log2,
                                               lc.sort_tile(n));
-    if (c.off > ws_bytes)
-        return fail(DR_ERR_WORKSPACE_TOO_SMALL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes, c.off);
+    if (cv.off > ws_bytes)
+        return fail(DR_ERR_WORKSPACE_TOO_SMALL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes, cv.off);
     const int32_t* p = perm;
     const int32_t* seg = seg_offsets;
     if (sort_inside) {
         // the sort writes the status word
-        st = run_sort(index, nullptr, 0, n, num_dests, b.perm, b.seg, nullptr, b.status, b.sort, lc.sort_tile(n),
-                      stream);
+        const dr_status st = run_sort(index, nullptr, 0, n, num_dests, b.perm, b.seg, nullptr, b.status, b.sort,
+                                      lc.sort_tile(n), stream);
         if (st != DR_OK) return st;
         p = b.perm;
         seg = b.seg;
@@ -473,12 +480,48 @@ dr_status dr_index_add(float* out, int32_t num_dests, int64_t hidden, const void
     DR_TRY_HIP(dr::launch_plan_write(seg, num_dests, lc.tile_chunks_log2, b.block_sums, b.tiles, b.multis, b.status,
                                      stream),
                "plan write launch");
-    DR_TRY_HIP(dr::launch_segreduce(out, hidden, src, src_dtype, n, p, b.tiles, b.partials, lc.tile_chunks_log2,
-                                    lc.chunks_in_flight, b.status, stream),
+    DR_TRY_HIP(dr::launch_segreduce(out, hidden, c.src, c.dtype, n, p, b.tiles, b.partials, lc.tile_chunks_log2,
+                                    lc.chunks_in_flight, c.scale, c.rows_per_src, b.status, stream),
                "segmented reduce launch");
     DR_TRY_HIP(dr::launch_tilecombine(out, hidden, b.partials, b.multis, n, lc.tile_chunks_log2, b.status, stream),
                "tile combine launch");
     return ok();
+}
+
+}  // namespace
+
+dr_status dr_index_add(float* out, int32_t num_dests, int64_t hidden, const void* src, dr_dtype src_dtype, int64_t n,
+                       const int32_t* index, const int32_t* perm, const int32_t* seg_offsets, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+    const char* what = "dr_index_add";
+    dr_status st = check_dtype(src_dtype, what);
+    if (st != DR_OK) return st;
+    if ((st = check_rows(src, src_dtype, hidden, what)) != DR_OK) return st;
+    return run_index_add(what, out, num_dests, hidden, Contributions{src, src_dtype, nullptr, 1}, n, index, perm,
+                         seg_offsets, ws, ws_bytes, stream);
+}
+
+size_t dr_sparse_attn_dk_workspace_size(int64_t num_queries, int32_t topk, int32_t num_keys, int64_t head_dim) {
+    const int64_t n = num_queries < 0 || topk < 1 ? 0 : num_queries * (int64_t)topk;
+    return dr_index_add_workspace_size(n, num_keys, head_dim);
+}
+
+dr_status dr_sparse_attn_dk(float* dK, int32_t num_keys, int64_t head_dim, const void* Q, dr_dtype q_dtype,
+                            const float* dS, const int32_t* key_idx, int64_t num_queries, int32_t topk,
+                            const int32_t* perm, const int32_t* seg_offsets, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+    const char* what = "dr_sparse_attn_dk";
+    dr_status st = check_dtype(q_dtype, what);
+    if (st != DR_OK) return st;
+    if ((st = check_rows(Q, q_dtype, head_dim, what)) != DR_OK) return st;
+    if (num_queries < 0 || topk < 1)
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: num_queries must be >= 0 and topk >= 1", what);
+    if (num_queries > kMaxN / topk)
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: num_queries * topk must be below 2^31", what);
+    const int64_t n = num_queries * (int64_t)topk;
+    if (n > 0 && (!dS || !aligned(dS, 4))) return fail(DR_ERR_INVALID_ARGUMENT, "%s: dS must be non-null and 4-byte aligned", what);
+    return run_index_add(what, dK, num_keys, head_dim, Contributions{Q, q_dtype, dS, topk}, n, key_idx, perm,
+                         seg_offsets, ws, ws_bytes, stream);
 }
 
 dr_status dr_index_add_atomic(float* out, int32_t num_dests, int64_t hidden, const void* src, dr_dtype src_dtype,

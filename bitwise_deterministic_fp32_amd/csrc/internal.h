@@ -112,9 +112,11 @@ hipError_t launch_plan_write(const int32_t* seg_offsets, int32_t num_dests, int 
                              hipStream_t s);
 hipError_t launch_plan_validate(const int32_t* perm, const int32_t* seg, const int32_t* index, int64_t n,
                                 int32_t num_dests, int32_t* status, hipStream_t s);
+// scale != null: source row p contributes fl32(scale[p] * src[p / rows_per_src])
 hipError_t launch_segreduce(float* out, int64_t hidden, const void* src, dr_dtype src_dtype, int64_t n,
                             const int32_t* perm, const TileRec* tiles, float* partials, int tile_chunks_log2,
-                            int chunks_in_flight, int32_t* status, hipStream_t s);
+                            int chunks_in_flight, const float* scale, int32_t rows_per_src, int32_t* status,
+                            hipStream_t s);
 hipError_t launch_tilecombine(float* out, int64_t hidden, const float* partials, const MultiRec* multis, int64_t n,
                               int tile_chunks_log2, int32_t* status, hipStream_t s);
 

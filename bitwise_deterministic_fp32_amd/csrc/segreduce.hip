@@ -266,10 +266,17 @@ __device__ __forceinline__ u32x4 pack4(const float* t) {
 // bf16 or 4 fp32 columns), so every row load is one 16-byte load per lane and
 // a group reads GROUP*16 contiguous bytes.  One group reduces one (tile,
 // column slice).
-template <dr_dtype DT, int GROUP, int TCLOG, int CIF>
+//
+// GEN: the contribution of source row p is formed here instead of loaded:
+// fl32(scale[p] * src[p / rows_per_src]) element by element (the sparse-
+// attention key gradient: scale = dS, src = Q, rows_per_src = top-k).  The
+// product is rounded before it enters the tree.  src rows are then shared by
+// many contributions and small, so they are read through the cache.
+template <dr_dtype DT, int GROUP, int TCLOG, int CIF, bool GEN>
 __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
     float* __restrict__ out, int64_t H, const void* __restrict__ src, const int32_t* __restrict__ perm,
-    const TileRec* __restrict__ tiles, float* __restrict__ partials, int64_t slices, int32_t* status) {
+    const TileRec* __restrict__ tiles, float* __restrict__ partials, int64_t slices, int32_t* status,
+    const float* __restrict__ scale, uint32_t rows_per_src) {
     using V = Vec<DT>;
     constexpr int E = V::kElems;  // columns of a lane
     constexpr int Q = E / 4;      // 16-byte fp32 pieces of a lane's output
@@ -311,8 +318,17 @@ __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
         for (int j = 0; j < R; ++j) idx[j] = perm[min(r_begin + j, r_end - 1)];
         for (int64_t r0 = r_begin; r0 < r_end; r0 += R) {
             u32x4 raw[R];
+            float sc[GEN ? R : 1];
             const int64_t live = r_end - r0;  // rows of this step that exist
-            if (live >= R) {
+            if (GEN) {
+#pragma unroll
+                for (int j = 0; j < R; ++j) {
+                    // rows past the tile's end repeat a live row (a cache hit) and are not added
+                    const uint32_t p = (uint32_t)idx[j];
+                    sc[j] = scale[p];
+                    raw[j] = load16(src_bytes + (int64_t)(p / rows_per_src) * row_bytes + lcol * kElemBytes);
+                }
+            } else if (live >= R) {
 #pragma unroll
                 for (int j = 0; j < R; ++j)
                     raw[j] = load16_stream(src_bytes + (int64_t)idx[j] * row_bytes + lcol * kElemBytes);
@@ -335,11 +351,19 @@ __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
                 if (m > 0) {
                     float s[E];
                     V::widen(raw[8 * c], s);
+                    if (GEN) {
+#pragma unroll
+                        for (int e = 0; e < E; ++e) s[e] = sc[8 * c] * s[e];
+                    }
                     if (m == 8) {
 #pragma unroll
                         for (int j = 1; j < 8; ++j) {
                             float v[E];
                             V::widen(raw[8 * c + j], v);
+                            if (GEN) {
+#pragma unroll
+                                for (int e = 0; e < E; ++e) v[e] = sc[8 * c + j] * v[e];  // rounded product
+                            }
 #pragma unroll
                             for (int e = 0; e < E; ++e) s[e] = s[e] + v[e];
                         }
@@ -348,6 +372,10 @@ __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
                         for (int j = 1; j < 8; ++j) {
                             float v[E];
                             V::widen(raw[8 * c + j], v);
+                            if (GEN) {
+#pragma unroll
+                                for (int e = 0; e < E; ++e) v[e] = sc[8 * c + j] * v[e];
+                            }
 #pragma unroll
                             for (int e = 0; e < E; ++e) {
                                 const float a = s[e] + v[e];
@@ -423,14 +451,14 @@ int group_for(int64_t pieces) {
     return 64;
 }
 
-template <dr_dtype DT, int GROUP, int CIF>
+template <dr_dtype DT, int GROUP, int CIF, bool GEN>
 hipError_t launch_segreduce_g(dim3 grid, float* out, int64_t H, const void* src, const int32_t* perm,
                               const TileRec* tiles, float* partials, int tc_log2, int64_t slices, int32_t* status,
-                              hipStream_t s) {
+                              const float* scale, uint32_t rows_per_src, hipStream_t s) {
 #define DR_SEGREDUCE_CASE(TC)                                                                                  \
     case TC:                                                                                                   \
-        hipLaunchKernelGGL((segreduce_kernel<DT, GROUP, TC, CIF>), grid, dim3(kReduceThreads), 0, s, out, H,    \
-                           src, perm, tiles, partials, slices, status);                                        \
+        hipLaunchKernelGGL((segreduce_kernel<DT, GROUP, TC, CIF, GEN>), grid, dim3(kReduceThreads), 0, s, out,  \
+                           H, src, perm, tiles, partials, slices, status, scale, rows_per_src);                \
         break;
     switch (tc_log2) {
         DR_SEGREDUCE_CASE(3)
@@ -478,25 +506,30 @@ hipError_t launch_plan_validate(const int32_t* perm, const int32_t* seg, const i
 }
 
 hipError_t launch_segreduce(float* out, int64_t hidden, const void* src, dr_dtype dt, int64_t n, const int32_t* perm,
-                            const TileRec* tiles, float* partials, int tc_log2, int cif, int32_t* status,
-                            hipStream_t s) {
+                            const TileRec* tiles, float* partials, int tc_log2, int cif, const float* scale,
+                            int32_t rows_per_src, int32_t* status, hipStream_t s) {
     (void)n;
     const int64_t lanes = dt == DR_BF16 ? hidden / 8 : hidden / 4;  // lanes needed per row
     const int g = group_for(lanes);
     const int64_t slices = (lanes + g - 1) / g;
     const dim3 grid(persistent_grid());
-#define DR_SR(DT, G)                                                                                              \
-    return cif == 1 ? launch_segreduce_g<DT, G, 1>(grid, out, hidden, src, perm, tiles, partials,    \
-                                                   tc_log2, slices, status, s)                                    \
-                    : launch_segreduce_g<DT, G, 2>(grid, out, hidden, src, perm, tiles, partials,    \
-                                                   tc_log2, slices, status, s)
+    const uint32_t rps = (uint32_t)rows_per_src;
+    // formed contributions (scale != null) always stream one chunk at a time
+#define DR_SR(DT, G)                                                                                           \
+    if (scale)                                                                                                 \
+        return launch_segreduce_g<DT, G, 1, true>(grid, out, hidden, src, perm, tiles, partials, tc_log2,      \
+                                                  slices, status, scale, rps, s);                              \
+    return cif == 1 ? launch_segreduce_g<DT, G, 1, false>(grid, out, hidden, src, perm, tiles, partials,       \
+                                                          tc_log2, slices, status, nullptr, 1u, s)             \
+                    : launch_segreduce_g<DT, G, 2, false>(grid, out, hidden, src, perm, tiles, partials,       \
+                                                          tc_log2, slices, status, nullptr, 1u, s)
     if (dt == DR_BF16) {
-        if (g == 16) DR_SR(DR_BF16, 16);
-        if (g == 32) DR_SR(DR_BF16, 32);
+        if (g == 16) { DR_SR(DR_BF16, 16); }
+        if (g == 32) { DR_SR(DR_BF16, 32); }
         DR_SR(DR_BF16, 64);
     }
-    if (g == 16) DR_SR(DR_F32, 16);
-    if (g == 32) DR_SR(DR_F32, 32);
+    if (g == 16) { DR_SR(DR_F32, 16); }
+    if (g == 32) { DR_SR(DR_F32, 32); }
     DR_SR(DR_F32, 64);
 #undef DR_SR
 }

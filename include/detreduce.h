@@ -197,6 +197,40 @@ dr_status dr_index_add(float* out, int32_t num_dests, int64_t hidden, const void
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Sparse-attention key gradient with the contributions formed on the fly:
+ *   dK[key] = dK[key] + T(fl32(dS[q][j] * Q[q]) over the (q, j) with
+ *             key_idx[q][j] == key, in order of q * topk + j).
+ *
+ * The backward of DeepSeek-V4's sparse attention (ch. 9, section 3.1): every
+ * query selected topk keys, and a selected key's gradient sums, over the
+ * queries that chose it, the query row scaled by its score gradient.  This is
+ * dr_index_add over the contributions c[q*topk + j] = fl32(dS[q][j] * Q[q])
+ * (each element rounded once, never fused into the add), computed inside the
+ * reduction, so the [num_queries * topk, head_dim] contribution matrix is
+ * never written or read.  Any softmax scale is folded into dS by the caller.
+ *
+ *   dK[num_keys, head_dim]    fp32, accumulated in place; keys no query
+ *                             selected are not written.
+ *   Q[num_queries, head_dim]  fp32 or bf16 rows (16-byte aligned; head_dim a
+ *                             multiple of 4 / 8).
+ *   dS[num_queries, topk]     fp32 score gradients.
+ *   key_idx[num_queries, topk] int32 selected keys.
+ *   perm, seg_offsets         both NULL (the call sorts key_idx), or both from
+ *                             dr_sort_by_dest(key_idx, src_id = NULL) on the
+ *                             same key_idx (a plan reused across calls).
+ *   ws, ws_bytes              >= dr_sparse_attn_dk_workspace_size(), 16-byte
+ *                             aligned; the first 256 bytes are the status word.
+ * num_queries * topk must be below 2^31.  A key index out of range (or an
+ * inconsistent plan) leaves dK untouched and is reported by
+ * dr_workspace_status.
+ * ---------------------------------------------------------------------- */
+size_t dr_sparse_attn_dk_workspace_size(int64_t num_queries, int32_t topk, int32_t num_keys, int64_t head_dim);
+dr_status dr_sparse_attn_dk(float* dK, int32_t num_keys, int64_t head_dim, const void* Q, dr_dtype q_dtype,
+                            const float* dS, const int32_t* key_idx, int64_t num_queries, int32_t topk,
+                            const int32_t* perm, const int32_t* seg_offsets, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Split-K contraction into private per-split buffers.
  *
  * partials[s] = X_s^T * dY_s for split s = tokens [s*c, min(K, (s+1)*c)),

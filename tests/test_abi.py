@@ -44,6 +44,7 @@ def declared():
 def test_header_declares_the_entry_points():
     names = declared()
     for required in ("dr_sort_by_dest", "dr_combine", "dr_index_add", "dr_splitk_reduce", "dr_fingerprint",
+                     "dr_combine_fingerprinted", "dr_sparse_attn_dk",
                      "dr_combine_atomic", "dr_index_add_atomic", "dr_splitk_gemm_tn", "dr_splitk_gemm_tn_atomic"):
         assert required in names
 
@@ -108,6 +109,38 @@ def test_index_add_rejects_bad_arguments(lib):
     # misaligned workspace or out
     assert f(FAKE, 64, 128, FAKE, 1, 1000, FAKE, None, None, FAKE + 4, need, None) == DR_ERR_INVALID_ARGUMENT
     assert f(FAKE + 4, 64, 128, FAKE, 1, 1000, FAKE, None, None, FAKE, need, None) == DR_ERR_INVALID_ARGUMENT
+
+
+def test_sparse_attn_dk_rejects_bad_arguments(lib):
+    f = lib.dr_sparse_attn_dk
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.dr_sparse_attn_dk_workspace_size.restype = ctypes.c_size_t
+    lib.dr_sparse_attn_dk_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64]
+    lib.dr_index_add_workspace_size.restype = ctypes.c_size_t
+    lib.dr_index_add_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int64]
+    need = lib.dr_sparse_attn_dk_workspace_size(100, 16, 512, 128)
+    assert need == lib.dr_index_add_workspace_size(1600, 512, 128)
+    ok_args = (FAKE, 512, 128, FAKE, 1, FAKE, FAKE, 100, 16, None, None, FAKE, need, None)
+
+    def call(**kw):
+        names = ["dK", "K", "H", "Q", "dt", "dS", "idx", "nq", "topk", "perm", "seg", "ws", "wsb", "s"]
+        args = dict(zip(names, ok_args))
+        args.update(kw)
+        return f(*[args[n] for n in names])
+
+    assert call(wsb=need - 1) == DR_ERR_WORKSPACE_TOO_SMALL
+    assert call(topk=0) == DR_ERR_INVALID_ARGUMENT
+    assert call(nq=-1) == DR_ERR_INVALID_ARGUMENT
+    assert call(nq=1 << 27, topk=16) == DR_ERR_INVALID_ARGUMENT      # 2^31 contributions
+    assert call(dS=None) == DR_ERR_INVALID_ARGUMENT
+    assert call(dS=FAKE + 2) == DR_ERR_INVALID_ARGUMENT
+    assert call(Q=FAKE + 8) == DR_ERR_INVALID_ARGUMENT               # 16-byte aligned rows
+    assert call(H=132) == DR_ERR_INVALID_ARGUMENT                    # bf16 rows need 8 | head_dim
+    assert call(dt=5) == DR_ERR_UNSUPPORTED
+    assert call(perm=FAKE) == DR_ERR_INVALID_ARGUMENT                # perm without seg_offsets
+    assert call(K=0) == DR_ERR_INVALID_ARGUMENT
 
 
 def test_sort_rejects_bad_arguments(lib):

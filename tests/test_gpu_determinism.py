@@ -174,6 +174,23 @@ def test_index_add_launch_invariance(dr, dk):
                 assert fp == ref, (grid, tc, st)
 
 
+def test_sparse_attn_dk_launch_invariance_and_replays(dr):
+    inp = workloads.sparse_attn_dk_inputs(31, 600, 400, 32, 128, s=1.1)
+    Q, dS, idx = dev_bf16(inp.Q), dev(inp.dS), dev(inp.key_idx)
+    ref = None
+    for grid, tc, st in ((0, 5, 0), (7, 3, 8), (1000, 7, 12), (0, 4, 13), (0, 6, 10), (0, 5, 0)):
+        say(f"sparse_attn_dk launch grid={grid} tile=2^{tc} sort_tile={st}")
+        dr.dr_set_launch_params(grid_blocks=grid, tile_chunks_log2=tc, sort_tile_log2=st)
+        try:
+            dK = dev(inp.dK0)
+            dr.dr_sparse_attn_dk(dK, Q, dS, idx)
+            fp = dr.fingerprint_value(dK)
+        finally:
+            dr.dr_set_launch_params(reset=True)
+        ref = fp if ref is None else ref
+        assert fp == ref, (grid, tc, st)
+
+
 def test_sort_launch_invariance(dr, dk):
     inp, src, index, out0 = dk
     ref = None

@@ -93,6 +93,35 @@ def test_index_add_full(dr, name):
     assert dr.fingerprint_value(out2) == dr.fingerprint_value(out)
 
 
+def test_sparse_attn_dk_fused_full(dr):
+    """The sparse-attention dK shape (8192 queries x 512 selected keys of 65,536,
+    head 128) with the contributions formed in the reduce."""
+    say("sparse_attn_dk fused: generating inputs")
+    inp = workloads.sparse_attn_dk_inputs(1003)
+    nq, topk = inp.key_idx.shape
+    Q, dS, idx = dev_bf16(inp.Q), dev(inp.dS), dev(inp.key_idx)
+    dK0 = dev(inp.dK0)
+    dK = dK0.clone()
+    say("sparse_attn_dk fused: reduce")
+    _, ws = dr.dr_sparse_attn_dk(dK, Q, dS, idx)
+    dr.dr_workspace_status(ws)
+    counts = np.bincount(inp.key_idx.reshape(-1), minlength=inp.num_keys)
+    rng = np.random.default_rng(5)
+    hot = np.argsort(-counts, kind="stable")[:8]
+    untouched = np.nonzero(counts == 0)[0]
+    keys = _sample(rng, inp.num_keys, extra=list(hot) + list(untouched[:4]), count=24)
+    say(f"sparse_attn_dk fused: oracle on {keys.size} sampled keys (hottest has {counts.max()} queries)")
+    want = oracle.sparse_attn_dk(inp.dK0, inp.Q, inp.dS, inp.key_idx, keys=keys)
+    assert_bits_equal(host(dK[dev(keys)]), want, "sparse_attn_dk fused")
+    mask = dev(counts == 0)
+    assert torch.equal(dK[mask].view(torch.int32), dK0[mask].view(torch.int32))
+    # a reused plan and a replay give the same bytes
+    perm, seg, _ = dr.dr_sort_by_dest(idx.reshape(-1), inp.num_keys, want_inv=False)
+    dK2 = dK0.clone()
+    dr.dr_sparse_attn_dk(dK2, Q, dS, idx, perm=perm, seg_offsets=seg)
+    assert dr.fingerprint_value(dK2) == dr.fingerprint_value(dK)
+
+
 def test_splitk_full(dr):
     say("splitk_mhc: generating inputs")
     inp = workloads.make("splitk_mhc")

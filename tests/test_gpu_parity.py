@@ -183,6 +183,49 @@ def test_index_add_order_example_fp32(dr):
 
 
 # ---------------------------------------------------------------------------
+# sparse-attention key gradient (contributions formed in the reduce)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("nq,topk,H,K,q_dtype", [
+    (300, 16, 128, 512, "bf16"),
+    (257, 7, 64, 100, "f32"),      # ragged chunks, fp32 query rows
+    (1000, 64, 128, 300, "bf16"),  # keys chosen by up to 1000 queries: several tiles per key
+    (3, 5, 8, 9, "bf16"),          # tiny, most keys untouched
+])
+def test_sparse_attn_dk_matches_oracle(dr, nq, topk, H, K, q_dtype):
+    say(f"sparse_attn_dk nq={nq} topk={topk} H={H} K={K} {q_dtype}")
+    inp = workloads.sparse_attn_dk_inputs(nq + K, nq, K, topk, H, s=1.1)
+    Qh = inp.Q if q_dtype == "bf16" else workloads.bf16_to_f32(inp.Q)
+    Q = dev_bf16(Qh) if q_dtype == "bf16" else dev(Qh)
+    dS, idx = dev(inp.dS), dev(inp.key_idx)
+    dK = dev(inp.dK0)
+    dr.dr_sparse_attn_dk(dK, Q, dS, idx)
+    want = oracle.sparse_attn_dk(inp.dK0, Qh, inp.dS, inp.key_idx)
+    assert_bits_equal(host(dK), want, "sparse_attn_dk")
+    # the same bits as index_add over contributions materialised by torch (fp32 products)
+    q_of = torch.arange(nq * topk, device="cuda") // topk
+    contrib = (dS.reshape(-1, 1) * Q.float()[q_of]).contiguous()
+    ref = dev(inp.dK0)
+    dr.dr_index_add(ref, contrib, idx.reshape(-1).contiguous())
+    assert_bits_equal(host(ref), want, "index_add over materialised contributions")
+    # a reused plan gives the same bits
+    perm, seg, _ = dr.dr_sort_by_dest(idx.reshape(-1).contiguous(), K, want_inv=False)
+    dK2 = dev(inp.dK0)
+    dr.dr_sparse_attn_dk(dK2, Q, dS, idx, perm=perm, seg_offsets=seg)
+    assert_bits_equal(host(dK2), want, "reused plan")
+
+
+def test_sparse_attn_dk_bad_key_leaves_dk_untouched(dr):
+    inp = workloads.sparse_attn_dk_inputs(5, 64, 128, 8, 64, s=1.1)
+    bad = inp.key_idx.copy()
+    bad[10, 3] = 128
+    dK = dev(inp.dK0)
+    _, ws = dr.dr_sparse_attn_dk(dK, dev_bf16(inp.Q), dev(inp.dS), dev(bad))
+    with pytest.raises(dr.DetReduceError):
+        dr.dr_workspace_status(ws)
+    assert_bits_equal(host(dK), inp.dK0, "dK after a bad key")
+
+
+# ---------------------------------------------------------------------------
 # split-K
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("K,M,N,splits", [

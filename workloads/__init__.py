@@ -207,6 +207,29 @@ def sparse_attn_inputs(seed: int, Q: int = 8192, K: int = 65536, S: int = 512, H
     return IndexAddInputs(n, K, H, "bf16", keys.reshape(-1), src, out0, {"Q": Q, "S": S})
 
 
+@dataclass
+class SparseAttnDkInputs:
+    nq: int
+    num_keys: int
+    H: int
+    key_idx: np.ndarray    # int32 [nq, topk]
+    Q: np.ndarray          # uint16 bf16 bits [nq, H]
+    dS: np.ndarray         # float32 [nq, topk]
+    dK0: np.ndarray        # float32 [num_keys, H]
+
+
+def sparse_attn_dk_inputs(seed: int, Q: int = 8192, K: int = 65536, S: int = 512, H: int = 128,
+                          s: float = 1.1, ds_scale: float = 0.1) -> SparseAttnDkInputs:
+    """The same key selection as sparse_attn_inputs, with the query rows (bf16
+    N(0,1)) and score gradients (fp32 N(0, ds_scale^2)) instead of
+    materialised contribution rows."""
+    keys = sparse_attn_keys(seed, Q, K, S, s)
+    q = normal_bf16(seed, 11, Q * H).reshape(Q, H)
+    ds = normal_f32(seed, 12, Q * S, ds_scale).reshape(Q, S)
+    dk0 = normal_f32(seed, 5, K * H).reshape(K, H)
+    return SparseAttnDkInputs(Q, K, H, keys, q, ds, dk0)
+
+
 def embedding_grad_inputs(seed: int, tokens: int = 8 * 4096, V: int = 131072, H: int = 4096,
                           s: float = 1.1, preset_out: bool = True) -> IndexAddInputs:
     """Token ids i.i.d. with P ~ (id+1)^-s; bf16 upstream gradients N(0,1)."""
