@@ -128,6 +128,7 @@ def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
         dr.dr_index_add_atomic(out, src, index)
     ms_atomic = _timed(torch, steps, lambda: dr.dr_index_add_atomic(out, src, index))
 
+    fused = _fused_dk(torch, dr, steps, warmup) if name == "sparse_attn_dk" else None
     det_ms = ph["index_add"]
     achieved = red_bytes / (det_ms * 1e-3) / 1e9
     res = {
@@ -150,9 +151,38 @@ def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
                                "overhead": round(det_ms / ms_atomic - 1, 4),
                                "overhead_reused_plan": round(ms_plan / ms_atomic - 1, 4)},
     }
+    if fused:
+        res["fused_dk"] = fused
     if want_cpu:
         res["cpu_baseline"] = _cpu_index_add(oracle, inp, cpu_seconds)
     return res
+
+
+def _fused_dk(torch, dr, steps, warmup):
+    """dr_sparse_attn_dk on the same key selection: the contributions
+    fl32(dS * Q) are formed in the reduce instead of read as 1.07 GB of rows."""
+    import workloads
+    _log("sparse_attn_dk: fused key gradient (query rows and score gradients)")
+    inp = workloads.sparse_attn_dk_inputs(workloads.CONFIGS["sparse_attn_dk"]["seed"])
+    nq, topk = inp.key_idx.shape
+    Q = torch.from_numpy(inp.Q.view(np.int16)).view(torch.bfloat16).cuda()
+    dS = torch.from_numpy(inp.dS).cuda()
+    idx = torch.from_numpy(inp.key_idx).cuda()
+    dK = torch.from_numpy(inp.dK0).cuda()
+    ws = torch.empty(dr.dr_sparse_attn_dk_workspace_size(nq, topk, inp.num_keys, inp.H), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(warmup):
+        dr.dr_sparse_attn_dk(dK, Q, dS, idx, ws=ws)
+    ms = _timed(torch, steps, lambda: dr.dr_sparse_attn_dk(dK, Q, dS, idx, ws=ws))
+    perm, seg, _ = dr.dr_sort_by_dest(idx.reshape(-1), inp.num_keys, want_inv=False)
+    for _ in range(warmup):
+        dr.dr_sparse_attn_dk(dK, Q, dS, idx, perm=perm, seg_offsets=seg, ws=ws)
+    ms_plan = _timed(torch, steps, lambda: dr.dr_sparse_attn_dk(dK, Q, dS, idx, perm=perm, seg_offsets=seg, ws=ws))
+    touched = int((np.bincount(inp.key_idx.reshape(-1), minlength=inp.num_keys) > 0).sum())
+    n = nq * topk
+    alg = nq * inp.H * 2 + n * 4 + n * 4 + 2 * touched * inp.H * 4  # Q, dS, key ids, dK read-modify-write
+    return {"ms": round(ms, 4), "reused_plan_ms": round(ms_plan, 4), "algorithmic_bytes": alg,
+            "note": "contributions formed from Q [8192,128] bf16 and dS [8192,512] fp32; the same key selection"}
 
 
 def _cpu_index_add(oracle, inp, seconds):

@@ -176,7 +176,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_write_kernel(const int32_t*
 }
 
 // Checks a caller-supplied plan: every sorted position r holds a source row
-// p = perm[r] in range whose index[p] = d satisfies seg[d] <= r < seg[d+1].
+// p = perm[r] in range whose index[p] = d satisfies seg[d] <= r < seg[d+1],
+// and the next position of the same segment holds a larger source row.  Then
+// perm is injective (rows of different segments have different indices), so
+// it is a permutation, each segment holds exactly its destination's rows, in
+// ascending source order: the stable sort itself, and nothing else passes.
 __global__ void plan_validate_kernel(const int32_t* __restrict__ perm, const int32_t* __restrict__ seg,
                                      const int32_t* __restrict__ index, int64_t n, int32_t num_dests,
                                      int32_t* status) {
@@ -188,8 +192,13 @@ __global__ void plan_validate_kernel(const int32_t* __restrict__ perm, const int
         err = kStatusPlan;
     } else {
         const int32_t d = index[p];
-        if (d < 0 || d >= num_dests) err = kStatusIndex;
-        else if (r < seg[d] || r >= seg[d + 1]) err = kStatusPlan;
+        if (d < 0 || d >= num_dests) {
+            err = kStatusIndex;
+        } else {
+            const int32_t lo = seg[d], hi = seg[d + 1];
+            if (r < lo || r >= hi) err = kStatusPlan;
+            else if (r + 1 < hi && r + 1 < n && perm[r + 1] <= p) err = kStatusPlan;  // source order
+        }
     }
     if (err) atomicOr(&status[kWordStatus], err);
 }

@@ -185,7 +185,10 @@ dr_status dr_combine_fingerprinted(const void* rows, dr_dtype rows_dtype, int64_
  *   index[n]                int32 destinations.
  *   perm, seg_offsets       either both NULL (the call sorts internally), or
  *                           both from dr_sort_by_dest(index, src_id = NULL) on
- *                           the same index (a reused plan).
+ *                           the same index (a reused plan).  A given plan is
+ *                           checked on the device: anything but that stable
+ *                           sort (rows in the wrong segment, out of source
+ *                           order, repeated or missing) is refused.
  *   ws, ws_bytes            workspace >= dr_index_add_workspace_size(), 16-byte
  *                           aligned; the first 256 bytes are the status word.
  * Device-detected errors (index out of range, inconsistent plan) leave out

@@ -315,12 +315,19 @@ def test_index_add_bad_plan_is_refused(dr, dk):
     say("index_add bad plan")
     inp, src, index, out0 = dk
     perm, seg, _ = dr.dr_sort_by_dest(index, inp.D, want_inv=False)
-    for corrupt in ("seg", "perm"):
+    seg_h = host(seg)
+    d_long = int(np.argmax(np.diff(seg_h)))  # a segment with at least two rows
+    lo = int(seg_h[d_long])
+    for corrupt in ("seg", "perm", "order", "duplicate"):
         p, s = perm.clone(), seg.clone()
         if corrupt == "seg":
             s[100] = s[101] + 1  # not monotone
-        else:
+        elif corrupt == "perm":
             p[0], p[-1] = p[-1].clone(), p[0].clone()  # rows in the wrong segments
+        elif corrupt == "order":
+            p[lo], p[lo + 1] = p[lo + 1].clone(), p[lo].clone()  # right segment, wrong source order
+        else:
+            p[lo + 1] = p[lo].clone()  # a source row twice, another never
         out = out0.clone()
         _, ws = dr.dr_index_add(out, src, index, perm=p, seg_offsets=s)
         with pytest.raises(dr.DetReduceError) as e:
