@@ -225,6 +225,56 @@ def splitk_partials(X, dY, splits: int):
     return P
 
 
+def grouped_slots(group_offsets, split_tokens: int):
+    """The private slots of a grouped split: group g owns tokens
+    [off[g], off[g+1]), cut into consecutive slots of split_tokens tokens from
+    its first token (the last one short).  Returns (slot_offsets [G+1],
+    slot token ranges [S, 2]), slots in (group, position) order."""
+    off = np.asarray(group_offsets, dtype=np.int64)
+    G = off.size - 1
+    slot_off = [0]
+    ranges = []
+    for g in range(G):
+        t = int(off[g])
+        while t < off[g + 1]:
+            ranges.append((t, min(int(off[g + 1]), t + split_tokens)))
+            t += split_tokens
+        slot_off.append(len(ranges))
+    return np.array(slot_off, np.int32), np.array(ranges, np.int64).reshape(-1, 2)
+
+
+def grouped_splitk_partials(X, dY, group_offsets, split_tokens: int):
+    """fp64 (exact for bf16 inputs) X_s^T dY_s of every private slot s [S, M, N]."""
+    X = _c(X, np.uint16)
+    dY = _c(dY, np.uint16)
+    _, ranges = grouped_slots(group_offsets, split_tokens)
+    M, N = X.shape[1], dY.shape[1]
+    P = np.empty((len(ranges), M, N), np.float64)
+    for s, (a, b) in enumerate(ranges):
+        P[s] = splitk_partials(X[a:b], dY[a:b], 1)[0]
+    return P
+
+
+def grouped_splitk_reduce(partials, slot_offsets):
+    """out[g] = T(partials[slot_offsets[g]], ..., partials[slot_offsets[g+1]-1]) in slot order;
+    a group with no slot (no tokens) has the zero gradient."""
+    p = _c(partials, np.float32)
+    so = np.asarray(slot_offsets, dtype=np.int64)
+    G = so.size - 1
+    out = np.zeros((G,) + p.shape[1:], np.float32)
+    for g in range(G):
+        if so[g + 1] > so[g]:
+            out[g] = splitk_reduce(p[so[g]:so[g + 1]])
+    return out
+
+
+def permute_rows(x, perm, k: int):
+    """Dispatch-side stable permute: out[r] = x[perm[r] // k] (bytes copied)."""
+    x = np.ascontiguousarray(x)
+    perm = np.asarray(perm, dtype=np.int64)
+    return x[perm // k].copy()
+
+
 def splitmix64_mix(z: int) -> int:
     return int(lib().oracle_splitmix64_mix(ctypes.c_uint64(z & ((1 << 64) - 1))))
 

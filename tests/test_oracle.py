@@ -505,6 +505,53 @@ def test_splitk_reference_against_matmul():
 
 
 # ---------------------------------------------------------------------------
+# Grouped split with private slots; the dispatch permute
+# ---------------------------------------------------------------------------
+def test_grouped_slots_brute_force():
+    """Slots cut each group from its first token; empty groups own no slot."""
+    off = [0, 0, 5, 5, 6, 14]
+    so, rng = oracle.grouped_slots(off, 3)
+    assert so.tolist() == [0, 0, 2, 2, 3, 6]
+    assert rng.tolist() == [[0, 3], [3, 5], [5, 6], [6, 9], [9, 12], [12, 14]]
+    so, rng = oracle.grouped_slots([0, 4], 4)
+    assert so.tolist() == [0, 1] and rng.tolist() == [[0, 4]]
+
+
+def test_grouped_splitk_reference_and_reduce():
+    rng = np.random.default_rng(81)
+    K, M, N = 200, 12, 5
+    X = workloads.bf16_bits(rng.standard_normal((K, M)).astype(F32))
+    dY = workloads.bf16_bits(rng.standard_normal((K, N)).astype(F32))
+    off = np.array([0, 37, 37, 120, 200], np.int32)
+    x = workloads.bf16_to_f32(X).astype(np.float64)
+    y = workloads.bf16_to_f32(dY).astype(np.float64)
+    so, ranges = oracle.grouped_slots(off, 16)
+    P = oracle.grouped_splitk_partials(X, dY, off, 16)
+    for s, (a, b) in enumerate(ranges):
+        assert np.allclose(P[s], x[a:b].T @ y[a:b], rtol=0, atol=1e-12)
+    # each group's slots sum to that group's matmul
+    for g in range(4):
+        want = x[off[g]:off[g + 1]].T @ y[off[g]:off[g + 1]]
+        assert np.allclose(P[so[g]:so[g + 1]].sum(axis=0), want, rtol=0, atol=1e-11)
+    # the reduce: up to 8 slots left to right in float32; an empty group is zero
+    Pf = P.astype(F32)
+    out = oracle.grouped_splitk_reduce(Pf, so)
+    assert np.array_equal(out[1], np.zeros((M, N), F32)) and so[2] == so[1]
+    g0 = Pf[so[0]:so[1]]
+    assert g0.shape[0] == 3
+    assert np.array_equal(out[0].view(np.uint32), ((g0[0] + g0[1]) + g0[2]).view(np.uint32))
+    assert np.array_equal(out[3], oracle.splitk_reduce(Pf[so[3]:so[4]]))
+
+
+def test_permute_rows_brute_force():
+    x = np.arange(5 * 3, dtype=np.int32).reshape(5, 3)
+    perm = np.array([4, 0, 9, 3, 1, 2, 8, 5, 7, 6], np.int32)   # a permutation of 5 tokens x 2 slots
+    out = oracle.permute_rows(x, perm, 2)
+    for r in range(10):
+        assert out[r].tolist() == x[perm[r] // 2].tolist()
+
+
+# ---------------------------------------------------------------------------
 # Fingerprint
 # ---------------------------------------------------------------------------
 def test_splitmix64_published_outputs(golden_dir):
