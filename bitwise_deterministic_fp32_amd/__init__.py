@@ -23,6 +23,8 @@ __all__ = [
     "dr_index_add_workspace_size", "dr_index_add", "dr_index_add_atomic",
     "dr_sparse_attn_dk_workspace_size", "dr_sparse_attn_dk",
     "dr_splitk_gemm_tn", "dr_splitk_gemm_tn_atomic", "dr_splitk_reduce",
+    "dr_grouped_splitk_max_slots", "dr_grouped_splitk_workspace_size", "dr_grouped_splitk_gemm_tn",
+    "dr_grouped_splitk_reduce", "dr_permute_rows",
     "dr_fingerprint_workspace_size", "dr_fingerprint", "fingerprint_value",
     "dr_workspace_status", "dr_read_status",
 ]
@@ -66,6 +68,11 @@ def _load() -> ctypes.CDLL:
         "dr_splitk_gemm_tn": ([vp, vp, i64, i64, i64, i32, vp, vp], ctypes.c_int),
         "dr_splitk_gemm_tn_atomic": ([vp, vp, i64, i64, i64, i32, vp, vp], ctypes.c_int),
         "dr_splitk_reduce": ([vp, i32, i64, vp, vp], ctypes.c_int),
+        "dr_grouped_splitk_max_slots": ([i64, i32, i32], i64),
+        "dr_grouped_splitk_workspace_size": ([i64, i32, i32], sz),
+        "dr_grouped_splitk_gemm_tn": ([vp, vp, i64, i64, i64, vp, i32, i32, vp, i64, vp, vp, sz, vp], ctypes.c_int),
+        "dr_grouped_splitk_reduce": ([vp, i64, vp, i32, i64, vp, vp, vp], ctypes.c_int),
+        "dr_permute_rows": ([vp, i64, i64, vp, i64, i32, vp, vp, vp], ctypes.c_int),
         "dr_fingerprint_workspace_size": ([i64], sz),
         "dr_fingerprint": ([vp, i64, vp, vp, sz, vp], ctypes.c_int),
         "dr_workspace_status": ([vp, vp], ctypes.c_int),
@@ -300,6 +307,60 @@ def dr_splitk_reduce(partials, *, out=None, stream=None):
     out = out if out is not None else torch.empty(partials.shape[1:], dtype=torch.float32, device=partials.device)
     _dev(out, "out", (torch.float32,))
     _check(lib.dr_splitk_reduce(_p(partials), S, count, _p(out), _stream(stream)), "dr_splitk_reduce")
+    return out
+
+
+def dr_grouped_splitk_max_slots(K: int, num_groups: int, split_tokens: int) -> int:
+    return int(lib.dr_grouped_splitk_max_slots(K, num_groups, split_tokens))
+
+
+def dr_grouped_splitk_workspace_size(K: int, num_groups: int, split_tokens: int) -> int:
+    return int(lib.dr_grouped_splitk_workspace_size(K, num_groups, split_tokens))
+
+
+def dr_grouped_splitk_gemm_tn(X, dY, group_offsets, split_tokens: int, *, partials=None, slot_offsets=None, ws=None,
+                              stream=None):
+    """Private slot partials X_s^T dY_s of every group's token slots.  Returns (partials, slot_offsets, ws)."""
+    _dev(X, "X", (torch.bfloat16,))
+    _dev(dY, "dY", (torch.bfloat16,))
+    _dev(group_offsets, "group_offsets", (torch.int32,))
+    K, M = X.shape
+    N = dY.shape[1]
+    G = group_offsets.numel() - 1
+    S = dr_grouped_splitk_max_slots(K, G, split_tokens)
+    partials = partials if partials is not None else torch.empty(S, M, N, dtype=torch.float32, device=X.device)
+    slot_offsets = slot_offsets if slot_offsets is not None else torch.empty(G + 1, dtype=torch.int32,
+                                                                            device=X.device)
+    ws = ws if ws is not None else _workspace(dr_grouped_splitk_workspace_size(K, G, split_tokens), X.device)
+    _dev(partials, "partials", (torch.float32,))
+    _check(lib.dr_grouped_splitk_gemm_tn(_p(X), _p(dY), K, M, N, _p(group_offsets), G, split_tokens, _p(partials),
+                                         partials.shape[0], _p(slot_offsets), _p(ws), ws.numel(), _stream(stream)),
+           "dr_grouped_splitk_gemm_tn")
+    return partials, slot_offsets, ws
+
+
+def dr_grouped_splitk_reduce(partials, slot_offsets, ws, *, out=None, stream=None):
+    """out[g] = ordered tree over group g's slots (zero for an empty group)."""
+    _dev(partials, "partials", (torch.float32,))
+    G = slot_offsets.numel() - 1
+    count = partials[0].numel() if partials.shape[0] else 0
+    out = out if out is not None else torch.empty((G,) + tuple(partials.shape[1:]), dtype=torch.float32,
+                                                  device=partials.device)
+    _check(lib.dr_grouped_splitk_reduce(_p(partials), partials.shape[0], _p(slot_offsets), G, count, _p(out),
+                                        _p(ws), _stream(stream)), "dr_grouped_splitk_reduce")
+    return out
+
+
+def dr_permute_rows(rows, perm, k: int, *, out=None, dev_status=None, stream=None):
+    """out[r] = rows[perm[r] // k] (the expert-major copy of the token rows)."""
+    _dev(perm, "perm", (torch.int32,))
+    if rows.device.type != "cuda" or not rows.is_contiguous():
+        raise ValueError("rows must be a contiguous CUDA tensor")
+    n = perm.numel()
+    row_bytes = rows[0].numel() * rows.element_size() if rows.shape[0] else 0
+    out = out if out is not None else torch.empty((n,) + tuple(rows.shape[1:]), dtype=rows.dtype, device=rows.device)
+    _check(lib.dr_permute_rows(_p(rows), row_bytes, rows.shape[0], _p(perm), n, k, _p(out), _p(dev_status),
+                               _stream(stream)), "dr_permute_rows")
     return out
 
 

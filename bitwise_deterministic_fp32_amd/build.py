@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdetreduce.so")
 
-SOURCES = ["api.cpp", "sort.hip", "segreduce.hip", "combine.hip", "splitk.hip", "fingerprint.hip", "atomic.hip"]
+SOURCES = ["api.cpp", "sort.hip", "segreduce.hip", "combine.hip", "splitk.hip", "fingerprint.hip", "atomic.hip",
+           "permute.hip"]
 ARCH = "gfx950"
 
 # -ffp-contract=off: no multiply-add fusion anywhere (products are rounded

@@ -592,6 +592,90 @@ dr_status dr_splitk_reduce(const float* partials, int32_t splits, int64_t count,
 }
 
 // ---------------------------------------------------------------------------
+int64_t dr_grouped_splitk_max_slots(int64_t K, int32_t num_groups, int32_t split_tokens) {
+    if (K < 0 || num_groups < 1 || split_tokens < 1) return 0;
+    // sum_g ceil(c_g / s) <= sum_g (c_g / s + 1) <= K / s + G
+    return K / split_tokens + num_groups;
+}
+
+size_t dr_grouped_splitk_workspace_size(int64_t K, int32_t num_groups, int32_t split_tokens) {
+    Carver c(nullptr);
+    c.take<int32_t>(dr::kStatusBytes / sizeof(int32_t));
+    c.take<int2>(dr_grouped_splitk_max_slots(K, num_groups, split_tokens));
+    return c.off;
+}
+
+dr_status dr_grouped_splitk_gemm_tn(const void* X, const void* dY, int64_t K, int64_t M, int64_t N,
+                                    const int32_t* group_offsets, int32_t num_groups, int32_t split_tokens,
+                                    float* partials, int64_t partial_slots, int32_t* slot_offsets, void* ws,
+                                    size_t ws_bytes, hipStream_t stream) {
+    const char* what = "dr_grouped_splitk_gemm_tn";
+    if (!X || !dY || !partials || !group_offsets || !slot_offsets || !ws)
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: null pointer", what);
+    if (K < 1 || M < 1 || N < 1) return fail(DR_ERR_INVALID_ARGUMENT, "%s: K, M, N must be >= 1", what);
+    if (num_groups < 1 || num_groups > 65535)
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: num_groups must be in [1, 65535]", what);
+    if (split_tokens < 1) return fail(DR_ERR_INVALID_ARGUMENT, "%s: split_tokens must be >= 1", what);
+    // token indices and slot ranges are int32 on the device
+    if (K >= kMaxN - split_tokens) return fail(DR_ERR_UNSUPPORTED, "%s: K too large for one call", what);
+    if (!aligned(X, 16) || !aligned(dY, 2) || !aligned(partials, 4) || !aligned(group_offsets, 4) ||
+        !aligned(slot_offsets, 4) || !aligned(ws, 16))
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: X and ws must be 16-byte aligned, the rest element-aligned", what);
+    const int64_t max_slots = dr_grouped_splitk_max_slots(K, num_groups, split_tokens);
+    if (partial_slots < max_slots)
+        return fail(DR_ERR_WORKSPACE_TOO_SMALL, "%s: partials hold %lld slots, need %lld", what,
+                    (long long)partial_slots, (long long)max_slots);
+    if (((M + 63) / 64) * ((N + 31) / 32) > 0x7FFFFFFF / max_slots)
+        return fail(DR_ERR_UNSUPPORTED, "%s: M, N and the slot bound give too many tiles for one launch", what);
+    if (ws_bytes < dr_grouped_splitk_workspace_size(K, num_groups, split_tokens))
+        return fail(DR_ERR_WORKSPACE_TOO_SMALL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes,
+                    dr_grouped_splitk_workspace_size(K, num_groups, split_tokens));
+    Carver c(ws);
+    int32_t* status = c.take<int32_t>(dr::kStatusBytes / sizeof(int32_t));
+    int2* ranges = c.take<int2>(max_slots);
+    DR_TRY_HIP(dr::launch_grouped_splitk_gemm(static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(dY), K,
+                                              M, N, group_offsets, num_groups, split_tokens, max_slots, slot_offsets,
+                                              ranges, status, partials, stream),
+               "grouped split-K launch");
+    return ok();
+}
+
+dr_status dr_grouped_splitk_reduce(const float* partials, int64_t partial_slots, const int32_t* slot_offsets,
+                                   int32_t num_groups, int64_t count, float* out, const void* ws,
+                                   hipStream_t stream) {
+    const char* what = "dr_grouped_splitk_reduce";
+    if (!partials || !slot_offsets || !out || !ws) return fail(DR_ERR_INVALID_ARGUMENT, "%s: null pointer", what);
+    if (num_groups < 1 || num_groups > 65535)
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: num_groups must be in [1, 65535]", what);
+    if (count < 0 || partial_slots < 0) return fail(DR_ERR_INVALID_ARGUMENT, "%s: negative size", what);
+    if (!aligned(partials, 4) || !aligned(out, 4) || !aligned(ws, 16))
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: misaligned pointer", what);
+    if ((count % 4 == 0) && (!aligned(partials, 16) || !aligned(out, 16)))
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: partials and out must be 16-byte aligned", what);
+    DR_TRY_HIP(dr::launch_grouped_reduce(partials, slot_offsets, partial_slots, num_groups, count, out,
+                                         static_cast<const int32_t*>(ws), stream),
+               "grouped reduce launch");
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+dr_status dr_permute_rows(const void* rows, int64_t row_bytes, int64_t num_rows, const int32_t* perm, int64_t n,
+                          int32_t k, void* out, int32_t* dev_status, hipStream_t stream) {
+    const char* what = "dr_permute_rows";
+    if (n < 0 || n >= kMaxN || num_rows < 0 || k < 1)
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: need 0 <= n < 2^31, num_rows >= 0, k >= 1", what);
+    if (row_bytes < 16 || row_bytes % 16 != 0)
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: row_bytes must be a positive multiple of 16", what);
+    if (n > 0 && (!rows || !perm || !out)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: null pointer", what);
+    if (n > 0 && (!aligned(rows, 16) || !aligned(out, 16) || !aligned(perm, 4)))
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: rows and out must be 16-byte aligned", what);
+    if (dev_status && !aligned(dev_status, 4)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: misaligned dev_status", what);
+    DR_TRY_HIP(dr::launch_permute_rows(rows, row_bytes, num_rows, perm, n, k, out, dev_status, stream),
+               "permute launch");
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
 size_t dr_fingerprint_workspace_size(int64_t nbytes) {
     (void)nbytes;
     return dr::kStatusBytes + dr::kMaxFingerprintBlocks * sizeof(uint64_t);

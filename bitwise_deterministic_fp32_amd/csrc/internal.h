@@ -22,6 +22,7 @@ constexpr size_t kStatusBytes = 256;  // status block at the head of a workspace
 constexpr int kWordStatus = 0;
 constexpr int kWordTiles = 1;
 constexpr int kWordMultis = 2;
+constexpr int kWordSlots = 1;  // grouped split: private slots in use (its own workspace)
 
 constexpr int kDefaultTileChunksLog2 = 5;
 constexpr int kMinTileChunksLog2 = 3;
@@ -134,6 +135,17 @@ hipError_t launch_splitk_gemm(const uint16_t* X, const uint16_t* dY, int64_t K, 
                               int32_t splits, float* out, bool atomic, hipStream_t s);
 hipError_t launch_splitk_reduce(const float* partials, int32_t splits, int64_t count, float* out,
                                 hipStream_t s);
+// grouped split with private slots: the slot table, then the partials of every slot
+hipError_t launch_grouped_splitk_gemm(const uint16_t* X, const uint16_t* dY, int64_t K, int64_t M, int64_t N,
+                                      const int32_t* group_offsets, int32_t num_groups, int32_t split_tokens,
+                                      int64_t max_slots, int32_t* slot_offsets, int2* ranges, int32_t* status,
+                                      float* out, hipStream_t s);
+hipError_t launch_grouped_reduce(const float* partials, const int32_t* slot_offsets, int64_t max_slots,
+                                 int32_t num_groups, int64_t count, float* out, const int32_t* status,
+                                 hipStream_t s);
+// dispatch-side permute: out[r] = rows[perm[r] / k]
+hipError_t launch_permute_rows(const void* rows, int64_t row_bytes, int64_t num_rows, const int32_t* perm,
+                               int64_t n, int32_t k, void* out, int32_t* dev_status, hipStream_t s);
 // fingerprint
 // most workgroups (and partials) of a fingerprint launch: 8 per SIMD of a
 // 256-CU device, enough wavefronts to hide the loads behind the hashing

@@ -55,9 +55,10 @@ struct UnitGeom {
     bool x_vec;      // full-width M tile with 16-byte rows
 };
 
-// 32-bit tile arithmetic: the host keeps the item count below 2^31.
+// 32-bit tile arithmetic: the host keeps the item count below 2^31.  With
+// ranges (a grouped split), split s covers tokens [ranges[s].x, ranges[s].y).
 __device__ __forceinline__ UnitGeom geometry(const Unit& u, int64_t K, int64_t M, int64_t kc, uint32_t mtiles,
-                                             uint32_t ntiles) {
+                                             uint32_t ntiles, const int2* __restrict__ ranges) {
     UnitGeom g;
     const uint32_t mt = u.item % mtiles;
     const uint32_t rest = u.item / mtiles;
@@ -65,8 +66,15 @@ __device__ __forceinline__ UnitGeom geometry(const Unit& u, int64_t K, int64_t M
     g.s = (int)(rest / ntiles);
     g.m0 = (int64_t)mt * BM;
     g.n0 = (int64_t)nt * BN;
-    const int64_t t_begin = (int64_t)g.s * kc;
-    const int64_t t_end = min(K, t_begin + kc);
+    int64_t t_begin, t_end;
+    if (ranges) {
+        const int2 r = ranges[g.s];
+        t_begin = r.x;
+        t_end = r.y;
+    } else {
+        t_begin = (int64_t)g.s * kc;
+        t_end = min(K, t_begin + kc);
+    }
     g.t0 = t_begin + (int64_t)u.stage * KT;
     g.rows = (int)min((int64_t)KT, t_end - g.t0);
     g.last = g.t0 + KT >= t_end;
@@ -102,24 +110,33 @@ static_assert(BM * OS * 4 <= KT * XS * 2, "output tile must fit in the X stage")
 // loads of the next unit are issued right after the current unit is staged in
 // LDS, so they are in flight during its MFMAs and epilogue.  A partial's
 // accumulation order (token order within its split) is the same for any grid.
+// Grouped split (ranges != null): the splits are the private slots of a slot
+// table, whose count the slot kernel left in the status block; a set status
+// word means the table is invalid and nothing is computed.
 template <bool ATOMIC>
 __global__ __launch_bounds__(kGemmThreads) void splitk_gemm_kernel(const uint16_t* __restrict__ X,
                                                                    const uint16_t* __restrict__ dY, int64_t K,
                                                                    int64_t M, int64_t N, int64_t kc, uint32_t items,
                                                                    uint32_t mtiles, uint32_t ntiles,
-                                                                   float* __restrict__ out) {
+                                                                   float* __restrict__ out,
+                                                                   const int2* __restrict__ ranges,
+                                                                   const int32_t* __restrict__ status) {
     __shared__ __attribute__((aligned(16))) uint16_t xs[KT * XS];
     __shared__ __attribute__((aligned(16))) uint16_t ys[BN * YS];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const bool y_vec = (N % 8) == 0 && (reinterpret_cast<uintptr_t>(dY) & 15) == 0;
     const bool out_vec = (N % 4) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
-    // 32-bit range split: the host keeps items < 2^31 and the grid <= items
+    if (ranges) {
+        if (status[kWordStatus] != 0) return;
+        items = (uint32_t)status[kWordSlots] * ntiles * mtiles;  // the host bounds this below 2^31
+    }
+    // 32-bit range split: the host keeps items < 2^31
     const uint32_t per = items / gridDim.x, extra = items % gridDim.x, wg = blockIdx.x;
     const uint32_t begin = wg * per + min(wg, extra), end = begin + per + (wg < extra ? 1u : 0u);
     if (begin >= end) return;
     Unit u{begin, 0};
     int64_t staged_t0 = -1, staged_n0 = -1;  // the dY stage held in ys
-    UnitGeom g = geometry(u, K, M, kc, mtiles, ntiles);
+    UnitGeom g = geometry(u, K, M, kc, mtiles, ntiles, ranges);
     u32x4 buf[kLoadsPerThread];
     if (g.x_vec) load_x(X, M, g, buf);
 
@@ -176,7 +193,7 @@ __global__ __launch_bounds__(kGemmThreads) void splitk_gemm_kernel(const uint16_
         const bool more = nu.item < end;
         UnitGeom ng = g;
         if (more) {
-            ng = geometry(nu, K, M, kc, mtiles, ntiles);
+            ng = geometry(nu, K, M, kc, mtiles, ntiles, ranges);
             if (ng.x_vec) load_x(X, M, ng, buf);
         }
         const int i = lane & 31, h = lane >> 5;
@@ -232,11 +249,10 @@ __global__ __launch_bounds__(kGemmThreads) void splitk_gemm_kernel(const uint16_
 constexpr int kReduceThreads = 256;
 constexpr int kReduceDepth = 24;  // chunk sums per element < 2^24 (splits < 2^27)
 
+// out[e0 .. e0+VEC) = T(P_0, ..., P_{S-1}) at those elements (S >= 1).
 template <int VEC>
-__global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(const float* __restrict__ P, int S,
-                                                                       int64_t count, float* __restrict__ out) {
-    const int64_t e0 = ((int64_t)blockIdx.x * kReduceThreads + threadIdx.x) * VEC;
-    if (e0 >= count) return;
+__device__ __forceinline__ void reduce_splits(const float* __restrict__ P, int S, int64_t count, int64_t e0,
+                                              float* __restrict__ out) {
     float level[kReduceDepth][VEC];
     uint32_t nchunks = 0;
     for (int c0 = 0; c0 < S; c0 += 8) {
@@ -301,6 +317,99 @@ __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(const flo
     }
 }
 
+template <int VEC>
+__global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(const float* __restrict__ P, int S,
+                                                                       int64_t count, float* __restrict__ out) {
+    const int64_t e0 = ((int64_t)blockIdx.x * kReduceThreads + threadIdx.x) * VEC;
+    if (e0 >= count) return;
+    reduce_splits<VEC>(P, S, count, e0, out);
+}
+
+// Group g (blockIdx.y): out[g] = T over its slots slot_offsets[g] .. slot_offsets[g+1]-1,
+// in slot order; a group with no slot gets the zero gradient.
+template <int VEC>
+__global__ __launch_bounds__(kReduceThreads) void grouped_reduce_kernel(const float* __restrict__ P,
+                                                                        const int32_t* __restrict__ slot_offsets,
+                                                                        int64_t max_slots, int64_t count,
+                                                                        float* __restrict__ out,
+                                                                        const int32_t* __restrict__ status) {
+    if (status[kWordStatus] != 0) return;
+    const int64_t e0 = ((int64_t)blockIdx.x * kReduceThreads + threadIdx.x) * VEC;
+    if (e0 >= count) return;
+    const int64_t g = blockIdx.y;
+    const int32_t lo = slot_offsets[g], hi = slot_offsets[g + 1];
+    if (lo < 0 || hi < lo || hi > max_slots) return;  // the slot kernel never writes such a table
+    float* o = out + g * count;
+    if (hi == lo) {
+        if (VEC == 4) store16(o + e0, u32x4{0u, 0u, 0u, 0u});
+        else o[e0] = 0.f;
+        return;
+    }
+    reduce_splits<VEC>(P + (int64_t)lo * count, hi - lo, count, e0, o);
+}
+
+// The private slots of a grouped split, by one workgroup: group g owns tokens
+// [off[g], off[g+1]), cut into consecutive slots of `split` tokens from its
+// first token; slots are numbered in (group, position) order.  Writes
+// slot_offsets[0 .. G], each slot's token range, and the status block (its
+// word cleared, or set when the offsets are not non-decreasing within
+// [0, K]; the slot count in kWordSlots).
+constexpr int kSlotThreads = 1024;
+__global__ __launch_bounds__(kSlotThreads) void grouped_slots_kernel(const int32_t* __restrict__ off, int32_t G,
+                                                                     int64_t K, int32_t split, int64_t max_slots,
+                                                                     int32_t* __restrict__ slot_offsets,
+                                                                     int2* __restrict__ ranges,
+                                                                     int32_t* __restrict__ status) {
+    __shared__ int32_t wave_tot[kSlotThreads / 64];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int64_t carry = 0;
+    int bad = 0;
+    for (int32_t g0 = 0; g0 < G; g0 += kSlotThreads) {
+        const int32_t g = g0 + tid;
+        int32_t a = 0, b = 0, cnt = 0;
+        if (g < G) {
+            a = off[g];
+            b = off[g + 1];
+            if (a < 0 || b < a || (int64_t)b > K) bad = 1;
+            else cnt = (int32_t)(((uint32_t)(b - a) + (uint32_t)split - 1u) / (uint32_t)split);
+        }
+        // exclusive scan of the slot counts over the workgroup
+        int32_t incl = cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int32_t t = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += t;
+        }
+        if (lane == 63) wave_tot[w] = incl;
+        __syncthreads();
+        int32_t before = 0, total = 0;
+        for (int i = 0; i < kSlotThreads / 64; ++i) {
+            before += i < w ? wave_tot[i] : 0;
+            total += wave_tot[i];
+        }
+        __syncthreads();
+        const int64_t base = carry + before + incl - cnt;
+        if (g < G) {
+            slot_offsets[g] = (int32_t)min(base, max_slots);
+            for (int32_t c = 0; c < cnt; ++c) {
+                if (base + c >= max_slots) {
+                    bad = 1;
+                    break;
+                }
+                const int32_t t0 = a + c * split;
+                ranges[base + c] = int2{t0, min(b, t0 + split)};
+            }
+        }
+        carry += total;
+    }
+    bad = __syncthreads_or(bad);
+    if (tid == 0) {
+        slot_offsets[G] = (int32_t)min(carry, max_slots);
+        status[kWordSlots] = bad ? 0 : (int32_t)carry;
+        status[kWordStatus] = bad ? kStatusPlan : 0;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_splitk_gemm(const uint16_t* X, const uint16_t* dY, int64_t K, int64_t M, int64_t N,
@@ -314,10 +423,45 @@ hipError_t launch_splitk_gemm(const uint16_t* X, const uint16_t* dY, int64_t K, 
     if (grid > items) grid = items;
     if (atomic)
         hipLaunchKernelGGL(splitk_gemm_kernel<true>, dim3((unsigned)grid), dim3(kGemmThreads), 0, s, X, dY, K, M, N, kc,
-                           (uint32_t)items, (uint32_t)mtiles, (uint32_t)ntiles, out);
+                           (uint32_t)items, (uint32_t)mtiles, (uint32_t)ntiles, out, nullptr, nullptr);
     else
         hipLaunchKernelGGL(splitk_gemm_kernel<false>, dim3((unsigned)grid), dim3(kGemmThreads), 0, s, X, dY, K, M, N,
-                           kc, (uint32_t)items, (uint32_t)mtiles, (uint32_t)ntiles, out);
+                           kc, (uint32_t)items, (uint32_t)mtiles, (uint32_t)ntiles, out, nullptr, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped_splitk_gemm(const uint16_t* X, const uint16_t* dY, int64_t K, int64_t M, int64_t N,
+                                      const int32_t* group_offsets, int32_t num_groups, int32_t split_tokens,
+                                      int64_t max_slots, int32_t* slot_offsets, int2* ranges, int32_t* status,
+                                      float* out, hipStream_t s) {
+    hipLaunchKernelGGL(grouped_slots_kernel, dim3(1), dim3(kSlotThreads), 0, s, group_offsets, num_groups, K,
+                       split_tokens, max_slots, slot_offsets, ranges, status);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t mtiles = (M + BM - 1) / BM, ntiles = (N + BN - 1) / BN;
+    const int64_t items_bound = mtiles * ntiles * max_slots;
+    const Launch lc = launch_config();
+    int64_t grid = lc.grid_blocks > 0 ? lc.grid_blocks : (int64_t)device_cu_count() * 3;
+    if (grid > items_bound) grid = items_bound;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(splitk_gemm_kernel<false>, dim3((unsigned)grid), dim3(kGemmThreads), 0, s, X, dY, K, M, N,
+                       (int64_t)0, 0u, (uint32_t)mtiles, (uint32_t)ntiles, out, ranges, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped_reduce(const float* partials, const int32_t* slot_offsets, int64_t max_slots,
+                                 int32_t num_groups, int64_t count, float* out, const int32_t* status,
+                                 hipStream_t s) {
+    if (count == 0 || num_groups == 0) return hipSuccess;
+    const bool vec = (count % 4) == 0;
+    const int64_t threads = vec ? count / 4 : count;
+    const dim3 grid((unsigned)((threads + kReduceThreads - 1) / kReduceThreads), (unsigned)num_groups);
+    if (vec)
+        hipLaunchKernelGGL(grouped_reduce_kernel<4>, grid, dim3(kReduceThreads), 0, s, partials, slot_offsets,
+                           max_slots, count, out, status);
+    else
+        hipLaunchKernelGGL(grouped_reduce_kernel<1>, grid, dim3(kReduceThreads), 0, s, partials, slot_offsets,
+                           max_slots, count, out, status);
     return hipGetLastError();
 }
 

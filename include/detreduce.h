@@ -260,6 +260,61 @@ dr_status dr_splitk_reduce(const float* partials, int32_t splits, int64_t count,
                            hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Grouped split with private slots: per group g (an expert),
+ *   dW[g] = T over its slots s of  X_s^T dY_s   (slot order),
+ * where group g owns tokens [group_offsets[g], group_offsets[g+1]) of the
+ * expert-major X and dY and is cut into consecutive slots of split_tokens
+ * tokens from its first token (the last slot short).
+ *
+ * The Megatron Core determinism blog's grouped-GEMM weight-gradient fix, as
+ * the bitwise-determinism interview note retells it: several tiles used to
+ * accumulate into one address in the epilogue, in arrival order; instead each
+ * writer gets a private slot and the slots are merged in a fixed order.  The
+ * slot boundaries depend only on the group sizes and split_tokens, never on
+ * the grid, so every partial and every dW[g] is repeatable; a group with no
+ * tokens gets the zero gradient.
+ *
+ *   X[K, M], dY[K, N]    bf16 (bit patterns), expert-major token rows.
+ *   group_offsets[G+1]   int32, device: non-decreasing within [0, K].
+ *   partials             fp32 [partial_slots, M, N], partial_slots >=
+ *                        dr_grouped_splitk_max_slots(K, G, split_tokens);
+ *                        slot s (in group order) is written for s below the
+ *                        slot count, the rest is not touched.
+ *   slot_offsets[G+1]    int32, device, written: group g's slots are
+ *                        slot_offsets[g] .. slot_offsets[g+1]-1.
+ *   ws                   >= dr_grouped_splitk_workspace_size(), 16-byte
+ *                        aligned: the status block and the slot table.
+ * Offsets that are not non-decreasing within [0, K] set the status word
+ * (dr_workspace_status reports DR_ERR_BAD_PLAN) and nothing is computed;
+ * dr_grouped_splitk_reduce with the same ws then leaves out untouched.
+ * ---------------------------------------------------------------------- */
+int64_t dr_grouped_splitk_max_slots(int64_t K, int32_t num_groups, int32_t split_tokens);
+size_t dr_grouped_splitk_workspace_size(int64_t K, int32_t num_groups, int32_t split_tokens);
+dr_status dr_grouped_splitk_gemm_tn(const void* X, const void* dY, int64_t K, int64_t M, int64_t N,
+                                    const int32_t* group_offsets, int32_t num_groups, int32_t split_tokens,
+                                    float* partials, int64_t partial_slots, int32_t* slot_offsets, void* ws,
+                                    size_t ws_bytes, hipStream_t stream);
+/* out[g][e] = T(partials[slot_offsets[g]][e], ..., partials[slot_offsets[g+1]-1][e]), zero for a group
+ * with no slot.  out[num_groups, count] fp32, written; ws is the one the partials were made with. */
+dr_status dr_grouped_splitk_reduce(const float* partials, int64_t partial_slots, const int32_t* slot_offsets,
+                                   int32_t num_groups, int64_t count, float* out, const void* ws,
+                                   hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Dispatch-side stable permute: out[r] = rows[perm[r] / k] (bytes copied).
+ *
+ * perm is dr_sort_by_dest's permutation of the T*k (token, slot) assignments
+ * by expert, so out holds each expert's tokens contiguously in token order,
+ * the layout of the DeepSeek-V4 MoE backward (ch. 9, section 3.2: tokens
+ * sorted by (expert_id, original_token_id)).  No arithmetic: exact.
+ *   rows[num_rows, row_bytes], out[n, row_bytes]: 16-byte aligned, row_bytes
+ *   a multiple of 16.  A perm entry outside [0, num_rows * k) sets *dev_status
+ *   (when given) and its output row is not written.
+ * ---------------------------------------------------------------------- */
+dr_status dr_permute_rows(const void* rows, int64_t row_bytes, int64_t num_rows, const int32_t* perm, int64_t n,
+                          int32_t k, void* out, int32_t* dev_status, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Byte fingerprint of a tensor, for comparing runs byte for byte rather than
  * by printed values (bitwise-determinism interview note, "how to verify":
  * per-step tensor fingerprints compared byte-wise).  The definition is this

@@ -143,6 +143,49 @@ def test_sparse_attn_dk_rejects_bad_arguments(lib):
     assert call(K=0) == DR_ERR_INVALID_ARGUMENT
 
 
+def test_grouped_splitk_and_permute_reject_bad_arguments(lib):
+    lib.dr_grouped_splitk_max_slots.restype = ctypes.c_int64
+    lib.dr_grouped_splitk_max_slots.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
+    assert lib.dr_grouped_splitk_max_slots(1000, 4, 256) == 3 + 4
+    lib.dr_grouped_splitk_workspace_size.restype = ctypes.c_size_t
+    lib.dr_grouped_splitk_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]
+    need = lib.dr_grouped_splitk_workspace_size(1000, 4, 256)
+    g = lib.dr_grouped_splitk_gemm_tn
+    g.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                  ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_size_t, ctypes.c_void_p]
+    ok = dict(X=FAKE, dY=FAKE, K=1000, M=64, N=24, off=FAKE, G=4, split=256, P=FAKE, slots=7, so=FAKE, ws=FAKE,
+              wsb=need, s=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return g(*a.values())
+
+    assert call(slots=6) == DR_ERR_WORKSPACE_TOO_SMALL        # fewer partial slots than the bound
+    assert call(wsb=need - 1) == DR_ERR_WORKSPACE_TOO_SMALL
+    assert call(G=0) == DR_ERR_INVALID_ARGUMENT
+    assert call(G=65536) == DR_ERR_INVALID_ARGUMENT
+    assert call(split=0) == DR_ERR_INVALID_ARGUMENT
+    assert call(X=FAKE + 2) == DR_ERR_INVALID_ARGUMENT
+    assert call(off=None) == DR_ERR_INVALID_ARGUMENT
+    assert call(K=0) == DR_ERR_INVALID_ARGUMENT
+    r = lib.dr_grouped_splitk_reduce
+    r.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    assert r(FAKE, 7, FAKE, 0, 100, FAKE, FAKE, None) == DR_ERR_INVALID_ARGUMENT
+    assert r(FAKE + 4, 7, FAKE, 4, 100, FAKE, FAKE, None) == DR_ERR_INVALID_ARGUMENT  # 4 | count: 16-byte rows
+    assert r(FAKE, 7, FAKE, 4, 100, FAKE, None, None) == DR_ERR_INVALID_ARGUMENT
+    p = lib.dr_permute_rows
+    p.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert p(FAKE, 24, 10, FAKE, 20, 2, FAKE, None, None) == DR_ERR_INVALID_ARGUMENT      # row_bytes % 16
+    assert p(FAKE, 32, 10, FAKE, 20, 0, FAKE, None, None) == DR_ERR_INVALID_ARGUMENT      # k
+    assert p(FAKE + 8, 32, 10, FAKE, 20, 2, FAKE, None, None) == DR_ERR_INVALID_ARGUMENT  # alignment
+    assert p(FAKE, 32, 10, None, 20, 2, FAKE, None, None) == DR_ERR_INVALID_ARGUMENT
+    assert p(None, 32, 10, None, 0, 2, None, None, None) == DR_OK                         # nothing to do
+
+
 def test_sort_rejects_bad_arguments(lib):
     f = lib.dr_sort_by_dest
     f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,

@@ -256,6 +256,92 @@ def test_splitk_matches_oracle(dr, K, M, N, splits):
     assert np.all(np.abs(host(dW) - exact) <= 1e-4 * A + 1e-30)
 
 
+# ---------------------------------------------------------------------------
+# grouped split with private slots; the dispatch permute
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("K,M,N,offsets,split", [
+    (2000, 136, 24, [0, 0, 700, 701, 1999, 2000], 256),   # empty, one-token and multi-stage slots
+    (1000, 64, 40, list(range(0, 1001, 50)), 37),          # many groups, two N tiles, ragged slots
+    (600, 72, 20, [0, 600], 600),                           # one group, one slot, scalar dY staging
+    (900, 128, 24, [100, 300, 300, 800], 128),             # tokens outside every group are ignored
+])
+def test_grouped_splitk_matches_oracle(dr, K, M, N, offsets, split):
+    say(f"grouped splitk K={K} M={M} N={N} groups={len(offsets) - 1} split={split}")
+    inp = workloads.splitk_inputs(K + M + split, K, M, N, 1)
+    X, dY = dev_bf16(inp.X), dev_bf16(inp.dY)
+    off = np.array(offsets, np.int32)
+    P, so, ws = dr.dr_grouped_splitk_gemm_tn(X, dY, dev(off), split)
+    dr.dr_workspace_status(ws)
+    want_so, ranges = oracle.grouped_slots(off, split)
+    assert np.array_equal(host(so), want_so)
+    S = int(want_so[-1])
+    Ph = host(P)[:S]
+    exact = oracle.grouped_splitk_partials(inp.X, inp.dY, off, split)
+    for s_, (a, b) in enumerate(ranges):
+        _, A = oracle.splitk_reference(inp.X[a:b], inp.dY[a:b])
+        assert np.all(np.abs(Ph[s_] - exact[s_]) <= 1e-4 * A + 1e-30), s_
+    dW = dr.dr_grouped_splitk_reduce(P, so, ws)
+    # reduce stage: bit-exact against the oracle's per-group tree over the same partials
+    assert_bits_equal(host(dW), oracle.grouped_splitk_reduce(Ph, want_so), "grouped reduce")
+    for g in range(len(offsets) - 1):
+        e, A = oracle.splitk_reference(inp.X[off[g]:off[g + 1]], inp.dY[off[g]:off[g + 1]])
+        assert np.all(np.abs(host(dW)[g] - e) <= 1e-4 * A + 1e-30), g
+
+
+def test_grouped_splitk_grid_invariance_and_bad_offsets(dr):
+    inp = workloads.splitk_inputs(91, 1500, 200, 24, 1)
+    X, dY = dev_bf16(inp.X), dev_bf16(inp.dY)
+    off = dev(np.array([0, 10, 10, 900, 1500], np.int32))
+    ref = None
+    for grid in (0, 1, 7, 1000):
+        dr.dr_set_launch_params(grid_blocks=grid)
+        try:
+            P, so, ws = dr.dr_grouped_splitk_gemm_tn(X, dY, off, 100)
+            S = int(host(so)[-1])
+            got = host(dr.dr_grouped_splitk_reduce(P, so, ws)), host(P)[:S]
+        finally:
+            dr.dr_set_launch_params(reset=True)
+        if ref is None:
+            ref = got
+        assert_bits_equal(got[0], ref[0], f"grid {grid}")
+        assert_bits_equal(got[1], ref[1], f"grid {grid} partials")
+    # offsets that run backwards or past K are refused, and out is left alone
+    for bad in ([0, 10, 5, 1500], [0, 10, 900, 1501], [-1, 10, 900, 1500]):
+        P, so, ws = dr.dr_grouped_splitk_gemm_tn(X, dY, dev(np.array(bad, np.int32)), 100)
+        with pytest.raises(dr.DetReduceError) as e:
+            dr.dr_workspace_status(ws)
+        assert e.value.status == 6, bad
+        out = torch.full((3, 200, 24), 7.0, device="cuda")
+        dr.dr_grouped_splitk_reduce(P, so, ws, out=out)
+        assert bool((out == 7.0).all()), bad
+
+
+@pytest.mark.parametrize("T,E,k,H,dtype", [(300, 16, 4, 256, "bf16"), (1000, 64, 8, 7168, "bf16"),
+                                            (77, 5, 1, 36, "f32")])
+def test_permute_rows_matches_oracle(dr, T, E, k, H, dtype):
+    say(f"permute T={T} E={E} k={k} H={H}")
+    inp = workloads.moe_inputs(T + E + k, T, E, k, H, dtype, zipf_bias_s=1.2)
+    rows = workloads.normal_f32(T, 3, T * H).reshape(T, H)
+    x = dev_bf16(workloads.bf16_bits(rows)) if dtype == "bf16" else dev(rows)
+    perm, _, _ = dr.dr_sort_by_dest(dev(inp.expert_ids.reshape(-1)), E)
+    out = dr.dr_permute_rows(x, perm, k)
+    want = oracle.permute_rows(host(x.view(torch.int16) if dtype == "bf16" else x), host(perm), k)
+    got = host(out.view(torch.int16) if dtype == "bf16" else out)
+    assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
+
+
+def test_permute_rows_bad_entry(dr):
+    x = dev(np.arange(40, dtype=np.float32).reshape(10, 4))
+    perm = dev(np.array([0, 3, 25, 7], np.int32))  # 25 // 2 = 12 is not a row
+    out = torch.full((4, 4), -1.0, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dr.dr_permute_rows(x, perm, 2, out=out, dev_status=status)
+    with pytest.raises(dr.DetReduceError):
+        dr.dr_read_status(status)
+    o = host(out)
+    assert (o[2] == -1.0).all() and o[1].tolist() == [4.0, 5.0, 6.0, 7.0]
+
+
 def test_splitk_reduce_ragged_counts(dr):
     for S, count in [(1, 5), (3, 7), (64, 172032), (100, 1001), (9, 4)]:
         say(f"splitk_reduce S={S} count={count}")
