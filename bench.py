@@ -174,6 +174,22 @@ def bench_moe(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
         fps.add(int(fp.item()))
     assert len(fps) == 1, "combine step output changed between replays"
 
+    # the forward's dispatch-side permute of the same routing: token rows copied to expert-major order
+    x = rows[:T]
+    out_p = torch.empty(n, H, dtype=rows.dtype, device="cuda")
+    for _ in range(warmup):
+        dr.dr_permute_rows(x, perm, k, inv_perm=inv, out=out_p)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        dr.dr_permute_rows(x, perm, k, inv_perm=inv, out=out_p)
+    e1.record()
+    torch.cuda.synchronize()
+    perm_ms = e0.elapsed_time(e1) / steps
+    perm_bytes = T * H * elem + n * 4 + n * H * elem  # each token row read once at least, every copy written
+    del out_p
+
     comb_ms = phases["combine_fingerprinted"]
     achieved = combine_bytes / (comb_ms * 1e-3) / 1e9
     from bench_workloads import measured_traffic, source_digest
@@ -201,6 +217,8 @@ def bench_moe(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
             "overhead_vs_atomic_kernel_only": round(comb_ms / aph["combine_atomic"] - 1, 4),
         },
         "wall_ms_per_step": round(wall_ms, 4),
+        "dispatch_permute": {"ms": round(perm_ms, 4), "algorithmic_bytes": perm_bytes,
+                             "achieved_gbs": round(perm_bytes / (perm_ms * 1e-3) / 1e9, 1)},
     }
     if want_cpu:
         result["cpu_baseline"] = cpu_baseline_moe(oracle, inp, cpu_seconds)

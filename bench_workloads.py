@@ -255,6 +255,21 @@ def _splitk(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
     for _ in range(warmup):
         dr.dr_splitk_gemm_tn(X, dY, 1, partials=p1)
     ms_nosplit = _timed(torch, steps, lambda: dr.dr_splitk_gemm_tn(X, dY, 1, partials=p1))
+    # the grouped form of the same contraction: 16 unequal groups (expert-like sizes), slots of 256 tokens
+    sizes = np.array([int(K * w) for w in np.linspace(2.0, 0.05, 16) / np.linspace(2.0, 0.05, 16).sum()])
+    sizes[0] += K - sizes.sum()
+    offs = torch.from_numpy(np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)).cuda()
+    Pg, so, wsg = dr.dr_grouped_splitk_gemm_tn(X, dY, offs, 256)
+    dWg = dr.dr_grouped_splitk_reduce(Pg, so, wsg)
+
+    def grouped():
+        dr.dr_grouped_splitk_gemm_tn(X, dY, offs, 256, partials=Pg, slot_offsets=so, ws=wsg)
+        dr.dr_grouped_splitk_reduce(Pg, so, wsg, out=dWg)
+
+    for _ in range(warmup):
+        grouped()
+    ms_grouped = _timed(torch, steps, grouped)
+    dr.dr_workspace_status(wsg)
     g_ms = ph["splitk_gemm"]
     achieved = gemm_bytes / (g_ms * 1e-3) / 1e9
     det_ms = ph["splitk_gemm"] + ph["splitk_reduce"]
@@ -275,6 +290,7 @@ def _splitk(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
         "overhead_vs_atomic": {"deterministic_ms": round(det_ms, 4), "atomic_zero_plus_gemm_ms": round(at_ms, 4),
                                "overhead": round(det_ms / at_ms - 1, 4)},
         "no_split_ms": round(ms_nosplit, 4),
+        "grouped_16_groups_ms": round(ms_grouped, 4),
     }
     if want_cpu:
         t0 = time.perf_counter()

@@ -72,7 +72,7 @@ def _load() -> ctypes.CDLL:
         "dr_grouped_splitk_workspace_size": ([i64, i32, i32], sz),
         "dr_grouped_splitk_gemm_tn": ([vp, vp, i64, i64, i64, vp, i32, i32, vp, i64, vp, vp, sz, vp], ctypes.c_int),
         "dr_grouped_splitk_reduce": ([vp, i64, vp, i32, i64, vp, vp, vp], ctypes.c_int),
-        "dr_permute_rows": ([vp, i64, i64, vp, i64, i32, vp, vp, vp], ctypes.c_int),
+        "dr_permute_rows": ([vp, i64, i64, vp, vp, i64, i32, vp, vp, vp], ctypes.c_int),
         "dr_fingerprint_workspace_size": ([i64], sz),
         "dr_fingerprint": ([vp, i64, vp, vp, sz, vp], ctypes.c_int),
         "dr_workspace_status": ([vp, vp], ctypes.c_int),
@@ -351,16 +351,17 @@ def dr_grouped_splitk_reduce(partials, slot_offsets, ws, *, out=None, stream=Non
     return out
 
 
-def dr_permute_rows(rows, perm, k: int, *, out=None, dev_status=None, stream=None):
-    """out[r] = rows[perm[r] // k] (the expert-major copy of the token rows)."""
+def dr_permute_rows(rows, perm, k: int, *, inv_perm=None, out=None, dev_status=None, stream=None):
+    """out[r] = rows[perm[r] // k] (the expert-major copy of the token rows); with inv_perm the copies
+    run in token order."""
     _dev(perm, "perm", (torch.int32,))
     if rows.device.type != "cuda" or not rows.is_contiguous():
         raise ValueError("rows must be a contiguous CUDA tensor")
     n = perm.numel()
     row_bytes = rows[0].numel() * rows.element_size() if rows.shape[0] else 0
     out = out if out is not None else torch.empty((n,) + tuple(rows.shape[1:]), dtype=rows.dtype, device=rows.device)
-    _check(lib.dr_permute_rows(_p(rows), row_bytes, rows.shape[0], _p(perm), n, k, _p(out), _p(dev_status),
-                               _stream(stream)), "dr_permute_rows")
+    _check(lib.dr_permute_rows(_p(rows), row_bytes, rows.shape[0], _p(perm), _p(inv_perm), n, k, _p(out),
+                               _p(dev_status), _stream(stream)), "dr_permute_rows")
     return out
 
 

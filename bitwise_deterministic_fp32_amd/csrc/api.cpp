@@ -659,18 +659,19 @@ dr_status dr_grouped_splitk_reduce(const float* partials, int64_t partial_slots,
 }
 
 // ---------------------------------------------------------------------------
-dr_status dr_permute_rows(const void* rows, int64_t row_bytes, int64_t num_rows, const int32_t* perm, int64_t n,
-                          int32_t k, void* out, int32_t* dev_status, hipStream_t stream) {
+dr_status dr_permute_rows(const void* rows, int64_t row_bytes, int64_t num_rows, const int32_t* perm,
+                          const int32_t* inv_perm, int64_t n, int32_t k, void* out, int32_t* dev_status,
+                          hipStream_t stream) {
     const char* what = "dr_permute_rows";
     if (n < 0 || n >= kMaxN || num_rows < 0 || k < 1)
         return fail(DR_ERR_INVALID_ARGUMENT, "%s: need 0 <= n < 2^31, num_rows >= 0, k >= 1", what);
     if (row_bytes < 16 || row_bytes % 16 != 0)
         return fail(DR_ERR_INVALID_ARGUMENT, "%s: row_bytes must be a positive multiple of 16", what);
     if (n > 0 && (!rows || !perm || !out)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: null pointer", what);
-    if (n > 0 && (!aligned(rows, 16) || !aligned(out, 16) || !aligned(perm, 4)))
+    if (n > 0 && (!aligned(rows, 16) || !aligned(out, 16) || !aligned(perm, 4) || !aligned(inv_perm, 4)))
         return fail(DR_ERR_INVALID_ARGUMENT, "%s: rows and out must be 16-byte aligned", what);
     if (dev_status && !aligned(dev_status, 4)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: misaligned dev_status", what);
-    DR_TRY_HIP(dr::launch_permute_rows(rows, row_bytes, num_rows, perm, n, k, out, dev_status, stream),
+    DR_TRY_HIP(dr::launch_permute_rows(rows, row_bytes, num_rows, perm, inv_perm, n, k, out, dev_status, stream),
                "permute launch");
     return ok();
 }

@@ -143,9 +143,10 @@ hipError_t launch_grouped_splitk_gemm(const uint16_t* X, const uint16_t* dY, int
 hipError_t launch_grouped_reduce(const float* partials, const int32_t* slot_offsets, int64_t max_slots,
                                  int32_t num_groups, int64_t count, float* out, const int32_t* status,
                                  hipStream_t s);
-// dispatch-side permute: out[r] = rows[perm[r] / k]
+// dispatch-side permute: out[r] = rows[perm[r] / k]; with inv_perm the work runs in token order
 hipError_t launch_permute_rows(const void* rows, int64_t row_bytes, int64_t num_rows, const int32_t* perm,
-                               int64_t n, int32_t k, void* out, int32_t* dev_status, hipStream_t s);
+                               const int32_t* inv_perm, int64_t n, int32_t k, void* out, int32_t* dev_status,
+                               hipStream_t s);
 // fingerprint
 // most workgroups (and partials) of a fingerprint launch: 8 per SIMD of a
 // 256-CU device, enough wavefronts to hide the loads behind the hashing

@@ -10,8 +10,12 @@
 // grouped weight gradient independent of the expert-parallel layout.
 //
 // One wavefront copies one output row in 16-byte pieces (four in flight per
-// lane).  A token row is read k times, so the loads go through the cache;
-// the output is written once with streaming stores.
+// lane); the output is written once, with streaming stores.  A token row is
+// read k times.  Given the sort's inverse permutation, wavefront w takes
+// output row inv[w] (w = t*k + j in token order), so the k copies of a token
+// are made by neighbouring wavefronts and its row is read from cache rather
+// than from HBM k times; the wavefront checks perm[inv[w]] == w, so every
+// output row is still the one perm assigns and is written once.
 #include "internal.h"
 
 namespace dr {
@@ -22,13 +26,20 @@ constexpr int kWaves = kThreads / 64;
 
 __global__ __launch_bounds__(kThreads) void permute_rows_kernel(const unsigned char* __restrict__ rows,
                                                                 int64_t row_bytes, int64_t num_rows,
-                                                                const int32_t* __restrict__ perm, int64_t n,
+                                                                const int32_t* __restrict__ perm,
+                                                                const int32_t* __restrict__ inv, int64_t n,
                                                                 uint32_t k, unsigned char* __restrict__ out,
                                                                 int32_t* dev_status) {
-    const int64_t r = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (r >= n) return;  // whole wavefront
+    const int64_t w = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (w >= n) return;  // whole wavefront
     const int lane = threadIdx.x & 63;
-    const int32_t p = perm[r];
+    int64_t r = w;
+    bool ok = true;
+    if (inv) {
+        r = inv[w];
+        ok = r >= 0 && r < n && perm[r] == (int32_t)w;
+    }
+    const int32_t p = ok ? perm[r] : -1;
     const int64_t src = p >= 0 ? (int64_t)((uint32_t)p / k) : -1;  // 32-bit division
     if (src < 0 || src >= num_rows) {
         // fail closed: the row is not written
@@ -56,11 +67,13 @@ __global__ __launch_bounds__(kThreads) void permute_rows_kernel(const unsigned c
 }  // namespace
 
 hipError_t launch_permute_rows(const void* rows, int64_t row_bytes, int64_t num_rows, const int32_t* perm,
-                               int64_t n, int32_t k, void* out, int32_t* dev_status, hipStream_t s) {
+                               const int32_t* inv_perm, int64_t n, int32_t k, void* out, int32_t* dev_status,
+                               hipStream_t s) {
     if (n == 0) return hipSuccess;
     const dim3 grid((unsigned)((n + kWaves - 1) / kWaves));
     hipLaunchKernelGGL(permute_rows_kernel, grid, dim3(kThreads), 0, s, static_cast<const unsigned char*>(rows),
-                       row_bytes, num_rows, perm, n, (uint32_t)k, static_cast<unsigned char*>(out), dev_status);
+                       row_bytes, num_rows, perm, inv_perm, n, (uint32_t)k, static_cast<unsigned char*>(out),
+                       dev_status);
     return hipGetLastError();
 }
 

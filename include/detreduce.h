@@ -308,11 +308,17 @@ dr_status dr_grouped_splitk_reduce(const float* partials, int64_t partial_slots,
  * the layout of the DeepSeek-V4 MoE backward (ch. 9, section 3.2: tokens
  * sorted by (expert_id, original_token_id)).  No arithmetic: exact.
  *   rows[num_rows, row_bytes], out[n, row_bytes]: 16-byte aligned, row_bytes
- *   a multiple of 16.  A perm entry outside [0, num_rows * k) sets *dev_status
- *   (when given) and its output row is not written.
+ *   a multiple of 16.
+ *   inv_perm  optional (NULL: the work runs in output order): the sort's
+ *             inverse permutation.  Then the copies run in token order and a
+ *             token row is read from HBM about once instead of k times; each
+ *             output row is still the one perm assigns, written once.
+ * A perm entry outside [0, num_rows * k), or an inv_perm entry that perm does
+ * not invert, sets *dev_status (when given) and that output row is not written.
  * ---------------------------------------------------------------------- */
-dr_status dr_permute_rows(const void* rows, int64_t row_bytes, int64_t num_rows, const int32_t* perm, int64_t n,
-                          int32_t k, void* out, int32_t* dev_status, hipStream_t stream);
+dr_status dr_permute_rows(const void* rows, int64_t row_bytes, int64_t num_rows, const int32_t* perm,
+                          const int32_t* inv_perm, int64_t n, int32_t k, void* out, int32_t* dev_status,
+                          hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Byte fingerprint of a tensor, for comparing runs byte for byte rather than

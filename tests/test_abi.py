@@ -177,13 +177,14 @@ def test_grouped_splitk_and_permute_reject_bad_arguments(lib):
     assert r(FAKE + 4, 7, FAKE, 4, 100, FAKE, FAKE, None) == DR_ERR_INVALID_ARGUMENT  # 4 | count: 16-byte rows
     assert r(FAKE, 7, FAKE, 4, 100, FAKE, None, None) == DR_ERR_INVALID_ARGUMENT
     p = lib.dr_permute_rows
-    p.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
-                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
-    assert p(FAKE, 24, 10, FAKE, 20, 2, FAKE, None, None) == DR_ERR_INVALID_ARGUMENT      # row_bytes % 16
-    assert p(FAKE, 32, 10, FAKE, 20, 0, FAKE, None, None) == DR_ERR_INVALID_ARGUMENT      # k
-    assert p(FAKE + 8, 32, 10, FAKE, 20, 2, FAKE, None, None) == DR_ERR_INVALID_ARGUMENT  # alignment
-    assert p(FAKE, 32, 10, None, 20, 2, FAKE, None, None) == DR_ERR_INVALID_ARGUMENT
-    assert p(None, 32, 10, None, 0, 2, None, None, None) == DR_OK                         # nothing to do
+    p.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    assert p(FAKE, 24, 10, FAKE, None, 20, 2, FAKE, None, None) == DR_ERR_INVALID_ARGUMENT      # row_bytes % 16
+    assert p(FAKE, 32, 10, FAKE, None, 20, 0, FAKE, None, None) == DR_ERR_INVALID_ARGUMENT      # k
+    assert p(FAKE + 8, 32, 10, FAKE, None, 20, 2, FAKE, None, None) == DR_ERR_INVALID_ARGUMENT  # alignment
+    assert p(FAKE, 32, 10, FAKE, FAKE + 2, 20, 2, FAKE, None, None) == DR_ERR_INVALID_ARGUMENT  # alignment
+    assert p(FAKE, 32, 10, None, None, 20, 2, FAKE, None, None) == DR_ERR_INVALID_ARGUMENT
+    assert p(None, 32, 10, None, None, 0, 2, None, None, None) == DR_OK                         # nothing to do
 
 
 def test_sort_rejects_bad_arguments(lib):

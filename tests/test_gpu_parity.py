@@ -323,11 +323,12 @@ def test_permute_rows_matches_oracle(dr, T, E, k, H, dtype):
     inp = workloads.moe_inputs(T + E + k, T, E, k, H, dtype, zipf_bias_s=1.2)
     rows = workloads.normal_f32(T, 3, T * H).reshape(T, H)
     x = dev_bf16(workloads.bf16_bits(rows)) if dtype == "bf16" else dev(rows)
-    perm, _, _ = dr.dr_sort_by_dest(dev(inp.expert_ids.reshape(-1)), E)
-    out = dr.dr_permute_rows(x, perm, k)
+    perm, _, inv = dr.dr_sort_by_dest(dev(inp.expert_ids.reshape(-1)), E)
     want = oracle.permute_rows(host(x.view(torch.int16) if dtype == "bf16" else x), host(perm), k)
-    got = host(out.view(torch.int16) if dtype == "bf16" else out)
-    assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
+    for inv_perm in (None, inv):  # output order, token order
+        out = dr.dr_permute_rows(x, perm, k, inv_perm=inv_perm)
+        got = host(out.view(torch.int16) if dtype == "bf16" else out)
+        assert np.array_equal(got.view(np.uint8), want.view(np.uint8))
 
 
 def test_permute_rows_bad_entry(dr):
@@ -340,6 +341,17 @@ def test_permute_rows_bad_entry(dr):
         dr.dr_read_status(status)
     o = host(out)
     assert (o[2] == -1.0).all() and o[1].tolist() == [4.0, 5.0, 6.0, 7.0]
+    # an inverse that perm does not invert: those rows are refused, the rest are copied
+    perm = dev(np.array([1, 0, 3, 2], np.int32))
+    inv = dev(np.array([1, 0, 3, 3], np.int32))   # w = 3 claims row 3, which perm gives to w = 2; row 2 is left
+    out = torch.full((4, 4), -1.0, device="cuda")
+    status.zero_()
+    dr.dr_permute_rows(x, perm, 2, inv_perm=inv, out=out, dev_status=status)
+    with pytest.raises(dr.DetReduceError):
+        dr.dr_read_status(status)
+    o = host(out)
+    assert o[0].tolist() == [0.0, 1.0, 2.0, 3.0] and o[1].tolist() == [0.0, 1.0, 2.0, 3.0]
+    assert o[3].tolist() == [4.0, 5.0, 6.0, 7.0] and (o[2] == -1.0).all()
 
 
 def test_splitk_reduce_ragged_counts(dr):
