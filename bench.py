@@ -174,6 +174,11 @@ def bench_moe(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
         fps.add(int(fp.item()))
     assert len(fps) == 1, "combine step output changed between replays"
 
+    from bench_workloads import cold_ms, cold_roofline
+    ms_cold = cold_ms(torch, step)
+    comb_cold = cold_ms(torch, lambda: dr.dr_combine_fingerprinted(rows, row_of, gates, out=out, out_hash=fp,
+                                                                   ws=ws_cfp))
+
     # the forward's dispatch-side permute of the same routing: token rows copied to expert-major order
     x = rows[:T]
     out_p = torch.empty(n, H, dtype=rows.dtype, device="cuda")
@@ -206,7 +211,8 @@ def bench_moe(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
                      "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("combine_kernel_fp", name, digest),
-                     "algorithmic_bytes_per_launch": combine_bytes, "avg_launch_ms": round(comb_ms, 4)},
+                     "algorithmic_bytes_per_launch": combine_bytes, "avg_launch_ms": round(comb_ms, 4),
+                     **cold_roofline(combine_bytes, comb_cold)},
         "phases_ms": {k2: round(v, 4) for k2, v in phases.items()},
         "unfused_ms": {k2: round(v, 4) for k2, v in plain.items()},
         "overhead_vs_atomic": {
@@ -217,6 +223,7 @@ def bench_moe(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
             "overhead_vs_atomic_kernel_only": round(comb_ms / aph["combine_atomic"] - 1, 4),
         },
         "wall_ms_per_step": round(wall_ms, 4),
+        "cold_cache_ms_per_step": round(ms_cold, 4),
         "dispatch_permute": {"ms": round(perm_ms, 4), "algorithmic_bytes": perm_bytes,
                              "achieved_gbs": round(perm_bytes / (perm_ms * 1e-3) / 1e9, 1)},
     }

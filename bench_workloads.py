@@ -75,6 +75,34 @@ def _timed(torch, steps, fn):
     return start.elapsed_time(stop) / steps
 
 
+def cold_ms(torch, fn, reps: int = 10, flush_mib: int = 1024) -> float:
+    """Median time of one call with the caches cold: before each call an
+    untimed read of 1 GiB (four times the 256 MB Infinity Cache) evicts L2
+    and the Infinity Cache.  A read leaves no dirty lines behind, so nothing
+    is written back during the timed call."""
+    buf = torch.zeros(flush_mib << 18, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ts = []
+    for _ in range(reps):
+        buf.sum()
+        torch.cuda.synchronize()
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del buf
+    return float(sorted(ts)[len(ts) // 2])
+
+
+def cold_roofline(alg_bytes: int, ms: float) -> dict:
+    """The roofline figures of one launch with cold caches."""
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    return {"cold_cache_launch_ms": round(ms, 4), "achieved_cold_cache": round(gbs, 1),
+            "frac_cold_cache": round(gbs / HBM_PEAK_GBS, 4)}
+
+
 def run(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
     if name in ("sparse_attn_dk", "embedding_grad"):
         return _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu)
@@ -113,6 +141,7 @@ def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
     _log(f"{name}: timing {steps} steps")
     ms_step = _timed(torch, steps, lambda: step(timer.step()))
     ph = timer.mean_ms()
+    ms_cold = cold_ms(torch, step)
 
     # reused plan: sort once, then only the plan + ordered reduction each step
     perm, seg, _ = dr.dr_sort_by_dest(index, D, want_inv=False)
@@ -130,6 +159,7 @@ def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
 
     fused = _fused_dk(torch, dr, steps, warmup) if name == "sparse_attn_dk" else None
     det_ms = ph["index_add"]
+    ia_cold = cold_ms(torch, lambda: dr.dr_index_add(out, src, index, ws=ws))
     achieved = red_bytes / (det_ms * 1e-3) / 1e9
     res = {
         "ms_per_step": ms_step,
@@ -144,8 +174,10 @@ def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("dr_index_add", name,
                                                  source_digest("sort.hip", "segreduce.hip", "internal.h", "device.h")),
-                     "algorithmic_bytes_per_launch": red_bytes, "avg_launch_ms": round(det_ms, 4)},
+                     "algorithmic_bytes_per_launch": red_bytes, "avg_launch_ms": round(det_ms, 4),
+                     **cold_roofline(red_bytes, ia_cold)},
         "phases_ms": {k: round(v, 4) for k, v in ph.items()},
+        "cold_cache_ms_per_step": round(ms_cold, 4),
         "reused_plan_ms": round(ms_plan, 4), "sort_only_ms": round(ms_sort, 4),
         "overhead_vs_atomic": {"deterministic_ms": round(det_ms, 4), "atomic_ms": round(ms_atomic, 4),
                                "overhead": round(det_ms / ms_atomic - 1, 4),
@@ -235,6 +267,7 @@ def _splitk(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
     _log(f"{name}: timing {steps} steps")
     ms_step = _timed(torch, steps, lambda: step(timer.step()))
     ph = timer.mean_ms()
+    ms_cold = cold_ms(torch, step)
     dW_a = torch.empty_like(dW)
     atimer = _Timer(torch, ["zero", "splitk_gemm_atomic"])
 
@@ -271,6 +304,7 @@ def _splitk(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
     ms_grouped = _timed(torch, steps, grouped)
     dr.dr_workspace_status(wsg)
     g_ms = ph["splitk_gemm"]
+    g_cold = cold_ms(torch, lambda: dr.dr_splitk_gemm_tn(X, dY, S, partials=partials))
     achieved = gemm_bytes / (g_ms * 1e-3) / 1e9
     det_ms = ph["splitk_gemm"] + ph["splitk_reduce"]
     at_ms = aph["zero"] + aph["splitk_gemm_atomic"]
@@ -284,11 +318,13 @@ def _splitk(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("splitk_gemm_kernel", name, source_digest("splitk.hip", "device.h")),
                      "algorithmic_bytes_per_launch": gemm_bytes, "avg_launch_ms": round(g_ms, 4),
+                     **cold_roofline(gemm_bytes, g_cold),
                      "mfma_tflops": round(flops / (g_ms * 1e-3) / 1e12, 2),
                      "mfma_frac_of_bf16_peak": round(flops / (g_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 5)},
         "phases_ms": {k: round(v, 4) for k, v in ph.items()},
         "overhead_vs_atomic": {"deterministic_ms": round(det_ms, 4), "atomic_zero_plus_gemm_ms": round(at_ms, 4),
                                "overhead": round(det_ms / at_ms - 1, 4)},
+        "cold_cache_ms_per_step": round(ms_cold, 4),
         "no_split_ms": round(ms_nosplit, 4),
         "grouped_16_groups_ms": round(ms_grouped, 4),
     }
