@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--workload", default="moe_combine",
                     choices=["moe_combine", "tiny_moe_combine", "sparse_attn_dk", "embedding_grad", "splitk_mhc"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time the step alone: no comparison legs (atomic, unfused, cold cache, extra entry points) "
+                         "and no copy ceiling, so that a profiler's trace holds only the step's kernels")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target duration of the CPU oracle sample")
     ap.add_argument("--json-out", default=None, help="also append the JSON line to this file")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -79,7 +82,7 @@ class Timer:
 
 
 # ---------------------------------------------------------------------------
-def bench_moe(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
+def bench_moe(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only=False):
     import oracle
     import workloads
     log(f"{name}: generating inputs")
@@ -137,37 +140,6 @@ def bench_moe(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
     phases = timer.mean_ms()
     fps.add(int(fp.item()))
 
-    # the same combine without the fused fingerprint, and the separate fingerprint pass
-    ws_fp = torch.empty(dr.dr_fingerprint_workspace_size(out.numel() * 4), dtype=torch.uint8, device="cuda")
-    ptimer = Timer(torch, ["combine", "fingerprint"])
-    for i in range(warmup + steps):
-        evs = ptimer.step() if i >= warmup else None
-        if evs: evs[0].record()
-        dr.dr_combine(rows, row_of, gates, out=out)
-        if evs: evs[1].record()
-        dr.dr_fingerprint(out, out=fp, ws=ws_fp)
-        if evs: evs[2].record()
-    plain = ptimer.mean_ms()
-    fps.add(int(fp.item()))
-
-    # atomic baseline: zeroing (scatter_add_ needs a zeroed output) + atomic combine
-    atimer = Timer(torch, ["zero", "combine_atomic"])
-    out_a = torch.empty_like(out)
-
-    def atomic_step(evs=None):
-        if evs: evs[0].record()
-        out_a.zero_()
-        if evs: evs[1].record()
-        dr.dr_combine_atomic(rows, row_of, gates, out=out_a)
-        if evs: evs[2].record()
-
-    for _ in range(warmup):
-        atomic_step()
-    for _ in range(steps):
-        atomic_step(atimer.step())
-    aph = atimer.mean_ms()
-    torch.testing.assert_close(out_a, out, rtol=1e-5, atol=1e-5)
-
     # the step's output is the same every replay
     for _ in range(2):
         step()
@@ -175,25 +147,74 @@ def bench_moe(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
     assert len(fps) == 1, "combine step output changed between replays"
 
     from bench_workloads import cold_ms, cold_roofline
-    ms_cold = cold_ms(torch, step)
-    comb_cold = cold_ms(torch, lambda: dr.dr_combine_fingerprinted(rows, row_of, gates, out=out, out_hash=fp,
-                                                                   ws=ws_cfp))
+    extras, extra_roofline = {}, {}
+    if not step_only:
+        # the same combine without the fused fingerprint, and the separate fingerprint pass
+        ws_fp = torch.empty(dr.dr_fingerprint_workspace_size(out.numel() * 4), dtype=torch.uint8, device="cuda")
+        ptimer = Timer(torch, ["combine", "fingerprint"])
+        for i in range(warmup + steps):
+            evs = ptimer.step() if i >= warmup else None
+            if evs: evs[0].record()
+            dr.dr_combine(rows, row_of, gates, out=out)
+            if evs: evs[1].record()
+            dr.dr_fingerprint(out, out=fp, ws=ws_fp)
+            if evs: evs[2].record()
+        plain = ptimer.mean_ms()
+        fps.add(int(fp.item()))
 
-    # the forward's dispatch-side permute of the same routing: token rows copied to expert-major order
-    x = rows[:T]
-    out_p = torch.empty(n, H, dtype=rows.dtype, device="cuda")
-    for _ in range(warmup):
-        dr.dr_permute_rows(x, perm, k, inv_perm=inv, out=out_p)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(steps):
-        dr.dr_permute_rows(x, perm, k, inv_perm=inv, out=out_p)
-    e1.record()
-    torch.cuda.synchronize()
-    perm_ms = e0.elapsed_time(e1) / steps
-    perm_bytes = T * H * elem + n * 4 + n * H * elem  # each token row read once at least, every copy written
-    del out_p
+        # atomic baseline: zeroing (scatter_add_ needs a zeroed output) + atomic combine
+        atimer = Timer(torch, ["zero", "combine_atomic"])
+        out_a = torch.empty_like(out)
+
+        def atomic_step(evs=None):
+            if evs: evs[0].record()
+            out_a.zero_()
+            if evs: evs[1].record()
+            dr.dr_combine_atomic(rows, row_of, gates, out=out_a)
+            if evs: evs[2].record()
+
+        for _ in range(warmup):
+            atomic_step()
+        for _ in range(steps):
+            atomic_step(atimer.step())
+        aph = atimer.mean_ms()
+        torch.testing.assert_close(out_a, out, rtol=1e-5, atol=1e-5)
+        assert len(fps) == 1, "the unfused combine and fingerprint differ from the fused step"
+
+        ms_cold = cold_ms(torch, step)
+        comb_cold = cold_ms(torch, lambda: dr.dr_combine_fingerprinted(rows, row_of, gates, out=out, out_hash=fp,
+                                                                       ws=ws_cfp))
+
+        # the forward's dispatch-side permute of the same routing: token rows copied to expert-major order
+        x = rows[:T]
+        out_p = torch.empty(n, H, dtype=rows.dtype, device="cuda")
+        for _ in range(warmup):
+            dr.dr_permute_rows(x, perm, k, inv_perm=inv, out=out_p)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            dr.dr_permute_rows(x, perm, k, inv_perm=inv, out=out_p)
+        e1.record()
+        torch.cuda.synchronize()
+        perm_ms = e0.elapsed_time(e1) / steps
+        perm_bytes = T * H * elem + n * 4 + n * H * elem  # each token row read once at least, every copy written
+        del out_p
+        extras = {
+            "unfused_ms": {k2: round(v, 4) for k2, v in plain.items()},
+            "overhead_vs_atomic": {
+                "deterministic_combine_ms": round(phases["combine_fingerprinted"], 4),
+                "atomic_zero_plus_combine_ms": round(aph["zero"] + aph["combine_atomic"], 4),
+                "atomic_combine_only_ms": round(aph["combine_atomic"], 4),
+                "overhead": round(phases["combine_fingerprinted"] / (aph["zero"] + aph["combine_atomic"]) - 1, 4),
+                "overhead_vs_atomic_kernel_only": round(phases["combine_fingerprinted"] / aph["combine_atomic"] - 1,
+                                                        4),
+            },
+            "cold_cache_ms_per_step": round(ms_cold, 4),
+            "dispatch_permute": {"ms": round(perm_ms, 4), "algorithmic_bytes": perm_bytes,
+                                 "achieved_gbs": round(perm_bytes / (perm_ms * 1e-3) / 1e9, 1)},
+        }
+        extra_roofline = cold_roofline(combine_bytes, comb_cold)
 
     comb_ms = phases["combine_fingerprinted"]
     achieved = combine_bytes / (comb_ms * 1e-3) / 1e9
@@ -212,20 +233,10 @@ def bench_moe(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("combine_kernel_fp", name, digest),
                      "algorithmic_bytes_per_launch": combine_bytes, "avg_launch_ms": round(comb_ms, 4),
-                     **cold_roofline(combine_bytes, comb_cold)},
+                     **extra_roofline},
         "phases_ms": {k2: round(v, 4) for k2, v in phases.items()},
-        "unfused_ms": {k2: round(v, 4) for k2, v in plain.items()},
-        "overhead_vs_atomic": {
-            "deterministic_combine_ms": round(comb_ms, 4),
-            "atomic_zero_plus_combine_ms": round(aph["zero"] + aph["combine_atomic"], 4),
-            "atomic_combine_only_ms": round(aph["combine_atomic"], 4),
-            "overhead": round(comb_ms / (aph["zero"] + aph["combine_atomic"]) - 1, 4),
-            "overhead_vs_atomic_kernel_only": round(comb_ms / aph["combine_atomic"] - 1, 4),
-        },
         "wall_ms_per_step": round(wall_ms, 4),
-        "cold_cache_ms_per_step": round(ms_cold, 4),
-        "dispatch_permute": {"ms": round(perm_ms, 4), "algorithmic_bytes": perm_bytes,
-                             "achieved_gbs": round(perm_bytes / (perm_ms * 1e-3) / 1e9, 1)},
+        **extras,
     }
     if want_cpu:
         result["cpu_baseline"] = cpu_baseline_moe(oracle, inp, cpu_seconds)
@@ -304,12 +315,14 @@ def main():
     dr.dr_set_launch_params(reset=True)
     name = args.workload
     if name in ("moe_combine", "tiny_moe_combine"):
-        res = bench_moe(torch, dr, name, args.steps, args.warmup, args.cpu_seconds, not args.no_cpu_baseline)
+        res = bench_moe(torch, dr, name, args.steps, args.warmup, args.cpu_seconds, not args.no_cpu_baseline,
+                        args.step_only)
     else:
         import bench_workloads
         res = bench_workloads.run(torch, dr, name, args.steps, args.warmup, args.cpu_seconds,
-                                  not args.no_cpu_baseline)
-    res["roofline"].update(copy_ceiling(torch, res["roofline"]["achieved"]))
+                                  not args.no_cpu_baseline, args.step_only)
+    if not args.step_only:
+        res["roofline"].update(copy_ceiling(torch, res["roofline"]["achieved"]))
     if "cpu_baseline" in res:
         res["cpu_baseline"].update(host_description())
     if args.calibrate_copy_mib > 0:

@@ -103,13 +103,13 @@ def cold_roofline(alg_bytes: int, ms: float) -> dict:
             "frac_cold_cache": round(gbs / HBM_PEAK_GBS, 4)}
 
 
-def run(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
+def run(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only=False):
     if name in ("sparse_attn_dk", "embedding_grad"):
-        return _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu)
-    return _splitk(torch, dr, name, steps, warmup, cpu_seconds, want_cpu)
+        return _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only)
+    return _splitk(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only)
 
 
-def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
+def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only):
     import oracle
     import workloads
     _log(f"{name}: generating inputs")
@@ -141,25 +141,37 @@ def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
     _log(f"{name}: timing {steps} steps")
     ms_step = _timed(torch, steps, lambda: step(timer.step()))
     ph = timer.mean_ms()
-    ms_cold = cold_ms(torch, step)
-
-    # reused plan: sort once, then only the plan + ordered reduction each step
-    perm, seg, _ = dr.dr_sort_by_dest(index, D, want_inv=False)
-    ws2 = torch.empty_like(ws)
-    for _ in range(warmup):
-        dr.dr_index_add(out, src, index, perm=perm, seg_offsets=seg, ws=ws2)
-    ms_plan = _timed(torch, steps, lambda: dr.dr_index_add(out, src, index, perm=perm, seg_offsets=seg, ws=ws2))
-    ws_sort = torch.empty(dr.dr_sort_workspace_size(n, D), dtype=torch.uint8, device="cuda")
-    ms_sort = _timed(torch, steps, lambda: dr.dr_sort_by_dest(index, D, perm=perm, seg_offsets=seg, want_inv=False,
-                                                               ws=ws_sort))
-    # atomic baseline on the same destination
-    for _ in range(warmup):
-        dr.dr_index_add_atomic(out, src, index)
-    ms_atomic = _timed(torch, steps, lambda: dr.dr_index_add_atomic(out, src, index))
-
-    fused = _fused_dk(torch, dr, steps, warmup) if name == "sparse_attn_dk" else None
     det_ms = ph["index_add"]
-    ia_cold = cold_ms(torch, lambda: dr.dr_index_add(out, src, index, ws=ws))
+    extras, extra_roofline = {}, {}
+    if not step_only:
+        ms_cold = cold_ms(torch, step)
+
+        # reused plan: sort once, then only the plan + ordered reduction each step
+        perm, seg, _ = dr.dr_sort_by_dest(index, D, want_inv=False)
+        ws2 = torch.empty_like(ws)
+        for _ in range(warmup):
+            dr.dr_index_add(out, src, index, perm=perm, seg_offsets=seg, ws=ws2)
+        ms_plan = _timed(torch, steps, lambda: dr.dr_index_add(out, src, index, perm=perm, seg_offsets=seg, ws=ws2))
+        ws_sort = torch.empty(dr.dr_sort_workspace_size(n, D), dtype=torch.uint8, device="cuda")
+        ms_sort = _timed(torch, steps, lambda: dr.dr_sort_by_dest(index, D, perm=perm, seg_offsets=seg, want_inv=False,
+                                                                   ws=ws_sort))
+        # atomic baseline on the same destination
+        for _ in range(warmup):
+            dr.dr_index_add_atomic(out, src, index)
+        ms_atomic = _timed(torch, steps, lambda: dr.dr_index_add_atomic(out, src, index))
+
+        fused = _fused_dk(torch, dr, steps, warmup) if name == "sparse_attn_dk" else None
+        ia_cold = cold_ms(torch, lambda: dr.dr_index_add(out, src, index, ws=ws))
+        extras = {
+            "cold_cache_ms_per_step": round(ms_cold, 4),
+            "reused_plan_ms": round(ms_plan, 4), "sort_only_ms": round(ms_sort, 4),
+            "overhead_vs_atomic": {"deterministic_ms": round(det_ms, 4), "atomic_ms": round(ms_atomic, 4),
+                                   "overhead": round(det_ms / ms_atomic - 1, 4),
+                                   "overhead_reused_plan": round(ms_plan / ms_atomic - 1, 4)},
+        }
+        if fused:
+            extras["fused_dk"] = fused
+        extra_roofline = cold_roofline(red_bytes, ia_cold)
     achieved = red_bytes / (det_ms * 1e-3) / 1e9
     res = {
         "ms_per_step": ms_step,
@@ -175,16 +187,10 @@ def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
                      "traffic": measured_traffic("dr_index_add", name,
                                                  source_digest("sort.hip", "segreduce.hip", "internal.h", "device.h")),
                      "algorithmic_bytes_per_launch": red_bytes, "avg_launch_ms": round(det_ms, 4),
-                     **cold_roofline(red_bytes, ia_cold)},
+                     **extra_roofline},
         "phases_ms": {k: round(v, 4) for k, v in ph.items()},
-        "cold_cache_ms_per_step": round(ms_cold, 4),
-        "reused_plan_ms": round(ms_plan, 4), "sort_only_ms": round(ms_sort, 4),
-        "overhead_vs_atomic": {"deterministic_ms": round(det_ms, 4), "atomic_ms": round(ms_atomic, 4),
-                               "overhead": round(det_ms / ms_atomic - 1, 4),
-                               "overhead_reused_plan": round(ms_plan / ms_atomic - 1, 4)},
+        **extras,
     }
-    if fused:
-        res["fused_dk"] = fused
     if want_cpu:
         res["cpu_baseline"] = _cpu_index_add(oracle, inp, cpu_seconds)
     return res
@@ -235,7 +241,7 @@ def _cpu_index_add(oracle, inp, seconds):
             "sample": f"first {m2} of {n} contributions of the same workload, {el:.1f} s", "seconds": round(el, 2)}
 
 
-def _splitk(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
+def _splitk(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only):
     import oracle
     import workloads
     _log(f"{name}: generating inputs")
@@ -267,47 +273,57 @@ def _splitk(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
     _log(f"{name}: timing {steps} steps")
     ms_step = _timed(torch, steps, lambda: step(timer.step()))
     ph = timer.mean_ms()
-    ms_cold = cold_ms(torch, step)
-    dW_a = torch.empty_like(dW)
-    atimer = _Timer(torch, ["zero", "splitk_gemm_atomic"])
-
-    def astep(evs=None):
-        if evs: evs[0].record()
-        dW_a.zero_()
-        if evs: evs[1].record()
-        dr.dr_splitk_gemm_tn_atomic(X, dY, S, out=dW_a)
-        if evs: evs[2].record()
-
-    for _ in range(warmup):
-        astep()
-    for _ in range(steps):
-        astep(atimer.step())
-    aph = atimer.mean_ms()
-    # the single-pass alternative: one split, so one workgroup per 64-column M tile walks all K tokens
-    p1 = torch.empty(1, M, N, dtype=torch.float32, device="cuda")
-    for _ in range(warmup):
-        dr.dr_splitk_gemm_tn(X, dY, 1, partials=p1)
-    ms_nosplit = _timed(torch, steps, lambda: dr.dr_splitk_gemm_tn(X, dY, 1, partials=p1))
-    # the grouped form of the same contraction: 16 unequal groups (expert-like sizes), slots of 256 tokens
-    sizes = np.array([int(K * w) for w in np.linspace(2.0, 0.05, 16) / np.linspace(2.0, 0.05, 16).sum()])
-    sizes[0] += K - sizes.sum()
-    offs = torch.from_numpy(np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)).cuda()
-    Pg, so, wsg = dr.dr_grouped_splitk_gemm_tn(X, dY, offs, 256)
-    dWg = dr.dr_grouped_splitk_reduce(Pg, so, wsg)
-
-    def grouped():
-        dr.dr_grouped_splitk_gemm_tn(X, dY, offs, 256, partials=Pg, slot_offsets=so, ws=wsg)
-        dr.dr_grouped_splitk_reduce(Pg, so, wsg, out=dWg)
-
-    for _ in range(warmup):
-        grouped()
-    ms_grouped = _timed(torch, steps, grouped)
-    dr.dr_workspace_status(wsg)
     g_ms = ph["splitk_gemm"]
-    g_cold = cold_ms(torch, lambda: dr.dr_splitk_gemm_tn(X, dY, S, partials=partials))
-    achieved = gemm_bytes / (g_ms * 1e-3) / 1e9
     det_ms = ph["splitk_gemm"] + ph["splitk_reduce"]
-    at_ms = aph["zero"] + aph["splitk_gemm_atomic"]
+    extras, extra_roofline = {}, {}
+    if not step_only:
+        ms_cold = cold_ms(torch, step)
+        dW_a = torch.empty_like(dW)
+        atimer = _Timer(torch, ["zero", "splitk_gemm_atomic"])
+
+        def astep(evs=None):
+            if evs: evs[0].record()
+            dW_a.zero_()
+            if evs: evs[1].record()
+            dr.dr_splitk_gemm_tn_atomic(X, dY, S, out=dW_a)
+            if evs: evs[2].record()
+
+        for _ in range(warmup):
+            astep()
+        for _ in range(steps):
+            astep(atimer.step())
+        aph = atimer.mean_ms()
+        # the single-pass alternative: one split, so one workgroup per 64-column M tile walks all K tokens
+        p1 = torch.empty(1, M, N, dtype=torch.float32, device="cuda")
+        for _ in range(warmup):
+            dr.dr_splitk_gemm_tn(X, dY, 1, partials=p1)
+        ms_nosplit = _timed(torch, steps, lambda: dr.dr_splitk_gemm_tn(X, dY, 1, partials=p1))
+        # the grouped form of the same contraction: 16 unequal groups (expert-like sizes), slots of 256 tokens
+        sizes = np.array([int(K * w) for w in np.linspace(2.0, 0.05, 16) / np.linspace(2.0, 0.05, 16).sum()])
+        sizes[0] += K - sizes.sum()
+        offs = torch.from_numpy(np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)).cuda()
+        Pg, so, wsg = dr.dr_grouped_splitk_gemm_tn(X, dY, offs, 256)
+        dWg = dr.dr_grouped_splitk_reduce(Pg, so, wsg)
+
+        def grouped():
+            dr.dr_grouped_splitk_gemm_tn(X, dY, offs, 256, partials=Pg, slot_offsets=so, ws=wsg)
+            dr.dr_grouped_splitk_reduce(Pg, so, wsg, out=dWg)
+
+        for _ in range(warmup):
+            grouped()
+        ms_grouped = _timed(torch, steps, grouped)
+        dr.dr_workspace_status(wsg)
+        g_cold = cold_ms(torch, lambda: dr.dr_splitk_gemm_tn(X, dY, S, partials=partials))
+        at_ms = aph["zero"] + aph["splitk_gemm_atomic"]
+        extras = {
+            "overhead_vs_atomic": {"deterministic_ms": round(det_ms, 4), "atomic_zero_plus_gemm_ms": round(at_ms, 4),
+                                   "overhead": round(det_ms / at_ms - 1, 4)},
+            "cold_cache_ms_per_step": round(ms_cold, 4),
+            "no_split_ms": round(ms_nosplit, 4),
+            "grouped_16_groups_ms": round(ms_grouped, 4),
+        }
+        extra_roofline = cold_roofline(gemm_bytes, g_cold)
+    achieved = gemm_bytes / (g_ms * 1e-3) / 1e9
     res = {
         "ms_per_step": ms_step,
         "value": step_bytes / (ms_step * 1e-3) / 1e9,
@@ -318,15 +334,11 @@ def _splitk(torch, dr, name, steps, warmup, cpu_seconds, want_cpu):
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("splitk_gemm_kernel", name, source_digest("splitk.hip", "device.h")),
                      "algorithmic_bytes_per_launch": gemm_bytes, "avg_launch_ms": round(g_ms, 4),
-                     **cold_roofline(gemm_bytes, g_cold),
+                     **extra_roofline,
                      "mfma_tflops": round(flops / (g_ms * 1e-3) / 1e12, 2),
                      "mfma_frac_of_bf16_peak": round(flops / (g_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 5)},
         "phases_ms": {k: round(v, 4) for k, v in ph.items()},
-        "overhead_vs_atomic": {"deterministic_ms": round(det_ms, 4), "atomic_zero_plus_gemm_ms": round(at_ms, 4),
-                               "overhead": round(det_ms / at_ms - 1, 4)},
-        "cold_cache_ms_per_step": round(ms_cold, 4),
-        "no_split_ms": round(ms_nosplit, 4),
-        "grouped_16_groups_ms": round(ms_grouped, 4),
+        **extras,
     }
     if want_cpu:
         t0 = time.perf_counter()
