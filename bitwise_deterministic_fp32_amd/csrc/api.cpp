@@ -3,6 +3,7 @@
 // launches for each entry point.  See include/detreduce.h for the contract.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -244,17 +245,20 @@ Launch launch_config() {
 }
 
 int device_cu_count() {
-    static int cache[64] = {0};
+    // per device, filled on first use; atomic because any host thread may launch
+    constexpr int kSlots = 256;
+    static std::atomic<int> cache[kSlots];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
-    const int slot = dev < 64 ? dev : 63;
-    if (cache[slot] <= 0) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-            cus = 256;
-        cache[slot] = cus;
+    if (dev < kSlots) {
+        const int known = cache[dev].load(std::memory_order_relaxed);
+        if (known > 0) return known;
     }
-    return cache[slot];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    if (dev < kSlots) cache[dev].store(cus, std::memory_order_relaxed);
+    return cus;
 }
 
 }  // namespace dr
