@@ -275,6 +275,42 @@ def permute_rows(x, perm, k: int):
     return x[perm // k].copy()
 
 
+def decode_attention(q, k_cache, v_cache, seq_lens, scale: float):
+    """Decode attention, the operation that a batch-invariant decode kernel
+    must evaluate with a KV partition that does not depend on the batch
+    (DeepSeek-V4 book ch. 9, section 2.1, giving up occupancy-chosen split-KV).
+    By its definition, in fp64: for sequence b and query
+    head h (key/value head h // (Hq // Hkv)), with s_j = scale * q.k_j over the
+    sequence's first seq_lens[b] cache rows,
+        out[b, h] = sum_j softmax(s)_j v_j,     A[b, h] = sum_j softmax(s)_j |v_j|
+    (A bounds the rounding error of any fp32 evaluation).  A sequence with no
+    cached token has out = 0.  q: [B, Hq, D]; caches: [B, Lmax, Hkv, D]; float32
+    or uint16 (bf16 bits)."""
+    def f64(a):
+        a = np.asarray(a)
+        if a.dtype == np.uint16:
+            a = (a.astype(np.uint32) << 16).view(np.float32)
+        return a.astype(np.float64)
+    q, kc, vc = f64(q), f64(k_cache), f64(v_cache)
+    B, Hq, D = q.shape
+    Hkv = kc.shape[2]
+    g = Hq // Hkv
+    out = np.zeros((B, Hq, D))
+    A = np.zeros((B, Hq, D))
+    for b in range(B):
+        L = int(seq_lens[b])
+        if L == 0:
+            continue
+        for h in range(Hq):
+            kk, vv = kc[b, :L, h // g], vc[b, :L, h // g]
+            s_ = scale * (kk @ q[b, h])
+            p_ = np.exp(s_ - s_.max())
+            p_ /= p_.sum()
+            out[b, h] = p_ @ vv
+            A[b, h] = p_ @ np.abs(vv)
+    return out, A
+
+
 def splitmix64_mix(z: int) -> int:
     return int(lib().oracle_splitmix64_mix(ctypes.c_uint64(z & ((1 << 64) - 1))))
 

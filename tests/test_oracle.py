@@ -552,6 +552,46 @@ def test_permute_rows_brute_force():
 
 
 # ---------------------------------------------------------------------------
+# Decode attention (by definition)
+# ---------------------------------------------------------------------------
+def test_decode_attention_against_torch_sdpa_and_closed_forms():
+    import torch
+    rng = np.random.default_rng(90)
+    B, Hq, Hkv, D, Lmax = 3, 8, 2, 16, 40
+    q = rng.standard_normal((B, Hq, D))
+    kc = rng.standard_normal((B, Lmax, Hkv, D))
+    vc = rng.standard_normal((B, Lmax, Hkv, D))
+    lens = np.array([40, 1, 17], np.int32)
+    scale = 0.25
+    out, A = oracle.decode_attention(q, kc, vc, lens, scale)
+    for b in range(B):
+        L = lens[b]
+        kk = torch.from_numpy(kc[b, :L]).permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)   # [Hq, L, D]
+        vv = torch.from_numpy(vc[b, :L]).permute(1, 0, 2).repeat_interleave(Hq // Hkv, 0)
+        qq = torch.from_numpy(q[b]).unsqueeze(1)                                          # [Hq, 1, D]
+        ref = torch.nn.functional.scaled_dot_product_attention(qq, kk, vv, scale=scale)[:, 0]
+        assert np.allclose(out[b], ref.numpy(), rtol=1e-12, atol=1e-12)
+    # one cached token: the value row itself; equal scores: the mean of the values
+    assert np.allclose(out[1], vc[1, 0].repeat(Hq // Hkv, axis=0), rtol=0, atol=1e-15)
+    z, _ = oracle.decode_attention(np.zeros((1, 2, D)), kc[:1], vc[:1], np.array([5], np.int32), 1.0)
+    assert np.allclose(z[0, 0], vc[0, :5, 0].mean(axis=0), rtol=0, atol=1e-14)
+    # |out| <= A, and an empty sequence gives zeros
+    assert np.all(np.abs(out) <= A + 1e-15)
+    e, _ = oracle.decode_attention(q[:1], kc[:1], vc[:1], np.array([0], np.int32), scale)
+    assert np.all(e == 0)
+    # hand example: scores ln 3 and 0 give weights 3/4 and 1/4
+    qh = np.array([[[1.0, 0.0]]])
+    kh = np.array([[[[1.0, 0.0]], [[0.0, 1.0]]]])
+    vh = np.array([[[[4.0, -8.0]], [[8.0, 16.0]]]])
+    oh, _ = oracle.decode_attention(qh, kh, vh, np.array([2], np.int32), float(np.log(3.0)))
+    assert np.allclose(oh[0, 0], [5.0, -2.0], rtol=0, atol=1e-14)
+    # key/value pairs in any order give the same result (a softmax-weighted average)
+    perm = rng.permutation(40)
+    o2, _ = oracle.decode_attention(q[:1], kc[:1, perm], vc[:1, perm], np.array([40], np.int32), scale)
+    assert np.allclose(o2[0], out[0], rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
 # Fingerprint
 # ---------------------------------------------------------------------------
 def test_splitmix64_published_outputs(golden_dir):
