@@ -25,6 +25,7 @@ __all__ = [
     "dr_splitk_gemm_tn", "dr_splitk_gemm_tn_atomic", "dr_splitk_reduce",
     "dr_grouped_splitk_max_slots", "dr_grouped_splitk_workspace_size", "dr_grouped_splitk_gemm_tn",
     "dr_grouped_splitk_reduce", "dr_permute_rows",
+    "dr_decode_attention_workspace_size", "dr_decode_attention", "dr_decode_attention_occupancy_chunk",
     "dr_fingerprint_workspace_size", "dr_fingerprint", "fingerprint_value",
     "dr_workspace_status", "dr_read_status",
 ]
@@ -73,6 +74,10 @@ def _load() -> ctypes.CDLL:
         "dr_grouped_splitk_gemm_tn": ([vp, vp, i64, i64, i64, vp, i32, i32, vp, i64, vp, vp, sz, vp], ctypes.c_int),
         "dr_grouped_splitk_reduce": ([vp, i64, vp, i32, i64, vp, vp, vp], ctypes.c_int),
         "dr_permute_rows": ([vp, i64, i64, vp, vp, i64, i32, vp, vp, vp], ctypes.c_int),
+        "dr_decode_attention_workspace_size": ([i64, i32, i32, i32, i64], sz),
+        "dr_decode_attention": ([vp, vp, vp, vp, vp, i64, i32, i32, i64, i32, ctypes.c_float, i32, vp, sz, vp, vp],
+                                ctypes.c_int),
+        "dr_decode_attention_occupancy_chunk": ([i64, i32, i32], i32),
         "dr_fingerprint_workspace_size": ([i64], sz),
         "dr_fingerprint": ([vp, i64, vp, vp, sz, vp], ctypes.c_int),
         "dr_workspace_status": ([vp, vp], ctypes.c_int),
@@ -363,6 +368,39 @@ def dr_permute_rows(rows, perm, k: int, *, inv_perm=None, out=None, dev_status=N
     _check(lib.dr_permute_rows(_p(rows), row_bytes, rows.shape[0], _p(perm), _p(inv_perm), n, k, _p(out),
                                _p(dev_status), _stream(stream)), "dr_permute_rows")
     return out
+
+
+# ---------------------------------------------------------------------------
+def dr_decode_attention_workspace_size(batch: int, num_q_heads: int, max_seq_len: int, kv_chunk: int,
+                                       head_dim: int = 128) -> int:
+    return int(lib.dr_decode_attention_workspace_size(batch, num_q_heads, max_seq_len, kv_chunk, head_dim))
+
+
+def dr_decode_attention(q, k_cache, v_cache, seq_lens, scale: float, kv_chunk: int, *, out=None, ws=None,
+                        dev_status=None, stream=None):
+    """Decode attention of q [B, Hq, D] (bf16) over the caches [B, Lmax, Hkv, D] (bf16) with a fixed KV
+    partition of kv_chunk tokens; returns fp32 [B, Hq, D]."""
+    for t, name in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _dev(t, name, (torch.bfloat16,))
+    _dev(seq_lens, "seq_lens", (torch.int32,))
+    if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [B, Hq, D] and the caches [B, Lmax, Hkv, D] of one shape")
+    B, Hq, D = q.shape
+    Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape[0] != B or k_cache.shape[3] != D or seq_lens.numel() != B:
+        raise ValueError("batch or head_dim mismatch")
+    out = out if out is not None else torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    ws = ws if ws is not None else _workspace(dr_decode_attention_workspace_size(B, Hq, Lmax, kv_chunk, D), q.device)
+    _check(lib.dr_decode_attention(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(seq_lens), B, Hq, Hkv, D, Lmax,
+                                   float(scale), kv_chunk, _p(ws), ws.numel(), _p(dev_status), _stream(stream)),
+           "dr_decode_attention")
+    return out
+
+
+def dr_decode_attention_occupancy_chunk(batch: int, num_kv_heads: int, max_seq_len: int) -> int:
+    """The batch-dependent kv_chunk of an occupancy-driven split-KV heuristic (a deliberately batch-variant
+    baseline)."""
+    return int(lib.dr_decode_attention_occupancy_chunk(batch, num_kv_heads, max_seq_len))
 
 
 # ---------------------------------------------------------------------------

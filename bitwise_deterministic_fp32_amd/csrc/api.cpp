@@ -681,6 +681,83 @@ dr_status dr_permute_rows(const void* rows, int64_t row_bytes, int64_t num_rows,
 }
 
 // ---------------------------------------------------------------------------
+namespace {
+constexpr int64_t kDecodeDim = 128;
+constexpr int32_t kMaxDecodeLen = 1 << 30;
+constexpr int32_t kMaxKvChunk = 1 << 20;
+
+bool decode_shape_ok(int64_t batch, int32_t hq, int32_t hkv, int64_t head_dim, int32_t max_seq_len, int32_t kv_chunk) {
+    if (batch < 0 || hq < 1 || hkv < 1 || head_dim != kDecodeDim) return false;
+    if (max_seq_len < 1 || max_seq_len > kMaxDecodeLen) return false;
+    if (kv_chunk < 64 || kv_chunk > kMaxKvChunk || kv_chunk % 64 != 0) return false;
+    if (hq % hkv != 0) return false;
+    const int32_t g = hq / hkv;
+    if (g != 1 && g != 2 && g != 4 && g != 8 && g != 16) return false;
+    const int64_t nc = dr::decode_num_chunks(max_seq_len, kv_chunk);
+    if (batch > 0 && (batch * hkv >= kMaxN || batch * hkv * nc >= kMaxN || batch * hq >= kMaxN)) return false;
+    return true;
+}
+
+size_t decode_slots_bytes(int64_t batch, int32_t hq, int32_t max_seq_len, int32_t kv_chunk) {
+    const int64_t slots = batch * hq * dr::decode_num_chunks(max_seq_len, kv_chunk);
+    return (size_t)slots * (sizeof(float2) + kDecodeDim * sizeof(float));
+}
+}  // namespace
+
+size_t dr_decode_attention_workspace_size(int64_t batch, int32_t num_q_heads, int32_t max_seq_len, int32_t kv_chunk,
+                                          int64_t head_dim) {
+    if (batch < 0 || num_q_heads < 1 || head_dim != kDecodeDim || max_seq_len < 1 || max_seq_len > kMaxDecodeLen ||
+        kv_chunk < 64 || kv_chunk > kMaxKvChunk || kv_chunk % 64 != 0)
+        return 0;
+    return dr::kStatusBytes + decode_slots_bytes(batch, num_q_heads, max_seq_len, kv_chunk);
+}
+
+dr_status dr_decode_attention(float* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* seq_lens, int64_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                              int64_t head_dim, int32_t max_seq_len, float scale, int32_t kv_chunk, void* ws,
+                              size_t ws_bytes, int32_t* dev_status, hipStream_t stream) {
+    const char* what = "dr_decode_attention";
+    if (!decode_shape_ok(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, kv_chunk))
+        return fail(DR_ERR_INVALID_ARGUMENT,
+                    "%s: need head_dim 128, num_q_heads / num_kv_heads in {1, 2, 4, 8, 16}, "
+                    "1 <= max_seq_len <= 2^30, kv_chunk a multiple of 64 in [64, 2^20], and fewer than 2^31 "
+                    "workgroups",
+                    what);
+    if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff())
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: scale must be finite", what);
+    if (batch == 0) return ok();
+    if (!out || !q || !k_cache || !v_cache || !seq_lens || !ws)
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: null pointer", what);
+    if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+        !aligned(seq_lens, 4) || !aligned(ws, 16) || (dev_status && !aligned(dev_status, 4)))
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: misaligned pointer", what);
+    const size_t need = dr_decode_attention_workspace_size(batch, num_q_heads, max_seq_len, kv_chunk, head_dim);
+    if (ws_bytes < need)
+        return fail(DR_ERR_WORKSPACE_TOO_SMALL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes, need);
+    char* base = static_cast<char*>(ws) + dr::kStatusBytes;
+    const int64_t slots = batch * num_q_heads * dr::decode_num_chunks(max_seq_len, kv_chunk);
+    float2* ml = reinterpret_cast<float2*>(base);
+    float* po = reinterpret_cast<float*>(base + (size_t)slots * sizeof(float2));
+    DR_TRY_HIP(dr::launch_decode_attention(out, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
+                                           static_cast<const uint16_t*>(v_cache), seq_lens, batch, num_q_heads,
+                                           num_kv_heads, max_seq_len, scale, kv_chunk, ml, po, dev_status, stream),
+               "decode attention launch");
+    return ok();
+}
+
+int32_t dr_decode_attention_occupancy_chunk(int64_t batch, int32_t num_kv_heads, int32_t max_seq_len) {
+    if (batch < 1 || num_kv_heads < 1 || max_seq_len < 1 || max_seq_len > kMaxDecodeLen) return 0;
+    const int64_t want = 2 * (int64_t)dr::device_cu_count();  // workgroups to fill the device twice over
+    const int64_t per_chunk = batch * num_kv_heads;            // workgroups per chunk index
+    int64_t splits = (want + per_chunk - 1) / per_chunk;
+    if (splits < 1) splits = 1;
+    int64_t chunk = ((max_seq_len + splits - 1) / splits + 63) / 64 * 64;
+    if (chunk < 64) chunk = 64;
+    if (chunk > kMaxKvChunk) chunk = kMaxKvChunk;
+    return (int32_t)chunk;
+}
+
+// ---------------------------------------------------------------------------
 size_t dr_fingerprint_workspace_size(int64_t nbytes) {
     (void)nbytes;
     return dr::kStatusBytes + dr::kMaxFingerprintBlocks * sizeof(uint64_t);

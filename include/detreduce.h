@@ -321,6 +321,54 @@ dr_status dr_permute_rows(const void* rows, int64_t row_bytes, int64_t num_rows,
                           hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * Batch-invariant decode attention (DeepSeek-V4 book ch. 9, section 2.1).
+ *
+ * One query token per sequence attends to the sequence's first seq_lens[b]
+ * cached keys and values:
+ *   out[b, h] = sum_j softmax_j(scale * q[b, h] . k[b, j, h / G]) v[b, j, h / G]
+ * with G = num_q_heads / num_kv_heads query heads per KV head (grouped-query
+ * attention); a sequence of length 0 gives zeros.  The pages give up split-KV
+ * decoding because its partition of the keys, and with it the order in which
+ * the partial softmax sums merge, follows the batch size and the occupancy.
+ * Here the keys of a sequence are cut into chunks of kv_chunk tokens from its
+ * first token, whatever the batch: each chunk computes private partials (its
+ * maximum, weight sum and weighted value sum per query head) in an order fixed
+ * by the chunk alone, and the partials merge in chunk order.  A sequence's
+ * output bits therefore depend only on its own q, cache rows, length, scale and
+ * kv_chunk: not on the other sequences, the batch size, its position in the
+ * batch or the device's size.  kv_chunk >= the sequence length runs the whole
+ * sequence serially in one workgroup, the pages' single-processor prefix.
+ * Scores are exact bf16 products summed in fp32 (matrix cores); weights are
+ * 2^(t - max) with t = score * scale * log2(e) in fp32.
+ *
+ *   out          OUT fp32 [batch, num_q_heads, head_dim], 16-byte aligned.
+ *   q            bf16 [batch, num_q_heads, head_dim].
+ *   k_cache, v_cache  bf16 [batch, max_seq_len, num_kv_heads, head_dim]; rows
+ *                at or past a sequence's length are never read.
+ *   seq_lens     int32 [batch], 0 <= seq_lens[b] <= max_seq_len.  A length
+ *                outside that range ORs an index error bit into *dev_status
+ *                (when given) and that sequence's output rows are not written.
+ *   head_dim     128.  num_q_heads / num_kv_heads must be 1, 2, 4, 8 or 16.
+ *   max_seq_len  1 .. 2^30.  kv_chunk: a multiple of 64 in [64, 2^20].
+ *   ws           >= dr_decode_attention_workspace_size(...) bytes, 16-byte
+ *                aligned: one partial slot per (sequence, query head, chunk).
+ * All pointers must be 16-byte aligned (seq_lens and dev_status 4-byte).
+ * ---------------------------------------------------------------------- */
+size_t dr_decode_attention_workspace_size(int64_t batch, int32_t num_q_heads, int32_t max_seq_len, int32_t kv_chunk,
+                                          int64_t head_dim);
+dr_status dr_decode_attention(float* out, const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* seq_lens, int64_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                              int64_t head_dim, int32_t max_seq_len, float scale, int32_t kv_chunk, void* ws,
+                              size_t ws_bytes, int32_t* dev_status, hipStream_t stream);
+
+/* The kv_chunk an occupancy-driven split-KV heuristic would pick for this batch
+ * on the current device: enough chunks to give every compute unit two
+ * workgroups, so it CHANGES WITH THE BATCH SIZE.  A deliberately batch-variant
+ * baseline, the pattern the pages reject; passing it to dr_decode_attention
+ * shows the output bits moving with the batch.  Returns 0 on bad arguments. */
+int32_t dr_decode_attention_occupancy_chunk(int64_t batch, int32_t num_kv_heads, int32_t max_seq_len);
+
+/* ------------------------------------------------------------------------
  * Byte fingerprint of a tensor, for comparing runs byte for byte rather than
  * by printed values (bitwise-determinism interview note, "how to verify":
  * per-step tensor fingerprints compared byte-wise).  The definition is this

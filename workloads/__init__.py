@@ -20,7 +20,9 @@ Workload shapes follow the pages' use cases:
   * embedding gradient (Megatron-LM determinism reference, section 3.1,
     vocab-parallel embedding row),
   * thin split-K contraction with per-split buffers (DeepSeek-V4 book, ch. 9,
-    section 3.3 "mHC backward").
+    section 3.3 "mHC backward"),
+  * decode attention over a KV cache (DeepSeek-V4 book, ch. 9, section 2.1);
+    the pages give no attention shape, so a common grouped-query one is used.
 No public dataset is involved; these synthetic draws stand in for activations
 and gradients of a real model.
 """
@@ -272,7 +274,45 @@ CONFIGS = {
     "sparse_attn_dk": dict(kind="sparse_attn", seed=1003, Q=8192, K=65536, S=512, H=128, s=1.1),
     "embedding_grad": dict(kind="embedding", seed=1004, tokens=32768, V=131072, H=4096, s=1.1),
     "splitk_mhc": dict(kind="splitk", seed=1005, K=16384, M=7168, N=24, splits=64),
+    "decode_attention": dict(kind="decode", seed=1006, B=64, Lmax=16384, Hq=32, Hkv=8, D=128),
 }
+
+
+# --------------------------------------------------------------------------
+# Decode attention
+# --------------------------------------------------------------------------
+BF16_NAN = 0x7FC0  # fills cache rows past a sequence's length: they must never be read
+
+
+@dataclass
+class DecodeInputs:
+    B: int
+    Lmax: int
+    Hq: int
+    Hkv: int
+    D: int
+    scale: float
+    lens: np.ndarray   # int32 [B]
+    q: np.ndarray      # uint16 bf16 bits [B, Hq, D]
+    k: np.ndarray      # uint16 bf16 bits [B, Lmax, Hkv, D]
+    v: np.ndarray
+
+
+def decode_inputs(seed: int, B: int = 64, Lmax: int = 16384, Hq: int = 32, Hkv: int = 8, D: int = 128,
+                  lens=None) -> DecodeInputs:
+    """Sequence lengths uniform in [1, Lmax] (unless given); q, K and V bf16
+    N(0,1); scale 1/sqrt(D).  Cache rows at or past a sequence's length hold
+    NaN."""
+    if lens is None:
+        lens = _block_rng(seed, 13, 0).integers(1, Lmax + 1, size=B)
+    lens = np.asarray(lens, np.int32)
+    q = normal_bf16(seed, 14, B * Hq * D).reshape(B, Hq, D)
+    k = normal_bf16(seed, 15, B * Lmax * Hkv * D).reshape(B, Lmax, Hkv, D)
+    v = normal_bf16(seed, 16, B * Lmax * Hkv * D).reshape(B, Lmax, Hkv, D)
+    for b in range(B):
+        k[b, lens[b]:] = BF16_NAN
+        v[b, lens[b]:] = BF16_NAN
+    return DecodeInputs(B, Lmax, Hq, Hkv, D, float(1.0 / np.sqrt(D)), lens, q, k, v)
 
 
 def make(name: str, **overrides):
@@ -289,4 +329,6 @@ def make(name: str, **overrides):
         return embedding_grad_inputs(seed, cfg["tokens"], cfg["V"], cfg["H"], cfg["s"], cfg.get("preset_out", True))
     if kind == "splitk":
         return splitk_inputs(seed, cfg["K"], cfg["M"], cfg["N"], cfg["splits"])
+    if kind == "decode":
+        return decode_inputs(seed, cfg["B"], cfg["Lmax"], cfg["Hq"], cfg["Hkv"], cfg["D"], cfg.get("lens"))
     raise ValueError(kind)
