@@ -16,7 +16,8 @@ stream it runs on), the overhead against the atomicAdd baseline, and the CPU
 oracle timed on a bounded sample of the same workload.
 
 Other workloads (--workload sparse_attn_dk | embedding_grad | splitk_mhc |
-tiny_moe_combine) print the same kind of line for their own step.
+decode_attention | tiny_moe_combine) print the same kind of line for their
+own step.
 """
 from __future__ import annotations
 
@@ -46,7 +47,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="moe_combine",
-                    choices=["moe_combine", "tiny_moe_combine", "sparse_attn_dk", "embedding_grad", "splitk_mhc"])
+                    choices=["moe_combine", "tiny_moe_combine", "sparse_attn_dk", "embedding_grad", "splitk_mhc",
+                             "decode_attention"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--step-only", action="store_true",
                     help="time the step alone: no comparison legs (atomic, unfused, cold cache, extra entry points) "

@@ -8,6 +8,9 @@ sparse_attn_dk / embedding_grad: a step is dr_index_add (stable sort of the
   known a step early) is reported beside it.
 splitk_mhc: a step is dr_splitk_gemm_tn (64 private fp32 partials by bf16
   MFMA), dr_splitk_reduce in split-id order, and dr_fingerprint of dW.
+decode_attention: a step is dr_decode_attention (chunk partials over the KV
+  cache with a fixed 512-token partition, then the merge in chunk order) and
+  dr_fingerprint of the output.
 """
 from __future__ import annotations
 
@@ -106,7 +109,145 @@ def cold_roofline(alg_bytes: int, ms: float) -> dict:
 def run(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only=False):
     if name in ("sparse_attn_dk", "embedding_grad"):
         return _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only)
+    if name == "decode_attention":
+        return _decode(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only)
     return _splitk(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only)
+
+
+DECODE_KV_CHUNK = 512
+
+
+def _decode_bytes(lens, Hq, Hkv, D, chunk):
+    """Algorithmic bytes of one decode attention call: the K and V rows of every
+    cached token, q, the private chunk partials (written, then read by the
+    merge) and the output."""
+    kv = int(lens.astype(np.int64).sum()) * Hkv * D * 2 * 2
+    chunks = int(((lens.astype(np.int64) + chunk - 1) // chunk).sum())
+    partials = chunks * Hq * (8 + D * 4)
+    return kv + len(lens) * Hq * D * 2 + 2 * partials + len(lens) * Hq * D * 4
+
+
+def _decode(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only):
+    import oracle
+    import workloads
+    _log(f"{name}: generating inputs")
+    inp = workloads.make(name)
+    B, Lmax, Hq, Hkv, D, C = inp.B, inp.Lmax, inp.Hq, inp.Hkv, inp.D, DECODE_KV_CHUNK
+    q = torch.from_numpy(inp.q.view(np.int16)).view(torch.bfloat16).cuda()
+    k = torch.from_numpy(inp.k.view(np.int16)).view(torch.bfloat16).cuda()
+    v = torch.from_numpy(inp.v.view(np.int16)).view(torch.bfloat16).cuda()
+    lens = torch.from_numpy(inp.lens).cuda()
+    out = torch.empty(B, Hq, D, dtype=torch.float32, device="cuda")
+    ws = torch.empty(dr.dr_decode_attention_workspace_size(B, Hq, Lmax, C), dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    fp = torch.empty(1, dtype=torch.int64, device="cuda")
+    ws_fp = torch.empty(dr.dr_fingerprint_workspace_size(B * Hq * D * 4), dtype=torch.uint8, device="cuda")
+    call_bytes = _decode_bytes(inp.lens, Hq, Hkv, D, C)
+    step_bytes = call_bytes + B * Hq * D * 4
+    timer = _Timer(torch, ["decode_attention", "fingerprint"])
+
+    def call(chunk=C, o=out, w=ws):
+        dr.dr_decode_attention(q, k, v, lens, inp.scale, chunk, out=o, ws=w, dev_status=status)
+
+    def step(evs=None):
+        if evs: evs[0].record()
+        call()
+        if evs: evs[1].record()
+        dr.dr_fingerprint(out, out=fp, ws=ws_fp)
+        if evs: evs[2].record()
+
+    for _ in range(warmup):
+        step()
+    dr.dr_read_status(status)
+    _log(f"{name}: timing {steps} steps")
+    ms_step = _timed(torch, steps, lambda: step(timer.step()))
+    ph = timer.mean_ms()
+    det_ms = ph["decode_attention"]
+    extras, extra_roofline = {}, {}
+    if not step_only:
+        ms_cold = cold_ms(torch, call)
+        legs = {}
+        # the occupancy-chosen partition of a split-KV heuristic (batch-variant) on the same batch
+        occ = dr.dr_decode_attention_occupancy_chunk(B, Hkv, Lmax)
+        ws_o = torch.empty(dr.dr_decode_attention_workspace_size(B, Hq, Lmax, occ), dtype=torch.uint8,
+                           device="cuda")
+        o2 = torch.empty_like(out)
+        for _ in range(warmup):
+            call(occ, o2, ws_o)
+        legs["occupancy_chunk"] = occ
+        legs["occupancy_chunk_ms"] = round(_timed(torch, steps, lambda: call(occ, o2, ws_o)), 4)
+        # the pages' long-prefix scheme: each (sequence, KV head) walked serially by one workgroup
+        serial = ((Lmax + 63) // 64) * 64
+        ws_s = torch.empty(dr.dr_decode_attention_workspace_size(B, Hq, Lmax, serial), dtype=torch.uint8,
+                           device="cuda")
+        for _ in range(warmup):
+            call(serial, o2, ws_s)
+        legs["one_workgroup_per_sequence_head_ms"] = round(_timed(torch, steps, lambda: call(serial, o2, ws_s)), 4)
+        # one long sequence alone: fixed chunks against the heuristic's choice for a batch of one
+        L1 = int(inp.lens.max())
+        b1 = int(np.argmax(inp.lens))
+        q1, k1, v1 = q[b1:b1 + 1].contiguous(), k[b1:b1 + 1].contiguous(), v[b1:b1 + 1].contiguous()
+        l1 = lens[b1:b1 + 1].contiguous()
+        o1 = torch.empty(1, Hq, D, dtype=torch.float32, device="cuda")
+        occ1 = dr.dr_decode_attention_occupancy_chunk(1, Hkv, Lmax)
+        for c1 in (C, occ1):
+            w1 = torch.empty(dr.dr_decode_attention_workspace_size(1, Hq, Lmax, c1), dtype=torch.uint8,
+                             device="cuda")
+            for _ in range(warmup):
+                dr.dr_decode_attention(q1, k1, v1, l1, inp.scale, c1, out=o1, ws=w1)
+            legs[f"single_sequence_L{L1}_chunk{c1}_ms"] = round(
+                _timed(torch, steps, lambda: dr.dr_decode_attention(q1, k1, v1, l1, inp.scale, c1, out=o1, ws=w1)), 4)
+        extras = {"cold_cache_ms_per_call": round(ms_cold, 4), "partition_legs": legs,
+                  "overhead_vs_occupancy_chunk": round(det_ms / legs["occupancy_chunk_ms"] - 1, 4)}
+        extra_roofline = cold_roofline(call_bytes, ms_cold)
+    achieved = call_bytes / (det_ms * 1e-3) / 1e9
+    res = {
+        "ms_per_step": ms_step,
+        "value": step_bytes / (ms_step * 1e-3) / 1e9,
+        "config": {"workload": f"{name}: {B} sequences, lengths U[1,{Lmax}] (total {int(inp.lens.sum())} tokens), "
+                               f"{Hq} query / {Hkv} KV heads, head dim {D}, bf16 KV cache, fp32 output, "
+                               f"KV chunk {C}",
+                   "batch": B, "max_seq_len": Lmax, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "kv_chunk": C,
+                   "step": "dr_decode_attention (chunk partials + ordered merge) + fingerprint",
+                   "step_algorithmic_bytes": step_bytes},
+        "roofline": {"bound": "hbm", "kernel": "dr_decode_attention call (decode_partial_kernel, decode_merge_kernel)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("dr_decode_attention", name, source_digest("decode.hip", "device.h")),
+                     "algorithmic_bytes_per_launch": call_bytes, "avg_launch_ms": round(det_ms, 4),
+                     **extra_roofline},
+        "phases_ms": {k: round(v, 4) for k, v in ph.items()},
+        **extras,
+    }
+    if want_cpu:
+        res["cpu_baseline"] = _cpu_decode(oracle, inp, cpu_seconds)
+    return res
+
+
+def _cpu_decode(oracle, inp, seconds):
+    """The oracle on the first sequences of the same batch, its numpy products
+    held to one thread."""
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        return _cpu_decode_1(oracle, inp, seconds)
+
+
+def _cpu_decode_1(oracle, inp, seconds):
+    import dataclasses
+    t0 = time.perf_counter()
+    oracle.decode_attention(inp.q[:1], inp.k[:1], inp.v[:1], inp.lens[:1], inp.scale)
+    dt = max(time.perf_counter() - t0, 1e-6)
+    budget = seconds / dt * max(int(inp.lens[0]), 1)       # cached tokens the oracle gets through in `seconds`
+    m = max(1, min(inp.B, int(np.searchsorted(np.cumsum(inp.lens), budget))))
+    _log(f"cpu baseline: oracle decode attention on the first {m} of {inp.B} sequences")
+    sub = dataclasses.replace(inp, B=m, q=inp.q[:m], k=inp.k[:m], v=inp.v[:m], lens=inp.lens[:m])
+    t0 = time.perf_counter()
+    oracle.decode_attention(sub.q, sub.k, sub.v, sub.lens, sub.scale)
+    el = time.perf_counter() - t0
+    kv = int(sub.lens.astype(np.int64).sum()) * inp.Hkv * inp.D * 4
+    return {"value": round(kv / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {m} of {inp.B} sequences ({int(sub.lens.sum())} cached tokens), KV bytes only, "
+                      f"{el:.1f} s", "seconds": round(el, 2)}
 
 
 def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only):

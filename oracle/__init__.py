@@ -291,9 +291,9 @@ def decode_attention(q, k_cache, v_cache, seq_lens, scale: float):
         if a.dtype == np.uint16:
             a = (a.astype(np.uint32) << 16).view(np.float32)
         return a.astype(np.float64)
-    q, kc, vc = f64(q), f64(k_cache), f64(v_cache)
+    q = f64(q)
     B, Hq, D = q.shape
-    Hkv = kc.shape[2]
+    Hkv = np.asarray(k_cache).shape[2]
     g = Hq // Hkv
     out = np.zeros((B, Hq, D))
     A = np.zeros((B, Hq, D))
@@ -301,8 +301,9 @@ def decode_attention(q, k_cache, v_cache, seq_lens, scale: float):
         L = int(seq_lens[b])
         if L == 0:
             continue
+        kc, vc = f64(k_cache[b, :L]), f64(v_cache[b, :L])   # one sequence's cached rows
         for h in range(Hq):
-            kk, vv = kc[b, :L, h // g], vc[b, :L, h // g]
+            kk, vv = kc[:, h // g], vc[:, h // g]
             s_ = scale * (kk @ q[b, h])
             p_ = np.exp(s_ - s_.max())
             p_ /= p_.sum()

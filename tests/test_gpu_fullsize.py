@@ -137,3 +137,28 @@ def test_splitk_full(dr):
     assert np.all(err <= 1e-4 * A), float((err / A).max())
     again = dr.dr_splitk_reduce(dr.dr_splitk_gemm_tn(X, dY, inp.splits))
     assert dr.fingerprint_value(again) == dr.fingerprint_value(dW)
+
+
+def test_decode_attention_full(dr):
+    """The bench's decode batch (64 sequences up to 16384 tokens, 32/8 heads)
+    at its 512-token KV chunk: sampled sequences against the oracle within the
+    derived bound, and two of them run alone give the same bits."""
+    from tests.test_gpu_decode import check_against_oracle
+    import dataclasses
+    say("decode_attention full: generating inputs")
+    inp = workloads.make("decode_attention")
+    q, k, v = dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v)
+    lens = dev(inp.lens)
+    chunk = 512
+    say("decode_attention full: batch")
+    got = host(dr.dr_decode_attention(q, k, v, lens, inp.scale, chunk))
+    sample = [0, int(np.argmax(inp.lens)), int(np.argmin(inp.lens)), 17, 40, inp.B - 1]
+    for b in sample:
+        sub = dataclasses.replace(inp, B=1, q=inp.q[b:b + 1], k=inp.k[b:b + 1], v=inp.v[b:b + 1],
+                                  lens=inp.lens[b:b + 1])
+        check_against_oracle(sub, got[b:b + 1], chunk)
+    for b in sample[:2]:
+        say(f"decode_attention full: sequence {b} alone")
+        one = host(dr.dr_decode_attention(q[b:b + 1].contiguous(), k[b:b + 1].contiguous(), v[b:b + 1].contiguous(),
+                                          lens[b:b + 1].contiguous(), inp.scale, chunk))
+        assert_bits_equal(one[0], got[b], f"sequence {b} alone")
