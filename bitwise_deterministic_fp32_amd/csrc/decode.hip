@@ -22,7 +22,10 @@
 // is walked in blocks of 16 tokens, block j going to wave j % 4.  Scores come
 // from v_mfma_f32_16x16x32_bf16: the 16 tokens are the rows, the G query heads
 // of the KV head (padded to 16) the columns, head_dim the contraction, so the
-// bf16 products are exact and only their fp32 accumulation rounds.  Weights
+// bf16 products are exact and only their fp32 accumulation rounds.  Key and
+// value rows are both read as whole 256-byte rows, four tokens per wave
+// instruction (streaming loads: the cache is read once); the key block then
+// passes through the wave's own LDS tile to reach the MFMA operand layout.  Weights
 // are 2^(t - m) with t = score * scale * log2(e) and m the running maximum.
 // The weighted value sum runs on the vector ALU: lane (g, c) holds value
 // columns 8c .. 8c + 7 of tokens 4g .. 4g + 3 of each block, for every head.
@@ -62,12 +65,15 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const uint16_t
     static_assert(G >= 1 && G <= 16, "heads per KV head");
     __shared__ float wm[kWaves][G], wl[kWaves][G];
     __shared__ float wo[kWaves][G][kDim];
+    __shared__ __align__(16) uint16_t ks[kWaves][kBlockTokens][kDim + 8];
 
     const uint32_t id = blockIdx.x;
-    const uint32_t c = id % (uint32_t)sh.num_chunks;
-    const uint32_t bk = id / (uint32_t)sh.num_chunks;
-    const uint32_t kvh = bk % (uint32_t)sh.num_kv_heads;
-    const uint32_t b = bk / (uint32_t)sh.num_kv_heads;
+    // the KV heads of one chunk are neighbouring workgroups, so that the
+    // rows of a token (all heads side by side) are read at about one time
+    const uint32_t kvh = id % (uint32_t)sh.num_kv_heads;
+    const uint32_t bc = id / (uint32_t)sh.num_kv_heads;
+    const uint32_t c = bc % (uint32_t)sh.num_chunks;
+    const uint32_t b = bc / (uint32_t)sh.num_chunks;
     const int32_t L = seq_lens[b];
     if (L < 0 || L > sh.max_seq_len) return;  // reported by the merge
     const int32_t t_begin = (int32_t)c * sh.kv_chunk;
@@ -100,13 +106,14 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const uint16_t
         for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
 
     for (int32_t t0 = t_begin + w * kBlockTokens; t0 < t_end; t0 += kWaves * kBlockTokens) {
-        // keys: MFMA A operand, row = token t0 + col, elements 32 s + 8 grp
-        const int32_t tk = t0 + col;
-        u32x4 kr[4];
+        // keys: loaded like the values (tokens t0 + 4 grp + i, 16 bytes at column 8 col), then
+        // rearranged through LDS into the MFMA A layout (row = token t0 + col, elements 32 s + 8 grp)
+        u32x4 kl[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            kr[s] = u32x4{0u, 0u, 0u, 0u};
-            if (tk < t_end) kr[s] = load16(kbase + (int64_t)tk * tok_stride + 32 * s + 8 * grp);
+        for (int i = 0; i < 4; ++i) {
+            const int32_t tv = t0 + 4 * grp + i;
+            kl[i] = u32x4{0u, 0u, 0u, 0u};
+            if (tv < t_end) kl[i] = load16_stream(kbase + (int64_t)tv * tok_stride + 8 * col);
         }
         // values: tokens t0 + 4 grp + i, columns 8 col .. 8 col + 7
         u32x4 vr[4];
@@ -114,8 +121,15 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const uint16_t
         for (int i = 0; i < 4; ++i) {
             const int32_t tv = t0 + 4 * grp + i;
             vr[i] = u32x4{0u, 0u, 0u, 0u};
-            if (tv < t_end) vr[i] = load16(vbase + (int64_t)tv * tok_stride + 8 * col);
+            if (tv < t_end) vr[i] = load16_stream(vbase + (int64_t)tv * tok_stride + 8 * col);
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(&ks[w][4 * grp + i][8 * col]) = kl[i];
+        __builtin_amdgcn_wave_barrier();
+        u32x4 kr[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) kr[s] = *reinterpret_cast<const u32x4*>(&ks[w][col][32 * s + 8 * grp]);
+        __builtin_amdgcn_wave_barrier();
         f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s) sacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[s]), qb[s], sacc, 0, 0, 0);
