@@ -238,16 +238,38 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(const float
     }
     const float2* mlr = ml + bh * sh.num_chunks;
     const float2* por = reinterpret_cast<const float2*>(po + bh * sh.num_chunks * kDim) + lane;
+    // the maximum over the chunks (exact in any order), lane c reading chunk c
     float M = -__builtin_inff();
-    for (int32_t c = 0; c < nc; ++c) M = fmaxf(M, mlr[c].x);
+    for (int32_t c0 = 0; c0 < nc; c0 += 64)
+        if (c0 + lane < nc) M = fmaxf(M, mlr[c0 + lane].x);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    // then the sums in chunk order: lane c holds chunk c's factor 2^(m_c - M)
+    // and weight sum, and every lane adds its two output columns
     float l = 0.f, ox = 0.f, oy = 0.f;
-    for (int32_t c = 0; c < nc; ++c) {
-        const float2 mc = mlr[c];
-        const float f = exp2_hw(mc.x - M);
-        const float2 pc = por[(int64_t)c * (kDim / 2)];
-        l = __builtin_fmaf(mc.y, f, l);
-        ox = __builtin_fmaf(pc.x, f, ox);
-        oy = __builtin_fmaf(pc.y, f, oy);
+    for (int32_t c0 = 0; c0 < nc; c0 += 64) {
+        float f = 0.f, lc = 0.f;
+        if (c0 + lane < nc) {
+            const float2 mc = mlr[c0 + lane];
+            f = exp2_hw(mc.x - M);
+            lc = mc.y;
+        }
+        const int32_t n = min(64, nc - c0);
+        for (int32_t j0 = 0; j0 < n; j0 += 8) {
+            float2 pc[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                pc[j] = j0 + j < n ? por[(int64_t)(c0 + j0 + j) * (kDim / 2)] : make_float2(0.f, 0.f);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (j0 + j < n) {
+                    const float fj = __shfl(f, j0 + j), lj = __shfl(lc, j0 + j);
+                    l = __builtin_fmaf(lj, fj, l);
+                    ox = __builtin_fmaf(pc[j].x, fj, ox);
+                    oy = __builtin_fmaf(pc[j].y, fj, oy);
+                }
+            }
+        }
     }
     *dst = make_float2(ox / l, oy / l);
 }
