@@ -8,9 +8,10 @@ sparse_attn_dk / embedding_grad: a step is dr_index_add (stable sort of the
   known a step early) is reported beside it.
 splitk_mhc: a step is dr_splitk_gemm_tn (64 private fp32 partials by bf16
   MFMA), dr_splitk_reduce in split-id order, and dr_fingerprint of dW.
-decode_attention: a step is dr_decode_attention (chunk partials over the KV
-  cache with a fixed 512-token partition, then the merge in chunk order) and
-  dr_fingerprint of the output.
+decode_attention: a step is dr_decode_attention (chunk partials over the
+  head-major KV cache with a fixed 512-token partition, then the merge in
+  chunk order) and dr_fingerprint of the output.  The token-major layout is
+  timed beside it.
 """
 from __future__ import annotations
 
@@ -134,8 +135,10 @@ def _decode(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only):
     inp = workloads.make(name)
     B, Lmax, Hq, Hkv, D, C = inp.B, inp.Lmax, inp.Hq, inp.Hkv, inp.D, DECODE_KV_CHUNK
     q = torch.from_numpy(inp.q.view(np.int16)).view(torch.bfloat16).cuda()
-    k = torch.from_numpy(inp.k.view(np.int16)).view(torch.bfloat16).cuda()
-    v = torch.from_numpy(inp.v.view(np.int16)).view(torch.bfloat16).cuda()
+    k_tok = torch.from_numpy(inp.k.view(np.int16)).view(torch.bfloat16).cuda()
+    v_tok = torch.from_numpy(inp.v.view(np.int16)).view(torch.bfloat16).cuda()
+    k = k_tok.permute(0, 2, 1, 3).contiguous()   # head-major [B, Hkv, Lmax, D]
+    v = v_tok.permute(0, 2, 1, 3).contiguous()
     lens = torch.from_numpy(inp.lens).cuda()
     out = torch.empty(B, Hq, D, dtype=torch.float32, device="cuda")
     ws = torch.empty(dr.dr_decode_attention_workspace_size(B, Hq, Lmax, C), dtype=torch.uint8, device="cuda")
@@ -146,8 +149,8 @@ def _decode(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only):
     step_bytes = call_bytes + B * Hq * D * 4
     timer = _Timer(torch, ["decode_attention", "fingerprint"])
 
-    def call(chunk=C, o=out, w=ws):
-        dr.dr_decode_attention(q, k, v, lens, inp.scale, chunk, out=o, ws=w, dev_status=status)
+    def call(chunk=C, o=out, w=ws, kk=k, vv=v, hm=True):
+        dr.dr_decode_attention(q, kk, vv, lens, inp.scale, chunk, head_major=hm, out=o, ws=w, dev_status=status)
 
     def step(evs=None):
         if evs: evs[0].record()
@@ -183,10 +186,17 @@ def _decode(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only):
         for _ in range(warmup):
             call(serial, o2, ws_s)
         legs["one_workgroup_per_sequence_head_ms"] = round(_timed(torch, steps, lambda: call(serial, o2, ws_s)), 4)
+        # the token-major layout of the same cache (same bits)
+        for _ in range(warmup):
+            call(C, o2, ws, k_tok, v_tok, False)
+        legs["token_major_layout_ms"] = round(_timed(torch, steps, lambda: call(C, o2, ws, k_tok, v_tok, False)), 4)
+        torch.cuda.synchronize()
+        if not torch.equal(o2.view(torch.int32), out.view(torch.int32)):
+            raise RuntimeError("token-major and head-major layouts gave different bits")
         # one long sequence alone: fixed chunks against the heuristic's choice for a batch of one
         L1 = int(inp.lens.max())
         b1 = int(np.argmax(inp.lens))
-        q1, k1, v1 = q[b1:b1 + 1].contiguous(), k[b1:b1 + 1].contiguous(), v[b1:b1 + 1].contiguous()
+        q1, k1, v1 = q[b1:b1 + 1].contiguous(), k[b1:b1 + 1].contiguous(), v[b1:b1 + 1].contiguous()  # head-major
         l1 = lens[b1:b1 + 1].contiguous()
         o1 = torch.empty(1, Hq, D, dtype=torch.float32, device="cuda")
         occ1 = dr.dr_decode_attention_occupancy_chunk(1, Hkv, Lmax)
@@ -194,9 +204,10 @@ def _decode(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only):
             w1 = torch.empty(dr.dr_decode_attention_workspace_size(1, Hq, Lmax, c1), dtype=torch.uint8,
                              device="cuda")
             for _ in range(warmup):
-                dr.dr_decode_attention(q1, k1, v1, l1, inp.scale, c1, out=o1, ws=w1)
+                dr.dr_decode_attention(q1, k1, v1, l1, inp.scale, c1, head_major=True, out=o1, ws=w1)
             legs[f"single_sequence_L{L1}_chunk{c1}_ms"] = round(
-                _timed(torch, steps, lambda: dr.dr_decode_attention(q1, k1, v1, l1, inp.scale, c1, out=o1, ws=w1)), 4)
+                _timed(torch, steps, lambda: dr.dr_decode_attention(q1, k1, v1, l1, inp.scale, c1, head_major=True,
+                                                                    out=o1, ws=w1)), 4)
         extras = {"cold_cache_ms_per_call": round(ms_cold, 4), "partition_legs": legs,
                   "overhead_vs_occupancy_chunk": round(det_ms / legs["occupancy_chunk_ms"] - 1, 4)}
         extra_roofline = cold_roofline(call_bytes, ms_cold)
@@ -205,9 +216,10 @@ def _decode(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only):
         "ms_per_step": ms_step,
         "value": step_bytes / (ms_step * 1e-3) / 1e9,
         "config": {"workload": f"{name}: {B} sequences, lengths U[1,{Lmax}] (total {int(inp.lens.sum())} tokens), "
-                               f"{Hq} query / {Hkv} KV heads, head dim {D}, bf16 KV cache, fp32 output, "
-                               f"KV chunk {C}",
+                               f"{Hq} query / {Hkv} KV heads, head dim {D}, bf16 head-major KV cache "
+                               f"[{B},{Hkv},{Lmax},{D}], fp32 output, KV chunk {C}",
                    "batch": B, "max_seq_len": Lmax, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "kv_chunk": C,
+                   "kv_layout": "head-major",
                    "step": "dr_decode_attention (chunk partials + ordered merge) + fingerprint",
                    "step_algorithmic_bytes": step_bytes},
         "roofline": {"bound": "hbm", "kernel": "dr_decode_attention call (decode_partial_kernel, decode_merge_kernel)",

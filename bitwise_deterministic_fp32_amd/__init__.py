@@ -75,7 +75,8 @@ def _load() -> ctypes.CDLL:
         "dr_grouped_splitk_reduce": ([vp, i64, vp, i32, i64, vp, vp, vp], ctypes.c_int),
         "dr_permute_rows": ([vp, i64, i64, vp, vp, i64, i32, vp, vp, vp], ctypes.c_int),
         "dr_decode_attention_workspace_size": ([i64, i32, i32, i32, i64], sz),
-        "dr_decode_attention": ([vp, vp, vp, vp, vp, i64, i32, i32, i64, i32, ctypes.c_float, i32, vp, sz, vp, vp],
+        "dr_decode_attention": ([vp, vp, vp, vp, ctypes.c_int, vp, i64, i32, i32, i64, i32, ctypes.c_float, i32, vp, sz,
+                                 vp, vp],
                                 ctypes.c_int),
         "dr_decode_attention_occupancy_chunk": ([i64, i32, i32], i32),
         "dr_fingerprint_workspace_size": ([i64], sz),
@@ -376,23 +377,28 @@ def dr_decode_attention_workspace_size(batch: int, num_q_heads: int, max_seq_len
     return int(lib.dr_decode_attention_workspace_size(batch, num_q_heads, max_seq_len, kv_chunk, head_dim))
 
 
-def dr_decode_attention(q, k_cache, v_cache, seq_lens, scale: float, kv_chunk: int, *, out=None, ws=None,
-                        dev_status=None, stream=None):
-    """Decode attention of q [B, Hq, D] (bf16) over the caches [B, Lmax, Hkv, D] (bf16) with a fixed KV
-    partition of kv_chunk tokens; returns fp32 [B, Hq, D]."""
+DR_KV_TOKEN_MAJOR, DR_KV_HEAD_MAJOR = 0, 1
+
+
+def dr_decode_attention(q, k_cache, v_cache, seq_lens, scale: float, kv_chunk: int, *, head_major: bool = False,
+                        out=None, ws=None, dev_status=None, stream=None):
+    """Decode attention of q [B, Hq, D] (bf16) over the caches (bf16; [B, Lmax, Hkv, D], or [B, Hkv, Lmax, D]
+    with head_major) with a fixed KV partition of kv_chunk tokens; returns fp32 [B, Hq, D]."""
     for t, name in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
         _dev(t, name, (torch.bfloat16,))
     _dev(seq_lens, "seq_lens", (torch.int32,))
     if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
-        raise ValueError("q must be [B, Hq, D] and the caches [B, Lmax, Hkv, D] of one shape")
+        raise ValueError("q must be [B, Hq, D] and the caches 4-D of one shape")
     B, Hq, D = q.shape
-    Lmax, Hkv = k_cache.shape[1], k_cache.shape[2]
+    Lmax, Hkv = (k_cache.shape[2], k_cache.shape[1]) if head_major else (k_cache.shape[1], k_cache.shape[2])
     if k_cache.shape[0] != B or k_cache.shape[3] != D or seq_lens.numel() != B:
         raise ValueError("batch or head_dim mismatch")
     out = out if out is not None else torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
     ws = ws if ws is not None else _workspace(dr_decode_attention_workspace_size(B, Hq, Lmax, kv_chunk, D), q.device)
-    _check(lib.dr_decode_attention(_p(out), _p(q), _p(k_cache), _p(v_cache), _p(seq_lens), B, Hq, Hkv, D, Lmax,
-                                   float(scale), kv_chunk, _p(ws), ws.numel(), _p(dev_status), _stream(stream)),
+    layout = DR_KV_HEAD_MAJOR if head_major else DR_KV_TOKEN_MAJOR
+    _check(lib.dr_decode_attention(_p(out), _p(q), _p(k_cache), _p(v_cache), layout, _p(seq_lens), B, Hq, Hkv, D,
+                                   Lmax, float(scale), kv_chunk, _p(ws), ws.numel(), _p(dev_status),
+                                   _stream(stream)),
            "dr_decode_attention")
     return out
 

@@ -713,10 +713,12 @@ size_t dr_decode_attention_workspace_size(int64_t batch, int32_t num_q_heads, in
 }
 
 dr_status dr_decode_attention(float* out, const void* q, const void* k_cache, const void* v_cache,
-                              const int32_t* seq_lens, int64_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                              int64_t head_dim, int32_t max_seq_len, float scale, int32_t kv_chunk, void* ws,
-                              size_t ws_bytes, int32_t* dev_status, hipStream_t stream) {
+                              dr_kv_layout kv_layout, const int32_t* seq_lens, int64_t batch, int32_t num_q_heads,
+                              int32_t num_kv_heads, int64_t head_dim, int32_t max_seq_len, float scale,
+                              int32_t kv_chunk, void* ws, size_t ws_bytes, int32_t* dev_status, hipStream_t stream) {
     const char* what = "dr_decode_attention";
+    if (kv_layout != DR_KV_TOKEN_MAJOR && kv_layout != DR_KV_HEAD_MAJOR)
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: unknown KV cache layout %d", what, (int)kv_layout);
     if (!decode_shape_ok(batch, num_q_heads, num_kv_heads, head_dim, max_seq_len, kv_chunk))
         return fail(DR_ERR_INVALID_ARGUMENT,
                     "%s: need head_dim 128, num_q_heads / num_kv_heads in {1, 2, 4, 8, 16}, "
@@ -740,7 +742,8 @@ dr_status dr_decode_attention(float* out, const void* q, const void* k_cache, co
     float* po = reinterpret_cast<float*>(base + (size_t)slots * sizeof(float2));
     DR_TRY_HIP(dr::launch_decode_attention(out, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k_cache),
                                            static_cast<const uint16_t*>(v_cache), seq_lens, batch, num_q_heads,
-                                           num_kv_heads, max_seq_len, scale, kv_chunk, ml, po, dev_status, stream),
+                                           num_kv_heads, max_seq_len, kv_layout == DR_KV_HEAD_MAJOR, scale, kv_chunk,
+                                           ml, po, dev_status, stream),
                "decode attention launch");
     return ok();
 }

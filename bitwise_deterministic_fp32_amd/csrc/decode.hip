@@ -14,8 +14,9 @@
 // grid.  With kv_chunk at least the sequence length the whole sequence runs in
 // one workgroup, the pages' one-processor serial prefix.
 //
-// Layouts: q [B, Hq, 128] bf16; k and v caches [B, Lmax, Hkv, 128] bf16 (a
-// token's row of one KV head is 256 contiguous bytes); out [B, Hq, 128] fp32.
+// Layouts: q [B, Hq, 128] bf16; k and v caches bf16, token-major
+// [B, Lmax, Hkv, 128] or head-major [B, Hkv, Lmax, 128] (either way a token's
+// row of one KV head is 256 contiguous bytes); out [B, Hq, 128] fp32.
 // Query head h reads KV head h / G, G = Hq / Hkv (grouped-query attention).
 //
 // One workgroup (4 waves) computes one (sequence, KV head, chunk).  The chunk
@@ -47,6 +48,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 struct DecodeShape {
     int32_t num_q_heads, num_kv_heads, max_seq_len, kv_chunk, num_chunks;  // num_chunks = slots per sequence
+    int64_t seq_stride, head_stride, tok_stride;  // cache elements between sequences, KV heads, tokens
 };
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -82,9 +84,9 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const uint16_t
 
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int col = lane & 15, grp = lane >> 4;
-    const int64_t tok_stride = (int64_t)sh.num_kv_heads * kDim;  // elements from one token to the next
-    const uint16_t* kbase = kc + ((int64_t)b * sh.max_seq_len * sh.num_kv_heads + kvh) * kDim;
-    const uint16_t* vbase = vc + ((int64_t)b * sh.max_seq_len * sh.num_kv_heads + kvh) * kDim;
+    const int64_t tok_stride = sh.tok_stride;
+    const uint16_t* kbase = kc + (int64_t)b * sh.seq_stride + (int64_t)kvh * sh.head_stride;
+    const uint16_t* vbase = vc + (int64_t)b * sh.seq_stride + (int64_t)kvh * sh.head_stride;
 
     // MFMA B operand: column = query head col (zero past G), contraction
     // elements 32 s + 8 grp .. + 7 in step s.
@@ -291,11 +293,14 @@ int64_t decode_num_chunks(int32_t max_seq_len, int32_t kv_chunk) {
 
 hipError_t launch_decode_attention(float* out, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                    const int32_t* seq_lens, int64_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                                   int32_t max_seq_len, float scale, int32_t kv_chunk, float2* ml, float* po,
-                                   int32_t* status, hipStream_t s) {
+                                   int32_t max_seq_len, bool head_major, float scale, int32_t kv_chunk, float2* ml,
+                                   float* po, int32_t* status, hipStream_t s) {
     if (batch == 0) return hipSuccess;
+    const int64_t seq = (int64_t)max_seq_len * num_kv_heads * kDim;
     const DecodeShape sh{num_q_heads, num_kv_heads, max_seq_len, kv_chunk,
-                         (int32_t)decode_num_chunks(max_seq_len, kv_chunk)};
+                         (int32_t)decode_num_chunks(max_seq_len, kv_chunk), seq,
+                         head_major ? (int64_t)max_seq_len * kDim : kDim,
+                         head_major ? kDim : (int64_t)num_kv_heads * kDim};
     hipError_t e = hipSuccess;
     switch (num_q_heads / num_kv_heads) {
         case 1: e = launch_partial_g<1>(q, k, v, seq_lens, batch, sh, scale, ml, po, s); break;

@@ -167,8 +167,8 @@ hipError_t launch_fingerprint_final(const uint64_t* block_partials, int64_t nblo
 int64_t decode_num_chunks(int32_t max_seq_len, int32_t kv_chunk);
 hipError_t launch_decode_attention(float* out, const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                    const int32_t* seq_lens, int64_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                                   int32_t max_seq_len, float scale, int32_t kv_chunk, float2* ml, float* po,
-                                   int32_t* status, hipStream_t s);
+                                   int32_t max_seq_len, bool head_major, float scale, int32_t kv_chunk, float2* ml,
+                                   float* po, int32_t* status, hipStream_t s);
 int64_t combine_fp_blocks(dr_dtype dt, int64_t hidden, int64_t T, int32_t k);
 
 }  // namespace dr

@@ -75,6 +75,12 @@ typedef enum dr_status {
 
 typedef enum dr_dtype { DR_F32 = 0, DR_BF16 = 1 } dr_dtype;
 
+/* KV cache layouts of dr_decode_attention. */
+typedef enum dr_kv_layout {
+    DR_KV_TOKEN_MAJOR = 0, /* [batch, max_seq_len, num_kv_heads, head_dim] */
+    DR_KV_HEAD_MAJOR = 1   /* [batch, num_kv_heads, max_seq_len, head_dim] */
+} dr_kv_layout;
+
 /* Launch shape overrides, for tests of launch invariance.  A zero field keeps
  * the library default.  The setting is thread-local. */
 typedef struct dr_launch_params {
@@ -343,8 +349,11 @@ dr_status dr_permute_rows(const void* rows, int64_t row_bytes, int64_t num_rows,
  *
  *   out          OUT fp32 [batch, num_q_heads, head_dim], 16-byte aligned.
  *   q            bf16 [batch, num_q_heads, head_dim].
- *   k_cache, v_cache  bf16 [batch, max_seq_len, num_kv_heads, head_dim]; rows
- *                at or past a sequence's length are never read.
+ *   k_cache, v_cache  bf16, laid out as kv_layout says: token-major
+ *                [batch, max_seq_len, num_kv_heads, head_dim] or head-major
+ *                [batch, num_kv_heads, max_seq_len, head_dim].  Rows at or past
+ *                a sequence's length are never read.  Both layouts give the
+ *                same bits.
  *   seq_lens     int32 [batch], 0 <= seq_lens[b] <= max_seq_len.  A length
  *                outside that range ORs an index error bit into *dev_status
  *                (when given) and that sequence's output rows are not written.
@@ -357,9 +366,9 @@ dr_status dr_permute_rows(const void* rows, int64_t row_bytes, int64_t num_rows,
 size_t dr_decode_attention_workspace_size(int64_t batch, int32_t num_q_heads, int32_t max_seq_len, int32_t kv_chunk,
                                           int64_t head_dim);
 dr_status dr_decode_attention(float* out, const void* q, const void* k_cache, const void* v_cache,
-                              const int32_t* seq_lens, int64_t batch, int32_t num_q_heads, int32_t num_kv_heads,
-                              int64_t head_dim, int32_t max_seq_len, float scale, int32_t kv_chunk, void* ws,
-                              size_t ws_bytes, int32_t* dev_status, hipStream_t stream);
+                              dr_kv_layout kv_layout, const int32_t* seq_lens, int64_t batch, int32_t num_q_heads,
+                              int32_t num_kv_heads, int64_t head_dim, int32_t max_seq_len, float scale,
+                              int32_t kv_chunk, void* ws, size_t ws_bytes, int32_t* dev_status, hipStream_t stream);
 
 /* The kv_chunk an occupancy-driven split-KV heuristic would pick for this batch
  * on the current device: enough chunks to give every compute unit two

@@ -189,7 +189,8 @@ def test_grouped_splitk_and_permute_reject_bad_arguments(lib):
 
 def test_decode_attention_rejects_bad_arguments(lib):
     f = lib.dr_decode_attention
-    f.argtypes = [ctypes.c_void_p] * 5 + [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+    f.argtypes = [ctypes.c_void_p] * 4 + [ctypes.c_int, ctypes.c_void_p] + [ctypes.c_int64, ctypes.c_int32,
+                                                                             ctypes.c_int32, ctypes.c_int64,
                                           ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_void_p,
                                           ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p]
     ws_size = lib.dr_decode_attention_workspace_size
@@ -200,12 +201,13 @@ def test_decode_attention_rejects_bad_arguments(lib):
     assert ws_size(4, 32, 1000, 100, 128) == 0 and ws_size(4, 32, 1000, 256, 64) == 0
 
     def call(**kw):
-        a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, lens=FAKE, B=4, hq=32, hkv=8, D=128, L=1000, scale=0.1,
+        a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, layout=0, lens=FAKE, B=4, hq=32, hkv=8, D=128, L=1000, scale=0.1,
                  chunk=256, ws=FAKE, ws_bytes=need, status=None)
         a.update(kw)
-        return f(a["out"], a["q"], a["k"], a["v"], a["lens"], a["B"], a["hq"], a["hkv"], a["D"], a["L"], a["scale"],
-                 a["chunk"], a["ws"], a["ws_bytes"], a["status"], None)
+        return f(a["out"], a["q"], a["k"], a["v"], a["layout"], a["lens"], a["B"], a["hq"], a["hkv"], a["D"], a["L"],
+                 a["scale"], a["chunk"], a["ws"], a["ws_bytes"], a["status"], None)
     assert call(D=64) == DR_ERR_INVALID_ARGUMENT               # head_dim 128 only
+    assert call(layout=2) == DR_ERR_INVALID_ARGUMENT           # unknown cache layout
     assert call(hq=24) == DR_ERR_INVALID_ARGUMENT              # 24 / 8 = 3 heads per KV head
     assert call(hq=20, hkv=6) == DR_ERR_INVALID_ARGUMENT       # not a multiple
     assert call(chunk=96) == DR_ERR_INVALID_ARGUMENT           # not a multiple of 64

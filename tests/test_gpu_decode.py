@@ -83,6 +83,10 @@ DECODE_CASES = [
 ]
 
 
+def head_major(t):
+    return t.permute(0, 2, 1, 3).contiguous()
+
+
 @pytest.mark.parametrize("B,Lmax,Hq,Hkv,lens,kv_chunk", DECODE_CASES)
 def test_decode_attention_matches_oracle(dr, B, Lmax, Hq, Hkv, lens, kv_chunk):
     say(f"decode B={B} Lmax={Lmax} Hq={Hq} Hkv={Hkv} lens={lens} chunk={kv_chunk}")
@@ -91,6 +95,9 @@ def test_decode_attention_matches_oracle(dr, B, Lmax, Hq, Hkv, lens, kv_chunk):
     got = host(dr.dr_decode_attention(q, k, v, L, inp.scale, kv_chunk))
     worst = check_against_oracle(inp, got, kv_chunk)
     say(f"  worst |err| / A = {worst:.3g}")
+    # the head-major cache layout gives the same bits
+    hm = host(dr.dr_decode_attention(q, head_major(k), head_major(v), L, inp.scale, kv_chunk, head_major=True))
+    assert_bits_equal(hm, got, "head-major layout")
 
 
 def test_decode_attention_is_batch_invariant(dr):
@@ -115,6 +122,10 @@ def test_decode_attention_is_batch_invariant(dr):
     big = host(dr.dr_decode_attention(q, torch.cat([k, pad], 1).contiguous(), torch.cat([v, pad], 1).contiguous(),
                                       L, inp.scale, chunk))
     assert_bits_equal(big, full, "capacity 2500")
+    say("  head-major layout, larger capacity")
+    bigh = host(dr.dr_decode_attention(q, head_major(torch.cat([k, pad], 1)), head_major(torch.cat([v, pad], 1)), L,
+                                       inp.scale, chunk, head_major=True))
+    assert_bits_equal(bigh, full, "head-major, capacity 2500")
     say("  repeated runs")
     h0 = dr.fingerprint_value(torch.from_numpy(full).cuda())
     for _ in range(3):

@@ -157,6 +157,11 @@ def test_decode_attention_full(dr):
         sub = dataclasses.replace(inp, B=1, q=inp.q[b:b + 1], k=inp.k[b:b + 1], v=inp.v[b:b + 1],
                                   lens=inp.lens[b:b + 1])
         check_against_oracle(sub, got[b:b + 1], chunk)
+    say("decode_attention full: head-major layout")
+    kh, vh = k.permute(0, 2, 1, 3).contiguous(), v.permute(0, 2, 1, 3).contiguous()
+    hm = host(dr.dr_decode_attention(q, kh, vh, lens, inp.scale, chunk, head_major=True))
+    assert_bits_equal(hm, got, "head-major layout")
+    del kh, vh
     for b in sample[:2]:
         say(f"decode_attention full: sequence {b} alone")
         one = host(dr.dr_decode_attention(q[b:b + 1].contiguous(), k[b:b + 1].contiguous(), v[b:b + 1].contiguous(),
