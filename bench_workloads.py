@@ -79,6 +79,21 @@ def _timed(torch, steps, fn):
     return start.elapsed_time(stop) / steps
 
 
+def graph_ms(torch, fn, steps: int, warmup: int) -> float:
+    """Per-step time of fn captured once in a HIP graph and replayed `steps`
+    times (the library's calls launch only kernels on the current stream, so
+    they capture whole; the replays cost no host launch time)."""
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(warmup):
+        g.replay()
+    ms = _timed(torch, steps, g.replay)
+    del g
+    return ms
+
+
 def cold_ms(torch, fn, reps: int = 10, flush_mib: int = 1024) -> float:
     """Median time of one call with the caches cold: before each call an
     untimed read of 1 GiB (four times the 256 MB Infinity Cache) evicts L2
@@ -163,9 +178,13 @@ def _decode(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only):
         step()
     dr.dr_read_status(status)
     _log(f"{name}: timing {steps} steps")
-    ms_step = _timed(torch, steps, lambda: step(timer.step()))
+    eager_ms = _timed(torch, steps, lambda: step(timer.step()))
     ph = timer.mean_ms()
     det_ms = ph["decode_attention"]
+    h0 = int(fp.item())
+    ms_step = graph_ms(torch, step, steps, warmup)
+    if int(fp.item()) != h0:
+        raise RuntimeError("graph replays of the decode step changed its output")
     extras, extra_roofline = {}, {}
     if not step_only:
         ms_cold = cold_ms(torch, call)
@@ -215,6 +234,8 @@ def _decode(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only):
     res = {
         "ms_per_step": ms_step,
         "value": step_bytes / (ms_step * 1e-3) / 1e9,
+        "timing": "step replayed from a HIP graph; eager_ms_per_step with HIP events between the calls",
+        "eager_ms_per_step": round(eager_ms, 4),
         "config": {"workload": f"{name}: {B} sequences, lengths U[1,{Lmax}] (total {int(inp.lens.sum())} tokens), "
                                f"{Hq} query / {Hkv} KV heads, head dim {D}, bf16 head-major KV cache "
                                f"[{B},{Hkv},{Lmax},{D}], fp32 output, KV chunk {C}",
@@ -292,9 +313,11 @@ def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only)
         step()
     dr.dr_workspace_status(ws)
     _log(f"{name}: timing {steps} steps")
-    ms_step = _timed(torch, steps, lambda: step(timer.step()))
+    eager_ms = _timed(torch, steps, lambda: step(timer.step()))
     ph = timer.mean_ms()
     det_ms = ph["index_add"]
+    ms_step = graph_ms(torch, step, steps, warmup)
+    dr.dr_workspace_status(ws)
     extras, extra_roofline = {}, {}
     if not step_only:
         ms_cold = cold_ms(torch, step)
@@ -329,6 +352,8 @@ def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only)
     res = {
         "ms_per_step": ms_step,
         "value": step_bytes / (ms_step * 1e-3) / 1e9,
+        "timing": "step replayed from a HIP graph; eager_ms_per_step with HIP events between the calls",
+        "eager_ms_per_step": round(eager_ms, 4),
         "config": {"workload": f"{name}: index_add of {n} bf16 rows of width {H} into {D} fp32 rows "
                                f"({touched} touched, longest segment {int(counts.max())})",
                    "n": n, "num_dests": D, "hidden": H, "touched_rows": touched,
@@ -424,9 +449,13 @@ def _splitk(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only):
     for _ in range(warmup):
         step()
     _log(f"{name}: timing {steps} steps")
-    ms_step = _timed(torch, steps, lambda: step(timer.step()))
+    eager_ms = _timed(torch, steps, lambda: step(timer.step()))
     ph = timer.mean_ms()
     g_ms = ph["splitk_gemm"]
+    h0 = int(fp.item())
+    ms_step = graph_ms(torch, step, steps, warmup)
+    if int(fp.item()) != h0:
+        raise RuntimeError("graph replays of the split-K step changed its output")
     det_ms = ph["splitk_gemm"] + ph["splitk_reduce"]
     extras, extra_roofline = {}, {}
     if not step_only:
@@ -480,6 +509,8 @@ def _splitk(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only):
     res = {
         "ms_per_step": ms_step,
         "value": step_bytes / (ms_step * 1e-3) / 1e9,
+        "timing": "step replayed from a HIP graph; eager_ms_per_step with HIP events between the calls",
+        "eager_ms_per_step": round(eager_ms, 4),
         "config": {"workload": f"{name}: dW = X^T dY, X bf16 [{K},{M}], dY bf16 [{K},{N}], {S} splits",
                    "K": K, "M": M, "N": N, "splits": S,
                    "step": "MFMA partials + ordered split reduce + fingerprint", "step_algorithmic_bytes": step_bytes},
