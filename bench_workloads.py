@@ -1,11 +1,13 @@
 """bench.py's steps for the index_add and split-K configurations.
 
-sparse_attn_dk / embedding_grad: a step is dr_index_add (stable sort of the
-  contributions by destination, tile plan, ordered segmented reduction,
-  destination update) followed by dr_fingerprint of the destination.  The
-  destination keeps accumulating from step to step; resetting it is not part of
-  the method.  The reused-plan time (sort done once, as when the indices are
-  known a step early) is reported beside it.
+sparse_attn_dk / embedding_grad: a step is dr_index_add_fingerprinted (stable
+  sort of the contributions by destination, tile plan, ordered segmented
+  reduction, destination update), which also moves the destination's
+  fingerprint by the change of the rows it rewrites.  The destination keeps
+  accumulating from step to step; resetting it is not part of the method.  The
+  same step with dr_index_add and a full dr_fingerprint of the destination, and
+  the reused-plan time (sort done once, as when the indices are known a step
+  early), are reported beside it.
 splitk_mhc: a step is dr_splitk_gemm_tn (64 private fp32 partials by bf16
   MFMA), dr_splitk_reduce in split-id order, and dr_fingerprint of dW.
 decode_attention: a step is dr_decode_attention (chunk partials over the
@@ -25,6 +27,7 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 HBM_PEAK_GBS = 8000.0
+MASK64 = (1 << 64) - 1  # fingerprints are unsigned; torch holds them as int64
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 
 
@@ -296,31 +299,46 @@ def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only)
     touched = int((counts > 0).sum())
     red_bytes = n * H * 2 + n * 4 + 2 * touched * H * 4     # contributions, index, RMW of touched rows
     fp_bytes = D * H * 4
-    step_bytes = red_bytes + fp_bytes
+    step_bytes = red_bytes  # the fingerprint update reads nothing the reduction does not already hold
     ws = torch.empty(dr.dr_index_add_workspace_size(n, D, H), dtype=torch.uint8, device="cuda")
     fp = torch.empty(1, dtype=torch.int64, device="cuda")
     ws_fp = torch.empty(dr.dr_fingerprint_workspace_size(fp_bytes), dtype=torch.uint8, device="cuda")
-    timer = _Timer(torch, ["index_add", "fingerprint"])
+    timer = _Timer(torch, ["index_add_fingerprinted"])
+    dr.dr_fingerprint(out, out=fp, ws=ws_fp)  # the destination's fingerprint, kept current from here on
 
     def step(evs=None):
         if evs: evs[0].record()
-        dr.dr_index_add(out, src, index, ws=ws)
+        dr.dr_index_add_fingerprinted(out, src, index, fp, ws=ws)
         if evs: evs[1].record()
-        dr.dr_fingerprint(out, out=fp, ws=ws_fp)
-        if evs: evs[2].record()
 
     for _ in range(warmup):
         step()
     dr.dr_workspace_status(ws)
+    torch.cuda.synchronize()
+    if int(fp.item()) & MASK64 != dr.fingerprint_value(out):
+        raise RuntimeError("the incremental fingerprint differs from the fingerprint of the destination")
     _log(f"{name}: timing {steps} steps")
     eager_ms = _timed(torch, steps, lambda: step(timer.step()))
     ph = timer.mean_ms()
-    det_ms = ph["index_add"]
+    det_ms = ph["index_add_fingerprinted"]
     ms_step = graph_ms(torch, step, steps, warmup)
     dr.dr_workspace_status(ws)
+    torch.cuda.synchronize()
+    if int(fp.item()) & MASK64 != dr.fingerprint_value(out):
+        raise RuntimeError("the incremental fingerprint drifted during the graph replays")
     extras, extra_roofline = {}, {}
     if not step_only:
         ms_cold = cold_ms(torch, step)
+
+        # the step with the plain call and a full fingerprint of the destination
+        def full_step():
+            dr.dr_index_add(out, src, index, ws=ws)
+            dr.dr_fingerprint(out, out=fp, ws=ws_fp)
+
+        for _ in range(warmup):
+            full_step()
+        ms_full = graph_ms(torch, full_step, steps, warmup)
+        ms_plain = _timed(torch, steps, lambda: dr.dr_index_add(out, src, index, ws=ws))
 
         # reused plan: sort once, then only the plan + ordered reduction each step
         perm, seg, _ = dr.dr_sort_by_dest(index, D, want_inv=False)
@@ -337,12 +355,14 @@ def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only)
         ms_atomic = _timed(torch, steps, lambda: dr.dr_index_add_atomic(out, src, index))
 
         fused = _fused_dk(torch, dr, steps, warmup) if name == "sparse_attn_dk" else None
-        ia_cold = cold_ms(torch, lambda: dr.dr_index_add(out, src, index, ws=ws))
+        ia_cold = cold_ms(torch, lambda: dr.dr_index_add_fingerprinted(out, src, index, fp, ws=ws))
         extras = {
             "cold_cache_ms_per_step": round(ms_cold, 4),
+            "plain_index_add_ms": round(ms_plain, 4),
+            "step_with_full_fingerprint_ms": round(ms_full, 4),
             "reused_plan_ms": round(ms_plan, 4), "sort_only_ms": round(ms_sort, 4),
-            "overhead_vs_atomic": {"deterministic_ms": round(det_ms, 4), "atomic_ms": round(ms_atomic, 4),
-                                   "overhead": round(det_ms / ms_atomic - 1, 4),
+            "overhead_vs_atomic": {"deterministic_ms": round(ms_plain, 4), "atomic_ms": round(ms_atomic, 4),
+                                   "overhead": round(ms_plain / ms_atomic - 1, 4),
                                    "overhead_reused_plan": round(ms_plan / ms_atomic - 1, 4)},
         }
         if fused:
@@ -357,13 +377,16 @@ def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only)
         "config": {"workload": f"{name}: index_add of {n} bf16 rows of width {H} into {D} fp32 rows "
                                f"({touched} touched, longest segment {int(counts.max())})",
                    "n": n, "num_dests": D, "hidden": H, "touched_rows": touched,
-                   "step": "dr_index_add (sort + plan + ordered reduce + update) + fingerprint",
+                   "step": "dr_index_add_fingerprinted (sort + plan + ordered reduce + update, fingerprint kept "
+                           "current from the rewritten rows)",
                    "step_algorithmic_bytes": step_bytes},
-        "roofline": {"bound": "hbm", "kernel": "dr_index_add call (sort, plan, segreduce, tilecombine)",
+        "roofline": {"bound": "hbm", "kernel": "dr_index_add_fingerprinted call (sort, plan, segreduce, tilecombine, "
+                                               "fingerprint update)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("dr_index_add", name,
-                                                 source_digest("sort.hip", "segreduce.hip", "internal.h", "device.h")),
+                     "traffic": measured_traffic("dr_index_add_fingerprinted", name,
+                                                 source_digest("sort.hip", "segreduce.hip", "fingerprint.hip",
+                                                               "internal.h", "device.h")),
                      "algorithmic_bytes_per_launch": red_bytes, "avg_launch_ms": round(det_ms, 4),
                      **extra_roofline},
         "phases_ms": {k: round(v, 4) for k, v in ph.items()},

@@ -20,7 +20,7 @@ __all__ = [
     "dr_status_string", "dr_last_error", "dr_version", "dr_set_launch_params",
     "dr_sort_workspace_size", "dr_sort_by_dest",
     "dr_combine", "dr_combine_atomic", "dr_combine_fingerprinted_workspace_size", "dr_combine_fingerprinted",
-    "dr_index_add_workspace_size", "dr_index_add", "dr_index_add_atomic",
+    "dr_index_add_workspace_size", "dr_index_add", "dr_index_add_fingerprinted", "dr_index_add_atomic",
     "dr_sparse_attn_dk_workspace_size", "dr_sparse_attn_dk",
     "dr_splitk_gemm_tn", "dr_splitk_gemm_tn_atomic", "dr_splitk_reduce",
     "dr_grouped_splitk_max_slots", "dr_grouped_splitk_workspace_size", "dr_grouped_splitk_gemm_tn",
@@ -63,6 +63,7 @@ def _load() -> ctypes.CDLL:
                                      ctypes.c_int),
         "dr_index_add_workspace_size": ([i64, i32, i64], sz),
         "dr_index_add": ([vp, i32, i64, vp, ctypes.c_int, i64, vp, vp, vp, vp, sz, vp], ctypes.c_int),
+        "dr_index_add_fingerprinted": ([vp, i32, i64, vp, ctypes.c_int, i64, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "dr_index_add_atomic": ([vp, i32, i64, vp, ctypes.c_int, i64, vp, vp, vp], ctypes.c_int),
         "dr_sparse_attn_dk_workspace_size": ([i64, i32, i32, i64], sz),
         "dr_sparse_attn_dk": ([vp, i32, i64, vp, ctypes.c_int, vp, vp, i64, i32, vp, vp, vp, sz, vp], ctypes.c_int),
@@ -246,6 +247,26 @@ def dr_index_add(out, src, index, *, perm=None, seg_offsets=None, ws=None, strea
     ws = ws if ws is not None else _workspace(dr_index_add_workspace_size(n, D, H), out.device)
     _check(lib.dr_index_add(_p(out), D, H, _p(src), _DTYPES[src.dtype], n, _p(index), _p(perm), _p(seg_offsets),
                             _p(ws), ws.numel(), _stream(stream)), "dr_index_add")
+    return out, ws
+
+
+def dr_index_add_fingerprinted(out, src, index, inout_hash, *, perm=None, seg_offsets=None, ws=None, stream=None):
+    """dr_index_add that moves inout_hash (an int64 device tensor of one element holding the fingerprint of
+    out) to the fingerprint of the updated out.  Returns (out, ws)."""
+    _dev(out, "out", (torch.float32,))
+    _dev(src, "src", tuple(_DTYPES))
+    _dev(index, "index", (torch.int32,))
+    _dev(inout_hash, "inout_hash", (torch.int64,))
+    if inout_hash.numel() != 1:
+        raise ValueError("inout_hash must hold one element")
+    D, H = out.shape
+    n = index.numel()
+    if src.shape != (n, H):
+        raise ValueError(f"src must be [{n}, {H}], got {tuple(src.shape)}")
+    ws = ws if ws is not None else _workspace(dr_index_add_workspace_size(n, D, H), out.device)
+    _check(lib.dr_index_add_fingerprinted(_p(out), D, H, _p(src), _DTYPES[src.dtype], n, _p(index), _p(perm),
+                                          _p(seg_offsets), _p(inout_hash), _p(ws), ws.numel(), _stream(stream)),
+           "dr_index_add_fingerprinted")
     return out, ws
 
 

@@ -194,7 +194,11 @@ struct IndexAddBuffers {
     dr::TileRec* tiles;
     dr::MultiRec* multis;
     float* partials;
+    uint64_t* fp_parts;  // fingerprint changes: segreduce's workgroups, then tilecombine's
 };
+
+// The persistent reduce grids hold at most this many workgroups each.
+constexpr int64_t kMaxReduceGrid = 65536;
 
 IndexAddBuffers carve_index_add(Carver& c, int64_t n, int32_t num_dests, int64_t hidden, bool sort_inside,
                                 int tc_log2, int sort_tile_log2) {
@@ -210,6 +214,7 @@ IndexAddBuffers carve_index_add(Carver& c, int64_t n, int32_t num_dests, int64_t
     b.tiles = c.take<dr::TileRec>(pb.tiles);
     b.multis = c.take<dr::MultiRec>(pb.multis);
     b.partials = c.take<float>(pb.pslots * hidden);
+    b.fp_parts = c.take<uint64_t>(2 * kMaxReduceGrid);
     return b;
 }
 
@@ -443,7 +448,7 @@ struct Contributions {
 
 dr_status run_index_add(const char* what, float* out, int32_t num_dests, int64_t hidden, const Contributions& c,
                         int64_t n, const int32_t* index, const int32_t* perm, const int32_t* seg_offsets, void* ws,
-                        size_t ws_bytes, hipStream_t stream) {
+                        size_t ws_bytes, uint64_t* inout_hash, hipStream_t stream) {
     if (!out || !aligned(out, 16)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: out must be non-null and 16-byte aligned", what);
     if (num_dests < 1) return fail(DR_ERR_INVALID_ARGUMENT, "%s: num_dests must be >= 1", what);
     if (n < 0 || n >= kMaxN) return fail(DR_ERR_INVALID_ARGUMENT, "%s: n must be in [0, 2^31)", what);
@@ -484,11 +489,18 @@ dr_status run_index_add(const char* what, float* out, int32_t num_dests, int64_t
     DR_TRY_HIP(dr::launch_plan_write(seg, num_dests, lc.tile_chunks_log2, b.block_sums, b.tiles, b.multis, b.status,
                                      stream),
                "plan write launch");
+    const int64_t grid = dr::persistent_grid();
+    uint64_t* fp_seg = inout_hash ? b.fp_parts : nullptr;
+    uint64_t* fp_tc = inout_hash ? b.fp_parts + grid : nullptr;
     DR_TRY_HIP(dr::launch_segreduce(out, hidden, c.src, c.dtype, n, p, b.tiles, b.partials, lc.tile_chunks_log2,
-                                    lc.chunks_in_flight, c.scale, c.rows_per_src, b.status, stream),
+                                    lc.chunks_in_flight, c.scale, c.rows_per_src, b.status, fp_seg, stream),
                "segmented reduce launch");
-    DR_TRY_HIP(dr::launch_tilecombine(out, hidden, b.partials, b.multis, n, lc.tile_chunks_log2, b.status, stream),
+    DR_TRY_HIP(dr::launch_tilecombine(out, hidden, b.partials, b.multis, n, lc.tile_chunks_log2, b.status, fp_tc,
+                                      stream),
                "tile combine launch");
+    if (inout_hash)
+        DR_TRY_HIP(dr::launch_fingerprint_update(b.fp_parts, 2 * grid, b.status, inout_hash, stream),
+                   "fingerprint update launch");
     return ok();
 }
 
@@ -502,7 +514,21 @@ dr_status dr_index_add(float* out, int32_t num_dests, int64_t hidden, const void
     if (st != DR_OK) return st;
     if ((st = check_rows(src, src_dtype, hidden, what)) != DR_OK) return st;
     return run_index_add(what, out, num_dests, hidden, Contributions{src, src_dtype, nullptr, 1}, n, index, perm,
-                         seg_offsets, ws, ws_bytes, stream);
+                         seg_offsets, ws, ws_bytes, nullptr, stream);
+}
+
+dr_status dr_index_add_fingerprinted(float* out, int32_t num_dests, int64_t hidden, const void* src,
+                                     dr_dtype src_dtype, int64_t n, const int32_t* index, const int32_t* perm,
+                                     const int32_t* seg_offsets, uint64_t* inout_hash, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+    const char* what = "dr_index_add_fingerprinted";
+    dr_status st = check_dtype(src_dtype, what);
+    if (st != DR_OK) return st;
+    if ((st = check_rows(src, src_dtype, hidden, what)) != DR_OK) return st;
+    if (!inout_hash || !aligned(inout_hash, 8))
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: inout_hash must be a non-null, 8-byte aligned device pointer", what);
+    return run_index_add(what, out, num_dests, hidden, Contributions{src, src_dtype, nullptr, 1}, n, index, perm,
+                         seg_offsets, ws, ws_bytes, inout_hash, stream);
 }
 
 size_t dr_sparse_attn_dk_workspace_size(int64_t num_queries, int32_t topk, int32_t num_keys, int64_t head_dim) {
@@ -525,7 +551,7 @@ dr_status dr_sparse_attn_dk(float* dK, int32_t num_keys, int64_t head_dim, const
     const int64_t n = num_queries * (int64_t)topk;
     if (n > 0 && (!dS || !aligned(dS, 4))) return fail(DR_ERR_INVALID_ARGUMENT, "%s: dS must be non-null and 4-byte aligned", what);
     return run_index_add(what, dK, num_keys, head_dim, Contributions{Q, q_dtype, dS, topk}, n, key_idx, perm,
-                         seg_offsets, ws, ws_bytes, stream);
+                         seg_offsets, ws, ws_bytes, nullptr, stream);
 }
 
 dr_status dr_index_add_atomic(float* out, int32_t num_dests, int64_t hidden, const void* src, dr_dtype src_dtype,

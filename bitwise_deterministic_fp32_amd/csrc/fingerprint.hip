@@ -151,6 +151,26 @@ hipError_t launch_fingerprint_final(const uint64_t* block_partials, int64_t nblo
     return hipGetLastError();
 }
 
+// An incremental update: the reduce kernels that rewrite destination pieces
+// leave the change of those pieces' terms (new minus old), one sum per
+// workgroup; the fingerprint of the whole tensor moves by their total.
+__global__ __launch_bounds__(kWideThreads) void fp_update_kernel(const uint64_t* __restrict__ parts, int64_t nparts,
+                                                                 const int32_t* __restrict__ status,
+                                                                 uint64_t* __restrict__ hash) {
+    __shared__ uint64_t smem[kWideThreads / 64];
+    if (status[kWordStatus] != 0) return;  // the call failed closed: its destination and hash stay as they were
+    uint64_t acc = 0;
+    for (int64_t i = threadIdx.x; i < nparts; i += kWideThreads) acc += parts[i];
+    const uint64_t s = block_sum_u64(acc, smem);
+    if (threadIdx.x == 0) *hash += s;
+}
+
+hipError_t launch_fingerprint_update(const uint64_t* parts, int64_t nparts, const int32_t* status, uint64_t* hash,
+                                     hipStream_t s) {
+    hipLaunchKernelGGL(fp_update_kernel, dim3(1), dim3(kWideThreads), 0, s, parts, nparts, status, hash);
+    return hipGetLastError();
+}
+
 hipError_t launch_fingerprint(const void* data, int64_t nbytes, uint64_t* out, uint64_t* block_partials,
                               hipStream_t s) {
     const int64_t nb = fingerprint_blocks(nbytes);

@@ -117,9 +117,15 @@ hipError_t launch_plan_validate(const int32_t* perm, const int32_t* seg, const i
 hipError_t launch_segreduce(float* out, int64_t hidden, const void* src, dr_dtype src_dtype, int64_t n,
                             const int32_t* perm, const TileRec* tiles, float* partials, int tile_chunks_log2,
                             int chunks_in_flight, const float* scale, int32_t rows_per_src, int32_t* status,
-                            hipStream_t s);
+                            uint64_t* fp_part, hipStream_t s);
 hipError_t launch_tilecombine(float* out, int64_t hidden, const float* partials, const MultiRec* multis, int64_t n,
-                              int tile_chunks_log2, int32_t* status, hipStream_t s);
+                              int tile_chunks_log2, int32_t* status, uint64_t* fp_part, hipStream_t s);
+// Workgroups of the persistent reduce kernels (segreduce, tilecombine); with
+// fp_part each of them writes one fingerprint change there.
+unsigned persistent_grid();
+// hash += sum of nparts fingerprint changes, unless the status word is set.
+hipError_t launch_fingerprint_update(const uint64_t* parts, int64_t nparts, const int32_t* status, uint64_t* hash,
+                                     hipStream_t s);
 
 // combine
 // fp_partials != nullptr: also hash the written output (one partial per workgroup)

@@ -267,6 +267,16 @@ __device__ __forceinline__ u32x4 add4(const u32x4& old, const float* t) {
     return r;
 }
 
+// Change of the fingerprint terms of one 16-byte piece of the destination
+// (two 8-byte words starting at word index i) when old becomes now: the
+// fingerprint is a wrapping sum of position-keyed word terms, so rewriting
+// the piece adds exactly this to it.
+__device__ __forceinline__ uint64_t fp_delta(const u32x4& old, const u32x4& now, int64_t i) {
+    const uint64_t o0 = ((uint64_t)old.y << 32) | old.x, o1 = ((uint64_t)old.w << 32) | old.z;
+    const uint64_t n0 = ((uint64_t)now.y << 32) | now.x, n1 = ((uint64_t)now.w << 32) | now.z;
+    return (fp_term(n0, i) + fp_term(n1, i + 1)) - (fp_term(o0, i) + fp_term(o1, i + 1));
+}
+
 __device__ __forceinline__ u32x4 pack4(const float* t) {
     return u32x4{__float_as_uint(t[0]), __float_as_uint(t[1]), __float_as_uint(t[2]), __float_as_uint(t[3])};
 }
@@ -285,7 +295,7 @@ template <dr_dtype DT, int GROUP, int TCLOG, int CIF, bool GEN>
 __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
     float* __restrict__ out, int64_t H, const void* __restrict__ src, const int32_t* __restrict__ perm,
     const TileRec* __restrict__ tiles, float* __restrict__ partials, int64_t slices, int32_t* status,
-    const float* __restrict__ scale, uint32_t rows_per_src) {
+    const float* __restrict__ scale, uint32_t rows_per_src, uint64_t* __restrict__ fp_part) {
     using V = Vec<DT>;
     constexpr int E = V::kElems;  // columns of a lane
     constexpr int Q = E / 4;      // 16-byte fp32 pieces of a lane's output
@@ -299,6 +309,7 @@ __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
     const uint32_t ngroups = (gridDim.x * kReduceThreads) / GROUP;
     const char* src_bytes = reinterpret_cast<const char*>(src);
     const int64_t row_bytes = H * kElemBytes;
+    uint64_t fp_acc = 0;  // change of the destination's fingerprint made by this lane
     // the next item's tile record is fetched one item ahead
     TileRec tr_next{};
     if (group < items) tr_next = tiles[group / (uint32_t)slices];
@@ -401,13 +412,22 @@ __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
         if (active) {
             if (tr.pslot < 0) {
 #pragma unroll
-                for (int q = 0; q < Q; ++q) store16(orow + col + 4 * q, add4(old[q], t + 4 * q));
+                for (int q = 0; q < Q; ++q) {
+                    const u32x4 now = add4(old[q], t + 4 * q);
+                    store16(orow + col + 4 * q, now);
+                    if (fp_part) fp_acc += fp_delta(old[q], now, ((int64_t)tr.dest * H + col + 4 * q) >> 1);
+                }
             } else {
                 float* prow = partials + (int64_t)tr.pslot * H;
 #pragma unroll
                 for (int q = 0; q < Q; ++q) store16(prow + col + 4 * q, pack4(t + 4 * q));
             }
         }
+    }
+    if (fp_part) {
+        __shared__ uint64_t fsm[kReduceThreads / 64];
+        const uint64_t b = block_sum_u64(fp_acc, fsm);
+        if (threadIdx.x == 0) fp_part[blockIdx.x] = b;
     }
 }
 
@@ -418,8 +438,10 @@ template <int GROUP, int DEPTH>
 __global__ __launch_bounds__(kReduceThreads) void tilecombine_kernel(float* __restrict__ out, int64_t H,
                                                                      const float* __restrict__ partials,
                                                                      const MultiRec* __restrict__ multis,
-                                                                     int64_t slices, int32_t* status) {
+                                                                     int64_t slices, int32_t* status,
+                                                                     uint64_t* __restrict__ fp_part) {
     if (status[kWordStatus] != 0) return;
+    uint64_t fp_acc = 0;
     const uint32_t items = (uint32_t)status[kWordMultis] * (uint32_t)slices;
     const int lig = threadIdx.x % GROUP;
     const uint32_t group = (blockIdx.x * kReduceThreads + threadIdx.x) / GROUP;
@@ -450,7 +472,14 @@ __global__ __launch_bounds__(kReduceThreads) void tilecombine_kernel(float* __re
         }
         float t[4];
         tc.fold(t);
-        store16(orow + col, add4(old, t));
+        const u32x4 now = add4(old, t);
+        store16(orow + col, now);
+        if (fp_part) fp_acc += fp_delta(old, now, ((int64_t)mr.dest * H + col) >> 1);
+    }
+    if (fp_part) {
+        __shared__ uint64_t fsm[kReduceThreads / 64];
+        const uint64_t b = block_sum_u64(fp_acc, fsm);
+        if (threadIdx.x == 0) fp_part[blockIdx.x] = b;
     }
 }
 
@@ -463,11 +492,11 @@ int group_for(int64_t pieces) {
 template <dr_dtype DT, int GROUP, int CIF, bool GEN>
 hipError_t launch_segreduce_g(dim3 grid, float* out, int64_t H, const void* src, const int32_t* perm,
                               const TileRec* tiles, float* partials, int tc_log2, int64_t slices, int32_t* status,
-                              const float* scale, uint32_t rows_per_src, hipStream_t s) {
+                              const float* scale, uint32_t rows_per_src, uint64_t* fp_part, hipStream_t s) {
 #define DR_SEGREDUCE_CASE(TC)                                                                                  \
     case TC:                                                                                                   \
         hipLaunchKernelGGL((segreduce_kernel<DT, GROUP, TC, CIF, GEN>), grid, dim3(kReduceThreads), 0, s, out,  \
-                           H, src, perm, tiles, partials, slices, status, scale, rows_per_src);                \
+                           H, src, perm, tiles, partials, slices, status, scale, rows_per_src, fp_part);       \
         break;
     switch (tc_log2) {
         DR_SEGREDUCE_CASE(3)
@@ -482,13 +511,13 @@ hipError_t launch_segreduce_g(dim3 grid, float* out, int64_t H, const void* src,
     return hipGetLastError();
 }
 
+}  // namespace
+
 unsigned persistent_grid() {
     const Launch lc = launch_config();
     if (lc.grid_blocks > 0) return (unsigned)lc.grid_blocks;
     return (unsigned)(device_cu_count() * 16);
 }
-
-}  // namespace
 
 int64_t plan_blocks(int32_t num_dests) { return ((int64_t)num_dests + kPlanThreads - 1) / kPlanThreads; }
 
@@ -516,7 +545,7 @@ hipError_t launch_plan_validate(const int32_t* perm, const int32_t* seg, const i
 
 hipError_t launch_segreduce(float* out, int64_t hidden, const void* src, dr_dtype dt, int64_t n, const int32_t* perm,
                             const TileRec* tiles, float* partials, int tc_log2, int cif, const float* scale,
-                            int32_t rows_per_src, int32_t* status, hipStream_t s) {
+                            int32_t rows_per_src, int32_t* status, uint64_t* fp_part, hipStream_t s) {
     (void)n;
     const int64_t lanes = dt == DR_BF16 ? hidden / 8 : hidden / 4;  // lanes needed per row
     const int g = group_for(lanes);
@@ -527,11 +556,11 @@ hipError_t launch_segreduce(float* out, int64_t hidden, const void* src, dr_dtyp
 #define DR_SR(DT, G)                                                                                           \
     if (scale)                                                                                                 \
         return launch_segreduce_g<DT, G, 1, true>(grid, out, hidden, src, perm, tiles, partials, tc_log2,      \
-                                                  slices, status, scale, rps, s);                              \
+                                                  slices, status, scale, rps, fp_part, s);                     \
     return cif == 1 ? launch_segreduce_g<DT, G, 1, false>(grid, out, hidden, src, perm, tiles, partials,       \
-                                                          tc_log2, slices, status, nullptr, 1u, s)             \
+                                                          tc_log2, slices, status, nullptr, 1u, fp_part, s)    \
                     : launch_segreduce_g<DT, G, 2, false>(grid, out, hidden, src, perm, tiles, partials,       \
-                                                          tc_log2, slices, status, nullptr, 1u, s)
+                                                          tc_log2, slices, status, nullptr, 1u, fp_part, s)
     if (dt == DR_BF16) {
         if (g == 16) { DR_SR(DR_BF16, 16); }
         if (g == 32) { DR_SR(DR_BF16, 32); }
@@ -544,7 +573,7 @@ hipError_t launch_segreduce(float* out, int64_t hidden, const void* src, dr_dtyp
 }
 
 hipError_t launch_tilecombine(float* out, int64_t hidden, const float* partials, const MultiRec* multis, int64_t n,
-                              int tc_log2, int32_t* status, hipStream_t s) {
+                              int tc_log2, int32_t* status, uint64_t* fp_part, hipStream_t s) {
     const int64_t lanes = hidden / 4;
     const int g = group_for(lanes);
     const int64_t slices = (lanes + g - 1) / g;
@@ -555,7 +584,7 @@ hipError_t launch_tilecombine(float* out, int64_t hidden, const float* partials,
     while (depth < 62 && ((int64_t)1 << depth) <= max_tiles) ++depth;
 #define DR_TC(G, D)                                                                                             \
     hipLaunchKernelGGL((tilecombine_kernel<G, D>), grid, dim3(kReduceThreads), 0, s, out, hidden, partials, multis, \
-                       slices, status)
+                       slices, status, fp_part)
 #define DR_TC_DEPTH(G)        \
     if (depth <= 8) DR_TC(G, 8);  \
     else if (depth <= 16) DR_TC(G, 16); \

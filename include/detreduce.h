@@ -205,6 +205,23 @@ dr_status dr_index_add(float* out, int32_t num_dests, int64_t hidden, const void
                        int64_t n, const int32_t* index, const int32_t* perm, const int32_t* seg_offsets,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* dr_index_add that keeps the destination's fingerprint current.  The
+ * fingerprint (dr_fingerprint's definition) is a wrapping sum of position-keyed
+ * word terms, so rewriting a row changes it by the new terms minus the old
+ * ones.  The reduce kernels form that change from the values they already
+ * hold for the read-modify-write, and never read the untouched rows: a step's
+ * byte-wise check ("how to verify" in the bitwise-determinism interview note)
+ * costs the touched rows only.
+ *   inout_hash   device uint64: on entry dr_fingerprint of out as it is; on
+ *                return (stream order) dr_fingerprint of the updated out.
+ *                When the call fails closed, out and *inout_hash both stay
+ *                as they were.
+ * Other arguments as dr_index_add. */
+dr_status dr_index_add_fingerprinted(float* out, int32_t num_dests, int64_t hidden, const void* src,
+                                     dr_dtype src_dtype, int64_t n, const int32_t* index, const int32_t* perm,
+                                     const int32_t* seg_offsets, uint64_t* inout_hash, void* ws, size_t ws_bytes,
+                                     hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Sparse-attention key gradient with the contributions formed on the fly:
  *   dK[key] = dK[key] + T(fl32(dS[q][j] * Q[q]) over the (q, j) with

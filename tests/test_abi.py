@@ -44,7 +44,7 @@ def declared():
 def test_header_declares_the_entry_points():
     names = declared()
     for required in ("dr_sort_by_dest", "dr_combine", "dr_index_add", "dr_splitk_reduce", "dr_fingerprint",
-                     "dr_combine_fingerprinted", "dr_sparse_attn_dk", "dr_decode_attention",
+                     "dr_combine_fingerprinted", "dr_sparse_attn_dk", "dr_decode_attention", "dr_index_add_fingerprinted",
                      "dr_combine_atomic", "dr_index_add_atomic", "dr_splitk_gemm_tn", "dr_splitk_gemm_tn_atomic"):
         assert required in names
 
@@ -109,6 +109,15 @@ def test_index_add_rejects_bad_arguments(lib):
     # misaligned workspace or out
     assert f(FAKE, 64, 128, FAKE, 1, 1000, FAKE, None, None, FAKE + 4, need, None) == DR_ERR_INVALID_ARGUMENT
     assert f(FAKE + 4, 64, 128, FAKE, 1, 1000, FAKE, None, None, FAKE, need, None) == DR_ERR_INVALID_ARGUMENT
+    # the fingerprinted form also needs an aligned hash word
+    g = lib.dr_index_add_fingerprinted
+    g.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int64,
+                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_size_t, ctypes.c_void_p]
+    assert g(FAKE, 64, 128, FAKE, 1, 1000, FAKE, None, None, None, FAKE, need, None) == DR_ERR_INVALID_ARGUMENT
+    assert g(FAKE, 64, 128, FAKE, 1, 1000, FAKE, None, None, FAKE + 4, FAKE, need, None) == DR_ERR_INVALID_ARGUMENT
+    assert g(FAKE, 64, 128, FAKE, 1, 1000, FAKE, None, None, FAKE, FAKE, need - 1, None) == DR_ERR_WORKSPACE_TOO_SMALL
+    assert g(FAKE, 64, 130, FAKE, 0, 1000, FAKE, None, None, FAKE, FAKE, need, None) == DR_ERR_INVALID_ARGUMENT
 
 
 def test_sparse_attn_dk_rejects_bad_arguments(lib):

@@ -128,3 +128,26 @@ def test_splitk_graph(dr):
         assert_bits_equal(host(dW), want, f"replay {r}")
         dr.dr_splitk_gemm_tn(X[:256].contiguous(), dY[:256].contiguous(), 1)
         torch.cuda.synchronize()
+
+
+def test_index_add_fingerprinted_graph(dr):
+    """The destination's fingerprint stays current over eager calls and over graph replays."""
+    say("graph: index_add_fingerprinted, accumulating")
+    rng = np.random.default_rng(45)
+    n, D, H = 8000, 40000, 512
+    index = dev(np.minimum(rng.zipf(1.1, n) - 1, D - 1).astype(np.int32))
+    src = dev_bf16(workloads.normal_bf16(45, 1, n * H).reshape(n, H))
+    out = dev(workloads.normal_f32(45, 2, D * H).reshape(D, H))
+    h = torch.empty(1, dtype=torch.int64, device="cuda")
+    dr.dr_fingerprint(out, out=h)
+    ws = torch.empty(dr.dr_index_add_workspace_size(n, D, H), dtype=torch.uint8, device="cuda")
+    call = lambda: dr.dr_index_add_fingerprinted(out, src, index, h, ws=ws)
+    for i in range(8):
+        call()
+        torch.cuda.synchronize()
+        assert (int(h.item()) & ((1 << 64) - 1)) == dr.fingerprint_value(out), f"eager call {i}"
+    g = capture(call)
+    for r in range(6):
+        g.replay()
+        torch.cuda.synchronize()
+        assert (int(h.item()) & ((1 << 64) - 1)) == dr.fingerprint_value(out), f"replay {r}"

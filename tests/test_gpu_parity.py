@@ -173,6 +173,60 @@ def test_index_add_reused_plan(dr):
     assert_bits_equal(host(out), oracle.index_add(out0, src, index), "index_add with plan")
 
 
+def _hash_tensor(v: int):
+    return torch.tensor([v - (1 << 64) if v >= (1 << 63) else v], dtype=torch.int64, device="cuda")
+
+
+def _hash_value(t) -> int:
+    return int(t.item()) & ((1 << 64) - 1)
+
+
+@pytest.mark.parametrize("n,D,H,src_dtype,dist", [
+    (20001, 50, 128, "f32", "hot"),         # long segments: tile partials and tilecombine rewrite rows
+    (3000, 131072, 4096, "bf16", "zipf"),   # embedding-like: mostly singletons
+    (5000, 300, 136, "f32", "uniform"),     # ragged lane group
+    (4000, 2000, 24, "bf16", "zipf"),       # a row narrower than one lane group
+    (0, 70, 64, "f32", "uniform"),          # nothing to add: the hash stays
+])
+def test_index_add_fingerprinted_matches_oracle(dr, n, D, H, src_dtype, dist):
+    """The incremental fingerprint equals the oracle's fingerprint of the whole updated destination."""
+    say(f"index_add_fingerprinted n={n} D={D} H={H} {src_dtype} {dist}")
+    index, src, out0 = _index_add_case(n + D + H + 1, n, D, H, src_dtype, dist)
+    out = dev(out0.copy())
+    h = _hash_tensor(oracle.fingerprint(out0))
+    s = dev(src) if src_dtype == "f32" else dev_bf16(src)
+    _, ws = dr.dr_index_add_fingerprinted(out, s, dev(index), h)
+    dr.dr_workspace_status(ws)
+    want = oracle.index_add(out0, src, index)
+    assert_bits_equal(host(out), want, "index_add_fingerprinted")
+    assert _hash_value(h) == oracle.fingerprint(want)
+    # a reused plan and other launch shapes give the same hash; a second call keeps it current
+    perm, seg, _ = dr.dr_sort_by_dest(dev(index), D, want_inv=False)
+    if n == 0:
+        perm = seg = None  # an empty plan has no storage to pass
+    dr.dr_set_launch_params(grid_blocks=37, tile_chunks_log2=3)
+    try:
+        dr.dr_index_add_fingerprinted(out, s, dev(index), h, perm=perm, seg_offsets=seg)
+    finally:
+        dr.dr_set_launch_params(reset=True)
+    want2 = oracle.index_add(want, src, index)
+    assert_bits_equal(host(out), want2, "second call")
+    assert _hash_value(h) == oracle.fingerprint(want2) == dr.fingerprint_value(out)
+
+
+def test_index_add_fingerprinted_fails_closed(dr):
+    index, src, out0 = _index_add_case(77, 3000, 100, 64, "f32", "uniform")
+    index[1234] = 100  # out of range
+    out = dev(out0.copy())
+    h0 = oracle.fingerprint(out0)
+    h = _hash_tensor(h0)
+    _, ws = dr.dr_index_add_fingerprinted(out, dev(src), dev(index), h)
+    with pytest.raises(dr.DetReduceError):
+        dr.dr_workspace_status(ws)
+    assert_bits_equal(host(out), out0, "untouched")
+    assert _hash_value(h) == h0
+
+
 def test_index_add_order_example_fp32(dr):
     """old value added last: out0 = 1, contributions [x, x] -> 1 + 2^-23."""
     x = np.float32(3 * 2.0 ** -26)
