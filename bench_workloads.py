@@ -368,7 +368,16 @@ def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only)
         if fused:
             extras["fused_dk"] = fused
         extra_roofline = cold_roofline(red_bytes, ia_cold)
-    achieved = red_bytes / (det_ms * 1e-3) / 1e9
+    # the ordered reduction alone (segmented reduce + tile combine): events the library records around it
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for b_, e_ in pairs:
+        dr.dr_set_phase_events(b_, e_)
+        step()
+    dr.dr_set_phase_events()
+    torch.cuda.synchronize()
+    red_ms = float(np.mean([b_.elapsed_time(e_) for b_, e_ in pairs]))
+    achieved = red_bytes / (red_ms * 1e-3) / 1e9
+    call_achieved = red_bytes / (det_ms * 1e-3) / 1e9
     res = {
         "ms_per_step": ms_step,
         "value": step_bytes / (ms_step * 1e-3) / 1e9,
@@ -380,15 +389,23 @@ def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only)
                    "step": "dr_index_add_fingerprinted (sort + plan + ordered reduce + update, fingerprint kept "
                            "current from the rewritten rows)",
                    "step_algorithmic_bytes": step_bytes},
-        "roofline": {"bound": "hbm", "kernel": "dr_index_add_fingerprinted call (sort, plan, segreduce, tilecombine, "
-                                               "fingerprint update)",
+        "roofline": {"bound": "hbm",
+                     "kernel": "segreduce_kernel + tilecombine_kernel (the ordered reduction of the call)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("dr_index_add_fingerprinted", name,
-                                                 source_digest("sort.hip", "segreduce.hip", "fingerprint.hip",
-                                                               "internal.h", "device.h")),
-                     "algorithmic_bytes_per_launch": red_bytes, "avg_launch_ms": round(det_ms, 4),
-                     **extra_roofline},
+                     "traffic": measured_traffic("segreduce+tilecombine", name,
+                                                 source_digest("segreduce.hip", "internal.h", "device.h")),
+                     "algorithmic_bytes_per_launch": red_bytes, "avg_launch_ms": round(red_ms, 4),
+                     "timed_by": "events recorded by the library around the two kernels (dr_set_phase_events)",
+                     "whole_call": {"kernel": "dr_index_add_fingerprinted (sort, plan, segreduce, tilecombine, "
+                                              "fingerprint update)",
+                                    "achieved": round(call_achieved, 1), "frac": round(call_achieved / HBM_PEAK_GBS, 4),
+                                    "avg_launch_ms": round(det_ms, 4),
+                                    "traffic": measured_traffic("dr_index_add_fingerprinted", name,
+                                                                source_digest("sort.hip", "segreduce.hip",
+                                                                              "fingerprint.hip", "internal.h",
+                                                                              "device.h")),
+                                    **extra_roofline}},
         "phases_ms": {k: round(v, 4) for k, v in ph.items()},
         **extras,
     }

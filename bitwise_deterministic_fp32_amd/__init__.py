@@ -17,7 +17,7 @@ import torch
 
 __all__ = [
     "DetReduceError", "LIB_PATH", "lib", "declared_functions",
-    "dr_status_string", "dr_last_error", "dr_version", "dr_set_launch_params",
+    "dr_status_string", "dr_last_error", "dr_version", "dr_set_launch_params", "dr_set_phase_events",
     "dr_sort_workspace_size", "dr_sort_by_dest",
     "dr_combine", "dr_combine_atomic", "dr_combine_fingerprinted_workspace_size", "dr_combine_fingerprinted",
     "dr_index_add_workspace_size", "dr_index_add", "dr_index_add_fingerprinted", "dr_index_add_atomic",
@@ -54,6 +54,7 @@ def _load() -> ctypes.CDLL:
         "dr_last_error": ([], ctypes.c_char_p),
         "dr_version": ([], i32),
         "dr_set_launch_params": ([vp], ctypes.c_int),
+        "dr_set_phase_events": ([vp, vp], ctypes.c_int),
         "dr_sort_workspace_size": ([i64, i32, i32], sz),
         "dr_sort_by_dest": ([vp, vp, i32, i64, i32, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "dr_combine": ([vp, ctypes.c_int, i64, i64, vp, vp, i64, i32, vp, vp, vp], ctypes.c_int),
@@ -155,6 +156,18 @@ def dr_set_launch_params(grid_blocks: int = 0, tile_chunks_log2: int = 0, sort_t
         return
     p = _LaunchParams(grid_blocks, tile_chunks_log2, sort_tile_log2, chunks_in_flight)
     _check(lib.dr_set_launch_params(ctypes.byref(p)), "dr_set_launch_params")
+
+
+def dr_set_phase_events(reduce_begin=None, reduce_end=None) -> None:
+    """Thread-local hook: index_add-family calls record these torch.cuda.Events (enable_timing=True) around
+    their ordered reduction kernels.  No arguments turns it off."""
+    def handle(e):
+        if e is None:
+            return None
+        if not e.cuda_event:
+            e.record()  # torch creates the underlying event at its first record
+        return e.cuda_event
+    _check(lib.dr_set_phase_events(handle(reduce_begin), handle(reduce_end)), "dr_set_phase_events")
 
 
 def _workspace(nbytes: int, device) -> torch.Tensor:

@@ -16,6 +16,7 @@ namespace {
 
 thread_local std::string g_err;
 thread_local dr_launch_params g_params = {0, 0, 0, 0};
+thread_local hipEvent_t g_reduce_begin = nullptr, g_reduce_end = nullptr;  // dr_set_phase_events
 
 dr_status fail(dr_status s, const char* fmt, ...) {
     char buf[512];
@@ -287,6 +288,14 @@ const char* dr_last_error(void) { return g_err.c_str(); }
 
 int32_t dr_version(void) { return 100; }
 
+dr_status dr_set_phase_events(hipEvent_t reduce_begin, hipEvent_t reduce_end) {
+    if ((reduce_begin == nullptr) != (reduce_end == nullptr))
+        return fail(DR_ERR_INVALID_ARGUMENT, "dr_set_phase_events: give both events or neither");
+    g_reduce_begin = reduce_begin;
+    g_reduce_end = reduce_end;
+    return ok();
+}
+
 dr_status dr_set_launch_params(const dr_launch_params* p) {
     if (!p) {
         g_params = dr_launch_params{0, 0, 0, 0};
@@ -492,12 +501,14 @@ dr_status run_index_add(const char* what, float* out, int32_t num_dests, int64_t
     const int64_t grid = dr::persistent_grid();
     uint64_t* fp_seg = inout_hash ? b.fp_parts : nullptr;
     uint64_t* fp_tc = inout_hash ? b.fp_parts + grid : nullptr;
+    if (g_reduce_begin) DR_TRY_HIP(hipEventRecord(g_reduce_begin, stream), "phase event");
     DR_TRY_HIP(dr::launch_segreduce(out, hidden, c.src, c.dtype, n, p, b.tiles, b.partials, lc.tile_chunks_log2,
                                     lc.chunks_in_flight, c.scale, c.rows_per_src, b.status, fp_seg, stream),
                "segmented reduce launch");
     DR_TRY_HIP(dr::launch_tilecombine(out, hidden, b.partials, b.multis, n, lc.tile_chunks_log2, b.status, fp_tc,
                                       stream),
                "tile combine launch");
+    if (g_reduce_end) DR_TRY_HIP(hipEventRecord(g_reduce_end, stream), "phase event");
     if (inout_hash)
         DR_TRY_HIP(dr::launch_fingerprint_update(b.fp_parts, 2 * grid, b.status, inout_hash, stream),
                    "fingerprint update launch");

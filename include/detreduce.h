@@ -107,6 +107,15 @@ int32_t dr_version(void);
  * previous setting in place. */
 dr_status dr_set_launch_params(const dr_launch_params* p);
 
+/* Measurement hook (thread-local).  With two events set, every later
+ * index_add-family call on this thread (dr_index_add, dr_index_add_fingerprinted,
+ * dr_sparse_attn_dk) records reduce_begin on its stream just before its ordered
+ * reduction kernels (segmented reduce, tile combine) and reduce_end just after,
+ * so a caller can time the reduction apart from the sort and the plan.  The
+ * events stay owned by the caller.  Both NULL turns the hook off; one NULL is
+ * DR_ERR_INVALID_ARGUMENT. */
+dr_status dr_set_phase_events(hipEvent_t reduce_begin, hipEvent_t reduce_end);
+
 /* ------------------------------------------------------------------------
  * Stable sort of contributions by destination.
  *

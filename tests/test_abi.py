@@ -58,6 +58,14 @@ def test_library_exports_every_declared_symbol(lib):
         assert getattr(lib, n) is not None
 
 
+def test_phase_events_hook(lib):
+    f = lib.dr_set_phase_events
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    assert f(None, None) == DR_OK
+    assert f(FAKE, None) == DR_ERR_INVALID_ARGUMENT
+    assert f(None, FAKE) == DR_ERR_INVALID_ARGUMENT
+
+
 def test_status_strings(lib):
     for code in range(7):
         assert lib.dr_status_string(code).decode().startswith("DR_")
