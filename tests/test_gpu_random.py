@@ -117,3 +117,31 @@ def test_random_sparse_attn_dk_and_grouped(dr):
         for g in range(G):
             e, A = oracle.splitk_reference(inp.X[off[g]:off[g + 1]], inp.dY[off[g]:off[g + 1]])
             assert np.all(np.abs(host(dW)[g] - e) <= 1e-4 * A + 1e-30), (case, g)
+
+
+def test_random_decode_attention(dr):
+    """Random batches, head groupings, lengths, chunk sizes and cache layouts against the oracle within the
+    derived bound; each batch's first sequence alone must give the same bits."""
+    from tests.test_gpu_decode import check_against_oracle
+    rng = np.random.default_rng(2027)
+    for case in range(12):
+        B = int(rng.integers(1, 7))
+        G = int(rng.choice([1, 2, 4, 8, 16]))
+        Hkv = int(rng.integers(1, 5))
+        Lmax = int(rng.integers(1, 1500))
+        lens = rng.integers(0, Lmax + 1, B)
+        if rng.random() < 0.3:
+            lens[0] = Lmax
+        chunk = int(rng.choice([64, 128, 192, 512, 1024, 1 << 20]))
+        head_major = bool(rng.integers(0, 2))
+        say(f"decode random {case}: B={B} G={G} Hkv={Hkv} Lmax={Lmax} lens={lens.tolist()} chunk={chunk} "
+            f"head_major={head_major}")
+        inp = workloads.decode_inputs(3000 + case, B, Lmax, G * Hkv, Hkv, 128, lens)
+        q, k, v, L = dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v), dev(inp.lens)
+        if head_major:
+            k, v = k.permute(0, 2, 1, 3).contiguous(), v.permute(0, 2, 1, 3).contiguous()
+        got = host(dr.dr_decode_attention(q, k, v, L, inp.scale, chunk, head_major=head_major))
+        check_against_oracle(inp, got, chunk)
+        one = host(dr.dr_decode_attention(q[:1].contiguous(), k[:1].contiguous(), v[:1].contiguous(),
+                                          L[:1].contiguous(), inp.scale, chunk, head_major=head_major))
+        assert_bits_equal(one[0], got[0], f"case {case}: first sequence alone")
