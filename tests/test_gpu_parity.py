@@ -227,6 +227,22 @@ def test_index_add_fingerprinted_fails_closed(dr):
     assert _hash_value(h) == h0
 
 
+def test_phase_events_time_the_reduction(dr):
+    """The measurement hook records the caller's events around the reduction kernels and changes no bit."""
+    index, src, out0 = _index_add_case(91, 50000, 3000, 256, "bf16", "zipf")
+    want = oracle.index_add(out0, src, index)
+    out = dev(out0.copy())
+    b_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dr.dr_set_phase_events(b_, e_)
+    try:
+        _, ws = dr.dr_index_add(out, dev_bf16(src), dev(index))
+    finally:
+        dr.dr_set_phase_events()
+    dr.dr_workspace_status(ws)
+    assert_bits_equal(host(out), want, "index_add with phase events")
+    assert b_.elapsed_time(e_) > 0
+
+
 def test_index_add_order_example_fp32(dr):
     """old value added last: out0 = 1, contributions [x, x] -> 1 + 2^-23."""
     x = np.float32(3 * 2.0 ** -26)
