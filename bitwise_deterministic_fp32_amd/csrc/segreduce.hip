@@ -206,10 +206,14 @@ __global__ void plan_validate_kernel(const int32_t* __restrict__ perm, const int
 // Binary counter of subtree sums: level l holds a complete subtree of 2^l
 // leaves.  push() merges the new leaf with the filled levels below the first
 // empty one (left operand first) and stores it there; fold() combines the
-// remaining subtrees from the right.  This gives T for any leaf count.  The
-// code is branch-free with compile-time level indices (selects, no stores
-// under branches), which keeps the levels in registers.
-template <int DEPTH, int E>
+// remaining subtrees from the right.  This gives T for any leaf count.  Level
+// indices are compile-time, which keeps the levels in registers.  When the
+// count is the same in the whole wavefront (UNIFORM: one lane group per
+// wavefront), a level's additions run under a wave-uniform branch, so a push
+// or fold adds only at the levels it touches; otherwise every level is
+// computed and selected.  Stores into the levels stay selects either way.
+// Both forms perform the same additions in the same order.
+template <int DEPTH, int E, bool UNIFORM = false>
 struct TreeCounter {
     float level[DEPTH][E];
     uint32_t count = 0;
@@ -223,6 +227,23 @@ struct TreeCounter {
     }
 
     __device__ __forceinline__ void push(float (&s)[E]) {
+        if (UNIFORM) {
+            const int merges = __builtin_amdgcn_readfirstlane(__builtin_ctz(~count));
+#pragma unroll
+            for (int l = 0; l < DEPTH; ++l) {
+                if (l < merges) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) s[e] = level[l][e] + s[e];
+                }
+            }
+#pragma unroll
+            for (int l = 0; l < DEPTH; ++l) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) level[l][e] = l == merges ? s[e] : level[l][e];
+            }
+            ++count;
+            return;
+        }
         const int merges = __builtin_ctz(~count);  // carries of this increment
 #pragma unroll
         for (int l = 0; l < DEPTH; ++l) {
@@ -244,6 +265,18 @@ struct TreeCounter {
         bool have = false;
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[e] = neg_zero();
+        if (UNIFORM) {
+            const uint32_t c = __builtin_amdgcn_readfirstlane(count);
+#pragma unroll
+            for (int l = 0; l < DEPTH; ++l) {
+                if ((c >> l) & 1u) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[e] = have ? level[l][e] + acc[e] : level[l][e];
+                    have = true;
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int l = 0; l < DEPTH; ++l) {
             const bool bit = (count >> l) & 1u;
@@ -329,7 +362,7 @@ __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
 #pragma unroll
             for (int q = 0; q < Q; ++q) old[q] = load16(orow + lcol + 4 * q);
         }
-        TreeCounter<TCLOG + 1, E> tc;
+        TreeCounter<TCLOG + 1, E, GROUP == 64> tc;
         // CIF chunks (8*CIF rows) are loaded at once; slots past the tile's
         // end are neither loaded nor added.
         constexpr int R = 8 * CIF;
@@ -367,7 +400,8 @@ __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
             }
 #pragma unroll
             for (int c = 0; c < CIF; ++c) {
-                const int m = (int)min((int64_t)8, r_end - (r0 + 8 * c));  // rows of chunk c (<= 0: none)
+                int m = (int)min((int64_t)8, r_end - (r0 + 8 * c));  // rows of chunk c (<= 0: none)
+                if (GROUP == 64) m = __builtin_amdgcn_readfirstlane(m);  // one tile per wavefront
                 if (m > 0) {
                     float s[E];
                     V::widen(raw[8 * c], s);
@@ -386,6 +420,21 @@ __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
                             }
 #pragma unroll
                             for (int e = 0; e < E; ++e) s[e] = s[e] + v[e];
+                        }
+                    } else if (GROUP == 64) {
+                        // wave-uniform row count: the rows past it are skipped, not computed
+#pragma unroll
+                        for (int j = 1; j < 8; ++j) {
+                            if (j < m) {
+                                float v[E];
+                                V::widen(raw[8 * c + j], v);
+                                if (GEN) {
+#pragma unroll
+                                    for (int e = 0; e < E; ++e) v[e] = sc[8 * c + j] * v[e];
+                                }
+#pragma unroll
+                                for (int e = 0; e < E; ++e) s[e] = s[e] + v[e];
+                            }
                         }
                     } else {
 #pragma unroll
