@@ -91,6 +91,15 @@ def test_index_add_full(dr, name):
     out2 = out0.clone()
     dr.dr_index_add(out2, dev_bf16(inp.src), index, perm=perm, seg_offsets=seg)
     assert dr.fingerprint_value(out2) == dr.fingerprint_value(out)
+    # the bench's step: the fingerprinted call gives the same bytes and keeps the hash current, starting from
+    # the oracle's fingerprint of the initial destination
+    say(f"{name}: fingerprinted call")
+    out3 = out0.clone()
+    h0 = oracle.fingerprint(inp.out0)
+    h = torch.tensor([h0 - (1 << 64) if h0 >= (1 << 63) else h0], dtype=torch.int64, device="cuda")
+    dr.dr_index_add_fingerprinted(out3, dev_bf16(inp.src), index, h)
+    assert torch.equal(out3.view(torch.int32), out.view(torch.int32))
+    assert int(h.item()) & ((1 << 64) - 1) == dr.fingerprint_value(out)
 
 
 def test_sparse_attn_dk_fused_full(dr):
