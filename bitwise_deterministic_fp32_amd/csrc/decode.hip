@@ -1,6 +1,6 @@
 // Batch-invariant decode attention (DeepSeek-V4 book ch. 9, section 2.1).
 //
-// The pages reject split-KV decode whose partition of a sequence's keys
+// That chapter gives up split-KV decode, whose partition of a sequence's keys
 // follows the batch size and the occupancy: a different partition merges the
 // partial softmax sums in a different order, so the same token gets different
 // bits in different batches.  Here the partition is a fixed function of the
@@ -12,7 +12,7 @@
 // alone, so a sequence's output bits depend on its own query, cache rows,
 // length and kv_chunk, never on the other sequences, the batch size or the
 // grid.  With kv_chunk at least the sequence length the whole sequence runs in
-// one workgroup, the pages' one-processor serial prefix.
+// one workgroup, the chapter's one-processor serial prefix.
 //
 // Layouts: q [B, Hq, 128] bf16; k and v caches bf16, token-major
 // [B, Lmax, Hkv, 128] or head-major [B, Hkv, Lmax, 128] (either way a token's

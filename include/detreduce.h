@@ -359,7 +359,7 @@ dr_status dr_permute_rows(const void* rows, int64_t row_bytes, int64_t num_rows,
  * cached keys and values:
  *   out[b, h] = sum_j softmax_j(scale * q[b, h] . k[b, j, h / G]) v[b, j, h / G]
  * with G = num_q_heads / num_kv_heads query heads per KV head (grouped-query
- * attention); a sequence of length 0 gives zeros.  The pages give up split-KV
+ * attention); a sequence of length 0 gives zeros.  That chapter gives up split-KV
  * decoding because its partition of the keys, and with it the order in which
  * the partial softmax sums merge, follows the batch size and the occupancy.
  * Here the keys of a sequence are cut into chunks of kv_chunk tokens from its
@@ -369,7 +369,7 @@ dr_status dr_permute_rows(const void* rows, int64_t row_bytes, int64_t num_rows,
  * output bits therefore depend only on its own q, cache rows, length, scale and
  * kv_chunk: not on the other sequences, the batch size, its position in the
  * batch or the device's size.  kv_chunk >= the sequence length runs the whole
- * sequence serially in one workgroup, the pages' single-processor prefix.
+ * sequence serially in one workgroup, the chapter's single-processor prefix.
  * Scores are exact bf16 products summed in fp32 (matrix cores); weights are
  * 2^(t - max) with t = score * scale * log2(e) in fp32.
  *
@@ -399,7 +399,7 @@ dr_status dr_decode_attention(float* out, const void* q, const void* k_cache, co
 /* The kv_chunk an occupancy-driven split-KV heuristic would pick for this batch
  * on the current device: enough chunks to give every compute unit two
  * workgroups, so it CHANGES WITH THE BATCH SIZE.  A deliberately batch-variant
- * baseline, the pattern the pages reject; passing it to dr_decode_attention
+ * baseline, the pattern that chapter rejects; passing it to dr_decode_attention
  * shows the output bits moving with the batch.  Returns 0 on bad arguments. */
 int32_t dr_decode_attention_occupancy_chunk(int64_t batch, int32_t num_kv_heads, int32_t max_seq_len);
 
