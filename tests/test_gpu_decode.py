@@ -171,3 +171,22 @@ def test_decode_attention_bad_length_fails_closed(dr):
     assert np.all(got[1:] == 7.0)
     inp.lens = np.array([5, 0, 0], np.int32)
     check_against_oracle(inp, got, 64, rows=[(0, h) for h in range(8)])
+
+
+def test_decode_attention_peaked_and_flat_weights(dr):
+    """Scores scaled up 16x (weights close to one-hot) and identical keys (uniform weights: the output is the
+    mean of the value rows) stay within the bound."""
+    inp = workloads.decode_inputs(34, 3, 900, 16, 4, 128, [900, 333, 64])
+    inp.q = workloads.bf16_bits(workloads.bf16_to_f32(inp.q) * 16.0)  # exact: a power of two
+    q, k, v, L = to_dev(inp)
+    say("decode peaked weights")
+    got = host(dr.dr_decode_attention(q, k, v, L, inp.scale, 128))
+    check_against_oracle(inp, got, 128)
+    say("decode flat weights")
+    flat = dataclasses.replace(inp, k=np.broadcast_to(inp.k[:, :1], inp.k.shape).copy())
+    for b in range(flat.B):
+        flat.k[b, flat.lens[b]:] = workloads.BF16_NAN
+    got = host(dr.dr_decode_attention(q, dev_bf16(flat.k), v, L, inp.scale, 128))
+    check_against_oracle(flat, got, 128)
+    want_mean = workloads.bf16_to_f32(inp.v[0, :900]).astype(np.float64).mean(axis=0)  # [Hkv, D]
+    assert np.allclose(got[0], np.repeat(want_mean, 4, axis=0), rtol=0, atol=1e-5)
