@@ -325,7 +325,7 @@ __device__ __forceinline__ u32x4 pack4(const float* t) {
 // product is rounded before it enters the tree.  src rows are then shared by
 // many contributions and small, so they are read through the cache.
 template <dr_dtype DT, int GROUP, int TCLOG, int CIF, bool GEN>
-__global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
+__global__ __launch_bounds__(kReduceThreads, GROUP == 64 && CIF == 1 ? 4 : 1) void segreduce_kernel(
     float* __restrict__ out, int64_t H, const void* __restrict__ src, const int32_t* __restrict__ perm,
     const TileRec* __restrict__ tiles, float* __restrict__ partials, int64_t slices, int32_t* status,
     const float* __restrict__ scale, uint32_t rows_per_src, uint64_t* __restrict__ fp_part) {
@@ -338,19 +338,42 @@ __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
     // the host keeps (tile bound) * slices below 2^32, so 32-bit division suffices
     const uint32_t items = (uint32_t)status[kWordTiles] * (uint32_t)slices;
     const int lig = threadIdx.x % GROUP;
-    const uint32_t group = (blockIdx.x * kReduceThreads + threadIdx.x) / GROUP;
+    uint32_t group = (blockIdx.x * kReduceThreads + threadIdx.x) / GROUP;
+    if (GROUP == 64) group = __builtin_amdgcn_readfirstlane(group);  // one item per wavefront
     const uint32_t ngroups = (gridDim.x * kReduceThreads) / GROUP;
     const char* src_bytes = reinterpret_cast<const char*>(src);
     const int64_t row_bytes = H * kElemBytes;
     uint64_t fp_acc = 0;  // change of the destination's fingerprint made by this lane
-    // the next item's tile record is fetched one item ahead
-    TileRec tr_next{};
-    if (group < items) tr_next = tiles[group / (uint32_t)slices];
+    // With one item per wavefront (AHEAD), tile records are fetched two items
+    // ahead and the source ids of an item's first rows while the previous
+    // item's last rows arrive, so an item starts with its row loads (the item
+    // index is wave-uniform, so the records sit in scalar registers).
+    // Otherwise the record is fetched one item ahead and the first ids at the
+    // item's start, which keeps the lane groups' registers within three
+    // wavefronts per SIMD.
+    constexpr bool AHEAD = GROUP == 64;
+    constexpr int R = 8 * CIF;  // rows loaded at once (CIF chunks of 8)
+    TileRec tr_next{}, tr_next2{};
+    int32_t idx[R];
+    if (group < items) {
+        tr_next = tiles[group / (uint32_t)slices];
+        if (AHEAD) {
+#pragma unroll
+            for (int j = 0; j < R; ++j) idx[j] = perm[min(tr_next.r_begin + j, tr_next.r_end - 1)];
+        }
+    }
+    if (AHEAD && (uint64_t)group + ngroups < items) tr_next2 = tiles[(group + ngroups) / (uint32_t)slices];
     for (uint32_t it = group; it < items; it += ngroups) {
         const uint32_t tile = it / (uint32_t)slices;
         const uint32_t slice = it - tile * (uint32_t)slices;
         const TileRec tr = tr_next;
-        if (it + ngroups < items) tr_next = tiles[(it + ngroups) / (uint32_t)slices];
+        const bool has_next = (uint64_t)it + ngroups < items;
+        if (AHEAD) {
+            tr_next = tr_next2;
+            if ((uint64_t)it + 2ull * ngroups < items) tr_next2 = tiles[(it + 2 * ngroups) / (uint32_t)slices];
+        } else if (has_next) {
+            tr_next = tiles[(it + ngroups) / (uint32_t)slices];
+        }
         const int64_t col = (int64_t)slice * W + E * lig;
         const bool active = col < H;
         const int64_t lcol = active ? col : 0;  // idle lanes read a valid piece
@@ -365,10 +388,10 @@ __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
         TreeCounter<TCLOG + 1, E, GROUP == 64> tc;
         // CIF chunks (8*CIF rows) are loaded at once; slots past the tile's
         // end are neither loaded nor added.
-        constexpr int R = 8 * CIF;
-        int32_t idx[R];
+        if (!AHEAD) {
 #pragma unroll
-        for (int j = 0; j < R; ++j) idx[j] = perm[min(r_begin + j, r_end - 1)];
+            for (int j = 0; j < R; ++j) idx[j] = perm[min(r_begin + j, r_end - 1)];
+        }
         for (int64_t r0 = r_begin; r0 < r_end; r0 += R) {
             u32x4 raw[R];
             float sc[GEN ? R : 1];
@@ -392,11 +415,15 @@ __global__ __launch_bounds__(kReduceThreads) void segreduce_kernel(
                     if (j < live) raw[j] = load16_stream(src_bytes + (int64_t)idx[j] * row_bytes + lcol * kElemBytes);
                 }
             }
-            // the next rows' source ids are fetched while these rows arrive
+            // the next rows' source ids (this item's, else the next item's
+            // first) are fetched while these rows arrive
             const int64_t r1 = r0 + R;
             if (r1 < r_end) {
 #pragma unroll
                 for (int j = 0; j < R; ++j) idx[j] = perm[min(r1 + j, r_end - 1)];
+            } else if (AHEAD && has_next) {
+#pragma unroll
+                for (int j = 0; j < R; ++j) idx[j] = perm[min(tr_next.r_begin + j, tr_next.r_end - 1)];
             }
 #pragma unroll
             for (int c = 0; c < CIF; ++c) {
