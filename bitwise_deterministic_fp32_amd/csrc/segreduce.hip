@@ -324,8 +324,10 @@ __device__ __forceinline__ u32x4 pack4(const float* t) {
 // attention key gradient: scale = dS, src = Q, rows_per_src = top-k).  The
 // product is rounded before it enters the tree.  src rows are then shared by
 // many contributions and small, so they are read through the cache.
+// Four wavefronts per SIMD (at most 128 VGPRs) for one item per wavefront with
+// tiles of up to 2^5 chunks; deeper counters would spill at that budget.
 template <dr_dtype DT, int GROUP, int TCLOG, int CIF, bool GEN>
-__global__ __launch_bounds__(kReduceThreads, GROUP == 64 && CIF == 1 ? 4 : 1) void segreduce_kernel(
+__global__ __launch_bounds__(kReduceThreads, GROUP == 64 && CIF == 1 && TCLOG <= 5 ? 4 : 1) void segreduce_kernel(
     float* __restrict__ out, int64_t H, const void* __restrict__ src, const int32_t* __restrict__ perm,
     const TileRec* __restrict__ tiles, float* __restrict__ partials, int64_t slices, int32_t* status,
     const float* __restrict__ scale, uint32_t rows_per_src, uint64_t* __restrict__ fp_part) {
