@@ -16,7 +16,9 @@
 //     stream is X (read once) plus the partials (written once); the MFMA work
 //     is small beside it.
 //   splitk_reduce: out[e] = T(P_0[e], ..., P_{S-1}[e]); chunks of 8 splits left
-//     to right, then the pairwise tree, one thread per 4 consecutive elements.
+//     to right, then the pairwise tree: for 9..512 splits a lane per chunk and
+//     the tree across lanes (shuffles), else one thread per 4 consecutive
+//     elements walking the chunks.
 // The atomic baseline runs the same tile code and adds each split's tile into
 // out with hardware fp32 atomics.
 #include "internal.h"
@@ -325,6 +327,67 @@ __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(const flo
     reduce_splits<VEC>(P, S, count, e0, out);
 }
 
+// The same tree with L lanes per output vector (L = the chunk count rounded up
+// to a power of two, at most 64): lane c sums chunk c (splits 8c .. 8c+7, left
+// to right), a lane without a chunk holds -0.0, and the chunk sums are paired
+// by stride doubling across the L lanes, the lower chunk as the left operand.
+// With the -0.0 padding that is T over the chunk sums for any chunk count.
+// All of a vector's loads are in flight at once instead of one chunk after
+// another.
+template <int VEC, int L>
+__global__ __launch_bounds__(kReduceThreads) void splitk_reduce_lanes_kernel(const float* __restrict__ P, int S,
+                                                                             int64_t count,
+                                                                             float* __restrict__ out) {
+    const int64_t t = (int64_t)blockIdx.x * kReduceThreads + threadIdx.x;
+    const int c = (int)(t % L);  // this lane's chunk
+    const int64_t e0 = (t / L) * VEC;
+    const bool live = e0 < count;  // whole groups of L lanes share e0
+    const int m = live ? max(0, min(8, S - 8 * c)) : 0;  // splits of the chunk
+    float v[8][VEC];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (j < m) {
+            const int64_t off = (int64_t)(8 * c + j) * count + e0;
+            if (VEC == 4) {
+                const u32x4 raw = load16_stream(P + off);
+                v[j][0] = __uint_as_float(raw.x);
+                v[j][VEC > 1 ? 1 : 0] = __uint_as_float(raw.y);
+                v[j][VEC > 2 ? 2 : 0] = __uint_as_float(raw.z);
+                v[j][VEC > 3 ? 3 : 0] = __uint_as_float(raw.w);
+            } else {
+                v[j][0] = P[off];
+            }
+        }
+    }
+    float s[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) s[e] = m > 0 ? v[0][e] : neg_zero();
+#pragma unroll
+    for (int j = 1; j < 8; ++j) {
+        if (j < m) {
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) s[e] = s[e] + v[j][e];
+        }
+    }
+#pragma unroll
+    for (int off = 1; off < L; off <<= 1) {
+        const bool upper = (c & off) != 0;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+            const float o = __shfl_xor(s[e], off, 64);
+            s[e] = upper ? o + s[e] : s[e] + o;
+        }
+    }
+    if (live && c == 0) {
+        if (VEC == 4) {
+            store16(out + e0, u32x4{__float_as_uint(s[0]), __float_as_uint(s[VEC > 1 ? 1 : 0]),
+                                    __float_as_uint(s[VEC > 2 ? 2 : 0]), __float_as_uint(s[VEC > 3 ? 3 : 0])});
+        } else {
+            out[e0] = s[0];
+        }
+    }
+}
+
 // Group g (blockIdx.y): out[g] = T over its slots slot_offsets[g] .. slot_offsets[g+1]-1,
 // in slot order; a group with no slot gets the zero gradient.
 template <int VEC>
@@ -468,7 +531,35 @@ hipError_t launch_grouped_reduce(const float* partials, const int32_t* slot_offs
 hipError_t launch_splitk_reduce(const float* partials, int32_t splits, int64_t count, float* out, hipStream_t s) {
     if (count == 0) return hipSuccess;
     const bool vec = (count % 4) == 0;
-    const int64_t threads = vec ? count / 4 : count;
+    const int64_t vectors = vec ? count / 4 : count;
+    const int64_t chunks = ((int64_t)splits + 7) / 8;
+    if (chunks >= 2 && chunks <= 64) {
+        // a lane per chunk of 8 splits
+        int lanes = 2;
+        while (lanes < chunks) lanes <<= 1;
+        const dim3 lgrid((unsigned)((vectors * lanes + kReduceThreads - 1) / kReduceThreads));
+#define DR_RL(V, LN)                                                                                           \
+    hipLaunchKernelGGL((splitk_reduce_lanes_kernel<V, LN>), lgrid, dim3(kReduceThreads), 0, s, partials, splits, \
+                       count, out)
+#define DR_RL_V(V)                    \
+    switch (lanes) {                  \
+        case 2: DR_RL(V, 2); break;   \
+        case 4: DR_RL(V, 4); break;   \
+        case 8: DR_RL(V, 8); break;   \
+        case 16: DR_RL(V, 16); break; \
+        case 32: DR_RL(V, 32); break; \
+        default: DR_RL(V, 64); break; \
+    }
+        if (vec) {
+            DR_RL_V(4)
+        } else {
+            DR_RL_V(1)
+        }
+#undef DR_RL_V
+#undef DR_RL
+        return hipGetLastError();
+    }
+    const int64_t threads = vectors;
     const dim3 grid((unsigned)((threads + kReduceThreads - 1) / kReduceThreads));
     if (vec)
         hipLaunchKernelGGL(splitk_reduce_kernel<4>, grid, dim3(kReduceThreads), 0, s, partials, splits, count, out);

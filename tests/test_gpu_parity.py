@@ -298,6 +298,27 @@ def test_sparse_attn_dk_bad_key_leaves_dk_untouched(dr):
 # ---------------------------------------------------------------------------
 # split-K
 # ---------------------------------------------------------------------------
+@pytest.mark.parametrize("S,count", [
+    (9, 4096),     # two chunks of 8 splits, the second a single split
+    (16, 1001),    # count not a multiple of 4: one element per lane group
+    (17, 4096),    # three chunks: the tree pads the fourth with -0.0
+    (64, 7168 * 24 // 4),
+    (100, 2052),   # 13 chunks on 16 lanes
+    (300, 1000),   # 38 chunks on 64 lanes
+    (512, 256),    # 64 chunks, the widest lane group
+    (513, 260),    # 65 chunks: one thread walks the chunks
+])
+def test_splitk_reduce_split_counts(dr, S, count):
+    """The reduce stage alone over given partials (wide magnitude range, signed
+    zeros), for split counts on both reduce paths; bit-exact to the oracle's tree."""
+    say(f"splitk_reduce S={S} count={count}")
+    rng = np.random.default_rng(S * 7919 + count)
+    P = (rng.standard_normal((S, count)) * np.exp2(rng.integers(-20, 20, (S, count)))).astype(np.float32)
+    P[rng.random((S, count)) < 0.01] = np.float32(-0.0)
+    got = host(dr.dr_splitk_reduce(dev(P)))
+    assert_bits_equal(got, oracle.splitk_reduce(P), f"splitk_reduce S={S}")
+
+
 @pytest.mark.parametrize("K,M,N,splits", [
     (1024, 256, 24, 4),
     (1000, 200, 24, 7),     # ragged splits and a ragged M tile
