@@ -76,17 +76,6 @@ __device__ void scan_bins_in_place(int32_t* a, int bins, int32_t* wave_tot) {
     __syncthreads();
 }
 
-// Lanes of the calling wavefront whose digit equals this lane's digit.
-__device__ __forceinline__ uint64_t peers_of(int dg, bool valid, int bits) {
-    uint64_t peers = __ballot(valid);
-    for (int b = 0; b < bits; ++b) {
-        const bool bit = (dg >> b) & 1;
-        const uint64_t m = __ballot(bit);
-        peers &= bit ? m : ~m;
-    }
-    return peers;
-}
-
 __global__ void fill_status_kernel(int32_t* status) {
     if (threadIdx.x < kStatusBytes / sizeof(int32_t)) status[threadIdx.x] = 0;
 }
@@ -180,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void radix_scan_kernel(int32_t* hist, int
 // consecutive keys.  A key's rank among equal digits of its wavefront is the
 // wavefront's count of that digit in earlier rounds (a per-wavefront LDS
 // counter, no barrier) plus the lower lanes of its round with the same digit
-// (ballots).  One barrier later, the tile rank adds the counts of earlier
+// (a per-wavefront LDS table of lane masks by digit).  One barrier later, the tile rank adds the counts of earlier
 // wavefronts; equal digits therefore keep input order.  The tile is staged in
 // LDS in (digit, rank) order and each digit's run is written to consecutive
 // global positions.
@@ -193,11 +182,17 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(SortPass p, int
     __shared__ int32_t lbase[BINS];          // position of digit d's run inside the staged tile
     __shared__ int32_t wcount[kWaves][BINS];  // per-wavefront digit counts, then prefixes
     __shared__ int32_t wave_tot[kWaves];
-    __shared__ int32_t st_dest[ITEMS * kThreads];
-    __shared__ int32_t st_val[ITEMS * kThreads];
-    __shared__ int32_t st_src[STAGE_SRC ? ITEMS * kThreads : 1];
+    // The staged tile, and before it (ranking only) each wavefront's table of
+    // lane masks by digit.
+    constexpr int kStageBytes = (STAGE_SRC ? 3 : 2) * ITEMS * kThreads * 4;
+    constexpr int kTableBytes = kWaves * BINS * 8;
+    __shared__ __align__(16) unsigned char shared_un[kStageBytes > kTableBytes ? kStageBytes : kTableBytes];
+    int32_t* st_dest = reinterpret_cast<int32_t*>(shared_un);
+    int32_t* st_val = st_dest + ITEMS * kThreads;
+    int32_t* st_src = st_val + ITEMS * kThreads;
     if (status[kWordStatus] != 0) return;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    unsigned long long* peer_tbl = reinterpret_cast<unsigned long long*>(shared_un) + w * BINS;
     const int bins = 1 << p.bits;
     const bool key_is_dest = p.digit_src == p.dest_in;
     const int64_t base = (int64_t)blockIdx.x << tile_log2;
@@ -223,15 +218,26 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(SortPass p, int
         for (int ww = 0; ww < kWaves; ++ww) wcount[ww][d] = 0;
         gbase[d] = totals[d];
     }
+    for (int d = lane; d < bins; d += 64) peer_tbl[d] = 0ull;  // this wavefront's table
     __syncthreads();
 
-    // ranks inside the wavefront, in input order
+    // ranks inside the wavefront, in input order.  The lanes holding a digit
+    // are found by each lane OR-ing its bit into the digit's entry of the
+    // wavefront's table, reading the entry back and clearing it (a
+    // wavefront's LDS operations complete in order, and OR does not depend on
+    // the order of the lanes); this replaces one ballot per digit bit.
+    const unsigned long long my_bit = 1ull << lane;
     int32_t rank[ITEMS];
 #pragma unroll
     for (int r = 0; r < ITEMS; ++r) {
         const bool valid = wbase + r * 64 + lane < end;
         const int dg = digit_of(key[r], p.shift, p.bits);
-        const uint64_t peers = peers_of(dg, valid, p.bits);
+        uint64_t peers = 0;
+        if (valid) {
+            atomicOr(&peer_tbl[dg], my_bit);
+            peers = peer_tbl[dg];
+            peer_tbl[dg] = 0ull;
+        }
         const int below = __popcll(peers & lanemask_lt());
         const int leader = peers ? __builtin_ctzll(peers) : lane;
         int32_t prev = 0;
