@@ -238,14 +238,13 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(SortPass p, int
             peers = peer_tbl[dg];
             peer_tbl[dg] = 0ull;
         }
-        const int below = __popcll(peers & lanemask_lt());
-        const int leader = peers ? __builtin_ctzll(peers) : lane;
+        const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(peers >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)peers, 0u));
+        // every lane of the digit reads the count (one instruction) before the
+        // lowest of them advances it
         int32_t prev = 0;
-        if (valid && below == 0) {
-            prev = wcount[w][dg];
-            wcount[w][dg] = prev + __popcll(peers);
-        }
-        prev = __shfl(prev, leader, 64);
+        if (valid) prev = wcount[w][dg];
+        if (valid && below == 0) wcount[w][dg] = prev + (int32_t)__popcll(peers);
         rank[r] = prev + below;
     }
     __syncthreads();
@@ -263,11 +262,16 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(SortPass p, int
     __syncthreads();
     scan_bins_in_place(gbase, bins, wave_tot);
     scan_bins_in_place(lbase, bins, wave_tot);
-    // gbase[d] now counts all keys of digits below d
+    // gbase[d] now counts all keys of digits below d.  From here on gbase[d]
+    // is the global position of staged position 0 of digit d's run, and
+    // wcount[w][d] the staged position of wavefront w's first key of digit d.
     int32_t* seg = blockIdx.x == 0 ? p.seg_out : nullptr;
     for (int d = tid; d < bins; d += kThreads) {
         if (seg && d <= p.num_dests) seg[d] = gbase[d];
-        gbase[d] += hist[(int64_t)d * nblocks + blockIdx.x];
+        const int32_t lb = lbase[d];
+        gbase[d] += hist[(int64_t)d * nblocks + blockIdx.x] - lb;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww) wcount[ww][d] += lb;
     }
     if (seg && tid == 0 && p.num_dests == bins) seg[bins] = (int32_t)n;
     __syncthreads();
@@ -275,7 +279,7 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(SortPass p, int
     for (int r = 0; r < ITEMS; ++r) {
         if (wbase + r * 64 + lane < end) {
             const int dg = digit_of(key[r], p.shift, p.bits);
-            const int32_t lp = lbase[dg] + wcount[w][dg] + rank[r];
+            const int32_t lp = wcount[w][dg] + rank[r];
             st_val[lp] = val[r];
             st_dest[lp] = key_is_dest ? key[r] : other[r];
             if (STAGE_SRC) st_src[lp] = key_is_dest ? other[r] : key[r];
@@ -287,7 +291,7 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(SortPass p, int
         const int32_t dk = st_dest[j];
         const int32_t sk = STAGE_SRC ? st_src[j] : 0;
         const int dg = digit_of(key_is_dest ? dk : sk, p.shift, p.bits);
-        const int32_t pos = gbase[dg] + (j - lbase[dg]);
+        const int32_t pos = gbase[dg] + j;
         const int32_t v = st_val[j];
         // consistent histograms keep pos and v inside [0, n); the guard keeps
         // a corrupted workspace from writing outside the outputs
