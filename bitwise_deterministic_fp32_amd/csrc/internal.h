@@ -108,6 +108,9 @@ hipError_t launch_seg_offsets(const int32_t* sorted_dest, int64_t n, int32_t num
 int64_t plan_blocks(int32_t num_dests);
 hipError_t launch_plan_count(const int32_t* seg_offsets, int32_t num_dests, int64_t n, int tile_chunks_log2,
                              int32_t* block_sums, int32_t* status, hipStream_t s);
+// plan_count for the library's own sort: segment offsets searched in the sorted destinations, written, and counted
+hipError_t launch_plan_count_search(const int32_t* sorted_dest, int64_t n, int32_t num_dests, int tile_chunks_log2,
+                                    int32_t* seg_offsets, int32_t* block_sums, int32_t* status, hipStream_t s);
 hipError_t launch_plan_write(const int32_t* seg_offsets, int32_t num_dests, int tile_chunks_log2,
                              const int32_t* block_sums, TileRec* tiles, MultiRec* multis, int32_t* status,
                              hipStream_t s);

@@ -95,6 +95,61 @@ __global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(const int32_t*
     }
 }
 
+// plan_count for a plan the library's own sort produced: thread d finds the
+// lower bound of d in the sorted destinations (the workgroup's last thread
+// also that of d + 1, in the same loop), the next destination's bound comes
+// from the neighbouring thread through LDS, and the thread writes the segment
+// offset (the last destination's thread also seg[num_dests] = n) and counts
+// tiles as plan_count does.  This replaces a separate offsets kernel.  The sort
+// has already checked every destination, so there is nothing to validate.
+__global__ __launch_bounds__(kPlanThreads) void plan_count_search_kernel(const int32_t* __restrict__ sorted_dest,
+                                                                         int64_t n, int32_t num_dests, int tc_log2,
+                                                                         int32_t* __restrict__ seg,
+                                                                         int32_t* block_sums, int32_t* status) {
+    __shared__ int32_t part[3][kPlanWaves];
+    __shared__ int32_t bound[kPlanThreads + 1];
+    if (status[kWordStatus] != 0) return;
+    const int64_t d = (int64_t)blockIdx.x * kPlanThreads + threadIdx.x;
+    const bool last = threadIdx.x == kPlanThreads - 1;
+    int64_t lo0 = 0, hi0 = d <= num_dests ? n : 0, lo1 = 0, hi1 = (last && d < num_dests) ? n : 0;
+    if (d > num_dests) lo0 = n;
+    while (lo0 < hi0 || lo1 < hi1) {
+        if (lo0 < hi0) {
+            const int64_t mid = (lo0 + hi0) >> 1;
+            if (sorted_dest[mid] < d) lo0 = mid + 1;
+            else hi0 = mid;
+        }
+        if (lo1 < hi1) {
+            const int64_t mid = (lo1 + hi1) >> 1;
+            if (sorted_dest[mid] < d + 1) lo1 = mid + 1;
+            else hi1 = mid;
+        }
+    }
+    bound[threadIdx.x] = (int32_t)lo0;
+    if (last) bound[kPlanThreads] = (int32_t)lo1;
+    __syncthreads();
+    TileCount c{0, 0, 0};
+    if (d < num_dests) {
+        const int32_t b = bound[threadIdx.x + 1];  // lower bound of d + 1
+        seg[d] = (int32_t)lo0;
+        if (d == num_dests - 1) seg[num_dests] = b;
+        c = tile_count(b - (int32_t)lo0, tc_log2);
+    }
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int32_t st = wave_sum(c.tiles), sm = wave_sum(c.multi), sp = wave_sum(c.pslots);
+    if (lane == 0) {
+        part[0][w] = st;
+        part[1][w] = sm;
+        part[2][w] = sp;
+    }
+    __syncthreads();
+    if (threadIdx.x < 3) {
+        int32_t t = 0;
+        for (int i = 0; i < kPlanWaves; ++i) t += part[threadIdx.x][i];
+        block_sums[3 * blockIdx.x + threadIdx.x] = t;
+    }
+}
+
 // Exclusive prefix of the three counts over all destinations; writes one
 // TileRec per tile and one MultiRec per destination with several tiles.
 __global__ __launch_bounds__(kPlanThreads) void plan_write_kernel(const int32_t* __restrict__ seg, int32_t num_dests,
@@ -603,6 +658,13 @@ hipError_t launch_plan_count(const int32_t* seg_offsets, int32_t num_dests, int6
                              int32_t* block_sums, int32_t* status, hipStream_t s) {
     hipLaunchKernelGGL(plan_count_kernel, dim3((unsigned)plan_blocks(num_dests)), dim3(kPlanThreads), 0, s,
                        seg_offsets, num_dests, n, tc_log2, block_sums, status);
+    return hipGetLastError();
+}
+
+hipError_t launch_plan_count_search(const int32_t* sorted_dest, int64_t n, int32_t num_dests, int tc_log2,
+                                    int32_t* seg_offsets, int32_t* block_sums, int32_t* status, hipStream_t s) {
+    hipLaunchKernelGGL(plan_count_search_kernel, dim3((unsigned)plan_blocks(num_dests)), dim3(kPlanThreads), 0, s,
+                       sorted_dest, n, num_dests, tc_log2, seg_offsets, block_sums, status);
     return hipGetLastError();
 }
 
