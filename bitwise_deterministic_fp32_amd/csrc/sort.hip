@@ -84,8 +84,10 @@ __global__ void fill_status_kernel(int32_t* status) {
 // loads its ITEMS keys (all loads in flight together), then counts them in
 // LDS; a wavefront whose keys all share one digit adds once.  With kValidate,
 // also checks every dest (and src_id) against its range: the first pass.
-template <bool kValidate, int ITEMS>
-__global__ __launch_bounds__(kThreads) void radix_hist_kernel(SortPass p, int64_t n, int tile_log2, int32_t* hist,
+// HT threads per workgroup: 1024 for tiles of at least 2^10 keys, so that a
+// CU holds more wavefronts to hide the key loads.
+template <bool kValidate, int HT, int ITEMS>
+__global__ __launch_bounds__(HT) void radix_hist_kernel(SortPass p, int64_t n, int tile_log2, int32_t* hist,
                                                               int64_t nblocks, const int32_t* __restrict__ dest,
                                                               int32_t num_dests, const int32_t* __restrict__ src_id,
                                                               int32_t src_bound, int32_t* status_or_flags) {
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void radix_hist_kernel(SortPass p, int64_
     // later passes: status word (same value for every thread); first pass: tile flags
     if (!kValidate && status_or_flags[kWordStatus] != 0) return;
     const int bins = 1 << p.bits;
-    for (int d = threadIdx.x; d < bins; d += kThreads) cnt[d] = 0;
+    for (int d = threadIdx.x; d < bins; d += HT) cnt[d] = 0;
     if (threadIdx.x == 0) bad = 0;
     const int64_t base = (int64_t)blockIdx.x << tile_log2;
     const int64_t end = min(n, base + ((int64_t)1 << tile_log2));
@@ -102,7 +104,7 @@ __global__ __launch_bounds__(kThreads) void radix_hist_kernel(SortPass p, int64_
     int my_bad = 0;
 #pragma unroll
     for (int r = 0; r < ITEMS; ++r) {
-        const int64_t i = base + r * kThreads + threadIdx.x;
+        const int64_t i = base + r * HT + threadIdx.x;
         key[r] = i < end ? p.digit_src[i] : 0;
         if (kValidate && i < end) {
             const int32_t dd = dest[i];
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void radix_hist_kernel(SortPass p, int64_
     __syncthreads();
 #pragma unroll
     for (int r = 0; r < ITEMS; ++r) {
-        const int64_t i = base + r * kThreads + threadIdx.x;
+        const int64_t i = base + r * HT + threadIdx.x;
         const bool valid = i < end;
         const int dg = digit_of(key[r], p.shift, p.bits);
         const uint64_t vmask = __ballot(valid);
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void radix_hist_kernel(SortPass p, int64_
     }
     if (my_bad) bad = 1;
     __syncthreads();
-    for (int d = threadIdx.x; d < bins; d += kThreads) hist[(int64_t)d * nblocks + blockIdx.x] = cnt[d];
+    for (int d = threadIdx.x; d < bins; d += HT) hist[(int64_t)d * nblocks + blockIdx.x] = cnt[d];
     if (kValidate && threadIdx.x == 0) status_or_flags[blockIdx.x] = bad;
 }
 
@@ -338,15 +340,25 @@ static int64_t tiles_for(int64_t n, int tile_log2) { return (n + ((int64_t)1 << 
         default: MACRO(32); break;       \
     }
 
+#define DR_HIST_BY_TILE(tile_log2, MACRO) \
+    switch (tile_log2) {                       \
+        case 8: MACRO(256, 1); break;          \
+        case 9: MACRO(256, 2); break;          \
+        case 10: MACRO(1024, 1); break;        \
+        case 11: MACRO(1024, 2); break;        \
+        case 12: MACRO(1024, 4); break;        \
+        default: MACRO(1024, 8); break;        \
+    }
+
 hipError_t launch_radix_validate_hist(const int32_t* dest, int32_t num_dests, const int32_t* src_id,
                                       int32_t src_bound, const SortPass& p, int64_t n, int tile_log2,
                                       int32_t* hist, int32_t* tile_flags, hipStream_t s) {
     const int64_t nb = tiles_for(n, tile_log2);
     if (nb == 0) return hipSuccess;
-#define DR_H(IT)                                                                                              \
-    hipLaunchKernelGGL((radix_hist_kernel<true, IT>), dim3((unsigned)nb), dim3(kThreads), 0, s, p, n, tile_log2, \
+#define DR_H(HTH, IT)                                                                                         \
+    hipLaunchKernelGGL((radix_hist_kernel<true, HTH, IT>), dim3((unsigned)nb), dim3(HTH), 0, s, p, n, tile_log2, \
                        hist, nb, dest, num_dests, src_id, src_bound, tile_flags)
-    DR_BY_ITEMS(tile_log2, DR_H)
+    DR_HIST_BY_TILE(tile_log2, DR_H)
 #undef DR_H
     return hipGetLastError();
 }
@@ -355,10 +367,10 @@ hipError_t launch_radix_hist(const SortPass& p, int64_t n, int tile_log2, int32_
                              hipStream_t s) {
     const int64_t nb = tiles_for(n, tile_log2);
     if (nb == 0) return hipSuccess;
-#define DR_H(IT)                                                                                               \
-    hipLaunchKernelGGL((radix_hist_kernel<false, IT>), dim3((unsigned)nb), dim3(kThreads), 0, s, p, n, tile_log2, \
+#define DR_H(HTH, IT)                                                                                          \
+    hipLaunchKernelGGL((radix_hist_kernel<false, HTH, IT>), dim3((unsigned)nb), dim3(HTH), 0, s, p, n, tile_log2, \
                        hist, nb, nullptr, 0, nullptr, 0, const_cast<int32_t*>(status))
-    DR_BY_ITEMS(tile_log2, DR_H)
+    DR_HIST_BY_TILE(tile_log2, DR_H)
 #undef DR_H
     return hipGetLastError();
 }
