@@ -97,7 +97,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(const int32_t*
 
 // plan_count for a plan the library's own sort produced: thread d finds the
 // lower bound of d in the sorted destinations (the workgroup's last thread
-// also that of d + 1, in the same loop), the next destination's bound comes
+// also that of d + 1, in the same loop), first among 1024 evenly spaced
+// samples held in LDS, then within one sample stride; the next destination's bound comes
 // from the neighbouring thread through LDS, and the thread writes the segment
 // offset (the last destination's thread also seg[num_dests] = n) and counts
 // tiles as plan_count does.  This replaces a separate offsets kernel.  The sort
@@ -106,13 +107,33 @@ __global__ __launch_bounds__(kPlanThreads) void plan_count_search_kernel(const i
                                                                          int64_t n, int32_t num_dests, int tc_log2,
                                                                          int32_t* __restrict__ seg,
                                                                          int32_t* block_sums, int32_t* status) {
+    constexpr int kSamples = 1024;  // every stride-th sorted destination, in LDS
     __shared__ int32_t part[3][kPlanWaves];
     __shared__ int32_t bound[kPlanThreads + 1];
+    __shared__ int32_t sample[kSamples];
     if (status[kWordStatus] != 0) return;
     const int64_t d = (int64_t)blockIdx.x * kPlanThreads + threadIdx.x;
     const bool last = threadIdx.x == kPlanThreads - 1;
-    int64_t lo0 = 0, hi0 = d <= num_dests ? n : 0, lo1 = 0, hi1 = (last && d < num_dests) ? n : 0;
-    if (d > num_dests) lo0 = n;
+    const int64_t stride = (n + kSamples - 1) / kSamples;
+    for (int k = threadIdx.x; k < kSamples; k += kPlanThreads)
+        sample[k] = (int64_t)k * stride < n ? sorted_dest[(int64_t)k * stride] : INT32_MAX;
+    __syncthreads();
+    // The samples bound each search to one stride: with k the first sample
+    // >= x, the lower bound of x lies in ((k-1)*stride, min(k*stride, n)].
+    auto narrow = [&](int64_t x, int64_t& lo, int64_t& hi) {
+        int a = 0, b = kSamples;  // first sample index with sample >= x
+        while (a < b) {
+            const int m = (a + b) >> 1;
+            if (sample[m] < x) a = m + 1;
+            else b = m;
+        }
+        lo = a == 0 ? 0 : (int64_t)(a - 1) * stride + 1;
+        hi = min((int64_t)a * stride, n);
+        if (lo > hi) lo = hi;
+    };
+    int64_t lo0 = n, hi0 = n, lo1 = 0, hi1 = 0;
+    if (d <= num_dests) narrow(d, lo0, hi0);
+    if (last && d < num_dests) narrow(d + 1, lo1, hi1);
     while (lo0 < hi0 || lo1 < hi1) {
         if (lo0 < hi0) {
             const int64_t mid = (lo0 + hi0) >> 1;
