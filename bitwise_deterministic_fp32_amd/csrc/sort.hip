@@ -88,9 +88,9 @@ __global__ void fill_status_kernel(int32_t* status) {
 // CU holds more wavefronts to hide the key loads.
 template <bool kValidate, int HT, int ITEMS>
 __global__ __launch_bounds__(HT) void radix_hist_kernel(SortPass p, int64_t n, int tile_log2, int32_t* hist,
-                                                              int64_t nblocks, const int32_t* __restrict__ dest,
-                                                              int32_t num_dests, const int32_t* __restrict__ src_id,
-                                                              int32_t src_bound, int32_t* status_or_flags) {
+                                                        int64_t nblocks, const int32_t* __restrict__ dest,
+                                                        int32_t num_dests, const int32_t* __restrict__ src_id,
+                                                        int32_t src_bound, int32_t* status_or_flags) {
     __shared__ int32_t cnt[kMaxBins];
     __shared__ int32_t bad;
     // later passes: status word (same value for every thread); first pass: tile flags
@@ -171,8 +171,9 @@ __global__ __launch_bounds__(kThreads) void radix_scan_kernel(int32_t* hist, int
 // consecutive keys.  A key's rank among equal digits of its wavefront is the
 // wavefront's count of that digit in earlier rounds (a per-wavefront LDS
 // counter, no barrier) plus the lower lanes of its round with the same digit
-// (a per-wavefront LDS table of lane masks by digit).  One barrier later, the tile rank adds the counts of earlier
-// wavefronts; equal digits therefore keep input order.  The tile is staged in
+// (a per-wavefront LDS table of lane masks by digit).  One barrier later, the
+// tile rank adds the counts of earlier wavefronts; equal digits therefore keep
+// input order.  The tile is staged in
 // LDS in (digit, rank) order and each digit's run is written to consecutive
 // global positions.
 template <int ITEMS, int BINS, bool STAGE_SRC>
