@@ -98,11 +98,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_count_kernel(const int32_t*
 // plan_count for a plan the library's own sort produced: thread d finds the
 // lower bound of d in the sorted destinations (the workgroup's last thread
 // also that of d + 1, in the same loop), first among 1024 evenly spaced
-// samples held in LDS, then within one sample stride; the next destination's bound comes
-// from the neighbouring thread through LDS, and the thread writes the segment
-// offset (the last destination's thread also seg[num_dests] = n) and counts
-// tiles as plan_count does.  This replaces a separate offsets kernel.  The sort
-// has already checked every destination, so there is nothing to validate.
+// samples held in LDS, then within one sample stride.  The next destination's
+// bound comes from the neighbouring thread through LDS, and the thread writes
+// the segment offset (the last destination's thread also seg[num_dests] = n)
+// and counts tiles as plan_count does.  This replaces a separate offsets
+// kernel.  The sort has already checked every destination, so there is
+// nothing to validate.
 __global__ __launch_bounds__(kPlanThreads) void plan_count_search_kernel(const int32_t* __restrict__ sorted_dest,
                                                                          int64_t n, int32_t num_dests, int tc_log2,
                                                                          int32_t* __restrict__ seg,
