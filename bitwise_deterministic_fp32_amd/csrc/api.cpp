@@ -118,12 +118,14 @@ SortBuffers carve_sort(Carver& c, int64_t n, bool has_src, int tile_log2) {
 // Launches the stable sort.  It writes the status word itself (the first
 // pass's scan sets or clears the index-error bit), so no reset launch is
 // needed before it.
-// With sorted_dest_out, segment offsets that would need a separate search
-// are left to the caller: *sorted_dest_out is then the sorted destinations
-// (else null, and seg_offsets is written here).
+// With seg_deferred, segment offsets that would need a separate search are
+// left to the caller: *seg_deferred is then true and *sorted_dest_out the
+// sorted destinations (not read when n == 0); otherwise seg_offsets is
+// written here.
 dr_status run_sort(const int32_t* dest, const int32_t* src_id, int32_t src_bound, int64_t n, int32_t num_dests,
                    int32_t* perm, int32_t* seg_offsets, int32_t* inv_perm, int32_t* status, const SortBuffers& b,
-                   int tile_log2, hipStream_t s, const int32_t** sorted_dest_out = nullptr) {
+                   int tile_log2, hipStream_t s, bool* seg_deferred = nullptr,
+                   const int32_t** sorted_dest_out = nullptr) {
     const bool has_src = src_id != nullptr;
     const std::vector<DigitPass> passes = sort_passes(num_dests, has_src, src_bound);
     int src_passes = 0;
@@ -167,8 +169,10 @@ dr_status run_sort(const int32_t* dest, const int32_t* src_id, int32_t src_bound
         cur_src = sp.src_out;
         cur_val = sp.val_out;
     }
-    if (sorted_dest_out) *sorted_dest_out = seg_in_scatter ? nullptr : cur_dest;
-    if (!seg_in_scatter && !sorted_dest_out)
+    const bool defer = seg_deferred && !seg_in_scatter;
+    if (seg_deferred) *seg_deferred = defer;
+    if (sorted_dest_out) *sorted_dest_out = cur_dest;
+    if (!seg_in_scatter && !defer)
         DR_TRY_HIP(dr::launch_seg_offsets(cur_dest, n, num_dests, seg_offsets, status, s), "segment offsets launch");
     return DR_OK;
 }
@@ -485,11 +489,12 @@ dr_status run_index_add(const char* what, float* out, int32_t num_dests, int64_t
         return fail(DR_ERR_WORKSPACE_TOO_SMALL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes, cv.off);
     const int32_t* p = perm;
     const int32_t* seg = seg_offsets;
-    const int32_t* sorted_dest = nullptr;  // set when the plan count also finds the segment offsets
+    bool seg_deferred = false;  // the plan count then also finds the segment offsets
+    const int32_t* sorted_dest = nullptr;
     if (sort_inside) {
         // the sort writes the status word
         const dr_status st = run_sort(index, nullptr, 0, n, num_dests, b.perm, b.seg, nullptr, b.status, b.sort,
-                                      lc.sort_tile(n), stream, &sorted_dest);
+                                      lc.sort_tile(n), stream, &seg_deferred, &sorted_dest);
         if (st != DR_OK) return st;
         p = b.perm;
         seg = b.seg;
@@ -498,7 +503,7 @@ dr_status run_index_add(const char* what, float* out, int32_t num_dests, int64_t
         DR_TRY_HIP(dr::launch_plan_validate(perm, seg_offsets, index, n, num_dests, b.status, stream),
                    "plan validation launch");
     }
-    if (sorted_dest)
+    if (seg_deferred)
         DR_TRY_HIP(dr::launch_plan_count_search(sorted_dest, n, num_dests, lc.tile_chunks_log2, b.seg, b.block_sums,
                                                 b.status, stream),
                    "plan count launch");

@@ -163,6 +163,22 @@ def test_index_add_matches_oracle(dr, n, D, H, src_dtype, dist):
     assert_bits_equal(host(out), want, "index_add")
 
 
+@pytest.mark.parametrize("D", [10, 4096, 131072])
+def test_index_add_empty_with_dirty_workspace(dr, D):
+    """No contributions, one or two sort passes, a workspace full of 0xFF bytes:
+    the call must clear its own status and plan state and leave out untouched."""
+    say(f"index_add n=0 D={D} dirty workspace")
+    H = 128
+    out0 = workloads.normal_f32(D, 2, D * H).reshape(D, H)
+    out = dev(out0.copy())
+    src = torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
+    index = torch.empty((0,), dtype=torch.int32, device="cuda")
+    ws = torch.full((dr.dr_index_add_workspace_size(0, D, H),), 0xFF, dtype=torch.uint8, device="cuda")
+    dr.dr_index_add(out, src, index, ws=ws)
+    dr.dr_workspace_status(ws)
+    assert_bits_equal(host(out), out0, "index_add with no contributions")
+
+
 def test_index_add_reused_plan(dr):
     say("index_add reused plan")
     index, src, out0 = _index_add_case(5, 30000, 1000, 128, "bf16", "zipf")
