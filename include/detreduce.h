@@ -386,7 +386,10 @@ dr_status dr_permute_rows(const void* rows, int64_t row_bytes, int64_t num_rows,
  *   head_dim     128.  num_q_heads / num_kv_heads must be 1, 2, 4, 8 or 16.
  *   max_seq_len  1 .. 2^30.  kv_chunk: a multiple of 64 in [64, 2^20].
  *   ws           >= dr_decode_attention_workspace_size(...) bytes, 16-byte
- *                aligned: one partial slot per (sequence, query head, chunk).
+ *                aligned: one partial slot per (sequence, query head, chunk)
+ *                after 256 reserved bytes.  Its contents on entry do not
+ *                matter; device errors go to dev_status only (the workspace
+ *                holds no status word, so dr_workspace_status does not apply).
  * All pointers must be 16-byte aligned (seq_lens and dev_status 4-byte).
  * ---------------------------------------------------------------------- */
 size_t dr_decode_attention_workspace_size(int64_t batch, int32_t num_q_heads, int32_t max_seq_len, int32_t kv_chunk,

@@ -520,3 +520,87 @@ def test_combine_fingerprinted_matches_separate_calls(dr, T, E, k, H, rows_dtype
     out2, h2 = dr.dr_combine_fingerprinted(rows, bad, gates, dev_status=status)
     assert np.isnan(host(out2)[T // 2]).all()
     assert int(h2.item()) & ((1 << 64) - 1) == oracle.fingerprint(host(out2))
+
+
+# ---------------------------------------------------------------------------
+# workspace contents
+# ---------------------------------------------------------------------------
+def _filled(nbytes, byte):
+    return torch.full((max(int(nbytes), 16),), byte, dtype=torch.uint8, device="cuda")
+
+
+def test_results_do_not_depend_on_workspace_contents(dr):
+    """Every entry point that takes a workspace gives the same bytes (and a clear
+    status) whether its workspace starts as zeros or as 0xFF bytes, and whatever
+    its outputs held before: no call may read state it has not written itself."""
+    say("workspace contents: sort, index_add, sparse_attn_dk, combine_fingerprinted, grouped split, decode, fingerprint")
+    runs = {}
+    for byte in (0x00, 0xFF):
+        got = {}
+        # sort: two destination passes with source ids, and one pass
+        rng = np.random.default_rng(1)
+        dest = dev(np.minimum(rng.zipf(1.2, 30000) - 1, 1999).astype(np.int32))
+        src = dev(rng.integers(0, 30000, 30000).astype(np.int32))
+        for D, s_ids, bound in ((2000, src, 30000), (256, None, 0)):
+            ws = _filled(dr.dr_sort_workspace_size(30000, D, bound), byte)
+            perm = torch.full((30000,), -7, dtype=torch.int32, device="cuda")
+            seg = torch.full((D + 1,), -7, dtype=torch.int32, device="cuda")
+            p, sg, inv = dr.dr_sort_by_dest(torch.minimum(dest, torch.tensor(D - 1, device="cuda", dtype=torch.int32)),
+                                            D, s_ids, bound, perm=perm, seg_offsets=seg, ws=ws)
+            dr.dr_workspace_status(ws)
+            got[f"sort{D}"] = (host(p), host(sg), host(inv))
+        # index_add with its own sort (two passes), plain and fingerprinted
+        index, srcr, out0 = _index_add_case(3, 20000, 4096, 128, "bf16", "zipf")
+        for fp in (False, True):
+            out = dev(out0.copy())
+            ws = _filled(dr.dr_index_add_workspace_size(20000, 4096, 128), byte)
+            if fp:
+                h = _hash_tensor(oracle.fingerprint(out0))
+                dr.dr_index_add_fingerprinted(out, dev_bf16(srcr), dev(index), h, ws=ws)
+                got["index_add_fp_hash"] = _hash_value(h)
+            else:
+                dr.dr_index_add(out, dev_bf16(srcr), dev(index), ws=ws)
+            dr.dr_workspace_status(ws)
+            got[f"index_add{fp}"] = host(out)
+        # fused sparse-attention key gradient
+        inp = workloads.sparse_attn_dk_inputs(5, Q=256, K=2048, S=32, H=128)
+        dK = dev(inp.dK0.copy())
+        ws = _filled(dr.dr_sparse_attn_dk_workspace_size(256, 32, 2048, 128), byte)
+        dr.dr_sparse_attn_dk(dK, dev_bf16(inp.Q), dev(inp.dS), dev(inp.key_idx), ws=ws)
+        dr.dr_workspace_status(ws)
+        got["sparse_attn_dk"] = host(dK)
+        # combine with its fingerprint
+        m = workloads.moe_inputs(9, 300, 64, 8, 520, "bf16", zipf_bias_s=1.2)
+        row_of = _row_of(dr, m.expert_ids, 64)
+        ws = _filled(dr.dr_combine_fingerprinted_workspace_size(torch.bfloat16, 520, 300), byte)
+        out, h = dr.dr_combine_fingerprinted(dev_bf16(m.rows), row_of, dev(m.gates), ws=ws)
+        got["combine"] = (host(out), _hash_value(h))
+        # grouped split: slot table, partials and per-group reduce
+        sk = workloads.splitk_inputs(11, 2000, 200, 24, 1)
+        off = dev(np.array([0, 700, 700, 1500, 2000], np.int32))
+        ws = _filled(dr.dr_grouped_splitk_workspace_size(2000, 4, 256), byte)
+        P, so, ws = dr.dr_grouped_splitk_gemm_tn(dev_bf16(sk.X), dev_bf16(sk.dY), off, 256, ws=ws)
+        dr.dr_workspace_status(ws)
+        got["grouped"] = (host(so), host(dr.dr_grouped_splitk_reduce(P, so, ws)))
+        # decode attention
+        di = workloads.decode_inputs(13, B=3, Lmax=1000, Hq=8, Hkv=2, D=128)
+        ws = _filled(dr.dr_decode_attention_workspace_size(3, 8, 1000, 256, 128), byte)
+        st = torch.zeros(1, dtype=torch.int32, device="cuda")  # decode reports device errors here only
+        o = dr.dr_decode_attention(dev_bf16(di.q), dev_bf16(di.k), dev_bf16(di.v), dev(di.lens), di.scale, 256,
+                                   ws=ws, dev_status=st)
+        dr.dr_read_status(st)
+        got["decode"] = host(o)
+        # fingerprint
+        data = dev(np.arange(1 << 18, dtype=np.int32))
+        ws = _filled(dr.dr_fingerprint_workspace_size(1 << 20), byte)
+        got["fingerprint"] = _hash_value(dr.dr_fingerprint(data, ws=ws))
+        runs[byte] = got
+    for key in runs[0x00]:
+        a, b = runs[0x00][key], runs[0xFF][key]
+        a = a if isinstance(a, tuple) else (a,)
+        b = b if isinstance(b, tuple) else (b,)
+        for x, y in zip(a, b):
+            if isinstance(x, np.ndarray):
+                assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), key
+            else:
+                assert x == y, key
