@@ -30,6 +30,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxBins = 1 << kMaxDigitBits;
+constexpr int64_t kXcds = 8;  // XCDs of an MI355X, each with its own L2
 
 __device__ __forceinline__ int digit_of(int32_t key, int shift, int bits) {
     return (int)(((uint32_t)key >> shift) & ((1u << bits) - 1u));
@@ -194,11 +195,19 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(SortPass p, int
     int32_t* st_val = st_dest + ITEMS * kThreads;
     int32_t* st_src = st_val + ITEMS * kThreads;
     if (status[kWordStatus] != 0) return;
+    // Workgroups are spread over the XCDs round-robin (workgroup b on XCD
+    // b % kXcds); each XCD takes a contiguous range of tiles, so the digit runs
+    // that neighbouring tiles write next to each other mostly meet in one L2
+    // and leave it as whole lines.  The grid is kXcds * per workgroups; the few
+    // past the last tile do nothing.
+    const int64_t per = (nblocks + kXcds - 1) / kXcds;
+    const int64_t tile = (int64_t)(blockIdx.x % kXcds) * per + blockIdx.x / kXcds;
+    if (tile >= nblocks) return;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     unsigned long long* peer_tbl = reinterpret_cast<unsigned long long*>(shared_un) + w * BINS;
     const int bins = 1 << p.bits;
     const bool key_is_dest = p.digit_src == p.dest_in;
-    const int64_t base = (int64_t)blockIdx.x << tile_log2;
+    const int64_t base = tile << tile_log2;
     const int64_t end = min(n, base + ((int64_t)1 << tile_log2));
     const int32_t count = (int32_t)(end - base);
     const int64_t wbase = base + (int64_t)w * 64 * ITEMS;  // this wavefront's slice
@@ -268,11 +277,11 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(SortPass p, int
     // gbase[d] now counts all keys of digits below d.  From here on gbase[d]
     // is the global position of staged position 0 of digit d's run, and
     // wcount[w][d] the staged position of wavefront w's first key of digit d.
-    int32_t* seg = blockIdx.x == 0 ? p.seg_out : nullptr;
+    int32_t* seg = tile == 0 ? p.seg_out : nullptr;
     for (int d = tid; d < bins; d += kThreads) {
         if (seg && d <= p.num_dests) seg[d] = gbase[d];
         const int32_t lb = lbase[d];
-        gbase[d] += hist[(int64_t)d * nblocks + blockIdx.x] - lb;
+        gbase[d] += hist[(int64_t)d * nblocks + tile] - lb;
 #pragma unroll
         for (int ww = 0; ww < kWaves; ++ww) wcount[ww][d] += lb;
     }
@@ -388,7 +397,7 @@ template <int ITEMS>
 static void launch_scatter_items(const SortPass& p, int64_t n, int tile_log2, const int32_t* hist,
                                  const int32_t* totals, const int32_t* status, int64_t nb, hipStream_t s) {
     const bool stage_src = p.src_out != nullptr || p.digit_src != p.dest_in;
-    const dim3 grid((unsigned)nb), block(kThreads);
+    const dim3 grid((unsigned)(kXcds * ((nb + kXcds - 1) / kXcds))), block(kThreads);
     if (p.bits <= 8) {
         if (stage_src)
             hipLaunchKernelGGL((radix_scatter_kernel<ITEMS, 256, true>), grid, block, 0, s, p, n, tile_log2, hist, nb,
