@@ -81,6 +81,68 @@ def test_sort_large_tiles_match_oracle(dr, sort_tile_log2, n, D, with_src, src_b
     assert np.array_equal(host(inv), want_inv)
 
 
+BOUNDARY_SORT_CASES = [
+    # (n, num_dests, distribution): sizes around the 1 K / 8 K tile steps,
+    # one to four digit passes, and a single repeated key
+    (1, 1, "uniform"),
+    (63, 5, "uniform"),
+    (64, 256, "uniform"),
+    (65, 257, "zipf"),
+    (1025, 65536, "zipf"),
+    (4097, 2, "uniform"),
+    (8191, 300, "zipf"),
+    (8192, 65536, "uniform"),
+    (8193, 65536, "zipf"),
+    (20000, 1 << 20, "uniform"),   # three 7-bit passes
+    (32767, 1 << 25, "uniform"),   # four passes
+    (32768, 65536, "zipf"),
+    (32768, 7, "same"),            # every key equal: the identity permutation
+    (32769, 65536, "zipf"),
+]
+
+
+@pytest.mark.parametrize("n,D,dist", BOUNDARY_SORT_CASES)
+def test_sort_tile_boundaries_match_oracle(dr, n, D, dist):
+    """Sizes one below, at and one above tile multiples, with the default tile
+    and with 2^10-key tiles, equal the oracle."""
+    say(f"sort n={n} D={D} {dist}")
+    rng = np.random.default_rng(3 * n + D)
+    if dist == "zipf":
+        dest = np.minimum(rng.zipf(1.2, n) - 1, D - 1).astype(np.int32)
+    elif dist == "same":
+        dest = np.full(n, D - 1, np.int32)
+    else:
+        dest = rng.integers(0, D, n).astype(np.int32)
+    want_perm, want_seg, want_inv = oracle.sort_by_dest(dest, D, None)
+    for tile in (0, 10):
+        dr.dr_set_launch_params(sort_tile_log2=tile)
+        try:
+            perm, seg, inv = dr.dr_sort_by_dest(dev(dest), D)
+        finally:
+            dr.dr_set_launch_params(reset=True)
+        assert np.array_equal(host(perm), want_perm), f"perm, sort tile {tile}"
+        assert np.array_equal(host(seg), want_seg), f"seg_offsets, sort tile {tile}"
+        assert np.array_equal(host(inv), want_inv), f"inv_perm, sort tile {tile}"
+
+
+@pytest.mark.parametrize("bad_value", [-1, 100])
+def test_index_add_rejects_bad_index(dr, bad_value):
+    """An index outside [0, D), here the last of a ragged tile, sets the status
+    and leaves out untouched."""
+    say(f"index_add with a bad index {bad_value}")
+    rng = np.random.default_rng(5)
+    n, D, H = 3000, 100, 64
+    index = rng.integers(0, D, n).astype(np.int32)
+    index[2999] = bad_value
+    out0 = workloads.normal_f32(5, 0, D * H).reshape(D, H)
+    o = dev(out0)
+    src = workloads.normal_f32(5, 1, n * H).reshape(n, H)
+    _, ws = dr.dr_index_add(o, dev(src), dev(index))
+    with pytest.raises(dr.DetReduceError):
+        dr.dr_workspace_status(ws)
+    assert_bits_equal(host(o), out0, "out after a bad index")
+
+
 # ---------------------------------------------------------------------------
 # combine
 # ---------------------------------------------------------------------------
