@@ -9,7 +9,8 @@ sparse_attn_dk / embedding_grad: a step is dr_index_add_fingerprinted (stable
   the reused-plan time (sort done once, as when the indices are known a step
   early), are reported beside it.
 splitk_mhc: a step is dr_splitk_gemm_tn (64 private fp32 partials by bf16
-  MFMA), dr_splitk_reduce in split-id order, and dr_fingerprint of dW.
+  MFMA) and dr_splitk_reduce_fingerprinted (the reduce in split-id order,
+  hashing dW as it stores it).
 decode_attention: a step is dr_decode_attention (chunk partials over the
   head-major KV cache with a fixed 512-token partition, then the merge in
   chunk order) and dr_fingerprint of the output.  The token-major layout is
@@ -470,21 +471,21 @@ def _splitk(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only):
     partials = torch.empty(S, M, N, dtype=torch.float32, device="cuda")
     dW = torch.empty(M, N, dtype=torch.float32, device="cuda")
     fp = torch.empty(1, dtype=torch.int64, device="cuda")
-    ws_fp = torch.empty(dr.dr_fingerprint_workspace_size(M * N * 4), dtype=torch.uint8, device="cuda")
+    ws_rf = torch.empty(dr.dr_splitk_reduce_fingerprinted_workspace_size(S, M * N), dtype=torch.uint8,
+                        device="cuda")
     gemm_bytes = K * M * 2 + K * N * 2 + S * M * N * 4
     red_bytes = S * M * N * 4 + M * N * 4
-    step_bytes = gemm_bytes + red_bytes + M * N * 4
+    # the reduce hashes dW as it stores it: the fingerprint reads nothing more
+    step_bytes = gemm_bytes + red_bytes
     flops = 2 * K * M * N
-    timer = _Timer(torch, ["splitk_gemm", "splitk_reduce", "fingerprint"])
+    timer = _Timer(torch, ["splitk_gemm", "splitk_reduce"])
 
     def step(evs=None):
         if evs: evs[0].record()
         dr.dr_splitk_gemm_tn(X, dY, S, partials=partials)
         if evs: evs[1].record()
-        dr.dr_splitk_reduce(partials, out=dW)
+        dr.dr_splitk_reduce_fingerprinted(partials, fp, out=dW, ws=ws_rf)
         if evs: evs[2].record()
-        dr.dr_fingerprint(dW, out=fp, ws=ws_fp)
-        if evs: evs[3].record()
 
     for _ in range(warmup):
         step()
@@ -553,7 +554,8 @@ def _splitk(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only):
         "eager_ms_per_step": round(eager_ms, 4),
         "config": {"workload": f"{name}: dW = X^T dY, X bf16 [{K},{M}], dY bf16 [{K},{N}], {S} splits",
                    "K": K, "M": M, "N": N, "splits": S,
-                   "step": "MFMA partials + ordered split reduce + fingerprint", "step_algorithmic_bytes": step_bytes},
+                   "step": "MFMA partials + ordered split reduce hashing dW as it stores it (the splitk_reduce "
+                           "phase includes the fingerprint)", "step_algorithmic_bytes": step_bytes},
         "roofline": {"bound": "hbm", "kernel": "splitk_gemm_kernel", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("splitk_gemm_kernel", name, source_digest("splitk.hip", "device.h")),

@@ -23,6 +23,7 @@ __all__ = [
     "dr_index_add_workspace_size", "dr_index_add", "dr_index_add_fingerprinted", "dr_index_add_atomic",
     "dr_sparse_attn_dk_workspace_size", "dr_sparse_attn_dk",
     "dr_splitk_gemm_tn", "dr_splitk_gemm_tn_atomic", "dr_splitk_reduce",
+    "dr_splitk_reduce_fingerprinted_workspace_size", "dr_splitk_reduce_fingerprinted",
     "dr_grouped_splitk_max_slots", "dr_grouped_splitk_workspace_size", "dr_grouped_splitk_gemm_tn",
     "dr_grouped_splitk_reduce", "dr_permute_rows",
     "dr_decode_attention_workspace_size", "dr_decode_attention", "dr_decode_attention_occupancy_chunk",
@@ -71,6 +72,8 @@ def _load() -> ctypes.CDLL:
         "dr_splitk_gemm_tn": ([vp, vp, i64, i64, i64, i32, vp, vp], ctypes.c_int),
         "dr_splitk_gemm_tn_atomic": ([vp, vp, i64, i64, i64, i32, vp, vp], ctypes.c_int),
         "dr_splitk_reduce": ([vp, i32, i64, vp, vp], ctypes.c_int),
+        "dr_splitk_reduce_fingerprinted_workspace_size": ([i32, i64], sz),
+        "dr_splitk_reduce_fingerprinted": ([vp, i32, i64, vp, vp, vp, sz, vp], ctypes.c_int),
         "dr_grouped_splitk_max_slots": ([i64, i32, i32], i64),
         "dr_grouped_splitk_workspace_size": ([i64, i32, i32], sz),
         "dr_grouped_splitk_gemm_tn": ([vp, vp, i64, i64, i64, vp, i32, i32, vp, i64, vp, vp, sz, vp], ctypes.c_int),
@@ -347,6 +350,25 @@ def dr_splitk_reduce(partials, *, out=None, stream=None):
     out = out if out is not None else torch.empty(partials.shape[1:], dtype=torch.float32, device=partials.device)
     _dev(out, "out", (torch.float32,))
     _check(lib.dr_splitk_reduce(_p(partials), S, count, _p(out), _stream(stream)), "dr_splitk_reduce")
+    return out
+
+
+def dr_splitk_reduce_fingerprinted_workspace_size(splits: int, count: int) -> int:
+    return lib.dr_splitk_reduce_fingerprinted_workspace_size(splits, count)
+
+
+def dr_splitk_reduce_fingerprinted(partials, out_hash, *, out=None, ws=None, stream=None):
+    """dr_splitk_reduce that also writes dr_fingerprint(out) to out_hash (int64 [1] on the device)."""
+    _dev(partials, "partials", (torch.float32,))
+    _dev(out_hash, "out_hash", (torch.int64,))
+    S = partials.shape[0]
+    count = partials.numel() // S
+    out = out if out is not None else torch.empty(partials.shape[1:], dtype=torch.float32, device=partials.device)
+    _dev(out, "out", (torch.float32,))
+    need = dr_splitk_reduce_fingerprinted_workspace_size(S, count)
+    ws = ws if ws is not None else _workspace(need, partials.device)
+    _check(lib.dr_splitk_reduce_fingerprinted(_p(partials), S, count, _p(out), _p(out_hash), _p(ws), ws.numel(),
+                                              _stream(stream)), "dr_splitk_reduce_fingerprinted")
     return out
 
 

@@ -643,7 +643,48 @@ dr_status dr_splitk_reduce(const float* partials, int32_t splits, int64_t count,
     if (count > 0 && (!aligned(partials, 16) || !aligned(out, 16)))
         return fail(DR_ERR_INVALID_ARGUMENT, "%s: partials and out must be 16-byte aligned", what);
     if (splits >= (1 << 27)) return fail(DR_ERR_UNSUPPORTED, "%s: too many splits", what);
-    DR_TRY_HIP(dr::launch_splitk_reduce(partials, splits, count, out, stream), "split reduce launch");
+    DR_TRY_HIP(dr::launch_splitk_reduce(partials, splits, count, out, nullptr, stream), "split reduce launch");
+    return ok();
+}
+
+size_t dr_splitk_reduce_fingerprinted_workspace_size(int32_t splits, int64_t count) {
+    if (splits < 1 || count < 0) return dr_fingerprint_workspace_size(0);
+    const int64_t nb = dr::splitk_reduce_blocks(splits, count);
+    const size_t fused = dr::kStatusBytes + align_up((size_t)nb * sizeof(uint64_t)) +
+                         align_up((size_t)dr::fingerprint_group_count(nb) * sizeof(uint64_t));
+    const size_t separate = dr_fingerprint_workspace_size(count * (int64_t)sizeof(float));
+    return fused > separate ? fused : separate;
+}
+
+dr_status dr_splitk_reduce_fingerprinted(const float* partials, int32_t splits, int64_t count, float* out,
+                                         uint64_t* out_hash, void* ws, size_t ws_bytes, hipStream_t stream) {
+    const char* what = "dr_splitk_reduce_fingerprinted";
+    if (splits < 1) return fail(DR_ERR_INVALID_ARGUMENT, "%s: splits must be >= 1", what);
+    if (count < 0) return fail(DR_ERR_INVALID_ARGUMENT, "%s: count must be >= 0", what);
+    if (count > 0 && (!partials || !out)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: null pointer", what);
+    if (count > 0 && (!aligned(partials, 16) || !aligned(out, 16)))
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: partials and out must be 16-byte aligned", what);
+    if (splits >= (1 << 27)) return fail(DR_ERR_UNSUPPORTED, "%s: too many splits", what);
+    if (!out_hash || !aligned(out_hash, 8)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: bad out_hash", what);
+    if (!ws || !aligned(ws, 16)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: bad workspace", what);
+    const size_t need = dr_splitk_reduce_fingerprinted_workspace_size(splits, count);
+    if (ws_bytes < need)
+        return fail(DR_ERR_WORKSPACE_TOO_SMALL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes, need);
+    const int64_t nbytes = count * (int64_t)sizeof(float);
+    if (count % 4 != 0) {
+        // pieces of 16 bytes are what the reduce hashes as it stores; otherwise hash out afterwards
+        DR_TRY_HIP(dr::launch_splitk_reduce(partials, splits, count, out, nullptr, stream), "split reduce launch");
+        uint64_t* parts = reinterpret_cast<uint64_t*>(static_cast<char*>(ws) + dr::kStatusBytes);
+        DR_TRY_HIP(dr::launch_fingerprint(out, nbytes, out_hash, parts, stream), "fingerprint launch");
+        return ok();
+    }
+    const int64_t nb = dr::splitk_reduce_blocks(splits, count);
+    Carver c(ws);
+    c.take<uint8_t>(dr::kStatusBytes);
+    uint64_t* parts = c.take<uint64_t>(nb);
+    uint64_t* group_sums = c.take<uint64_t>(dr::fingerprint_group_count(nb));
+    DR_TRY_HIP(dr::launch_splitk_reduce(partials, splits, count, out, parts, stream), "split reduce launch");
+    DR_TRY_HIP(dr::launch_fingerprint_final(parts, nb, nbytes, out_hash, group_sums, stream), "fingerprint launch");
     return ok();
 }
 

@@ -142,7 +142,10 @@ hipError_t launch_index_add_atomic(float* out, int32_t num_dests, int64_t hidden
 // split-K
 hipError_t launch_splitk_gemm(const uint16_t* X, const uint16_t* dY, int64_t K, int64_t M, int64_t N,
                               int32_t splits, float* out, bool atomic, hipStream_t s);
-hipError_t launch_splitk_reduce(const float* partials, int32_t splits, int64_t count, float* out,
+// fp_part != nullptr (count a multiple of 4): the launch also writes the
+// fingerprint terms of out, one partial sum per workgroup
+int64_t splitk_reduce_blocks(int32_t splits, int64_t count);
+hipError_t launch_splitk_reduce(const float* partials, int32_t splits, int64_t count, float* out, uint64_t* fp_part,
                                 hipStream_t s);
 // grouped split with private slots: the slot table, then the partials of every slot
 hipError_t launch_grouped_splitk_gemm(const uint16_t* X, const uint16_t* dY, int64_t K, int64_t M, int64_t N,

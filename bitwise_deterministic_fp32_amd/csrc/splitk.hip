@@ -319,12 +319,31 @@ __device__ __forceinline__ void reduce_splits(const float* __restrict__ P, int S
     }
 }
 
+// With fp_part (VEC == 4 only), each workgroup also writes the fingerprint
+// terms of the 16-byte pieces it stored (words e0/2 and e0/2 + 1) to
+// fp_part[blockIdx.x]; the thread reads back its own store.
+__device__ __forceinline__ uint64_t fp_terms_of_piece(const float* out, int64_t e0) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(out + e0);
+    return fp_term(((uint64_t)v.y << 32) | v.x, e0 >> 1) + fp_term(((uint64_t)v.w << 32) | v.z, (e0 >> 1) + 1);
+}
+
 template <int VEC>
 __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(const float* __restrict__ P, int S,
-                                                                       int64_t count, float* __restrict__ out) {
+                                                                       int64_t count, float* __restrict__ out,
+                                                                       uint64_t* __restrict__ fp_part) {
     const int64_t e0 = ((int64_t)blockIdx.x * kReduceThreads + threadIdx.x) * VEC;
-    if (e0 >= count) return;
-    reduce_splits<VEC>(P, S, count, e0, out);
+    if (!fp_part) {
+        if (e0 < count) reduce_splits<VEC>(P, S, count, e0, out);
+        return;
+    }
+    uint64_t h = 0;
+    if (e0 < count) {
+        reduce_splits<VEC>(P, S, count, e0, out);
+        if (VEC == 4) h = fp_terms_of_piece(out, e0);
+    }
+    __shared__ uint64_t fsm[kReduceThreads / 64];
+    const uint64_t b = block_sum_u64(h, fsm);
+    if (threadIdx.x == 0) fp_part[blockIdx.x] = b;
 }
 
 // The same tree with L lanes per output vector (L = the chunk count rounded up
@@ -337,7 +356,8 @@ __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_kernel(const flo
 template <int VEC, int L>
 __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_lanes_kernel(const float* __restrict__ P, int S,
                                                                              int64_t count,
-                                                                             float* __restrict__ out) {
+                                                                             float* __restrict__ out,
+                                                                             uint64_t* __restrict__ fp_part) {
     const int64_t t = (int64_t)blockIdx.x * kReduceThreads + threadIdx.x;
     const int c = (int)(t % L);  // this lane's chunk
     const int64_t e0 = (t / L) * VEC;
@@ -385,6 +405,19 @@ __global__ __launch_bounds__(kReduceThreads) void splitk_reduce_lanes_kernel(con
         } else {
             out[e0] = s[0];
         }
+    }
+    if (fp_part) {
+        // the fingerprint terms of the stored piece (VEC == 4 only), summed per workgroup
+        uint64_t h = 0;
+        if (VEC == 4 && live && c == 0) {
+            const uint64_t w0 = ((uint64_t)__float_as_uint(s[VEC > 1 ? 1 : 0]) << 32) | __float_as_uint(s[0]);
+            const uint64_t w1 =
+                ((uint64_t)__float_as_uint(s[VEC > 3 ? 3 : 0]) << 32) | __float_as_uint(s[VEC > 2 ? 2 : 0]);
+            h = fp_term(w0, e0 >> 1) + fp_term(w1, (e0 >> 1) + 1);
+        }
+        __shared__ uint64_t fsm[kReduceThreads / 64];
+        const uint64_t b = block_sum_u64(h, fsm);
+        if (threadIdx.x == 0) fp_part[blockIdx.x] = b;
     }
 }
 
@@ -528,19 +561,33 @@ hipError_t launch_grouped_reduce(const float* partials, const int32_t* slot_offs
     return hipGetLastError();
 }
 
-hipError_t launch_splitk_reduce(const float* partials, int32_t splits, int64_t count, float* out, hipStream_t s) {
+// Workgroups of a split reduce launch (and fingerprint partials it writes).
+int64_t splitk_reduce_blocks(int32_t splits, int64_t count) {
+    if (count <= 0) return 0;
+    const int64_t vectors = (count % 4) == 0 ? count / 4 : count;
+    const int64_t chunks = ((int64_t)splits + 7) / 8;
+    int64_t lanes = 1;
+    if (chunks >= 2 && chunks <= 64) {
+        lanes = 2;
+        while (lanes < chunks) lanes <<= 1;
+    }
+    return (vectors * lanes + kReduceThreads - 1) / kReduceThreads;
+}
+
+hipError_t launch_splitk_reduce(const float* partials, int32_t splits, int64_t count, float* out, uint64_t* fp_part,
+                                hipStream_t s) {
     if (count == 0) return hipSuccess;
     const bool vec = (count % 4) == 0;
-    const int64_t vectors = vec ? count / 4 : count;
+    if (fp_part && !vec) return hipErrorInvalidValue;  // the fused fingerprint hashes 16-byte pieces
     const int64_t chunks = ((int64_t)splits + 7) / 8;
+    const dim3 grid((unsigned)splitk_reduce_blocks(splits, count)), block(kReduceThreads);
     if (chunks >= 2 && chunks <= 64) {
         // a lane per chunk of 8 splits
         int lanes = 2;
         while (lanes < chunks) lanes <<= 1;
-        const dim3 lgrid((unsigned)((vectors * lanes + kReduceThreads - 1) / kReduceThreads));
 #define DR_RL(V, LN)                                                                                           \
-    hipLaunchKernelGGL((splitk_reduce_lanes_kernel<V, LN>), lgrid, dim3(kReduceThreads), 0, s, partials, splits, \
-                       count, out)
+    hipLaunchKernelGGL((splitk_reduce_lanes_kernel<V, LN>), grid, block, 0, s, partials, splits, count, out, \
+                       fp_part)
 #define DR_RL_V(V)                    \
     switch (lanes) {                  \
         case 2: DR_RL(V, 2); break;   \
@@ -559,12 +606,10 @@ hipError_t launch_splitk_reduce(const float* partials, int32_t splits, int64_t c
 #undef DR_RL
         return hipGetLastError();
     }
-    const int64_t threads = vectors;
-    const dim3 grid((unsigned)((threads + kReduceThreads - 1) / kReduceThreads));
     if (vec)
-        hipLaunchKernelGGL(splitk_reduce_kernel<4>, grid, dim3(kReduceThreads), 0, s, partials, splits, count, out);
+        hipLaunchKernelGGL(splitk_reduce_kernel<4>, grid, block, 0, s, partials, splits, count, out, fp_part);
     else
-        hipLaunchKernelGGL(splitk_reduce_kernel<1>, grid, dim3(kReduceThreads), 0, s, partials, splits, count, out);
+        hipLaunchKernelGGL(splitk_reduce_kernel<1>, grid, block, 0, s, partials, splits, count, out, fp_part);
     return hipGetLastError();
 }
 

@@ -291,6 +291,19 @@ dr_status dr_splitk_gemm_tn(const void* X, const void* dY, int64_t K, int64_t M,
 dr_status dr_splitk_reduce(const float* partials, int32_t splits, int64_t count, float* out,
                            hipStream_t stream);
 
+/* The same reduce, also writing dr_fingerprint(out) to *out_hash (device
+ * uint64).  When count is a multiple of 4, the reduce hashes each 16-byte
+ * piece as it stores it, so out is not read back; otherwise out is hashed
+ * after the reduce.  out and *out_hash equal those of dr_splitk_reduce
+ * followed by dr_fingerprint(out, 4 * count).
+ *   ws   >= dr_splitk_reduce_fingerprinted_workspace_size() bytes, 16-byte
+ *        aligned, contents on entry do not matter.
+ * Errors: the argument checks of dr_splitk_reduce, a null or misaligned
+ * out_hash or ws, and a short workspace return an error before any launch. */
+size_t dr_splitk_reduce_fingerprinted_workspace_size(int32_t splits, int64_t count);
+dr_status dr_splitk_reduce_fingerprinted(const float* partials, int32_t splits, int64_t count, float* out,
+                                         uint64_t* out_hash, void* ws, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Grouped split with private slots: per group g (an expert),
  *   dW[g] = T over its slots s of  X_s^T dY_s   (slot order),

@@ -130,6 +130,38 @@ def test_splitk_graph(dr):
         torch.cuda.synchronize()
 
 
+def test_splitk_reduce_fingerprinted_graph(dr):
+    """The split-K step with the fused reduce and fingerprint, replayed from a graph."""
+    say("graph: split-K partials + reduce with its fingerprint")
+    sk = workloads.splitk_inputs(46, 4096, 1000, 24, 64)
+    X, dY = dev_bf16(sk.X), dev_bf16(sk.dY)
+    P = torch.empty(64, 1000, 24, dtype=torch.float32, device="cuda")
+    dW = torch.empty(1000, 24, dtype=torch.float32, device="cuda")
+    h = torch.zeros(1, dtype=torch.int64, device="cuda")
+    ws = torch.empty(dr.dr_splitk_reduce_fingerprinted_workspace_size(64, 1000 * 24), dtype=torch.uint8,
+                     device="cuda")
+
+    def call():
+        dr.dr_splitk_gemm_tn(X, dY, 64, partials=P)
+        dr.dr_splitk_reduce_fingerprinted(P, h, out=dW, ws=ws)
+
+    call()
+    want = host(dW).copy()
+    want_h = int(h.item())
+    assert want_h == int(dr.dr_fingerprint(dW).item())
+    g = capture(call)
+    for r in range(3):
+        dW.fill_(3.0)
+        P.fill_(float("nan"))
+        h.fill_(0)
+        ws.fill_(0xFF)
+        g.replay()
+        assert_bits_equal(host(dW), want, f"replay {r}")
+        assert int(h.item()) == want_h, f"replay {r}: fingerprint"
+        dr.dr_splitk_gemm_tn(X[:256].contiguous(), dY[:256].contiguous(), 1)
+        torch.cuda.synchronize()
+
+
 def test_index_add_fingerprinted_graph(dr):
     """The destination's fingerprint stays current over eager calls and over graph replays."""
     say("graph: index_add_fingerprinted, accumulating")

@@ -397,6 +397,32 @@ def test_splitk_reduce_split_counts(dr, S, count):
     assert_bits_equal(got, oracle.splitk_reduce(P), f"splitk_reduce S={S}")
 
 
+@pytest.mark.parametrize("S,count", [
+    (64, 7168 * 24),  # a lane per chunk, hashed as stored
+    (1, 4096),        # one thread per 4 elements, hashed as stored
+    (600, 4096),      # more than 64 chunks: one thread walks them
+    (9, 1001),        # count not a multiple of 4: hashed after the reduce
+    (5, 0),
+    (16, 4),
+])
+def test_splitk_reduce_fingerprinted(dr, S, count):
+    """The reduce with its fingerprint equals dr_splitk_reduce and
+    dr_fingerprint, and the oracle's tree and fingerprint, bit for bit."""
+    say(f"splitk_reduce_fingerprinted S={S} count={count}")
+    rng = np.random.default_rng(S * 31 + count)
+    P = (rng.standard_normal((S, count)) * np.exp2(rng.integers(-20, 20, (S, count)))).astype(np.float32)
+    P[rng.random((S, count)) < 0.01] = np.float32(-0.0)
+    h = torch.zeros(1, dtype=torch.int64, device="cuda")
+    ws = torch.full((dr.dr_splitk_reduce_fingerprinted_workspace_size(S, count),), 0xFF, dtype=torch.uint8,
+                    device="cuda")
+    got = dr.dr_splitk_reduce_fingerprinted(dev(P), h, ws=ws)
+    want = oracle.splitk_reduce(P)
+    assert_bits_equal(host(got), want, f"splitk_reduce_fingerprinted S={S}")
+    assert _hash_value(h) == oracle.fingerprint(want), "fused fingerprint differs from the oracle's"
+    h2 = dr.dr_fingerprint(dr.dr_splitk_reduce(dev(P)))
+    assert _hash_value(h) == _hash_value(h2), "fused fingerprint differs from dr_fingerprint"
+
+
 @pytest.mark.parametrize("K,M,N,splits", [
     (1024, 256, 24, 4),
     (1000, 200, 24, 7),     # ragged splits and a ragged M tile
