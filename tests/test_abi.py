@@ -322,3 +322,24 @@ def test_kernels_have_no_fused_multiply_add():
             found = [x for x in found if x.startswith(("v_pk_", "v_mad_", "v_mac_"))]
         assert not found, (src, found)
         assert "scratch_store" not in asm or src == "splitk.hip", src
+
+
+def test_splitk_reduce_fingerprinted_rejects_bad_arguments(lib):
+    """Argument checks of the reduce with its fingerprint fail before any launch."""
+    lib.dr_splitk_reduce_fingerprinted_workspace_size.restype = ctypes.c_size_t
+    lib.dr_splitk_reduce_fingerprinted_workspace_size.argtypes = [ctypes.c_int32, ctypes.c_int64]
+    need = lib.dr_splitk_reduce_fingerprinted_workspace_size(64, 7168 * 24)
+    assert need >= lib.dr_splitk_reduce_fingerprinted_workspace_size(64, 0) > 0
+    f = lib.dr_splitk_reduce_fingerprinted
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_size_t, ctypes.c_void_p]
+    n = 7168 * 24
+    assert f(FAKE, 0, n, FAKE, FAKE, FAKE, need, None) == DR_ERR_INVALID_ARGUMENT        # no splits
+    assert f(FAKE, 64, -1, FAKE, FAKE, FAKE, need, None) == DR_ERR_INVALID_ARGUMENT      # negative count
+    assert f(None, 64, n, FAKE, FAKE, FAKE, need, None) == DR_ERR_INVALID_ARGUMENT       # null partials
+    assert f(FAKE + 4, 64, n, FAKE, FAKE, FAKE, need, None) == DR_ERR_INVALID_ARGUMENT   # misaligned partials
+    assert f(FAKE, 64, n, FAKE, None, FAKE, need, None) == DR_ERR_INVALID_ARGUMENT       # null out_hash
+    assert f(FAKE, 64, n, FAKE, FAKE + 4, FAKE, need, None) == DR_ERR_INVALID_ARGUMENT   # misaligned out_hash
+    assert f(FAKE, 64, n, FAKE, FAKE, None, need, None) == DR_ERR_INVALID_ARGUMENT       # null workspace
+    assert f(FAKE, 64, n, FAKE, FAKE, FAKE, need - 1, None) == DR_ERR_WORKSPACE_TOO_SMALL
+    assert f(FAKE, 1 << 27, n, FAKE, FAKE, FAKE, need, None) == DR_ERR_UNSUPPORTED
