@@ -36,6 +36,7 @@ LIB_PATH = os.path.join(_HERE, "libdetreduce.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "detreduce.h")
 
 DR_F32, DR_BF16 = 0, 1
+_STATUS_BYTES = 256  # the status block at the start of every workspace
 _DTYPES = {torch.float32: DR_F32, torch.bfloat16: DR_BF16}
 
 
@@ -177,6 +178,41 @@ def _workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 16), dtype=torch.uint8, device=device)
 
 
+def _sized(t: torch.Tensor, name: str, device, dtypes=None, shape=None, numel=None, min_numel=None) -> torch.Tensor:
+    """A caller-supplied buffer: on `device`, contiguous, of the given dtype and
+    exactly `shape` (or `numel` elements, or at least `min_numel`).  A buffer
+    too small for what the kernels write would be an out-of-bounds access on the
+    device, so every mismatch is refused here, before anything is launched."""
+    _dev(t, name, dtypes)
+    if t.device != torch.device(device):
+        raise ValueError(f"{name} is on {t.device}, the other tensors on {device}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, got {t.numel()}")
+    if min_numel is not None and t.numel() < min_numel:
+        raise ValueError(f"{name} must hold at least {min_numel} elements, got {t.numel()}")
+    return t
+
+
+def _ws(ws, need: int, device, name: str = "ws") -> torch.Tensor:
+    """A workspace: the caller's (a uint8 tensor on `device`, its numel is the
+    byte count passed on) or a new one of `need` bytes."""
+    if ws is None:
+        return _workspace(need, device)
+    return _sized(ws, name, device, (torch.uint8,), min_numel=need)
+
+
+def _status_buf(dev_status, device):
+    if dev_status is not None:
+        _sized(dev_status, "dev_status", device, (torch.int32,), min_numel=1)
+    return dev_status
+
+
+def _hash_buf(h, name: str, device) -> torch.Tensor:
+    return _sized(h, name, device, (torch.int64,), numel=1)
+
+
 # ---------------------------------------------------------------------------
 def dr_sort_workspace_size(n: int, num_dests: int, src_id_bound: int = 0) -> int:
     return int(lib.dr_sort_workspace_size(n, num_dests, src_id_bound))
@@ -189,13 +225,18 @@ def dr_sort_by_dest(dest, num_dests: int, src_id=None, src_id_bound: int = 0, *,
     n = dest.numel()
     dev = dest.device
     if src_id is not None:
-        _dev(src_id, "src_id", (torch.int32,))
-    perm = perm if perm is not None else torch.empty(n, dtype=torch.int32, device=dev)
-    seg_offsets = seg_offsets if seg_offsets is not None else torch.empty(num_dests + 1, dtype=torch.int32, device=dev)
+        _sized(src_id, "src_id", dev, (torch.int32,), numel=n)
+    i32 = (torch.int32,)
+    perm = _sized(perm, "perm", dev, i32, numel=n) if perm is not None else \
+        torch.empty(n, dtype=torch.int32, device=dev)
+    seg_offsets = _sized(seg_offsets, "seg_offsets", dev, i32, numel=num_dests + 1) if seg_offsets is not None \
+        else torch.empty(num_dests + 1, dtype=torch.int32, device=dev)
     if inv_perm is None and want_inv:
         inv_perm = torch.empty(n, dtype=torch.int32, device=dev)
+    elif inv_perm is not None:
+        _sized(inv_perm, "inv_perm", dev, i32, numel=n)
     need = dr_sort_workspace_size(n, num_dests, src_id_bound if src_id is not None else 0)
-    ws = ws if ws is not None else _workspace(need, dev)
+    ws = _ws(ws, need, dev)
     _check(lib.dr_sort_by_dest(_p(dest), _p(src_id), src_id_bound, n, num_dests, _p(perm), _p(seg_offsets),
                                _p(inv_perm), _p(ws), ws.numel(), _stream(stream)), "dr_sort_by_dest")
     return perm, seg_offsets, inv_perm
@@ -203,18 +244,24 @@ def dr_sort_by_dest(dest, num_dests: int, src_id=None, src_id_bound: int = 0, *,
 
 def _combine_args(rows, row_of, gates):
     _dev(rows, "rows", tuple(_DTYPES))
-    _dev(row_of, "row_of", (torch.int32,))
-    _dev(gates, "gates", (torch.float32,))
+    _sized(row_of, "row_of", rows.device, (torch.int32,))
+    _sized(gates, "gates", rows.device, (torch.float32,))
     if rows.dim() != 2 or row_of.dim() != 2 or gates.shape != row_of.shape:
         raise ValueError("rows must be [R, H]; row_of and gates [T, k]")
     return rows.shape[0], rows.shape[1], row_of.shape[0], row_of.shape[1]
 
 
+def _combine_out(out, rows, T, H):
+    if out is None:
+        return torch.empty(T, H, dtype=torch.float32, device=rows.device)
+    return _sized(out, "out", rows.device, (torch.float32,), shape=(T, H))
+
+
 def dr_combine(rows, row_of, gates, *, out=None, dev_status=None, stream=None):
     """out[t] = ordered tree over fl32(gate * row) of the token's k rows (written)."""
     R, H, T, k = _combine_args(rows, row_of, gates)
-    out = out if out is not None else torch.empty(T, H, dtype=torch.float32, device=rows.device)
-    _dev(out, "out", (torch.float32,))
+    out = _combine_out(out, rows, T, H)
+    _status_buf(dev_status, rows.device)
     _check(lib.dr_combine(_p(rows), _DTYPES[rows.dtype], R, H, _p(row_of), _p(gates), T, k, _p(out),
                           _p(dev_status), _stream(stream)), "dr_combine")
     return out
@@ -227,10 +274,11 @@ def dr_combine_fingerprinted_workspace_size(rows_dtype, hidden: int, T: int) -> 
 def dr_combine_fingerprinted(rows, row_of, gates, *, out=None, out_hash=None, ws=None, dev_status=None, stream=None):
     """dr_combine plus the fingerprint of its output, hashed as it is stored.  Returns (out, out_hash)."""
     R, H, T, k = _combine_args(rows, row_of, gates)
-    out = out if out is not None else torch.empty(T, H, dtype=torch.float32, device=rows.device)
-    _dev(out, "out", (torch.float32,))
-    out_hash = out_hash if out_hash is not None else torch.empty(1, dtype=torch.int64, device=rows.device)
-    ws = ws if ws is not None else _workspace(dr_combine_fingerprinted_workspace_size(rows.dtype, H, T), rows.device)
+    out = _combine_out(out, rows, T, H)
+    out_hash = _hash_buf(out_hash, "out_hash", rows.device) if out_hash is not None else \
+        torch.empty(1, dtype=torch.int64, device=rows.device)
+    ws = _ws(ws, dr_combine_fingerprinted_workspace_size(rows.dtype, H, T), rows.device)
+    _status_buf(dev_status, rows.device)
     _check(lib.dr_combine_fingerprinted(_p(rows), _DTYPES[rows.dtype], R, H, _p(row_of), _p(gates), T, k, _p(out),
                                         _p(out_hash), _p(ws), ws.numel(), _p(dev_status), _stream(stream)),
            "dr_combine_fingerprinted")
@@ -240,7 +288,8 @@ def dr_combine_fingerprinted(rows, row_of, gates, *, out=None, out_hash=None, ws
 def dr_combine_atomic(rows, row_of, gates, *, out, dev_status=None, stream=None):
     """Nondeterministic baseline: atomically adds each fl32(gate * row) into out (caller zeroes it)."""
     R, H, T, k = _combine_args(rows, row_of, gates)
-    _dev(out, "out", (torch.float32,))
+    _sized(out, "out", rows.device, (torch.float32,), shape=(T, H))
+    _status_buf(dev_status, rows.device)
     _check(lib.dr_combine_atomic(_p(rows), _DTYPES[rows.dtype], R, H, _p(row_of), _p(gates), T, k, _p(out),
                                  _p(dev_status), _stream(stream)), "dr_combine_atomic")
     return out
@@ -251,16 +300,30 @@ def dr_index_add_workspace_size(n: int, num_dests: int, hidden: int) -> int:
     return int(lib.dr_index_add_workspace_size(n, num_dests, hidden))
 
 
+def _index_add_args(out, src, index, perm, seg_offsets):
+    _dev(out, "out", (torch.float32,))
+    if out.dim() != 2:
+        raise ValueError("out must be [num_dests, hidden]")
+    D, H = out.shape
+    _sized(index, "index", out.device, (torch.int32,))
+    n = index.numel()
+    _sized(src, "src", out.device, tuple(_DTYPES), shape=(n, H))
+    _plan_args(perm, seg_offsets, n, D, out.device)
+    return D, H, n
+
+
+def _plan_args(perm, seg_offsets, n, D, device):
+    if (perm is None) != (seg_offsets is None):
+        raise ValueError("perm and seg_offsets must both be given or both be None")
+    if perm is not None:
+        _sized(perm, "perm", device, (torch.int32,), numel=n)
+        _sized(seg_offsets, "seg_offsets", device, (torch.int32,), numel=D + 1)
+
+
 def dr_index_add(out, src, index, *, perm=None, seg_offsets=None, ws=None, stream=None):
     """out[d] += ordered tree of src rows i with index[i] == d (in place).  Returns (out, ws)."""
-    _dev(out, "out", (torch.float32,))
-    _dev(src, "src", tuple(_DTYPES))
-    _dev(index, "index", (torch.int32,))
-    D, H = out.shape
-    n = index.numel()
-    if src.shape != (n, H):
-        raise ValueError(f"src must be [{n}, {H}], got {tuple(src.shape)}")
-    ws = ws if ws is not None else _workspace(dr_index_add_workspace_size(n, D, H), out.device)
+    D, H, n = _index_add_args(out, src, index, perm, seg_offsets)
+    ws = _ws(ws, dr_index_add_workspace_size(n, D, H), out.device)
     _check(lib.dr_index_add(_p(out), D, H, _p(src), _DTYPES[src.dtype], n, _p(index), _p(perm), _p(seg_offsets),
                             _p(ws), ws.numel(), _stream(stream)), "dr_index_add")
     return out, ws
@@ -269,17 +332,9 @@ def dr_index_add(out, src, index, *, perm=None, seg_offsets=None, ws=None, strea
 def dr_index_add_fingerprinted(out, src, index, inout_hash, *, perm=None, seg_offsets=None, ws=None, stream=None):
     """dr_index_add that moves inout_hash (an int64 device tensor of one element holding the fingerprint of
     out) to the fingerprint of the updated out.  Returns (out, ws)."""
-    _dev(out, "out", (torch.float32,))
-    _dev(src, "src", tuple(_DTYPES))
-    _dev(index, "index", (torch.int32,))
-    _dev(inout_hash, "inout_hash", (torch.int64,))
-    if inout_hash.numel() != 1:
-        raise ValueError("inout_hash must hold one element")
-    D, H = out.shape
-    n = index.numel()
-    if src.shape != (n, H):
-        raise ValueError(f"src must be [{n}, {H}], got {tuple(src.shape)}")
-    ws = ws if ws is not None else _workspace(dr_index_add_workspace_size(n, D, H), out.device)
+    D, H, n = _index_add_args(out, src, index, perm, seg_offsets)
+    _hash_buf(inout_hash, "inout_hash", out.device)
+    ws = _ws(ws, dr_index_add_workspace_size(n, D, H), out.device)
     _check(lib.dr_index_add_fingerprinted(_p(out), D, H, _p(src), _DTYPES[src.dtype], n, _p(index), _p(perm),
                                           _p(seg_offsets), _p(inout_hash), _p(ws), ws.numel(), _stream(stream)),
            "dr_index_add_fingerprinted")
@@ -294,61 +349,75 @@ def dr_sparse_attn_dk(dK, Q, dS, key_idx, *, perm=None, seg_offsets=None, ws=Non
     """dK[key] += ordered tree of fl32(dS[q, j] * Q[q]) over the (q, j) that selected key (in place).
     Returns (dK, ws)."""
     _dev(dK, "dK", (torch.float32,))
-    _dev(Q, "Q", tuple(_DTYPES))
-    _dev(dS, "dS", (torch.float32,))
-    _dev(key_idx, "key_idx", (torch.int32,))
+    _sized(key_idx, "key_idx", dK.device, (torch.int32,))
+    if dK.dim() != 2 or key_idx.dim() != 2:
+        raise ValueError("dK must be [num_keys, head_dim] and key_idx [num_queries, topk]")
     K, H = dK.shape
     nq, topk = key_idx.shape
-    if Q.shape != (nq, H) or dS.shape != (nq, topk):
-        raise ValueError(f"Q must be [{nq}, {H}] and dS [{nq}, {topk}], got {tuple(Q.shape)} and {tuple(dS.shape)}")
-    ws = ws if ws is not None else _workspace(dr_sparse_attn_dk_workspace_size(nq, topk, K, H), dK.device)
+    _sized(Q, "Q", dK.device, tuple(_DTYPES), shape=(nq, H))
+    _sized(dS, "dS", dK.device, (torch.float32,), shape=(nq, topk))
+    _plan_args(perm, seg_offsets, nq * topk, K, dK.device)
+    ws = _ws(ws, dr_sparse_attn_dk_workspace_size(nq, topk, K, H), dK.device)
     _check(lib.dr_sparse_attn_dk(_p(dK), K, H, _p(Q), _DTYPES[Q.dtype], _p(dS), _p(key_idx), nq, topk, _p(perm),
                                  _p(seg_offsets), _p(ws), ws.numel(), _stream(stream)), "dr_sparse_attn_dk")
     return dK, ws
 
 
 def dr_index_add_atomic(out, src, index, *, dev_status=None, stream=None):
-    _dev(out, "out", (torch.float32,))
-    _dev(src, "src", tuple(_DTYPES))
-    _dev(index, "index", (torch.int32,))
-    D, H = out.shape
-    n = index.numel()
+    D, H, n = _index_add_args(out, src, index, None, None)
+    _status_buf(dev_status, out.device)
     _check(lib.dr_index_add_atomic(_p(out), D, H, _p(src), _DTYPES[src.dtype], n, _p(index), _p(dev_status),
                                    _stream(stream)), "dr_index_add_atomic")
     return out
 
 
 # ---------------------------------------------------------------------------
+def _gemm_args(X, dY):
+    _dev(X, "X", (torch.bfloat16,))
+    if X.dim() != 2 or dY.dim() != 2:
+        raise ValueError("X must be [K, M] and dY [K, N]")
+    _sized(dY, "dY", X.device, (torch.bfloat16,))
+    if dY.shape[0] != X.shape[0]:
+        raise ValueError(f"X and dY must have the same number of rows (tokens), got {X.shape[0]} and {dY.shape[0]}")
+    return X.shape[0], X.shape[1], dY.shape[1]
+
+
 def dr_splitk_gemm_tn(X, dY, splits: int, *, partials=None, stream=None):
     """partials[s] = X_s^T dY_s (bf16 MFMA into fp32), one private buffer per split."""
-    _dev(X, "X", (torch.bfloat16,))
-    _dev(dY, "dY", (torch.bfloat16,))
-    K, M = X.shape
-    N = dY.shape[1]
-    partials = partials if partials is not None else torch.empty(splits, M, N, dtype=torch.float32, device=X.device)
-    _dev(partials, "partials", (torch.float32,))
+    K, M, N = _gemm_args(X, dY)
+    partials = _sized(partials, "partials", X.device, (torch.float32,), shape=(splits, M, N)) \
+        if partials is not None else torch.empty(splits, M, N, dtype=torch.float32, device=X.device)
     _check(lib.dr_splitk_gemm_tn(_p(X), _p(dY), K, M, N, splits, _p(partials), _stream(stream)), "dr_splitk_gemm_tn")
     return partials
 
 
 def dr_splitk_gemm_tn_atomic(X, dY, splits: int, *, out, stream=None):
-    _dev(X, "X", (torch.bfloat16,))
-    _dev(dY, "dY", (torch.bfloat16,))
-    _dev(out, "out", (torch.float32,))
-    K, M = X.shape
-    N = dY.shape[1]
+    """Nondeterministic baseline: adds every split's X_s^T dY_s into out [M, N] with fp32 atomics."""
+    K, M, N = _gemm_args(X, dY)
+    _sized(out, "out", X.device, (torch.float32,), shape=(M, N))
     _check(lib.dr_splitk_gemm_tn_atomic(_p(X), _p(dY), K, M, N, splits, _p(out), _stream(stream)),
            "dr_splitk_gemm_tn_atomic")
     return out
 
 
+def _reduce_args(partials):
+    _dev(partials, "partials", (torch.float32,))
+    if partials.dim() < 1 or partials.shape[0] < 1:
+        raise ValueError("partials must be [S, ...] with S >= 1")
+    S = partials.shape[0]
+    return S, partials.numel() // S
+
+
+def _reduce_out(out, partials, count):
+    if out is None:
+        return torch.empty(partials.shape[1:], dtype=torch.float32, device=partials.device)
+    return _sized(out, "out", partials.device, (torch.float32,), numel=count)
+
+
 def dr_splitk_reduce(partials, *, out=None, stream=None):
     """out = ordered tree over the split axis of partials [S, ...]."""
-    _dev(partials, "partials", (torch.float32,))
-    S = partials.shape[0]
-    count = partials.numel() // S
-    out = out if out is not None else torch.empty(partials.shape[1:], dtype=torch.float32, device=partials.device)
-    _dev(out, "out", (torch.float32,))
+    S, count = _reduce_args(partials)
+    out = _reduce_out(out, partials, count)
     _check(lib.dr_splitk_reduce(_p(partials), S, count, _p(out), _stream(stream)), "dr_splitk_reduce")
     return out
 
@@ -359,14 +428,10 @@ def dr_splitk_reduce_fingerprinted_workspace_size(splits: int, count: int) -> in
 
 def dr_splitk_reduce_fingerprinted(partials, out_hash, *, out=None, ws=None, stream=None):
     """dr_splitk_reduce that also writes dr_fingerprint(out) to out_hash (int64 [1] on the device)."""
-    _dev(partials, "partials", (torch.float32,))
-    _dev(out_hash, "out_hash", (torch.int64,))
-    S = partials.shape[0]
-    count = partials.numel() // S
-    out = out if out is not None else torch.empty(partials.shape[1:], dtype=torch.float32, device=partials.device)
-    _dev(out, "out", (torch.float32,))
-    need = dr_splitk_reduce_fingerprinted_workspace_size(S, count)
-    ws = ws if ws is not None else _workspace(need, partials.device)
+    S, count = _reduce_args(partials)
+    _hash_buf(out_hash, "out_hash", partials.device)
+    out = _reduce_out(out, partials, count)
+    ws = _ws(ws, dr_splitk_reduce_fingerprinted_workspace_size(S, count), partials.device)
     _check(lib.dr_splitk_reduce_fingerprinted(_p(partials), S, count, _p(out), _p(out_hash), _p(ws), ws.numel(),
                                               _stream(stream)), "dr_splitk_reduce_fingerprinted")
     return out
@@ -383,18 +448,19 @@ def dr_grouped_splitk_workspace_size(K: int, num_groups: int, split_tokens: int)
 def dr_grouped_splitk_gemm_tn(X, dY, group_offsets, split_tokens: int, *, partials=None, slot_offsets=None, ws=None,
                               stream=None):
     """Private slot partials X_s^T dY_s of every group's token slots.  Returns (partials, slot_offsets, ws)."""
-    _dev(X, "X", (torch.bfloat16,))
-    _dev(dY, "dY", (torch.bfloat16,))
-    _dev(group_offsets, "group_offsets", (torch.int32,))
-    K, M = X.shape
-    N = dY.shape[1]
+    K, M, N = _gemm_args(X, dY)
+    _sized(group_offsets, "group_offsets", X.device, (torch.int32,), min_numel=2)
     G = group_offsets.numel() - 1
     S = dr_grouped_splitk_max_slots(K, G, split_tokens)
-    partials = partials if partials is not None else torch.empty(S, M, N, dtype=torch.float32, device=X.device)
-    slot_offsets = slot_offsets if slot_offsets is not None else torch.empty(G + 1, dtype=torch.int32,
-                                                                            device=X.device)
-    ws = ws if ws is not None else _workspace(dr_grouped_splitk_workspace_size(K, G, split_tokens), X.device)
-    _dev(partials, "partials", (torch.float32,))
+    if partials is None:
+        partials = torch.empty(S, M, N, dtype=torch.float32, device=X.device)
+    else:
+        _sized(partials, "partials", X.device, (torch.float32,))
+        if partials.dim() != 3 or tuple(partials.shape[1:]) != (M, N) or partials.shape[0] < S:
+            raise ValueError(f"partials must be [>= {S}, {M}, {N}], got {tuple(partials.shape)}")
+    slot_offsets = _sized(slot_offsets, "slot_offsets", X.device, (torch.int32,), numel=G + 1) \
+        if slot_offsets is not None else torch.empty(G + 1, dtype=torch.int32, device=X.device)
+    ws = _ws(ws, dr_grouped_splitk_workspace_size(K, G, split_tokens), X.device)
     _check(lib.dr_grouped_splitk_gemm_tn(_p(X), _p(dY), K, M, N, _p(group_offsets), G, split_tokens, _p(partials),
                                          partials.shape[0], _p(slot_offsets), _p(ws), ws.numel(), _stream(stream)),
            "dr_grouped_splitk_gemm_tn")
@@ -402,12 +468,19 @@ def dr_grouped_splitk_gemm_tn(X, dY, group_offsets, split_tokens: int, *, partia
 
 
 def dr_grouped_splitk_reduce(partials, slot_offsets, ws, *, out=None, stream=None):
-    """out[g] = ordered tree over group g's slots (zero for an empty group)."""
+    """out[g] = ordered tree over group g's slots (zero for an empty group); ws is the workspace the
+    partials' call filled (it holds the slot table)."""
     _dev(partials, "partials", (torch.float32,))
+    if partials.dim() < 1:
+        raise ValueError("partials must be [slots, ...]")
+    _sized(slot_offsets, "slot_offsets", partials.device, (torch.int32,), min_numel=2)
+    _sized(ws, "ws", partials.device, (torch.uint8,), min_numel=_STATUS_BYTES)
     G = slot_offsets.numel() - 1
     count = partials[0].numel() if partials.shape[0] else 0
-    out = out if out is not None else torch.empty((G,) + tuple(partials.shape[1:]), dtype=torch.float32,
-                                                  device=partials.device)
+    if out is None:
+        out = torch.empty((G,) + tuple(partials.shape[1:]), dtype=torch.float32, device=partials.device)
+    else:
+        _sized(out, "out", partials.device, (torch.float32,), numel=G * count)
     _check(lib.dr_grouped_splitk_reduce(_p(partials), partials.shape[0], _p(slot_offsets), G, count, _p(out),
                                         _p(ws), _stream(stream)), "dr_grouped_splitk_reduce")
     return out
@@ -416,12 +489,20 @@ def dr_grouped_splitk_reduce(partials, slot_offsets, ws, *, out=None, stream=Non
 def dr_permute_rows(rows, perm, k: int, *, inv_perm=None, out=None, dev_status=None, stream=None):
     """out[r] = rows[perm[r] // k] (the expert-major copy of the token rows); with inv_perm the copies
     run in token order."""
-    _dev(perm, "perm", (torch.int32,))
-    if rows.device.type != "cuda" or not rows.is_contiguous():
-        raise ValueError("rows must be a contiguous CUDA tensor")
+    _dev(rows, "rows")
+    if rows.dim() < 1:
+        raise ValueError("rows must be [tokens, ...]")
+    _sized(perm, "perm", rows.device, (torch.int32,))
     n = perm.numel()
+    if inv_perm is not None:
+        _sized(inv_perm, "inv_perm", rows.device, (torch.int32,), numel=n)
     row_bytes = rows[0].numel() * rows.element_size() if rows.shape[0] else 0
-    out = out if out is not None else torch.empty((n,) + tuple(rows.shape[1:]), dtype=rows.dtype, device=rows.device)
+    shape = (n,) + tuple(rows.shape[1:])
+    if out is None:
+        out = torch.empty(shape, dtype=rows.dtype, device=rows.device)
+    else:
+        _sized(out, "out", rows.device, (rows.dtype,), shape=shape)
+    _status_buf(dev_status, rows.device)
     _check(lib.dr_permute_rows(_p(rows), row_bytes, rows.shape[0], _p(perm), _p(inv_perm), n, k, _p(out),
                                _p(dev_status), _stream(stream)), "dr_permute_rows")
     return out
@@ -440,17 +521,20 @@ def dr_decode_attention(q, k_cache, v_cache, seq_lens, scale: float, kv_chunk: i
                         out=None, ws=None, dev_status=None, stream=None):
     """Decode attention of q [B, Hq, D] (bf16) over the caches (bf16; [B, Lmax, Hkv, D], or [B, Hkv, Lmax, D]
     with head_major) with a fixed KV partition of kv_chunk tokens; returns fp32 [B, Hq, D]."""
-    for t, name in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache")):
-        _dev(t, name, (torch.bfloat16,))
-    _dev(seq_lens, "seq_lens", (torch.int32,))
+    _dev(q, "q", (torch.bfloat16,))
+    for t, name in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _sized(t, name, q.device, (torch.bfloat16,))
+    _sized(seq_lens, "seq_lens", q.device, (torch.int32,))
     if q.dim() != 3 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
         raise ValueError("q must be [B, Hq, D] and the caches 4-D of one shape")
     B, Hq, D = q.shape
     Lmax, Hkv = (k_cache.shape[2], k_cache.shape[1]) if head_major else (k_cache.shape[1], k_cache.shape[2])
     if k_cache.shape[0] != B or k_cache.shape[3] != D or seq_lens.numel() != B:
         raise ValueError("batch or head_dim mismatch")
-    out = out if out is not None else torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
-    ws = ws if ws is not None else _workspace(dr_decode_attention_workspace_size(B, Hq, Lmax, kv_chunk, D), q.device)
+    out = _sized(out, "out", q.device, (torch.float32,), shape=(B, Hq, D)) if out is not None else \
+        torch.empty((B, Hq, D), dtype=torch.float32, device=q.device)
+    ws = _ws(ws, dr_decode_attention_workspace_size(B, Hq, Lmax, kv_chunk, D), q.device)
+    _status_buf(dev_status, q.device)
     layout = DR_KV_HEAD_MAJOR if head_major else DR_KV_TOKEN_MAJOR
     _check(lib.dr_decode_attention(_p(out), _p(q), _p(k_cache), _p(v_cache), layout, _p(seq_lens), B, Hq, Hkv, D,
                                    Lmax, float(scale), kv_chunk, _p(ws), ws.numel(), _p(dev_status),
@@ -474,8 +558,8 @@ def dr_fingerprint(t, *, out=None, ws=None, stream=None):
     """Device-side 64-bit fingerprint of t's bytes in logical order (an int64 tensor of one element)."""
     _dev(t, "tensor")
     nbytes = t.numel() * t.element_size()
-    out = out if out is not None else torch.empty(1, dtype=torch.int64, device=t.device)
-    ws = ws if ws is not None else _workspace(dr_fingerprint_workspace_size(nbytes), t.device)
+    out = _hash_buf(out, "out", t.device) if out is not None else torch.empty(1, dtype=torch.int64, device=t.device)
+    ws = _ws(ws, dr_fingerprint_workspace_size(nbytes), t.device)
     _check(lib.dr_fingerprint(_p(t), nbytes, _p(out), _p(ws), ws.numel(), _stream(stream)), "dr_fingerprint")
     return out
 

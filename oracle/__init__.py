@@ -22,7 +22,7 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 # Flags that keep float arithmetic exactly IEEE binary32 with round-to-nearest:
 # no contraction into fused multiply-add, no reassociation, no excess precision.
 CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
-          "-fexcess-precision=standard", "-msse2", "-mfpmath=sse", "-Wall", "-Wextra"]
+          "-fexcess-precision=standard", "-msse2", "-mfpmath=sse", "-pthread", "-Wall", "-Wextra"]
 
 F32, BF16 = 0, 1
 ERRORS = {0: "ok", 1: "bad argument", 4: "index out of range", 6: "out of memory"}
@@ -54,9 +54,9 @@ def lib():
         L.oracle_tree_sum_f32.argtypes = [vp, i64, vp]
         L.oracle_tree_sum_bf16.argtypes = [vp, i64, vp]
         L.oracle_sort_by_dest.argtypes = [vp, vp, i64, i32, vp, vp, vp]
-        L.oracle_scatter_reduce.argtypes = [vp, i32, i64, vp, ctypes.c_int, i64, vp, vp, vp, i64]
-        L.oracle_combine.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, i64, i32, vp, i64, vp]
-        L.oracle_sparse_attn_dk.argtypes = [vp, i32, i64, vp, ctypes.c_int, vp, vp, i64, i32, vp, i64]
+        L.oracle_scatter_reduce.argtypes = [vp, i32, i64, vp, ctypes.c_int, i64, vp, vp, vp, i64, i32]
+        L.oracle_combine.argtypes = [vp, ctypes.c_int, i64, i64, vp, vp, i64, i32, vp, i64, vp, i32]
+        L.oracle_sparse_attn_dk.argtypes = [vp, i32, i64, vp, ctypes.c_int, vp, vp, i64, i32, vp, i64, i32]
         L.oracle_splitk_reduce.argtypes = [vp, i32, i64, vp]
         L.oracle_splitk_reference.argtypes = [vp, vp, i64, i64, i64, vp, vp]
         L.oracle_splitk_partials.argtypes = [vp, vp, i64, i64, i64, i32, vp]
@@ -120,12 +120,14 @@ def _dtype_code(a) -> int:
     raise TypeError(f"unsupported source dtype {a.dtype}")
 
 
-def scatter_reduce(out0, src, index, src_id=None, dests=None):
+def scatter_reduce(out0, src, index, src_id=None, dests=None, threads: int = 1):
     """out[d] = out0[d] + T(contributions of d in (src_id, position) order).
 
     out0: float32 [D, H].  src: float32 or uint16 (bf16 bits) [n, H].
     dests: optional list of destination ids; then only those rows are returned
     (shape [len(dests), H]) and out0 is only read at those rows.
+    threads: host threads sharing the destination rows (the result does not
+    depend on it).
     """
     out0 = np.asarray(out0, dtype=np.float32)
     D, H = out0.shape
@@ -142,16 +144,16 @@ def scatter_reduce(out0, src, index, src_id=None, dests=None):
         nd = dl.size
         out = np.ascontiguousarray(out0[dl], dtype=np.float32)
     _check(lib().oracle_scatter_reduce(_ptr(out), D, H, _ptr(src), _dtype_code(src), n, _ptr(index),
-                                       _ptr(sid), _ptr(dl), nd), "scatter_reduce")
+                                       _ptr(sid), _ptr(dl), nd, int(threads)), "scatter_reduce")
     return out
 
 
-def index_add(out0, src, index, dests=None):
+def index_add(out0, src, index, dests=None, threads: int = 1):
     """torch-style index_add_(0, index, src) in the defined order (source id = row i)."""
-    return scatter_reduce(out0, src, index, None, dests)
+    return scatter_reduce(out0, src, index, None, dests, threads)
 
 
-def sparse_attn_dk(dK0, Q, dS, key_idx, keys=None):
+def sparse_attn_dk(dK0, Q, dS, key_idx, keys=None, threads: int = 1):
     """dK[key] = dK0[key] + T(fl32(dS[q, j] * Q[q]) over the (q, j) with key_idx[q, j] == key, in order of
     q * topk + j).  Q: float32 or uint16 (bf16 bits) [nq, H]; dS: float32 [nq, topk]; key_idx: int32 [nq, topk].
     keys: optional list of keys; then only those rows are returned."""
@@ -170,11 +172,11 @@ def sparse_attn_dk(dK0, Q, dS, key_idx, keys=None):
         nk = kl.size
         out = np.ascontiguousarray(dK0[kl], dtype=np.float32)
     _check(lib().oracle_sparse_attn_dk(_ptr(out), num_keys, H, _ptr(Q), _dtype_code(Q), _ptr(dS), _ptr(key_idx),
-                                       nq, topk, _ptr(kl), nk), "sparse_attn_dk")
+                                       nq, topk, _ptr(kl), nk, int(threads)), "sparse_attn_dk")
     return out
 
 
-def combine(rows, row_of, gates, tokens=None):
+def combine(rows, row_of, gates, tokens=None, threads: int = 1):
     """out[t] = T(fl32(gate*row) over the token's slots, ordered by row index)."""
     rows = np.ascontiguousarray(rows)
     R, H = rows.shape
@@ -188,7 +190,7 @@ def combine(rows, row_of, gates, tokens=None):
         nt = tl.size
     out = np.empty((nt, H), np.float32)
     _check(lib().oracle_combine(_ptr(rows), _dtype_code(rows), R, H, _ptr(row_of), _ptr(gates), T, k,
-                                _ptr(tl), nt if tl is not None else 0, _ptr(out)), "combine")
+                                _ptr(tl), nt if tl is not None else 0, _ptr(out), int(threads)), "combine")
     return out
 
 

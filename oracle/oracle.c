@@ -43,6 +43,7 @@
  * Everything here is plain loops; speed is not a goal.
  */
 #include <float.h>
+#include <pthread.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -238,60 +239,167 @@ int oracle_sort_by_dest(const int32_t* dest, const int32_t* src_id, int64_t n, i
 }
 
 /* ------------------------------------------------------------------ */
+/* Running independent output rows on several host threads             */
+/* ------------------------------------------------------------------ */
+
+/* Every output row (a destination, a key, a token) is computed from its own
+ * inputs only, so rows can be handed to threads in contiguous ranges without
+ * changing a bit: the threads only divide the row loop.  threads <= 1 runs
+ * the loop on the calling thread. */
+typedef struct row_job {
+    int (*fn)(const struct row_job* job, int64_t r0, int64_t r1);
+    const void* ctx;
+    int64_t r0, r1;
+    int rc;
+} row_job;
+
+static void* row_job_main(void* arg)
+{
+    row_job* j = (row_job*)arg;
+    j->rc = j->fn(j, j->r0, j->r1);
+    return NULL;
+}
+
+static int run_rows(int (*fn)(const row_job*, int64_t, int64_t), const void* ctx, int64_t rows, int32_t threads)
+{
+    if (threads > 256)
+        threads = 256;
+    if (threads <= 1 || rows < 2) {
+        row_job one = {fn, ctx, 0, rows, ORC_OK};
+        return fn(&one, 0, rows);
+    }
+    row_job jobs[256];
+    pthread_t tid[256];
+    int started[256];
+    int64_t per = (rows + threads - 1) / threads;
+    for (int32_t t = 0; t < threads; ++t) {
+        int64_t lo = (int64_t)t * per < rows ? (int64_t)t * per : rows;
+        int64_t hi = lo + per < rows ? lo + per : rows;
+        jobs[t].fn = fn;
+        jobs[t].ctx = ctx;
+        jobs[t].r0 = lo;
+        jobs[t].r1 = hi;
+        jobs[t].rc = ORC_OK;
+        started[t] = pthread_create(&tid[t], NULL, row_job_main, &jobs[t]) == 0;
+        if (!started[t])
+            row_job_main(&jobs[t]); /* no thread: run the range here */
+    }
+    int rc = ORC_OK;
+    for (int32_t t = 0; t < threads; ++t) {
+        if (started[t])
+            pthread_join(tid[t], NULL);
+        if (rc == ORC_OK && jobs[t].rc != ORC_OK)
+            rc = jobs[t].rc;
+    }
+    return rc;
+}
+
+/* Longest segment of a CSR offset array (the size of a per-thread buffer). */
+static int64_t max_segment(const int32_t* seg, int32_t num_dests)
+{
+    int64_t m = 1;
+    for (int32_t d = 0; d < num_dests; ++d)
+        if (seg[d + 1] - seg[d] > m)
+            m = seg[d + 1] - seg[d];
+    return m;
+}
+
+/* ------------------------------------------------------------------ */
 /* Scatter-reduce / index_add                                          */
 /* ------------------------------------------------------------------ */
+
+/* One reduction problem after the sort: destination d's contributions are
+ * perm[seg[d]] .. perm[seg[d+1]-1], in that order.  A contribution i is
+ * src row i (scale == NULL), or fl32(scale[i] * src row i / rows_per_src). */
+typedef struct {
+    float* out;
+    int32_t num_dests;
+    int64_t H;
+    const void* src;
+    int src_dtype;
+    const float* scale;
+    int32_t rows_per_src;
+    const int32_t* perm;
+    const int32_t* seg;
+    const int32_t* dests;
+    int64_t max_len;
+} reduce_ctx;
+
+static int reduce_rows(const row_job* job, int64_t r0, int64_t r1)
+{
+    const reduce_ctx* c = (const reduce_ctx*)job->ctx;
+    float* vals = (float*)malloc((size_t)c->max_len * sizeof(float));
+    if (!vals)
+        return ORC_NO_MEMORY;
+    int rc = ORC_OK;
+    for (int64_t q = r0; q < r1 && rc == ORC_OK; ++q) {
+        int32_t d = c->dests ? c->dests[q] : (int32_t)q;
+        if (d < 0 || d >= c->num_dests) {
+            rc = ORC_INDEX_OUT_OF_RANGE;
+            break;
+        }
+        int64_t lo = c->seg[d], L = c->seg[d + 1] - c->seg[d];
+        if (L == 0)
+            continue; /* untouched row */
+        float* row = c->out + q * c->H;
+        for (int64_t h = 0; h < c->H && rc == ORC_OK; ++h) {
+            for (int64_t j = 0; j < L; ++j) {
+                int64_t i = c->perm[lo + j];
+                if (c->scale) {
+                    float product = c->scale[i] * load_elem(c->src, c->src_dtype, (i / c->rows_per_src) * c->H + h);
+                    vals[j] = product; /* rounded to float before any add */
+                } else {
+                    vals[j] = load_elem(c->src, c->src_dtype, i * c->H + h);
+                }
+            }
+            float t;
+            rc = tree_sum(vals, L, &t);
+            if (rc == ORC_OK)
+                row[h] = row[h] + t;
+        }
+    }
+    free(vals);
+    return rc;
+}
+
+/* Sorts the contributions by (index, src_id), then reduces every requested row. */
+static int sort_and_reduce(reduce_ctx* c, int64_t n, const int32_t* index, const int32_t* src_id, int64_t rows,
+                           int32_t threads)
+{
+    int32_t* perm = (int32_t*)malloc((size_t)(n > 0 ? n : 1) * sizeof(int32_t));
+    int32_t* seg = (int32_t*)malloc((size_t)(c->num_dests + 1) * sizeof(int32_t));
+    if (!perm || !seg) {
+        free(perm); free(seg);
+        return ORC_NO_MEMORY;
+    }
+    int rc = oracle_sort_by_dest(index, src_id, n, c->num_dests, perm, seg, NULL);
+    if (rc == ORC_OK) {
+        c->perm = perm;
+        c->seg = seg;
+        c->max_len = max_segment(seg, c->num_dests);
+        rc = run_rows(reduce_rows, c, rows, threads);
+    }
+    free(perm); free(seg);
+    return rc;
+}
 
 /* For every destination d (or the listed ones), with its contributions taken in
  * (src_id, position) order:  out[d][h] = out[d][h] + T(src[i_0][h], ...).
  *
  * dests == NULL: out is [num_dests][H], updated in place.
  * dests != NULL: out is [ndest][H] and holds the listed destinations' rows
- * (initial contents in, result out); other destinations are not computed. */
+ * (initial contents in, result out); other destinations are not computed.
+ * threads: host threads that share the rows (the bits do not depend on it). */
 int oracle_scatter_reduce(float* out, int32_t num_dests, int64_t H, const void* src, int src_dtype,
                           int64_t n, const int32_t* index, const int32_t* src_id,
-                          const int32_t* dests, int64_t ndest)
+                          const int32_t* dests, int64_t ndest, int32_t threads)
 {
     if (!out || H < 1 || num_dests < 1 || n < 0 || (n > 0 && (!src || !index)))
         return ORC_BAD_ARG;
     if (src_dtype != ORC_F32 && src_dtype != ORC_BF16)
         return ORC_BAD_ARG;
-    int32_t* perm = (int32_t*)malloc((size_t)(n > 0 ? n : 1) * sizeof(int32_t));
-    int32_t* seg = (int32_t*)malloc((size_t)(num_dests + 1) * sizeof(int32_t));
-    float* vals = (float*)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
-    if (!perm || !seg || !vals) {
-        free(perm); free(seg); free(vals);
-        return ORC_NO_MEMORY;
-    }
-    int rc = oracle_sort_by_dest(index, src_id, n, num_dests, perm, seg, NULL);
-    if (rc != ORC_OK) {
-        free(perm); free(seg); free(vals);
-        return rc;
-    }
-    int64_t rows = dests ? ndest : num_dests;
-    for (int64_t q = 0; q < rows; ++q) {
-        int32_t d = dests ? dests[q] : (int32_t)q;
-        if (d < 0 || d >= num_dests) {
-            rc = ORC_INDEX_OUT_OF_RANGE;
-            break;
-        }
-        int64_t lo = seg[d], L = seg[d + 1] - seg[d];
-        if (L == 0)
-            continue; /* untouched row */
-        float* row = out + q * H;
-        for (int64_t h = 0; h < H; ++h) {
-            for (int64_t j = 0; j < L; ++j)
-                vals[j] = load_elem(src, src_dtype, (int64_t)perm[lo + j] * H + h);
-            float t;
-            rc = tree_sum(vals, L, &t);
-            if (rc != ORC_OK)
-                break;
-            row[h] = row[h] + t;
-        }
-        if (rc != ORC_OK)
-            break;
-    }
-    free(perm); free(seg); free(vals);
-    return rc;
+    reduce_ctx c = {out, num_dests, H, src, src_dtype, NULL, 1, NULL, NULL, dests, 1};
+    return sort_and_reduce(&c, n, index, src_id, dests ? ndest : num_dests, threads);
 }
 
 /* ------------------------------------------------------------------ */
@@ -309,7 +417,8 @@ int oracle_scatter_reduce(float* out, int32_t num_dests, int64_t H, const void* 
  * keys == NULL: dK is [num_keys][H], updated in place.
  * keys != NULL: dK is [nkeys][H] holding the listed keys' rows. */
 int oracle_sparse_attn_dk(float* dK, int32_t num_keys, int64_t H, const void* Q, int q_dtype, const float* dS,
-                          const int32_t* key_idx, int64_t nq, int32_t topk, const int32_t* keys, int64_t nkeys)
+                          const int32_t* key_idx, int64_t nq, int32_t topk, const int32_t* keys, int64_t nkeys,
+                          int32_t threads)
 {
     if (!dK || H < 1 || num_keys < 1 || nq < 0 || topk < 1)
         return ORC_BAD_ARG;
@@ -318,47 +427,8 @@ int oracle_sparse_attn_dk(float* dK, int32_t num_keys, int64_t H, const void* Q,
     const int64_t n = nq * (int64_t)topk;
     if (n > 0 && (!Q || !dS || !key_idx))
         return ORC_BAD_ARG;
-    int32_t* perm = (int32_t*)malloc((size_t)(n > 0 ? n : 1) * sizeof(int32_t));
-    int32_t* seg = (int32_t*)malloc((size_t)(num_keys + 1) * sizeof(int32_t));
-    float* vals = (float*)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
-    if (!perm || !seg || !vals) {
-        free(perm); free(seg); free(vals);
-        return ORC_NO_MEMORY;
-    }
-    int rc = oracle_sort_by_dest(key_idx, NULL, n, num_keys, perm, seg, NULL);
-    if (rc != ORC_OK) {
-        free(perm); free(seg); free(vals);
-        return rc;
-    }
-    int64_t rows = keys ? nkeys : num_keys;
-    for (int64_t r = 0; r < rows; ++r) {
-        int32_t key = keys ? keys[r] : (int32_t)r;
-        if (key < 0 || key >= num_keys) {
-            rc = ORC_INDEX_OUT_OF_RANGE;
-            break;
-        }
-        int64_t lo = seg[key], L = seg[key + 1] - seg[key];
-        if (L == 0)
-            continue; /* a key no query selected */
-        float* row = dK + r * H;
-        for (int64_t h = 0; h < H; ++h) {
-            for (int64_t j = 0; j < L; ++j) {
-                int64_t i = perm[lo + j];
-                int64_t q = i / topk;
-                float product = dS[i] * load_elem(Q, q_dtype, q * H + h);
-                vals[j] = product;
-            }
-            float t;
-            rc = tree_sum(vals, L, &t);
-            if (rc != ORC_OK)
-                break;
-            row[h] = row[h] + t;
-        }
-        if (rc != ORC_OK)
-            break;
-    }
-    free(perm); free(seg); free(vals);
-    return rc;
+    reduce_ctx c = {dK, num_keys, H, Q, q_dtype, dS, topk, NULL, NULL, keys, 1};
+    return sort_and_reduce(&c, n, key_idx, NULL, keys ? nkeys : num_keys, threads);
 }
 
 /* ------------------------------------------------------------------ */
@@ -367,15 +437,24 @@ int oracle_sparse_attn_dk(float* dK, int32_t num_keys, int64_t H, const void* Q,
 
 /* out[t][h] = T over the token's k contributions fl32(gate[t][j] * rows[row_of[t][j]][h]),
  * ordered by row index (ties by slot j).  Written, not accumulated.
- * tokens == NULL: all T tokens, out is [T][H]; else out is [ntok][H]. */
-int oracle_combine(const void* rows, int rows_dtype, int64_t num_rows, int64_t H,
-                   const int32_t* row_of, const float* gates, int64_t T, int32_t k,
-                   const int64_t* tokens, int64_t ntok, float* out)
+ * tokens == NULL: all T tokens, out is [T][H]; else out is [ntok][H].
+ * threads: host threads that share the tokens (the bits do not depend on it). */
+typedef struct {
+    const void* rows;
+    int rows_dtype;
+    int64_t num_rows, H;
+    const int32_t* row_of;
+    const float* gates;
+    int64_t T;
+    int32_t k;
+    const int64_t* tokens;
+    float* out;
+} combine_ctx;
+
+static int combine_rows(const row_job* job, int64_t q0, int64_t q1)
 {
-    if (!rows || !row_of || !gates || !out || H < 1 || k < 1 || T < 0 || num_rows < 0)
-        return ORC_BAD_ARG;
-    if (rows_dtype != ORC_F32 && rows_dtype != ORC_BF16)
-        return ORC_BAD_ARG;
+    const combine_ctx* c = (const combine_ctx*)job->ctx;
+    const int32_t k = c->k;
     int32_t* order = (int32_t*)malloc((size_t)k * sizeof(int32_t));
     float* vals = (float*)malloc((size_t)k * sizeof(float));
     if (!order || !vals) {
@@ -383,17 +462,16 @@ int oracle_combine(const void* rows, int rows_dtype, int64_t num_rows, int64_t H
         return ORC_NO_MEMORY;
     }
     int rc = ORC_OK;
-    int64_t count = tokens ? ntok : T;
-    for (int64_t q = 0; q < count && rc == ORC_OK; ++q) {
-        int64_t t = tokens ? tokens[q] : q;
-        if (t < 0 || t >= T) {
+    for (int64_t q = q0; q < q1 && rc == ORC_OK; ++q) {
+        int64_t t = c->tokens ? c->tokens[q] : q;
+        if (t < 0 || t >= c->T) {
             rc = ORC_INDEX_OUT_OF_RANGE;
             break;
         }
-        const int32_t* r = row_of + t * k;
-        const float* g = gates + t * k;
+        const int32_t* r = c->row_of + t * k;
+        const float* g = c->gates + t * k;
         for (int32_t j = 0; j < k; ++j) {
-            if (r[j] < 0 || r[j] >= num_rows)
+            if (r[j] < 0 || r[j] >= c->num_rows)
                 rc = ORC_INDEX_OUT_OF_RANGE;
         }
         if (rc != ORC_OK)
@@ -410,10 +488,10 @@ int oracle_combine(const void* rows, int rows_dtype, int64_t num_rows, int64_t H
             }
             order[b + 1] = cur;
         }
-        for (int64_t h = 0; h < H; ++h) {
+        for (int64_t h = 0; h < c->H; ++h) {
             for (int32_t j = 0; j < k; ++j) {
                 int32_t slot = order[j];
-                float y = load_elem(rows, rows_dtype, (int64_t)r[slot] * H + h);
+                float y = load_elem(c->rows, c->rows_dtype, (int64_t)r[slot] * c->H + h);
                 float p = g[slot] * y; /* rounded to float before any add */
                 vals[j] = p;
             }
@@ -421,11 +499,23 @@ int oracle_combine(const void* rows, int rows_dtype, int64_t num_rows, int64_t H
             rc = tree_sum(vals, k, &s);
             if (rc != ORC_OK)
                 break;
-            out[q * H + h] = s;
+            c->out[q * c->H + h] = s;
         }
     }
     free(order); free(vals);
     return rc;
+}
+
+int oracle_combine(const void* rows, int rows_dtype, int64_t num_rows, int64_t H,
+                   const int32_t* row_of, const float* gates, int64_t T, int32_t k,
+                   const int64_t* tokens, int64_t ntok, float* out, int32_t threads)
+{
+    if (!rows || !row_of || !gates || !out || H < 1 || k < 1 || T < 0 || num_rows < 0)
+        return ORC_BAD_ARG;
+    if (rows_dtype != ORC_F32 && rows_dtype != ORC_BF16)
+        return ORC_BAD_ARG;
+    combine_ctx c = {rows, rows_dtype, num_rows, H, row_of, gates, T, k, tokens, out};
+    return run_rows(combine_rows, &c, tokens ? ntok : T, threads);
 }
 
 /* ------------------------------------------------------------------ */

@@ -321,7 +321,7 @@ def test_kernels_have_no_fused_multiply_add():
             # (its order is still fixed), but packed fp32 forms stay out
             found = [x for x in found if x.startswith(("v_pk_", "v_mad_", "v_mac_"))]
         assert not found, (src, found)
-        assert "scratch_store" not in asm or src == "splitk.hip", src
+        assert "scratch_store" not in asm, src   # no kernel spills registers to scratch
 
 
 def test_splitk_reduce_fingerprinted_rejects_bad_arguments(lib):

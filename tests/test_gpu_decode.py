@@ -30,28 +30,67 @@ def to_dev(inp):
     return dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v), dev(inp.lens)
 
 
-def tolerance(inp, A, kv_chunk, b, h):
-    """First-order bound on |fp32 result - exact| for output row (b, h).
+def tolerance(inp, want, A, kv_chunk, b, h):
+    """First-order bound on |fp32 result - exact|, per column of output row (b, h).
 
-    A score is a sum of 128 exact bf16 products rounded in fp32, then scaled:
-    its error is at most 129 u S with S = scale * sum_i |q_i k_i|, which moves
-    the normalised weights by a relative 2 * 129 u S (after the log2(e) and
-    ln 2 factors cancel); rounding the exponent t - m adds u |t - m| <= 2 u S.
-    Every other step is a sum of non-negative weights or of weight * value
-    products along a chain of at most d roundings (d = 5 kv_chunk / 64 in a
-    lane, 6 in the butterfly and the wave merge, one per chunk in the merge,
-    one for the division), each within 2 u of the hardware exp2 factors.
-    Everything is relative to A = sum_j w_j |v_j| >= |out|."""
+    Weights.  With s_j the exact scores and w_j = softmax(s)_j, an fp32
+    evaluation sees weights w_j e^{d_j} / sum_k w_k e^{d_k} for some errors d_j,
+    so to first order out' - out = sum_j w_j d_j (v_j - out), bounded per column
+    by sum_j w_j |d_j| |v_jc - out_c|.  A score is a sum of 128 exact bf16
+    products rounded in fp32 (at most 129 u S_j, S_j = scale * sum_i |q_i k_ji|),
+    then scaled by a rounded scale * log2(e) (2 u S_j, the log2(e) and ln 2
+    factors cancel); the exponent t_j - m is rounded (u (S_j + S_max)); the
+    running-maximum rescales inside a chunk and the chunk factors of the merge
+    are exponents of rounded differences of maxima (2 u S_max each).  So
+    |d_j| <= u (132 S_j + 6 S_max) =: d_j.  Exactly, out' - out =
+    (1/Z) sum_j w_j (d_j + r(d_j)) (v_j - out) with Z = sum_k w_k e^{d_k} and
+    r(x) = e^x - 1 - x (the terms constant in j cancel, since
+    sum_j w_j (v_j - out) = 0), which gives the factor `second` below.
+
+    Sums.  Every other step is a sum of non-negative weights or of weight *
+    value products along a chain of at most d roundings (d = 5 kv_chunk / 64 in
+    a lane, 6 in the butterfly and the wave merge, one per chunk in the merge,
+    one for the division), each within 2 u of the hardware exp2 factors:
+    u (4 d + 32) A_c with A_c = sum_j w_j |v_jc| >= |out_c|.
+
+    Keeping the per-token and per-column terms (rather than the largest S_j and
+    |v_j| + |out|) makes the bound tight enough that one dropped or doubled
+    cached token of average weight falls outside it at 16,384 tokens
+    (test_decode_bound_sees_a_dropped_or_doubled_token)."""
     L = int(inp.lens[b])
     if L == 0:
         return np.zeros(inp.D)
     g = inp.Hq // inp.Hkv
     q = workloads.bf16_to_f32(inp.q[b, h]).astype(np.float64)
     k = workloads.bf16_to_f32(inp.k[b, :L, h // g]).astype(np.float64)
-    S = inp.scale * float((np.abs(k) @ np.abs(q)).max())
+    v = workloads.bf16_to_f32(inp.v[b, :L, h // g]).astype(np.float64)
+    s = inp.scale * (k @ q)
+    w = np.exp(s - s.max())
+    w /= w.sum()
+    S = inp.scale * (np.abs(k) @ np.abs(q))
+    d_j = U * (132.0 * S + 6.0 * S.max())
+    D, d_min = float(d_j.max()), float(d_j.min())
+    # exact remainder of the expansion: e^x = 1 + x + r(x), |r(x)| <= x^2 e^|x| / 2, and the normaliser 1/Z <= e^D
+    second = np.exp(D) * (1.0 + 0.5 * D * D * np.exp(D) / d_min)
+    score_term = second * ((w * d_j) @ np.abs(v - want[b, h]))
     nc = -(-L // kv_chunk)
     d = 5 * min(kv_chunk, L) // 64 + 5 + 6 + nc + 1
-    return A[b, h] * U * (270.0 * S + 4.0 * d + 32.0)
+    return score_term + A[b, h] * U * (4.0 * d + 32.0)
+
+
+def worst_ratio(inp, got, kv_chunk, rows=None):
+    """max over the rows and columns of |got - exact| / bound (<= 1 passes)."""
+    want, A = oracle.decode_attention(inp.q, inp.k, inp.v, inp.lens, inp.scale)
+    rows = rows if rows is not None else [(b, h) for b in range(inp.B) for h in range(inp.Hq)]
+    worst = 0.0
+    for b, h in rows:
+        tol = tolerance(inp, want, A, kv_chunk, b, h)
+        err = np.abs(got[b, h].astype(np.float64) - want[b, h])
+        if int(inp.lens[b]) == 0:
+            worst = max(worst, 0.0 if np.all(got[b, h] == 0) else np.inf)
+            continue
+        worst = max(worst, float((err / tol).max()))
+    return worst
 
 
 def check_against_oracle(inp, got, kv_chunk, rows=None):
@@ -60,7 +99,7 @@ def check_against_oracle(inp, got, kv_chunk, rows=None):
     rows = rows if rows is not None else [(b, h) for b in range(inp.B) for h in range(inp.Hq)]
     worst = 0.0
     for b, h in rows:
-        tol = tolerance(inp, A, kv_chunk, b, h)
+        tol = tolerance(inp, want, A, kv_chunk, b, h)
         err = np.abs(got[b, h].astype(np.float64) - want[b, h])
         assert np.all(err <= tol), (b, h, float(err.max()), float(tol.max()))
         if int(inp.lens[b]) == 0:
@@ -190,3 +229,42 @@ def test_decode_attention_peaked_and_flat_weights(dr):
     check_against_oracle(flat, got, 128)
     want_mean = workloads.bf16_to_f32(inp.v[0, :900]).astype(np.float64).mean(axis=0)  # [Hkv, D]
     assert np.allclose(got[0], np.repeat(want_mean, 4, axis=0), rtol=0, atol=1e-5)
+
+
+def test_decode_bound_sees_a_dropped_or_doubled_token(dr):
+    """Negative control of the decode check at full length: the GPU output of a
+    16,384-token sequence passes against the oracle, and fails against the
+    oracle recomputed with one cached token dropped or doubled.  The tokens are
+    taken near the start, a chunk boundary, the middle and the end, each the
+    one among 64 neighbours whose weight is closest to the average weight 1/L
+    (for the query head that weighs it most): a token of far less than average
+    weight moves the output by less than rounding, and no tolerance can see it."""
+    L, chunk = 16384, 512
+    inp = workloads.decode_inputs(35, 1, L, 32, 8, 128, [L])
+    q, k, v, lens = to_dev(inp)
+    say("decode negative control: 16,384 tokens")
+    got = host(dr.dr_decode_attention(q, k, v, lens, inp.scale, chunk))
+    assert worst_ratio(inp, got, chunk) <= 1.0
+    g = inp.Hq // inp.Hkv
+    kv_head = 3
+    heads = list(range(kv_head * g, kv_head * g + g))
+    qf = workloads.bf16_to_f32(inp.q[0, heads]).astype(np.float64)                # [g, D]
+    kf = workloads.bf16_to_f32(inp.k[0, :, kv_head]).astype(np.float64)           # [L, D]
+    s = inp.scale * (kf @ qf.T)                                                    # [L, g]
+    w = np.exp(s - s.max(axis=0))
+    w /= w.sum(axis=0)
+    rows = [(0, h) for h in heads]
+    for start in (0, chunk - 32, L // 2, L - 64):
+        j = start + int(np.argmin(np.abs(w[start:start + 64].max(axis=1) * L - 1.0)))
+        for kind in ("dropped", "doubled"):
+            if kind == "dropped":
+                kk = np.delete(inp.k, j, axis=1)
+                vv = np.delete(inp.v, j, axis=1)
+            else:
+                kk = np.insert(inp.k, j, inp.k[:, j], axis=1)
+                vv = np.insert(inp.v, j, inp.v[:, j], axis=1)
+            bad = dataclasses.replace(inp, Lmax=kk.shape[1], k=kk, v=vv,
+                                      lens=np.array([kk.shape[1]], np.int32))
+            ratio = worst_ratio(bad, got, chunk, rows=rows)
+            say(f"  token {j} {kind} (weight x L = {float(w[j].max()) * L:.2f}): worst |err| / bound = {ratio:.2f}")
+            assert ratio > 1.0, (j, kind, ratio)

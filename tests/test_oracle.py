@@ -551,6 +551,29 @@ def test_permute_rows_brute_force():
         assert out[r].tolist() == x[perm[r] // 2].tolist()
 
 
+@pytest.mark.parametrize("seed,T,E,k", [(1, 40, 6, 2), (2, 257, 32, 8), (3, 9, 64, 4), (4, 100, 3, 3)])
+def test_permute_rows_expert_blocks_hold_tokens_in_ascending_order(seed, T, E, k):
+    """The dispatch layout the DeepSeek-V4 book fixes (ch. 9, section 3.2): the
+    rows routed to one expert sit together, experts in id order, and within an
+    expert's block the tokens are in ascending original token order.  The
+    expected layout is built by brute force from the (expert, token) pairs
+    sorted with Python's sort; nothing divides a permutation index by k."""
+    rng = np.random.default_rng(seed)
+    expert_ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    x = rng.standard_normal((T, 5)).astype(F32)
+    x[:, 0] = np.arange(T)              # a token's row carries its own id
+    pairs = sorted((int(expert_ids[t, j]), t) for t in range(T) for j in range(k))
+    want = np.stack([x[t] for _, t in pairs])
+    perm, seg, _ = oracle.sort_by_dest(expert_ids.reshape(-1), E)
+    got = oracle.permute_rows(x, perm, k)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    # block by block: expert e owns rows [seg[e], seg[e+1]), exactly its tokens, ascending
+    for e in range(E):
+        block = got[seg[e]:seg[e + 1], 0].astype(np.int64)
+        tokens = sorted(t for t in range(T) if e in expert_ids[t])
+        assert block.tolist() == tokens
+
+
 # ---------------------------------------------------------------------------
 # Decode attention (by definition)
 # ---------------------------------------------------------------------------
@@ -680,3 +703,35 @@ def test_generators_are_seeded():
     for t in range(a.T):
         assert len(set(a.expert_ids[t])) == a.k
     assert np.allclose(a.gates.sum(axis=1), 1.0, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# Host threads divide the row loop only
+# ---------------------------------------------------------------------------
+def test_oracle_threads_do_not_change_bits():
+    """The oracle's multi-threaded form hands contiguous destination (or token)
+    ranges to threads; every row is computed from its own inputs, so the bytes
+    equal the single-threaded result for any thread count."""
+    rng = np.random.default_rng(95)
+    D, H, n = 300, 16, 6000
+    index = np.minimum(rng.zipf(1.2, n) - 1, D - 1).astype(np.int32)
+    src = workloads.bf16_bits(mixed_values(rng, n * H).reshape(n, H))
+    out0 = mixed_values(rng, D * H).reshape(D, H)
+    one = oracle.index_add(out0, src, index)
+    for t in (2, 3, 8, 64):
+        assert np.array_equal(oracle.index_add(out0, src, index, threads=t).view(np.uint32), one.view(np.uint32))
+    nq, topk, K = 200, 16, 97
+    key_idx = np.stack([rng.choice(K, topk, replace=False) for _ in range(nq)]).astype(np.int32)
+    Q = workloads.bf16_bits(rng.standard_normal((nq, H)).astype(F32))
+    dS = mixed_values(rng, nq * topk).reshape(nq, topk)
+    dk0 = mixed_values(rng, K * H).reshape(K, H)
+    one = oracle.sparse_attn_dk(dk0, Q, dS, key_idx)
+    for t in (2, 7):
+        assert np.array_equal(oracle.sparse_attn_dk(dk0, Q, dS, key_idx, threads=t).view(np.uint32),
+                              one.view(np.uint32))
+    inp = workloads.make("moe_combine", T=64, E=16, H=64)
+    row_of = _expert_major_rows(inp.expert_ids)
+    one = oracle.combine(inp.rows, row_of, inp.gates)
+    for t in (2, 5, 16):
+        assert np.array_equal(oracle.combine(inp.rows, row_of, inp.gates, threads=t).view(np.uint32),
+                              one.view(np.uint32))
