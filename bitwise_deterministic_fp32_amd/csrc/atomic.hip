@@ -11,9 +11,13 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// One wavefront per (contribution row, slice of 64*E columns); lane l owns
-// columns l + 64*e so every load and atomic instruction covers 64 consecutive
-// elements.
+// One wavefront per (contribution row, slice of 64*E columns).  Lane l reads
+// the 16 bytes of columns [E*l, E*l + E) of the slice with one vector load
+// (the access the ordered kernels use), the wavefront re-deals the widened
+// values through LDS so that lane l holds columns l + 64*e, and every atomic
+// instruction then covers 64 consecutive elements (two or four whole cache
+// lines).  So the baseline reads and adds as efficiently as the hardware
+// allows; only the order of the adds is left to the arrival order.
 template <dr_dtype DT>
 __global__ __launch_bounds__(kThreads) void index_add_atomic_kernel(float* __restrict__ out, int32_t num_dests,
                                                                     int64_t H, const void* __restrict__ src,
@@ -21,30 +25,36 @@ __global__ __launch_bounds__(kThreads) void index_add_atomic_kernel(float* __res
                                                                     int32_t* dev_status, int64_t slices) {
     constexpr int E = Vec<DT>::kElems;
     constexpr int kElemBytes = DT == DR_BF16 ? 2 : 4;
+    __shared__ float stage[kThreads / 64][64 * E];
     const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
     // the host keeps n * slices below 2^32
-    const uint32_t wave = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    const uint32_t wave = blockIdx.x * (kThreads / 64) + w;
     const uint32_t i = wave / (uint32_t)slices;
-    if (i >= n) return;
-    const uint32_t slice = wave - i * (uint32_t)slices;
-    const int32_t d = index[i];
-    if (d < 0 || d >= num_dests) {
+    bool live = i < n;
+    const uint32_t slice = live ? wave - i * (uint32_t)slices : 0;
+    const int32_t d = live ? index[i] : 0;
+    if (live && (d < 0 || d >= num_dests)) {
         if (dev_status && lane == 0 && slice == 0) atomicOr(dev_status, kStatusIndex);
-        return;
+        live = false;
     }
-    const char* row = reinterpret_cast<const char*>(src) + (int64_t)i * H * kElemBytes;
+    // hidden is a multiple of E, so a lane's 16 bytes lie wholly inside or wholly past the row
+    const int64_t cv = (int64_t)slice * 64 * E + (int64_t)lane * E;
+    if (live && cv < H) {
+        const char* row = reinterpret_cast<const char*>(src) + (int64_t)i * H * kElemBytes;
+        float v[E];
+        Vec<DT>::widen(load16_stream(row + cv * kElemBytes), v);
+#pragma unroll
+        for (int e = 0; e < E; ++e) stage[w][lane * E + e] = v[e];
+    }
+    __syncthreads();
+    if (!live) return;
     float* o = out + (int64_t)d * H;
     const int64_t c0 = (int64_t)slice * 64 * E + lane;
-    float v[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const int64_t c = c0 + 64 * e;
-        v[e] = c < H ? load_elem<DT>(row, c) : 0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int64_t c = c0 + 64 * e;
-        if (c < H) unsafeAtomicAdd(o + c, v[e]);
+        if (c < H) unsafeAtomicAdd(o + c, stage[w][lane + 64 * e]);
     }
 }
 

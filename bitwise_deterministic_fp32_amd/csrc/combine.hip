@@ -230,8 +230,9 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(const void* __restrict
 // The baseline: one wavefront per (token, slot, slice of 64*E columns), so
 // the k contributions of an output element come from k different wavefronts
 // and are added by hardware fp32 atomics in whatever order they arrive (the
-// scatter_add_ pattern over permuted rows).  Lane l owns columns l + 64*e, so
-// every load and atomic instruction covers 64 consecutive elements.
+// scatter_add_ pattern over permuted rows).  Each lane reads 16 bytes with one
+// vector load; after an exchange through LDS, lane l holds columns l + 64*e,
+// so every atomic instruction covers 64 consecutive elements.
 template <dr_dtype DT>
 __global__ __launch_bounds__(kThreads) void combine_atomic_kernel(const void* __restrict__ rows, int64_t num_rows,
                                                                   int64_t H, const int32_t* __restrict__ row_of,
@@ -240,33 +241,40 @@ __global__ __launch_bounds__(kThreads) void combine_atomic_kernel(const void* __
                                                                   int64_t slices) {
     constexpr int E = Vec<DT>::kElems;
     constexpr int kElemBytes = DT == DR_BF16 ? 2 : 4;
+    __shared__ float stage[kWavesPerBlock][64 * E];
     const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
     // the host keeps T * k * slices below 2^32
-    const uint32_t wave = blockIdx.x * kWavesPerBlock + (threadIdx.x >> 6);
+    const uint32_t wave = blockIdx.x * kWavesPerBlock + w;
     const uint32_t a = wave / (uint32_t)slices;  // assignment index t*k + j
-    if (a >= (uint64_t)T * k) return;
-    const uint32_t slice = wave - a * (uint32_t)slices;
-    const int64_t t = a / (uint32_t)k;
-    const int32_t r = row_of[a];
-    if (r < 0 || r >= num_rows) {
+    bool live = a < (uint64_t)T * k;
+    const uint32_t slice = live ? wave - a * (uint32_t)slices : 0;
+    const int32_t r = live ? row_of[a] : 0;
+    if (live && (r < 0 || r >= num_rows)) {
         if (dev_status && lane == 0 && slice == 0) atomicOr(dev_status, kStatusIndex);
-        return;
+        live = false;
     }
+    // one 16-byte load per lane, re-dealt through LDS so that each atomic
+    // instruction covers 64 consecutive output elements
+    const int64_t cv = (int64_t)slice * 64 * E + (int64_t)lane * E;
+    if (live && cv < H) {
+        const char* row = reinterpret_cast<const char*>(rows) + (int64_t)r * H * kElemBytes;
+        float y[E];
+        Vec<DT>::widen(load16_stream(row + cv * kElemBytes), y);
+#pragma unroll
+        for (int e = 0; e < E; ++e) stage[w][lane * E + e] = y[e];
+    }
+    __syncthreads();
+    if (!live) return;
+    const int64_t t = a / (uint32_t)k;
     const float g = gates[a];
-    const char* row = reinterpret_cast<const char*>(rows) + (int64_t)r * H * kElemBytes;
     float* o = out + t * H;
     const int64_t c0 = (int64_t)slice * 64 * E + lane;
-    float y[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int64_t c = c0 + 64 * e;
-        y[e] = c < H ? load_elem<DT>(row, c) : 0.f;
-    }
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const int64_t c = c0 + 64 * e;
         if (c < H) {
-            const float p = g * y[e];
+            const float p = g * stage[w][lane + 64 * e];
             unsafeAtomicAdd(o + c, p);
         }
     }
