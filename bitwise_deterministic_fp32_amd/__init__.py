@@ -20,6 +20,7 @@ __all__ = [
     "dr_status_string", "dr_last_error", "dr_version", "dr_set_launch_params", "dr_set_phase_events",
     "dr_sort_workspace_size", "dr_sort_by_dest",
     "dr_combine", "dr_combine_atomic", "dr_combine_fingerprinted_workspace_size", "dr_combine_fingerprinted",
+    "dr_combine_fingerprinted_noalloc",
     "dr_index_add_workspace_size", "dr_index_add", "dr_index_add_fingerprinted", "dr_index_add_atomic",
     "dr_sparse_attn_dk_workspace_size", "dr_sparse_attn_dk",
     "dr_splitk_gemm_tn", "dr_splitk_gemm_tn_atomic", "dr_splitk_reduce",
@@ -64,6 +65,8 @@ def _load() -> ctypes.CDLL:
         "dr_combine_fingerprinted_workspace_size": ([ctypes.c_int, i64, i64], sz),
         "dr_combine_fingerprinted": ([vp, ctypes.c_int, i64, i64, vp, vp, i64, i32, vp, vp, vp, sz, vp, vp],
                                      ctypes.c_int),
+        "dr_combine_fingerprinted_noalloc": ([vp, ctypes.c_int, i64, i64, vp, vp, i64, i32, vp, vp, vp, vp],
+                                             ctypes.c_int),
         "dr_index_add_workspace_size": ([i64, i32, i64], sz),
         "dr_index_add": ([vp, i32, i64, vp, ctypes.c_int, i64, vp, vp, vp, vp, sz, vp], ctypes.c_int),
         "dr_index_add_fingerprinted": ([vp, i32, i64, vp, ctypes.c_int, i64, vp, vp, vp, vp, vp, sz, vp], ctypes.c_int),
@@ -282,6 +285,19 @@ def dr_combine_fingerprinted(rows, row_of, gates, *, out=None, out_hash=None, ws
     _check(lib.dr_combine_fingerprinted(_p(rows), _DTYPES[rows.dtype], R, H, _p(row_of), _p(gates), T, k, _p(out),
                                         _p(out_hash), _p(ws), ws.numel(), _p(dev_status), _stream(stream)),
            "dr_combine_fingerprinted")
+    return out, out_hash
+
+
+def dr_combine_fingerprinted_noalloc(rows, row_of, gates, *, out, out_hash, dev_status=None, stream=None):
+    """dr_combine_fingerprinted with the library's static scratch instead of a workspace (nothing is
+    allocated, here or in the library: the caller passes out and out_hash).  Returns (out, out_hash)."""
+    R, H, T, k = _combine_args(rows, row_of, gates)
+    _sized(out, "out", rows.device, (torch.float32,), shape=(T, H))
+    _hash_buf(out_hash, "out_hash", rows.device)
+    _status_buf(dev_status, rows.device)
+    _check(lib.dr_combine_fingerprinted_noalloc(_p(rows), _DTYPES[rows.dtype], R, H, _p(row_of), _p(gates), T, k,
+                                                _p(out), _p(out_hash), _p(dev_status), _stream(stream)),
+           "dr_combine_fingerprinted_noalloc")
     return out, out_hash
 
 

@@ -249,6 +249,39 @@ constexpr int64_t kMaxN = (int64_t)1 << 31;
 
 namespace dr {
 
+dr_status report(dr_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+dr_status report_ok() { return ok(); }
+
+dr_status report_hip(hipError_t e, const char* what) { return hip_fail(e, what); }
+
+dr_status validate_combine(const char* what, const void* rows, dr_dtype rows_dtype, int64_t num_rows, int64_t hidden,
+                           const int32_t* row_of, const float* gates, int64_t T, int32_t k, const float* out,
+                           const int32_t* dev_status) {
+    dr_status st = check_dtype(rows_dtype, what);
+    if (st != DR_OK) return st;
+    if ((st = check_rows(rows, rows_dtype, hidden, what)) != DR_OK) return st;
+    if (!aligned(out, 16)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: out must be 16-byte aligned", what);
+    if (T < 0 || num_rows < 0 || num_rows >= kMaxN) return fail(DR_ERR_INVALID_ARGUMENT, "%s: bad T or num_rows", what);
+    if (k < 1) return fail(DR_ERR_INVALID_ARGUMENT, "%s: k must be >= 1", what);
+    if (k > 64) return fail(DR_ERR_UNSUPPORTED, "%s: k = %d > 64 is not supported", what, k);
+    if (T > 0 && (!rows || !row_of || !gates || !out)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: null pointer", what);
+    if (T > 0 && (!aligned(row_of, 4) || !aligned(gates, 4)))
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: row_of/gates must be 4-byte aligned", what);
+    if (dev_status && !aligned(dev_status, 4)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: misaligned dev_status", what);
+    if (T * ((hidden / elems16(rows_dtype) + 63) / 64) >= ((int64_t)1 << 32))
+        return fail(DR_ERR_UNSUPPORTED, "%s: T * column slices must be below 2^32", what);
+    return DR_OK;
+}
+
 Launch launch_config() {
     Launch l;
     l.grid_blocks = g_params.grid_blocks;
@@ -359,20 +392,9 @@ dr_status dr_sort_by_dest(const int32_t* dest, const int32_t* src_id, int32_t sr
 dr_status dr_combine(const void* rows, dr_dtype rows_dtype, int64_t num_rows, int64_t hidden,
                      const int32_t* row_of, const float* gates, int64_t T, int32_t k, float* out,
                      int32_t* dev_status, hipStream_t stream) {
-    const char* what = "dr_combine";
-    dr_status st = check_dtype(rows_dtype, what);
+    const dr_status st = dr::validate_combine("dr_combine", rows, rows_dtype, num_rows, hidden, row_of, gates, T, k,
+                                              out, dev_status);
     if (st != DR_OK) return st;
-    if ((st = check_rows(rows, rows_dtype, hidden, what)) != DR_OK) return st;
-    if (!aligned(out, 16)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: out must be 16-byte aligned", what);
-    if (T < 0 || num_rows < 0 || num_rows >= kMaxN) return fail(DR_ERR_INVALID_ARGUMENT, "%s: bad T or num_rows", what);
-    if (k < 1) return fail(DR_ERR_INVALID_ARGUMENT, "%s: k must be >= 1", what);
-    if (k > 64) return fail(DR_ERR_UNSUPPORTED, "%s: k = %d > 64 is not supported", what, k);
-    if (T > 0 && (!rows || !row_of || !gates || !out)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: null pointer", what);
-    if (T > 0 && (!aligned(row_of, 4) || !aligned(gates, 4)))
-        return fail(DR_ERR_INVALID_ARGUMENT, "%s: row_of/gates must be 4-byte aligned", what);
-    if (dev_status && !aligned(dev_status, 4)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: misaligned dev_status", what);
-    if (T * ((hidden / elems16(rows_dtype) + 63) / 64) >= ((int64_t)1 << 32))
-        return fail(DR_ERR_UNSUPPORTED, "%s: T * column slices must be below 2^32", what);
     DR_TRY_HIP(dr::launch_combine(rows, rows_dtype, num_rows, hidden, row_of, gates, T, k, out, dev_status, false,
                                   nullptr, stream),
                "combine launch");
@@ -391,24 +413,14 @@ dr_status dr_combine_fingerprinted(const void* rows, dr_dtype rows_dtype, int64_
                                    uint64_t* out_hash, void* ws, size_t ws_bytes, int32_t* dev_status,
                                    hipStream_t stream) {
     const char* what = "dr_combine_fingerprinted";
-    dr_status st = check_dtype(rows_dtype, what);
+    const dr_status st = dr::validate_combine(what, rows, rows_dtype, num_rows, hidden, row_of, gates, T, k, out,
+                                              dev_status);
     if (st != DR_OK) return st;
-    if ((st = check_rows(rows, rows_dtype, hidden, what)) != DR_OK) return st;
-    if (!aligned(out, 16)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: out must be 16-byte aligned", what);
-    if (T < 0 || num_rows < 0 || num_rows >= kMaxN) return fail(DR_ERR_INVALID_ARGUMENT, "%s: bad T or num_rows", what);
-    if (k < 1) return fail(DR_ERR_INVALID_ARGUMENT, "%s: k must be >= 1", what);
-    if (k > 64) return fail(DR_ERR_UNSUPPORTED, "%s: k = %d > 64 is not supported", what, k);
-    if (T > 0 && (!rows || !row_of || !gates || !out)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: null pointer", what);
-    if (T > 0 && (!aligned(row_of, 4) || !aligned(gates, 4)))
-        return fail(DR_ERR_INVALID_ARGUMENT, "%s: row_of/gates must be 4-byte aligned", what);
     if (!out_hash || !aligned(out_hash, 8)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: bad out_hash", what);
     if (!ws || !aligned(ws, 16)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: bad workspace", what);
     if (ws_bytes < dr_combine_fingerprinted_workspace_size(rows_dtype, hidden, T))
         return fail(DR_ERR_WORKSPACE_TOO_SMALL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes,
                     dr_combine_fingerprinted_workspace_size(rows_dtype, hidden, T));
-    if (dev_status && !aligned(dev_status, 4)) return fail(DR_ERR_INVALID_ARGUMENT, "%s: misaligned dev_status", what);
-    if (T * ((hidden / elems16(rows_dtype) + 63) / 64) >= ((int64_t)1 << 32))
-        return fail(DR_ERR_UNSUPPORTED, "%s: T * column slices must be below 2^32", what);
     const int64_t nb_max = dr::combine_fp_blocks(rows_dtype, hidden, T, 64);
     const int64_t nb = dr::combine_fp_blocks(rows_dtype, hidden, T, k);
     Carver c(ws);

@@ -50,6 +50,16 @@ struct Launch {
     int sort_tile(int64_t n) const { return sort_tile_log2 ? sort_tile_log2 : default_sort_tile_log2(n); }
 };
 Launch launch_config();
+
+// Error reporting of the C ABI (the thread-local text dr_last_error returns).
+dr_status report(dr_status s, const char* fmt, ...);
+dr_status report_ok();
+dr_status report_hip(hipError_t e, const char* what);
+// Argument checks shared by the combine entry points (nothing is launched on
+// an error; the error text is set).
+dr_status validate_combine(const char* what, const void* rows, dr_dtype rows_dtype, int64_t num_rows, int64_t hidden,
+                           const int32_t* row_of, const float* gates, int64_t T, int32_t k, const float* out,
+                           const int32_t* dev_status);
 int device_cu_count();  // compute units of the current device (cached)
 
 // ---------------------------------------------------------------------------

@@ -30,7 +30,9 @@
  * CONVENTIONS
  *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
  *     allocates no memory.  Scratch space comes from caller workspaces sized
- *     by the *_workspace_size functions.
+ *     by the *_workspace_size functions; the one exception is
+ *     dr_combine_fingerprinted_noalloc, whose scratch is a static device array
+ *     of the library.
  *   - Every call is asynchronous on the given HIP stream and does not
  *     synchronise, apart from dr_workspace_status and dr_read_status.
  *   - Argument errors are returned synchronously and nothing is launched.
@@ -183,6 +185,23 @@ dr_status dr_combine_fingerprinted(const void* rows, dr_dtype rows_dtype, int64_
                                    const int32_t* row_of, const float* gates, int64_t T, int32_t k, float* out,
                                    uint64_t* out_hash, void* ws, size_t ws_bytes, int32_t* dev_status,
                                    hipStream_t stream);
+
+/* dr_combine_fingerprinted without a workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and bits as
+ * dr_combine_fingerprinted, minus ws and ws_bytes; the library allocates
+ * nothing and calls no allocating routine.  Its scratch (one fingerprint
+ * partial per combine workgroup) is a static 1 MiB device array of the
+ * library, of which every GPU the call runs on holds a copy until the process
+ * ends.  A call whose scratch would exceed it (T * column slices above about
+ * 1,000,000 wavefronts for k <= 8, half that for k > 8: e.g. more than 65,536
+ * tokens of 7168 bf16 columns) returns DR_ERR_UNSUPPORTED and launches
+ * nothing.  Calls on one GPU share its copy: calls that overlap on one GPU
+ * (different streams or host threads) race and must be ordered by the caller;
+ * calls in one stream are ordered already. */
+dr_status dr_combine_fingerprinted_noalloc(const void* rows, dr_dtype rows_dtype, int64_t num_rows, int64_t hidden,
+                                           const int32_t* row_of, const float* gates, int64_t T, int32_t k, float* out,
+                                           uint64_t* out_hash, int32_t* dev_status, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * index_add: out[d] = out[d] + T(src rows i with index[i] == d, in order of i).

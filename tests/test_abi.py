@@ -343,3 +343,24 @@ def test_splitk_reduce_fingerprinted_rejects_bad_arguments(lib):
     assert f(FAKE, 64, n, FAKE, FAKE, None, need, None) == DR_ERR_INVALID_ARGUMENT       # null workspace
     assert f(FAKE, 64, n, FAKE, FAKE, FAKE, need - 1, None) == DR_ERR_WORKSPACE_TOO_SMALL
     assert f(FAKE, 1 << 27, n, FAKE, FAKE, FAKE, need, None) == DR_ERR_UNSUPPORTED
+
+
+def test_combine_fingerprinted_noalloc_rejects_before_any_device_work(lib):
+    """The no-allocation combine checks its arguments and its scratch bound
+    before it looks up the static scratch or launches anything: a call whose
+    scratch would exceed the 1 MiB static array is refused as unsupported."""
+    f = lib.dr_combine_fingerprinted_noalloc
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                  ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    bf16 = 1
+    # too big for the static scratch: 200,000 tokens of 7168 bf16 columns (2.8 M wavefronts at k = 8)
+    assert f(FAKE, bf16, 10 ** 6, 7168, FAKE, FAKE, 200_000, 8, FAKE, FAKE, None, None) == DR_ERR_UNSUPPORTED
+    assert b"scratch" in lib.dr_last_error()
+    # k > 8 halves the workgroup, so the bound is reached at half the tokens
+    assert f(FAKE, bf16, 10 ** 6, 7168, FAKE, FAKE, 60_000, 16, FAKE, FAKE, None, None) == DR_ERR_UNSUPPORTED
+    # the usual argument checks come first
+    assert f(FAKE, bf16, 100, 7168, FAKE, FAKE, 10, 8, FAKE, None, None, None) == DR_ERR_INVALID_ARGUMENT  # no hash
+    assert f(FAKE, bf16, 100, 7168, FAKE, FAKE, 10, 8, FAKE, FAKE + 4, None, None) == DR_ERR_INVALID_ARGUMENT
+    assert f(FAKE, bf16, 100, 7, FAKE, FAKE, 10, 8, FAKE, FAKE, None, None) == DR_ERR_INVALID_ARGUMENT  # hidden % 8
+    assert f(FAKE, 7, 100, 7168, FAKE, FAKE, 10, 8, FAKE, FAKE, None, None) == DR_ERR_UNSUPPORTED  # dtype
+    assert f(FAKE, bf16, 100, 7168, FAKE, FAKE, 10, 65, FAKE, FAKE, None, None) == DR_ERR_UNSUPPORTED  # k > 64
