@@ -26,7 +26,7 @@ __all__ = [
     "dr_splitk_gemm_tn", "dr_splitk_gemm_tn_atomic", "dr_splitk_reduce",
     "dr_splitk_reduce_fingerprinted_workspace_size", "dr_splitk_reduce_fingerprinted",
     "dr_grouped_splitk_max_slots", "dr_grouped_splitk_workspace_size", "dr_grouped_splitk_gemm_tn",
-    "dr_grouped_splitk_reduce", "dr_permute_rows",
+    "dr_grouped_splitk_reduce", "dr_grouped_wgrad_workspace_size", "dr_grouped_wgrad", "dr_permute_rows",
     "dr_decode_attention_workspace_size", "dr_decode_attention", "dr_decode_attention_occupancy_chunk",
     "dr_fingerprint_workspace_size", "dr_fingerprint", "fingerprint_value",
     "dr_workspace_status", "dr_read_status",
@@ -82,6 +82,8 @@ def _load() -> ctypes.CDLL:
         "dr_grouped_splitk_workspace_size": ([i64, i32, i32], sz),
         "dr_grouped_splitk_gemm_tn": ([vp, vp, i64, i64, i64, vp, i32, i32, vp, i64, vp, vp, sz, vp], ctypes.c_int),
         "dr_grouped_splitk_reduce": ([vp, i64, vp, i32, i64, vp, vp, vp], ctypes.c_int),
+        "dr_grouped_wgrad_workspace_size": ([i64, i32, i32, i64, i64], sz),
+        "dr_grouped_wgrad": ([vp, vp, i64, i64, i64, vp, i32, i32, vp, vp, sz, vp], ctypes.c_int),
         "dr_permute_rows": ([vp, i64, i64, vp, vp, i64, i32, vp, vp, vp], ctypes.c_int),
         "dr_decode_attention_workspace_size": ([i64, i32, i32, i32, i64], sz),
         "dr_decode_attention": ([vp, vp, vp, vp, ctypes.c_int, vp, i64, i32, i32, i64, i32, ctypes.c_float, i32, vp, sz,
@@ -500,6 +502,26 @@ def dr_grouped_splitk_reduce(partials, slot_offsets, ws, *, out=None, stream=Non
     _check(lib.dr_grouped_splitk_reduce(_p(partials), partials.shape[0], _p(slot_offsets), G, count, _p(out),
                                         _p(ws), _stream(stream)), "dr_grouped_splitk_reduce")
     return out
+
+
+def dr_grouped_wgrad_workspace_size(K: int, num_groups: int, split_tokens: int, M: int, N: int) -> int:
+    return int(lib.dr_grouped_wgrad_workspace_size(K, num_groups, split_tokens, M, N))
+
+
+def dr_grouped_wgrad(X, dY, group_offsets, split_tokens: int, *, out=None, ws=None, stream=None):
+    """out[g] = ordered tree over group g's slot partials X_s^T dY_s (large M, N; partials kept in registers).
+    Returns (out, ws)."""
+    K, M, N = _gemm_args(X, dY)
+    _sized(group_offsets, "group_offsets", X.device, (torch.int32,), min_numel=2)
+    G = group_offsets.numel() - 1
+    if out is None:
+        out = torch.empty(G, M, N, dtype=torch.float32, device=X.device)
+    else:
+        _sized(out, "out", X.device, (torch.float32,), shape=(G, M, N))
+    ws = _ws(ws, dr_grouped_wgrad_workspace_size(K, G, split_tokens, M, N), X.device)
+    _check(lib.dr_grouped_wgrad(_p(X), _p(dY), K, M, N, _p(group_offsets), G, split_tokens, _p(out), _p(ws),
+                                ws.numel(), _stream(stream)), "dr_grouped_wgrad")
+    return out, ws
 
 
 def dr_permute_rows(rows, perm, k: int, *, inv_perm=None, out=None, dev_status=None, stream=None):

@@ -20,7 +20,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdetreduce.so")
 
 SOURCES = ["api.cpp", "sort.hip", "segreduce.hip", "combine.hip", "splitk.hip", "fingerprint.hip", "atomic.hip",
-           "permute.hip", "decode.hip", "noalloc.hip"]
+           "permute.hip", "decode.hip", "noalloc.hip", "wgrad.hip"]
 ARCH = "gfx950"
 
 # -ffp-contract=off: no multiply-add fusion anywhere (products are rounded

@@ -245,6 +245,21 @@ dr_status check_rows(const void* p, dr_dtype dt, int64_t hidden, const char* wha
 
 constexpr int64_t kMaxN = (int64_t)1 << 31;
 
+struct WgradBuffers {
+    int32_t* status;
+    int32_t* cum_items;
+    int32_t* chunk_base;
+    float* chunks;
+};
+WgradBuffers carve_wgrad(Carver& c, int64_t K, int32_t num_groups, int32_t split, int64_t M, int64_t N) {
+    WgradBuffers b{};
+    b.status = c.take<int32_t>(dr::kStatusBytes / sizeof(int32_t));
+    b.cum_items = c.take<int32_t>((int64_t)num_groups + 1);
+    b.chunk_base = c.take<int32_t>(num_groups);
+    b.chunks = c.take<float>(dr::wgrad_max_chunk_rows(K, split) * M * N);
+    return b;
+}
+
 }  // namespace
 
 namespace dr {
@@ -764,6 +779,46 @@ dr_status dr_grouped_splitk_reduce(const float* partials, int64_t partial_slots,
     DR_TRY_HIP(dr::launch_grouped_reduce(partials, slot_offsets, partial_slots, num_groups, count, out,
                                          static_cast<const int32_t*>(ws), stream),
                "grouped reduce launch");
+    return ok();
+}
+
+// ---------------------------------------------------------------------------
+
+size_t dr_grouped_wgrad_workspace_size(int64_t K, int32_t num_groups, int32_t split_tokens, int64_t M, int64_t N) {
+    if (K < 0 || num_groups < 1 || split_tokens < 1 || M < 1 || N < 1) return 0;
+    Carver c(nullptr);
+    carve_wgrad(c, K, num_groups, split_tokens, M, N);
+    return c.off;
+}
+
+dr_status dr_grouped_wgrad(const void* X, const void* dY, int64_t K, int64_t M, int64_t N,
+                           const int32_t* group_offsets, int32_t num_groups, int32_t split_tokens, float* out,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+    const char* what = "dr_grouped_wgrad";
+    if (!X || !dY || !group_offsets || !out || !ws) return fail(DR_ERR_INVALID_ARGUMENT, "%s: null pointer", what);
+    if (K < 1 || M < 1 || N < 1) return fail(DR_ERR_INVALID_ARGUMENT, "%s: K, M, N must be >= 1", what);
+    if (num_groups < 1 || num_groups > 65535)
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: num_groups must be in [1, 65535]", what);
+    if (split_tokens < 1) return fail(DR_ERR_INVALID_ARGUMENT, "%s: split_tokens must be >= 1", what);
+    if (M % 8 != 0 || N % 8 != 0)
+        return fail(DR_ERR_UNSUPPORTED, "%s: M and N must be multiples of 8 (the thin split handles other shapes)",
+                    what);
+    if (!aligned(X, 16) || !aligned(dY, 16) || !aligned(out, 16) || !aligned(group_offsets, 4) || !aligned(ws, 16))
+        return fail(DR_ERR_INVALID_ARGUMENT, "%s: X, dY, out and ws must be 16-byte aligned", what);
+    // token indices are int32 on the device; work items are counted in 31 bits
+    if (K >= kMaxN - split_tokens) return fail(DR_ERR_UNSUPPORTED, "%s: K too large for one call", what);
+    if (dr::wgrad_max_items(K, num_groups, split_tokens, M, N) >= ((int64_t)1 << 31))
+        return fail(DR_ERR_UNSUPPORTED, "%s: M, N and the chunk bound give too many tiles for one call", what);
+    if (dr::wgrad_max_chunk_rows(K, split_tokens) >= ((int64_t)1 << 31))
+        return fail(DR_ERR_UNSUPPORTED, "%s: too many chunks for one call", what);
+    Carver c(ws);
+    const WgradBuffers b = carve_wgrad(c, K, num_groups, split_tokens, M, N);
+    if (c.off > ws_bytes)
+        return fail(DR_ERR_WORKSPACE_TOO_SMALL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes, c.off);
+    DR_TRY_HIP(dr::launch_wgrad(static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(dY), K, M, N,
+                                group_offsets, num_groups, split_tokens, out, b.status, b.cum_items, b.chunk_base,
+                                b.chunks, stream),
+               "grouped wgrad launch");
     return ok();
 }
 

@@ -165,6 +165,13 @@ hipError_t launch_grouped_splitk_gemm(const uint16_t* X, const uint16_t* dY, int
 hipError_t launch_grouped_reduce(const float* partials, const int32_t* slot_offsets, int64_t max_slots,
                                  int32_t num_groups, int64_t count, float* out, const int32_t* status,
                                  hipStream_t s);
+// grouped-GEMM weight gradient with private slots, slot partials kept in registers (large M and N):
+// the plan, the tile kernel and the merge of chunk sums of groups of more than 8 slots
+int64_t wgrad_max_chunk_rows(int64_t K, int32_t split);
+int64_t wgrad_max_items(int64_t K, int32_t num_groups, int32_t split, int64_t M, int64_t N);
+hipError_t launch_wgrad(const uint16_t* X, const uint16_t* dY, int64_t K, int64_t M, int64_t N,
+                        const int32_t* group_offsets, int32_t num_groups, int32_t split, float* out,
+                        int32_t* status, int32_t* cum_items, int32_t* chunk_base, float* chunks, hipStream_t s);
 // dispatch-side permute: out[r] = rows[perm[r] / k]; with inv_perm the work runs in token order
 hipError_t launch_permute_rows(const void* rows, int64_t row_bytes, int64_t num_rows, const int32_t* perm,
                                const int32_t* inv_perm, int64_t n, int32_t k, void* out, int32_t* dev_status,

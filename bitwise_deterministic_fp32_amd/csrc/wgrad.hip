@@ -1,0 +1,585 @@
+// Grouped-GEMM weight gradient with private token slots, merged in slot order,
+// for expert shapes (large M and N).
+//
+// dW[g] = X_g^T dY_g for every group (expert) g, where group g owns the
+// expert-major tokens [off[g], off[g+1]).  The group's tokens are cut into
+// private slots of `split` tokens from its first token (the last one short);
+// slot s's partial P_s = X_s^T dY_s is accumulated in token order with the
+// bf16 MFMA into fp32, and dW[g] = T(P_0, ..., P_{S_g-1}): chunks of 8 slots
+// summed left to right, the chunk sums combined by the pairwise tree.  This is
+// the private-slot fix the pages give for the grouped-GEMM epilogue (every
+// writer gets its own slot, merged in a fixed order: bitwise-determinism
+// interview note, "where nondeterminism comes from", multiple-writers row;
+// Megatron-LM determinism reference, section 3.3, grouped-GEMM wgrad).  The
+// bits equal those of dr_grouped_splitk_gemm_tn + dr_grouped_splitk_reduce:
+// the same MFMA sequence per slot and the same tree.
+//
+// Where the thin split-K kernel streams X once past 32-column tiles, here a
+// workgroup owns a 256 (M) x 128 (N) output tile of one chunk of one group and
+// walks the chunk's slots: each slot's partial is accumulated in registers
+// (4 wavefronts x 64 x 128), then added into the chunk's running sum, also in
+// registers, so the partials never go to memory.  A group of at most 8 slots
+// writes dW[g] directly; a longer group writes its chunk sums to a workspace,
+// and a merge kernel applies the pairwise tree over them in chunk order.
+//
+// Stages of 64 tokens go from global memory straight into LDS (16-byte
+// direct loads, gfx950), in their natural token-major layout, into a ring of
+// three stage buffers: the loads of stage j+2 fly while stage j is computed.
+// The MFMA operands (8 consecutive tokens of one column) come out of LDS
+// with the transposing read ds_read_b64_tr_b16 (two per operand): lane j of a
+// 16-lane group receives column j of the group's 4-token x 16-column block.
+// The 16-byte chunks of a row are XOR-swizzled by the row's low two bits, so
+// the four rows a transposing read touches fall in different banks.
+#include "internal.h"
+
+namespace dr {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int TM = 256;          // output rows (M) per workgroup
+constexpr int TN = 128;          // output columns (N) per workgroup
+constexpr int TK = 64;           // tokens per stage
+constexpr int kThreads = 256;    // 4 wavefronts, each 64 (M) x 128 (N)
+constexpr int kChunk = 8;        // slots summed left to right before the pairwise tree
+
+// LDS element offset of (row r, column c) in a stage tile of `cols` columns:
+// the 16-byte chunk c / 8 of row r sits at position (c / 8) ^ 4 (r & 3).
+template <int COLS>
+__device__ __forceinline__ int lds_at(int r, int c) {
+    return r * COLS + ((((c >> 3) ^ ((r & 3) << 2))) << 3) + (c & 7);
+}
+
+struct Plan {
+    const int32_t* cum_items;   // [G + 1] work items before each group
+    const int32_t* chunk_base;  // [G] first chunk-sum row of a group of more than one chunk, else -1
+};
+
+// One work item: chunk c of group g, output tile (m0, n0).
+struct Item {
+    int32_t g, c;
+    int64_t m0, n0;
+    int32_t t0, t1;     // the group's tokens
+    int32_t slot0;      // first slot of the chunk
+    int32_t nslots;     // slots of the chunk (0 for an empty group)
+    float* dst;         // dW[g] or the chunk's sum row
+};
+
+__device__ __forceinline__ Item item_of(uint32_t it, const int32_t* __restrict__ off, int32_t G, int32_t split,
+                                        uint32_t mtiles, uint32_t ntiles, int64_t M, int64_t N, const Plan& p,
+                                        float* __restrict__ out, float* __restrict__ chunks) {
+    // the group: the last g with cum_items[g] <= it
+    int32_t lo = 0, hi = G;  // invariant: cum_items[lo] <= it < cum_items[hi]
+    while (hi - lo > 1) {
+        const int32_t mid = (lo + hi) >> 1;
+        if ((uint32_t)p.cum_items[mid] <= it) lo = mid;
+        else hi = mid;
+    }
+    Item w;
+    w.g = lo;
+    const uint32_t local = it - (uint32_t)p.cum_items[lo];
+    const uint32_t tiles = mtiles * ntiles;
+    w.c = (int32_t)(local / tiles);
+    const uint32_t t = local - (uint32_t)w.c * tiles;
+    w.m0 = (int64_t)(t / ntiles) * TM;
+    w.n0 = (int64_t)(t % ntiles) * TN;
+    w.t0 = off[lo];
+    w.t1 = off[lo + 1];
+    const int32_t slots = (int32_t)(((uint32_t)(w.t1 - w.t0) + (uint32_t)split - 1u) / (uint32_t)split);
+    w.slot0 = w.c * kChunk;
+    w.nslots = min(kChunk, slots - w.slot0);
+    if (w.nslots < 0) w.nslots = 0;
+    const int32_t cb = p.chunk_base[lo];
+    w.dst = cb < 0 ? out + (int64_t)lo * M * N : chunks + (int64_t)(cb + w.c) * M * N;
+    return w;
+}
+
+// One stage of work: the `stage`-th 64 tokens of slot `slot` of an item.
+struct Unit {
+    uint32_t it;
+    int32_t slot;   // within the chunk
+    int32_t stage;
+};
+
+struct Stage {
+    int32_t t;      // first token
+    int32_t rows;   // valid tokens (0 for an empty group)
+    int32_t slot_last, chunk_first, chunk_last;  // flags (0 or 1)
+};
+
+__device__ __forceinline__ Stage stage_of(const Item& w, const Unit& u, int32_t split) {
+    Stage s;
+    s.chunk_first = u.slot == 0;
+    if (w.nslots == 0) {
+        s.t = w.t0;
+        s.rows = 0;
+        s.slot_last = s.chunk_last = 1;
+        return s;
+    }
+    const int32_t ts = w.t0 + (w.slot0 + u.slot) * split;  // the slot's first token
+    const int32_t te = min(w.t1, ts + split);
+    s.t = ts + u.stage * TK;
+    s.rows = min(TK, te - s.t);
+    s.slot_last = s.t + TK >= te;
+    s.chunk_last = s.slot_last && u.slot + 1 == w.nslots;
+    return s;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// 16 zero bytes: the source of every direct load of a token row past the
+// stage or a column past M or N, so those LDS entries are zero and the MFMAs
+// need no masking (a read-only constant, not scratch).
+__device__ __align__(16) const uint32_t kZero16[4] = {0u, 0u, 0u, 0u};
+
+constexpr int kXLoads = TM * TK * 2 / 16 / kThreads;  // 16-byte direct loads per thread per stage: 8
+constexpr int kYLoads = TN * TK * 2 / 16 / kThreads;  // 4
+constexpr int kLoadsPerStage = kXLoads + kYLoads;
+
+// Issues the direct loads of a stage into one ring buffer.  Instruction k of
+// wavefront w fills the 1 KB at position 64 (n w + k) of the tile (lane L at
+// 16 L); position p is row p / (COLS / 8), chunk (p % (COLS / 8)) ^ 4 (row & 3).
+// Every instruction is issued (so each stage adds the same count to the
+// wavefront's vector memory counter); lanes whose row is past the stage's
+// tokens or whose columns are past M or N load 16 zero bytes instead.
+template <int COLS>
+__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ src, int64_t ld, int64_t col0, int64_t cols_total,
+                                          int32_t t, int32_t rows, uint16_t* tile) {
+    constexpr int kChunks = COLS / 8;                      // 16-byte chunks per row
+    constexpr int kLoads = COLS * TK * 2 / 16 / kThreads;  // instructions per thread
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+        const int pos = 64 * (kLoads * wv + k) + lane;
+        const int r = pos / kChunks;
+        const int cc = (pos % kChunks) ^ ((r & 3) << 2);
+        const int64_t col = col0 + 8 * cc;
+        const void* from = (r < rows && col < cols_total) ? static_cast<const void*>(src + (int64_t)(t + r) * ld + col)
+                                                          : static_cast<const void*>(kZero16);
+        __builtin_amdgcn_global_load_lds(from, (lds_void*)(tile + 64 * (kLoads * wv + k) * 8), 16, 0, 0);
+    }
+}
+
+// Per-lane element offset, within a stage tile of COLS columns, of the first
+// transposing read of an MFMA operand whose 32 columns start at `colbase`
+// (lane (i, h) gets tokens 16 ks + 8 h + 0..7 of column colbase + i): lane
+// (a, b, c) of the read addresses row 8 (a >> 1) + b, columns
+// colbase + 16 (a & 1) + 4 c .. + 3.  The read for tokens +4 is 4 rows on,
+// and the k-step ks 16 rows on; neither changes the swizzle (row & 3 = b).
+template <int COLS>
+__device__ __forceinline__ int operand_offset(int colbase) {
+    const int lane = threadIdx.x & 63;
+    const int a = lane >> 4, b = (lane >> 2) & 3, c = lane & 3;
+    return lds_at<COLS>(8 * (a >> 1) + b, colbase + 16 * (a & 1) + 4 * c);
+}
+
+// The operands of one k-step: A for the wavefront's two 32-row blocks of X,
+// B for the four 32-column blocks of dY, by twelve transposing LDS reads.
+// The reads sit in one asm block that also waits for them: the compiler does
+// not see them as reads of LDS written by direct loads, so it adds no wait on
+// the loads still in flight for the next stages (the vector-memory wait before
+// the stage's barrier is what makes this stage's data valid), and no output
+// register is used before its read is complete.
+struct KOps {
+    bf16x8 a[2], b[4];
+};
+
+__device__ __forceinline__ KOps read_kstep(const uint16_t* xt, const uint16_t* yt, const int (&xoff)[2],
+                                           const int (&yoff)[4], int ks) {
+    typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+    typedef __attribute__((address_space(3))) const uint16_t lds_u16;
+    const uint32_t xb = (uint32_t)(uintptr_t)((lds_u16*)(xt + 16 * ks * TM));
+    const uint32_t yb = (uint32_t)(uintptr_t)((lds_u16*)(yt + 16 * ks * TN));
+    u32x2v r[12];
+    const uint32_t a0 = xb + 2 * xoff[0], a1 = xb + 2 * xoff[1];
+    const uint32_t b0 = yb + 2 * yoff[0], b1 = yb + 2 * yoff[1], b2 = yb + 2 * yoff[2], b3 = yb + 2 * yoff[3];
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %12\n"
+        "ds_read_b64_tr_b16 %1, %12 offset:2048\n"
+        "ds_read_b64_tr_b16 %2, %13\n"
+        "ds_read_b64_tr_b16 %3, %13 offset:2048\n"
+        "ds_read_b64_tr_b16 %4, %14\n"
+        "ds_read_b64_tr_b16 %5, %14 offset:1024\n"
+        "ds_read_b64_tr_b16 %6, %15\n"
+        "ds_read_b64_tr_b16 %7, %15 offset:1024\n"
+        "ds_read_b64_tr_b16 %8, %16\n"
+        "ds_read_b64_tr_b16 %9, %16 offset:1024\n"
+        "ds_read_b64_tr_b16 %10, %17\n"
+        "ds_read_b64_tr_b16 %11, %17 offset:1024\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
+          "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11])
+        : "v"(a0), "v"(a1), "v"(b0), "v"(b1), "v"(b2), "v"(b3)
+        : "memory");
+    KOps o;
+    typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int q = 0; q < 6; ++q) {
+        const u32x4v v{r[2 * q][0], r[2 * q][1], r[2 * q + 1][0], r[2 * q + 1][1]};
+        if (q < 2) o.a[q] = __builtin_bit_cast(bf16x8, v);
+        else o.b[q - 2] = __builtin_bit_cast(bf16x8, v);
+    }
+    return o;
+}
+
+// The chunk sum s (or the empty group's zero tile) to its destination.  Lane
+// (i, h) holds column 32nb + i and rows 8(v/4) + 4h + v%4 of each 32x32 block.
+// One 32x32 block at a time, walking one row pointer, so that few addresses
+// are live at once.
+__device__ __forceinline__ void store_tile(const f32x16 (&s)[2][4], const Item& w, int64_t M, int64_t N) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int i = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const int64_t m_first = w.m0 + 64 * wv + 32 * mb + 4 * h;
+            const int64_t n = w.n0 + 32 * nb + i;
+            float* p = w.dst + m_first * N + n;
+            const bool col_ok = n < N;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int dm = 8 * (v / 4) + (v % 4);
+                if (col_ok && m_first + dm < M) __builtin_nontemporal_store(s[mb][nb][v], p);
+                p += (v % 4 == 3) ? 5 * N : N;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+}
+
+struct Work {
+    Item w;
+    Stage s;
+    Unit u;
+    int32_t valid;  // flag (0 or 1)
+};
+
+__device__ __forceinline__ Work advance(const Work& c, uint32_t P, uint32_t items, const int32_t* __restrict__ off,
+                                        int32_t G, int32_t split, uint32_t mtiles, uint32_t ntiles, int64_t M,
+                                        int64_t N, const Plan& plan, float* __restrict__ out,
+                                        float* __restrict__ chunks) {
+    Work n = c;
+    if (!c.valid) return n;
+    if (!c.s.slot_last) {
+        n.u.stage += 1;
+    } else if (!c.s.chunk_last) {
+        n.u.slot += 1;
+        n.u.stage = 0;
+    } else {
+        n.u = Unit{c.u.it + P, 0, 0};
+    }
+    n.valid = n.u.it < items;
+    if (!n.valid) return n;
+    if (n.u.it != c.u.it) n.w = item_of(n.u.it, off, G, split, mtiles, ntiles, M, N, plan, out, chunks);
+    n.s = stage_of(n.w, n.u, split);
+    return n;
+}
+
+// s_waitcnt with only the vector memory count: vmcnt(n), expcnt and lgkmcnt left alone (gfx9 encoding)
+#define DR_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// One stage in ring buffer B: wait for its loads, issue the loads of the
+// stage two ahead into buffer (B + 2) % 3, compute, and close the slot and
+// the chunk when they end.  Returns false when the worker has no more work.
+template <int B>
+__device__ __forceinline__ bool step(Work& cur, Work& nx1, const uint16_t* __restrict__ xrd,
+                                     const uint16_t* __restrict__ yrd, uint16_t* __restrict__ xdma,
+                                     uint16_t* __restrict__ ydma,
+                                     f32x16 (&acc)[2][4], f32x16 (&sum)[2][4], const uint16_t* __restrict__ X,
+                                     const uint16_t* __restrict__ dY, int64_t K, int64_t M, int64_t N, uint32_t P,
+                                     uint32_t items, const int32_t* __restrict__ off, int32_t G, int32_t split,
+                                     uint32_t mtiles, uint32_t ntiles, const Plan& plan, float* __restrict__ out,
+                                     float* __restrict__ chunks) {
+    if (!cur.valid) return false;
+    // this stage's loads are done once at most the next stage's are outstanding
+    if (nx1.valid) DR_WAIT_VMCNT(kLoadsPerStage);
+    else DR_WAIT_VMCNT(0);
+    // Every wavefront's loads of this stage have landed (each waited for its own
+    // above) and every wavefront is done reading buffer (B + 2) % 3 (its
+    // operands were consumed by the previous stage's MFMAs).  A plain barrier:
+    // the workgroup fences of __syncthreads would wait for the loads still in
+    // flight for the next two stages.
+    __builtin_amdgcn_s_barrier();
+    const Work nx2 = advance(nx1, P, items, off, G, split, mtiles, ntiles, M, N, plan, out, chunks);
+    if (nx2.valid) {
+        load_tile<TM>(X, M, nx2.w.m0, M, nx2.s.t, nx2.s.rows, xdma);
+        load_tile<TN>(dY, N, nx2.w.n0, N, nx2.s.t, nx2.s.rows, ydma);
+    }
+    const int wv = threadIdx.x >> 6;
+    const int ksteps = (cur.s.rows + 15) >> 4;
+    int xoff[2], yoff[4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) xoff[mb] = operand_offset<TM>(64 * wv + 32 * mb);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) yoff[nb] = operand_offset<TN>(32 * nb);
+    if (ksteps > 0) {
+        KOps cur_ops = read_kstep(xrd, yrd, xoff, yoff, 0);
+#pragma unroll
+        for (int ks = 0; ks < TK / 16; ++ks) {
+            if (ks >= ksteps) break;
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb)
+                    acc[mb][nb] =
+                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur_ops.a[mb], cur_ops.b[nb], acc[mb][nb], 0, 0, 0);
+            // the next k-step's reads run while these MFMAs execute
+            __builtin_amdgcn_sched_barrier(0);
+            if (ks + 1 < TK / 16 && ks + 1 < ksteps) cur_ops = read_kstep(xrd, yrd, xoff, yoff, ks + 1);
+        }
+    }
+    if (cur.s.slot_last) {
+        // the slot's partial joins the chunk's left-to-right sum, which starts
+        // as -0.0 (an exact additive identity: -0.0 + x is x for every x, -0.0
+        // included), so the first slot's partial enters unchanged
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    sum[mb][nb][v] = sum[mb][nb][v] + acc[mb][nb][v];
+                    acc[mb][nb][v] = 0.f;
+                }
+                // one 16-value block at a time: keeps the copies out of the accumulators few
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        if (cur.s.chunk_last) {
+            store_tile(sum, cur.w, M, N);
+            DR_WAIT_VMCNT(0);  // stores count too: settle the counter so the next waits stay exact
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) sum[mb][nb][v] = neg_zero();
+        }
+    }
+    cur = nx1;
+    nx1 = nx2;
+    return true;
+}
+
+// Persistent workgroups; worker w takes items w, w + P, w + 2P, ...  Logical
+// workers are numbered XCD by XCD (workgroup b runs on XCD b mod 8), so the
+// items in flight at one time on one XCD are neighbouring tiles: the 16 N
+// tiles of one M panel share their X stage in that XCD's L2.
+__global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(const uint16_t* __restrict__ X,
+                                                            const uint16_t* __restrict__ dY, int64_t K, int64_t M,
+                                                            int64_t N, const int32_t* __restrict__ off, int32_t G,
+                                                            int32_t split, uint32_t mtiles, uint32_t ntiles,
+                                                            const int32_t* __restrict__ cum_items,
+                                                            const int32_t* __restrict__ chunk_base,
+                                                            const int32_t* __restrict__ status,
+                                                            float* __restrict__ out, float* __restrict__ chunks) {
+    __shared__ __attribute__((aligned(1024))) uint16_t xs[3][TM * TK];
+    __shared__ __attribute__((aligned(1024))) uint16_t ys[3][TN * TK];
+    if (status[kWordStatus] != 0) return;  // the offsets failed the plan's check: nothing is written
+    const Plan plan{cum_items, chunk_base};
+    const uint32_t items = (uint32_t)plan.cum_items[G];
+    const uint32_t P = gridDim.x;
+    const uint32_t b = blockIdx.x;
+    const uint32_t wkr = (P % 8 == 0) ? (b % 8) * (P / 8) + b / 8 : b;
+    if (wkr >= items) return;
+
+    Work cur;
+    cur.u = Unit{wkr, 0, 0};
+    cur.valid = 1;
+    cur.w = item_of(wkr, off, G, split, mtiles, ntiles, M, N, plan, out, chunks);
+    cur.s = stage_of(cur.w, cur.u, split);
+    Work nx1 = advance(cur, P, items, off, G, split, mtiles, ntiles, M, N, plan, out, chunks);
+    load_tile<TM>(X, M, cur.w.m0, M, cur.s.t, cur.s.rows, xs[0]);
+    load_tile<TN>(dY, N, cur.w.n0, N, cur.s.t, cur.s.rows, ys[0]);
+    if (nx1.valid) {
+        load_tile<TM>(X, M, nx1.w.m0, M, nx1.s.t, nx1.s.rows, xs[1]);
+        load_tile<TN>(dY, N, nx1.w.n0, N, nx1.s.t, nx1.s.rows, ys[1]);
+    }
+
+    f32x16 acc[2][4], sum[2][4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                acc[mb][nb][v] = 0.f;
+                sum[mb][nb][v] = neg_zero();
+            }
+    while (true) {
+        if (!step<0>(cur, nx1, xs[0], ys[0], xs[2], ys[2], acc, sum, X, dY, K, M, N, P, items,
+                     off, G, split, mtiles, ntiles, plan, out, chunks))
+            break;
+        if (!step<1>(cur, nx1, xs[1], ys[1], xs[0], ys[0], acc, sum, X, dY, K, M, N, P, items,
+                     off, G, split, mtiles, ntiles, plan, out, chunks))
+            break;
+        if (!step<2>(cur, nx1, xs[2], ys[2], xs[1], ys[1], acc, sum, X, dY, K, M, N, P, items,
+                     off, G, split, mtiles, ntiles, plan, out, chunks))
+            break;
+    }
+}
+
+// out[g] = the pairwise tree over the group's chunk sums, in chunk order
+// (groups of more than one chunk; blockIdx.y = group).  Binary counter: a new
+// chunk sum merges with the stored ones while the count's low bits carry, and
+// the stored ones fold from the right at the end, which is the tree that
+// splits at the largest power of two below the chunk count.
+constexpr int kMergeThreads = 256;
+constexpr int kMergeDepth = 24;
+__global__ __launch_bounds__(kMergeThreads) void wgrad_merge_kernel(const float* __restrict__ chunks,
+                                                                    const int32_t* __restrict__ off,
+                                                                    const int32_t* __restrict__ chunk_base,
+                                                                    int32_t split, int64_t count,
+                                                                    float* __restrict__ out,
+                                                                    const int32_t* __restrict__ status) {
+    if (status[kWordStatus] != 0) return;
+    const int64_t g = blockIdx.y;
+    const int32_t cb = chunk_base[g];
+    if (cb < 0) return;
+    const int64_t e0 = ((int64_t)blockIdx.x * kMergeThreads + threadIdx.x) * 4;
+    if (e0 >= count) return;
+    const uint32_t slots = ((uint32_t)(off[g + 1] - off[g]) + (uint32_t)split - 1u) / (uint32_t)split;
+    const uint32_t nch = (slots + kChunk - 1) / kChunk;
+    float level[kMergeDepth][4];
+    for (uint32_t c = 0; c < nch; ++c) {
+        const u32x4 raw = load16_stream(chunks + (int64_t)(cb + c) * count + e0);
+        float v[4] = {__uint_as_float(raw.x), __uint_as_float(raw.y), __uint_as_float(raw.z),
+                      __uint_as_float(raw.w)};
+        bool carry = true;
+#pragma unroll
+        for (int l = 0; l < kMergeDepth; ++l) {
+            if (carry) {
+                if ((c >> l) & 1u) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) v[e] = level[l][e] + v[e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) level[l][e] = v[e];
+                    carry = false;
+                }
+            }
+        }
+    }
+    float acc[4];
+    bool have = false;
+#pragma unroll
+    for (int l = 0; l < kMergeDepth; ++l) {
+        if ((nch >> l) & 1u) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[e] = have ? level[l][e] + acc[e] : level[l][e];
+            have = true;
+        }
+    }
+    store16(out + g * count + e0, u32x4{__float_as_uint(acc[0]), __float_as_uint(acc[1]), __float_as_uint(acc[2]),
+                                        __float_as_uint(acc[3])});
+}
+
+// The plan, by one workgroup: per group, its chunk count (at least one work
+// item per tile, also for an empty group, which gets the zero gradient), the
+// cumulative work items and, for groups of more than one chunk, the first row
+// of their chunk sums.  Offsets that are not non-decreasing within [0, K], or
+// chunk sums beyond the workspace bound, set the status word (nothing is then
+// computed or written); otherwise the word is cleared.
+constexpr int kPlanThreads = 1024;
+__device__ __forceinline__ int32_t block_exclusive_scan(int32_t v, int32_t* total, int32_t* wave_tot) {
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int32_t incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int32_t t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+    }
+    if (lane == 63) wave_tot[w] = incl;
+    __syncthreads();
+    int32_t before = 0, all = 0;
+    for (int k = 0; k < kPlanThreads / 64; ++k) {
+        before += k < w ? wave_tot[k] : 0;
+        all += wave_tot[k];
+    }
+    __syncthreads();
+    *total = all;
+    return before + incl - v;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void wgrad_plan_kernel(const int32_t* __restrict__ off, int32_t G,
+                                                                  int64_t K, int32_t split, int64_t tiles,
+                                                                  int64_t max_items, int64_t max_chunk_rows,
+                                                                  int32_t* __restrict__ cum_items,
+                                                                  int32_t* __restrict__ chunk_base,
+                                                                  int32_t* __restrict__ status) {
+    __shared__ int32_t wave_tot[2][kPlanThreads / 64];
+    const int tid = threadIdx.x;
+    int64_t item_carry = 0, chunk_carry = 0;
+    int bad = 0;
+    for (int32_t g0 = 0; g0 < G; g0 += kPlanThreads) {
+        const int32_t g = g0 + tid;
+        int32_t nitems = 0, nchunk_rows = 0;
+        if (g < G) {
+            const int32_t a = off[g], b = off[g + 1];
+            if (a < 0 || b < a || (int64_t)b > K) {
+                bad = 1;
+            } else {
+                const uint32_t slots = ((uint32_t)(b - a) + (uint32_t)split - 1u) / (uint32_t)split;
+                const int32_t nch = (int32_t)((slots + kChunk - 1) / kChunk);
+                nitems = (nch > 1 ? nch : 1) * (int32_t)tiles;  // the host bounds the total below 2^31
+                nchunk_rows = nch > 1 ? nch : 0;
+            }
+        }
+        int32_t it_total, ch_total;
+        const int32_t it_before = block_exclusive_scan(nitems, &it_total, wave_tot[0]);
+        const int32_t ch_before = block_exclusive_scan(nchunk_rows, &ch_total, wave_tot[1]);
+        if (g < G) {
+            cum_items[g] = (int32_t)min(item_carry + it_before, max_items);
+            chunk_base[g] = nchunk_rows ? (int32_t)min(chunk_carry + ch_before, max_chunk_rows) : -1;
+        }
+        item_carry += it_total;
+        chunk_carry += ch_total;
+    }
+    if (item_carry > max_items || chunk_carry > max_chunk_rows) bad = 1;
+    bad = __syncthreads_or(bad);
+    if (tid == 0) {
+        cum_items[G] = bad ? 0 : (int32_t)item_carry;
+        status[kWordStatus] = bad ? kStatusPlan : 0;
+    }
+}
+
+}  // namespace
+
+int64_t wgrad_max_chunk_rows(int64_t K, int32_t split) {
+    // a group of C >= 2 chunks has C <= 2 (C - 1) and C - 1 <= (K_g - 1) / (8 split)
+    return K / (4 * (int64_t)split) + 1;
+}
+
+int64_t wgrad_max_items(int64_t K, int32_t num_groups, int32_t split, int64_t M, int64_t N) {
+    const int64_t tiles = ((M + TM - 1) / TM) * ((N + TN - 1) / TN);
+    // sum_g max(1, C_g) <= G + K / (8 split)
+    return (num_groups + K / (kChunk * (int64_t)split) + 1) * tiles;
+}
+
+hipError_t launch_wgrad(const uint16_t* X, const uint16_t* dY, int64_t K, int64_t M, int64_t N,
+                        const int32_t* group_offsets, int32_t num_groups, int32_t split, float* out,
+                        int32_t* status, int32_t* cum_items, int32_t* chunk_base, float* chunks, hipStream_t s) {
+    const int64_t mtiles = (M + TM - 1) / TM, ntiles = (N + TN - 1) / TN;
+    const int64_t max_items = wgrad_max_items(K, num_groups, split, M, N);
+    hipLaunchKernelGGL(wgrad_plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, group_offsets, num_groups, K, split,
+                       mtiles * ntiles, max_items, wgrad_max_chunk_rows(K, split), cum_items, chunk_base, status);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const Launch lc = launch_config();
+    int64_t grid = lc.grid_blocks > 0 ? lc.grid_blocks : (int64_t)device_cu_count();
+    if (grid > max_items) grid = max_items;
+    if (grid < 1) grid = 1;
+    hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)grid), dim3(kThreads), 0, s, X, dY, K, M, N, group_offsets,
+                       num_groups, split, (uint32_t)mtiles, (uint32_t)ntiles, cum_items, chunk_base, status,
+                       out, chunks);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t count = M * N;
+    const dim3 mgrid((unsigned)((count / 4 + kMergeThreads - 1) / kMergeThreads), (unsigned)num_groups);
+    hipLaunchKernelGGL(wgrad_merge_kernel, mgrid, dim3(kMergeThreads), 0, s, chunks, group_offsets, chunk_base, split,
+                       count, out, status);
+    return hipGetLastError();
+}
+
+}  // namespace dr

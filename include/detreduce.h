@@ -365,6 +365,41 @@ dr_status dr_grouped_splitk_reduce(const float* partials, int64_t partial_slots,
                                    hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * The same grouped weight gradient for expert shapes (large M and N), with
+ * the slot partials kept in registers: per group g,
+ *   dW[g] = T over its slots s of  X_s^T dY_s   (slot order),
+ * slots as in dr_grouped_splitk_gemm_tn (consecutive runs of split_tokens
+ * tokens from the group's first token).  Same bits as
+ * dr_grouped_splitk_gemm_tn followed by dr_grouped_splitk_reduce: each slot's
+ * partial is accumulated in token order by the same bf16 MFMA steps, and the
+ * slots are summed by the same tree (chunks of 8 slots left to right, then the
+ * pairwise tree over the chunk sums).  The partials never reach memory: a
+ * workgroup owns a 256 x 128 tile of dW[g] and adds each slot's partial into
+ * the chunk's running sum as the slot ends; a group of more than 8 slots
+ * leaves its chunk sums in ws, and a merge applies the pairwise tree over them
+ * (the private-slot grouped-GEMM weight gradient of the bitwise-determinism
+ * interview note, multiple-writers row; Megatron-LM determinism reference,
+ * section 3.3, grouped-GEMM weight gradient as a determinism hotspot).
+ *
+ *   X[K, M], dY[K, N]    bf16 (bit patterns), expert-major token rows, 16-byte
+ *                        aligned; M and N multiples of 8 (other shapes:
+ *                        dr_grouped_splitk_gemm_tn).
+ *   group_offsets[G+1]   int32, device: non-decreasing within [0, K].
+ *   out[G, M, N]         fp32, written; a group with no token gets zeros.
+ *   ws                   >= dr_grouped_wgrad_workspace_size(K, G, split_tokens,
+ *                        M, N) bytes, 16-byte aligned: the status block, the
+ *                        work plan and room for the chunk sums of groups of
+ *                        more than 8 slots (at most K / (4 split_tokens) + 1
+ *                        tiles of M x N).  Its contents on entry do not matter.
+ * Offsets that are not non-decreasing within [0, K] set the status word
+ * (dr_workspace_status reports DR_ERR_BAD_PLAN) and out is not written.
+ * ---------------------------------------------------------------------- */
+size_t dr_grouped_wgrad_workspace_size(int64_t K, int32_t num_groups, int32_t split_tokens, int64_t M, int64_t N);
+dr_status dr_grouped_wgrad(const void* X, const void* dY, int64_t K, int64_t M, int64_t N,
+                           const int32_t* group_offsets, int32_t num_groups, int32_t split_tokens, float* out,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * Dispatch-side stable permute: out[r] = rows[perm[r] / k] (bytes copied).
  *
  * perm is dr_sort_by_dest's permutation of the T*k (token, slot) assignments

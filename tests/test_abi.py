@@ -364,3 +364,32 @@ def test_combine_fingerprinted_noalloc_rejects_before_any_device_work(lib):
     assert f(FAKE, bf16, 100, 7, FAKE, FAKE, 10, 8, FAKE, FAKE, None, None) == DR_ERR_INVALID_ARGUMENT  # hidden % 8
     assert f(FAKE, 7, 100, 7168, FAKE, FAKE, 10, 8, FAKE, FAKE, None, None) == DR_ERR_UNSUPPORTED  # dtype
     assert f(FAKE, bf16, 100, 7168, FAKE, FAKE, 10, 65, FAKE, FAKE, None, None) == DR_ERR_UNSUPPORTED  # k > 64
+
+
+def test_grouped_wgrad_rejects_bad_arguments(lib):
+    lib.dr_grouped_wgrad_workspace_size.restype = ctypes.c_size_t
+    lib.dr_grouped_wgrad_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                                                    ctypes.c_int64]
+    need = lib.dr_grouped_wgrad_workspace_size(4096, 4, 256, 512, 256)
+    assert need > 256
+    f = lib.dr_grouped_wgrad
+    f.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                  ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    ok = [FAKE, FAKE, 4096, 512, 256, FAKE, 4, 256, FAKE, FAKE, need, None]
+
+    def call(**kw):
+        a = list(ok)
+        names = ["X", "dY", "K", "M", "N", "off", "G", "split", "out", "ws", "ws_bytes", "s"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+    assert call(X=None) == DR_ERR_INVALID_ARGUMENT
+    assert call(K=0) == DR_ERR_INVALID_ARGUMENT
+    assert call(G=0) == DR_ERR_INVALID_ARGUMENT
+    assert call(G=70000) == DR_ERR_INVALID_ARGUMENT
+    assert call(split=0) == DR_ERR_INVALID_ARGUMENT
+    assert call(M=500) == DR_ERR_UNSUPPORTED          # not a multiple of 8
+    assert call(N=20) == DR_ERR_UNSUPPORTED
+    assert call(X=FAKE + 8) == DR_ERR_INVALID_ARGUMENT  # 16-byte alignment
+    assert call(ws_bytes=need - 1) == DR_ERR_WORKSPACE_TOO_SMALL
+    assert call(K=(1 << 31) - 100) == DR_ERR_UNSUPPORTED
