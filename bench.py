@@ -54,6 +54,12 @@ def parse():
                     help="time the step alone: no comparison legs (atomic, unfused, cold cache, extra entry points) "
                          "and no copy ceiling, so that a profiler's trace holds only the step's kernels")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target duration of the CPU oracle sample")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="time the MoE combine only; by default the line also carries a block per other "
+                         "configuration (sparse-attention dK index_add and its fused form, embedding-gradient "
+                         "index_add, split-K, grouped expert weight gradient)")
+    ap.add_argument("--other-cpu-seconds", type=float, default=4.0,
+                    help="target duration of each other configuration's CPU oracle sample")
     ap.add_argument("--json-out", default=None, help="also append the JSON line to this file")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after timing, run a plain fp32 copy kernel of this many MiB (read + write), so that "
@@ -256,7 +262,9 @@ def bench_moe(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only=F
 
 
 def cpu_baseline_moe(oracle, inp, seconds):
-    """The oracle (single-threaded C) timed on a bounded sample of tokens."""
+    """The oracle (C) timed on a bounded sample of tokens, on one thread and on the host's cores (token
+    ranges per thread; the bits must not change)."""
+    from bench_workloads import host_threads
     _, _, inv = oracle.sort_by_dest(inp.expert_ids.reshape(-1), inp.E)
     row_of = inv.reshape(inp.T, inp.k)
     elem = 2 if inp.rows_dtype == "bf16" else 4
@@ -269,11 +277,21 @@ def cpu_baseline_moe(oracle, inp, seconds):
     tokens = np.arange(count)
     log(f"cpu baseline: oracle combine on {count} tokens (~{count * dt:.1f} s)")
     t0 = time.perf_counter()
-    oracle.combine(inp.rows, row_of, inp.gates, tokens=tokens)
+    one = oracle.combine(inp.rows, row_of, inp.gates, tokens=tokens)
     el = time.perf_counter() - t0
-    return {"value": round(per_token * count / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {count} of {inp.T} tokens of the same workload (combine only), {el:.1f} s",
-            "seconds": round(el, 2)}
+    th = host_threads()
+    t0 = time.perf_counter()
+    many = oracle.combine(inp.rows, row_of, inp.gates, tokens=tokens, threads=th)
+    el_mt = time.perf_counter() - t0
+    same = bool(np.array_equal(one.view(np.uint32), many.view(np.uint32)))
+    if not same:
+        raise RuntimeError("the oracle's bits changed with its thread count")
+    return {"value": round(per_token * count / el_mt / 1e9, 4), "unit": "GB/s", "cores": th, "kind": "oracle",
+            "sample": f"first {count} of {inp.T} tokens of the same workload (combine only); {th} threads "
+                      f"{el_mt:.1f} s, 1 thread {el:.1f} s",
+            "seconds": round(el_mt, 2),
+            "single_thread": {"value": round(per_token * count / el / 1e9, 4), "cores": 1, "seconds": round(el, 2)},
+            "bits_identical_across_thread_counts": same}
 
 
 # ---------------------------------------------------------------------------
@@ -335,6 +353,18 @@ def main():
                                   not args.no_cpu_baseline, args.step_only)
     if not args.step_only:
         res["roofline"].update(copy_ceiling(torch, res["roofline"]["achieved"]))
+    others = {}
+    if name == "moe_combine" and not args.step_only and not args.no_other_configs:
+        import bench_workloads
+        for other in ("sparse_attn_dk", "embedding_grad", "splitk_mhc", "grouped_wgrad"):
+            r = bench_workloads.run(torch, dr, other, args.steps, args.warmup, args.other_cpu_seconds,
+                                    not args.no_cpu_baseline, False)
+            if "cpu_baseline" in r:
+                r["cpu_baseline"].update(host_description())
+            r["value_gbs" if r["roofline"]["unit"] == "GB/s" else "value"] = round(r.pop("value"), 2)
+            r["ms_per_step"] = round(r["ms_per_step"], 4)
+            others[other] = r
+            torch.cuda.empty_cache()
     if "cpu_baseline" in res:
         res["cpu_baseline"].update(host_description())
     if args.calibrate_copy_mib > 0:
@@ -350,6 +380,8 @@ def main():
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
             "data": "synthetic (seeded numpy PCG64 draws of the configuration's shapes and distributions)"}
     line.update(res)
+    if others:
+        line["other_configs"] = others
     text = json.dumps(line)
     print(text, flush=True)
     if args.json_out:

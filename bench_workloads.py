@@ -8,6 +8,11 @@ sparse_attn_dk / embedding_grad: a step is dr_index_add_fingerprinted (stable
   same step with dr_index_add and a full dr_fingerprint of the destination, and
   the reused-plan time (sort done once, as when the indices are known a step
   early), are reported beside it.
+grouped_wgrad: a step is dr_grouped_wgrad (plan, tile kernel, chunk merge): the
+  weight gradient of 8 experts (the hottest of the MoE routing, one GPU's share
+  at expert parallelism 32: 86,165 token rows), M = 7168, N = 2048, private
+  slots of 2048 tokens merged in slot order.  MFMA-bound: reported in TFLOP/s
+  against the bf16 dense peak.
 splitk_mhc: a step is dr_splitk_gemm_tn (64 private fp32 partials by bf16
   MFMA) and dr_splitk_reduce_fingerprinted (the reduce in split-id order,
   hashing dW as it stores it).
@@ -127,6 +132,8 @@ def cold_roofline(alg_bytes: int, ms: float) -> dict:
 
 
 def run(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only=False):
+    if name == "grouped_wgrad":
+        return _grouped_wgrad(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only)
     if name in ("sparse_attn_dk", "embedding_grad"):
         return _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only)
     if name == "decode_attention":
@@ -354,8 +361,15 @@ def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only)
         for _ in range(warmup):
             dr.dr_index_add_atomic(out, src, index)
         ms_atomic = _timed(torch, steps, lambda: dr.dr_index_add_atomic(out, src, index))
+        # the pages' default path itself: torch's index_add_ (atomic adds), on fp32 rows converted beforehand
+        # (index_add_ needs the destination's dtype), so it reads twice the bytes of the bf16 rows
+        src32 = src.float()
+        for _ in range(warmup):
+            out.index_add_(0, index, src32)
+        ms_torch = _timed(torch, steps, lambda: out.index_add_(0, index, src32))
+        del src32
 
-        fused = _fused_dk(torch, dr, steps, warmup) if name == "sparse_attn_dk" else None
+        fused = _fused_dk(torch, dr, steps, warmup, want_cpu, cpu_seconds) if name == "sparse_attn_dk" else None
         ia_cold = cold_ms(torch, lambda: dr.dr_index_add_fingerprinted(out, src, index, fp, ws=ws))
         extras = {
             "cold_cache_ms_per_step": round(ms_cold, 4),
@@ -363,8 +377,11 @@ def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only)
             "step_with_full_fingerprint_ms": round(ms_full, 4),
             "reused_plan_ms": round(ms_plan, 4), "sort_only_ms": round(ms_sort, 4),
             "overhead_vs_atomic": {"deterministic_ms": round(ms_plain, 4), "atomic_ms": round(ms_atomic, 4),
-                                   "overhead": round(ms_plain / ms_atomic - 1, 4),
-                                   "overhead_reused_plan": round(ms_plan / ms_atomic - 1, 4)},
+                                   "torch_index_add_fp32_ms": round(ms_torch, 4),
+                                   "overhead": round(ms_plain / min(ms_atomic, ms_torch) - 1, 4),
+                                   "overhead_reused_plan": round(ms_plan / min(ms_atomic, ms_torch) - 1, 4),
+                                   "note": "overhead against the faster of dr_index_add_atomic (bf16 rows, 16-byte "
+                                           "loads) and torch index_add_ (fp32 rows)"},
         }
         if fused:
             extras["fused_dk"] = fused
@@ -415,9 +432,10 @@ def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only)
     return res
 
 
-def _fused_dk(torch, dr, steps, warmup):
+def _fused_dk(torch, dr, steps, warmup, want_cpu=False, cpu_seconds=4.0):
     """dr_sparse_attn_dk on the same key selection: the contributions
     fl32(dS * Q) are formed in the reduce instead of read as 1.07 GB of rows."""
+    import oracle
     import workloads
     _log("sparse_attn_dk: fused key gradient (query rows and score gradients)")
     inp = workloads.sparse_attn_dk_inputs(workloads.CONFIGS["sparse_attn_dk"]["seed"])
@@ -435,15 +453,66 @@ def _fused_dk(torch, dr, steps, warmup):
     for _ in range(warmup):
         dr.dr_sparse_attn_dk(dK, Q, dS, idx, perm=perm, seg_offsets=seg, ws=ws)
     ms_plan = _timed(torch, steps, lambda: dr.dr_sparse_attn_dk(dK, Q, dS, idx, perm=perm, seg_offsets=seg, ws=ws))
-    touched = int((np.bincount(inp.key_idx.reshape(-1), minlength=inp.num_keys) > 0).sum())
+    # the ordered reduction alone, timed by the events the library records around it
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for b_, e_ in pairs:
+        dr.dr_set_phase_events(b_, e_)
+        dr.dr_sparse_attn_dk(dK, Q, dS, idx, ws=ws)
+    dr.dr_set_phase_events()
+    torch.cuda.synchronize()
+    red_ms = float(np.mean([b_.elapsed_time(e_) for b_, e_ in pairs]))
+    counts = np.bincount(inp.key_idx.reshape(-1), minlength=inp.num_keys)
+    touched = int((counts > 0).sum())
     n = nq * topk
     alg = nq * inp.H * 2 + n * 4 + n * 4 + 2 * touched * inp.H * 4  # Q, dS, key ids, dK read-modify-write
-    return {"ms": round(ms, 4), "reused_plan_ms": round(ms_plan, 4), "algorithmic_bytes": alg,
-            "note": "contributions formed from Q [8192,128] bf16 and dS [8192,512] fp32; the same key selection"}
+    res = {"ms": round(ms, 4), "reused_plan_ms": round(ms_plan, 4), "algorithmic_bytes": alg,
+           "roofline": {"bound": "hbm", "kernel": "segreduce_kernel + tilecombine_kernel (contributions formed "
+                                                  "from Q and dS)",
+                        "achieved": round(alg / (red_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(alg / (red_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "avg_launch_ms": round(red_ms, 4),
+                        "traffic": measured_traffic("segreduce+tilecombine", "sparse_attn_dk_fused",
+                                                    source_digest("segreduce.hip", "internal.h", "device.h")),
+                        "whole_call": {"achieved": round(alg / (ms * 1e-3) / 1e9, 1),
+                                       "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                       "avg_launch_ms": round(ms, 4)}},
+           "note": "contributions formed from Q [8192,128] bf16 and dS [8192,512] fp32; the same key selection"}
+    if want_cpu:
+        # the oracle on the first queries of the same selection, one thread and the host's cores
+        q = max(1, min(nq, int(nq * min(1.0, cpu_seconds / 8.0))))
+        t0 = time.perf_counter()
+        one = oracle.sparse_attn_dk(inp.dK0, inp.Q[:q], inp.dS[:q], inp.key_idx[:q])
+        el = time.perf_counter() - t0
+        th = host_threads()
+        t0 = time.perf_counter()
+        many = oracle.sparse_attn_dk(inp.dK0, inp.Q[:q], inp.dS[:q], inp.key_idx[:q], threads=th)
+        el_mt = time.perf_counter() - t0
+        same = bool(np.array_equal(one.view(np.uint32), many.view(np.uint32)))
+        if not same:
+            raise RuntimeError("the oracle's bits changed with its thread count")
+        per_q = inp.H * 2 + topk * 8
+        res["cpu_baseline"] = {"value": round(per_q * q / el_mt / 1e9, 4), "unit": "GB/s", "cores": th,
+                               "kind": "oracle",
+                               "sample": f"first {q} of {nq} queries; {th} threads {el_mt:.1f} s, 1 thread {el:.1f} s",
+                               "seconds": round(el_mt, 2),
+                               "single_thread": {"value": round(per_q * q / el / 1e9, 4), "cores": 1,
+                                                 "seconds": round(el, 2)},
+                               "bits_identical_across_thread_counts": same}
+    return res
+
+
+def host_threads() -> int:
+    """Host threads for the oracle's multi-threaded timing: the CPU share of one GPU (16) at most."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 def _cpu_index_add(oracle, inp, seconds):
-    """The oracle on the first contributions of the same workload (a prefix of the batch)."""
+    """The oracle on the first contributions of the same workload (a prefix of the batch), on one thread and
+    on the host's cores (destination ranges per thread; the bits must not change)."""
     n, H = inp.n, inp.H
     per_row = H * 2 + 4
     m = min(n, 4096)
@@ -454,10 +523,117 @@ def _cpu_index_add(oracle, inp, seconds):
     m2 = int(min(n, m * max(1.0, seconds / dt)))
     _log(f"cpu baseline: oracle index_add on the first {m2} of {n} contributions")
     t0 = time.perf_counter()
-    oracle.index_add(inp.out0, inp.src[:m2], inp.index[:m2])
+    one = oracle.index_add(inp.out0, inp.src[:m2], inp.index[:m2])
     el = time.perf_counter() - t0
-    return {"value": round(per_row * m2 / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {m2} of {n} contributions of the same workload, {el:.1f} s", "seconds": round(el, 2)}
+    th = host_threads()
+    t0 = time.perf_counter()
+    many = oracle.index_add(inp.out0, inp.src[:m2], inp.index[:m2], threads=th)
+    el_mt = time.perf_counter() - t0
+    same = bool(np.array_equal(one.view(np.uint32), many.view(np.uint32)))
+    if not same:
+        raise RuntimeError("the oracle's bits changed with its thread count")
+    return {"value": round(per_row * m2 / el_mt / 1e9, 4), "unit": "GB/s", "cores": th, "kind": "oracle",
+            "sample": f"first {m2} of {n} contributions of the same workload; {th} threads {el_mt:.1f} s, "
+                      f"1 thread {el:.1f} s",
+            "seconds": round(el_mt, 2),
+            "single_thread": {"value": round(per_row * m2 / el / 1e9, 4), "cores": 1, "seconds": round(el, 2)},
+            "bits_identical_across_thread_counts": same}
+
+
+def _grouped_wgrad(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only):
+    import oracle
+    import workloads
+    _log(f"{name}: generating inputs")
+    inp = workloads.grouped_wgrad_inputs(1002)
+    K, M, N, S = inp.K, inp.M, inp.N, inp.split_tokens
+    G = inp.group_offsets.size - 1
+    X = torch.from_numpy(inp.X.view(np.int16)).view(torch.bfloat16).cuda()
+    dY = torch.from_numpy(inp.dY.view(np.int16)).view(torch.bfloat16).cuda()
+    off = torch.from_numpy(inp.group_offsets).cuda()
+    out = torch.empty(G, M, N, dtype=torch.float32, device="cuda")
+    ws = torch.empty(dr.dr_grouped_wgrad_workspace_size(K, G, S, M, N), dtype=torch.uint8, device="cuda")
+    flops = 2 * K * M * N
+    hbm_bytes = K * M * 2 + K * N * 2 + G * M * N * 4  # X and dY read once, dW written once
+
+    def step():
+        dr.dr_grouped_wgrad(X, dY, off, S, out=out, ws=ws)
+
+    for _ in range(warmup):
+        step()
+    dr.dr_workspace_status(ws)
+    h0 = dr.fingerprint_value(out)
+    _log(f"{name}: timing {steps} steps")
+    eager_ms = _timed(torch, steps, step)
+    ms_step = graph_ms(torch, step, steps, warmup)
+    if dr.fingerprint_value(out) != h0:
+        raise RuntimeError("replays of the grouped weight gradient changed its output")
+    tflops = flops / (eager_ms * 1e-3) / 1e12
+    extras = {}
+    if not step_only:
+        # the same result through materialised slot partials: the thin-N split-K tiles, then the reduce
+        Pg, so, wsg = dr.dr_grouped_splitk_gemm_tn(X, dY, off, S)
+
+        def materialised():
+            dr.dr_grouped_splitk_gemm_tn(X, dY, off, S, partials=Pg, slot_offsets=so, ws=wsg)
+            return dr.dr_grouped_splitk_reduce(Pg, so, wsg)
+        ref = materialised()
+        if dr.fingerprint_value(ref) != h0:
+            raise RuntimeError("the register-slot and materialised-partial paths differ")
+        ms_mat = _timed(torch, 2, materialised)
+        del Pg, ref
+        torch.cuda.empty_cache()
+        # a library GEMM per expert (hipBLASLt through torch, bf16 out, no slots): context for the MFMA rate
+        Xt = [X[int(inp.group_offsets[g]):int(inp.group_offsets[g + 1])].t().contiguous() for g in range(G)]
+        dYg = [dY[int(inp.group_offsets[g]):int(inp.group_offsets[g + 1])] for g in range(G)]
+
+        def library():
+            for g in range(G):
+                torch.matmul(Xt[g], dYg[g])
+        for _ in range(warmup):
+            library()
+        ms_lib = _timed(torch, steps, library)
+        del Xt, dYg
+        extras = {
+            "materialised_partials_ms": round(ms_mat, 4),
+            "library_gemm_per_expert_ms": round(ms_lib, 4),
+            "library_gemm_tflops": round(flops / (ms_lib * 1e-3) / 1e12, 1),
+            "library_note": "torch.matmul of each expert's pre-transposed X rows with dY (hipBLASLt, bf16 output, "
+                            "one GEMM per expert, no private slots); the transposes are outside the timing",
+        }
+    res = {
+        "ms_per_step": ms_step,
+        "value": tflops,
+        "timing": "step replayed from a HIP graph; the roofline uses the eager per-call time",
+        "eager_ms_per_step": round(eager_ms, 4),
+        "config": {"workload": f"{name}: dW[g] = X_g^T dY_g for the {G} hottest experts of the MoE routing "
+                               f"(token counts {np.diff(inp.group_offsets).tolist()}), M {M}, N {N}, "
+                               f"private slots of {S} tokens merged in slot order",
+                   "K": K, "M": M, "N": N, "groups": G, "split_tokens": S, "flops": flops},
+        "roofline": {"bound": "mfma", "kernel": "wgrad_kernel (with its plan and merge launches)",
+                     "achieved": round(tflops, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic("wgrad_kernel", name, source_digest("wgrad.hip", "device.h")),
+                     "algorithmic_flops_per_launch": flops, "hbm_algorithmic_bytes": hbm_bytes,
+                     "avg_launch_ms": round(eager_ms, 4)},
+        **extras,
+    }
+    if want_cpu:
+        # the oracle's fp64 reference of the first expert's product on a sample of X's columns
+        a, b = int(inp.group_offsets[0]), int(inp.group_offsets[1])
+        cols = 8
+        t0 = time.perf_counter()
+        oracle.splitk_reference(np.ascontiguousarray(inp.X[a:b, :cols]), inp.dY[a:b])
+        dt = max(time.perf_counter() - t0, 1e-6)
+        cols = int(min(M, cols * max(1.0, cpu_seconds / dt)))
+        Xs = np.ascontiguousarray(inp.X[a:b, :cols])
+        t0 = time.perf_counter()
+        oracle.splitk_reference(Xs, inp.dY[a:b])
+        el = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": round(2 * (b - a) * cols * N / el / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+                               "kind": "oracle",
+                               "sample": f"fp64 reference of expert 0's product on {cols} of {M} columns, {el:.1f} s",
+                               "seconds": round(el, 2)}
+    return res
 
 
 def _splitk(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only):
@@ -561,6 +737,8 @@ def _splitk(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only):
                      "traffic": measured_traffic("splitk_gemm_kernel", name, source_digest("splitk.hip", "device.h")),
                      "algorithmic_bytes_per_launch": gemm_bytes, "avg_launch_ms": round(g_ms, 4),
                      **extra_roofline,
+                     "headline": "cold-cache fraction: X (235 MB) fits the 256 MB Infinity Cache, so back-to-back "
+                                 "launches are partly served by it",
                      "mfma_tflops": round(flops / (g_ms * 1e-3) / 1e12, 2),
                      "mfma_frac_of_bf16_peak": round(flops / (g_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS, 5)},
         "phases_ms": {k: round(v, 4) for k, v in ph.items()},

@@ -266,6 +266,33 @@ def splitk_inputs(seed: int, K: int = 16384, M: int = 7168, N: int = 24, splits:
 
 
 # --------------------------------------------------------------------------
+# Grouped expert weight gradient
+# --------------------------------------------------------------------------
+@dataclass
+class GroupedWgradInputs:
+    K: int
+    M: int
+    N: int
+    split_tokens: int
+    group_offsets: np.ndarray  # int32 [G + 1]
+    X: np.ndarray              # uint16 bf16 bits [K, M]: the experts' token rows, expert-major
+    dY: np.ndarray             # uint16 bf16 bits [K, N]: the gradient of the expert layer's output
+
+
+def grouped_wgrad_inputs(seed: int, experts: int = 8, M: int = 7168, N: int = 2048, split_tokens: int = 2048,
+                         T: int = 16384, E: int = 256, k: int = 8, zipf_bias_s: float = 1.2) -> GroupedWgradInputs:
+    """The hottest `experts` experts of the MoE routing (one GPU's share at expert parallelism E / experts),
+    with their token counts from that routing; X and dY bf16 N(0,1)."""
+    expert_ids, _ = moe_routing(seed, T, E, k, zipf_bias_s)
+    counts = np.bincount(expert_ids.reshape(-1), minlength=E)[:experts]
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    K = int(off[-1])
+    X = normal_bf16(seed, 17, K * M).reshape(K, M)
+    dY = normal_bf16(seed, 18, K * N).reshape(K, N)
+    return GroupedWgradInputs(K, M, N, split_tokens, off, X, dY)
+
+
+# --------------------------------------------------------------------------
 # The five named configurations (full sizes); seed = 1000 + configuration number
 # --------------------------------------------------------------------------
 CONFIGS = {
