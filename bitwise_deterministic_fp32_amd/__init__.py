@@ -154,16 +154,17 @@ def _dev(t: torch.Tensor, name: str, dtypes=None) -> torch.Tensor:
 
 class _LaunchParams(ctypes.Structure):
     _fields_ = [("grid_blocks", ctypes.c_int32), ("tile_chunks_log2", ctypes.c_int32),
-                ("sort_tile_log2", ctypes.c_int32), ("chunks_in_flight", ctypes.c_int32)]
+                ("sort_tile_log2", ctypes.c_int32), ("chunks_in_flight", ctypes.c_int32),
+                ("splitk_stream", ctypes.c_int32)]
 
 
 def dr_set_launch_params(grid_blocks: int = 0, tile_chunks_log2: int = 0, sort_tile_log2: int = 0,
-                         chunks_in_flight: int = 0, reset: bool = False) -> None:
+                         chunks_in_flight: int = 0, splitk_stream: int = 0, reset: bool = False) -> None:
     """Thread-local launch overrides (tests of launch invariance); reset=True restores defaults."""
     if reset:
         _check(lib.dr_set_launch_params(None), "dr_set_launch_params")
         return
-    p = _LaunchParams(grid_blocks, tile_chunks_log2, sort_tile_log2, chunks_in_flight)
+    p = _LaunchParams(grid_blocks, tile_chunks_log2, sort_tile_log2, chunks_in_flight, splitk_stream)
     _check(lib.dr_set_launch_params(ctypes.byref(p)), "dr_set_launch_params")
 
 

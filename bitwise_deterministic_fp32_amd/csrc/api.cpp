@@ -15,7 +15,7 @@
 namespace {
 
 thread_local std::string g_err;
-thread_local dr_launch_params g_params = {0, 0, 0, 0};
+thread_local dr_launch_params g_params = {0, 0, 0, 0, 0};
 thread_local hipEvent_t g_reduce_begin = nullptr, g_reduce_end = nullptr;  // dr_set_phase_events
 
 dr_status fail(dr_status s, const char* fmt, ...) {
@@ -303,6 +303,7 @@ Launch launch_config() {
     l.tile_chunks_log2 = g_params.tile_chunks_log2 ? g_params.tile_chunks_log2 : kDefaultTileChunksLog2;
     l.sort_tile_log2 = g_params.sort_tile_log2;
     l.chunks_in_flight = g_params.chunks_in_flight ? g_params.chunks_in_flight : 1;
+    l.splitk_stream = g_params.splitk_stream != 2;
     return l;
 }
 
@@ -342,7 +343,7 @@ const char* dr_status_string(dr_status s) {
 
 const char* dr_last_error(void) { return g_err.c_str(); }
 
-int32_t dr_version(void) { return 100; }
+int32_t dr_version(void) { return 101; }
 
 dr_status dr_set_phase_events(hipEvent_t reduce_begin, hipEvent_t reduce_end) {
     if ((reduce_begin == nullptr) != (reduce_end == nullptr))
@@ -354,7 +355,7 @@ dr_status dr_set_phase_events(hipEvent_t reduce_begin, hipEvent_t reduce_end) {
 
 dr_status dr_set_launch_params(const dr_launch_params* p) {
     if (!p) {
-        g_params = dr_launch_params{0, 0, 0, 0};
+        g_params = dr_launch_params{0, 0, 0, 0, 0};
         return ok();
     }
     if (p->grid_blocks < 0 || p->grid_blocks > 65536)
@@ -369,6 +370,8 @@ dr_status dr_set_launch_params(const dr_launch_params* p) {
                     dr::kMaxSortTileLog2);
     if (p->chunks_in_flight != 0 && p->chunks_in_flight != 1 && p->chunks_in_flight != 2)
         return fail(DR_ERR_INVALID_ARGUMENT, "chunks_in_flight must be 0, 1 or 2");
+    if (p->splitk_stream < 0 || p->splitk_stream > 2)
+        return fail(DR_ERR_INVALID_ARGUMENT, "splitk_stream must be 0, 1 or 2");
     g_params = *p;
     return ok();
 }

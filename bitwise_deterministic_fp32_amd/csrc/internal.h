@@ -47,6 +47,7 @@ struct Launch {
     int tile_chunks_log2;  // resolved value
     int sort_tile_log2;    // 0 = default_sort_tile_log2(n)
     int chunks_in_flight;  // resolved value (1 or 2)
+    bool splitk_stream;    // thin-N split-K partials may use the streaming kernel
     int sort_tile(int64_t n) const { return sort_tile_log2 ? sort_tile_log2 : default_sort_tile_log2(n); }
 };
 Launch launch_config();

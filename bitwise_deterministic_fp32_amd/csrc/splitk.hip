@@ -15,6 +15,10 @@
 //     (split, m, n): not on the grid, the M/N tiling or other columns.  The HBM
 //     stream is X (read once) plus the partials (written once); the MFMA work
 //     is small beside it.
+//   splitk_stream: the same partials for thin N (at most 32 columns, a
+//     multiple of 8; the mHC shape), one persistent workgroup of eight
+//     wavefronts per CU, 256-column M tiles in 64-token stages, loads two
+//     stages ahead through registers; the default for those shapes (same bits).
 //   splitk_reduce: out[e] = T(P_0[e], ..., P_{S-1}[e]); chunks of 8 splits left
 //     to right, then the pairwise tree: for 9..512 splits a lane per chunk and
 //     the tree across lanes (shuffles), else one thread per 4 consecutive
@@ -22,6 +26,7 @@
 // The atomic baseline runs the same tile code and adds each split's tile into
 // out with hardware fp32 atomics.
 #include "internal.h"
+#include "lds_tile.h"
 
 namespace dr {
 namespace {
@@ -506,6 +511,207 @@ __global__ __launch_bounds__(kSlotThreads) void grouped_slots_kernel(const int32
     }
 }
 
+// ---------------------------------------------------------------------------
+// The streaming form of the split-K partials, for thin N (at most 32 columns,
+// a multiple of 8) and M a multiple of 8.  Items are (split, 256-column M
+// tile), M tile fastest, dealt round-robin to the persistent workgroups (one
+// per CU), so the workgroups running at one time read neighbouring pieces of
+// the same token rows.  A stage is 64 tokens of X and dY.  Eight wavefronts,
+// two per SIMD, each own 32 columns of the tile: each thread loads its 16-byte
+// pieces into registers two stages ahead (buffer loads whose range check
+// supplies the zeros past the stage's last token), writes them to one of two
+// LDS buffers, and the MFMA operands come back with the transposing LDS read;
+// one workgroup barrier per stage.  The accumulation is the same MFMA sequence
+// as splitk_gemm_kernel (16-token steps from the split's first token, rows
+// past it zero), so the partials have the same bits; the tile leaves through
+// LDS as contiguous 16-byte stores (a split's 256 x N tile is one contiguous
+// block of P_s).
+constexpr int SM_TM = 256;       // M columns per item
+constexpr int SM_TN = 32;        // N columns (one MFMA block, zero-padded past N)
+constexpr int SM_TK = 64;        // tokens per stage
+constexpr int SM_THREADS = 512;  // 8 wavefronts of 32 M columns
+constexpr int SM_XLOADS = SM_TM * SM_TK * 2 / 16 / SM_THREADS;  // 4 pieces of X per thread and stage
+constexpr int SM_YPIECES = SM_TN * SM_TK * 2 / 16;               // 256 pieces of dY: threads 0..255
+constexpr uint32_t kBufferFlags = 0x00020000u;  // raw buffer (gfx9 resource word 3)
+constexpr int kNonTemporal = 2;                 // buffer load cache policy: streaming
+constexpr uint32_t kOutOfRange = 0x80000000u;   // a byte offset past every stage's range
+
+struct SmCursor {
+    uint32_t item;
+    int32_t stage;
+    int32_t valid;
+};
+
+struct SmStage {
+    int64_t t;      // first token
+    int32_t rows;   // tokens of the stage
+    int32_t last;   // last stage of the split
+    int64_t m0;
+    int32_t s;      // split
+};
+
+__device__ __forceinline__ SmStage sm_stage(const SmCursor& u, int64_t K, int64_t kc, uint32_t mtiles) {
+    SmStage g;
+    g.s = (int32_t)(u.item / mtiles);
+    g.m0 = (int64_t)(u.item % mtiles) * SM_TM;
+    const int64_t t_begin = (int64_t)g.s * kc, t_end = min(K, t_begin + kc);
+    g.t = t_begin + (int64_t)u.stage * SM_TK;
+    g.rows = (int32_t)min((int64_t)SM_TK, t_end - g.t);
+    g.last = g.t + SM_TK >= t_end;
+    return g;
+}
+
+// The stage after u: the next stage of the split, else the worker's next item.
+__device__ __forceinline__ SmCursor sm_next(const SmCursor& u, int32_t last, uint32_t P, uint32_t items) {
+    SmCursor b = last ? SmCursor{u.item + P, 0, 1} : SmCursor{u.item, u.stage + 1, 1};
+    b.valid = u.valid && b.item < items;
+    return b;
+}
+
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+// One stage's pieces of this thread, in registers between their load and their LDS write.
+struct SmRegs {
+    u32x4v x[SM_XLOADS];
+    u32x4v y;
+};
+
+__global__ __launch_bounds__(SM_THREADS, 1) void splitk_stream_kernel(const uint16_t* __restrict__ X,
+                                                                      const uint16_t* __restrict__ dY, int64_t K,
+                                                                      int64_t M, int64_t N, int64_t kc,
+                                                                      uint32_t items, uint32_t mtiles,
+                                                                      float* __restrict__ out) {
+    __shared__ __attribute__((aligned(1024))) uint16_t xs[2][SM_TM * SM_TK];
+    __shared__ __attribute__((aligned(1024))) uint16_t ys[2][SM_TN * SM_TK];
+    __shared__ __attribute__((aligned(16))) float ot[SM_TM * SM_TN];  // the finished tile, rows of 32
+    const uint32_t P = gridDim.x;
+    if (blockIdx.x >= items) return;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int i = lane & 31, h = lane >> 5;
+    const bool writes_y = tid < SM_YPIECES;  // wavefronts 0..3 write the dY pieces to LDS
+
+    // Piece k of X: position 64 (4 w + k) + lane of the stage, token row p / 32,
+    // 16-byte chunk p % 32; its byte offset from the stage's first token row
+    // at column m0, and its swizzled LDS element offset.
+    int x_row_off[SM_XLOADS], x_col[SM_XLOADS], x_lds[SM_XLOADS];
+#pragma unroll
+    for (int k = 0; k < SM_XLOADS; ++k) {
+        const int pos = 64 * (SM_XLOADS * wv + k) + lane, r = pos / 32, cc = pos % 32;
+        x_row_off[k] = (int)(r * M * 2 + 16 * cc);
+        x_col[k] = 8 * cc;
+        x_lds[k] = lds_at<SM_TM>(r, 8 * cc);
+    }
+    // Piece tid % 256 of dY: token row (tid % 256) / 4, chunk tid % 4; columns
+    // at or past N read zeros.
+    const int y_r = (tid & 255) / 4, y_c = 8 * (tid & 3);
+    const uint32_t y_off = y_c < N ? (uint32_t)(y_r * N * 2 + 2 * y_c) : kOutOfRange;
+    const int y_lds = lds_at<SM_TN>(y_r, y_c);
+
+    const int xoff = operand_offset<SM_TM>(32 * wv);
+    const int yoff = operand_offset<SM_TN>(0);
+
+    SmCursor cu{blockIdx.x, 0, 1};  // the stage computed
+    SmCursor iu = cu;               // the next stage to load
+    // Every call issues the same loads, so the compiler's waits on the
+    // registers of a stage count the same instructions on every path; past the
+    // worker's last stage every piece is out of range and reads zeros.
+    auto issue = [&](SmRegs& rg) {
+        const SmStage g = sm_stage(iu, K, kc, mtiles);
+        const int32_t rows = iu.valid ? max(g.rows, 0) : 0;
+        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(X + (iu.valid ? g.t * M + g.m0 : 0)), 0, (int)(rows * M * 2), kBufferFlags);
+#pragma unroll
+        for (int k = 0; k < SM_XLOADS; ++k) {
+            const uint32_t off = g.m0 + x_col[k] < M ? (uint32_t)x_row_off[k] : kOutOfRange;
+            rg.x[k] = __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(xr, (int)off, 0, kNonTemporal));
+        }
+        // every thread loads a dY piece (threads 256.. repeat those of 0..255,
+        // from L2) so that every wavefront issues the same loads
+        const __amdgpu_buffer_rsrc_t yr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(dY + (iu.valid ? g.t * N : 0)), 0, (int)(rows * N * 2), kBufferFlags);
+        rg.y = __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(yr, (int)y_off, 0, 0));
+        iu = sm_next(iu, g.last, P, items);
+    };
+    SmRegs r0, r1;
+    issue(r0);
+    issue(r1);
+    f32x16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+    int b = 0;  // LDS buffer of the stage computed
+
+    // A finished tile leaves one stage late, after that stage's loads are
+    // issued: the vector memory counter retires in issue order, so a load
+    // issued after the stores is not known complete before the stores are, and
+    // the stage after the stores is waited for only two stages on.
+    float* pend_dst = out;
+    int pend_pieces = 0;  // 16-byte pieces of the tile waiting in ot (wave-uniform)
+    const int q4 = (int)(N / 4);
+    float* mine = ot + 32 * wv * SM_TN;  // this wavefront's 32 rows of the tile
+    auto flush = [&]() {
+        for (int p = lane; p < pend_pieces; p += 64) {
+            const int r = p / q4, c = (p % q4) * 4;
+            store16_stream(pend_dst + (int64_t)r * N + c, *reinterpret_cast<const u32x4*>(mine + r * SM_TN + c));
+        }
+        pend_pieces = 0;
+    };
+
+    // One stage: its registers go to LDS buffer b, the same registers take the
+    // loads of the stage two ahead, and the stage is computed once every
+    // wavefront's writes are in.
+    auto step = [&](SmRegs& rg) {
+        // Buffer b was last read two stages ago; every wavefront has passed the
+        // barrier of the stage since, so it is free.
+#pragma unroll
+        for (int k = 0; k < SM_XLOADS; ++k) *reinterpret_cast<u32x4v*>(xs[b] + x_lds[k]) = rg.x[k];
+        if (writes_y) *reinterpret_cast<u32x4v*>(ys[b] + y_lds) = rg.y;
+        issue(rg);
+        flush();
+        lds_barrier();
+        const SmStage g = sm_stage(cu, K, kc, mtiles);
+        const int ksteps = (g.rows + 15) >> 4;
+        for (int ks = 0; ks < ksteps; ++ks) {
+            const bf16x8 a = tr_read8(xs[b], xoff + 16 * ks * SM_TM, 4 * SM_TM);
+            const bf16x8 bb = tr_read8(ys[b], yoff + 16 * ks * SM_TN, 4 * SM_TN);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bb, acc, 0, 0, 0);
+        }
+        if (g.last) {
+            // Each wavefront writes its rows of the tile to its own part of ot
+            // and stores them from there: lane (i, h) holds column i and rows
+            // 8 (v / 4) + 4 h + v % 4, and the rows leave as 16-byte pieces (a
+            // wavefront's rows are contiguous in P_s).  Only this wavefront
+            // touches these rows, and a wavefront's LDS accesses are done in
+            // order (the previous tile's stores read ot before these writes),
+            // so no workgroup barrier is needed.
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                mine[(8 * (v / 4) + 4 * h + (v % 4)) * SM_TN + i] = acc[v];
+                acc[v] = 0.f;
+            }
+            __builtin_amdgcn_wave_barrier();
+            const int64_t m_first = g.m0 + 32 * wv;
+            const int rows_out = (int)max((int64_t)0, min(M - m_first, (int64_t)32));
+            pend_dst = out + (int64_t)g.s * M * N + m_first * N;
+            pend_pieces = rows_out * q4;
+        }
+        cu = sm_next(cu, g.last, P, items);
+        b ^= 1;
+    };
+    // The worker's stage count, so that the loop below has no exit between
+    // its two steps (the compiler's waits then see one order of loads).
+    uint32_t stages = 0;
+    for (uint32_t it = blockIdx.x; it < items; it += P) {
+        const int64_t t_begin = (int64_t)(it / mtiles) * kc, n = min(K, t_begin + kc) - t_begin;
+        stages += n > 0 ? (uint32_t)((n + SM_TK - 1) / SM_TK) : 1u;
+    }
+    for (uint32_t j = 0; j + 2 <= stages; j += 2) {
+        step(r0);
+        step(r1);
+    }
+    if (stages & 1) step(r0);
+    flush();
+}
+
 }  // namespace
 
 hipError_t launch_splitk_gemm(const uint16_t* X, const uint16_t* dY, int64_t K, int64_t M, int64_t N,
@@ -514,6 +720,18 @@ hipError_t launch_splitk_gemm(const uint16_t* X, const uint16_t* dY, int64_t K, 
     const int64_t mtiles = (M + BM - 1) / BM, ntiles = (N + BN - 1) / BN;
     const int64_t items = mtiles * ntiles * splits;
     const Launch lc = launch_config();
+    // The stream kernel's buffer ranges are 32-bit byte counts of up to 64 token rows.
+    if (!atomic && lc.splitk_stream && N <= SM_TN && N % 8 == 0 && M % 8 == 0 && M <= ((int64_t)1 << 23) &&
+        (reinterpret_cast<uintptr_t>(X) & 15) == 0 && (reinterpret_cast<uintptr_t>(dY) & 15) == 0 &&
+        (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+        const int64_t sm_mtiles = (M + SM_TM - 1) / SM_TM;
+        const int64_t sm_items = sm_mtiles * splits;
+        int64_t grid = lc.grid_blocks > 0 ? lc.grid_blocks : (int64_t)device_cu_count();
+        if (grid > sm_items) grid = sm_items;
+        hipLaunchKernelGGL(splitk_stream_kernel, dim3((unsigned)grid), dim3(SM_THREADS), 0, s, X, dY, K, M, N, kc,
+                           (uint32_t)sm_items, (uint32_t)sm_mtiles, out);
+        return hipGetLastError();
+    }
     // three workgroups fit in a CU's LDS; each takes a contiguous range of items
     int64_t grid = lc.grid_blocks > 0 ? lc.grid_blocks : (int64_t)device_cu_count() * 3;
     if (grid > items) grid = items;

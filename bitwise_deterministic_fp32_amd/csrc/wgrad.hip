@@ -31,6 +31,7 @@
 // The 16-byte chunks of a row are XOR-swizzled by the row's low two bits, so
 // the four rows a transposing read touches fall in different banks.
 #include "internal.h"
+#include "lds_tile.h"
 
 namespace dr {
 namespace {
@@ -43,13 +44,6 @@ constexpr int TN = 128;          // output columns (N) per workgroup
 constexpr int TK = 64;           // tokens per stage
 constexpr int kThreads = 256;    // 4 wavefronts, each 64 (M) x 128 (N)
 constexpr int kChunk = 8;        // slots summed left to right before the pairwise tree
-
-// LDS element offset of (row r, column c) in a stage tile of `cols` columns:
-// the 16-byte chunk c / 8 of row r sits at position (c / 8) ^ 4 (r & 3).
-template <int COLS>
-__device__ __forceinline__ int lds_at(int r, int c) {
-    return r * COLS + ((((c >> 3) ^ ((r & 3) << 2))) << 3) + (c & 7);
-}
 
 struct Plan {
     const int32_t* cum_items;   // [G + 1] work items before each group
@@ -126,55 +120,10 @@ __device__ __forceinline__ Stage stage_of(const Item& w, const Unit& u, int32_t 
     return s;
 }
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// 16 zero bytes: the source of every direct load of a token row past the
-// stage or a column past M or N, so those LDS entries are zero and the MFMAs
-// need no masking (a read-only constant, not scratch).
-__device__ __align__(16) const uint32_t kZero16[4] = {0u, 0u, 0u, 0u};
 
 constexpr int kXLoads = TM * TK * 2 / 16 / kThreads;  // 16-byte direct loads per thread per stage: 8
 constexpr int kYLoads = TN * TK * 2 / 16 / kThreads;  // 4
 constexpr int kLoadsPerStage = kXLoads + kYLoads;
-
-// Issues the direct loads of a stage into one ring buffer.  Instruction k of
-// wavefront w fills the 1 KB at position 64 (n w + k) of the tile (lane L at
-// 16 L); position p is row p / (COLS / 8), chunk (p % (COLS / 8)) ^ 4 (row & 3).
-// Every instruction is issued (so each stage adds the same count to the
-// wavefront's vector memory counter); lanes whose row is past the stage's
-// tokens or whose columns are past M or N load 16 zero bytes instead.
-template <int COLS>
-__device__ __forceinline__ void load_tile(const uint16_t* __restrict__ src, int64_t ld, int64_t col0, int64_t cols_total,
-                                          int32_t t, int32_t rows, uint16_t* tile) {
-    constexpr int kChunks = COLS / 8;                      // 16-byte chunks per row
-    constexpr int kLoads = COLS * TK * 2 / 16 / kThreads;  // instructions per thread
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-    for (int k = 0; k < kLoads; ++k) {
-        const int pos = 64 * (kLoads * wv + k) + lane;
-        const int r = pos / kChunks;
-        const int cc = (pos % kChunks) ^ ((r & 3) << 2);
-        const int64_t col = col0 + 8 * cc;
-        const void* from = (r < rows && col < cols_total) ? static_cast<const void*>(src + (int64_t)(t + r) * ld + col)
-                                                          : static_cast<const void*>(kZero16);
-        __builtin_amdgcn_global_load_lds(from, (lds_void*)(tile + 64 * (kLoads * wv + k) * 8), 16, 0, 0);
-    }
-}
-
-// Per-lane element offset, within a stage tile of COLS columns, of the first
-// transposing read of an MFMA operand whose 32 columns start at `colbase`
-// (lane (i, h) gets tokens 16 ks + 8 h + 0..7 of column colbase + i): lane
-// (a, b, c) of the read addresses row 8 (a >> 1) + b, columns
-// colbase + 16 (a & 1) + 4 c .. + 3.  The read for tokens +4 is 4 rows on,
-// and the k-step ks 16 rows on; neither changes the swizzle (row & 3 = b).
-template <int COLS>
-__device__ __forceinline__ int operand_offset(int colbase) {
-    const int lane = threadIdx.x & 63;
-    const int a = lane >> 4, b = (lane >> 2) & 3, c = lane & 3;
-    return lds_at<COLS>(8 * (a >> 1) + b, colbase + 16 * (a & 1) + 4 * c);
-}
 
 // The operands of one k-step: A for the wavefront's two 32-row blocks of X,
 // B for the four 32-column blocks of dY, by twelve transposing LDS reads.
@@ -190,9 +139,7 @@ struct KOps {
 __device__ __forceinline__ KOps read_kstep(const uint16_t* xt, const uint16_t* yt, const int (&xoff)[2],
                                            const int (&yoff)[4], int ks) {
     typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
-    typedef __attribute__((address_space(3))) const uint16_t lds_u16;
-    const uint32_t xb = (uint32_t)(uintptr_t)((lds_u16*)(xt + 16 * ks * TM));
-    const uint32_t yb = (uint32_t)(uintptr_t)((lds_u16*)(yt + 16 * ks * TN));
+    const uint32_t xb = lds_byte_address(xt, 16 * ks * TM), yb = lds_byte_address(yt, 16 * ks * TN);
     u32x2v r[12];
     const uint32_t a0 = xb + 2 * xoff[0], a1 = xb + 2 * xoff[1];
     const uint32_t b0 = yb + 2 * yoff[0], b1 = yb + 2 * yoff[1], b2 = yb + 2 * yoff[2], b3 = yb + 2 * yoff[3];
@@ -279,7 +226,6 @@ __device__ __forceinline__ Work advance(const Work& c, uint32_t P, uint32_t item
 }
 
 // s_waitcnt with only the vector memory count: vmcnt(n), expcnt and lgkmcnt left alone (gfx9 encoding)
-#define DR_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
 // One stage in ring buffer B: wait for its loads, issue the loads of the
 // stage two ahead into buffer (B + 2) % 3, compute, and close the slot and
@@ -305,8 +251,8 @@ __device__ __forceinline__ bool step(Work& cur, Work& nx1, const uint16_t* __res
     __builtin_amdgcn_s_barrier();
     const Work nx2 = advance(nx1, P, items, off, G, split, mtiles, ntiles, M, N, plan, out, chunks);
     if (nx2.valid) {
-        load_tile<TM>(X, M, nx2.w.m0, M, nx2.s.t, nx2.s.rows, xdma);
-        load_tile<TN>(dY, N, nx2.w.n0, N, nx2.s.t, nx2.s.rows, ydma);
+        dma_tile<TM, TK, kThreads>(X, M, nx2.w.m0, M, nx2.s.t, nx2.s.rows, xdma);
+        dma_tile<TN, TK, kThreads>(dY, N, nx2.w.n0, N, nx2.s.t, nx2.s.rows, ydma);
     }
     const int wv = threadIdx.x >> 6;
     const int ksteps = (cur.s.rows + 15) >> 4;
@@ -391,11 +337,11 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(const uint16_t* __re
     cur.w = item_of(wkr, off, G, split, mtiles, ntiles, M, N, plan, out, chunks);
     cur.s = stage_of(cur.w, cur.u, split);
     Work nx1 = advance(cur, P, items, off, G, split, mtiles, ntiles, M, N, plan, out, chunks);
-    load_tile<TM>(X, M, cur.w.m0, M, cur.s.t, cur.s.rows, xs[0]);
-    load_tile<TN>(dY, N, cur.w.n0, N, cur.s.t, cur.s.rows, ys[0]);
+    dma_tile<TM, TK, kThreads>(X, M, cur.w.m0, M, cur.s.t, cur.s.rows, xs[0]);
+    dma_tile<TN, TK, kThreads>(dY, N, cur.w.n0, N, cur.s.t, cur.s.rows, ys[0]);
     if (nx1.valid) {
-        load_tile<TM>(X, M, nx1.w.m0, M, nx1.s.t, nx1.s.rows, xs[1]);
-        load_tile<TN>(dY, N, nx1.w.n0, N, nx1.s.t, nx1.s.rows, ys[1]);
+        dma_tile<TM, TK, kThreads>(X, M, nx1.w.m0, M, nx1.s.t, nx1.s.rows, xs[1]);
+        dma_tile<TN, TK, kThreads>(dY, N, nx1.w.n0, N, nx1.s.t, nx1.s.rows, ys[1]);
     }
 
     f32x16 acc[2][4], sum[2][4];

@@ -93,6 +93,8 @@ typedef struct dr_launch_params {
                                    n / 512, clamped to that range) */
     int32_t chunks_in_flight;   /* index_add: chunks of 8 rows loaded at once per lane group, 1 or 2
                                    (default 1) */
+    int32_t splitk_stream;      /* split-K partials for thin N: 1 = the streaming kernel where it
+                                   applies (the default), 2 = always the general tile kernel */
 } dr_launch_params;
 
 /* Human-readable name of a status code.  Never NULL. */

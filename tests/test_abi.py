@@ -288,16 +288,18 @@ def test_fingerprint_rejects_bad_arguments(lib):
 def test_launch_params_validation(lib):
     class P(ctypes.Structure):
         _fields_ = [("grid_blocks", ctypes.c_int32), ("tile_chunks_log2", ctypes.c_int32),
-                    ("sort_tile_log2", ctypes.c_int32), ("chunks_in_flight", ctypes.c_int32)]
+                    ("sort_tile_log2", ctypes.c_int32), ("chunks_in_flight", ctypes.c_int32),
+                    ("splitk_stream", ctypes.c_int32)]
     lib.dr_set_launch_params.argtypes = [ctypes.c_void_p]
-    assert lib.dr_set_launch_params(ctypes.byref(P(0, 2, 0, 0))) == DR_ERR_INVALID_ARGUMENT
-    assert lib.dr_set_launch_params(ctypes.byref(P(0, 0, 20, 0))) == DR_ERR_INVALID_ARGUMENT
-    assert lib.dr_set_launch_params(ctypes.byref(P(-1, 0, 0, 0))) == DR_ERR_INVALID_ARGUMENT
-    assert lib.dr_set_launch_params(ctypes.byref(P(0, 0, 0, 3))) == DR_ERR_INVALID_ARGUMENT
+    assert lib.dr_set_launch_params(ctypes.byref(P(0, 2, 0, 0, 0))) == DR_ERR_INVALID_ARGUMENT
+    assert lib.dr_set_launch_params(ctypes.byref(P(0, 0, 20, 0, 0))) == DR_ERR_INVALID_ARGUMENT
+    assert lib.dr_set_launch_params(ctypes.byref(P(-1, 0, 0, 0, 0))) == DR_ERR_INVALID_ARGUMENT
+    assert lib.dr_set_launch_params(ctypes.byref(P(0, 0, 0, 3, 0))) == DR_ERR_INVALID_ARGUMENT
+    assert lib.dr_set_launch_params(ctypes.byref(P(0, 0, 0, 0, 3))) == DR_ERR_INVALID_ARGUMENT
     lib.dr_index_add_workspace_size.restype = ctypes.c_size_t
     lib.dr_index_add_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int64]
     default = lib.dr_index_add_workspace_size(100000, 1000, 128)
-    assert lib.dr_set_launch_params(ctypes.byref(P(64, 3, 10, 1))) == DR_OK
+    assert lib.dr_set_launch_params(ctypes.byref(P(64, 3, 10, 1, 2))) == DR_OK
     # smaller tiles need more partial-row space
     assert lib.dr_index_add_workspace_size(100000, 1000, 128) > default
     assert lib.dr_set_launch_params(None) == DR_OK

@@ -432,6 +432,10 @@ def test_splitk_reduce_fingerprinted(dr, S, count):
     (2000, 136, 24, 3),     # three 256-token stages per split, the last one short
     (1500, 128, 20, 1),     # six stages; N not a multiple of 8 (scalar dY staging)
     (600, 64, 36, 2),       # second N tile of 4 columns
+    (5000, 1000, 32, 3),    # streaming kernel: four 256-column M tiles, the last 232 wide
+    (4100, 520, 8, 9),      # streaming kernel: N = 8, a 4-token tail stage per split
+    (700, 2056, 16, 2),     # streaming kernel: nine M tiles, the last 8 wide
+    (120, 64, 16, 40),      # streaming kernel: 3-token splits (one short k-step each)
 ])
 def test_splitk_matches_oracle(dr, K, M, N, splits):
     say(f"splitk K={K} M={M} N={N} S={splits}")
@@ -449,6 +453,25 @@ def test_splitk_matches_oracle(dr, K, M, N, splits):
         assert np.all(np.abs(P[s] - Pexact[s]) <= 1e-4 * A + 1e-30), s
     exact, A = oracle.splitk_reference(inp.X, inp.dY)
     assert np.all(np.abs(host(dW) - exact) <= 1e-4 * A + 1e-30)
+
+
+@pytest.mark.parametrize("K,M,N,splits", [(1000, 200, 24, 7), (5000, 1000, 32, 3), (4100, 520, 8, 9),
+                                           (120, 64, 16, 40), (16384, 7168, 24, 64)])
+def test_splitk_stream_kernel_matches_tile_kernel(dr, K, M, N, splits):
+    """Thin-N partials come from the streaming kernel by default; forcing the
+    general tile kernel must give the same bits (both take the same MFMA steps
+    of 16 tokens from each split's first token)."""
+    say(f"splitk stream vs tile K={K} M={M} N={N} S={splits}")
+    inp = workloads.splitk_inputs(K + 3 * M + N, K, M, N, splits)
+    X, dY = dev_bf16(inp.X), dev_bf16(inp.dY)
+    got = {}
+    for mode in (1, 2):
+        dr.dr_set_launch_params(splitk_stream=mode)
+        try:
+            got[mode] = host(dr.dr_splitk_gemm_tn(X, dY, splits))
+        finally:
+            dr.dr_set_launch_params(reset=True)
+    assert_bits_equal(got[1], got[2], "stream vs tile partials")
 
 
 # ---------------------------------------------------------------------------
