@@ -48,7 +48,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="moe_combine",
                     choices=["moe_combine", "tiny_moe_combine", "sparse_attn_dk", "embedding_grad", "splitk_mhc",
-                             "decode_attention"])
+                             "decode_attention", "sparse_attn_dk_fused", "grouped_wgrad"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--step-only", action="store_true",
                     help="time the step alone: no comparison legs (atomic, unfused, cold cache, extra entry points) "

@@ -134,6 +134,8 @@ def cold_roofline(alg_bytes: int, ms: float) -> dict:
 
 
 def run(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only=False):
+    if name == "sparse_attn_dk_fused":
+        return _fused_dk_main(torch, dr, steps, warmup, cpu_seconds, want_cpu, step_only)
     if name == "grouped_wgrad":
         return _grouped_wgrad(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only)
     if name in ("sparse_attn_dk", "embedding_grad"):
@@ -432,6 +434,38 @@ def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only)
     if want_cpu:
         res["cpu_baseline"] = _cpu_index_add(oracle, inp, cpu_seconds)
     return res
+
+
+def _fused_dk_main(torch, dr, steps, warmup, cpu_seconds, want_cpu, step_only):
+    """The fused key gradient as the line's own workload (for profiling it
+    alone): step_only times the call and nothing else."""
+    import workloads
+    if not step_only:
+        r = _fused_dk(torch, dr, steps, warmup, want_cpu, cpu_seconds)
+        ms = r.pop("ms")
+        alg = r["algorithmic_bytes"]
+        return {"ms_per_step": ms, "value": alg / (ms * 1e-3) / 1e9,
+                "config": {"workload": "sparse_attn_dk_fused: dK[key] += fl32(dS[q,j] Q[q]) over the queries "
+                                       "that selected the key; Q bf16 [8192,128], dS fp32 [8192,512], 65,536 keys"},
+                **r}
+    inp = workloads.sparse_attn_dk_inputs(workloads.CONFIGS["sparse_attn_dk"]["seed"])
+    nq, topk = inp.key_idx.shape
+    Q = torch.from_numpy(inp.Q.view(np.int16)).view(torch.bfloat16).cuda()
+    dS = torch.from_numpy(inp.dS).cuda()
+    idx = torch.from_numpy(inp.key_idx).cuda()
+    dK = torch.from_numpy(inp.dK0).cuda()
+    ws = torch.empty(dr.dr_sparse_attn_dk_workspace_size(nq, topk, inp.num_keys, inp.H), dtype=torch.uint8,
+                     device="cuda")
+    for _ in range(warmup):
+        dr.dr_sparse_attn_dk(dK, Q, dS, idx, ws=ws)
+    ms = _timed(torch, steps, lambda: dr.dr_sparse_attn_dk(dK, Q, dS, idx, ws=ws))
+    touched = int((np.bincount(inp.key_idx.reshape(-1), minlength=inp.num_keys) > 0).sum())
+    n = nq * topk
+    alg = nq * inp.H * 2 + n * 4 + n * 4 + 2 * touched * inp.H * 4
+    return {"ms_per_step": ms, "value": alg / (ms * 1e-3) / 1e9,
+            "config": {"workload": "sparse_attn_dk_fused (step only)"},
+            "roofline": {"bound": "hbm", "achieved": round(alg / (ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}
 
 
 def _fused_dk(torch, dr, steps, warmup, want_cpu=False, cpu_seconds=4.0):

@@ -97,10 +97,11 @@ struct SortBuffers {
     int32_t* tile_flags;  // first pass: index-error flag per tile
     int32_t* totals;
     int32_t *dest_a, *dest_b, *val_a, *val_b, *src_a, *src_b;
+    float *pay_a, *pay_b;  // a payload moved with the keys (optional)
     int64_t nblocks;
 };
 
-SortBuffers carve_sort(Carver& c, int64_t n, bool has_src, int tile_log2) {
+SortBuffers carve_sort(Carver& c, int64_t n, bool has_src, int tile_log2, bool has_pay = false) {
     SortBuffers b{};
     b.nblocks = (n + ((int64_t)1 << tile_log2) - 1) >> tile_log2;
     b.hist = c.take<int32_t>((int64_t)(1 << dr::kMaxDigitBits) * b.nblocks);
@@ -112,6 +113,8 @@ SortBuffers carve_sort(Carver& c, int64_t n, bool has_src, int tile_log2) {
     b.val_b = c.take<int32_t>(n);
     b.src_a = has_src ? c.take<int32_t>(n) : nullptr;
     b.src_b = has_src ? c.take<int32_t>(n) : nullptr;
+    b.pay_a = has_pay ? c.take<float>(n) : nullptr;
+    b.pay_b = has_pay ? c.take<float>(n) : nullptr;
     return b;
 }
 
@@ -121,11 +124,13 @@ SortBuffers carve_sort(Carver& c, int64_t n, bool has_src, int tile_log2) {
 // With seg_deferred, segment offsets that would need a separate search are
 // left to the caller: *seg_deferred is then true and *sorted_dest_out the
 // sorted destinations (not read when n == 0); otherwise seg_offsets is
-// written here.
+// written here.  With pay (no source ids then, and buffers carved for it),
+// pay[i] moves with key i and *pay_sorted_out receives the sorted payload.
 dr_status run_sort(const int32_t* dest, const int32_t* src_id, int32_t src_bound, int64_t n, int32_t num_dests,
                    int32_t* perm, int32_t* seg_offsets, int32_t* inv_perm, int32_t* status, const SortBuffers& b,
                    int tile_log2, hipStream_t s, bool* seg_deferred = nullptr,
-                   const int32_t** sorted_dest_out = nullptr) {
+                   const int32_t** sorted_dest_out = nullptr, const float* pay = nullptr,
+                   const float** pay_sorted_out = nullptr) {
     const bool has_src = src_id != nullptr;
     const std::vector<DigitPass> passes = sort_passes(num_dests, has_src, src_bound);
     int src_passes = 0;
@@ -137,6 +142,7 @@ dr_status run_sort(const int32_t* dest, const int32_t* src_id, int32_t src_bound
     const int32_t* cur_dest = dest;
     const int32_t* cur_src = src_id;
     const int32_t* cur_val = nullptr;
+    const float* cur_pay = pay;
     for (size_t i = 0; i < passes.size(); ++i) {
         const bool last = i + 1 == passes.size();
         const bool odd = i & 1;
@@ -155,6 +161,8 @@ dr_status run_sort(const int32_t* dest, const int32_t* src_id, int32_t src_bound
         sp.inv_out = last ? inv_perm : nullptr;
         sp.seg_out = last && seg_in_scatter ? seg_offsets : nullptr;
         sp.num_dests = num_dests;
+        sp.pay_in = cur_pay;
+        sp.pay_out = pay ? (odd ? b.pay_b : b.pay_a) : nullptr;
         if (i == 0)
             DR_TRY_HIP(dr::launch_radix_validate_hist(dest, num_dests, src_id, src_bound, sp, n, tile_log2, b.hist,
                                                       b.tile_flags, s),
@@ -168,7 +176,9 @@ dr_status run_sort(const int32_t* dest, const int32_t* src_id, int32_t src_bound
         cur_dest = sp.dest_out;
         cur_src = sp.src_out;
         cur_val = sp.val_out;
+        cur_pay = sp.pay_out;
     }
+    if (pay_sorted_out) *pay_sorted_out = cur_pay;
     const bool defer = seg_deferred && !seg_in_scatter;
     if (seg_deferred) *seg_deferred = defer;
     if (sorted_dest_out) *sorted_dest_out = cur_dest;
@@ -209,14 +219,24 @@ struct IndexAddBuffers {
 // The persistent reduce grids hold at most this many workgroups each.
 constexpr int64_t kMaxReduceGrid = 65536;
 
+// The sort tile of an index_add: a sort that also moves a payload keeps a
+// third array per key in registers and LDS, so its default tile is at most
+// 2^12 keys (two workgroups per CU instead of one).
+int index_add_sort_tile(const dr::Launch& lc, int64_t n, bool with_pay) {
+    const int t = lc.sort_tile(n);
+    return with_pay && lc.sort_tile_log2 == 0 && t > 12 ? 12 : t;
+}
+
+// with_pay: the formed-contribution path, whose sort also moves the scales
+// into sorted order.
 IndexAddBuffers carve_index_add(Carver& c, int64_t n, int32_t num_dests, int64_t hidden, bool sort_inside,
-                                int tc_log2, int sort_tile_log2) {
+                                int tc_log2, int sort_tile_log2, bool with_pay = false) {
     IndexAddBuffers b{};
     b.status = c.take<int32_t>(dr::kStatusBytes / sizeof(int32_t));
     if (sort_inside) {
         b.perm = c.take<int32_t>(n);
         b.seg = c.take<int32_t>((int64_t)num_dests + 1);
-        b.sort = carve_sort(c, n, false, sort_tile_log2);
+        b.sort = carve_sort(c, n, false, sort_tile_log2, with_pay);
     }
     const PlanBounds pb = plan_bounds(n, num_dests, tc_log2);
     b.block_sums = c.take<int32_t>(3 * dr::plan_blocks(num_dests));
@@ -513,19 +533,29 @@ dr_status run_index_add(const char* what, float* out, int32_t num_dests, int64_t
             return fail(DR_ERR_UNSUPPORTED, "%s: n and hidden too large for one call", what);
     }
     Carver cv(ws);
+    const int sort_tile = index_add_sort_tile(lc, n, c.scale != nullptr);
     const IndexAddBuffers b = carve_index_add(cv, n, num_dests, hidden, sort_inside, lc.tile_chunks_log2,
-                                              lc.sort_tile(n));
+                                              sort_tile, c.scale != nullptr);
     if (cv.off > ws_bytes)
         return fail(DR_ERR_WORKSPACE_TOO_SMALL, "%s: workspace has %zu bytes, needs %zu", what, ws_bytes, cv.off);
     const int32_t* p = perm;
     const int32_t* seg = seg_offsets;
     bool seg_deferred = false;  // the plan count then also finds the segment offsets
     const int32_t* sorted_dest = nullptr;
+    // Formed contributions read their scale at each sorted position.  When
+    // the sort runs here the scales travel with the keys (read in input
+    // order, written in sorted order), so the reduce reads them contiguously
+    // instead of one scattered 4-byte load (a whole cache line) per row.
+    const float* scale = c.scale;
+    bool scale_sorted = false;
     if (sort_inside) {
         // the sort writes the status word
         const dr_status st = run_sort(index, nullptr, 0, n, num_dests, b.perm, b.seg, nullptr, b.status, b.sort,
-                                      lc.sort_tile(n), stream, &seg_deferred, &sorted_dest);
+                                      sort_tile, stream, &seg_deferred, &sorted_dest, c.scale,
+                                      c.scale ? &scale : nullptr);
         if (st != DR_OK) return st;
+        scale_sorted = c.scale != nullptr && n > 0;
+        if (c.scale && n == 0) scale = c.scale;
         p = b.perm;
         seg = b.seg;
     } else {
@@ -548,7 +578,8 @@ dr_status run_index_add(const char* what, float* out, int32_t num_dests, int64_t
     uint64_t* fp_tc = inout_hash ? b.fp_parts + grid : nullptr;
     if (g_reduce_begin) DR_TRY_HIP(hipEventRecord(g_reduce_begin, stream), "phase event");
     DR_TRY_HIP(dr::launch_segreduce(out, hidden, c.src, c.dtype, n, p, b.tiles, b.partials, lc.tile_chunks_log2,
-                                    lc.chunks_in_flight, c.scale, c.rows_per_src, b.status, fp_seg, stream),
+                                    lc.chunks_in_flight, scale, scale_sorted, c.rows_per_src, b.status, fp_seg,
+                                    stream),
                "segmented reduce launch");
     DR_TRY_HIP(dr::launch_tilecombine(out, hidden, b.partials, b.multis, n, lc.tile_chunks_log2, b.status, fp_tc,
                                       stream),
@@ -589,7 +620,11 @@ dr_status dr_index_add_fingerprinted(float* out, int32_t num_dests, int64_t hidd
 
 size_t dr_sparse_attn_dk_workspace_size(int64_t num_queries, int32_t topk, int32_t num_keys, int64_t head_dim) {
     const int64_t n = num_queries < 0 || topk < 1 ? 0 : num_queries * (int64_t)topk;
-    return dr_index_add_workspace_size(n, num_keys, head_dim);
+    const dr::Launch lc = dr::launch_config();
+    Carver c(nullptr);
+    carve_index_add(c, n, num_keys < 1 ? 1 : num_keys, head_dim < 1 ? 1 : head_dim, true, lc.tile_chunks_log2,
+                    index_add_sort_tile(lc, n, true), true);
+    return c.off;
 }
 
 dr_status dr_sparse_attn_dk(float* dK, int32_t num_keys, int64_t head_dim, const void* Q, dr_dtype q_dtype,

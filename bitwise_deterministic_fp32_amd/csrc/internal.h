@@ -100,6 +100,8 @@ struct SortPass {
     int32_t* seg_out;          // set when this pass's digit is the whole destination (a single dest
                                // pass): workgroup 0 then writes seg_offsets[0 .. num_dests]
     int32_t num_dests;
+    const float* pay_in;       // optional payload moved with the keys (input order on the first pass)
+    float* pay_out;            // set together with pay_in; no source ids are carried then
 };
 hipError_t launch_radix_validate_hist(const int32_t* dest, int32_t num_dests, const int32_t* src_id,
                                       int32_t src_bound, const SortPass& p, int64_t n, int tile_log2,
@@ -128,10 +130,12 @@ hipError_t launch_plan_write(const int32_t* seg_offsets, int32_t num_dests, int 
 hipError_t launch_plan_validate(const int32_t* perm, const int32_t* seg, const int32_t* index, int64_t n,
                                 int32_t num_dests, int32_t* status, hipStream_t s);
 // scale != null: source row p contributes fl32(scale[p] * src[p / rows_per_src])
+// scale_sorted: scale is in sorted order (scale[r] belongs to sorted position
+// r) instead of indexed by source row.
 hipError_t launch_segreduce(float* out, int64_t hidden, const void* src, dr_dtype src_dtype, int64_t n,
                             const int32_t* perm, const TileRec* tiles, float* partials, int tile_chunks_log2,
-                            int chunks_in_flight, const float* scale, int32_t rows_per_src, int32_t* status,
-                            uint64_t* fp_part, hipStream_t s);
+                            int chunks_in_flight, const float* scale, bool scale_sorted, int32_t rows_per_src,
+                            int32_t* status, uint64_t* fp_part, hipStream_t s);
 hipError_t launch_tilecombine(float* out, int64_t hidden, const float* partials, const MultiRec* multis, int64_t n,
                               int tile_chunks_log2, int32_t* status, uint64_t* fp_part, hipStream_t s);
 // Workgroups of the persistent reduce kernels (segreduce, tilecombine); with

@@ -21,7 +21,11 @@
 //                a longer one write private partial rows.
 //   tilecombine: merges a destination's partial rows by the same counter, in
 //                tile order, then updates the destination row.
+//   segreduce_gen16 / segreduce_gen: the formed-contribution form (the
+//                sparse-attention key gradient), each row fl32(scale * a short
+//                shared source row), one wavefront per tile.
 #include "internal.h"
+#include "lds_tile.h"
 
 namespace dr {
 namespace {
@@ -305,10 +309,13 @@ struct TreeCounter {
 
     __device__ __forceinline__ void push(float (&s)[E]) {
         if (UNIFORM) {
+            // (the empty asm statement keeps the compiler from turning the
+            // wave-uniform merge branches into per-lane selects over every level)
             const int merges = __builtin_amdgcn_readfirstlane(__builtin_ctz(~count));
 #pragma unroll
             for (int l = 0; l < DEPTH; ++l) {
                 if (l < merges) {
+                    asm volatile("");
 #pragma unroll
                     for (int e = 0; e < E; ++e) s[e] = level[l][e] + s[e];
                 }
@@ -396,18 +403,13 @@ __device__ __forceinline__ u32x4 pack4(const float* t) {
 // a group reads GROUP*16 contiguous bytes.  One group reduces one (tile,
 // column slice).
 //
-// GEN: the contribution of source row p is formed here instead of loaded:
-// fl32(scale[p] * src[p / rows_per_src]) element by element (the sparse-
-// attention key gradient: scale = dS, src = Q, rows_per_src = top-k).  The
-// product is rounded before it enters the tree.  src rows are then shared by
-// many contributions and small, so they are read through the cache.
 // Four wavefronts per SIMD (at most 128 VGPRs) for one item per wavefront with
 // tiles of up to 2^5 chunks; deeper counters would spill at that budget.
-template <dr_dtype DT, int GROUP, int TCLOG, int CIF, bool GEN>
+template <dr_dtype DT, int GROUP, int TCLOG, int CIF>
 __global__ __launch_bounds__(kReduceThreads, GROUP == 64 && CIF == 1 && TCLOG <= 5 ? 4 : 1) void segreduce_kernel(
     float* __restrict__ out, int64_t H, const void* __restrict__ src, const int32_t* __restrict__ perm,
     const TileRec* __restrict__ tiles, float* __restrict__ partials, int64_t slices, int32_t* status,
-    const float* __restrict__ scale, uint32_t rows_per_src, uint64_t* __restrict__ fp_part) {
+    uint64_t* __restrict__ fp_part) {
     using V = Vec<DT>;
     constexpr int E = V::kElems;  // columns of a lane
     constexpr int Q = E / 4;      // 16-byte fp32 pieces of a lane's output
@@ -473,17 +475,8 @@ __global__ __launch_bounds__(kReduceThreads, GROUP == 64 && CIF == 1 && TCLOG <=
         }
         for (int64_t r0 = r_begin; r0 < r_end; r0 += R) {
             u32x4 raw[R];
-            float sc[GEN ? R : 1];
             const int64_t live = r_end - r0;  // rows of this step that exist
-            if (GEN) {
-#pragma unroll
-                for (int j = 0; j < R; ++j) {
-                    // rows past the tile's end repeat a live row (a cache hit) and are not added
-                    const uint32_t p = (uint32_t)idx[j];
-                    sc[j] = scale[p];
-                    raw[j] = load16(src_bytes + (int64_t)(p / rows_per_src) * row_bytes + lcol * kElemBytes);
-                }
-            } else if (live >= R) {
+            if (live >= R) {
 #pragma unroll
                 for (int j = 0; j < R; ++j)
                     raw[j] = load16_stream(src_bytes + (int64_t)idx[j] * row_bytes + lcol * kElemBytes);
@@ -511,19 +504,11 @@ __global__ __launch_bounds__(kReduceThreads, GROUP == 64 && CIF == 1 && TCLOG <=
                 if (m > 0) {
                     float s[E];
                     V::widen(raw[8 * c], s);
-                    if (GEN) {
-#pragma unroll
-                        for (int e = 0; e < E; ++e) s[e] = sc[8 * c] * s[e];
-                    }
                     if (m == 8) {
 #pragma unroll
                         for (int j = 1; j < 8; ++j) {
                             float v[E];
                             V::widen(raw[8 * c + j], v);
-                            if (GEN) {
-#pragma unroll
-                                for (int e = 0; e < E; ++e) v[e] = sc[8 * c + j] * v[e];  // rounded product
-                            }
 #pragma unroll
                             for (int e = 0; e < E; ++e) s[e] = s[e] + v[e];
                         }
@@ -534,10 +519,6 @@ __global__ __launch_bounds__(kReduceThreads, GROUP == 64 && CIF == 1 && TCLOG <=
                             if (j < m) {
                                 float v[E];
                                 V::widen(raw[8 * c + j], v);
-                                if (GEN) {
-#pragma unroll
-                                    for (int e = 0; e < E; ++e) v[e] = sc[8 * c + j] * v[e];
-                                }
 #pragma unroll
                                 for (int e = 0; e < E; ++e) s[e] = s[e] + v[e];
                             }
@@ -547,10 +528,6 @@ __global__ __launch_bounds__(kReduceThreads, GROUP == 64 && CIF == 1 && TCLOG <=
                         for (int j = 1; j < 8; ++j) {
                             float v[E];
                             V::widen(raw[8 * c + j], v);
-                            if (GEN) {
-#pragma unroll
-                                for (int e = 0; e < E; ++e) v[e] = sc[8 * c + j] * v[e];
-                            }
 #pragma unroll
                             for (int e = 0; e < E; ++e) {
                                 const float a = s[e] + v[e];
@@ -583,6 +560,285 @@ __global__ __launch_bounds__(kReduceThreads, GROUP == 64 && CIF == 1 && TCLOG <=
         __shared__ uint64_t fsm[kReduceThreads / 64];
         const uint64_t b = block_sum_u64(fp_acc, fsm);
         if (threadIdx.x == 0) fp_part[blockIdx.x] = b;
+    }
+}
+
+// The formed-contribution reduce (the sparse-attention key gradient): the
+// contribution of sorted position r, source row p = perm[r], is
+// fl32(scale * src[p / rows_per_src]) element by element, with scale the
+// score gradient of that row (scale[r] when the sort moved the scales into
+// sorted order, else scale[p]).  One wavefront per (tile, column slice), lane
+// l owning E consecutive columns, so that a short source row (128 columns)
+// still fills the wavefront and every row step is wave-uniform: lanes 0..7
+// fetch a chunk's ids and scales and the row loads read them back with
+// readlane, each row is one small load per lane (the source rows are few and
+// shared, so they are read through the cache), and the chunk sums and the
+// tree need no per-lane selects.  This form serves fp32 source rows and
+// sources of 2^31 bytes or more; bf16 rows take the LDS form below.  The arithmetic
+// is the same as the row kernel's: chunks of 8 rows left to right, the chunk
+// sums into the pairwise tree, the tile's result added once into the
+// destination row (or stored as the tile's partial row for tilecombine).
+template <dr_dtype DT, int E>
+struct GenRow {
+    static constexpr int kBytes = E * (DT == DR_BF16 ? 2 : 4);
+    static constexpr int kWords = kBytes / 4;
+    typedef uint32_t Raw __attribute__((ext_vector_type(kWords)));
+    __device__ __forceinline__ static Raw load(const char* p) { return *reinterpret_cast<const Raw*>(p); }
+    __device__ __forceinline__ static void widen(const Raw& r, float (&v)[E]) {
+#pragma unroll
+        for (int w = 0; w < kWords; ++w) {
+            if (DT == DR_BF16) {
+                v[2 * w] = __uint_as_float(r[w] << 16);
+                v[2 * w + 1] = __uint_as_float(r[w] & 0xFFFF0000u);
+            } else {
+                v[w] = __uint_as_float(r[w]);
+            }
+        }
+    }
+};
+
+#ifndef GEN_CHUNKS
+#define GEN_CHUNKS 2
+#endif
+// Source row of contribution p: p / rows_per_src as (p * m) >> (31 + sh), with
+// m = ceil(2^(31+sh) / d) and sh = ceil(log2 d): exact for p < 2^31 (the error
+// of m, below d, moves p * m / 2^(31+sh) by less than 2^-sh <= 1/d).
+__device__ __forceinline__ uint32_t gen_row_of(uint32_t p, uint32_t m, uint32_t sh) {
+    return (uint32_t)(((uint64_t)p * m) >> (31 + sh));
+}
+
+template <dr_dtype DT, int E, int TCLOG, bool SORTED>
+__global__ __launch_bounds__(kReduceThreads) void segreduce_gen_kernel(
+    float* __restrict__ out, int64_t H, const char* __restrict__ src, const int32_t* __restrict__ perm,
+    const TileRec* __restrict__ tiles, float* __restrict__ partials, int64_t slices, const int32_t* __restrict__ status,
+    const float* __restrict__ scale, uint32_t div_m, uint32_t div_sh) {
+    using G = GenRow<DT, E>;
+    constexpr int kElemBytes = DT == DR_BF16 ? 2 : 4;
+    constexpr int CH = GEN_CHUNKS;  // chunks of 8 rows loaded at once
+    constexpr int R = 8 * CH;
+    if (status[kWordStatus] != 0) return;
+    // the host keeps (tile bound) * slices below 2^32, so 32-bit division suffices
+    const uint32_t items = (uint32_t)status[kWordTiles] * (uint32_t)slices;
+    const int lane = threadIdx.x & 63;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane((blockIdx.x * kReduceThreads + threadIdx.x) / 64);
+    const uint32_t nwaves = gridDim.x * (kReduceThreads / 64);
+    const int64_t row_bytes = H * kElemBytes;
+    const int jl = lane % R;
+    // Lanes 0..R-1 hold the source ids of the next R rows (rows past a tile's
+    // end repeat its last row and are not added), fetched one step ahead: the
+    // next item's first ids are fetched during the current item's last step.
+    TileRec tr_next{};
+    int32_t ids = 0;
+    if (wave < items) {
+        tr_next = tiles[wave / (uint32_t)slices];
+        ids = perm[min((int64_t)tr_next.r_begin + jl, (int64_t)tr_next.r_end - 1)];
+    }
+    for (uint32_t it = wave; it < items; it += nwaves) {
+        const uint32_t slice = it % (uint32_t)slices;
+        const TileRec tr = tr_next;
+        const bool has_next = (uint64_t)it + nwaves < items;
+        if (has_next) tr_next = tiles[(it + nwaves) / (uint32_t)slices];
+        const int64_t col = (int64_t)slice * 64 * E + E * lane;
+        const bool active = col < H;
+        const int64_t lcol = active ? col : 0;  // idle lanes read a valid piece
+        const char* src_col = src + lcol * kElemBytes;
+        const int64_t r_begin = tr.r_begin, r_end = tr.r_end;
+        float* orow = out + (int64_t)tr.dest * H;
+        float old[E];
+        if (tr.pslot < 0) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) old[e] = orow[lcol + e];
+        }
+        TreeCounter<TCLOG + 1, E, true> tc;
+        for (int64_t r0 = r_begin; r0 < r_end; r0 += R) {
+            const float scl = scale[SORTED ? min(r0 + jl, r_end - 1) : (int64_t)ids];
+            typename G::Raw raw[R];
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                const uint32_t p = (uint32_t)__builtin_amdgcn_readlane(ids, j);
+                raw[j] = G::load(src_col + (int64_t)gen_row_of(p, div_m, div_sh) * row_bytes);
+            }
+            const int64_t r1 = r0 + R;
+            if (r1 < r_end) ids = perm[min(r1 + jl, r_end - 1)];
+            else if (has_next) ids = perm[min((int64_t)tr_next.r_begin + jl, (int64_t)tr_next.r_end - 1)];
+#pragma unroll
+            for (int c = 0; c < CH; ++c) {
+                const int m = (int)min((int64_t)8, r_end - (r0 + 8 * c));  // rows of chunk c (wave-uniform)
+                if (m > 0) {
+                    float s[E];
+                    G::widen(raw[8 * c], s);
+                    const float s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                                 __builtin_bit_cast(int32_t, scl), 8 * c));
+#pragma unroll
+                    for (int e = 0; e < E; ++e) s[e] = s0 * s[e];
+#pragma unroll
+                    for (int j = 1; j < 8; ++j) {
+                        if (j < m) {
+                            const float sj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                                         __builtin_bit_cast(int32_t, scl), 8 * c + j));
+                            float v[E];
+                            G::widen(raw[8 * c + j], v);
+#pragma unroll
+                            for (int e = 0; e < E; ++e) v[e] = sj * v[e];  // rounded product
+#pragma unroll
+                            for (int e = 0; e < E; ++e) s[e] = s[e] + v[e];
+                        }
+                    }
+                    tc.push(s);
+                }
+            }
+        }
+        float t[E];
+        tc.fold(t);
+        if (active) {
+            if (tr.pslot < 0) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) orow[col + e] = old[e] + t[e];  // out = old + T
+            } else {
+                float* prow = partials + (int64_t)tr.pslot * H;
+#pragma unroll
+                for (int e = 0; e < E; ++e) prow[col + e] = t[e];
+            }
+        }
+    }
+}
+
+// The formed-contribution reduce for bf16 source rows, through LDS.  Row
+// loads are 16 bytes per lane (a 16-lane group reads one 128-column slice of a
+// row, four rows per instruction: 16-byte loads move four times the bytes of
+// the 4-byte loads above for the same address work); the wavefront writes a
+// chunk's 8 rows to its own 2 KB of LDS and reads them back transposed with
+// ds_read_b64_tr_b16, so that lane l holds columns l and 64 + l of all 8 rows
+// and the chunk sum, the tree and the destination update run wave-uniform, as
+// above.  A chunk's 8 ids (and sorted scales) arrive in scalar registers by
+// one 8-dword scalar buffer load each.  The LDS tile is row-major with the
+// 16-byte chunks of row r swizzled by r & 3, so a transposing read's four rows
+// fall in different banks.
+typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
+// Eight consecutive dwords through the scalar cache, range-checked: a dword at
+// or past the resource's size reads as 0.
+__device__ i32x8_t dr_s_buffer_load_x8(i32x4_t rsrc, int32_t offset, int32_t cachepolicy)
+    __asm("llvm.amdgcn.s.buffer.load.v8i32");
+
+__device__ __forceinline__ i32x4_t dword_rsrc(const void* p, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    return i32x4_t{(int32_t)(uint32_t)a, (int32_t)(uint32_t)(a >> 32), (int32_t)bytes, 0x00020000};
+}
+
+template <int TCLOG, bool SORTED, bool POW2>
+__global__ __launch_bounds__(kReduceThreads) void segreduce_gen16_kernel(
+    float* __restrict__ out, int64_t H, const char* __restrict__ src, uint32_t src_bytes,
+    const int32_t* __restrict__ perm, uint32_t n, const TileRec* __restrict__ tiles, float* __restrict__ partials,
+    int64_t slices, const int32_t* __restrict__ status, const float* __restrict__ scale, uint32_t div_m,
+    uint32_t div_sh) {
+    constexpr int kCols = 128;  // columns of a slice
+    __shared__ __attribute__((aligned(16))) uint16_t lds_rows[kReduceThreads / 64][8 * kCols];
+    if (status[kWordStatus] != 0) return;
+    // the host keeps (tile bound) * slices below 2^32, so 32-bit division suffices
+    const uint32_t items = (uint32_t)status[kWordTiles] * (uint32_t)slices;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int g = lane >> 4, li = lane & 15;  // loads: group g reads rows g and 4 + g, 16-byte piece li
+    const uint32_t wave = __builtin_amdgcn_readfirstlane((blockIdx.x * kReduceThreads + threadIdx.x) / 64);
+    const uint32_t nwaves = gridDim.x * (kReduceThreads / 64);
+    const uint32_t row_bytes = (uint32_t)H * 2;  // the host keeps the source rows below 2^31 bytes
+    // source rows, ids and sorted scales through buffer resources (32-bit offsets)
+    const __amdgpu_buffer_rsrc_t srsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src), 0, (int)src_bytes, 0x00020000);
+    const i32x4_t prsrc = dword_rsrc(perm, 4 * n);
+    const i32x4_t crsrc = dword_rsrc(scale, 4 * n);
+    uint16_t* rows = lds_rows[wv];
+    // LDS offsets: this lane's two row writes, and its transposing reads (read k
+    // covers rows 4 (k >> 1) .. + 3 of column block g + 4 (k & 1); lane (g, b, c)
+    // addresses row 4 (k >> 1) + b, columns 16 (g + 4 (k & 1)) + 4 c).
+    const int w0 = lds_at<kCols>(g, 8 * li), w1 = lds_at<kCols>(4 + g, 8 * li);
+    int rd[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        rd[k] = lds_at<kCols>(4 * (k >> 1) + ((lane >> 2) & 3), 16 * (g + 4 * (k & 1)) + 4 * (lane & 3));
+    for (uint32_t it = wave; it < items; it += nwaves) {
+        const uint32_t tile = it / (uint32_t)slices;
+        const uint32_t slice = it - tile * (uint32_t)slices;
+        const TileRec tr = tiles[tile];
+        const int32_t c0 = (int32_t)slice * kCols;
+        // loads: 8 columns from c0 + 8 li (idle pieces past H read the slice's first piece)
+        const uint32_t lcol_off = (uint32_t)(c0 + 8 * li < H ? c0 + 8 * li : c0) * 2;
+        const int32_t r_begin = tr.r_begin, r_end = tr.r_end;
+        float* orow = out + (int64_t)tr.dest * H;
+        // results: lane l owns columns c0 + l and c0 + 64 + l
+        const int64_t oc0 = c0 + lane, oc1 = c0 + 64 + lane;
+        const bool act0 = oc0 < H, act1 = oc1 < H;
+        float old0 = 0.f, old1 = 0.f;
+        if (tr.pslot < 0) {
+            old0 = orow[act0 ? oc0 : 0];
+            old1 = orow[act1 ? oc1 : 0];
+        }
+        TreeCounter<TCLOG + 1, 2, true> tc;
+        for (int32_t r0 = r_begin; r0 < r_end; r0 += 8) {
+            const int m = min(8, r_end - r0);  // rows of the chunk (wave-uniform)
+            // the chunk's ids and scales, wave-uniform; rows past the tile's end
+            // (other tiles' rows, or 0 past the arrays' end: the loads check
+            // each dword against the size) are loaded but not added
+            const i32x8_t pv = dr_s_buffer_load_x8(prsrc, 4 * r0, 0);
+            i32x8_t sv{};
+            if (SORTED) sv = dr_s_buffer_load_x8(crsrc, 4 * r0, 0);
+            float sc[8];
+            if (SORTED) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) sc[j] = __int_as_float(sv[j]);  // (not a bit_cast of the element lvalue)
+            } else {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) sc[j] = scale[(uint32_t)pv[j]];
+            }
+            uint32_t off[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t p = (uint32_t)pv[j];
+                off[j] = (POW2 ? p >> div_sh : gen_row_of(p, div_m, div_sh)) * row_bytes;
+            }
+            uint32_t oa = off[0], ob = off[4];
+            oa = g == 1 ? off[1] : oa;
+            ob = g == 1 ? off[5] : ob;
+            oa = g == 2 ? off[2] : oa;
+            ob = g == 2 ? off[6] : ob;
+            oa = g == 3 ? off[3] : oa;
+            ob = g == 3 ? off[7] : ob;
+            const u32x4 va = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(srsrc, (int)(oa + lcol_off), 0, 0));
+            const u32x4 vb = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(srsrc, (int)(ob + lcol_off), 0, 0));
+            *reinterpret_cast<u32x4*>(rows + w0) = va;
+            *reinterpret_cast<u32x4*>(rows + w1) = vb;
+            __builtin_amdgcn_wave_barrier();
+            typedef short s16x4 __attribute__((ext_vector_type(4)));
+            typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+            s16x4 t[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) t[k] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(rows + rd[k]));
+            __builtin_amdgcn_wave_barrier();
+            // row j of column l: t[2 (j >> 2)][j & 3]; of column 64 + l: t[2 (j >> 2) + 1][j & 3]
+            float s2[2];
+            s2[0] = sc[0] * __uint_as_float((uint32_t)(uint16_t)t[0][0] << 16);
+            s2[1] = sc[0] * __uint_as_float((uint32_t)(uint16_t)t[1][0] << 16);
+#pragma unroll
+            for (int j = 1; j < 8; ++j) {
+                if (j < m) {
+                    const float v0 = sc[j] * __uint_as_float((uint32_t)(uint16_t)t[(j >> 2) * 2][j & 3] << 16);
+                    const float v1 = sc[j] * __uint_as_float((uint32_t)(uint16_t)t[(j >> 2) * 2 + 1][j & 3] << 16);
+                    s2[0] = s2[0] + v0;  // rounded products, added left to right
+                    s2[1] = s2[1] + v1;
+                }
+            }
+            tc.push(s2);
+        }
+        float t2[2];
+        tc.fold(t2);
+        if (tr.pslot < 0) {
+            if (act0) orow[oc0] = old0 + t2[0];  // out = old + T
+            if (act1) orow[oc1] = old1 + t2[1];
+        } else {
+            float* prow = partials + (int64_t)tr.pslot * H;
+            if (act0) prow[oc0] = t2[0];
+            if (act1) prow[oc1] = t2[1];
+        }
     }
 }
 
@@ -644,14 +900,14 @@ int group_for(int64_t pieces) {
     return 64;
 }
 
-template <dr_dtype DT, int GROUP, int CIF, bool GEN>
+template <dr_dtype DT, int GROUP, int CIF>
 hipError_t launch_segreduce_g(dim3 grid, float* out, int64_t H, const void* src, const int32_t* perm,
                               const TileRec* tiles, float* partials, int tc_log2, int64_t slices, int32_t* status,
-                              const float* scale, uint32_t rows_per_src, uint64_t* fp_part, hipStream_t s) {
+                              uint64_t* fp_part, hipStream_t s) {
 #define DR_SEGREDUCE_CASE(TC)                                                                                  \
     case TC:                                                                                                   \
-        hipLaunchKernelGGL((segreduce_kernel<DT, GROUP, TC, CIF, GEN>), grid, dim3(kReduceThreads), 0, s, out,  \
-                           H, src, perm, tiles, partials, slices, status, scale, rows_per_src, fp_part);       \
+        hipLaunchKernelGGL((segreduce_kernel<DT, GROUP, TC, CIF>), grid, dim3(kReduceThreads), 0, s, out, H,    \
+                           src, perm, tiles, partials, slices, status, fp_part);                               \
         break;
     switch (tc_log2) {
         DR_SEGREDUCE_CASE(3)
@@ -664,6 +920,101 @@ hipError_t launch_segreduce_g(dim3 grid, float* out, int64_t H, const void* src,
     }
 #undef DR_SEGREDUCE_CASE
     return hipGetLastError();
+}
+
+// Columns per lane of the formed-contribution reduce: the fewest (at least 2)
+// that cover the row with one wavefront, capped at 16 bytes per lane.
+template <dr_dtype DT, int E>
+hipError_t launch_gen_e(dim3 grid, float* out, int64_t H, const void* src, const int32_t* perm,
+                        const TileRec* tiles, float* partials, int tc_log2, const int32_t* status, const float* scale,
+                        bool scale_sorted, uint32_t rps, hipStream_t s) {
+    const int64_t slices = (H + 64 * E - 1) / (64 * E);
+    // p / rps as a multiply and shift (gen_row_of); rps >= 1
+    uint32_t sh = 0;
+    while (((uint64_t)1 << sh) < rps) ++sh;
+    const uint32_t m = (uint32_t)((((uint64_t)1 << (31 + sh)) + rps - 1) / rps);
+#define DR_GEN_CASE(TC)                                                                                         \
+    case TC:                                                                                                    \
+        if (scale_sorted)                                                                                       \
+            hipLaunchKernelGGL((segreduce_gen_kernel<DT, E, TC, true>), grid, dim3(kReduceThreads), 0, s, out,   \
+                               H, static_cast<const char*>(src), perm, tiles, partials, slices, status, scale,  \
+                               m, sh);                                                                          \
+        else                                                                                                    \
+            hipLaunchKernelGGL((segreduce_gen_kernel<DT, E, TC, false>), grid, dim3(kReduceThreads), 0, s, out,  \
+                               H, static_cast<const char*>(src), perm, tiles, partials, slices, status, scale,  \
+                               m, sh);                                                                          \
+        break;
+    switch (tc_log2) {
+        DR_GEN_CASE(3)
+        DR_GEN_CASE(4)
+        DR_GEN_CASE(5)
+        DR_GEN_CASE(6)
+        DR_GEN_CASE(7)
+        default:
+            return hipErrorInvalidValue;
+    }
+#undef DR_GEN_CASE
+    return hipGetLastError();
+}
+
+template <bool SORTED, bool POW2>
+hipError_t launch_gen16(dim3 grid, float* out, int64_t H, const void* src, uint32_t src_bytes, const int32_t* perm,
+                        uint32_t n, const TileRec* tiles, float* partials, int tc_log2, const int32_t* status,
+                        const float* scale, uint32_t m, uint32_t sh, hipStream_t s) {
+    const int64_t slices = (H + 127) / 128;
+#define DR_GEN16_CASE(TC)                                                                                       \
+    case TC:                                                                                                    \
+        hipLaunchKernelGGL((segreduce_gen16_kernel<TC, SORTED, POW2>), grid, dim3(kReduceThreads), 0, s, out,   \
+                           H, static_cast<const char*>(src), src_bytes, perm, n, tiles, partials, slices,       \
+                           status, scale, m, sh);                                                               \
+        break;
+    switch (tc_log2) {
+        DR_GEN16_CASE(3)
+        DR_GEN16_CASE(4)
+        DR_GEN16_CASE(5)
+        DR_GEN16_CASE(6)
+        DR_GEN16_CASE(7)
+        default:
+            return hipErrorInvalidValue;
+    }
+#undef DR_GEN16_CASE
+    return hipGetLastError();
+}
+
+hipError_t launch_segreduce_gen(dim3 grid, float* out, int64_t H, const void* src, int64_t src_rows, int64_t n,
+                                dr_dtype dt, const int32_t* perm, const TileRec* tiles, float* partials, int tc_log2,
+                                const int32_t* status, const float* scale, bool scale_sorted, uint32_t rps,
+                                hipStream_t s) {
+    // bf16 source rows of fewer than 2^31 bytes in all take the LDS form (32-bit buffer offsets)
+    const int64_t src_bytes = src_rows * H * 2;
+    if (dt == DR_BF16 && src_bytes < ((int64_t)1 << 31) && n < ((int64_t)1 << 29)) {
+        uint32_t sh = 0;
+        while (((uint64_t)1 << sh) < rps) ++sh;
+        const uint32_t m = (uint32_t)((((uint64_t)1 << (31 + sh)) + rps - 1) / rps);
+        const bool pow2 = (rps & (rps - 1)) == 0;
+        const uint32_t sb = (uint32_t)src_bytes, nn = (uint32_t)n;
+        if (scale_sorted)
+            return pow2 ? launch_gen16<true, true>(grid, out, H, src, sb, perm, nn, tiles, partials, tc_log2, status,
+                                                   scale, m, sh, s)
+                        : launch_gen16<true, false>(grid, out, H, src, sb, perm, nn, tiles, partials, tc_log2, status,
+                                                    scale, m, sh, s);
+        return pow2 ? launch_gen16<false, true>(grid, out, H, src, sb, perm, nn, tiles, partials, tc_log2, status,
+                                                scale, m, sh, s)
+                    : launch_gen16<false, false>(grid, out, H, src, sb, perm, nn, tiles, partials, tc_log2, status,
+                                                 scale, m, sh, s);
+    }
+    if (dt == DR_BF16) {
+        if (H <= 128) return launch_gen_e<DR_BF16, 2>(grid, out, H, src, perm, tiles, partials, tc_log2, status, scale,
+                                                      scale_sorted, rps, s);
+        if (H <= 256) return launch_gen_e<DR_BF16, 4>(grid, out, H, src, perm, tiles, partials, tc_log2, status, scale,
+                                                      scale_sorted, rps, s);
+        return launch_gen_e<DR_BF16, 8>(grid, out, H, src, perm, tiles, partials, tc_log2, status, scale,
+                                        scale_sorted, rps, s);
+    }
+    if (H <= 128) return launch_gen_e<DR_F32, 2>(grid, out, H, src, perm, tiles, partials, tc_log2, status, scale,
+                                                 scale_sorted, rps, s);
+    return launch_gen_e<DR_F32, 4>(grid, out, H, src, perm, tiles, partials, tc_log2, status, scale, scale_sorted,
+                                   rps, s);
 }
 
 }  // namespace
@@ -707,22 +1058,23 @@ hipError_t launch_plan_validate(const int32_t* perm, const int32_t* seg, const i
 
 hipError_t launch_segreduce(float* out, int64_t hidden, const void* src, dr_dtype dt, int64_t n, const int32_t* perm,
                             const TileRec* tiles, float* partials, int tc_log2, int cif, const float* scale,
-                            int32_t rows_per_src, int32_t* status, uint64_t* fp_part, hipStream_t s) {
-    (void)n;
+                            bool scale_sorted, int32_t rows_per_src, int32_t* status, uint64_t* fp_part,
+                            hipStream_t s) {
     const int64_t lanes = dt == DR_BF16 ? hidden / 8 : hidden / 4;  // lanes needed per row
     const int g = group_for(lanes);
     const int64_t slices = (lanes + g - 1) / g;
     const dim3 grid(persistent_grid());
     const uint32_t rps = (uint32_t)rows_per_src;
-    // formed contributions (scale != null) always stream one chunk at a time
+    if (scale) {
+        if (fp_part) return hipErrorInvalidValue;  // formed contributions keep no fingerprint
+        return launch_segreduce_gen(grid, out, hidden, src, (n + rows_per_src - 1) / rows_per_src, n, dt, perm,
+                                    tiles, partials, tc_log2, status, scale, scale_sorted, rps, s);
+    }
 #define DR_SR(DT, G)                                                                                           \
-    if (scale)                                                                                                 \
-        return launch_segreduce_g<DT, G, 1, true>(grid, out, hidden, src, perm, tiles, partials, tc_log2,      \
-                                                  slices, status, scale, rps, fp_part, s);                     \
-    return cif == 1 ? launch_segreduce_g<DT, G, 1, false>(grid, out, hidden, src, perm, tiles, partials,       \
-                                                          tc_log2, slices, status, nullptr, 1u, fp_part, s)    \
-                    : launch_segreduce_g<DT, G, 2, false>(grid, out, hidden, src, perm, tiles, partials,       \
-                                                          tc_log2, slices, status, nullptr, 1u, fp_part, s)
+    return cif == 1 ? launch_segreduce_g<DT, G, 1>(grid, out, hidden, src, perm, tiles, partials, tc_log2,     \
+                                                   slices, status, fp_part, s)                                 \
+                    : launch_segreduce_g<DT, G, 2>(grid, out, hidden, src, perm, tiles, partials, tc_log2,     \
+                                                   slices, status, fp_part, s)
     if (dt == DR_BF16) {
         if (g == 16) { DR_SR(DR_BF16, 16); }
         if (g == 32) { DR_SR(DR_BF16, 32); }

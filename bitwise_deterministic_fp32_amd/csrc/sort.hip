@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void radix_scan_kernel(int32_t* hist, int
 // input order.  The tile is staged in
 // LDS in (digit, rank) order and each digit's run is written to consecutive
 // global positions.
-template <int ITEMS, int BINS, bool STAGE_SRC>
+template <int ITEMS, int BINS, bool STAGE_SRC, bool PAY>
 __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(SortPass p, int64_t n, int tile_log2,
                                                                  const int32_t* __restrict__ hist, int64_t nblocks,
                                                                  const int32_t* __restrict__ totals,
@@ -188,12 +188,13 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(SortPass p, int
     __shared__ int32_t wave_tot[kWaves];
     // The staged tile, and before it (ranking only) each wavefront's table of
     // lane masks by digit.
-    constexpr int kStageBytes = (STAGE_SRC ? 3 : 2) * ITEMS * kThreads * 4;
+    constexpr int kStageBytes = (2 + (STAGE_SRC ? 1 : 0) + (PAY ? 1 : 0)) * ITEMS * kThreads * 4;
     constexpr int kTableBytes = kWaves * BINS * 8;
     __shared__ __align__(16) unsigned char shared_un[kStageBytes > kTableBytes ? kStageBytes : kTableBytes];
     int32_t* st_dest = reinterpret_cast<int32_t*>(shared_un);
     int32_t* st_val = st_dest + ITEMS * kThreads;
     int32_t* st_src = st_val + ITEMS * kThreads;
+    float* st_pay = reinterpret_cast<float*>(st_val + (STAGE_SRC ? 2 : 1) * ITEMS * kThreads);
     if (status[kWordStatus] != 0) return;
     // Workgroups are spread over the XCDs round-robin (workgroup b on XCD
     // b % kXcds); each XCD takes a contiguous range of tiles, so the digit runs
@@ -214,15 +215,18 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(SortPass p, int
 
     // this thread's keys, values and carried ids, all loads in flight together
     int32_t key[ITEMS], other[ITEMS], val[ITEMS];
+    float pay[PAY ? ITEMS : 1];
 #pragma unroll
     for (int r = 0; r < ITEMS; ++r) {
         const int64_t i = wbase + r * 64 + lane;
         key[r] = other[r] = 0;
         val[r] = (int32_t)i;
+        if (PAY) pay[r] = 0.f;
         if (i < end) {
             key[r] = p.digit_src[i];
             other[r] = key_is_dest ? (STAGE_SRC ? p.src_in[i] : 0) : p.dest_in[i];
             if (p.val_in) val[r] = p.val_in[i];
+            if (PAY) pay[r] = p.pay_in[i];
         }
     }
     for (int d = tid; d < bins; d += kThreads) {
@@ -295,6 +299,7 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(SortPass p, int
             st_val[lp] = val[r];
             st_dest[lp] = key_is_dest ? key[r] : other[r];
             if (STAGE_SRC) st_src[lp] = key_is_dest ? other[r] : key[r];
+            if (PAY) st_pay[lp] = pay[r];
         }
     }
     __syncthreads();
@@ -311,6 +316,7 @@ __global__ __launch_bounds__(kThreads) void radix_scatter_kernel(SortPass p, int
         p.val_out[pos] = v;
         if (p.dest_out) p.dest_out[pos] = dk;
         if (STAGE_SRC && p.src_out) p.src_out[pos] = sk;
+        if (PAY) p.pay_out[pos] = st_pay[j];
         if (p.inv_out) p.inv_out[v] = pos;
     }
 }
@@ -397,29 +403,30 @@ template <int ITEMS>
 static void launch_scatter_items(const SortPass& p, int64_t n, int tile_log2, const int32_t* hist,
                                  const int32_t* totals, const int32_t* status, int64_t nb, hipStream_t s) {
     const bool stage_src = p.src_out != nullptr || p.digit_src != p.dest_in;
+    const bool pay = p.pay_out != nullptr;  // the host never asks for a payload together with source ids
     const dim3 grid((unsigned)(kXcds * ((nb + kXcds - 1) / kXcds))), block(kThreads);
+#define DR_SC(BINS, SRC, PY)                                                                                      \
+    hipLaunchKernelGGL((radix_scatter_kernel<ITEMS, BINS, SRC, PY>), grid, block, 0, s, p, n, tile_log2, hist, nb, \
+                       totals, status)
     if (p.bits <= 8) {
-        if (stage_src)
-            hipLaunchKernelGGL((radix_scatter_kernel<ITEMS, 256, true>), grid, block, 0, s, p, n, tile_log2, hist, nb,
-                               totals, status);
-        else
-            hipLaunchKernelGGL((radix_scatter_kernel<ITEMS, 256, false>), grid, block, 0, s, p, n, tile_log2, hist,
-                               nb, totals, status);
+        if (stage_src) DR_SC(256, true, false);
+        else if (pay) DR_SC(256, false, true);
+        else DR_SC(256, false, false);
     } else {
-        if (stage_src)
-            hipLaunchKernelGGL((radix_scatter_kernel<ITEMS, kMaxBins, true>), grid, block, 0, s, p, n, tile_log2, hist,
-                               nb, totals, status);
-        else
-            hipLaunchKernelGGL((radix_scatter_kernel<ITEMS, kMaxBins, false>), grid, block, 0, s, p, n, tile_log2,
-                               hist, nb, totals, status);
+        if (stage_src) DR_SC(kMaxBins, true, false);
+        else if (pay) DR_SC(kMaxBins, false, true);
+        else DR_SC(kMaxBins, false, false);
     }
+#undef DR_SC
 }
 
 hipError_t launch_radix_scatter(const SortPass& p, int64_t n, int tile_log2, const int32_t* hist,
                                 const int32_t* totals, const int32_t* status, hipStream_t s) {
     const int64_t nb = tiles_for(n, tile_log2);
     if (nb == 0) return hipSuccess;
-    // the staged tile (dest, value and source id of 2^13 keys: 96 KB) plus
+    if ((p.pay_out != nullptr) != (p.pay_in != nullptr) || (p.pay_out && (p.src_out || p.digit_src != p.dest_in)))
+        return hipErrorInvalidValue;
+    // the staged tile (dest, value and a source id or a payload of 2^13 keys: 96 KB) plus
     // counters stays within a gfx950 workgroup's 160 KB of LDS
     static_assert(kMaxSortTileLog2 <= 13, "staged tile must fit in LDS");
 #define DR_S(IT) launch_scatter_items<IT>(p, n, tile_log2, hist, totals, status, nb, s)

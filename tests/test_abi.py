@@ -138,7 +138,8 @@ def test_sparse_attn_dk_rejects_bad_arguments(lib):
     lib.dr_index_add_workspace_size.restype = ctypes.c_size_t
     lib.dr_index_add_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_int64]
     need = lib.dr_sparse_attn_dk_workspace_size(100, 16, 512, 128)
-    assert need == lib.dr_index_add_workspace_size(1600, 512, 128)
+    # the index_add workspace plus the two buffers the sort moves the 1600 scales through
+    assert need >= lib.dr_index_add_workspace_size(1600, 512, 128) + 2 * 1600 * 4
     ok_args = (FAKE, 512, 128, FAKE, 1, FAKE, FAKE, 100, 16, None, None, FAKE, need, None)
 
     def call(**kw):

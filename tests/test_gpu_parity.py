@@ -338,6 +338,8 @@ def test_index_add_order_example_fp32(dr):
     (257, 7, 64, 100, "f32"),      # ragged chunks, fp32 query rows
     (1000, 64, 128, 300, "bf16"),  # keys chosen by up to 1000 queries: several tiles per key
     (3, 5, 8, 9, "bf16"),          # tiny, most keys untouched
+    (500, 24, 384, 1000, "bf16"),  # three 128-column slices; top-k not a power of two
+    (200, 12, 136, 50, "bf16"),    # a second slice of 8 columns
 ])
 def test_sparse_attn_dk_matches_oracle(dr, nq, topk, H, K, q_dtype):
     say(f"sparse_attn_dk nq={nq} topk={topk} H={H} K={K} {q_dtype}")
