@@ -416,7 +416,8 @@ def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only)
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("segreduce+tilecombine", name,
-                                                 source_digest("segreduce.hip", "internal.h", "device.h")),
+                                                 source_digest("segreduce.hip", "lds_tile.h", "internal.h",
+                                                               "device.h")),
                      "algorithmic_bytes_per_launch": red_bytes, "avg_launch_ms": round(red_ms, 4),
                      "timed_by": "events recorded by the library around the two kernels (dr_set_phase_events)",
                      "whole_call": {"kernel": "dr_index_add_fingerprinted (sort, plan, segreduce, tilecombine, "
@@ -425,8 +426,8 @@ def _index_add(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_only)
                                     "avg_launch_ms": round(det_ms, 4),
                                     "traffic": measured_traffic("dr_index_add_fingerprinted", name,
                                                                 source_digest("sort.hip", "segreduce.hip",
-                                                                              "fingerprint.hip", "internal.h",
-                                                                              "device.h")),
+                                                                              "lds_tile.h", "fingerprint.hip",
+                                                                              "internal.h", "device.h")),
                                     **extra_roofline}},
         "phases_ms": {k: round(v, 4) for k, v in ph.items()},
         **extras,
@@ -502,13 +503,14 @@ def _fused_dk(torch, dr, steps, warmup, want_cpu=False, cpu_seconds=4.0):
     n = nq * topk
     alg = nq * inp.H * 2 + n * 4 + n * 4 + 2 * touched * inp.H * 4  # Q, dS, key ids, dK read-modify-write
     res = {"ms": round(ms, 4), "reused_plan_ms": round(ms_plan, 4), "algorithmic_bytes": alg,
-           "roofline": {"bound": "hbm", "kernel": "segreduce_kernel + tilecombine_kernel (contributions formed "
-                                                  "from Q and dS)",
+           "roofline": {"bound": "hbm", "kernel": "segreduce_gen16_kernel + tilecombine_kernel (contributions "
+                                                  "formed from Q and the sorted dS)",
                         "achieved": round(alg / (red_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(alg / (red_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                         "avg_launch_ms": round(red_ms, 4),
                         "traffic": measured_traffic("segreduce+tilecombine", "sparse_attn_dk_fused",
-                                                    source_digest("segreduce.hip", "internal.h", "device.h")),
+                                                    source_digest("segreduce.hip", "lds_tile.h", "internal.h",
+                                                                  "device.h")),
                         "whole_call": {"achieved": round(alg / (ms * 1e-3) / 1e9, 1),
                                        "frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                        "avg_launch_ms": round(ms, 4)}},
@@ -648,7 +650,8 @@ def _grouped_wgrad(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_o
         "roofline": {"bound": "mfma", "kernel": "wgrad_kernel (with its plan and merge launches)",
                      "achieved": round(tflops, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic("wgrad_kernel", name, source_digest("wgrad.hip", "device.h")),
+                     "traffic": measured_traffic("wgrad_kernel", name,
+                                                 source_digest("wgrad.hip", "lds_tile.h", "device.h")),
                      "algorithmic_flops_per_launch": flops, "hbm_algorithmic_bytes": hbm_bytes,
                      "avg_launch_ms": round(eager_ms, 4)},
         **extras,
