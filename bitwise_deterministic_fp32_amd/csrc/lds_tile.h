@@ -2,10 +2,11 @@
 // (through registers, or with gfx950's 16-byte direct loads) and read MFMA
 // operands back with the transposing LDS read ds_read_b64_tr_b16.
 //
-// Direct loads into LDS are the cheaper instruction stream, but on gfx950 they
-// stream from HBM at about half the rate of plain 16-byte loads into
-// registers (about 3.0 against 6.0 TB/s over the whole chip, whatever the
-// number in flight), so the HBM-bound kernels stage through registers.
+// Direct loads into LDS need no registers, but on gfx950 they stream from HBM
+// at about half the rate of plain 16-byte loads into registers (about 3.0
+// against 6.0 TB/s over the whole chip, whatever the number in flight), so
+// the HBM-bound kernels stage through registers; the weight gradient, whose
+// stages come mostly from L2, loads directly.
 //
 // Tile layout: a stage of TK tokens x COLS columns of bf16 in LDS, row-major
 // (token rows), 16-byte chunks.  For COLS >= 128 the chunk c of row r sits at
@@ -28,11 +29,6 @@ __device__ __forceinline__ int lds_at(int r, int c) {
     return r * COLS + c;
 }
 
-// 16 zero bytes: the source of every direct load of a token row past a stage
-// or a column past the matrix, so those LDS entries are zero and the MFMAs
-// need no masking (a read-only constant).
-__device__ __align__(16) const uint32_t kZero16[4] = {0u, 0u, 0u, 0u};
-
 // A workgroup barrier that orders LDS accesses only.  __syncthreads' fences
 // also cover global memory and so wait for every vector memory operation in
 // flight, the direct loads of later stages included; these wait for LDS only.
@@ -46,33 +42,6 @@ __device__ __forceinline__ void lds_barrier() {
 
 // s_waitcnt on the vector memory count only: vmcnt(n), expcnt and lgkmcnt left alone (gfx9 encoding).
 #define DR_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
-
-// Direct loads of one stage of a token-major matrix into an LDS tile:
-// instructions K0 .. K1-1 of this thread.  Instruction k of wavefront w fills
-// the 1 KB at position 64 (n w + k) of the tile (lane L at 16 L, n the
-// instructions per thread); position p is row p / (COLS / 8), chunk
-// (p % (COLS / 8)) swizzled as in lds_at.  Every instruction is issued, so each
-// stage adds the same count to the wavefront's vector memory counter; lanes
-// whose row is at or past `rows` or whose columns are at or past `cols_total`
-// load 16 zero bytes instead.
-template <int COLS, int TK, int THREADS, int K0 = 0, int K1 = COLS * TK * 2 / 16 / THREADS>
-__device__ __forceinline__ void dma_tile(const uint16_t* __restrict__ src, int64_t ld, int64_t col0,
-                                         int64_t cols_total, int64_t t, int32_t rows, uint16_t* tile) {
-    constexpr int kChunks = COLS / 8;
-    constexpr int kLoads = COLS * TK * 2 / 16 / THREADS;
-    static_assert(kLoads * THREADS * 16 == COLS * TK * 2, "a stage must split evenly into 16-byte loads");
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-    for (int k = K0; k < K1; ++k) {
-        const int pos = 64 * (kLoads * wv + k) + lane;
-        const int r = pos / kChunks;
-        const int cc = COLS >= 128 ? (pos % kChunks) ^ ((r & 3) << 2) : pos % kChunks;
-        const int64_t col = col0 + 8 * cc;
-        const void* from = (r < rows && col < cols_total) ? static_cast<const void*>(src + (t + r) * ld + col)
-                                                          : static_cast<const void*>(kZero16);
-        __builtin_amdgcn_global_load_lds(from, (lds_void*)(tile + 64 * (kLoads * wv + k) * 8), 16, 0, 0);
-    }
-}
 
 // Per-lane element offset, within a tile of COLS columns, of the first
 // transposing read of an MFMA operand whose 32 columns start at `colbase`

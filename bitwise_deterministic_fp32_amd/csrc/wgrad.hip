@@ -25,11 +25,16 @@
 // Stages of 64 tokens go from global memory straight into LDS (16-byte
 // direct loads, gfx950), in their natural token-major layout, into a ring of
 // three stage buffers: the loads of stage j+2 fly while stage j is computed.
-// The MFMA operands (8 consecutive tokens of one column) come out of LDS
-// with the transposing read ds_read_b64_tr_b16 (two per operand): lane j of a
-// 16-lane group receives column j of the group's 4-token x 16-column block.
-// The 16-byte chunks of a row are XOR-swizzled by the row's low two bits, so
-// the four rows a transposing read touches fall in different banks.
+// The loads go through a buffer resource over the stage's token rows, so rows
+// past a slot's end and columns past the matrix read zeros from the range
+// check and each lane's offset is fixed for a tile; the stage's base address
+// is the only per-stage work of the load side.  The MFMA operands (8
+// consecutive tokens of one column) come out of LDS with the transposing read
+// ds_read_b64_tr_b16 (two per operand): lane j of a 16-lane group receives
+// column j of the group's 4-token x 16-column block, and the next k-step's
+// reads are issued before the current k-step's MFMAs.  The 16-byte chunks of
+// a row are XOR-swizzled by the row's low two bits, so the four rows a
+// transposing read touches fall in different banks.
 #include "internal.h"
 #include "lds_tile.h"
 
@@ -75,9 +80,13 @@ __device__ __forceinline__ Item item_of(uint32_t it, const int32_t* __restrict__
     const uint32_t local = it - (uint32_t)p.cum_items[lo];
     const uint32_t tiles = mtiles * ntiles;
     w.c = (int32_t)(local / tiles);
+    // tiles in bands of 8 N tiles, each band M row by M row: 32 consecutive
+    // tiles are 4 M panels x 8 N tiles
     const uint32_t t = local - (uint32_t)w.c * tiles;
-    w.m0 = (int64_t)(t / ntiles) * TM;
-    w.n0 = (int64_t)(t % ntiles) * TN;
+    const uint32_t band = t / (mtiles * 8u), u = t - band * (mtiles * 8u);
+    const uint32_t wb = min(8u, ntiles - band * 8u);
+    w.m0 = (int64_t)(u / wb) * TM;
+    w.n0 = (int64_t)(band * 8u + u % wb) * TN;
     w.t0 = off[lo];
     w.t1 = off[lo + 1];
     const int32_t slots = (int32_t)(((uint32_t)(w.t1 - w.t0) + (uint32_t)split - 1u) / (uint32_t)split);
@@ -89,58 +98,108 @@ __device__ __forceinline__ Item item_of(uint32_t it, const int32_t* __restrict__
     return w;
 }
 
-// One stage of work: the `stage`-th 64 tokens of slot `slot` of an item.
-struct Unit {
-    uint32_t it;
-    int32_t slot;   // within the chunk
-    int32_t stage;
+// The walk of one worker over its stages: item by item (items w, w + P, ...),
+// within an item the chunk's slots in order, within a slot 64-token stages
+// from its first token (the last one short).  An empty group's item is one
+// stage of no tokens.  All fields are wave-uniform.
+struct Cursor {
+    uint32_t it;        // current item
+    int32_t t;          // the stage's first token
+    int32_t te;         // end of the stage's slot
+    int32_t ce;         // end of the item's chunk
+    int64_t m0, n0;     // the item's tile
+    int32_t valid;      // flag: a stage of this worker (0 past its last)
 };
 
-struct Stage {
-    int32_t t;      // first token
-    int32_t rows;   // valid tokens (0 for an empty group)
-    int32_t slot_last, chunk_first, chunk_last;  // flags (0 or 1)
-};
-
-__device__ __forceinline__ Stage stage_of(const Item& w, const Unit& u, int32_t split) {
-    Stage s;
-    s.chunk_first = u.slot == 0;
-    if (w.nslots == 0) {
-        s.t = w.t0;
-        s.rows = 0;
-        s.slot_last = s.chunk_last = 1;
-        return s;
-    }
-    const int32_t ts = w.t0 + (w.slot0 + u.slot) * split;  // the slot's first token
-    const int32_t te = min(w.t1, ts + split);
-    s.t = ts + u.stage * TK;
-    s.rows = min(TK, te - s.t);
-    s.slot_last = s.t + TK >= te;
-    s.chunk_last = s.slot_last && u.slot + 1 == w.nslots;
-    return s;
+__device__ __forceinline__ void cursor_item(Cursor& c, uint32_t it, uint32_t items, const int32_t* __restrict__ off,
+                                            int32_t G, int32_t split, uint32_t mtiles, uint32_t ntiles, int64_t M,
+                                            int64_t N, const Plan& plan, float* __restrict__ out,
+                                            float* __restrict__ chunks) {
+    c.it = it;
+    c.valid = it < items;
+    if (!c.valid) return;
+    const Item w = item_of(it, off, G, split, mtiles, ntiles, M, N, plan, out, chunks);
+    const int64_t cs = (int64_t)w.t0 + (int64_t)w.slot0 * split;
+    c.t = w.nslots ? (int32_t)cs : w.t0;
+    c.ce = w.nslots ? (int32_t)min((int64_t)w.t1, cs + (int64_t)w.nslots * split) : w.t0;
+    c.te = (int32_t)min((int64_t)c.ce, (int64_t)c.t + split);
+    c.m0 = w.m0;
+    c.n0 = w.n0;
 }
 
+// The stage's descriptor for the compute side: token rows (0..64) in bits
+// 0..7, slot-last in bit 8, chunk-last in bit 9.
+__device__ __forceinline__ uint32_t cursor_desc(const Cursor& c) {
+    const int32_t rows = max(0, min(TK, c.te - c.t));
+    const uint32_t slot_last = c.t + TK >= c.te;
+    const uint32_t chunk_last = slot_last && c.te >= c.ce;
+    return (uint32_t)rows | slot_last << 8 | chunk_last << 9;
+}
 
+// The stages of an item: ceil(tokens / TK) per slot of its chunk, one for an
+// empty group (the walk of the kernel's load cursor).
+__device__ __forceinline__ uint32_t item_stages(const Item& w, int32_t split) {
+    if (w.nslots == 0) return 1u;
+    const int64_t cs = (int64_t)w.t0 + (int64_t)w.slot0 * split;
+    const int64_t last = min((int64_t)w.t1, cs + (int64_t)w.nslots * split) - (cs + (int64_t)(w.nslots - 1) * split);
+    return (uint32_t)(w.nslots - 1) * (uint32_t)((split + TK - 1) / TK) + (uint32_t)((last + TK - 1) / TK);
+}
+
+constexpr uint32_t kOutOfRange = 0x80000000u;  // a byte offset past every buffer range
 constexpr int kXLoads = TM * TK * 2 / 16 / kThreads;  // 16-byte direct loads per thread per stage: 8
 constexpr int kYLoads = TN * TK * 2 / 16 / kThreads;  // 4
-constexpr int kLoadsPerStage = kXLoads + kYLoads;
 
-// The operands of one k-step: A for the wavefront's two 32-row blocks of X,
-// B for the four 32-column blocks of dY, by twelve transposing LDS reads.
-// The reads sit in one asm block that also waits for them: the compiler does
-// not see them as reads of LDS written by direct loads, so it adds no wait on
-// the loads still in flight for the next stages (the vector-memory wait before
-// the stage's barrier is what makes this stage's data valid), and no output
-// register is used before its read is complete.
-struct KOps {
-    bf16x8 a[2], b[4];
+// Byte offset of this thread's direct-load piece k of a stage, from the
+// stage's first token row at the tile's first column: instruction k of
+// wavefront w fills the 1 KB at position 64 (n w + k) of the LDS tile (lane L
+// at 16 L, n the instructions per thread), position p being token row
+// p / (COLS / 8) and 16-byte chunk p % (COLS / 8), swizzled as in lds_at.
+// A chunk whose columns are past the matrix gets an offset past every range.
+template <int COLS>
+__device__ __forceinline__ uint32_t piece_offset(int k, int64_t ld, int64_t col0, int64_t cols_total) {
+    constexpr int kChunks = COLS / 8;
+    constexpr int kLoads = COLS * TK * 2 / 16 / kThreads;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int pos = 64 * (kLoads * wv + k) + lane;
+    const int r = pos / kChunks;
+    const int cc = (pos % kChunks) ^ ((r & 3) << 2);
+    return col0 + 8 * cc < cols_total ? (uint32_t)(r * ld * 2 + 16 * cc) : kOutOfRange;
+}
+
+// The direct loads of one stage of a token-major matrix into an LDS tile,
+// through a buffer resource over the stage's rows: its range check returns
+// zeros for the token rows at or past `rows` and for the out-of-range offset.
+template <int COLS>
+__device__ __forceinline__ void dma_stage(const uint16_t* base, int64_t ld, int32_t rows, const uint32_t* voff,
+                                          uint16_t* tile) {
+    constexpr int kLoads = COLS * TK * 2 / 16 / kThreads;
+    const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    // the stage's base and size are wave-uniform: say so, so that the
+    // resource is built in scalar registers once
+    const uint64_t bp = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)bp);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(bp >> 32));
+    const int nbytes = __builtin_amdgcn_readfirstlane((int)(rows * ld * 2));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<uint16_t*>((uint64_t)hi << 32 | lo), 0, nbytes, 0x00020000);
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(tile + 64 * (kLoads * wv + k) * 8), 16, voff[k], 0,
+                                                 0, 0);
+}
+
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+struct KRaw {
+    u32x2v r[12];
 };
 
-__device__ __forceinline__ KOps read_kstep(const uint16_t* xt, const uint16_t* yt, const int (&xoff)[2],
-                                           const int (&yoff)[4], int ks) {
-    typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+// Issues the twelve transposing reads of k-step ks; their registers are not
+// valid until wait_kstep.  The compiler does not see them as LDS reads (so it
+// adds no wait on the direct loads in flight for later stages); wait_kstep
+// takes the registers as operands, so no use of them moves above the wait.
+__device__ __forceinline__ void issue_kstep(KRaw& k, const uint16_t* xt, const uint16_t* yt, const int (&xoff)[2],
+                                            const int (&yoff)[4], int ks) {
     const uint32_t xb = lds_byte_address(xt, 16 * ks * TM), yb = lds_byte_address(yt, 16 * ks * TN);
-    u32x2v r[12];
     const uint32_t a0 = xb + 2 * xoff[0], a1 = xb + 2 * xoff[1];
     const uint32_t b0 = yb + 2 * yoff[0], b1 = yb + 2 * yoff[1], b2 = yb + 2 * yoff[2], b3 = yb + 2 * yoff[3];
     asm volatile(
@@ -155,37 +214,52 @@ __device__ __forceinline__ KOps read_kstep(const uint16_t* xt, const uint16_t* y
         "ds_read_b64_tr_b16 %8, %16\n"
         "ds_read_b64_tr_b16 %9, %16 offset:1024\n"
         "ds_read_b64_tr_b16 %10, %17\n"
-        "ds_read_b64_tr_b16 %11, %17 offset:1024\n"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]), "=&v"(r[7]),
-          "=&v"(r[8]), "=&v"(r[9]), "=&v"(r[10]), "=&v"(r[11])
+        "ds_read_b64_tr_b16 %11, %17 offset:1024"
+        : "=&v"(k.r[0]), "=&v"(k.r[1]), "=&v"(k.r[2]), "=&v"(k.r[3]), "=&v"(k.r[4]), "=&v"(k.r[5]), "=&v"(k.r[6]),
+          "=&v"(k.r[7]), "=&v"(k.r[8]), "=&v"(k.r[9]), "=&v"(k.r[10]), "=&v"(k.r[11])
         : "v"(a0), "v"(a1), "v"(b0), "v"(b1), "v"(b2), "v"(b3)
         : "memory");
-    KOps o;
+}
+
+__device__ __forceinline__ void wait_kstep(KRaw& k) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(k.r[0]), "+v"(k.r[1]), "+v"(k.r[2]), "+v"(k.r[3]), "+v"(k.r[4]), "+v"(k.r[5]), "+v"(k.r[6]),
+                   "+v"(k.r[7]), "+v"(k.r[8]), "+v"(k.r[9]), "+v"(k.r[10]), "+v"(k.r[11])
+                 :
+                 : "memory");
+}
+
+__device__ __forceinline__ void mfma_kstep(f32x16 (&acc)[2][4], const KRaw& k) {
     typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+    bf16x8 a[2], b[4];
 #pragma unroll
     for (int q = 0; q < 6; ++q) {
-        const u32x4v v{r[2 * q][0], r[2 * q][1], r[2 * q + 1][0], r[2 * q + 1][1]};
-        if (q < 2) o.a[q] = __builtin_bit_cast(bf16x8, v);
-        else o.b[q - 2] = __builtin_bit_cast(bf16x8, v);
+        const u32x4v v{k.r[2 * q][0], k.r[2 * q][1], k.r[2 * q + 1][0], k.r[2 * q + 1][1]};
+        if (q < 2) a[q] = __builtin_bit_cast(bf16x8, v);
+        else b[q - 2] = __builtin_bit_cast(bf16x8, v);
     }
-    return o;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
 }
 
 // The chunk sum s (or the empty group's zero tile) to its destination.  Lane
 // (i, h) holds column 32nb + i and rows 8(v/4) + 4h + v%4 of each 32x32 block.
 // One 32x32 block at a time, walking one row pointer, so that few addresses
 // are live at once.
-__device__ __forceinline__ void store_tile(const f32x16 (&s)[2][4], const Item& w, int64_t M, int64_t N) {
+__device__ __forceinline__ void store_tile(const f32x16 (&s)[2][4], float* dst, int64_t m0, int64_t n0, int64_t M,
+                                           int64_t N) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     const int i = lane & 31, h = lane >> 5;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
-            const int64_t m_first = w.m0 + 64 * wv + 32 * mb + 4 * h;
-            const int64_t n = w.n0 + 32 * nb + i;
-            float* p = w.dst + m_first * N + n;
+            const int64_t m_first = m0 + 64 * wv + 32 * mb + 4 * h;
+            const int64_t n = n0 + 32 * nb + i;
+            float* p = dst + m_first * N + n;
             const bool col_ok = n < N;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
@@ -197,122 +271,16 @@ __device__ __forceinline__ void store_tile(const f32x16 (&s)[2][4], const Item& 
         }
 }
 
-struct Work {
-    Item w;
-    Stage s;
-    Unit u;
-    int32_t valid;  // flag (0 or 1)
-};
-
-__device__ __forceinline__ Work advance(const Work& c, uint32_t P, uint32_t items, const int32_t* __restrict__ off,
-                                        int32_t G, int32_t split, uint32_t mtiles, uint32_t ntiles, int64_t M,
-                                        int64_t N, const Plan& plan, float* __restrict__ out,
-                                        float* __restrict__ chunks) {
-    Work n = c;
-    if (!c.valid) return n;
-    if (!c.s.slot_last) {
-        n.u.stage += 1;
-    } else if (!c.s.chunk_last) {
-        n.u.slot += 1;
-        n.u.stage = 0;
-    } else {
-        n.u = Unit{c.u.it + P, 0, 0};
-    }
-    n.valid = n.u.it < items;
-    if (!n.valid) return n;
-    if (n.u.it != c.u.it) n.w = item_of(n.u.it, off, G, split, mtiles, ntiles, M, N, plan, out, chunks);
-    n.s = stage_of(n.w, n.u, split);
-    return n;
-}
-
-// s_waitcnt with only the vector memory count: vmcnt(n), expcnt and lgkmcnt left alone (gfx9 encoding)
-
-// One stage in ring buffer B: wait for its loads, issue the loads of the
-// stage two ahead into buffer (B + 2) % 3, compute, and close the slot and
-// the chunk when they end.  Returns false when the worker has no more work.
-template <int B>
-__device__ __forceinline__ bool step(Work& cur, Work& nx1, const uint16_t* __restrict__ xrd,
-                                     const uint16_t* __restrict__ yrd, uint16_t* __restrict__ xdma,
-                                     uint16_t* __restrict__ ydma,
-                                     f32x16 (&acc)[2][4], f32x16 (&sum)[2][4], const uint16_t* __restrict__ X,
-                                     const uint16_t* __restrict__ dY, int64_t K, int64_t M, int64_t N, uint32_t P,
-                                     uint32_t items, const int32_t* __restrict__ off, int32_t G, int32_t split,
-                                     uint32_t mtiles, uint32_t ntiles, const Plan& plan, float* __restrict__ out,
-                                     float* __restrict__ chunks) {
-    if (!cur.valid) return false;
-    // this stage's loads are done once at most the next stage's are outstanding
-    if (nx1.valid) DR_WAIT_VMCNT(kLoadsPerStage);
-    else DR_WAIT_VMCNT(0);
-    // Every wavefront's loads of this stage have landed (each waited for its own
-    // above) and every wavefront is done reading buffer (B + 2) % 3 (its
-    // operands were consumed by the previous stage's MFMAs).  A plain barrier:
-    // the workgroup fences of __syncthreads would wait for the loads still in
-    // flight for the next two stages.
-    __builtin_amdgcn_s_barrier();
-    const Work nx2 = advance(nx1, P, items, off, G, split, mtiles, ntiles, M, N, plan, out, chunks);
-    if (nx2.valid) {
-        dma_tile<TM, TK, kThreads>(X, M, nx2.w.m0, M, nx2.s.t, nx2.s.rows, xdma);
-        dma_tile<TN, TK, kThreads>(dY, N, nx2.w.n0, N, nx2.s.t, nx2.s.rows, ydma);
-    }
-    const int wv = threadIdx.x >> 6;
-    const int ksteps = (cur.s.rows + 15) >> 4;
-    int xoff[2], yoff[4];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) xoff[mb] = operand_offset<TM>(64 * wv + 32 * mb);
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb) yoff[nb] = operand_offset<TN>(32 * nb);
-    if (ksteps > 0) {
-        KOps cur_ops = read_kstep(xrd, yrd, xoff, yoff, 0);
-#pragma unroll
-        for (int ks = 0; ks < TK / 16; ++ks) {
-            if (ks >= ksteps) break;
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < 4; ++nb)
-                    acc[mb][nb] =
-                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur_ops.a[mb], cur_ops.b[nb], acc[mb][nb], 0, 0, 0);
-            // the next k-step's reads run while these MFMAs execute
-            __builtin_amdgcn_sched_barrier(0);
-            if (ks + 1 < TK / 16 && ks + 1 < ksteps) cur_ops = read_kstep(xrd, yrd, xoff, yoff, ks + 1);
-        }
-    }
-    if (cur.s.slot_last) {
-        // the slot's partial joins the chunk's left-to-right sum, which starts
-        // as -0.0 (an exact additive identity: -0.0 + x is x for every x, -0.0
-        // included), so the first slot's partial enters unchanged
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    sum[mb][nb][v] = sum[mb][nb][v] + acc[mb][nb][v];
-                    acc[mb][nb][v] = 0.f;
-                }
-                // one 16-value block at a time: keeps the copies out of the accumulators few
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        if (cur.s.chunk_last) {
-            store_tile(sum, cur.w, M, N);
-            DR_WAIT_VMCNT(0);  // stores count too: settle the counter so the next waits stay exact
-#pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) sum[mb][nb][v] = neg_zero();
-        }
-    }
-    cur = nx1;
-    nx1 = nx2;
-    return true;
-}
-
 // Persistent workgroups; worker w takes items w, w + P, w + 2P, ...  Logical
 // workers are numbered XCD by XCD (workgroup b runs on XCD b mod 8), so the
-// items in flight at one time on one XCD are neighbouring tiles: the 16 N
-// tiles of one M panel share their X stage in that XCD's L2.
+// 32 items in flight at one time on one XCD are 4 M panels x 8 N tiles of one
+// group: each X stage is read by 8 of them and each dY stage by 4, mostly
+// from that XCD's L2.
+//
+// Stages go through a ring of three LDS buffers: the direct loads of stage
+// j + 2 are issued while stage j is computed.  The load side walks a cursor
+// two stages ahead of the compute side, which sees each stage as a
+// descriptor (rows and slot and chunk ends) and the item it belongs to.
 __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(const uint16_t* __restrict__ X,
                                                             const uint16_t* __restrict__ dY, int64_t K, int64_t M,
                                                             int64_t N, const int32_t* __restrict__ off, int32_t G,
@@ -330,19 +298,50 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(const uint16_t* __re
     const uint32_t b = blockIdx.x;
     const uint32_t wkr = (P % 8 == 0) ? (b % 8) * (P / 8) + b / 8 : b;
     if (wkr >= items) return;
+    const int wv = threadIdx.x >> 6;
+    int xoff[2], yoff[4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) xoff[mb] = operand_offset<TM>(64 * wv + 32 * mb);
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) yoff[nb] = operand_offset<TN>(32 * nb);
 
-    Work cur;
-    cur.u = Unit{wkr, 0, 0};
-    cur.valid = 1;
-    cur.w = item_of(wkr, off, G, split, mtiles, ntiles, M, N, plan, out, chunks);
-    cur.s = stage_of(cur.w, cur.u, split);
-    Work nx1 = advance(cur, P, items, off, G, split, mtiles, ntiles, M, N, plan, out, chunks);
-    dma_tile<TM, TK, kThreads>(X, M, cur.w.m0, M, cur.s.t, cur.s.rows, xs[0]);
-    dma_tile<TN, TK, kThreads>(dY, N, cur.w.n0, N, cur.s.t, cur.s.rows, ys[0]);
-    if (nx1.valid) {
-        dma_tile<TM, TK, kThreads>(X, M, nx1.w.m0, M, nx1.s.t, nx1.s.rows, xs[1]);
-        dma_tile<TN, TK, kThreads>(dY, N, nx1.w.n0, N, nx1.s.t, nx1.s.rows, ys[1]);
-    }
+    // The load side: its cursor and the piece offsets of its item's tile.
+    Cursor ld;
+    uint32_t xv[kXLoads], yv[kYLoads];
+    auto tile_offsets = [&]() {
+#pragma unroll
+        for (int k = 0; k < kXLoads; ++k) xv[k] = piece_offset<TM>(k, M, ld.m0, M);
+#pragma unroll
+        for (int k = 0; k < kYLoads; ++k) yv[k] = piece_offset<TN>(k, N, ld.n0, N);
+    };
+    cursor_item(ld, wkr, items, off, G, split, mtiles, ntiles, M, N, plan, out, chunks);
+    tile_offsets();
+    // Every call issues the same loads (a stage past the worker's last has no
+    // rows and reads zeros), so each stage adds the same count to the vector
+    // memory counter.
+    auto issue = [&](uint16_t* xt, uint16_t* yt) {
+        const int32_t rows = ld.valid ? max(0, min(TK, ld.te - ld.t)) : 0;
+        const int64_t t = ld.valid ? ld.t : 0, m0 = ld.valid ? ld.m0 : 0, n0 = ld.valid ? ld.n0 : 0;
+        dma_stage<TM>(X + t * M + m0, M, rows, xv, xt);
+        dma_stage<TN>(dY + t * N + n0, N, rows, yv, yt);
+    };
+    auto advance = [&]() {
+        if (!ld.valid) return;
+        if (ld.t + TK < ld.te) {
+            ld.t += TK;
+        } else if (ld.te < ld.ce) {
+            ld.t = ld.te;
+            ld.te = (int32_t)min((int64_t)ld.ce, (int64_t)ld.te + split);
+        } else {
+            cursor_item(ld, ld.it + P, items, off, G, split, mtiles, ntiles, M, N, plan, out, chunks);
+            if (ld.valid) tile_offsets();
+        }
+    };
+
+    // the worker's stage count, so that the loop below has no exit inside its three steps
+    uint32_t stages = 0;
+    for (uint32_t it = wkr; it < items; it += P)
+        stages += item_stages(item_of(it, off, G, split, mtiles, ntiles, M, N, plan, out, chunks), split);
 
     f32x16 acc[2][4], sum[2][4];
 #pragma unroll
@@ -354,17 +353,84 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(const uint16_t* __re
                 acc[mb][nb][v] = 0.f;
                 sum[mb][nb][v] = neg_zero();
             }
-    while (true) {
-        if (!step<0>(cur, nx1, xs[0], ys[0], xs[2], ys[2], acc, sum, X, dY, K, M, N, P, items,
-                     off, G, split, mtiles, ntiles, plan, out, chunks))
-            break;
-        if (!step<1>(cur, nx1, xs[1], ys[1], xs[0], ys[0], acc, sum, X, dY, K, M, N, P, items,
-                     off, G, split, mtiles, ntiles, plan, out, chunks))
-            break;
-        if (!step<2>(cur, nx1, xs[2], ys[2], xs[1], ys[1], acc, sum, X, dY, K, M, N, P, items,
-                     off, G, split, mtiles, ntiles, plan, out, chunks))
-            break;
+
+    // the compute side's view of the two stages in flight
+    uint32_t d_cur = cursor_desc(ld), it_cur = ld.it;
+    issue(xs[0], ys[0]);
+    advance();
+    uint32_t d_nx1 = cursor_desc(ld), it_nx1 = ld.it;
+    issue(xs[1], ys[1]);
+    advance();
+
+    auto step = [&](const uint16_t* xt, const uint16_t* yt, uint16_t* xn, uint16_t* yn) {
+        // This stage's pieces have landed once at most the next stage's are
+        // outstanding; after the barrier every wavefront's have, and every
+        // wavefront is done reading xn / yn (the previous stage's buffers,
+        // whose operands its MFMAs consumed).  A plain barrier: the workgroup
+        // fences of __syncthreads would wait for the loads still in flight.
+        DR_WAIT_VMCNT(kXLoads + kYLoads);
+        __builtin_amdgcn_s_barrier();
+        const uint32_t d_nx2 = cursor_desc(ld), it_nx2 = ld.it;
+        issue(xn, yn);
+        advance();
+        const int ksteps = (int)((d_cur & 0xFFu) + 15) >> 4;
+        if (ksteps > 0) {
+            KRaw kr[2];
+            issue_kstep(kr[0], xt, yt, xoff, yoff, 0);
+            wait_kstep(kr[0]);
+#pragma unroll
+            for (int ks = 0; ks < TK / 16; ++ks) {
+                if (ks >= ksteps) break;
+                const bool more = ks + 1 < TK / 16 && ks + 1 < ksteps;
+                // the next k-step's reads run while these MFMAs execute
+                if (more) issue_kstep(kr[(ks + 1) & 1], xt, yt, xoff, yoff, ks + 1);
+                __builtin_amdgcn_sched_barrier(0);
+                mfma_kstep(acc, kr[ks & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (more) wait_kstep(kr[(ks + 1) & 1]);
+            }
+        }
+        if (d_cur & 0x100u) {
+            // the slot's partial joins the chunk's left-to-right sum, which
+            // starts as -0.0 (an exact additive identity: -0.0 + x is x for
+            // every x, -0.0 included), so the first slot's partial enters
+            // unchanged
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        sum[mb][nb][v] = sum[mb][nb][v] + acc[mb][nb][v];
+                        acc[mb][nb][v] = 0.f;
+                    }
+                    // one 16-value block at a time: keeps the copies out of the accumulators few
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            if (d_cur & 0x200u) {
+                const Item w = item_of(it_cur, off, G, split, mtiles, ntiles, M, N, plan, out, chunks);
+                store_tile(sum, w.dst, w.m0, w.n0, M, N);
+#pragma unroll
+                for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) sum[mb][nb][v] = neg_zero();
+            }
+        }
+        d_cur = d_nx1;
+        it_cur = it_nx1;
+        d_nx1 = d_nx2;
+        it_nx1 = it_nx2;
+    };
+    uint32_t j = 0;
+    for (; j + 3 <= stages; j += 3) {
+        step(xs[0], ys[0], xs[2], ys[2]);
+        step(xs[1], ys[1], xs[0], ys[0]);
+        step(xs[2], ys[2], xs[1], ys[1]);
     }
+    if (j < stages) step(xs[0], ys[0], xs[2], ys[2]);
+    if (j + 1 < stages) step(xs[1], ys[1], xs[0], ys[0]);
 }
 
 // out[g] = the pairwise tree over the group's chunk sums, in chunk order
