@@ -17,8 +17,12 @@
 // Where the thin split-K kernel streams X once past 32-column tiles, here a
 // workgroup owns a 256 (M) x 128 (N) output tile of one chunk of one group and
 // walks the chunk's slots: each slot's partial is accumulated in registers
-// (4 wavefronts x 64 x 128), then added into the chunk's running sum, also in
-// registers, so the partials never go to memory.  A group of at most 8 slots
+// (8 wavefronts, a 4 x 2 grid of 64 x 64 blocks), then added into the chunk's
+// running sum, also in registers, so the partials never go to memory.  The
+// two sets take 128 registers per lane, so two wavefronts fit on each SIMD
+// and one's waits are covered by the other's MFMAs (with 64 x 128 blocks the
+// sets took 256 registers and one wavefront per SIMD ran 1.3 times slower,
+// although it reads less from LDS per MFMA).  A group of at most 8 slots
 // writes dW[g] directly; a longer group writes its chunk sums to a workspace,
 // and a merge kernel applies the pairwise tree over them in chunk order.
 //
@@ -47,7 +51,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int TM = 256;          // output rows (M) per workgroup
 constexpr int TN = 128;          // output columns (N) per workgroup
 constexpr int TK = 64;           // tokens per stage
-constexpr int kThreads = 256;    // 4 wavefronts, each 64 (M) x 128 (N)
+constexpr int kThreads = 512;    // 8 wavefronts, each 64 (M) x 64 (N)
 constexpr int kChunk = 8;        // slots summed left to right before the pairwise tree
 
 struct Plan {
@@ -190,7 +194,7 @@ __device__ __forceinline__ void dma_stage(const uint16_t* base, int64_t ld, int3
 
 typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
 struct KRaw {
-    u32x2v r[12];
+    u32x2v r[8];
 };
 
 // Issues the twelve transposing reads of k-step ks; their registers are not
@@ -198,42 +202,38 @@ struct KRaw {
 // adds no wait on the direct loads in flight for later stages); wait_kstep
 // takes the registers as operands, so no use of them moves above the wait.
 __device__ __forceinline__ void issue_kstep(KRaw& k, const uint16_t* xt, const uint16_t* yt, const int (&xoff)[2],
-                                            const int (&yoff)[4], int ks) {
+                                            const int (&yoff)[2], int ks) {
     const uint32_t xb = lds_byte_address(xt, 16 * ks * TM), yb = lds_byte_address(yt, 16 * ks * TN);
     const uint32_t a0 = xb + 2 * xoff[0], a1 = xb + 2 * xoff[1];
-    const uint32_t b0 = yb + 2 * yoff[0], b1 = yb + 2 * yoff[1], b2 = yb + 2 * yoff[2], b3 = yb + 2 * yoff[3];
+    const uint32_t b0 = yb + 2 * yoff[0], b1 = yb + 2 * yoff[1];
     asm volatile(
-        "ds_read_b64_tr_b16 %0, %12\n"
-        "ds_read_b64_tr_b16 %1, %12 offset:2048\n"
-        "ds_read_b64_tr_b16 %2, %13\n"
-        "ds_read_b64_tr_b16 %3, %13 offset:2048\n"
-        "ds_read_b64_tr_b16 %4, %14\n"
-        "ds_read_b64_tr_b16 %5, %14 offset:1024\n"
-        "ds_read_b64_tr_b16 %6, %15\n"
-        "ds_read_b64_tr_b16 %7, %15 offset:1024\n"
-        "ds_read_b64_tr_b16 %8, %16\n"
-        "ds_read_b64_tr_b16 %9, %16 offset:1024\n"
-        "ds_read_b64_tr_b16 %10, %17\n"
-        "ds_read_b64_tr_b16 %11, %17 offset:1024"
+        "ds_read_b64_tr_b16 %0, %8\n"
+        "ds_read_b64_tr_b16 %1, %8 offset:2048\n"
+        "ds_read_b64_tr_b16 %2, %9\n"
+        "ds_read_b64_tr_b16 %3, %9 offset:2048\n"
+        "ds_read_b64_tr_b16 %4, %10\n"
+        "ds_read_b64_tr_b16 %5, %10 offset:1024\n"
+        "ds_read_b64_tr_b16 %6, %11\n"
+        "ds_read_b64_tr_b16 %7, %11 offset:1024"
         : "=&v"(k.r[0]), "=&v"(k.r[1]), "=&v"(k.r[2]), "=&v"(k.r[3]), "=&v"(k.r[4]), "=&v"(k.r[5]), "=&v"(k.r[6]),
-          "=&v"(k.r[7]), "=&v"(k.r[8]), "=&v"(k.r[9]), "=&v"(k.r[10]), "=&v"(k.r[11])
-        : "v"(a0), "v"(a1), "v"(b0), "v"(b1), "v"(b2), "v"(b3)
+          "=&v"(k.r[7])
+        : "v"(a0), "v"(a1), "v"(b0), "v"(b1)
         : "memory");
 }
 
 __device__ __forceinline__ void wait_kstep(KRaw& k) {
     asm volatile("s_waitcnt lgkmcnt(0)"
                  : "+v"(k.r[0]), "+v"(k.r[1]), "+v"(k.r[2]), "+v"(k.r[3]), "+v"(k.r[4]), "+v"(k.r[5]), "+v"(k.r[6]),
-                   "+v"(k.r[7]), "+v"(k.r[8]), "+v"(k.r[9]), "+v"(k.r[10]), "+v"(k.r[11])
+                   "+v"(k.r[7])
                  :
                  : "memory");
 }
 
-__device__ __forceinline__ void mfma_kstep(f32x16 (&acc)[2][4], const KRaw& k) {
+__device__ __forceinline__ void mfma_kstep(f32x16 (&acc)[2][2], const KRaw& k) {
     typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-    bf16x8 a[2], b[4];
+    bf16x8 a[2], b[2];
 #pragma unroll
-    for (int q = 0; q < 6; ++q) {
+    for (int q = 0; q < 4; ++q) {
         const u32x4v v{k.r[2 * q][0], k.r[2 * q][1], k.r[2 * q + 1][0], k.r[2 * q + 1][1]};
         if (q < 2) a[q] = __builtin_bit_cast(bf16x8, v);
         else b[q - 2] = __builtin_bit_cast(bf16x8, v);
@@ -241,7 +241,7 @@ __device__ __forceinline__ void mfma_kstep(f32x16 (&acc)[2][4], const KRaw& k) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < 2; ++nb)
             acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
 }
 
@@ -249,16 +249,17 @@ __device__ __forceinline__ void mfma_kstep(f32x16 (&acc)[2][4], const KRaw& k) {
 // (i, h) holds column 32nb + i and rows 8(v/4) + 4h + v%4 of each 32x32 block.
 // One 32x32 block at a time, walking one row pointer, so that few addresses
 // are live at once.
-__device__ __forceinline__ void store_tile(const f32x16 (&s)[2][4], float* dst, int64_t m0, int64_t n0, int64_t M,
+__device__ __forceinline__ void store_tile(const f32x16 (&s)[2][2], float* dst, int64_t m0, int64_t n0, int64_t M,
                                            int64_t N) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int wm = wv & 3, wn = wv >> 2;
     const int i = lane & 31, h = lane >> 5;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            const int64_t m_first = m0 + 64 * wv + 32 * mb + 4 * h;
-            const int64_t n = n0 + 32 * nb + i;
+        for (int nb = 0; nb < 2; ++nb) {
+            const int64_t m_first = m0 + 64 * wm + 32 * mb + 4 * h;
+            const int64_t n = n0 + 64 * wn + 32 * nb + i;
             float* p = dst + m_first * N + n;
             const bool col_ok = n < N;
 #pragma unroll
@@ -299,11 +300,11 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(const uint16_t* __re
     const uint32_t wkr = (P % 8 == 0) ? (b % 8) * (P / 8) + b / 8 : b;
     if (wkr >= items) return;
     const int wv = threadIdx.x >> 6;
-    int xoff[2], yoff[4];
+    int xoff[2], yoff[2];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) xoff[mb] = operand_offset<TM>(64 * wv + 32 * mb);
+    for (int mb = 0; mb < 2; ++mb) xoff[mb] = operand_offset<TM>(64 * (wv & 3) + 32 * mb);
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) yoff[nb] = operand_offset<TN>(32 * nb);
+    for (int nb = 0; nb < 2; ++nb) yoff[nb] = operand_offset<TN>(64 * (wv >> 2) + 32 * nb);
 
     // The load side: its cursor and the piece offsets of its item's tile.
     Cursor ld;
@@ -343,11 +344,11 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(const uint16_t* __re
     for (uint32_t it = wkr; it < items; it += P)
         stages += item_stages(item_of(it, off, G, split, mtiles, ntiles, M, N, plan, out, chunks), split);
 
-    f32x16 acc[2][4], sum[2][4];
+    f32x16 acc[2][2], sum[2][2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 acc[mb][nb][v] = 0.f;
@@ -398,7 +399,7 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(const uint16_t* __re
 #pragma unroll
             for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) {
+                for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         sum[mb][nb][v] = sum[mb][nb][v] + acc[mb][nb][v];
@@ -413,7 +414,7 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(const uint16_t* __re
 #pragma unroll
                 for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-                    for (int nb = 0; nb < 4; ++nb)
+                    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
                         for (int v = 0; v < 16; ++v) sum[mb][nb][v] = neg_zero();
             }
