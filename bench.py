@@ -351,7 +351,7 @@ def main():
         import bench_workloads
         res = bench_workloads.run(torch, dr, name, args.steps, args.warmup, args.cpu_seconds,
                                   not args.no_cpu_baseline, args.step_only)
-    if not args.step_only:
+    if not args.step_only and res["roofline"]["unit"] == "GB/s":
         res["roofline"].update(copy_ceiling(torch, res["roofline"]["achieved"]))
     others = {}
     if name == "moe_combine" and not args.step_only and not args.no_other_configs:

@@ -641,6 +641,10 @@ def _grouped_wgrad(torch, dr, name, steps, warmup, cpu_seconds, want_cpu, step_o
     res = {
         "ms_per_step": ms_step,
         "value": tflops,
+        # this line's value is MFMA work, not bytes
+        "metric": "grouped weight gradient bf16 MFMA TFLOP/s (private token slots merged in slot order)",
+        "unit": "TFLOP/s",
+        "dtype": "bf16 products, f32 accumulation",
         "timing": "step replayed from a HIP graph; the roofline uses the eager per-call time",
         "eager_ms_per_step": round(eager_ms, 4),
         "config": {"workload": f"{name}: dW[g] = X_g^T dY_g for the {G} hottest experts of the MoE routing "
