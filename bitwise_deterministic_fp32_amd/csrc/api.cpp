@@ -843,6 +843,9 @@ dr_status dr_grouped_wgrad(const void* X, const void* dY, int64_t K, int64_t M, 
                     what);
     if (!aligned(X, 16) || !aligned(dY, 16) || !aligned(out, 16) || !aligned(group_offsets, 4) || !aligned(ws, 16))
         return fail(DR_ERR_INVALID_ARGUMENT, "%s: X, dY, out and ws must be 16-byte aligned", what);
+    // a stage's buffer range (64 token rows) is a 32-bit byte count
+    if (M > ((int64_t)1 << 23) || N > ((int64_t)1 << 23))
+        return fail(DR_ERR_UNSUPPORTED, "%s: M and N must be at most 2^23", what);
     // token indices are int32 on the device; work items are counted in 31 bits
     if (K >= kMaxN - split_tokens) return fail(DR_ERR_UNSUPPORTED, "%s: K too large for one call", what);
     if (dr::wgrad_max_items(K, num_groups, split_tokens, M, N) >= ((int64_t)1 << 31))

@@ -384,8 +384,8 @@ dr_status dr_grouped_splitk_reduce(const float* partials, int64_t partial_slots,
  * section 3.3, grouped-GEMM weight gradient as a determinism hotspot).
  *
  *   X[K, M], dY[K, N]    bf16 (bit patterns), expert-major token rows, 16-byte
- *                        aligned; M and N multiples of 8 (other shapes:
- *                        dr_grouped_splitk_gemm_tn).
+ *                        aligned; M and N multiples of 8 and at most 2^23
+ *                        (other shapes: dr_grouped_splitk_gemm_tn).
  *   group_offsets[G+1]   int32, device: non-decreasing within [0, K].
  *   out[G, M, N]         fp32, written; a group with no token gets zeros.
  *   ws                   >= dr_grouped_wgrad_workspace_size(K, G, split_tokens,

@@ -393,6 +393,8 @@ def test_grouped_wgrad_rejects_bad_arguments(lib):
     assert call(split=0) == DR_ERR_INVALID_ARGUMENT
     assert call(M=500) == DR_ERR_UNSUPPORTED          # not a multiple of 8
     assert call(N=20) == DR_ERR_UNSUPPORTED
+    assert call(M=(1 << 23) + 8) == DR_ERR_UNSUPPORTED  # a stage's byte range must fit 32 bits
+    assert call(N=(1 << 23) + 8) == DR_ERR_UNSUPPORTED
     assert call(X=FAKE + 8) == DR_ERR_INVALID_ARGUMENT  # 16-byte alignment
     assert call(ws_bytes=need - 1) == DR_ERR_WORKSPACE_TOO_SMALL
     assert call(K=(1 << 31) - 100) == DR_ERR_UNSUPPORTED
