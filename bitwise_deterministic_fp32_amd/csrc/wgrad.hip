@@ -21,7 +21,7 @@
 // running sum, also in registers, so the partials never go to memory.  The
 // two sets take 128 registers per lane, so two wavefronts fit on each SIMD
 // and one's waits are covered by the other's MFMAs (with 64 x 128 blocks the
-// sets took 256 registers and one wavefront per SIMD ran 1.3 times slower,
+// sets took 256 registers and one wavefront per SIMD ran about 1.25 times slower,
 // although it reads less from LDS per MFMA).  A group of at most 8 slots
 // writes dW[g] directly; a longer group writes its chunk sums to a workspace,
 // and a merge kernel applies the pairwise tree over them in chunk order.
@@ -197,7 +197,7 @@ struct KRaw {
     u32x2v r[8];
 };
 
-// Issues the twelve transposing reads of k-step ks; their registers are not
+// Issues the eight transposing reads of k-step ks; their registers are not
 // valid until wait_kstep.  The compiler does not see them as LDS reads (so it
 // adds no wait on the direct loads in flight for later stages); wait_kstep
 // takes the registers as operands, so no use of them moves above the wait.
@@ -245,8 +245,9 @@ __device__ __forceinline__ void mfma_kstep(f32x16 (&acc)[2][2], const KRaw& k) {
             acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb], b[nb], acc[mb][nb], 0, 0, 0);
 }
 
-// The chunk sum s (or the empty group's zero tile) to its destination.  Lane
-// (i, h) holds column 32nb + i and rows 8(v/4) + 4h + v%4 of each 32x32 block.
+// The chunk sum s (or the empty group's zero tile) to its destination.  In
+// wavefront (wm, wn), lane (i, h) holds column 64 wn + 32 nb + i and rows
+// 64 wm + 32 mb + 8 (v/4) + 4h + v%4 of the tile.
 // One 32x32 block at a time, walking one row pointer, so that few addresses
 // are live at once.
 __device__ __forceinline__ void store_tile(const f32x16 (&s)[2][2], float* dst, int64_t m0, int64_t n0, int64_t M,
