@@ -136,6 +136,43 @@ def test_splitk_full(dr):
     assert dr.fingerprint_value(again) == dr.fingerprint_value(dW)
 
 
+@pytest.mark.parametrize("split", [2048, 512])
+def test_grouped_wgrad_full(dr, split):
+    """The grouped weight gradient at the expert shape the bench times (the 8
+    hottest experts of the MoE routing, 86,165 token rows, M 7168, N 2048):
+    bit-equal to the materialised slot partials and their reduce, with 2048-
+    token slots (at most 8 per expert: dW written directly) and 512-token
+    slots (up to 32: chunk sums merged by the tree); sampled columns of every
+    expert within 1e-4 * sum |x dy| of the oracle's exact product."""
+    say(f"grouped wgrad full: generating inputs (split {split})")
+    inp = workloads.grouped_wgrad_inputs(1002)
+    K, M, N = inp.K, inp.M, inp.N
+    off = inp.group_offsets
+    Xd, dYd, offd = dev_bf16(inp.X), dev_bf16(inp.dY), dev(off)
+    say(f"grouped wgrad full: K={K} M={M} N={N} experts={off.size - 1}")
+    out, ws = dr.dr_grouped_wgrad(Xd, dYd, offd, split)
+    dr.dr_workspace_status(ws)
+    fp = dr.fingerprint_value(out)
+    say("grouped wgrad full: materialised partials")
+    P, so, wsg = dr.dr_grouped_splitk_gemm_tn(Xd, dYd, offd, split)
+    ref = dr.dr_grouped_splitk_reduce(P, so, wsg)
+    assert dr.fingerprint_value(ref) == fp
+    del P, ref
+    torch.cuda.empty_cache()
+    again, _ = dr.dr_grouped_wgrad(Xd, dYd, offd, split, ws=ws)
+    assert dr.fingerprint_value(again) == fp
+    say("grouped wgrad full: oracle on sampled columns")
+    rng = np.random.default_rng(split)
+    got = host(out)
+    for g in range(off.size - 1):
+        a, b = int(off[g]), int(off[g + 1])
+        cols = np.sort(rng.choice(M, 6, replace=False))
+        cols[0], cols[-1] = 0, M - 1  # the first and last columns of X among them
+        exact, A = oracle.splitk_reference(np.ascontiguousarray(inp.X[a:b][:, cols]), inp.dY[a:b])
+        err = np.abs(got[g][cols].astype(np.float64) - exact)
+        assert np.all(err <= 1e-4 * A), (g, float((err / np.maximum(A, 1e-300)).max()))
+
+
 def test_decode_attention_full(dr):
     """The bench's decode batch (64 sequences up to 16384 tokens, 32/8 heads)
     at its 512-token KV chunk: every sequence and head against the oracle within

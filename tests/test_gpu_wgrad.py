@@ -36,6 +36,7 @@ CASES = [
     (3, 264, 136, [0, 700, 1500], 100),                # ragged M and N tiles; slots of 100 tokens (partial stages)
     (4, 256, 128, [0, 17, 33, 1000], 2048),            # every group one slot, shorter than a stage
     (5, 7168, 256, [0, 640, 1900], 512),               # the expert hidden size
+    (6, 8, 8, [0, 5, 300], 64),                        # one 8 x 8 corner of a tile: the rest of it zeros
 ]
 
 
