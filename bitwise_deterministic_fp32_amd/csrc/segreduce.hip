@@ -374,6 +374,69 @@ struct TreeCounter {
     }
 };
 
+// The binary counter for a count that is the same in the whole wavefront
+// (one lane group per wavefront), with the same additions in the same order
+// as TreeCounter.  A push merges under wave-uniform branches, and its one
+// store goes to the level the carries end at: a wave-uniform index into a
+// register vector (relative VGPR addressing: one move per element, where a
+// store into an array of levels is a select at every level).  A vector of 16
+// holds the levels of two elements up to depth 8, of one up to 16; deeper
+// counters take a vector of 32 per element.
+template <int DEPTH, int E>
+struct UniformTreeCounter {
+    static_assert(DEPTH <= 32, "levels");
+    static constexpr int kPer = DEPTH <= 8 ? 8 : (DEPTH <= 16 ? 16 : 32);  // slots per element
+    static constexpr int kW = kPer <= 16 ? 16 : 32;                         // vector width
+    static constexpr int kEpv = kW / kPer;                                  // elements per vector
+    typedef float lv_t __attribute__((ext_vector_type(kW)));
+    lv_t lev[(E + kEpv - 1) / kEpv];  // level l of element e: lev[e / kEpv][kPer (e % kEpv) + l]
+    uint32_t count = 0;
+
+    __device__ __forceinline__ UniformTreeCounter() {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+#pragma unroll
+            for (int l = 0; l < DEPTH; ++l) lev[e / kEpv][kPer * (e % kEpv) + l] = neg_zero();
+        }
+    }
+
+    __device__ __forceinline__ void push(float (&s)[E]) {
+        // (the empty asm statement keeps the merge branches from becoming
+        // per-lane selects over every level)
+        const int merges = __builtin_amdgcn_readfirstlane(__builtin_ctz(~count));
+#pragma unroll
+        for (int l = 0; l < DEPTH; ++l) {
+            if (l < merges) {
+                asm volatile("");
+#pragma unroll
+                for (int e = 0; e < E; ++e) s[e] = lev[e / kEpv][kPer * (e % kEpv) + l] + s[e];
+            }
+        }
+        // the count stays below 2^DEPTH - 1 (the host sizes DEPTH), so merges < DEPTH
+#pragma unroll
+        for (int e = 0; e < E; ++e) lev[e / kEpv][kPer * (e % kEpv) + merges] = s[e];
+        ++count;
+    }
+
+    __device__ __forceinline__ void fold(float (&acc)[E]) const {
+        bool have = false;
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[e] = neg_zero();
+        const uint32_t c = __builtin_amdgcn_readfirstlane(count);
+#pragma unroll
+        for (int l = 0; l < DEPTH; ++l) {
+            if ((c >> l) & 1u) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const float v = lev[e / kEpv][kPer * (e % kEpv) + l];
+                    acc[e] = have ? v + acc[e] : v;
+                }
+                have = true;
+            }
+        }
+    }
+};
+
 __device__ __forceinline__ u32x4 add4(const u32x4& old, const float* t) {
     // out = old + T: the old value is the left operand, added once, last
     u32x4 r;
@@ -574,7 +637,8 @@ __global__ __launch_bounds__(kReduceThreads, GROUP == 64 && CIF == 1 && TCLOG <=
 // readlane, each row is one small load per lane (the source rows are few and
 // shared, so they are read through the cache), and the chunk sums and the
 // tree need no per-lane selects.  This form serves fp32 source rows and
-// sources of 2^31 bytes or more; bf16 rows take the LDS form below.  The arithmetic
+// sources of 2^31 bytes or 2^24 rows or more; bf16 rows take the LDS form
+// below.  The arithmetic
 // is the same as the row kernel's: chunks of 8 rows left to right, the chunk
 // sums into the pairwise tree, the tile's result added once into the
 // destination row (or stored as the tile's partial row for tilecombine).
@@ -710,8 +774,13 @@ __global__ __launch_bounds__(kReduceThreads) void segreduce_gen_kernel(
 // chunk's 8 rows to its own 2 KB of LDS and reads them back transposed with
 // ds_read_b64_tr_b16, so that lane l holds columns l and 64 + l of all 8 rows
 // and the chunk sum, the tree and the destination update run wave-uniform, as
-// above.  A chunk's 8 ids (and sorted scales) arrive in scalar registers by
-// one 8-dword scalar buffer load each.  The LDS tile is row-major with the
+// above.  Each lane group fetches the ids of its two rows of a chunk with one
+// 8-byte vector load, one chunk ahead (so a chunk waits for its rows only),
+// and forms their byte offsets with two 24-bit multiply-adds (the host keeps
+// source rows and row bytes below 2^24); the chunk's 8 scales arrive in scalar
+// registers by one 8-dword scalar buffer load (sorted scales; else the ids
+// come the same way and the scales are fetched by id through the scalar
+// cache).  The LDS tile is row-major with the
 // 16-byte chunks of row r swizzled by r & 3, so a transposing read's four rows
 // fall in different banks.
 typedef int32_t i32x4_t __attribute__((ext_vector_type(4)));
@@ -738,73 +807,83 @@ __global__ __launch_bounds__(kReduceThreads) void segreduce_gen16_kernel(
     // the host keeps (tile bound) * slices below 2^32, so 32-bit division suffices
     const uint32_t items = (uint32_t)status[kWordTiles] * (uint32_t)slices;
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int g = lane >> 4, li = lane & 15;  // loads: group g reads rows g and 4 + g, 16-byte piece li
+    const int g = lane >> 4, li = lane & 15;  // loads: group g reads rows 2g and 2g + 1, 16-byte piece li
     const uint32_t wave = __builtin_amdgcn_readfirstlane((blockIdx.x * kReduceThreads + threadIdx.x) / 64);
     const uint32_t nwaves = gridDim.x * (kReduceThreads / 64);
+    if (wave >= items) return;
+    const uint32_t nsl = (uint32_t)slices;
     const uint32_t row_bytes = (uint32_t)H * 2;  // the host keeps the source rows below 2^31 bytes
     // source rows, ids and sorted scales through buffer resources (32-bit offsets)
     const __amdgpu_buffer_rsrc_t srsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(src), 0, (int)src_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t pvrsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(perm), 0, (int)(4 * n), 0x00020000);
     const i32x4_t prsrc = dword_rsrc(perm, 4 * n);
     const i32x4_t crsrc = dword_rsrc(scale, 4 * n);
     uint16_t* rows = lds_rows[wv];
     // LDS offsets: this lane's two row writes, and its transposing reads (read k
     // covers rows 4 (k >> 1) .. + 3 of column block g + 4 (k & 1); lane (g, b, c)
     // addresses row 4 (k >> 1) + b, columns 16 (g + 4 (k & 1)) + 4 c).
-    const int w0 = lds_at<kCols>(g, 8 * li), w1 = lds_at<kCols>(4 + g, 8 * li);
+    const int w0 = lds_at<kCols>(2 * g, 8 * li), w1 = lds_at<kCols>(2 * g + 1, 8 * li);
     int rd[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k)
         rd[k] = lds_at<kCols>(4 * (k >> 1) + ((lane >> 2) & 3), 16 * (g + 4 * (k & 1)) + 4 * (lane & 3));
+    typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+    // this group's two ids (rows 2g and 2g + 1 of the chunk at r0) by one vector
+    // load; rows past a tile's end (other tiles' rows, or 0 past the array's
+    // end: the buffer loads check each dword against the size) are loaded but
+    // not added
+    auto load_ids = [&](int32_t r0) {
+        return __builtin_bit_cast(u32x2v, __builtin_amdgcn_raw_buffer_load_b64(pvrsrc, 4 * (r0 + 2 * g), 0, 0));
+    };
+    auto tile_of = [&](uint32_t it) { return nsl == 1 ? it : it / nsl; };
+    // The ids of each chunk are fetched one chunk ahead (the next item's first
+    // ones during the current item's last chunk), and the next item's tile
+    // record one item ahead, so a chunk waits for its rows only.
+    TileRec tr = tiles[tile_of(wave)];
+    TileRec trn{0, 0, 0, -1};
+    if ((uint64_t)wave + nwaves < items) trn = tiles[tile_of(wave + nwaves)];
+    u32x2v idv = load_ids(tr.r_begin);
     for (uint32_t it = wave; it < items; it += nwaves) {
-        const uint32_t tile = it / (uint32_t)slices;
-        const uint32_t slice = it - tile * (uint32_t)slices;
-        const TileRec tr = tiles[tile];
-        const int32_t c0 = (int32_t)slice * kCols;
+        const uint32_t tile = tile_of(it);
+        const int32_t c0 = (int32_t)(it - tile * nsl) * kCols;
         // loads: 8 columns from c0 + 8 li (idle pieces past H read the slice's first piece)
         const uint32_t lcol_off = (uint32_t)(c0 + 8 * li < H ? c0 + 8 * li : c0) * 2;
         const int32_t r_begin = tr.r_begin, r_end = tr.r_end;
         float* orow = out + (int64_t)tr.dest * H;
+        const int32_t pslot = tr.pslot;
         // results: lane l owns columns c0 + l and c0 + 64 + l
         const int64_t oc0 = c0 + lane, oc1 = c0 + 64 + lane;
         const bool act0 = oc0 < H, act1 = oc1 < H;
         float old0 = 0.f, old1 = 0.f;
-        if (tr.pslot < 0) {
+        if (pslot < 0) {
             old0 = orow[act0 ? oc0 : 0];
             old1 = orow[act1 ? oc1 : 0];
         }
-        TreeCounter<TCLOG + 1, 2, true> tc;
+        UniformTreeCounter<TCLOG + 1, 2> tc;
         for (int32_t r0 = r_begin; r0 < r_end; r0 += 8) {
             const int m = min(8, r_end - r0);  // rows of the chunk (wave-uniform)
-            // the chunk's ids and scales, wave-uniform; rows past the tile's end
-            // (other tiles' rows, or 0 past the arrays' end: the loads check
-            // each dword against the size) are loaded but not added
-            const i32x8_t pv = dr_s_buffer_load_x8(prsrc, 4 * r0, 0);
-            i32x8_t sv{};
-            if (SORTED) sv = dr_s_buffer_load_x8(crsrc, 4 * r0, 0);
+            // source rows are below 2^24 and rows below 2^24 bytes (the host
+            // checks), so 24-bit multiplies give the byte offsets
+            const uint32_t ra = POW2 ? idv[0] >> div_sh : gen_row_of(idv[0], div_m, div_sh);
+            const uint32_t rb = POW2 ? idv[1] >> div_sh : gen_row_of(idv[1], div_m, div_sh);
+            const uint32_t oa = (uint32_t)__umul24(ra, row_bytes), ob = (uint32_t)__umul24(rb, row_bytes);
+            const u32x4 va = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(srsrc, (int)(oa + lcol_off), 0, 0));
+            const u32x4 vb = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(srsrc, (int)(ob + lcol_off), 0, 0));
+            // the next chunk's ids: this tile's next chunk, else the next item's first
+            const u32x2v idn = load_ids(r0 + 8 < r_end ? r0 + 8 : trn.r_begin);
+            // the chunk's scales, wave-uniform
             float sc[8];
             if (SORTED) {
+                const i32x8_t sv = dr_s_buffer_load_x8(crsrc, 4 * r0, 0);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) sc[j] = __int_as_float(sv[j]);  // (not a bit_cast of the element lvalue)
             } else {
+                const i32x8_t pv = dr_s_buffer_load_x8(prsrc, 4 * r0, 0);
 #pragma unroll
                 for (int j = 0; j < 8; ++j) sc[j] = scale[(uint32_t)pv[j]];
             }
-            uint32_t off[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const uint32_t p = (uint32_t)pv[j];
-                off[j] = (POW2 ? p >> div_sh : gen_row_of(p, div_m, div_sh)) * row_bytes;
-            }
-            uint32_t oa = off[0], ob = off[4];
-            oa = g == 1 ? off[1] : oa;
-            ob = g == 1 ? off[5] : ob;
-            oa = g == 2 ? off[2] : oa;
-            ob = g == 2 ? off[6] : ob;
-            oa = g == 3 ? off[3] : oa;
-            ob = g == 3 ? off[7] : ob;
-            const u32x4 va = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(srsrc, (int)(oa + lcol_off), 0, 0));
-            const u32x4 vb = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(srsrc, (int)(ob + lcol_off), 0, 0));
             *reinterpret_cast<u32x4*>(rows + w0) = va;
             *reinterpret_cast<u32x4*>(rows + w1) = vb;
             __builtin_amdgcn_wave_barrier();
@@ -828,64 +907,78 @@ __global__ __launch_bounds__(kReduceThreads) void segreduce_gen16_kernel(
                 }
             }
             tc.push(s2);
+            idv = idn;
         }
         float t2[2];
         tc.fold(t2);
-        if (tr.pslot < 0) {
+        if (pslot < 0) {
             if (act0) orow[oc0] = old0 + t2[0];  // out = old + T
             if (act1) orow[oc1] = old1 + t2[1];
         } else {
-            float* prow = partials + (int64_t)tr.pslot * H;
+            float* prow = partials + (int64_t)pslot * H;
             if (act0) prow[oc0] = t2[0];
             if (act1) prow[oc1] = t2[1];
         }
+        tr = trn;
+        if ((uint64_t)it + 2 * (uint64_t)nwaves < items) trn = tiles[tile_of(it + 2 * nwaves)];
     }
 }
 
 // Merges the partial rows of each multi-tile destination in tile order (the
-// tiles are the leaves of the destination's tree at this level).  Eight
-// partial rows are in flight per lane.
-template <int GROUP, int DEPTH>
+// tiles are the leaves of the destination's tree at this level).  One
+// wavefront per (destination, 128-column slice), lane l owning columns 2l and
+// 2l + 1 of the slice (one 8-byte piece), so the tile count and the counter
+// are the same in the whole wavefront; up to 16 partial rows are in flight
+// per lane.
+template <int DEPTH>
 __global__ __launch_bounds__(kReduceThreads) void tilecombine_kernel(float* __restrict__ out, int64_t H,
                                                                      const float* __restrict__ partials,
                                                                      const MultiRec* __restrict__ multis,
                                                                      int64_t slices, int32_t* status,
                                                                      uint64_t* __restrict__ fp_part) {
     if (status[kWordStatus] != 0) return;
+    constexpr int R = 16;  // partial rows in flight
     uint64_t fp_acc = 0;
     const uint32_t items = (uint32_t)status[kWordMultis] * (uint32_t)slices;
-    const int lig = threadIdx.x % GROUP;
-    const uint32_t group = (blockIdx.x * kReduceThreads + threadIdx.x) / GROUP;
-    const uint32_t ngroups = (gridDim.x * kReduceThreads) / GROUP;
-    for (uint32_t it = group; it < items; it += ngroups) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t wave = __builtin_amdgcn_readfirstlane((blockIdx.x * kReduceThreads + threadIdx.x) / 64);
+    const uint32_t nwaves = gridDim.x * (kReduceThreads / 64);
+    for (uint32_t it = wave; it < items; it += nwaves) {
         const uint32_t mi = it / (uint32_t)slices;
         const uint32_t slice = it - mi * (uint32_t)slices;
         const MultiRec mr = multis[mi];
-        const int64_t col = (int64_t)slice * GROUP * 4 + 4 * lig;
-        if (col >= H) continue;
+        const int64_t col = (int64_t)slice * 128 + 2 * lane;
+        const bool active = col < H;
+        const int64_t lcol = active ? col : 0;  // idle lanes read a valid piece
         float* orow = out + (int64_t)mr.dest * H;
-        const u32x4 old = load16(orow + col);
-        TreeCounter<DEPTH, 4> tc;  // DEPTH levels hold any count below 2^DEPTH
-        for (int32_t q0 = 0; q0 < mr.ntiles; q0 += 8) {
-            const int m = min(8, mr.ntiles - q0);
-            u32x4 raw[8];
+        const u32x2 old = *reinterpret_cast<const u32x2*>(orow + lcol);
+        UniformTreeCounter<DEPTH, 2> tc;
+        for (int32_t q0 = 0; q0 < mr.ntiles; q0 += R) {
+            const int m = min(R, mr.ntiles - q0);  // wave-uniform
+            u32x2 raw[R];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                raw[j] = load16(partials + (int64_t)(mr.pslot0 + q0 + min(j, m - 1)) * H + col);
+            for (int j = 0; j < R; ++j)
+                raw[j] = *reinterpret_cast<const u32x2*>(partials + (int64_t)(mr.pslot0 + q0 + min(j, m - 1)) * H +
+                                                         lcol);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
+            for (int j = 0; j < R; ++j) {
                 if (j < m) {
-                    float s[4];
-                    Vec<DR_F32>::widen(raw[j], s);
-                    tc.push(s);
+                    float v[2] = {__uint_as_float(raw[j].x), __uint_as_float(raw[j].y)};
+                    tc.push(v);
                 }
             }
         }
-        float t[4];
+        float t[2];
         tc.fold(t);
-        const u32x4 now = add4(old, t);
-        store16(orow + col, now);
-        if (fp_part) fp_acc += fp_delta(old, now, ((int64_t)mr.dest * H + col) >> 1);
+        // out = old + T: the old value is the left operand, added once, last
+        const u32x2 now{__float_as_uint(__uint_as_float(old.x) + t[0]), __float_as_uint(__uint_as_float(old.y) + t[1])};
+        if (active) {
+            *reinterpret_cast<u32x2*>(orow + col) = now;
+            if (fp_part) {
+                const int64_t w = ((int64_t)mr.dest * H + col) >> 1;
+                fp_acc += fp_term(((uint64_t)now.y << 32) | now.x, w) - fp_term(((uint64_t)old.y << 32) | old.x, w);
+            }
+        }
     }
     if (fp_part) {
         __shared__ uint64_t fsm[kReduceThreads / 64];
@@ -985,9 +1078,12 @@ hipError_t launch_segreduce_gen(dim3 grid, float* out, int64_t H, const void* sr
                                 dr_dtype dt, const int32_t* perm, const TileRec* tiles, float* partials, int tc_log2,
                                 const int32_t* status, const float* scale, bool scale_sorted, uint32_t rps,
                                 hipStream_t s) {
-    // bf16 source rows of fewer than 2^31 bytes in all take the LDS form (32-bit buffer offsets)
+    // bf16 source rows of fewer than 2^31 bytes in all take the LDS form (32-bit
+    // buffer offsets, formed by 24-bit multiplies: fewer than 2^24 rows of fewer
+    // than 2^24 bytes)
     const int64_t src_bytes = src_rows * H * 2;
-    if (dt == DR_BF16 && src_bytes < ((int64_t)1 << 31) && n < ((int64_t)1 << 29)) {
+    if (dt == DR_BF16 && src_bytes < ((int64_t)1 << 31) && n < ((int64_t)1 << 29) && src_rows < ((int64_t)1 << 24) &&
+        H * 2 < ((int64_t)1 << 24)) {
         uint32_t sh = 0;
         while (((uint64_t)1 << sh) < rps) ++sh;
         const uint32_t m = (uint32_t)((((uint64_t)1 << (31 + sh)) + rps - 1) / rps);
@@ -1088,30 +1184,19 @@ hipError_t launch_segreduce(float* out, int64_t hidden, const void* src, dr_dtyp
 
 hipError_t launch_tilecombine(float* out, int64_t hidden, const float* partials, const MultiRec* multis, int64_t n,
                               int tc_log2, int32_t* status, uint64_t* fp_part, hipStream_t s) {
-    const int64_t lanes = hidden / 4;
-    const int g = group_for(lanes);
-    const int64_t slices = (lanes + g - 1) / g;
+    const int64_t slices = (hidden + 127) / 128;
     const dim3 grid(persistent_grid());
     // the most tiles one destination can have, and the counter depth it needs
     const int64_t max_tiles = n / ((int64_t)8 << tc_log2) + 1;
     int depth = 1;
     while (depth < 62 && ((int64_t)1 << depth) <= max_tiles) ++depth;
-#define DR_TC(G, D)                                                                                             \
-    hipLaunchKernelGGL((tilecombine_kernel<G, D>), grid, dim3(kReduceThreads), 0, s, out, hidden, partials, multis, \
-                       slices, status, fp_part)
-#define DR_TC_DEPTH(G)        \
-    if (depth <= 8) DR_TC(G, 8);  \
-    else if (depth <= 16) DR_TC(G, 16); \
-    else DR_TC(G, 26);
-    if (depth > 26) return hipErrorInvalidValue;
-    if (g == 16) {
-        DR_TC_DEPTH(16)
-    } else if (g == 32) {
-        DR_TC_DEPTH(32)
-    } else {
-        DR_TC_DEPTH(64)
-    }
-#undef DR_TC_DEPTH
+    if (depth > 32) return hipErrorInvalidValue;
+#define DR_TC(D) \
+    hipLaunchKernelGGL((tilecombine_kernel<D>), grid, dim3(kReduceThreads), 0, s, out, hidden, partials, multis, slices, \
+                       status, fp_part)
+    if (depth <= 8) DR_TC(8);
+    else if (depth <= 16) DR_TC(16);
+    else DR_TC(32);
 #undef DR_TC
     return hipGetLastError();
 }
