@@ -364,6 +364,25 @@ def test_sparse_attn_dk_matches_oracle(dr, nq, topk, H, K, q_dtype):
     assert_bits_equal(host(dK2), want, "reused plan")
 
 
+@pytest.mark.parametrize("nq", [(1 << 24) - 1, 1 << 24])
+def test_sparse_attn_dk_at_the_row_offset_limit(dr, nq):
+    """The bf16 LDS form forms row byte offsets with 24-bit multiplies, so it takes
+    sources of fewer than 2^24 rows; 2^24 rows go to the generic form.  Both sides
+    of that limit, with the last query rows selected, equal the oracle bit for bit."""
+    say(f"sparse_attn_dk row-offset limit nq={nq}")
+    H, K, topk = 8, 1000, 1
+    rng = np.random.default_rng(24 + nq % 7)
+    key_idx = rng.integers(0, K, size=(nq, topk), dtype=np.int32)
+    key_idx[-3:, 0] = K - 1  # the last source rows land on one key
+    Qh = workloads.normal_bf16(31, 0, nq * H).reshape(nq, H)
+    dS = workloads.normal_f32(31, 1, nq * topk, 0.1).reshape(nq, topk)
+    dK0 = workloads.normal_f32(31, 2, K * H).reshape(K, H)
+    dK = dev(dK0)
+    dr.dr_sparse_attn_dk(dK, dev_bf16(Qh), dev(dS), dev(key_idx))
+    want = oracle.sparse_attn_dk(dK0, Qh, dS, key_idx, threads=8)
+    assert_bits_equal(host(dK), want, f"sparse_attn_dk nq={nq}")
+
+
 def test_sparse_attn_dk_bad_key_leaves_dk_untouched(dr):
     inp = workloads.sparse_attn_dk_inputs(5, 64, 128, 8, 64, s=1.1)
     bad = inp.key_idx.copy()
