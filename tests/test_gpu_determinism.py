@@ -174,12 +174,17 @@ def test_index_add_launch_invariance(dr, dk):
                 assert fp == ref, (grid, tc, st)
 
 
-def test_sparse_attn_dk_launch_invariance_and_replays(dr):
-    inp = workloads.sparse_attn_dk_inputs(31, 600, 400, 32, 128, s=1.1)
+@pytest.mark.parametrize("H", [128, 384])
+def test_sparse_attn_dk_launch_invariance_and_replays(dr, H):
+    """Grid, tile and sort-tile sizes never change a bit; with a grid of one or
+    seven workgroups every wavefront walks many items (and with H = 384 the
+    items of a tile's three column slices), so the look-ahead across items is
+    exercised.  The first result is also the oracle's."""
+    inp = workloads.sparse_attn_dk_inputs(31, 600, 400, 32, H, s=1.1)
     Q, dS, idx = dev_bf16(inp.Q), dev(inp.dS), dev(inp.key_idx)
     ref = None
-    for grid, tc, st in ((0, 5, 0), (7, 3, 8), (1000, 7, 12), (0, 4, 13), (0, 6, 10), (0, 5, 0)):
-        say(f"sparse_attn_dk launch grid={grid} tile=2^{tc} sort_tile={st}")
+    for grid, tc, st in ((0, 5, 0), (7, 3, 8), (1000, 7, 12), (0, 4, 13), (0, 6, 10), (1, 5, 0), (0, 5, 0)):
+        say(f"sparse_attn_dk H={H} launch grid={grid} tile=2^{tc} sort_tile={st}")
         dr.dr_set_launch_params(grid_blocks=grid, tile_chunks_log2=tc, sort_tile_log2=st)
         try:
             dK = dev(inp.dK0)
@@ -187,8 +192,22 @@ def test_sparse_attn_dk_launch_invariance_and_replays(dr):
             fp = dr.fingerprint_value(dK)
         finally:
             dr.dr_set_launch_params(reset=True)
+        if ref is None:
+            assert_bits_equal(host(dK), oracle.sparse_attn_dk(inp.dK0, inp.Q, inp.dS, inp.key_idx), "sparse_attn_dk")
         ref = fp if ref is None else ref
         assert fp == ref, (grid, tc, st)
+    # a reused plan (scales read by source id) on small grids
+    perm, seg, _ = dr.dr_sort_by_dest(idx.reshape(-1).contiguous(), 400, want_inv=False)
+    for grid in (1, 7):
+        say(f"sparse_attn_dk H={H} reused plan grid={grid}")
+        dr.dr_set_launch_params(grid_blocks=grid)
+        try:
+            dK = dev(inp.dK0)
+            dr.dr_sparse_attn_dk(dK, Q, dS, idx, perm=perm, seg_offsets=seg)
+            fp = dr.fingerprint_value(dK)
+        finally:
+            dr.dr_set_launch_params(reset=True)
+        assert fp == ref, ("reused plan", grid)
 
 
 def test_sort_launch_invariance(dr, dk):
