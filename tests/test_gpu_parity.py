@@ -225,6 +225,36 @@ def test_index_add_matches_oracle(dr, n, D, H, src_dtype, dist):
     assert_bits_equal(host(out), want, "index_add")
 
 
+def test_index_add_deep_tile_merge(dr):
+    """With tiles of 2^3 chunks (64 rows), 2^22 rows make the host's bound ask
+    tilecombine for 17 levels, its deepest counter form; the hot destination
+    (half the rows, about 32,768 tiles) merges its partial rows through it,
+    and the result and the kept fingerprint equal the oracle's."""
+    n, D, H = (1 << 22) + 5, 1000, 8
+    say(f"index_add deep tile merge n={n} D={D} H={H} tile=2^3")
+    index, src, out0 = _index_add_case(77, n, D, H, "bf16", "hot")
+    dr.dr_set_launch_params(tile_chunks_log2=3)
+    try:
+        out = dev(out0)
+        dr.dr_index_add(out, dev_bf16(src), dev(index))
+        got = host(out)
+    finally:
+        dr.dr_set_launch_params(reset=True)
+    assert_bits_equal(got, oracle.index_add(out0, src, index, threads=8), "index_add deep tile merge")
+    # the same with the fingerprint kept current
+    h0 = oracle.fingerprint(out0)
+    h = torch.tensor([h0 - (1 << 64) if h0 >= (1 << 63) else h0], dtype=torch.int64, device="cuda")
+    dr.dr_set_launch_params(tile_chunks_log2=3)
+    try:
+        out = dev(out0)
+        dr.dr_index_add_fingerprinted(out, dev_bf16(src), dev(index), h)
+        got2 = host(out)
+    finally:
+        dr.dr_set_launch_params(reset=True)
+    assert_bits_equal(got2, got, "fingerprinted")
+    assert (int(h.item()) & ((1 << 64) - 1)) == oracle.fingerprint(got), "kept fingerprint"
+
+
 @pytest.mark.parametrize("D", [10, 4096, 131072])
 def test_index_add_empty_with_dirty_workspace(dr, D):
     """No contributions, one or two sort passes, a workspace full of 0xFF bytes:
