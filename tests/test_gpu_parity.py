@@ -213,6 +213,8 @@ def _index_add_case(seed, n, D, H, src_dtype, dist):
     (3000, 131072, 4096, "bf16", "zipf"),   # embedding-like: mostly singletons
     (5000, 300, 136, "f32", "uniform"),     # ragged lane group (34 pieces)
     (4000, 2000, 24, "bf16", "zipf"),       # a row narrower than one lane group
+    (30000, 40, 136, "bf16", "hot"),        # long segments merged over a partial second 128-column slice
+    (30001, 40, 132, "f32", "hot"),         # the same with fp32 rows (4 columns in the last slice)
 ])
 def test_index_add_matches_oracle(dr, n, D, H, src_dtype, dist):
     say(f"index_add n={n} D={D} H={H} {src_dtype} {dist}")
