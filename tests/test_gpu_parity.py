@@ -372,6 +372,7 @@ def test_index_add_order_example_fp32(dr):
     (3, 5, 8, 9, "bf16"),          # tiny, most keys untouched
     (500, 24, 384, 1000, "bf16"),  # three 128-column slices; top-k not a power of two
     (200, 12, 136, 50, "bf16"),    # a second slice of 8 columns
+    (2000, 40, 136, 200, "bf16"),  # keys of several tiles merged over that partial slice
 ])
 def test_sparse_attn_dk_matches_oracle(dr, nq, topk, H, K, q_dtype):
     say(f"sparse_attn_dk nq={nq} topk={topk} H={H} K={K} {q_dtype}")
